@@ -1,0 +1,102 @@
+"""Reference implementation of the repacked INT4 tile layout (test infrastructure only).
+
+The layout is this library's own (the pages give none); it is written out here
+independently of the device code so that the device repack can be checked byte
+for byte, and so that ``unrepack_ref(repack_ref(.))`` pins it as a bijection.
+The point of repacking once, offline, is the one [P5] "关键数据解读" item 4
+makes: a format whose layout is translated on every run is slow.
+
+Layout (G = 128, KT = K / G, NP = ceil(N / 64)):
+
+* Column permutation.  If ``g_idx`` is given and is not the trivial
+  k // G map, ``perm`` = stable argsort(g_idx): permuted column k' is original
+  column perm[k'], and every run of G permuted columns is one whole group
+  (act-order, [P2] §三 3.1 / [P4] "技术原理" section).  Otherwise perm is None.
+* Codes: uint8 [NP][KT][4][64][16].  For output column n = 64p + 16c + i and
+  permuted column k' = 128t + 32j + 8b + e, the code sits in lane l = i + 16b,
+  32-bit word j of that lane's 16 bytes (little endian), at nibble slot
+  (e >> 1) + 4 * (e & 1).  Columns n >= N are zero padding.
+* Scales: fp16 [NP][KT][16][4], entry [p][t][i][c] = scale of column
+  64p + 16c + i in group t (0 for padding).
+* Zeros: uint16 [NP][KT][16], bits [4c, 4c + 4) of [p][t][i] = zero of column
+  64p + 16c + i in group t (0 for padding).
+"""
+
+import numpy as np
+
+from .int4 import unpack_qweight, unpack_qzeros, default_g_idx
+
+GROUP = 128
+
+
+def nibble_slot(e):
+    return (e >> 1) + 4 * (e & 1)
+
+
+def canonical_perm(g_idx, K, group_size=GROUP):
+    """perm for a g_idx, or None when g_idx is absent or trivial."""
+    if g_idx is None:
+        return None
+    gi = np.asarray(g_idx, dtype=np.int64)
+    if np.array_equal(gi, default_g_idx(K, group_size)):
+        return None
+    return np.argsort(gi, kind="stable").astype(np.int32)
+
+
+def repack_ref(qweight, scales, qzeros, g_idx=None, group_size=GROUP):
+    """Canonical GPTQ-style tensors -> (codes_r, scales_r, zeros_r, perm)."""
+    assert group_size == GROUP
+    q = unpack_qweight(qweight)                      # [N, K]
+    N, K = q.shape
+    z = unpack_qzeros(qzeros)[:, :N]                 # [KT, N]
+    s = np.asarray(scales, dtype=np.float16)         # [KT, N]
+    KT = K // GROUP
+    NP = (N + 63) // 64
+    perm = canonical_perm(g_idx, K, group_size)
+    if perm is not None:
+        q = q[:, perm]
+    Np = NP * 64
+    qp = np.zeros((Np, K), dtype=np.uint8)
+    qp[:N] = q
+    zp = np.zeros((KT, Np), dtype=np.uint8)
+    zp[:, :N] = z
+    sp = np.zeros((KT, Np), dtype=np.float16)
+    sp[:, :N] = s
+
+    # qp[n, k'] with n = 64p + 16c + i and k' = 128t + 32j + 8b + e
+    v = qp.reshape(NP, 4, 16, KT, 4, 4, 8).astype(np.uint32)   # p c i t j b e
+    words = np.zeros((NP, 4, 16, KT, 4, 4), dtype=np.uint32)   # p c i t j b
+    for e in range(8):
+        words |= v[..., e] << np.uint32(4 * nibble_slot(e))
+    # -> [p][t][c][lane = i + 16 b][j]
+    words = words.transpose(0, 3, 1, 5, 2, 4).reshape(NP, KT, 4, 64, 4)
+    codes_r = np.ascontiguousarray(words).view(np.uint8).reshape(-1)
+
+    scales_r = sp.reshape(KT, NP, 4, 16).transpose(1, 0, 3, 2).copy()   # p t i c
+    zz = zp.reshape(KT, NP, 4, 16).transpose(1, 0, 3, 2).astype(np.uint16)  # p t i c
+    zeros_r = np.zeros((NP, KT, 16), dtype=np.uint16)
+    for c in range(4):
+        zeros_r |= zz[..., c] << np.uint16(4 * c)
+    return codes_r, scales_r.reshape(-1), zeros_r.reshape(-1), perm
+
+
+def unrepack_ref(codes_r, scales_r, zeros_r, K, N):
+    """Inverse of the tile layout: -> (codes [N, K] in permuted column order,
+    scales fp16 [KT, N], zeros uint8 [KT, N])."""
+    KT = K // GROUP
+    NP = (N + 63) // 64
+    words = np.asarray(codes_r, dtype=np.uint8).view(np.uint32).reshape(NP, KT, 4, 4, 16, 4)
+    # p t c b i j -> p c i t j b
+    words = words.transpose(0, 2, 4, 1, 5, 3)
+    v = np.zeros(words.shape + (8,), dtype=np.uint8)
+    for e in range(8):
+        v[..., e] = (words >> np.uint32(4 * nibble_slot(e))) & np.uint32(0xF)
+    q = v.reshape(NP * 64, K)[:N]
+    s = np.asarray(scales_r, dtype=np.float16).reshape(NP, KT, 16, 4).transpose(1, 0, 3, 2)
+    s = s.reshape(KT, NP * 64)[:, :N]
+    zr = np.asarray(zeros_r, dtype=np.uint16).reshape(NP, KT, 16)
+    z = np.zeros((NP, KT, 16, 4), dtype=np.uint8)
+    for c in range(4):
+        z[..., c] = (zr >> np.uint16(4 * c)) & np.uint16(0xF)
+    z = z.transpose(1, 0, 3, 2).reshape(KT, NP * 64)[:, :N]
+    return q.copy(), s.copy(), z.copy()

@@ -1,0 +1,139 @@
+"""Pins for oracle/gemm.py and oracle/repack.py."""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import gemm, int4, repack, fp
+from bit_weight_only_gemm_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_fp64_matmul_vs_exact_fraction_triple_loop():
+    M, N, K = 2, 3, 16
+    x = synth.to_f16_bits(synth.activations("test/gemm/frac/x", M, K))
+    w = synth.to_f16_bits(synth.weights("test/gemm/frac/w", N, K, std=1.0))
+    y = gemm.gemm_ref_bits(x, w, "f16")
+    xf = fp.bits_to_f64(x, "f16")
+    wf = fp.bits_to_f64(w, "f16")
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(xf[m, k])) * Fraction(float(wf[n, k])) for k in range(K))
+            bound = K * 2.0**-52 * sum(abs(float(xf[m, k]) * float(wf[n, k])) for k in range(K))
+            assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(bound)
+
+
+def test_scaling_invariance_and_zero_weights():
+    M, N, K = 4, 8, 256
+    x = synth.activations("test/gemm/scale/x", M, K).astype(np.float64)
+    w = synth.weights("test/gemm/scale/w", N, K).astype(np.float64)
+    y1 = gemm.gemm_ref_fp64(x, w)
+    y2 = gemm.gemm_ref_fp64(2.0 * x, w)
+    assert np.array_equal(y2, 2.0 * y1)
+    assert not gemm.gemm_ref_fp64(x, np.zeros_like(w)).any()
+
+
+def test_onehot_probe_reads_one_weight():
+    N, K = 8, 256
+    w = synth.to_f16_bits(synth.weights("test/gemm/onehot/w", N, K))
+    for k in (0, 77, 255):
+        x = np.zeros((1, K), dtype=np.float32)
+        x[0, k] = 1.0
+        y = gemm.gemm_ref_bits(synth.to_f16_bits(x), w, "f16")
+        assert np.array_equal(y[0], fp.bits_to_f64(w[:, k], "f16"))
+
+
+def test_rel_err_definition():
+    assert gemm.rel_err(np.array([1.0, 2.0]), np.array([1.0, 2.0])) == 0.0
+    assert gemm.rel_err(np.array([1.0, 2.5]), np.array([1.0, 2.0])) == 0.25
+    assert gemm.rel_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+def test_quantized_product_within_closed_form_bound_of_float_product():
+    # |x W^T - x W_deq^T| <= sum_k |x_k| (|w - deq| bound): RTN error per weight
+    # is <= s (1/2 + 15 * 2^-11) and the fp16 round of deq adds <= 2^-11 |deq|.
+    M, N, K, G = 3, 16, 512, 128
+    W = synth.weights("test/gemm/bound/W", N, K)
+    x = synth.to_f16_bits(synth.activations("test/gemm/bound/x", M, K))
+    q, s, z = int4.quantize_rtn_int4(W, G)
+    wd = int4.dequant_int4(int4.pack_qweight(q), s, int4.pack_qzeros(z), None, G, "f16")
+    xf = fp.bits_to_f64(x, "f16")
+    y_ref = gemm.gemm_ref_bits(x, wd, "f16")
+    y_flt = gemm.gemm_ref_fp64(xf, W.astype(np.float64))
+    sk = s.astype(np.float64)[np.arange(K) // G].T
+    per_w = sk * (0.5 + 15 * 2.0**-11) + 2.0**-11 * np.abs(fp.bits_to_f64(wd, "f16")) + 1e-12
+    bound = np.abs(xf) @ per_w.T
+    assert np.all(np.abs(y_ref - y_flt) <= bound)
+
+
+# ---------------------------------------------------------------- repack (P13)
+
+@pytest.mark.parametrize("N", [64, 200, 512])
+@pytest.mark.parametrize("act_order", [False, True])
+def test_repack_is_a_bijection(N, act_order):
+    K, G = 512, 128
+    W = synth.weights(f"test/repack/W/{N}", N, K)
+    gi = synth.act_order_gidx(f"test/repack/g/{N}", K, G) if act_order else None
+    q, s, z = int4.quantize_rtn_int4(W, G, gi)
+    codes_r, scales_r, zeros_r, perm = repack.repack_ref(
+        int4.pack_qweight(q), s, int4.pack_qzeros(z), gi)
+    NP = (N + 63) // 64
+    assert codes_r.size == NP * (K // G) * 4096
+    assert scales_r.size == NP * (K // G) * 64 and zeros_r.size == NP * (K // G) * 16
+    assert (perm is None) == (not act_order)
+    q2, s2, z2 = repack.unrepack_ref(codes_r, scales_r, zeros_r, K, N)
+    qp = q if perm is None else q[:, perm]
+    assert np.array_equal(q2, qp)
+    assert np.array_equal(s2, s) and np.array_equal(z2, z)
+
+
+def test_repack_tile_addressing_single_code():
+    # one nonzero code lands at the documented byte and nibble
+    K, N, G = 256, 128, 128
+    rr = np.random.default_rng(9)
+    for _ in range(50):
+        n, k = int(rr.integers(N)), int(rr.integers(K))
+        q = np.zeros((N, K), dtype=np.uint8)
+        q[n, k] = 0xB
+        codes_r, _, _, _ = repack.repack_ref(
+            int4.pack_qweight(q), np.zeros((K // G, N), np.float16),
+            int4.pack_qzeros(np.zeros((K // G, N), np.uint8)))
+        p, c, i = n // 64, (n % 64) // 16, n % 16
+        t, j, b, e = k // 128, (k % 128) // 32, (k % 32) // 8, k % 8
+        lane = i + 16 * b
+        off = (((p * (K // G) + t) * 4 + c) * 64 + lane) * 16 + 4 * j
+        word = int(codes_r[off:off + 4].view(np.uint32)[0])
+        slot = (e >> 1) + 4 * (e & 1)
+        assert word == 0xB << (4 * slot)
+        assert np.count_nonzero(codes_r) == 1
+
+
+def test_repack_trivial_gidx_gives_no_perm():
+    K, N, G = 256, 64, 128
+    q = np.zeros((N, K), np.uint8)
+    out = repack.repack_ref(int4.pack_qweight(q), np.zeros((2, N), np.float16),
+                            int4.pack_qzeros(np.zeros((2, N), np.uint8)),
+                            int4.default_g_idx(K, G))
+    assert out[3] is None
+
+
+# ------------------------------------------------------- facts printed on the pages
+
+def test_page_facts_fixture():
+    with open(os.path.join(GOLDEN, "page_facts.json")) as f:
+        facts = json.load(f)
+    gptq = facts["gptq_quantize_config"]["value"]
+    assert gptq["bits"] == 4 and gptq["group_size"] == repack.GROUP
+    assert facts["int4_levels"]["value"] == 16 == len(range(0, 16))
+    # 4-bit codes are a quarter of fp16 bytes; with G = 128 the scales (fp16)
+    # and 4-bit zeros add 2.5 / 128 bytes per weight
+    ratio = facts["qwen32b_weight_bytes_fp16_vs_4bit"]["value"]
+    assert ratio["fp16_GB"] / ratio["int4_GB"] == 4
+    K, N, G = 5120, 55296, 128
+    codes = K * N // 2
+    meta = (K // G) * N * 2 + (K // G) * N // 2
+    assert abs((codes + meta) / (2 * K * N) - 0.25) < 0.011

@@ -1,0 +1,121 @@
+"""Pins for oracle/nf4.py: closed-form codebook, brute-force argmin, double quant."""
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+from scipy.special import ndtri
+
+from oracle import nf4
+from bit_weight_only_gemm_amd import synth
+
+
+def test_codebook_closed_form_properties():
+    L = nf4.nf4_codebook()
+    assert L.dtype == np.float32 and L.shape == (16,)
+    assert np.all(np.diff(L) > 0)
+    assert L[0] == -1.0 and L[15] == 1.0 and L[7] == 0.0
+    assert np.sum(L > 0) == 8 and np.sum(L < 0) == 7      # asymmetric: 8 up, 7 down
+    # levels crowd near zero: gaps grow away from the centre on each side
+    pos = L[7:]
+    neg = L[:8][::-1]
+    assert np.all(np.diff(np.diff(pos)) > 0) and np.all(np.diff(np.diff(-neg)) > 0)
+
+
+def test_codebook_matches_independent_inverse_normal():
+    # recompute with scipy's ndtri (a different inverse-normal implementation)
+    d = 0.5 * ((1 - 1 / 30) + (1 - 1 / 32))
+    pos = ndtri(np.linspace(d, 0.5, 9)[:-1])
+    neg = -ndtri(np.linspace(d, 0.5, 8)[:-1])
+    v = np.sort(np.concatenate([pos, [0.0], neg])) / ndtri(d)
+    assert np.array_equal(v.astype(np.float32), nf4.nf4_codebook())
+
+
+def test_quantize_brute_force_argmin():
+    L = nf4.nf4_codebook()
+    W = synth.weights("test/nf4/brute", 3, 256)
+    W[2, 64:128] = 0.0                                     # an all-zero block
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    assert absmax.shape == (12,) and absmax[2 * 4 + 1] == 0.0
+    for n in range(3):
+        for k in range(256):
+            a = absmax[n * 4 + k // 64]
+            v = np.float32(0.0) if a == 0 else np.float32(W[n, k]) / np.float32(a)
+            best, bi = None, None
+            for i in range(16):                            # first strict minimum
+                d = np.float32(abs(np.float32(v) - L[i]))
+                if best is None or d < best:
+                    best, bi = d, i
+            assert codes[n, k] == bi
+    assert np.all(codes[2, 64:128] == 7)
+
+
+def test_quantize_error_bound_and_block_max():
+    L = nf4.nf4_codebook()
+    W = synth.weights("test/nf4/bound", 16, 1024)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    v = W.reshape(-1, 64) / absmax[:, None]
+    err = np.abs(v - L[codes.reshape(-1, 64)])
+    assert err.max() <= 0.5 * np.diff(L).max() + 1e-6
+    # the element that sets absmax maps to an endpoint (+-1) exactly
+    idx = np.abs(W.reshape(-1, 64)).argmax(axis=1)
+    ends = codes.reshape(-1, 64)[np.arange(idx.size), idx]
+    assert np.all((ends == 0) | (ends == 15))
+
+
+def test_tie_goes_to_lower_index():
+    L = nf4.nf4_codebook()
+    for i in range(15):
+        m = np.float32((np.float64(L[i]) + np.float64(L[i + 1])) / 2)
+        d0 = np.float32(abs(m - L[i]))
+        d1 = np.float32(abs(m - L[i + 1]))
+        W = np.zeros((1, 64), dtype=np.float32)
+        W[0, 0] = 1.0                                      # absmax = 1
+        W[0, 1] = m
+        codes, _ = nf4.quantize_nf4(W, 64)
+        want = i if d0 <= d1 else i + 1
+        assert codes[0, 1] == want
+
+
+def test_pack_unpack_exhaustive():
+    c = np.array([[a, b] for a in range(16) for b in range(16)], dtype=np.uint8).reshape(1, 512)
+    p = nf4.pack_nf4(c)
+    assert p.shape == (1, 256)
+    assert np.array_equal(p[0], np.arange(256, dtype=np.uint8) // 16 | (np.arange(256) % 16 << 4).astype(np.uint8))
+    assert np.array_equal(nf4.unpack_nf4(p), c)
+
+
+def test_double_quant_closed_form():
+    r = np.random.default_rng(7)
+    absmax = np.abs(r.standard_normal(1000)).astype(np.float32) * np.float32(0.08)
+    aq, sc = nf4.double_quant(absmax, 256)
+    assert sc.shape == (4,) and aq.dtype == np.uint8
+    for g in range(4):
+        blk = absmax[g * 256:(g + 1) * 256]
+        assert aq[g * 256 + int(np.argmax(blk))] == 255
+        back = aq[g * 256:(g + 1) * 256].astype(np.float64) * float(sc[g])
+        assert np.abs(back - blk).max() <= float(sc[g]) * (0.5 + 1e-5)
+    z = nf4.double_quant(np.zeros(300, dtype=np.float32), 256)
+    assert not z[0].any() and not z[1].any()
+
+
+def test_dequant_nf4_vs_exact_rational():
+    L = nf4.nf4_codebook()
+    r = np.random.default_rng(8)
+    N, K = 4, 512                                        # 32 blocks
+    codes = r.integers(0, 16, size=(N, K)).astype(np.uint8)
+    codes[0, :16] = np.arange(16)
+    aq = r.integers(0, 256, size=N * K // 64).astype(np.uint8)
+    aq[0] = 255
+    sc = np.array([0.0123], dtype=np.float32)
+    for dtype in ("bf16", "f16"):
+        got = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)
+        for n in range(N):
+            for k in range(0, K, 5):
+                b = n * (K // 64) + k // 64
+                a32 = np.float32(Fraction(int(aq[b])) * Fraction(float(sc[0])))
+                w32 = np.float32(Fraction(float(L[codes[n, k]])) * Fraction(float(a32)))
+                t = torch.tensor([float(w32)], dtype=torch.float64)
+                t = t.to(torch.bfloat16 if dtype == "bf16" else torch.float16)
+                want = t.view(torch.int16).numpy().view(np.uint16)[0]
+                assert got[n, k] == want, (n, k, dtype)
