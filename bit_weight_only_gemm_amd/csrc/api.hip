@@ -1,0 +1,277 @@
+// api.hip -- the C ABI declared in include/w4a16.h: host-side validation,
+// the act-order permutation, the NF4 codebook, and dispatch to the kernels.
+//
+// Every entry point validates all arguments on the host before launching
+// anything and returns a status code; nothing throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/w4a16.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a16 {
+void set_target_wgs(int v);
+}
+
+using namespace w4a16;
+
+namespace {
+
+constexpr int kGroup = 128;
+constexpr int64_t kMaxM = (int64_t)1 << 21;  // keeps the row-block grid dimension < 65536
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptrs(std::initializer_list<const void*> required) {
+  for (const void* p : required) {
+    if (!p) return W4A16_ERR_INVALID_ARG;
+  }
+  for (const void* p : required) {
+    if (!aligned16(p)) return W4A16_ERR_MISALIGNED;
+  }
+  return W4A16_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+
+// ---- NF4 codebook, computed here from its closed form (independent of any
+// table elsewhere): Phi^-1 by Newton iteration on erfc in double precision.
+double norm_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+double norm_ppf(double p) {
+  double x = 0.0;
+  for (int it = 0; it < 100; ++it) {
+    const double pdf = std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+    const double dx = (norm_cdf(x) - p) / pdf;
+    x -= dx;
+    if (std::fabs(dx) <= 1e-17 * std::fmax(1.0, std::fabs(x))) break;
+  }
+  return x;
+}
+
+struct Codebook {
+  Nf4Table t;
+  Codebook() {
+    const double d = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
+    std::vector<double> v;
+    // equal probability steps from d down to 1/2 (the 1/2 end, level 0, dropped)
+    const double step9 = (0.5 - d) / 8.0, step8 = (0.5 - d) / 7.0;
+    for (int i = 0; i < 8; ++i) v.push_back(norm_ppf((double)i * step9 + d));
+    for (int i = 0; i < 7; ++i) v.push_back(-norm_ppf((double)i * step8 + d));
+    v.push_back(0.0);
+    std::sort(v.begin(), v.end());
+    const double top = norm_ppf(d);
+    for (int i = 0; i < 16; ++i) t.v[i] = (float)(v[i] / top);
+  }
+};
+
+const Nf4Table& codebook() {
+  static const Codebook cb;
+  return cb.t;
+}
+
+int validate_int4_shape(int64_t K, int64_t N, int32_t group_size) {
+  if (K <= 0 || N <= 0) return W4A16_ERR_INVALID_ARG;
+  if (group_size != kGroup) return W4A16_ERR_UNSUPPORTED;
+  if (K % kGroup != 0 || N % 8 != 0) return W4A16_ERR_INVALID_ARG;
+  if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30) return W4A16_ERR_UNSUPPORTED;
+  return W4A16_OK;
+}
+
+int validate_dtype(int32_t dtype) {
+  return (dtype == W4A16_F16 || dtype == W4A16_BF16) ? W4A16_OK : W4A16_ERR_INVALID_ARG;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(int status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_INVALID_ARG: return "invalid argument";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported configuration";
+    case W4A16_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case W4A16_ERR_BAD_GIDX: return "malformed g_idx (value out of range or group size != G)";
+    case W4A16_ERR_WORKSPACE: return "workspace smaller than required";
+    case W4A16_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int w4a16_version(void) { return 1; }
+
+int w4a16_tune(int32_t key, int64_t value) {
+  if (key == W4A16_TUNE_TARGET_WORKGROUPS) {
+    if (value < 0 || value > (1 << 20)) return W4A16_ERR_INVALID_ARG;
+    set_target_wgs((int)value);
+    return W4A16_OK;
+  }
+  return W4A16_ERR_INVALID_ARG;
+}
+
+int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which) {
+  if (validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
+  const int64_t NP = ceil_div(N, 64), KT = K / kGroup;
+  switch (which) {
+    case W4A16_CODES: return NP * KT * 4096;
+    case W4A16_SCALES: return NP * KT * 128;
+    case W4A16_ZEROS: return NP * KT * 32;
+    default: return -1;
+  }
+}
+
+int w4a16_make_perm(const int32_t* g_idx, int64_t K, int32_t group_size, int32_t* perm,
+                    int32_t* nontrivial_host, void* stream) {
+  if (!nontrivial_host) return W4A16_ERR_INVALID_ARG;
+  if (K <= 0 || group_size != kGroup) return group_size != kGroup ? W4A16_ERR_UNSUPPORTED
+                                                                  : W4A16_ERR_INVALID_ARG;
+  if (K % kGroup != 0) return W4A16_ERR_INVALID_ARG;
+  if (int s = check_ptrs({g_idx, perm})) return s;
+  hipStream_t st = (hipStream_t)stream;
+  std::vector<int32_t> g((size_t)K);
+  if (hipMemcpyAsync(g.data(), g_idx, (size_t)K * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return W4A16_ERR_HIP;
+  const int64_t ng = K / kGroup;
+  std::vector<int64_t> count((size_t)ng, 0);
+  bool trivial = true;
+  for (int64_t k = 0; k < K; ++k) {
+    if (g[k] < 0 || g[k] >= ng) return W4A16_ERR_BAD_GIDX;
+    ++count[g[k]];
+    if (g[k] != k / kGroup) trivial = false;
+  }
+  for (int64_t c : count)
+    if (c != kGroup) return W4A16_ERR_BAD_GIDX;
+  // stable counting sort: columns of group 0 in original order, then group 1, ...
+  std::vector<int32_t> p((size_t)K);
+  std::vector<int64_t> next((size_t)ng);
+  for (int64_t i = 0; i < ng; ++i) next[i] = i * kGroup;
+  for (int64_t k = 0; k < K; ++k) p[next[g[k]]++] = (int32_t)k;
+  if (hipMemcpyAsync(perm, p.data(), (size_t)K * 4, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return W4A16_ERR_HIP;
+  *nontrivial_host = trivial ? 0 : 1;
+  return W4A16_OK;
+}
+
+int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm, int64_t N,
+                       int64_t K, int32_t group_size, int32_t* qweight, uint16_t* scales,
+                       int32_t* qzeros, void* stream) {
+  if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if ((g_idx == nullptr) != (perm == nullptr)) return W4A16_ERR_INVALID_ARG;
+  if (int s = check_ptrs({W, qweight, scales, qzeros})) return s;
+  if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
+  return hip_status(launch_rtn_int4(W, perm, N, K, qweight, scales, qzeros, (hipStream_t)stream));
+}
+
+int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                 const int32_t* g_idx, int64_t K, int64_t N, int32_t group_size, void* codes_r,
+                 void* scales_r, void* zeros_r, int32_t* perm, int32_t* perm_used_host,
+                 void* stream) {
+  if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if (!perm_used_host) return W4A16_ERR_INVALID_ARG;
+  if (int s = check_ptrs({qweight, scales, qzeros, codes_r, scales_r, zeros_r})) return s;
+  int32_t used = 0;
+  if (g_idx) {
+    if (!perm) return W4A16_ERR_INVALID_ARG;
+    if (int s = w4a16_make_perm(g_idx, K, group_size, perm, &used, stream)) return s;
+  }
+  if (int s = hip_status(launch_repack(qweight, scales, qzeros, used ? perm : nullptr, K, N,
+                                       codes_r, scales_r, zeros_r, (hipStream_t)stream)))
+    return s;
+  *perm_used_host = used;
+  return W4A16_OK;
+}
+
+int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
+  if (M <= 0 || validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
+  return plan_int4(M, N, K, true).ws_bytes;
+}
+
+int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
+               const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
+               int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
+               void* stream) {
+  if (M <= 0 || M > kMaxM) return M <= 0 ? W4A16_ERR_INVALID_ARG : W4A16_ERR_UNSUPPORTED;
+  if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if (int s = validate_dtype(dtype)) return s;
+  if (int s = check_ptrs({x, codes_r, scales_r, zeros_r, out})) return s;
+  if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
+  if (workspace) {
+    if (!aligned16(workspace)) return W4A16_ERR_MISALIGNED;
+    if (workspace_bytes < plan_int4(M, N, K, true).ws_bytes) return W4A16_ERR_WORKSPACE;
+  }
+  return hip_status(launch_int4_gemm(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, dtype,
+                                     workspace, workspace_bytes, (hipStream_t)stream));
+}
+
+int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
+                  int64_t N, int32_t group_size, int32_t dtype, void* w_out, void* stream) {
+  if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if (int s = validate_dtype(dtype)) return s;
+  if (int s = check_ptrs({codes_r, scales_r, zeros_r, w_out})) return s;
+  return hip_status(
+      launch_dequant_int4(codes_r, scales_r, zeros_r, K, N, dtype, w_out, (hipStream_t)stream));
+}
+
+int nf4_codebook(float* out16_host) {
+  if (!out16_host) return W4A16_ERR_INVALID_ARG;
+  std::memcpy(out16_host, codebook().v, sizeof(float) * 16);
+  return W4A16_OK;
+}
+
+static int validate_nf4_shape(int64_t N, int64_t K, int32_t blocksize) {
+  if (N <= 0 || K <= 0) return W4A16_ERR_INVALID_ARG;
+  if (blocksize != 64) return W4A16_ERR_UNSUPPORTED;
+  if (K % 64 != 0) return W4A16_ERR_INVALID_ARG;
+  if (N > (int64_t)1 << 30 || K > (int64_t)1 << 30) return W4A16_ERR_UNSUPPORTED;
+  return W4A16_OK;
+}
+
+int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_t* qweight,
+                 uint8_t* absmax_q, float* absmax_scale, void* stream) {
+  if (int s = validate_nf4_shape(N, K, blocksize)) return s;
+  if (int s = check_ptrs({W, qweight, absmax_q, absmax_scale})) return s;
+  return hip_status(launch_nf4_quant(W, N, K, codebook(), qweight, absmax_q, absmax_scale,
+                                     (hipStream_t)stream));
+}
+
+int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize) {
+  if (M <= 0 || validate_nf4_shape(N, K, blocksize) != W4A16_OK) return -1;
+  return plan_nf4(M, N, K, true).ws_bytes;
+}
+
+int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
+             const float* absmax_scale, int32_t blocksize, void* out, int64_t M, int64_t N,
+             int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (M <= 0 || M > kMaxM) return M <= 0 ? W4A16_ERR_INVALID_ARG : W4A16_ERR_UNSUPPORTED;
+  if (int s = validate_nf4_shape(N, K, blocksize)) return s;
+  if (N % 16 != 0) return W4A16_ERR_INVALID_ARG;
+  if (int s = validate_dtype(dtype)) return s;
+  if (int s = check_ptrs({x, qweight, absmax_q, absmax_scale, out})) return s;
+  if (workspace) {
+    if (!aligned16(workspace)) return W4A16_ERR_MISALIGNED;
+    if (workspace_bytes < plan_nf4(M, N, K, true).ws_bytes) return W4A16_ERR_WORKSPACE;
+  }
+  return hip_status(launch_nf4_gemm(x, qweight, absmax_q, absmax_scale, codebook(), out, M, N, K,
+                                    dtype, workspace, workspace_bytes, (hipStream_t)stream));
+}
+
+int nf4_dequant(const uint8_t* qweight, const uint8_t* absmax_q, const float* absmax_scale,
+                int64_t N, int64_t K, int32_t blocksize, int32_t dtype, void* w_out,
+                void* stream) {
+  if (int s = validate_nf4_shape(N, K, blocksize)) return s;
+  if (int s = validate_dtype(dtype)) return s;
+  if (int s = check_ptrs({qweight, absmax_q, absmax_scale, w_out})) return s;
+  return hip_status(launch_dequant_nf4(qweight, absmax_q, absmax_scale, N, K, dtype, codebook(),
+                                       w_out, (hipStream_t)stream));
+}
+
+}  // extern "C"

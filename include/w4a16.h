@@ -1,0 +1,235 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) 4-bit weight-only GEMM library.
+ *
+ * Computes y = x * dequant(Wq)^T for fp16/bf16 activations x [M, K] and 4-bit
+ * weights Wq [N, K] (row = output channel) with fp32 accumulation, in two
+ * weight formats:
+ *
+ *   INT4  group-wise asymmetric: per (column, group of 128 along K) an fp16
+ *         scale and a 4-bit zero; optional act-order column map g_idx.
+ *   NF4   block-wise normal-float: per 64-element block an absmax that is
+ *         itself 8-bit quantized with one fp32 scale per 256 blocks.
+ *
+ * Sources (cited by page title and section):
+ *  [P1] "GPTQ、AWQ与Bitsandbytes：大模型量化三大技术路径深度对比" (tqpw.cn/news/80721)
+ *  [P2] "模型量化实践：GPTQ 与 AWQ 在生产环境的精度与速度权衡" (jsqmd.com/news/975148)
+ *  [P3] "LLM 量化技术详解：GPTQ、AWQ 与 GGUF 的选型与实践"
+ *       (cloud.tencent.com/developer/article/2726413)
+ *  [P4] "GPTQ与bitsandbytes对比：谁是2024年大模型量化的终极选择？"
+ *       (blog.csdn.net/gitblog_00436/article/details/141051550)
+ *  [P5] "LLM量化技术深度对比:GPTQ vs AWQ vs bitsandbytes 2026基准全解析"
+ *       (5ulink.com/archives/1952)
+ *
+ * Conventions for every entry point
+ *  - Pointers named *_host are host memory; every other pointer is device
+ *    memory owned by the caller.  The library never allocates or frees caller
+ *    memory and never calls hipMalloc/hipFree.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Launches are asynchronous on it unless the entry point says it blocks.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    non-zero status means nothing was launched.  Device-side faults surface
+ *    at the caller's next stream synchronization, not in the return value.
+ *    Nothing throws or aborts across the ABI.
+ *  - All device pointers must be 16-byte aligned (W4A16_ERR_MISALIGNED).
+ *  - 16-bit floats are passed as their bit patterns (uint16_t / void*).
+ *  - Rounding: every conversion to fp16/bf16 is round-to-nearest-even;
+ *    subnormals are kept (no flush to zero).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_INVALID_ARG = 1,   /* bad size, NULL required pointer, unknown dtype */
+  W4A16_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement   */
+  W4A16_ERR_MISALIGNED = 3,    /* a device pointer is not 16-byte aligned        */
+  W4A16_ERR_BAD_GIDX = 4,      /* g_idx out of range or a group not of size G     */
+  W4A16_ERR_WORKSPACE = 5,     /* workspace given but smaller than required       */
+  W4A16_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed      */
+} w4a16_status_t;
+
+typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype_t;
+
+/* Which array w4a16_repacked_bytes sizes. */
+typedef enum { W4A16_CODES = 0, W4A16_SCALES = 1, W4A16_ZEROS = 2 } w4a16_array_t;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* w4a16_status_string(int status);
+
+/* ABI version; bumped on any incompatible change. */
+int w4a16_version(void);
+
+/*
+ * Process-wide tuning knob for later calls (not thread-safe against
+ * concurrent GEMM calls).  W4A16_TUNE_TARGET_WORKGROUPS: number of workgroups
+ * the split-K planner aims for (default 512; 0 restores the default).  It
+ * changes only how K is split, never the result beyond fp32 summation order.
+ */
+enum { W4A16_TUNE_TARGET_WORKGROUPS = 0 };
+int w4a16_tune(int32_t key, int64_t value);
+
+/* ------------------------------------------------------------------ INT4 --- */
+
+/*
+ * Bytes of one array of the repacked INT4 layout for a [N, K] weight.
+ * Group size must be 128; K % 128 == 0; N % 8 == 0.  Returns -1 on bad input.
+ *
+ * Repacked layout (KT = K/128 groups, NP = ceil(N/64) panels of 64 columns):
+ *   codes  uint8 [NP][KT][4][64][16]: output column n = 64p + 16c + i and
+ *          (permuted) input column k = 128t + 32j + 8b + e are stored in lane
+ *          l = i + 16b, 32-bit little-endian word j of that lane's 16 bytes,
+ *          nibble slot (e >> 1) + 4*(e & 1).  Padding columns are zero.
+ *   scales fp16  [NP][KT][16][4]: entry [p][t][i][c] = scale(64p+16c+i, t).
+ *   zeros  uint16 [NP][KT][16]: bits [4c, 4c+4) = zero(64p+16c+i, t).
+ */
+int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which);
+
+/*
+ * Canonical act-order permutation from a group map ([P2] §三 3.1 desc_act;
+ * [P4] "技术原理" --act-order): perm = stable argsort(g_idx), so permuted
+ * column k' is original column perm[k'] and each run of G permuted columns is
+ * one whole group.
+ *   g_idx      int32 [K] device: group of each original input column.
+ *   perm       int32 [K] device, written.
+ *   nontrivial_host  int32 host, written: 0 if g_idx == k/G for all k.
+ * Validates that every value is in [0, K/G) and every group has exactly G
+ * members (W4A16_ERR_BAD_GIDX otherwise).  BLOCKS: copies g_idx to the host
+ * and synchronizes `stream`.
+ */
+int w4a16_make_perm(const int32_t* g_idx, int64_t K, int32_t group_size, int32_t* perm,
+                    int32_t* nontrivial_host, void* stream);
+
+/*
+ * Round-to-nearest group quantizer ([P4] "技术原理": RTN is the baseline GPTQ
+ * improves on; [P3] §2.1 asymmetric with a zero point; [P3] §2.2 group-wise).
+ * Per output row n and group g (the columns {perm[gG .. gG+G-1]} when perm is
+ * given, else G consecutive columns):
+ *   s = fp16(fp32(max - min) / 15)  (s = 1 if that rounds to 0);
+ *   z = clip(rint(-min / s), 0, 15);  q = clip(rint(w / s) + z, 0, 15),
+ * all decisions in fp32, rint = half to even.
+ *   W        fp32 [N, K] device (finite values).
+ *   g_idx    int32 [K] or NULL; perm int32 [K] (from w4a16_make_perm) iff g_idx.
+ *   qweight  int32 [K/8, N]: bits [4j,4j+4) of (i, n) = q(n, 8i+j), original order.
+ *   scales   fp16 [K/G, N];  qzeros int32 [K/G, N/8]: bits [4j,4j+4) of
+ *            (g, i) = z(g, 8i+j).
+ * Constraints: G == 128, K % G == 0, N % 8 == 0.
+ */
+int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm,
+                       int64_t N, int64_t K, int32_t group_size, int32_t* qweight,
+                       uint16_t* scales, int32_t* qzeros, void* stream);
+
+/*
+ * Offline repack of canonical GPTQ-style tensors into the tile layout above
+ * (pay the layout translation once, not per call: [P5] "关键数据解读" item 4).
+ *   qweight int32 [K/8, N]; scales fp16 [K/G, N]; qzeros int32 [K/G, N/8].
+ *   g_idx   int32 [K] or NULL.  When given, `perm` (int32 [K], required then)
+ *           receives w4a16_make_perm's permutation (the identity for the
+ *           trivial k/G map).  If g_idx is non-trivial the codes are stored in
+ *           perm order and *perm_used_host is set to 1: pass `perm` to
+ *           w4a16_gemm.  Otherwise *perm_used_host = 0: pass NULL.
+ *   codes_r / scales_r / zeros_r: sized by w4a16_repacked_bytes.
+ * BLOCKS when g_idx is non-NULL (host validation of g_idx); otherwise async.
+ */
+int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                 const int32_t* g_idx, int64_t K, int64_t N, int32_t group_size,
+                 void* codes_r, void* scales_r, void* zeros_r, int32_t* perm,
+                 int32_t* perm_used_host, void* stream);
+
+/*
+ * Workspace bytes w4a16_gemm may use for split-K partial sums at this shape
+ * (0 if it needs none).  The workspace must be zero-filled once when it is
+ * allocated; every completed call leaves it in that state again, so it can be
+ * reused by later calls on the same stream.  Calls that overlap in time must
+ * not share a workspace.
+ */
+int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/*
+ * Fused dequantize-and-multiply, the method of [P5] "关键数据解读" item 1
+ * (weights are never written back as 16-bit values):
+ *   y[m, n] = sum_k x[m, perm[k]] * w[n, k],
+ *   w[n, k] = round_dtype(fp32(q - z) * fp32(s))  (q, z, s of column n, group k/128),
+ * with fp32 accumulation and one round-to-nearest-even to the output dtype.
+ *   x      [M, K] row-major, dtype;  out [M, N] row-major, dtype.
+ *   perm   int32 [K] from w4a16_repack (or NULL for identity).
+ *   codes_r, scales_r, zeros_r from w4a16_repack.
+ *   dtype  W4A16_F16 or W4A16_BF16 (activations and output).
+ *   workspace / workspace_bytes: optional split-K workspace (see above); NULL
+ *          forces a single pass over K per output tile (correct, may be slower).
+ * Constraints: M >= 1, K % 128 == 0, N % 8 == 0, group_size == 128.
+ * Async on `stream`.  Results are bitwise reproducible run to run.
+ */
+int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
+               const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
+               int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
+               void* stream);
+
+/*
+ * Test/debug export: the dequantized weight matrix w [N, K] (dtype), in the
+ * permuted column order of the repacked codes, computed by the same device
+ * routine the GEMM uses.  Async on `stream`.
+ */
+int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
+                  int64_t N, int32_t group_size, int32_t dtype, void* w_out, void* stream);
+
+/* ------------------------------------------------------------------- NF4 --- */
+
+/*
+ * The library's 16 NF4 levels as fp32 (ascending; L[0] = -1, L[7] = 0,
+ * L[15] = 1): normal quantiles at 8 equal steps from 1/2 to delta on the
+ * positive side and 7 on the negative side, divided by the largest, with
+ * delta = ((1 - 1/30) + (1 - 1/32)) / 2 ([P1] §2.3 and §3.3: levels at
+ * quantiles of N(0,1); [P5] "关键数据解读" item 2: levels crowd near zero).
+ *   out16_host  float[16] host, written.
+ */
+int nf4_codebook(float* out16_host);
+
+/*
+ * On-device NF4 block quantizer with double quantization (calibration-free,
+ * done at load time: [P5] "2026 年选型建议" item 4; [P4] "技术原理"):
+ *   per block b of `blocksize` consecutive elements of row-major W:
+ *   absmax_b = max|w|;  code = argmin_i |w/absmax_b - L_i| (fp32, ties to the
+ *   lower index; an all-zero block gives code 7);
+ *   per group of 256 consecutive blocks: absmax_scale = fp32(max absmax / 255),
+ *   absmax_q = clip(rint(absmax / absmax_scale), 0, 255) (0 if the scale is 0).
+ *   W            fp32 [N, K] device (finite values).
+ *   qweight      uint8 [N, K/2]: element 2j in the low nibble of byte j.
+ *   absmax_q     uint8 [N*K/blocksize];  absmax_scale fp32 [ceil(N*K/blocksize/256)].
+ * Constraints: blocksize == 64, K % 64 == 0.
+ */
+int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_t* qweight,
+                 uint8_t* absmax_q, float* absmax_scale, void* stream);
+
+/* Workspace bytes nf4_gemm may use at this shape (same contract as above). */
+int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
+
+/*
+ * Fused NF4 dequantize-and-multiply (bitsandbytes' 4-bit format, dequantized
+ * on every forward in its own kernels: [P5] "关键数据解读" item 2; here fused):
+ *   y[m, n] = sum_k x[m, k] * w[n, k],
+ *   w[n, k] = round_dtype(fp32(L[c] * a')),  a' = fp32(fp32(absmax_q[b]) *
+ *   absmax_scale[b / 256]),  b = (n*K + k) / blocksize.
+ *   x [M, K] and out [M, N] row-major in dtype; qweight/absmax as nf4_quantize.
+ * Constraints: M >= 1, blocksize == 64, K % 64 == 0, N % 16 == 0.  Async.
+ */
+int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
+             const float* absmax_scale, int32_t blocksize, void* out, int64_t M, int64_t N,
+             int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Test/debug export: dequantized NF4 weights w [N, K] in dtype.  Async. */
+int nf4_dequant(const uint8_t* qweight, const uint8_t* absmax_q, const float* absmax_scale,
+                int64_t N, int64_t K, int32_t blocksize, int32_t dtype, void* w_out,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -123,8 +123,15 @@ def dequant_int4(qweight, scales, qzeros, g_idx=None, group_size=128, dtype="f16
     w[n, k] = round_dtype(fp32(q[n,k] - z[g,n]) * fp32(s[g,n])), g = g_idx[k].
     """
     q = unpack_qweight(qweight)
+    return dequant_codes(q, scales, unpack_qzeros(qzeros)[:, :q.shape[0]], g_idx, group_size,
+                         dtype)
+
+
+def dequant_codes(q, scales, zeros, g_idx=None, group_size=128, dtype="f16"):
+    """Same definition on unpacked codes q [N, K], scales [K/G, N], zeros [K/G, N]."""
+    q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
-    z = unpack_qzeros(qzeros)[:, :N]
+    z = np.asarray(zeros, dtype=np.uint8)
     s = np.asarray(scales, dtype=np.float16)
     gi = default_g_idx(K, group_size) if g_idx is None else np.asarray(g_idx, dtype=np.int64)
     zk = z[gi, :].T.astype(np.float32)                    # [N, K]

@@ -1,0 +1,104 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, validates arguments before touching the GPU, and its own NF4
+codebook equals the oracle's.  No kernel is launched here."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_weight_only_gemm_amd import _lib
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+if not os.path.exists(_lib.LIB_PATH):
+    pytest.skip("libw4a16.so not built", allow_module_level=True)
+
+L = _lib.load()
+NULL = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10008)         # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_what_binding_binds():
+    assert declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported():
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    assert L.w4a16_version() == 1
+    for s in range(7):
+        assert L.w4a16_status_string(s)
+    assert L.w4a16_status_string(99) == b"unknown status"
+
+
+def test_repacked_bytes():
+    assert L.w4a16_repacked_bytes(4096, 4096, 128, 0) == 4096 * 4096 // 2
+    assert L.w4a16_repacked_bytes(4096, 4096, 128, 1) == 32 * 4096 * 2
+    assert L.w4a16_repacked_bytes(4096, 4096, 128, 2) == 32 * 4096 // 2
+    assert L.w4a16_repacked_bytes(512, 200, 128, 0) == 4 * 4 * 4096   # N padded to 256
+    assert L.w4a16_repacked_bytes(500, 256, 128, 0) == -1             # K % 128
+    assert L.w4a16_repacked_bytes(512, 20, 128, 0) == -1              # N % 8
+    assert L.w4a16_repacked_bytes(512, 256, 64, 0) == -1              # G != 128
+
+
+def test_gemm_validation_without_gpu():
+    g = L.w4a16_gemm
+    # M <= 0
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 0, 256, 512, 0, NULL, 0, NULL) == 1
+    # K not a multiple of the group size
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 500, 0, NULL, 0, NULL) == 1
+    # unsupported group size
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 64, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 2
+    # unknown dtype
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 512, 7, NULL, 0, NULL) == 1
+    # NULL required pointer
+    assert g(NULL, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 1
+    # misaligned pointer
+    assert g(ODD, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 3
+    # workspace too small
+    need = L.w4a16_workspace_bytes(1, 4096, 4096, 128)
+    assert need > 0
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 4096, 4096, 0, FAKE, need - 16, NULL) == 5
+
+
+def test_nf4_validation_without_gpu():
+    g = L.nf4_gemm
+    assert g(FAKE, FAKE, FAKE, FAKE, 32, FAKE, 1, 256, 512, 1, NULL, 0, NULL) == 2   # blocksize
+    assert g(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 1, 256, 96, 1, NULL, 0, NULL) == 1    # K % 64
+    assert g(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 1, 250, 512, 1, NULL, 0, NULL) == 1   # N % 16
+    assert g(FAKE, NULL, FAKE, FAKE, 64, FAKE, 1, 256, 512, 1, NULL, 0, NULL) == 1
+    assert L.nf4_quantize(FAKE, 16, 100, 64, FAKE, FAKE, FAKE, NULL) == 1
+    assert L.nf4_workspace_bytes(1, 28672, 8192, 64) >= 0
+
+
+def test_quantize_and_repack_validation_without_gpu():
+    used = ctypes.c_int32(0)
+    # g_idx given without a perm buffer
+    assert L.w4a16_repack(FAKE, FAKE, FAKE, FAKE, 512, 256, 128, FAKE, FAKE, FAKE, NULL,
+                          ctypes.byref(used), NULL) == 1
+    # quantize: g_idx without perm
+    assert L.w4a16_quantize_rtn(FAKE, FAKE, NULL, 256, 512, 128, FAKE, FAKE, FAKE, NULL) == 1
+    assert L.w4a16_tune(0, -1) == 1 and L.w4a16_tune(5, 1) == 1
+
+
+def test_library_codebook_equals_oracle_codebook():
+    buf = (ctypes.c_float * 16)()
+    assert L.nf4_codebook(ctypes.cast(buf, ctypes.c_void_p)) == 0
+    got = np.frombuffer(buf, dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), nf4.nf4_codebook().view(np.uint32))

@@ -1,0 +1,176 @@
+"""GPU parity of the INT4 path against the oracle: quantizer, repack and dequant
+bit-exact; GEMM within max|y - y_ref| / max|y_ref| <= 5e-3."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_gemm_amd as w4
+from bit_weight_only_gemm_amd import synth
+from oracle import int4, repack, gemm
+from gpu_util import (DEV, say, bits_to_tensor, tensor_bits, tensor_f64, int4_inputs,
+                      gpu_int4_pack, oracle_int4_rows, compare_gemm)
+
+pytestmark = pytest.mark.gpu
+TOL = gemm.TOL
+
+
+@pytest.mark.parametrize("N,K,act", [(512, 512, False), (200, 384, False), (256, 1024, True),
+                                     (72, 256, True)])
+def test_quantizer_bit_exact(N, K, act):
+    say("quantizer", N, K, act)
+    W, gi, _ = int4_inputs("gpu/quant/%d/%d" % (N, K), N, K, act_order=act)
+    (qw, sc, qz), _ = gpu_int4_pack(W, gi)
+    q, s, z = int4.quantize_rtn_int4(W, 128, gi)
+    assert np.array_equal(qw.cpu().numpy(), int4.pack_qweight(q))
+    assert np.array_equal(tensor_bits(sc), s.view(np.uint16))
+    assert np.array_equal(qz.cpu().numpy(), int4.pack_qzeros(z))
+
+
+@pytest.mark.parametrize("N,K,act", [(512, 512, False), (200, 384, True), (1024, 256, True)])
+def test_repack_bytes_equal_reference(N, K, act):
+    say("repack", N, K, act)
+    W, gi, _ = int4_inputs("gpu/repack/%d/%d" % (N, K), N, K, act_order=act)
+    (qw, sc, qz), packed = gpu_int4_pack(W, gi)
+    ref = repack.repack_ref(qw.cpu().numpy(), sc.cpu().numpy(), qz.cpu().numpy(), gi)
+    assert np.array_equal(packed["codes"].cpu().numpy(), ref[0])
+    assert np.array_equal(tensor_bits(packed["scales"]), ref[1].view(np.uint16))
+    assert np.array_equal(packed["zeros"].cpu().numpy().view(np.uint16), ref[2])
+    if ref[3] is None:
+        assert packed["perm"] is None
+    else:
+        assert np.array_equal(packed["perm"].cpu().numpy(), ref[3])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("act", [False, True])
+def test_dequant_bit_exact(dtype, act):
+    N, K = 264, 512
+    say("dequant", dtype, act)
+    W, gi, _ = int4_inputs("gpu/deq/%s" % dtype, N, K, act_order=act)
+    _, packed = gpu_int4_pack(W, gi)
+    got = tensor_bits(w4.w4a16_dequant(packed, torch.float16 if dtype == "f16" else torch.bfloat16))
+    want = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    perm = repack.canonical_perm(gi, K)
+    if perm is not None:
+        want = want[:, perm]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_dequant_special_scales_bit_exact(dtype):
+    # all 256 (q, z) pairs against powers of two, fp16 subnormals, large scales
+    N, K = 64, 16 * 128
+    r = np.random.default_rng(11)
+    q = np.tile(np.arange(16, dtype=np.uint8), (N, K // 16))
+    z = (np.arange(K // 128)[:, None] + np.arange(N)[None, :]) % 16
+    svals = np.array([2.0**-24, 3 * 2.0**-24, 2.0**-15, 0.5, 1.0, 3.0, 1024.0, 4095.0,
+                      60000.0, 2.0**-14, 1e-3, 0.0071, 7.0e-5, 2.0, 0.25, 65504.0], np.float16)
+    s = svals[(np.arange(K // 128)[:, None] * 7 + np.arange(N)[None, :]) % 16]
+    s = np.where(r.random(s.shape) < 0.2, -s, s).astype(np.float16)
+    qw = torch.from_numpy(int4.pack_qweight(q)).to(DEV)
+    sc = torch.from_numpy(s.view(np.int16)).view(torch.float16).to(DEV)
+    qz = torch.from_numpy(int4.pack_qzeros(z.astype(np.uint8))).to(DEV)
+    packed = w4.w4a16_repack(qw, sc, qz)
+    got = tensor_bits(w4.w4a16_dequant(packed, torch.float16 if dtype == "f16" else torch.bfloat16))
+    want = int4.dequant_int4(int4.pack_qweight(q), s, int4.pack_qzeros(z.astype(np.uint8)), None,
+                             128, dtype)
+    assert np.array_equal(got, want)
+
+
+def _run_gemm(tag, M, N, K, dtype, act=False, awq=False, use_ws=True, xscale=1.0):
+    W, gi, s = int4_inputs(tag, N, K, act_order=act, awq=awq)
+    x32 = synth.activations(tag + "/x", M, K) * np.float32(xscale)
+    if awq:
+        x32 = (x32 / s[None, :]).astype(np.float32)
+    xb = synth.to_bits(x32, dtype)
+    _, packed = gpu_int4_pack(W, gi)
+    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed, use_workspace=use_ws)
+    torch.cuda.synchronize()
+    return y, xb, W, gi, packed
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 130])
+def test_gemm_m_sweep_f16(M):
+    N, K = 200, 512                         # ragged N: one zero-padded panel
+    say("gemm f16 M", M)
+    y, xb, W, gi, _ = _run_gemm("gpu/gemm/msweep/%d" % M, M, N, K, "f16")
+    wd = oracle_int4_rows(W, gi, np.arange(N), "f16")
+    assert compare_gemm(y, xb, wd, "f16") <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 16, 33, 64, 100])
+@pytest.mark.parametrize("act", [False, True])
+def test_gemm_bf16_and_act_order(M, act):
+    N, K = 256, 1024
+    say("gemm bf16 M", M, "act", act)
+    y, xb, W, gi, _ = _run_gemm("gpu/gemm/bf16/%d/%d" % (M, act), M, N, K, "bf16", act=act)
+    wd = oracle_int4_rows(W, gi, np.arange(N), "bf16")
+    assert compare_gemm(y, xb, wd, "bf16") <= TOL
+
+
+def test_gemm_config1_tiny():
+    # x fp16 [16, 512] ~ N(0,1); W [512, 512] ~ N(0, 0.02) RTN G=128; y fp16
+    say("config 1 tiny")
+    y, xb, W, gi, _ = _run_gemm("C1", 16, 512, 512, "f16")
+    wd = oracle_int4_rows(W, gi, np.arange(512), "f16")
+    err = compare_gemm(y, xb, wd, "f16")
+    say("config 1 rel err", err)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("use_ws", [True, False])
+def test_gemm_split_and_unsplit_agree_with_oracle(use_ws):
+    M, N, K = 4, 1024, 4096
+    say("split-K", use_ws)
+    y, xb, W, gi, _ = _run_gemm("gpu/gemm/split", M, N, K, "f16", act=True, use_ws=use_ws)
+    rows = np.arange(0, N, 7)
+    wd = oracle_int4_rows(W, gi, rows, "f16")
+    assert compare_gemm(y, xb, wd, "f16", cols=rows) <= TOL
+
+
+def test_gemm_deterministic_and_scaling_exact():
+    M, N, K = 16, 512, 2048
+    say("determinism")
+    W, gi, _ = int4_inputs("gpu/gemm/det", N, K, act_order=True)
+    x32 = synth.activations("gpu/gemm/det/x", M, K)
+    xb = synth.to_f16_bits(x32)
+    # exact doubling of the fp16 inputs (doubling before rounding would differ
+    # for fp16-subnormal inputs)
+    x2b = synth.to_f16_bits(2 * xb.view(np.float16).astype(np.float32))
+    _, packed = gpu_int4_pack(W, gi)
+    y1 = tensor_bits(w4.w4a16_gemm(bits_to_tensor(xb, "f16"), packed))
+    y2 = tensor_bits(w4.w4a16_gemm(bits_to_tensor(xb, "f16"), packed))
+    assert np.array_equal(y1, y2)
+    y3 = w4.w4a16_gemm(bits_to_tensor(x2b, "f16"), packed).float().cpu().numpy()
+    y1f = y1.view(np.float16).astype(np.float32)
+    assert np.array_equal(y3, 2 * y1f)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gemm_onehot_reads_dequantized_weight_exactly(dtype):
+    N, K = 128, 512
+    say("onehot", dtype)
+    W, gi, _ = int4_inputs("gpu/onehot", N, K, act_order=True)
+    _, packed = gpu_int4_pack(W, gi)
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    ks = [0, 1, 127, 128, 300, 511]
+    x = np.zeros((len(ks), K), dtype=np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, dtype), dtype), packed))
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r], wd[:, k]), k
+
+
+def test_gemm_q_equals_z_gives_zero():
+    M, N, K = 5, 128, 256
+    z = np.random.default_rng(12).integers(0, 16, size=(K // 128, N)).astype(np.uint8)
+    q = z[np.arange(K) // 128].T.copy()
+    s = np.full((K // 128, N), 0.01, dtype=np.float16)
+    packed = w4.w4a16_repack(torch.from_numpy(int4.pack_qweight(q)).to(DEV),
+                             torch.from_numpy(s.view(np.int16)).view(torch.float16).to(DEV),
+                             torch.from_numpy(int4.pack_qzeros(z)).to(DEV))
+    x = bits_to_tensor(synth.to_f16_bits(synth.activations("gpu/qz/x", M, K)), "f16")
+    y = w4.w4a16_gemm(x, packed)
+    assert not torch.any(y.view(torch.int16) & 0x7FFF)

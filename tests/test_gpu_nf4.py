@@ -1,0 +1,76 @@
+"""GPU parity of the NF4 path: on-device quantizer and dequant bit-exact vs the
+oracle; fused GEMM within the 5e-3 relative bar."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_gemm_amd as w4
+from bit_weight_only_gemm_amd import synth
+from oracle import nf4, gemm
+from gpu_util import DEV, say, bits_to_tensor, tensor_bits, compare_gemm
+
+pytestmark = pytest.mark.gpu
+TOL = gemm.TOL
+
+
+def _pack(W):
+    return w4.nf4_quantize(torch.from_numpy(W).to(DEV), 64)
+
+
+@pytest.mark.parametrize("N,K", [(64, 512), (48, 192), (512, 1024)])
+def test_nf4_quantizer_bit_exact(N, K):
+    say("nf4 quant", N, K)
+    W = synth.weights("gpu/nf4q/%d/%d" % (N, K), N, K)
+    W[1, :64] = 0.0                                   # an all-zero block
+    p = _pack(W)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    assert np.array_equal(p["qweight"].cpu().numpy(), nf4.pack_nf4(codes))
+    assert np.array_equal(p["absmax_q"].cpu().numpy(), aq)
+    assert np.array_equal(p["absmax_scale"].cpu().numpy().view(np.uint32), sc.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nf4_dequant_bit_exact(dtype):
+    N, K = 96, 1024
+    say("nf4 dequant", dtype)
+    W = synth.weights("gpu/nf4d", N, K)
+    p = _pack(W)
+    got = tensor_bits(w4.nf4_dequant(p, torch.bfloat16 if dtype == "bf16" else torch.float16))
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    want = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("M", [1, 2, 16, 17, 32, 33, 64, 70])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nf4_gemm(M, dtype):
+    N, K = 208, 1088                          # ragged: N % 64 != 0, K % 128 == 64
+    say("nf4 gemm", M, dtype)
+    W = synth.weights("gpu/nf4g/W", N, K)
+    x32 = synth.activations("gpu/nf4g/x/%d" % M, M, K)
+    xb = synth.to_bits(x32, dtype)
+    p = _pack(W)
+    y = w4.nf4_gemm(bits_to_tensor(xb, dtype), p)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)
+    assert compare_gemm(y, xb, wd, dtype) <= TOL
+
+
+def test_nf4_gemm_onehot_exact():
+    N, K = 64, 512
+    W = synth.weights("gpu/nf4/onehot", N, K)
+    p = _pack(W)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, "bf16")
+    ks = [0, 5, 63, 64, 200, 511]
+    x = np.zeros((len(ks), K), dtype=np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    y = tensor_bits(w4.nf4_gemm(bits_to_tensor(synth.to_bf16_bits(x), "bf16"), p))
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r], wd[:, k]), k
