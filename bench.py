@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused 4-bit weight-only GEMM on one MI355X.
+
+Workload (one "step" = one pass of the whole decode hot path over one batch):
+Llama-2-7B-shaped decode layers in GPTQ layout with act-order -- (K, N) in
+{(4096, 4096), (4096, 11008), (11008, 4096)} at M in {1, 4, 16} tokens, group
+size 128, fp16 activations ~ N(0, 1), W ~ N(0, 0.02) RTN-quantized on the
+device.  Each (shape, M) pair is its own layer with its own weights, and R
+rotating copies of the weight set (>= 512 MB in total, twice the 256 MB
+Infinity Cache) make every step stream its weights from HBM.  Inputs are
+resident in HBM before timing starts.
+
+Printed: ONE JSON line with the weight-stream GB/s of the step (value), the
+effective TFLOP/s, the roofline of the dominant kernel (HIP-event durations of
+every GEMM launch in the timed region), and the CPU oracle timed on a bounded
+sample on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
+SHAPES = [(4096, 4096), (4096, 11008), (11008, 4096)]   # (K, N)
+MS = [1, 4, 16]
+G = 128
+
+
+def weight_bytes(K, N, perm=True):
+    return K * N // 2 + 2 * N * K // G + N * K // (2 * G) + (4 * K if perm else 0)
+
+
+def call_bytes(M, K, N):
+    """Algorithmic bytes of the GEMM kernel itself: codes + scales + zeros, the
+    (permuted) activations and the output.  The permutation vector is read by
+    the separate act-order gather kernel."""
+    return weight_bytes(K, N, perm=False) + 2 * M * K + 2 * M * N
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-rotation-mb", type=float, default=512.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_weight_only_gemm_amd as w4
+    from bit_weight_only_gemm_amd import synth, _lib
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = _lib.load()
+    stream = torch.cuda.Stream()          # graphs are captured on a non-default stream
+    torch.cuda.set_stream(stream)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    # ---- inputs: weights quantized + repacked on the device, x per M
+    base = {}
+    for K, N in SHAPES:
+        W = torch.from_numpy(synth.weights("C2/W/%dx%d" % (K, N), N, K)).to(dev)
+        gi = torch.from_numpy(synth.act_order_gidx("C2/gidx/%dx%d" % (K, N), K, G)).to(dev)
+        qw, sc, qz = w4.w4a16_quantize_rtn(W, G, g_idx=gi)
+        base[(K, N)] = w4.w4a16_repack(qw, sc, qz, gi)
+        del W, qw, sc, qz
+    set_bytes = sum(weight_bytes(K, N) for K, N in SHAPES) * len(MS)
+    R = max(1, int(np.ceil(args.min_rotation_mb * 1e6 / set_bytes)))
+    rot = []
+    for r in range(R):
+        step_layers = []
+        for K, N in SHAPES:
+            p = base[(K, N)]
+            for M in MS:
+                q = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in p.items()}
+                step_layers.append((K, N, M, q))
+        rot.append(step_layers)
+    xs = {}
+    outs = {}
+    for K, N in SHAPES:
+        for M in MS:
+            xb = synth.to_f16_bits(synth.activations("C2/x/%dx%d" % (M, K), M, K))
+            xs[(M, K)] = torch.from_numpy(xb.view(np.int16)).view(torch.float16).to(dev)
+            outs[(M, N, K)] = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ws_need = max(w4.w4a16_workspace_bytes(M, N, K) for K, N in SHAPES for M in MS)
+    ws = w4.workspace(ws_need, dev)
+    ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+    ws_len = ws.numel() * 4 if ws is not None else 0
+
+    # pre-bound C calls (argument marshalling done once)
+    calls = []
+    for step_layers in rot:
+        cl = []
+        for K, N, M, q in step_layers:
+            a = (ctypes.c_void_p(xs[(M, K)].data_ptr()), ctypes.c_void_p(q["codes"].data_ptr()),
+                 ctypes.c_void_p(q["scales"].data_ptr()), ctypes.c_void_p(q["zeros"].data_ptr()),
+                 ctypes.c_void_p(q["perm"].data_ptr()), G,
+                 ctypes.c_void_p(outs[(M, N, K)].data_ptr()), M, N, K, w4.F16, ws_ptr, ws_len,
+                 sptr)
+            cl.append((a, call_bytes(M, K, N), 2 * M * N * K, weight_bytes(K, N)))
+        calls.append(cl)
+    torch.cuda.synchronize()
+
+    def run_step(i):
+        for a, _, _, _ in calls[i % R]:
+            st = L.w4a16_gemm(*a)
+            if st != 0:
+                raise RuntimeError("w4a16_gemm status %d" % st)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    # ---- one HIP graph per weight-rotation set: a step is one graph replay
+    # (the 9 GEMM calls with their act-order permutation kernels), so host
+    # launch overhead is out of the measured step.
+    graphs = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            run_step(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(max(args.warmup, R)):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region, part 1: K steps (graph replays), synchronized both sides
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+
+    # ---- timed region, part 2: the same K steps launched eagerly with HIP
+    # timing events attached to every GEMM kernel's own dispatch
+    # (hipExtLaunchKernel start/stop), on the stream the kernels run on.
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    nper = len(calls[0])
+    nev = args.steps * nper
+    ev = (ctypes.c_void_p * (2 * nev))()
+    for k in range(2 * nev):
+        if hip.hipEventCreate(ctypes.byref(ev, k * ctypes.sizeof(ctypes.c_void_p))) != 0:
+            raise RuntimeError("hipEventCreate failed")
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for j, (a, _, _, _) in enumerate(calls[i % R]):
+            k = i * nper + j
+            L.w4a16_set_timing_events(ctypes.c_void_p(ev[2 * k]), ctypes.c_void_p(ev[2 * k + 1]))
+            if L.w4a16_gemm(*a) != 0:
+                raise RuntimeError("w4a16_gemm failed")
+    torch.cuda.synchronize()
+    ms = ctypes.c_float(0.0)
+    dur = np.zeros((args.steps, nper))
+    for i in range(args.steps):
+        for j in range(nper):
+            k = i * nper + j
+            if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[2 * k]),
+                                       ctypes.c_void_p(ev[2 * k + 1])) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            dur[i, j] = ms.value * 1e-3
+    for k in range(2 * nev):
+        hip.hipEventDestroy(ctypes.c_void_p(ev[k]))
+
+    step_wbytes = sum(c[3] for c in calls[0])
+    step_flops = sum(c[2] for c in calls[0])
+    step_bytes = sum(c[1] for c in calls[0])
+    avg_launch_s = float(dur.mean())
+    achieved = step_bytes / nper / avg_launch_s / 1e9
+    per_point = []
+    for j, (K, N, M, _) in enumerate(rot[0]):
+        d = float(dur[:, j].mean())
+        per_point.append({"M": M, "K": K, "N": N, "us": round(d * 1e6, 2),
+                          "weight_GBps": round(weight_bytes(K, N) / d / 1e9, 1),
+                          "pct_hbm": round(100 * call_bytes(M, K, N) / d / 1e9 / HBM_PEAK_GBS, 1)})
+
+    props = torch.cuda.get_device_properties(dev)
+    result = {
+        "metric": "W4A16 GEMM TFLOP/s + weight GB/s (% of HBM/MFMA peak), M=1..16 and M=2048",
+        "value": round(step_wbytes / step_s / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,0.02) weights RTN-quantized on device, N(0,1) activations)",
+        "config": {
+            "workload": "Llama-2-7B-shaped decode GEMMs, GPTQ act-order int4 G=128: "
+                        "(K,N) in {(4096,4096),(4096,11008),(11008,4096)} x M in {1,4,16}",
+            "gemm_calls_per_step": nper,
+            "step_timing": "HIP graph replay per step (GEMM + act-order permutation kernels)",
+            "weight_rotation_copies": R,
+            "tflops": round(step_flops / step_s / 1e12, 3),
+            "pct_hbm_step": round(100 * step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 1),
+            "gpu": props.name,
+            "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "int4_decode_kernel<f16, MT=1>",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "timing": "hipExtLaunchKernel start/stop events on every GEMM kernel of K eager steps",
+            "algorithmic_bytes_per_launch": round(step_bytes / nper),
+        },
+        "points": per_point,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(calls, rot, xs, outs)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(calls, rot, xs, outs):
+    """The oracle, as it stands, on one whole step (all 9 calls) of the same
+    workload: unpack + dequant + fp64 product per call, on this host."""
+    import torch
+    from bit_weight_only_gemm_amd import synth
+    from oracle import int4, gemm, fp
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    packed = {}
+    for K, N in SHAPES:           # oracle inputs from the oracle's own quantizer (untimed)
+        W = synth.weights("C2/W/%dx%d" % (K, N), N, K)
+        gi = synth.act_order_gidx("C2/gidx/%dx%d" % (K, N), K, G)
+        q, s, z = int4.quantize_rtn_int4(W, G, gi)
+        packed[(K, N)] = (int4.pack_qweight(q), s, int4.pack_qzeros(z), gi)
+    wbytes = 0
+    worst = 0.0
+    t_total = 0.0
+    for K, N, M, _ in rot[0]:
+        qw, s, qz, gi = packed[(K, N)]
+        xb = xs[(M, K)].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        wd = int4.dequant_int4(qw, s, qz, gi, G, "f16")
+        y_ref = gemm.gemm_ref_bits(xb, wd, "f16")
+        t_total += time.perf_counter() - t0
+        wbytes += weight_bytes(K, N)
+        y = fp.bits_to_f64(outs[(M, N, K)].view(torch.int16).cpu().numpy().view(np.uint16), "f16")
+        worst = max(worst, gemm.rel_err(y, y_ref))
+    return {"value": round(wbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": "one full step (9 calls: 3 shapes x M in {1,4,16}); numpy dequant is "
+                      "single-threaded, the fp64 matmul uses the BLAS threads counted in cores",
+            "seconds": round(t_total, 2),
+            "host_cpus": os.cpu_count(),
+            "max_rel_err_gpu_vs_oracle": worst}
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,6 @@ from ._lib import W4A16Error  # noqa: F401
 
 F16, BF16 = 0, 1
 GROUP = 128
-TUNE_TARGET_WORKGROUPS = 0
 
 _DT = {torch.float16: F16, torch.bfloat16: BF16}
 
@@ -51,8 +50,11 @@ def version():
     return _lib.lib().w4a16_version()
 
 
-def w4a16_tune(key, value):
-    _lib.check(_lib.lib().w4a16_tune(key, value), "w4a16_tune")
+def w4a16_set_timing_events(start_event, stop_event):
+    """Attach raw hipEvent_t handles (ints) to the next GEMM kernel launch."""
+    _lib.check(_lib.lib().w4a16_set_timing_events(ctypes.c_void_p(start_event),
+                                                  ctypes.c_void_p(stop_event)),
+               "w4a16_set_timing_events")
 
 
 def w4a16_repacked_bytes(K, N, group_size=GROUP):
@@ -114,7 +116,7 @@ def w4a16_repack(qweight, scales, qzeros, g_idx=None, group_size=GROUP, stream=N
     dev = qweight.device
     codes_r = torch.empty(nc, dtype=torch.uint8, device=dev)
     scales_r = torch.empty(ns // 2, dtype=torch.float16, device=dev)
-    zeros_r = torch.empty(nz // 2, dtype=torch.int16, device=dev)
+    zeros_r = torch.empty(nz // 4, dtype=torch.int32, device=dev)
     perm = None
     if g_idx is not None:
         _need(g_idx, torch.int32, "g_idx", K)

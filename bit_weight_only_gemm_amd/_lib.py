@@ -17,7 +17,7 @@ _i32, _i64, _p = _c.c_int32, _c.c_int64, _c.c_void_p
 SIGNATURES = {
     "w4a16_status_string": (_c.c_char_p, [_c.c_int]),
     "w4a16_version": (_c.c_int, []),
-    "w4a16_tune": (_c.c_int, [_i32, _i64]),
+    "w4a16_set_timing_events": (_c.c_int, [_p, _p]),
     "w4a16_repacked_bytes": (_i64, [_i64, _i64, _i32, _i32]),
     "w4a16_make_perm": (_c.c_int, [_p, _i64, _i32, _p, _p, _p]),
     "w4a16_quantize_rtn": (_c.c_int, [_p, _p, _p, _i64, _i64, _i32, _p, _p, _p, _p]),

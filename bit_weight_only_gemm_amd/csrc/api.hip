@@ -15,10 +15,6 @@
 #include "common.h"
 #include "kernels.h"
 
-namespace w4a16 {
-void set_target_wgs(int v);
-}
-
 using namespace w4a16;
 
 namespace {
@@ -107,22 +103,13 @@ const char* w4a16_status_string(int status) {
 
 int w4a16_version(void) { return 1; }
 
-int w4a16_tune(int32_t key, int64_t value) {
-  if (key == W4A16_TUNE_TARGET_WORKGROUPS) {
-    if (value < 0 || value > (1 << 20)) return W4A16_ERR_INVALID_ARG;
-    set_target_wgs((int)value);
-    return W4A16_OK;
-  }
-  return W4A16_ERR_INVALID_ARG;
-}
-
 int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which) {
   if (validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
-  const int64_t NP = ceil_div(N, 64), KT = K / kGroup;
+  const int64_t NP = ceil_div(N, 64), KT = K / kGroup, KT8 = ceil_div(KT, 8);
   switch (which) {
     case W4A16_CODES: return NP * KT * 4096;
-    case W4A16_SCALES: return NP * KT * 128;
-    case W4A16_ZEROS: return NP * KT * 32;
+    case W4A16_SCALES: return NP * KT8 * 1024;
+    case W4A16_ZEROS: return NP * KT8 * 256;
     default: return -1;
   }
 }
@@ -192,7 +179,12 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
 
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (M <= 0 || validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
-  return plan_int4(M, N, K, true).ws_bytes;
+  return int4_workspace_bytes(M, N, K);
+}
+
+int w4a16_set_timing_events(void* start_event, void* stop_event) {
+  set_timing_events((hipEvent_t)start_event, (hipEvent_t)stop_event);
+  return W4A16_OK;
 }
 
 int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
@@ -204,10 +196,9 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({x, codes_r, scales_r, zeros_r, out})) return s;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
-  if (workspace) {
-    if (!aligned16(workspace)) return W4A16_ERR_MISALIGNED;
-    if (workspace_bytes < plan_int4(M, N, K, true).ws_bytes) return W4A16_ERR_WORKSPACE;
-  }
+  if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
+  if (perm && (!workspace || workspace_bytes < int4_workspace_bytes(M, N, K)))
+    return W4A16_ERR_WORKSPACE;
   return hip_status(launch_int4_gemm(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, dtype,
                                      workspace, workspace_bytes, (hipStream_t)stream));
 }
@@ -245,7 +236,8 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_
 
 int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize) {
   if (M <= 0 || validate_nf4_shape(N, K, blocksize) != W4A16_OK) return -1;
-  return plan_nf4(M, N, K, true).ws_bytes;
+  (void)M;
+  return 0;
 }
 
 int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
@@ -256,10 +248,8 @@ int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
   if (N % 16 != 0) return W4A16_ERR_INVALID_ARG;
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({x, qweight, absmax_q, absmax_scale, out})) return s;
-  if (workspace) {
-    if (!aligned16(workspace)) return W4A16_ERR_MISALIGNED;
-    if (workspace_bytes < plan_nf4(M, N, K, true).ws_bytes) return W4A16_ERR_WORKSPACE;
-  }
+  if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
+  (void)workspace_bytes;
   return hip_status(launch_nf4_gemm(x, qweight, absmax_q, absmax_scale, codebook(), out, M, N, K,
                                     dtype, workspace, workspace_bytes, (hipStream_t)stream));
 }

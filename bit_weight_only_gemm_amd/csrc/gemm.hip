@@ -6,102 +6,254 @@
 // only the 4-bit codes plus their scales (decode time tracks weight bytes,
 // item 3 of the same section).
 //
-// Work decomposition (skinny M, memory bound):
-//  * A workgroup is 4 waves.  Wave w owns one 64-column panel (4 MFMA column
-//    tiles of 16) of a 256-column block and a range of K tiles of 128; the 4
-//    waves share the same K range, so the activation slice for that range is
-//    staged in LDS once per workgroup, already in MFMA operand order.  For an
-//    act-order weight the staging gathers x[:, perm[k]] here, fused into the
-//    load (no separate permutation pass).
-//  * Per K tile a lane issues four 16-byte loads (one per column tile) of
-//    consecutive, fully coalesced 1 KB code tiles, dequantizes each 32-bit word
-//    into an 8-element MFMA operand and issues v_mfma_f32_16x16x32_{f16,bf16}
-//    with the M rows padded to 16 (x rows >= M are zero in LDS).
-//  * Split-K: when a workspace is given, the K range is split over several
-//    workgroups; each writes fp32 partial sums, and the last workgroup to
-//    arrive (device-scope atomic counter) adds them in split order and writes
-//    the rounded output, then re-arms the counter.  The reduction order is
-//    fixed, so results are bitwise reproducible.
+// Skinny-M kernel (decode), memory bound:
+//  * One workgroup of DW waves per 16-column MFMA tile (and per block of 16*MT
+//    rows).  The waves split the K tiles of 128 between them in runs of 8
+//    tiles (intra-workgroup split-K); each wave keeps fp32 accumulators in
+//    registers and the partial tiles are added in wave order through LDS at
+//    the end -- a fixed order, so results are bitwise reproducible and no
+//    global reduction, atomic or fence is needed.
+//  * The load pipe, not HBM, is what a naive version of this loop saturates:
+//    every wave64 vector-memory instruction costs the CU's load path about
+//    the same whatever its active lanes.  So per K tile a wave issues one
+//    16-byte-per-lane load of codes (a contiguous, coalesced 1 KB tile), the
+//    scales and zeros come once per run of 8 tiles (one 16-byte and one 4-byte
+//    load per lane), and for M <= 4 one 16-byte load per lane carries the
+//    activations of all 4 MFMA steps of the tile (see "packed" below).
+//  * Each 32-bit code word is dequantized exactly into an 8-element MFMA
+//    operand (the routine the dequant export uses) and multiplied with
+//    v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation.
+//  * "Packed" activations (M <= 4): the 16 A-operand rows are 4 K-steps x 4
+//    batch rows (row 4j + m holds step j of batch row m), so one load feeds
+//    the 4 MFMAs of a tile; step j accumulates into its own tile acc[j], whose
+//    rows 4j .. 4j+3 are the wanted products (the other rows mix steps and are
+//    dropped).  At the end a cross-lane shuffle adds the 4 step tiles.
+//  * Latency hiding: a ring of 8 tiles of codes (and of activations) is in
+//    flight per wave.  All loads are buffer loads with per-lane offsets fixed
+//    and the tile index in the wave-uniform offset, so the loop has no
+//    divergent branch and no load result merges through a branch (either
+//    would make the compiler drain every outstanding load per tile); rows
+//    >= M read 0 through the descriptor range.
+//  * For an act-order weight the activations are first permuted once,
+//    x_p[:, k] = x[:, perm[k]], into the workspace by a small gather kernel, so
+//    the GEMM itself always streams contiguous rows.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace w4a16 {
 
-// LDS activation staging capacity: 8 units of (one K tile x one 16-row tile)
-// of 4 KB each = 32 KB per workgroup.
-constexpr int XS_UNITS = 8;
+#ifndef W4A16_DECODE_WAVES
+#define W4A16_DECODE_WAVES 4
+#endif
+constexpr int DW = W4A16_DECODE_WAVES;  // waves per decode workgroup
+constexpr int RUN = 8;                  // K tiles per meta run and ring pass
+
+enum { AM_PACKED = 0, AM_FULL = 1 };
+
+// Buffer resource word 3 for gfx9-family (CDNA) raw buffers.
+constexpr int kRsrcWord3 = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// A per-lane buffer offset past every descriptor's range: the load returns 0.
+// (Only the per-lane offset is relied on for range checks.)
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ u32x4_t bld128(rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bld32(rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Timing events for the next main-kernel launch on this host thread (set by
+// w4a16_set_timing_events; consumed by one launch).
+thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void set_timing_events(hipEvent_t a, hipEvent_t b) {
+  t_ev_start = a;
+  t_ev_stop = b;
+}
+
+template <typename K, typename... Args>
+static void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  if (t_ev_start || t_ev_stop) {
+    hipEvent_t a = t_ev_start, b = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a, b, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  }
+}
+
+// Multiply-accumulate the 4 MFMA steps of one K tile given its 4 B operands.
+template <int DT, int AM, int MT, int NA, int NACC>
+__device__ __forceinline__ void mma_tile(const typename Op<DT>::vec b[4],
+                                         const typename Op<DT>::vec (&a)[NA],
+                                         float4_t (&acc)[NACC]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (AM == AM_PACKED) {
+      acc[j] = mfma16x16x32<DT>(a[0], b[j], acc[j]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = mfma16x16x32<DT>(a[m * 4 + j], b[j], acc[m]);
+    }
+  }
+}
 
 // --------------------------------------------------------------- INT4 policy --
-// Tile (panel p, group t): 4 column tiles x 64 lanes x 16 bytes of codes,
-// 16 x 4 fp16 scales, 16 packed zero nibble quads.  Word j of a lane covers
-// K = 32j + 8(lane >> 4) + e of the tile, which fixes the x staging order.
+// Column tile ct = 4p + c of panel p.  Word j of lane l covers K = 128t + 32j +
+// 8(l >> 4) + e, so lane-group b feeds x[row][128t + 32j + 8b ...] in step j.
 template <int DT>
 struct Int4W {
-  const u32x4_t* codes;
-  const uint2* scales;
-  const uint16_t* zeros;
+  static constexpr bool kRaggedK = false;  // K % 128 == 0 for this format
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint8_t* zeros;
   int KT;
-  u32x4_t cw[4];
-  uint2 sc;
-  uint32_t zz;
-  __device__ __forceinline__ void load(int panel, int t, int lane, int /*N*/, int /*K*/) {
-    const size_t tile = (size_t)panel * KT + t;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) cw[c] = codes[tile * 256 + c * 64 + lane];
-    sc = scales[tile * 16 + (lane & 15)];
-    zz = zeros[tile * 16 + (lane & 15)];
+  rsrc_t rc, rs, rz;
+  uint32_t voc, vos, voz;
+  int c;
+  struct Meta {
+    u32x4_t s;   // 8 fp16 scales of this lane's column, one per tile of the run
+    uint32_t z;  // 8 zero nibbles
+  };
+  __device__ __forceinline__ void init(int ct, int lane, int /*N*/, int /*K*/) {
+    const int p = ct >> 2;
+    c = ct & 3;
+    const int i = lane & 15;
+    const int KT8 = (KT + RUN - 1) / RUN;
+    // one descriptor per array, based at this panel: offsets stay 32-bit
+    rc = make_rsrc(codes + (size_t)p * KT * 4096, (uint32_t)KT * 4096u);
+    rs = make_rsrc(scales + (size_t)p * KT8 * 1024, (uint32_t)KT8 * 1024u);
+    rz = make_rsrc(zeros + (size_t)p * KT8 * 256, (uint32_t)KT8 * 256u);
+    voc = (uint32_t)(c * 1024 + lane * 16);
+    vos = (uint32_t)((c * 16 + i) * 16);
+    voz = (uint32_t)((c * 16 + i) * 4);
   }
-  // operand for column tile c, MFMA step j
-  __device__ __forceinline__ void operands(int c, typename Op<DT>::vec b[4]) const {
+  __device__ static __forceinline__ Meta zero_meta() {
+    Meta m;
+    m.s = u32x4_t{0u, 0u, 0u, 0u};
+    m.z = 0u;
+    return m;
+  }
+  __device__ __forceinline__ Meta load_meta(int run) const {
+    Meta m;
+    m.s = bld128(rs, vos, run * 1024);
+    m.z = bld32(rz, voz, run * 256);
+    return m;
+  }
+  __device__ __forceinline__ u32x4_t load_codes(int t, int /*lane*/) const {
+    return bld128(rc, voc, t * 4096);
+  }
+  // B operands of tile slot s (0..7 within the run) from the exact dequant.
+  __device__ __forceinline__ void operands(const u32x4_t& w, int s, const Meta& m,
+                                           typename Op<DT>::vec b[4]) const {
     QParam<DT> qp;
-    const uint32_t sbits = ((c < 2 ? sc.x : sc.y) >> (16 * (c & 1))) & 0xFFFFu;
-    qp.set(sbits, (zz >> (4 * c)) & 0xFu);
+    qp.set((m.s[s >> 1] >> (16 * (s & 1))) & 0xFFFFu, (m.z >> (4 * s)) & 0xFu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = dequant_word(cw[c][j], qp);
+    for (int j = 0; j < 4; ++j) b[j] = dequant_word(w[j], qp);
   }
-  // K offset (within the 128-wide tile) of the 8 x values lane-group b feeds in step j
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }
 };
 
 // ---------------------------------------------------------------- NF4 policy --
-// Raw bitsandbytes-style layout: row n of qweight holds K/2 bytes, element 2j
-// in the low nibble of byte j.  Lane (column i = lane & 15, group b = lane >> 4)
-// loads 16 bytes = 32 consecutive elements k0 + 32b .. k0 + 32b + 31 of its
-// column, all inside one 64-element absmax block; word j of the load feeds MFMA
-// step j.  Dequant follows the definition exactly: a' = fp32(absmax_q) * scale,
-// w = round16(fp32(L[c] * a')).
-template <int DT>
+// Raw layout: row n of qweight holds K/2 bytes, element 2j in the low nibble of
+// byte j.  Lane (column n = 16 ct + (l & 15), group b = l >> 4) loads 16 bytes =
+// elements 128t + 32b .. +31 of its row, all in one 64-element absmax block;
+// word j feeds MFMA step j.  Dequant is the definition: a' = fp32(absmax_q) *
+// absmax_scale, w = round16(fp32(L[c] * a')), L from a 16-entry LDS table.
+// BATCH (K % 1024 == 0): the 16 absmax bytes of a run of 8 tiles of a row are
+// one aligned 16-byte load and share one double-quant scale (a run of 16
+// blocks never straddles a group of 256); otherwise they are loaded per tile.
+template <int DT, bool BATCH>
 struct Nf4W {
+  static constexpr bool kRaggedK = true;  // K % 64 == 0 only: a last tile may be half
   const uint8_t* q;
   const uint8_t* aq;
   const float* asc;
-  const float* lut;  // 16 fp32 levels in LDS
-  u32x4_t cw[4];
-  float a[4];
-  __device__ __forceinline__ void load(int panel, int t, int lane, int N, int K) {
-    const int b = lane >> 4;
-    const int k = t * 128 + 32 * b;
+  const float* lut;
+  int N, K;
+  rsrc_t rq, raq, ras;
+  int kb;
+  uint32_t voq, vob, blk0;
+  struct Meta {
+    // BATCH: a16 = 16 absmax codes of the run, sc = its double-quant scale.
+    // otherwise: a[s] = dequantized absmax of tile slot s for this lane.
+    u32x4_t a16;
+    float sc;
+    float a[BATCH ? 1 : RUN];
+  };
+  __device__ __forceinline__ void init(int ct, int lane, int N_, int K_) {
+    N = N_;
+    K = K_;
+    const size_t n0 = (size_t)ct * 16;
+    const int nloc = lane & 15;
+    kb = lane >> 4;
+    rq = make_rsrc(q + n0 * (K >> 1), 16u * (uint32_t)(K >> 1));
+    raq = make_rsrc(aq + n0 * (K >> 6), 16u * (uint32_t)(K >> 6));
+    const size_t nblocks = (size_t)N * (K >> 6);
+    ras = make_rsrc(asc, (uint32_t)(((nblocks + 255) >> 8) * 4));
+    blk0 = (uint32_t)(n0 * (K >> 6));
+    voq = (uint32_t)(nloc * (K >> 1) + 16 * kb);
+    vob = (uint32_t)(nloc * (K >> 6));
+  }
+  __device__ static __forceinline__ Meta zero_meta() {
+    Meta m;
+    m.a16 = u32x4_t{0u, 0u, 0u, 0u};
+    m.sc = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int n = panel * 64 + c * 16 + (lane & 15);
-      if (n < N && k < K) {
-        cw[c] = *(const u32x4_t*)(q + (size_t)n * (K >> 1) + (k >> 1));
-        const size_t blk = ((size_t)n * K + k) >> 6;
-        a[c] = (float)aq[blk] * asc[blk >> 8];
-      } else {
-        cw[c] = u32x4_t{0, 0, 0, 0};
-        a[c] = 0.0f;
+    for (int s = 0; s < (BATCH ? 1 : RUN); ++s) m.a[s] = 0.0f;
+    return m;
+  }
+  __device__ __forceinline__ Meta load_meta(int run) const {
+    Meta m = zero_meta();
+    if constexpr (BATCH) {
+      m.a16 = bld128(raq, vob + (uint32_t)(16 * run), 0);
+      m.sc = __builtin_bit_cast(float, bld32(ras, ((blk0 + vob + 16u * run) >> 8) * 4u, 0));
+    } else {
+#pragma unroll
+      for (int s = 0; s < RUN; ++s) {
+        // block of (row, tile 8 run + s, lane group); reads past the row meet
+        // zero activations
+        const uint32_t bl = vob + (uint32_t)(2 * (RUN * run + s) + (kb >> 1));
+        const uint32_t qa = __builtin_amdgcn_raw_buffer_load_b8(raq, bl, 0, 0);
+        const float sa = __builtin_bit_cast(float, bld32(ras, ((blk0 + bl) >> 8) * 4u, 0));
+        m.a[s] = (float)qa * sa;
       }
     }
+    return m;
   }
-  __device__ __forceinline__ void operands(int c, typename Op<DT>::vec b[4]) const {
+  // t is a valid K tile.  In a half-filled last tile the lanes past K use an
+  // out-of-range per-lane offset and read zeros.
+  __device__ __forceinline__ u32x4_t load_codes(int t, int /*lane*/) const {
+    const uint32_t vq = (t * 128 + 32 * kb < K) ? voq : kOutOfRange;
+    return bld128(rq, vq, t * 64);
+  }
+  __device__ __forceinline__ void operands(const u32x4_t& w4, int s, const Meta& m,
+                                           typename Op<DT>::vec b[4]) const {
+    float a;
+    if constexpr (BATCH) {
+      // absmax code of block 2 s + (b >> 1) of the run: byte 2 (s & 1) + (b >> 1)
+      // of word s >> 1
+      const uint32_t qa = (m.a16[s >> 1] >> (16 * (s & 1) + 8 * (kb >> 1))) & 0xFFu;
+      a = (float)qa * m.sc;
+    } else {
+      a = m.a[s];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w = cw[c][j];
+      const uint32_t w = w4[j];
       typename Op<DT>::vec v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float f = lut[(w >> (4 * e)) & 0xFu] * a[c];
+        const float f = lut[(w >> (4 * e)) & 0xFu] * a;
         if constexpr (DT == DT_F16) v[e] = (_Float16)f;
         else v[e] = (__bf16)f;
       }
@@ -111,278 +263,294 @@ struct Nf4W {
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * b + 8 * j; }
 };
 
-template <int DT, int MT, bool PERM, class WP>
-__device__ __forceinline__ void gemm_body(const uint16_t* __restrict__ x,
-                                          const int32_t* __restrict__ perm, WP& wp,
-                                          uint16_t* __restrict__ out, uint32_t* __restrict__ cnt,
-                                          float* __restrict__ part, int M, int N, int K, int NP,
-                                          int KT, int kt_per, int nsplit, u32x4_t* xs) {
-  __shared__ uint32_t s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cb = blockIdx.x, sp = blockIdx.y, rb = blockIdx.z;
-  const int row0 = rb * 16 * MT;
-  const int panel = cb * 4 + wave;
-  const bool active = panel < NP;
-  const int kt0 = sp * kt_per;
-  const int kt1 = min(KT, kt0 + kt_per);
-  constexpr int CH = XS_UNITS / MT;  // K tiles per staged chunk
-
-  float4_t acc[MT][4];
+// Activations of one K tile.  PACKED: one vector, lane row r = 4 j + m holds
+// step j of batch row m.  FULL: MT x 4 vectors (row tile m, step j), lane row
+// r = batch row.  Rows >= M read 0 through the descriptor range; k >= K (only
+// in a half NF4 tile) uses an out-of-range offset.
+template <int DT, int AM, int MT, int NA, class WP>
+__device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
+                                       typename Op<DT>::vec (&a)[NA]) {
+  const int r = lane & 15, b = lane >> 4;
+  if constexpr (AM == AM_PACKED) {
+    const int j = r >> 2, m = r & 3;
+    const int kin = WP::xk(j, b);
+    uint32_t off = (uint32_t)m * (uint32_t)K * 2u + (uint32_t)kin * 2u;
+    if constexpr (WP::kRaggedK) off = (t * 128 + kin < K) ? off : kOutOfRange;
+    a[0] = __builtin_bit_cast(typename Op<DT>::vec, bld128(rx, off, t * 256));
+  } else {
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) {
+      const uint32_t rowoff = (uint32_t)(m * 16 + r) * (uint32_t)K * 2u;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[m][c] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = kt0; c0 < kt1; c0 += CH) {
-    const int nct = min(CH, kt1 - c0);
-    if (active) wp.load(panel, c0, lane, N, K);  // first tile's weights in flight
-    __syncthreads();                             // previous chunk fully consumed
-    // ---- stage x[row0 .. row0+16MT, K chunk] in MFMA A-operand order
-    const int units = nct * MT * 256;
-    for (int idx = tid; idx < units; idx += 256) {
-      const int l = idx & 63, j = (idx >> 6) & 3, r = idx >> 8;
-      const int mt = r % MT, t = r / MT;
-      const int row = row0 + mt * 16 + (l & 15);
-      const int kp = (c0 + t) * 128 + WP::xk(j, l >> 4);
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (row < M && kp < K) {
-        const uint16_t* xr = x + (size_t)row * K;
-        if constexpr (!PERM) {
-          v = *(const u32x4_t*)(xr + kp);
-        } else {
-#pragma unroll
-          for (int h = 0; h < 4; ++h)
-            v[h] = (uint32_t)xr[perm[kp + 2 * h]] | ((uint32_t)xr[perm[kp + 2 * h + 1]] << 16);
-        }
-      }
-      xs[idx] = v;
-    }
-    __syncthreads();
-    if (active) {
-      for (int t = 0; t < nct; ++t) {
-        WP cur = wp;
-        if (t + 1 < nct) wp.load(panel, c0 + t + 1, lane, N, K);  // prefetch next tile
-        typename Op<DT>::vec a[MT][4];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            a[m][j] = __builtin_bit_cast(typename Op<DT>::vec, xs[((t * MT + m) * 4 + j) * 64 + lane]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          typename Op<DT>::vec b[4];
-          cur.operands(c, b);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m][c] = mfma16x16x32<DT>(a[m][j], b[j], acc[m][c]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int kin = WP::xk(j, b);
+        uint32_t off = rowoff + (uint32_t)kin * 2u;
+        if constexpr (WP::kRaggedK) off = (t * 128 + kin < K) ? off : kOutOfRange;
+        a[m * 4 + j] = __builtin_bit_cast(typename Op<DT>::vec, bld128(rx, off, t * 256));
       }
     }
   }
-
-  // ---- epilogue.  v_mfma_f32_16x16x32 result layout: element i of lane l is
-  // row 4 * (l >> 4) + i, column l & 15 of the 16x16 tile.
-  const int rsub = 4 * (lane >> 4);
-  if (nsplit == 1) {
-    if (!active) return;
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int col = panel * 64 + c * 16 + (lane & 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = row0 + m * 16 + rsub + i;
-          if (row < M && col < N) out[(size_t)row * N + col] = round16<DT>(acc[m][c][i]);
-        }
-      }
-    return;
-  }
-  const int Np = NP * 64;
-  if (active) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int col = panel * 64 + c * 16 + (lane & 15);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = row0 + m * 16 + rsub + i;
-          if (row < M) part[((size_t)sp * M + row) * Np + col] = acc[m][c][i];
-        }
-      }
-  }
-  __threadfence();
-  __syncthreads();
-  uint32_t* ctr = cnt + (size_t)rb * gridDim.x + cb;
-  if (tid == 0) s_last = (atomicAdd(ctr, 1u) == (uint32_t)(nsplit - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int col = cb * 256 + tid;
-  if (col < N) {
-    for (int r = 0; r < 16 * MT; ++r) {
-      const int row = row0 + r;
-      if (row >= M) break;
-      float s = 0.0f;
-      for (int q = 0; q < nsplit; ++q) s += part[((size_t)q * M + row) * Np + col];
-      out[(size_t)row * N + col] = round16<DT>(s);
-    }
-  }
-  if (tid == 0) *ctr = 0u;  // re-arm for the next call
 }
 
-template <int DT, int MT, bool PERM>
-__global__ void __launch_bounds__(256)
-int4_gemm_kernel(const uint16_t* __restrict__ x, const u32x4_t* __restrict__ codes,
-                 const uint2* __restrict__ scales, const uint16_t* __restrict__ zeros,
-                 const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
-                 uint32_t* __restrict__ cnt, float* __restrict__ part, int M, int N, int K,
-                 int NP, int KT, int kt_per, int nsplit) {
-  __shared__ u32x4_t xs[XS_UNITS * 256];
+template <int DT, int MT, int AM, class WP>
+__device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& wp,
+                                            uint16_t* __restrict__ out, int M, int N, int K,
+                                            int KT, float* red) {
+  constexpr int NA = AM == AM_PACKED ? 1 : MT * 4;                 // A vectors per tile
+  constexpr int NACC = AM == AM_PACKED ? 4 : MT;                   // accumulator tiles
+  constexpr int PA = AM == AM_PACKED ? RUN : (MT == 1 ? 2 : 1);    // A ring depth
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ct = blockIdx.x;
+  const int row0 = blockIdx.y * 16 * MT;
+  wp.init(ct, lane, N, K);
+  const int nrun = (KT + RUN - 1) / RUN;
+  const int r0 = (nrun * wave) / DW, r1 = (nrun * (wave + 1)) / DW;
+  const int t0 = r0 * RUN;
+  const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
+  const int vrows = min(16 * MT, M - row0);
+  const rsrc_t rx = make_rsrc(x + (size_t)row0 * K, (uint32_t)vrows * (uint32_t)K * 2u);
+
+  float4_t acc[NACC];
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Ring of RUN tiles: slot s holds tile i + s of the current pass.  All
+  // loads are issued from one program point: the first pass (i = -RUN) only
+  // fills the ring; later passes compute slot s and refill it with tile
+  // i + s + RUN (clamped into range: the tail re-reads the last tile from
+  // cache, and slots past the wave's range are not computed).  The meta of a
+  // run is double-buffered.  Scheduling barriers keep slot order in the
+  // instruction stream so each slot's wait covers only its own loads.
+  if (n > 0) {
+    u32x4_t ring[RUN];
+    typename Op<DT>::vec ra[PA][NA];
+#pragma unroll
+    for (int s = 0; s < RUN; ++s) ring[s] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < PA; ++s)
+#pragma unroll
+      for (int q = 0; q < NA; ++q) ra[s][q] = typename Op<DT>::vec{};
+    typename WP::Meta mc, mn = WP::zero_meta();
+    for (int i = -RUN; i < n; i += RUN) {
+      mc = mn;
+      mn = wp.load_meta(r0 + min(i / RUN + 1, (n - 1) / RUN));
+#pragma unroll
+      for (int s = 0; s < RUN; ++s) {
+        const int sa = s % PA;
+        if (i + s >= 0 && i + s < n) {  // wave-uniform
+          typename Op<DT>::vec b[4];
+          wp.operands(ring[s], s, mc, b);
+          mma_tile<DT, AM, MT, NA, NACC>(b, ra[sa], acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        ring[s] = wp.load_codes(t0 + min(i + s + RUN, n - 1), lane);
+        load_a<DT, AM, MT, NA, WP>(rx, K, t0 + max(0, min(i + s + PA, n - 1)), lane, ra[sa]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- v_mfma_f32_16x16x32 result layout: element e of lane l is row
+  // 4 (l >> 4) + e, column l & 15 of the 16x16 tile.
+  float4_t res[MT];
+  if constexpr (AM == AM_PACKED) {
+    // rows 4g .. 4g+3 of step tile acc[g] (g = lane group) are batch rows
+    // 0..3 of step g: take them and add the 4 lane groups (a shuffle
+    // reduction across the wave); lane group 0 then holds rows 0..3.
+    const int g = lane >> 4;
+    float4_t v = g == 0 ? acc[0] : (g == 1 ? acc[1] : (g == 2 ? acc[2] : acc[3]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += __shfl_xor(v[e], 16, 64);
+      v[e] += __shfl_xor(v[e], 32, 64);
+    }
+    res[0] = g == 0 ? v : float4_t{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) res[m] = acc[m];
+  }
+
+  // ---- wave partials -> LDS, summed in wave order
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    *(float4_t*)(red + ((wave * MT + m) * 64 + lane) * 4) = res[m];
+  __syncthreads();
+  if (wave < MT) {
+    const int m = wave;
+    float4_t s = *(const float4_t*)(red + ((0 * MT + m) * 64 + lane) * 4);
+#pragma unroll
+    for (int w = 1; w < DW; ++w) {
+      const float4_t v = *(const float4_t*)(red + ((w * MT + m) * 64 + lane) * 4);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+    const int col = ct * 16 + (lane & 15);
+    if (col < N) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + m * 16 + 4 * (lane >> 4) + e;
+        if (row < M) out[(size_t)row * N + col] = round16<DT>(s[e]);
+      }
+    }
+  }
+}
+
+template <int DT, int MT, int AM>
+__global__ void __launch_bounds__(64 * DW)
+int4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
+                   const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                   uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+  __shared__ float red[DW * MT * 64 * 4];
   Int4W<DT> wp;
   wp.codes = codes;
   wp.scales = scales;
   wp.zeros = zeros;
   wp.KT = KT;
-  gemm_body<DT, MT, PERM>(x, perm, wp, out, cnt, part, M, N, K, NP, KT, kt_per, nsplit, xs);
+  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red);
 }
 
-template <int DT, int MT>
-__global__ void __launch_bounds__(256)
-nf4_gemm_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
-                const uint8_t* __restrict__ aq, const float* __restrict__ asc, Nf4Table L,
-                uint16_t* __restrict__ out, uint32_t* __restrict__ cnt,
-                float* __restrict__ part, int M, int N, int K, int NP, int KT, int kt_per,
-                int nsplit) {
-  __shared__ u32x4_t xs[XS_UNITS * 256];
+template <int DT, int MT, int AM, bool BATCH>
+__global__ void __launch_bounds__(64 * DW)
+nf4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
+                  const uint8_t* __restrict__ aq, const float* __restrict__ asc, Nf4Table L,
+                  uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+  __shared__ float red[DW * MT * 64 * 4];
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
-  Nf4W<DT> wp;
+  __syncthreads();
+  Nf4W<DT, BATCH> wp;
   wp.q = q;
   wp.aq = aq;
   wp.asc = asc;
   wp.lut = lut;
-  __syncthreads();
-  gemm_body<DT, MT, false>(x, nullptr, wp, out, cnt, part, M, N, K, NP, KT, kt_per, nsplit, xs);
+  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red);
+}
+
+// x_p[m, k] = x[m, perm[k]]: one thread per 8 consecutive permuted columns.
+__global__ void __launch_bounds__(256)
+permute_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                 uint16_t* __restrict__ xp, int M, int K) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = K >> 3;
+  if (idx >= (int64_t)M * per_row) return;
+  const int64_t m = idx / per_row;
+  const int k = (int)(idx - m * per_row) * 8;
+  const uint16_t* xr = x + m * K;
+  const int4* pp = (const int4*)(perm + k);
+  const int4 p0 = pp[0], p1 = pp[1];
+  u32x4_t v;
+  v[0] = (uint32_t)xr[p0.x] | ((uint32_t)xr[p0.y] << 16);
+  v[1] = (uint32_t)xr[p0.z] | ((uint32_t)xr[p0.w] << 16);
+  v[2] = (uint32_t)xr[p1.x] | ((uint32_t)xr[p1.y] << 16);
+  v[3] = (uint32_t)xr[p1.z] | ((uint32_t)xr[p1.w] << 16);
+  *(u32x4_t*)(xp + m * K + k) = v;
 }
 
 // ---------------------------------------------------------------- planning --
-static int g_target_wgs = 512;
+int64_t int4_workspace_bytes(int64_t M, int64_t /*N*/, int64_t K) {
+  // room for the permuted activations of an act-order weight
+  return ceil_div(M * K * 2, 256) * 256;
+}
 
-SplitPlan plan_common(int64_t M, int64_t N, int64_t K, bool have_ws) {
-  SplitPlan p;
-  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  p.nrb = ceil_div(M, 16 * p.mt);
-  const int64_t NP = ceil_div(N, 64);
-  p.ncb = ceil_div(NP, 4);
-  p.kt = ceil_div(K, 128);
-  p.nsplit = 1;
-  if (have_ws) {
-    const int64_t base = p.ncb * p.nrb;
-    p.nsplit = std::max<int64_t>(1, std::min<int64_t>(p.kt, ceil_div(g_target_wgs, base)));
+// Activation mode and row tiles per workgroup row block for M rows.
+static int pick_mode(int64_t M, int* mt) {
+  if (M <= 4) {
+    *mt = 1;
+    return AM_PACKED;
   }
-  p.kt_per = ceil_div(p.kt, p.nsplit);
-  p.nsplit = ceil_div(p.kt, p.kt_per);
-  p.ws_bytes = 0;
-  if (p.nsplit > 1) {
-    const int64_t cnt_bytes = ceil_div(p.nrb * p.ncb * 4, 256) * 256;
-    p.ws_bytes = cnt_bytes + p.nsplit * M * NP * 64 * 4;
-  }
-  return p;
+  *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  return AM_FULL;
 }
 
-SplitPlan plan_int4(int64_t M, int64_t N, int64_t K, bool have_ws) {
-  return plan_common(M, N, K, have_ws);
-}
-SplitPlan plan_nf4(int64_t M, int64_t N, int64_t K, bool have_ws) {
-  return plan_common(M, N, K, have_ws);
+template <int DT, int MT, int AM>
+static void launch_int4_v(const void* x, const void* codes_r, const void* scales_r,
+                          const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
+                          hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
+  launch_timed(int4_decode_kernel<DT, MT, AM>, grid, dim3(64 * DW), stream, (const uint16_t*)x,
+               (const uint8_t*)codes_r, (const uint8_t*)scales_r, (const uint8_t*)zeros_r,
+               (uint16_t*)out, (int)M, (int)N, (int)K, (int)(K / 128));
 }
 
-void set_target_wgs(int v) { g_target_wgs = v > 0 ? v : 512; }
-
-template <int DT, int MT>
-static void launch_int4_mt(const void* x, const void* codes_r, const void* scales_r,
-                           const void* zeros_r, const int32_t* perm, void* out, int64_t M,
-                           int64_t N, int64_t K, const SplitPlan& p, uint32_t* cnt, float* part,
+template <int DT>
+static void launch_int4_dt(const void* x, const void* codes_r, const void* scales_r,
+                           const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream) {
-  const dim3 grid((unsigned)p.ncb, (unsigned)p.nsplit, (unsigned)p.nrb);
-  const int NP = (int)ceil_div(N, 64);
-  if (perm)
-    hipLaunchKernelGGL((int4_gemm_kernel<DT, MT, true>), grid, dim3(256), 0, stream,
-                       (const uint16_t*)x, (const u32x4_t*)codes_r, (const uint2*)scales_r,
-                       (const uint16_t*)zeros_r, perm, (uint16_t*)out, cnt, part, (int)M,
-                       (int)N, (int)K, NP, (int)p.kt, (int)p.kt_per, (int)p.nsplit);
+  int mt;
+  const int am = pick_mode(M, &mt);
+  if (am == AM_PACKED)
+    launch_int4_v<DT, 1, AM_PACKED>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+  else if (mt == 1)
+    launch_int4_v<DT, 1, AM_FULL>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+  else if (mt == 2)
+    launch_int4_v<DT, 2, AM_FULL>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
   else
-    hipLaunchKernelGGL((int4_gemm_kernel<DT, MT, false>), grid, dim3(256), 0, stream,
-                       (const uint16_t*)x, (const u32x4_t*)codes_r, (const uint2*)scales_r,
-                       (const uint16_t*)zeros_r, perm, (uint16_t*)out, cnt, part, (int)M,
-                       (int)N, (int)K, NP, (int)p.kt, (int)p.kt_per, (int)p.nsplit);
-}
-
-static void split_ws(const SplitPlan& p, void* ws, uint32_t** cnt, float** part) {
-  *cnt = nullptr;
-  *part = nullptr;
-  if (p.nsplit > 1) {
-    *cnt = (uint32_t*)ws;
-    *part = (float*)((char*)ws + ceil_div(p.nrb * p.ncb * 4, 256) * 256);
-  }
+    launch_int4_v<DT, 4, AM_FULL>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
 }
 
 hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scales_r,
                             const void* zeros_r, const int32_t* perm, void* out, int64_t M,
                             int64_t N, int64_t K, int dtype, void* workspace,
                             int64_t /*workspace_bytes*/, hipStream_t stream) {
-  const SplitPlan p = plan_int4(M, N, K, workspace != nullptr);
-  uint32_t* cnt;
-  float* part;
-  split_ws(p, workspace, &cnt, &part);
-#define W4_LAUNCH(DTV, MTV) \
-  launch_int4_mt<DTV, MTV>(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, p, cnt, part, stream)
-  if (dtype == DT_F16) {
-    if (p.mt == 1) W4_LAUNCH(DT_F16, 1);
-    else if (p.mt == 2) W4_LAUNCH(DT_F16, 2);
-    else W4_LAUNCH(DT_F16, 4);
-  } else {
-    if (p.mt == 1) W4_LAUNCH(DT_BF16, 1);
-    else if (p.mt == 2) W4_LAUNCH(DT_BF16, 2);
-    else W4_LAUNCH(DT_BF16, 4);
+  const void* xa = x;
+  if (perm) {
+    const int64_t n8 = M * (K / 8);
+    hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, stream,
+                       (const uint16_t*)x, perm, (uint16_t*)workspace, (int)M, (int)K);
+    xa = workspace;
   }
-#undef W4_LAUNCH
+  if (dtype == DT_F16)
+    launch_int4_dt<DT_F16>(xa, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+  else
+    launch_int4_dt<DT_BF16>(xa, codes_r, scales_r, zeros_r, out, M, N, K, stream);
   return hipGetLastError();
 }
 
-template <int DT, int MT>
-static void launch_nf4_mt(const void* x, const uint8_t* q, const uint8_t* aq, const float* asc,
+template <int DT, int MT, int AM, bool BATCH>
+static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, const float* asc,
+                         const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
+                         hipStream_t stream) {
+  const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
+  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), stream,
+               (const uint16_t*)x, q, aq, asc, L, (uint16_t*)out, (int)M, (int)N, (int)K,
+               (int)ceil_div(K, 128));
+}
+
+template <int DT, bool BATCH>
+static void launch_nf4_dt(const void* x, const uint8_t* q, const uint8_t* aq, const float* asc,
                           const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
-                          const SplitPlan& p, uint32_t* cnt, float* part, hipStream_t stream) {
-  const dim3 grid((unsigned)p.ncb, (unsigned)p.nsplit, (unsigned)p.nrb);
-  hipLaunchKernelGGL((nf4_gemm_kernel<DT, MT>), grid, dim3(256), 0, stream, (const uint16_t*)x, q,
-                     aq, asc, L, (uint16_t*)out, cnt, part, (int)M, (int)N, (int)K,
-                     (int)ceil_div(N, 64), (int)p.kt, (int)p.kt_per, (int)p.nsplit);
+                          hipStream_t stream) {
+  int mt;
+  const int am = pick_mode(M, &mt);
+  if (am == AM_PACKED)
+    launch_nf4_v<DT, 1, AM_PACKED, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+  else if (mt == 1)
+    launch_nf4_v<DT, 1, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+  else if (mt == 2)
+    launch_nf4_v<DT, 2, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+  else
+    launch_nf4_v<DT, 4, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
 }
 
 hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,
-                           int64_t N, int64_t K, int dtype, void* workspace,
+                           int64_t N, int64_t K, int dtype, void* /*workspace*/,
                            int64_t /*workspace_bytes*/, hipStream_t stream) {
-  const SplitPlan p = plan_nf4(M, N, K, workspace != nullptr);
-  uint32_t* cnt;
-  float* part;
-  split_ws(p, workspace, &cnt, &part);
-#define NF_LAUNCH(DTV, MTV) \
-  launch_nf4_mt<DTV, MTV>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, p, cnt, part, stream)
+  const bool batch = K % 1024 == 0;
   if (dtype == DT_F16) {
-    if (p.mt == 1) NF_LAUNCH(DT_F16, 1);
-    else if (p.mt == 2) NF_LAUNCH(DT_F16, 2);
-    else NF_LAUNCH(DT_F16, 4);
+    if (batch)
+      launch_nf4_dt<DT_F16, true>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+    else
+      launch_nf4_dt<DT_F16, false>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
   } else {
-    if (p.mt == 1) NF_LAUNCH(DT_BF16, 1);
-    else if (p.mt == 2) NF_LAUNCH(DT_BF16, 2);
-    else NF_LAUNCH(DT_BF16, 4);
+    if (batch)
+      launch_nf4_dt<DT_BF16, true>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+    else
+      launch_nf4_dt<DT_BF16, false>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
   }
-#undef NF_LAUNCH
   return hipGetLastError();
 }
 

@@ -13,19 +13,13 @@ struct Nf4Table {
   float v[16];
 };
 
-// Split-K plan shared by the GEMM launchers and the workspace-size query.
-struct SplitPlan {
-  int mt;          // 16-row MFMA tiles per workgroup row block (1, 2 or 4)
-  int64_t nrb;     // row blocks of 16 * mt rows
-  int64_t ncb;     // column blocks (4 panels of 64 columns each)
-  int64_t kt;      // K tiles of 128
-  int64_t kt_per;  // K tiles per workgroup
-  int64_t nsplit;  // workgroups along K per output tile
-  int64_t ws_bytes;
-};
+// Workspace bytes the INT4 GEMM needs at this shape when a column permutation
+// is given (room for the permuted activations); 0 otherwise.
+int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-SplitPlan plan_int4(int64_t M, int64_t N, int64_t K, bool have_workspace);
-SplitPlan plan_nf4(int64_t M, int64_t N, int64_t K, bool have_workspace);
+// Attach HIP timing events to the next main GEMM kernel launched by the
+// calling host thread (hipExtLaunchKernel start/stop events).
+void set_timing_events(hipEvent_t start, hipEvent_t stop);
 
 hipError_t launch_rtn_int4(const float* W, const int32_t* perm, int64_t N, int64_t K,
                            int32_t* qweight, uint16_t* scales, int32_t* qzeros,

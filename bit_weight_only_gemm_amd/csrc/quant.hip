@@ -160,31 +160,35 @@ repack_codes_kernel(const uint32_t* __restrict__ qweight, const int32_t* __restr
   codes_r[idx] = word;
 }
 
-// One thread per (panel p, group t, column-in-tile i): 4 scales + packed zeros.
+// One thread per (panel p, run g of 8 groups, column tile c, column i): the 8
+// scales (16 bytes) and the 8 zero nibbles (one word) of that column.
 __global__ void __launch_bounds__(256)
 repack_meta_kernel(const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
                    int64_t K, int64_t N, int64_t NP, uint16_t* __restrict__ scales_r,
-                   uint16_t* __restrict__ zeros_r) {
-  const int64_t KT = K / 128;
+                   uint32_t* __restrict__ zeros_r) {
+  const int64_t KT = K / 128, KT8 = ceil_div(KT, 8);
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= NP * KT * 16) return;
+  if (idx >= NP * KT8 * 64) return;
   const int i = (int)(idx & 15);
-  const int64_t pt = idx >> 4;
-  const int64_t t = pt % KT, p = pt / KT;
-  uint32_t zp = 0;
+  const int c = (int)((idx >> 4) & 3);
+  const int64_t pg = idx >> 6;
+  const int64_t g = pg % KT8, p = pg / KT8;
+  const int64_t n = p * 64 + c * 16 + i;
+  uint32_t zw = 0;
+  u32x4_t sv = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int64_t n = p * 64 + c * 16 + i;
-    uint16_t s = 0;
-    uint32_t z = 0;
-    if (n < N) {
-      s = scales[t * N + n];
+  for (int s = 0; s < 8; ++s) {
+    const int64_t t = g * 8 + s;
+    uint32_t sb = 0, z = 0;
+    if (n < N && t < KT) {
+      sb = scales[t * N + n];
       z = (qzeros[t * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
     }
-    scales_r[idx * 4 + c] = s;
-    zp |= z << (4 * c);
+    sv[s >> 1] |= sb << (16 * (s & 1));
+    zw |= z << (4 * s);
   }
-  zeros_r[idx] = (uint16_t)zp;
+  *(u32x4_t*)(scales_r + idx * 8) = sv;
+  zeros_r[idx] = zw;
 }
 
 hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
@@ -194,10 +198,10 @@ hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const i
   const int64_t words = NP * KT * 1024;
   hipLaunchKernelGGL(repack_codes_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0,
                      stream, (const uint32_t*)qweight, perm, K, N, NP, (uint32_t*)codes_r);
-  const int64_t metas = NP * KT * 16;
+  const int64_t metas = NP * ceil_div(KT, 8) * 64;
   hipLaunchKernelGGL(repack_meta_kernel, dim3((unsigned)ceil_div(metas, 256)), dim3(256), 0,
                      stream, scales, (const uint32_t*)qzeros, K, N, NP, (uint16_t*)scales_r,
-                     (uint16_t*)zeros_r);
+                     (uint32_t*)zeros_r);
   return hipGetLastError();
 }
 
@@ -207,9 +211,9 @@ hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const i
 template <int DT>
 __global__ void __launch_bounds__(256)
 dequant_int4_kernel(const uint32_t* __restrict__ codes_r, const uint16_t* __restrict__ scales_r,
-                    const uint16_t* __restrict__ zeros_r, int64_t K, int64_t N, int64_t NP,
+                    const uint32_t* __restrict__ zeros_r, int64_t K, int64_t N, int64_t NP,
                     uint16_t* __restrict__ w_out) {
-  const int64_t KT = K / 128;
+  const int64_t KT = K / 128, KT8 = ceil_div(KT, 8);
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= NP * KT * 1024) return;
   const int j = (int)(idx & 3);
@@ -220,9 +224,9 @@ dequant_int4_kernel(const uint32_t* __restrict__ codes_r, const uint16_t* __rest
   const int i = lane & 15;
   const int64_t n = p * 64 + c * 16 + i;
   if (n >= N) return;
-  const int64_t meta = pt * 16 + i;
+  const int64_t meta = ((p * KT8 + (t >> 3)) * 4 + c) * 16 + i;
   QParam<DT> qp;
-  qp.set(scales_r[meta * 4 + c], (zeros_r[meta] >> (4 * c)) & 0xFu);
+  qp.set(scales_r[meta * 8 + (t & 7)], (zeros_r[meta] >> (4 * (t & 7))) & 0xFu);
   const auto v = dequant_word(codes_r[idx], qp);
   const int64_t k = t * 128 + j * 32 + (lane >> 4) * 8;
   *(u32x4_t*)(w_out + n * K + k) = __builtin_bit_cast(u32x4_t, v);
@@ -236,11 +240,11 @@ hipError_t launch_dequant_int4(const void* codes_r, const void* scales_r, const 
   if (dtype == DT_F16)
     hipLaunchKernelGGL(dequant_int4_kernel<DT_F16>, grid, dim3(256), 0, stream,
                        (const uint32_t*)codes_r, (const uint16_t*)scales_r,
-                       (const uint16_t*)zeros_r, K, N, NP, (uint16_t*)w_out);
+                       (const uint32_t*)zeros_r, K, N, NP, (uint16_t*)w_out);
   else
     hipLaunchKernelGGL(dequant_int4_kernel<DT_BF16>, grid, dim3(256), 0, stream,
                        (const uint32_t*)codes_r, (const uint16_t*)scales_r,
-                       (const uint16_t*)zeros_r, K, N, NP, (uint16_t*)w_out);
+                       (const uint32_t*)zeros_r, K, N, NP, (uint16_t*)w_out);
   return hipGetLastError();
 }
 

@@ -67,13 +67,14 @@ const char* w4a16_status_string(int status);
 int w4a16_version(void);
 
 /*
- * Process-wide tuning knob for later calls (not thread-safe against
- * concurrent GEMM calls).  W4A16_TUNE_TARGET_WORKGROUPS: number of workgroups
- * the split-K planner aims for (default 512; 0 restores the default).  It
- * changes only how K is split, never the result beyond fp32 summation order.
+ * Kernel timing (for benchmarks): attach two HIP events (hipEvent_t, created
+ * by the caller) to the NEXT main GEMM kernel that w4a16_gemm or nf4_gemm
+ * launches from the calling host thread.  The events are recorded by the
+ * kernel's own dispatch (hipExtLaunchKernel), so hipEventElapsedTime between
+ * them is that kernel's execution time.  One-shot: cleared by that launch.
+ * Passing NULLs clears a pending request.  Do not use under graph capture.
  */
-enum { W4A16_TUNE_TARGET_WORKGROUPS = 0 };
-int w4a16_tune(int32_t key, int64_t value);
+int w4a16_set_timing_events(void* start_event, void* stop_event);
 
 /* ------------------------------------------------------------------ INT4 --- */
 
@@ -86,8 +87,11 @@ int w4a16_tune(int32_t key, int64_t value);
  *          (permuted) input column k = 128t + 32j + 8b + e are stored in lane
  *          l = i + 16b, 32-bit little-endian word j of that lane's 16 bytes,
  *          nibble slot (e >> 1) + 4*(e & 1).  Padding columns are zero.
- *   scales fp16  [NP][KT][16][4]: entry [p][t][i][c] = scale(64p+16c+i, t).
- *   zeros  uint16 [NP][KT][16]: bits [4c, 4c+4) = zero(64p+16c+i, t).
+ *   scales fp16  [NP][KT8][4][16][8] (KT8 = ceil(KT/8)): entry [p][g][c][i][s]
+ *          = scale(64p+16c+i, group 8g+s); zero for padding columns/groups.
+ *   zeros  uint32 [NP][KT8][4][16]: bits [4s, 4s+4) = zero(64p+16c+i, 8g+s).
+ *   (Runs of 8 groups let a decode wave fetch 8 groups' scales in one 16-byte
+ *   load and their zeros in one dword.)
  */
 int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which);
 
@@ -143,11 +147,10 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
                  int32_t* perm_used_host, void* stream);
 
 /*
- * Workspace bytes w4a16_gemm may use for split-K partial sums at this shape
- * (0 if it needs none).  The workspace must be zero-filled once when it is
- * allocated; every completed call leaves it in that state again, so it can be
- * reused by later calls on the same stream.  Calls that overlap in time must
- * not share a workspace.
+ * Workspace bytes w4a16_gemm needs at this shape when it is given a column
+ * permutation `perm` (room for the permuted activations x[:, perm]); without
+ * a permutation no workspace is used.  Calls that overlap in time must not
+ * share a workspace.
  */
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
 
@@ -161,10 +164,11 @@ int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_siz
  *   perm   int32 [K] from w4a16_repack (or NULL for identity).
  *   codes_r, scales_r, zeros_r from w4a16_repack.
  *   dtype  W4A16_F16 or W4A16_BF16 (activations and output).
- *   workspace / workspace_bytes: optional split-K workspace (see above); NULL
- *          forces a single pass over K per output tile (correct, may be slower).
+ *   workspace / workspace_bytes: required when perm is given (at least
+ *          w4a16_workspace_bytes; W4A16_ERR_WORKSPACE otherwise), else ignored.
  * Constraints: M >= 1, K % 128 == 0, N % 8 == 0, group_size == 128.
- * Async on `stream`.  Results are bitwise reproducible run to run.
+ * Async on `stream`.  Results are bitwise reproducible run to run (the split of
+ * K over a workgroup's waves is reduced in a fixed order).
  */
 int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
                const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
@@ -207,7 +211,7 @@ int nf4_codebook(float* out16_host);
 int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_t* qweight,
                  uint8_t* absmax_q, float* absmax_scale, void* stream);
 
-/* Workspace bytes nf4_gemm may use at this shape (same contract as above). */
+/* Workspace bytes nf4_gemm needs at this shape (currently always 0). */
 int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
 
 /*

@@ -16,10 +16,11 @@ Layout (G = 128, KT = K / G, NP = ceil(N / 64)):
   permuted column k' = 128t + 32j + 8b + e, the code sits in lane l = i + 16b,
   32-bit word j of that lane's 16 bytes (little endian), at nibble slot
   (e >> 1) + 4 * (e & 1).  Columns n >= N are zero padding.
-* Scales: fp16 [NP][KT][16][4], entry [p][t][i][c] = scale of column
-  64p + 16c + i in group t (0 for padding).
-* Zeros: uint16 [NP][KT][16], bits [4c, 4c + 4) of [p][t][i] = zero of column
-  64p + 16c + i in group t (0 for padding).
+* Scales, in runs of 8 groups (KT8 = ceil(KT / 8)): fp16 [NP][KT8][4][16][8],
+  entry [p][g][c][i][s] = scale of column 64p + 16c + i in group 8g + s
+  (0 for padding columns and for groups >= KT).
+* Zeros: uint32 [NP][KT8][4][16], bits [4s, 4s + 4) of [p][g][c][i] = zero
+  of column 64p + 16c + i in group 8g + s (0 for padding).
 """
 
 import numpy as np
@@ -72,11 +73,17 @@ def repack_ref(qweight, scales, qzeros, g_idx=None, group_size=GROUP):
     words = words.transpose(0, 3, 1, 5, 2, 4).reshape(NP, KT, 4, 64, 4)
     codes_r = np.ascontiguousarray(words).view(np.uint8).reshape(-1)
 
-    scales_r = sp.reshape(KT, NP, 4, 16).transpose(1, 0, 3, 2).copy()   # p t i c
-    zz = zp.reshape(KT, NP, 4, 16).transpose(1, 0, 3, 2).astype(np.uint16)  # p t i c
-    zeros_r = np.zeros((NP, KT, 16), dtype=np.uint16)
-    for c in range(4):
-        zeros_r |= zz[..., c] << np.uint16(4 * c)
+    KT8 = (KT + 7) // 8
+    sp8 = np.zeros((KT8 * 8, Np), dtype=np.float16)
+    sp8[:KT] = sp
+    zp8 = np.zeros((KT8 * 8, Np), dtype=np.uint32)
+    zp8[:KT] = zp
+    # [g s][p c i] -> [p][g][c][i][s]
+    scales_r = sp8.reshape(KT8, 8, NP, 4, 16).transpose(2, 0, 3, 4, 1).copy()
+    zz = zp8.reshape(KT8, 8, NP, 4, 16).transpose(2, 0, 3, 4, 1)          # p g c i s
+    zeros_r = np.zeros((NP, KT8, 4, 16), dtype=np.uint32)
+    for t8 in range(8):
+        zeros_r |= zz[..., t8] << np.uint32(4 * t8)
     return codes_r, scales_r.reshape(-1), zeros_r.reshape(-1), perm
 
 
@@ -92,11 +99,12 @@ def unrepack_ref(codes_r, scales_r, zeros_r, K, N):
     for e in range(8):
         v[..., e] = (words >> np.uint32(4 * nibble_slot(e))) & np.uint32(0xF)
     q = v.reshape(NP * 64, K)[:N]
-    s = np.asarray(scales_r, dtype=np.float16).reshape(NP, KT, 16, 4).transpose(1, 0, 3, 2)
-    s = s.reshape(KT, NP * 64)[:, :N]
-    zr = np.asarray(zeros_r, dtype=np.uint16).reshape(NP, KT, 16)
-    z = np.zeros((NP, KT, 16, 4), dtype=np.uint8)
-    for c in range(4):
-        z[..., c] = (zr >> np.uint16(4 * c)) & np.uint16(0xF)
-    z = z.transpose(1, 0, 3, 2).reshape(KT, NP * 64)[:, :N]
+    KT8 = (KT + 7) // 8
+    s8 = np.asarray(scales_r, dtype=np.float16).reshape(NP, KT8, 4, 16, 8)
+    s = s8.transpose(1, 4, 0, 2, 3).reshape(KT8 * 8, NP * 64)[:KT, :N]
+    zr = np.asarray(zeros_r, dtype=np.uint32).reshape(NP, KT8, 4, 16)
+    z8 = np.zeros((NP, KT8, 4, 16, 8), dtype=np.uint8)
+    for t8 in range(8):
+        z8[..., t8] = (zr >> np.uint32(4 * t8)) & np.uint32(0xF)
+    z = z8.transpose(1, 4, 0, 2, 3).reshape(KT8 * 8, NP * 64)[:KT, :N]
     return q.copy(), s.copy(), z.copy()

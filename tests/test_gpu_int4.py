@@ -35,7 +35,7 @@ def test_repack_bytes_equal_reference(N, K, act):
     ref = repack.repack_ref(qw.cpu().numpy(), sc.cpu().numpy(), qz.cpu().numpy(), gi)
     assert np.array_equal(packed["codes"].cpu().numpy(), ref[0])
     assert np.array_equal(tensor_bits(packed["scales"]), ref[1].view(np.uint16))
-    assert np.array_equal(packed["zeros"].cpu().numpy().view(np.uint16), ref[2])
+    assert np.array_equal(packed["zeros"].cpu().numpy().view(np.uint32), ref[2])
     if ref[3] is None:
         assert packed["perm"] is None
     else:
@@ -78,14 +78,14 @@ def test_dequant_special_scales_bit_exact(dtype):
     assert np.array_equal(got, want)
 
 
-def _run_gemm(tag, M, N, K, dtype, act=False, awq=False, use_ws=True, xscale=1.0):
+def _run_gemm(tag, M, N, K, dtype, act=False, awq=False, xscale=1.0):
     W, gi, s = int4_inputs(tag, N, K, act_order=act, awq=awq)
     x32 = synth.activations(tag + "/x", M, K) * np.float32(xscale)
     if awq:
         x32 = (x32 / s[None, :]).astype(np.float32)
     xb = synth.to_bits(x32, dtype)
     _, packed = gpu_int4_pack(W, gi)
-    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed, use_workspace=use_ws)
+    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed)
     torch.cuda.synchronize()
     return y, xb, W, gi, packed
 
@@ -119,14 +119,22 @@ def test_gemm_config1_tiny():
     assert err <= TOL
 
 
-@pytest.mark.parametrize("use_ws", [True, False])
-def test_gemm_split_and_unsplit_agree_with_oracle(use_ws):
+@pytest.mark.parametrize("act", [True, False])
+def test_gemm_long_k_sampled_columns(act):
     M, N, K = 4, 1024, 4096
-    say("split-K", use_ws)
-    y, xb, W, gi, _ = _run_gemm("gpu/gemm/split", M, N, K, "f16", act=True, use_ws=use_ws)
+    say("long K", act)
+    y, xb, W, gi, _ = _run_gemm("gpu/gemm/split", M, N, K, "f16", act=act)
     rows = np.arange(0, N, 7)
     wd = oracle_int4_rows(W, gi, rows, "f16")
     assert compare_gemm(y, xb, wd, "f16", cols=rows) <= TOL
+
+
+def test_gemm_perm_requires_workspace():
+    W, gi, _ = int4_inputs("gpu/gemm/nows", 64, 256, act_order=True)
+    _, packed = gpu_int4_pack(W, gi)
+    x = bits_to_tensor(synth.to_f16_bits(synth.activations("gpu/gemm/nows/x", 2, 256)), "f16")
+    with pytest.raises(w4.W4A16Error):
+        w4.w4a16_gemm(x, packed, use_workspace=False)
 
 
 def test_gemm_deterministic_and_scaling_exact():
@@ -144,7 +152,11 @@ def test_gemm_deterministic_and_scaling_exact():
     assert np.array_equal(y1, y2)
     y3 = w4.w4a16_gemm(bits_to_tensor(x2b, "f16"), packed).float().cpu().numpy()
     y1f = y1.view(np.float16).astype(np.float32)
-    assert np.array_equal(y3, 2 * y1f)
+    # doubling is exact through the fp32 accumulation; the final fp16 rounding
+    # commutes with it except in the fp16 subnormal range (absolute step 2^-24)
+    normal = np.abs(y1f) >= 2.0**-14
+    bad = np.nonzero(normal & (y3 != 2 * y1f))
+    assert bad[0].size == 0, list(zip(bad[0][:5], bad[1][:5], y1f[bad][:5], y3[bad][:5]))
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -174,3 +186,26 @@ def test_gemm_q_equals_z_gives_zero():
     x = bits_to_tensor(synth.to_f16_bits(synth.activations("gpu/qz/x", M, K)), "f16")
     y = w4.w4a16_gemm(x, packed)
     assert not torch.any(y.view(torch.int16) & 0x7FFF)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gemm_subnormal_activation_is_not_flushed(dtype):
+    # one-hot rows whose single nonzero is the smallest subnormal of the input
+    # type, against a weight column of large exact values: y = x * w is exact
+    # and far from underflow in the output, so a flushed input shows as 0.
+    N, K = 64, 256
+    q = np.full((N, K), 15, dtype=np.uint8)
+    z = np.zeros((K // 128, N), dtype=np.uint8)
+    s = np.full((K // 128, N), 1024.0, dtype=np.float16)       # w = 15 * 1024
+    packed = w4.w4a16_repack(torch.from_numpy(int4.pack_qweight(q)).to(DEV),
+                             torch.from_numpy(s.view(np.int16)).view(torch.float16).to(DEV),
+                             torch.from_numpy(int4.pack_qzeros(z)).to(DEV))
+    tiny = np.uint16(0x0001)                                    # smallest subnormal
+    xb = np.zeros((2, K), dtype=np.uint16)
+    xb[0, 3] = tiny
+    xb[1, 200] = tiny | 0x8000
+    y = tensor_f64(w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed), dtype)
+    sub = 2.0**-24 if dtype == "f16" else 2.0**-133
+    want = 15 * 1024.0 * sub          # 1.875 * 2^e: exact in both output types
+    assert np.all(y[0] == want), y[0][:4]
+    assert np.all(y[1] == -want)

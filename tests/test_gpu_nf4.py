@@ -74,3 +74,35 @@ def test_nf4_gemm_onehot_exact():
     y = tensor_bits(w4.nf4_gemm(bits_to_tensor(synth.to_bf16_bits(x), "bf16"), p))
     for r, k in enumerate(ks):
         assert np.array_equal(y[r], wd[:, k]), k
+
+
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 16, 40])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nf4_gemm_k_multiple_of_1024(M, dtype):
+    # K % 1024 == 0: the kernel reads the 16 absmax codes of 8 K tiles at once
+    N, K = 144, 3072
+    say("nf4 gemm k1024", M, dtype)
+    W = synth.weights("gpu/nf4k/W", N, K)
+    xb = synth.to_bits(synth.activations("gpu/nf4k/x/%d" % M, M, K), dtype)
+    p = _pack(W)
+    y = w4.nf4_gemm(bits_to_tensor(xb, dtype), p)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)
+    assert compare_gemm(y, xb, wd, dtype) <= TOL
+
+
+def test_nf4_gemm_onehot_exact_k1024():
+    N, K = 32, 1024
+    W = synth.weights("gpu/nf4/onehot1024", N, K)
+    p = _pack(W)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, "f16")
+    ks = [0, 127, 128, 500, 1023]
+    x = np.zeros((len(ks), K), dtype=np.float32)
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    y = tensor_bits(w4.nf4_gemm(bits_to_tensor(synth.to_f16_bits(x), "f16"), p))
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r], wd[:, k]), k

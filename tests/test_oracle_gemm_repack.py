@@ -72,18 +72,20 @@ def test_quantized_product_within_closed_form_bound_of_float_product():
 
 # ---------------------------------------------------------------- repack (P13)
 
+@pytest.mark.parametrize("K", [512, 1280, 2048])
 @pytest.mark.parametrize("N", [64, 200, 512])
 @pytest.mark.parametrize("act_order", [False, True])
-def test_repack_is_a_bijection(N, act_order):
-    K, G = 512, 128
-    W = synth.weights(f"test/repack/W/{N}", N, K)
-    gi = synth.act_order_gidx(f"test/repack/g/{N}", K, G) if act_order else None
+def test_repack_is_a_bijection(K, N, act_order):
+    G = 128
+    W = synth.weights(f"test/repack/W/{N}/{K}", N, K)
+    gi = synth.act_order_gidx(f"test/repack/g/{N}/{K}", K, G) if act_order else None
     q, s, z = int4.quantize_rtn_int4(W, G, gi)
     codes_r, scales_r, zeros_r, perm = repack.repack_ref(
         int4.pack_qweight(q), s, int4.pack_qzeros(z), gi)
     NP = (N + 63) // 64
+    KT8 = (K // G + 7) // 8
     assert codes_r.size == NP * (K // G) * 4096
-    assert scales_r.size == NP * (K // G) * 64 and zeros_r.size == NP * (K // G) * 16
+    assert scales_r.size == NP * KT8 * 512 and zeros_r.size == NP * KT8 * 64
     assert (perm is None) == (not act_order)
     q2, s2, z2 = repack.unrepack_ref(codes_r, scales_r, zeros_r, K, N)
     qp = q if perm is None else q[:, perm]
@@ -137,3 +139,23 @@ def test_page_facts_fixture():
     codes = K * N // 2
     meta = (K // G) * N * 2 + (K // G) * N // 2
     assert abs((codes + meta) / (2 * K * N) - 0.25) < 0.011
+
+
+def test_repack_meta_addressing_single_group():
+    # one nonzero scale / zero lands at the documented index and nibble
+    K, N, G = 1280, 128, 128
+    KT, KT8 = K // G, (K // G + 7) // 8
+    rr = np.random.default_rng(10)
+    for _ in range(30):
+        n, t = int(rr.integers(N)), int(rr.integers(KT))
+        s = np.zeros((KT, N), np.float16)
+        z = np.zeros((KT, N), np.uint8)
+        s[t, n] = 0.5
+        z[t, n] = 0xD
+        _, scales_r, zeros_r, _ = repack.repack_ref(
+            int4.pack_qweight(np.zeros((N, K), np.uint8)), s, int4.pack_qzeros(z))
+        p, c, i = n // 64, (n % 64) // 16, n % 16
+        g, s8 = t // 8, t % 8
+        idx = (((p * KT8 + g) * 4 + c) * 16 + i)
+        assert scales_r[idx * 8 + s8] == np.float16(0.5) and np.count_nonzero(scales_r) == 1
+        assert zeros_r[idx] == 0xD << (4 * s8) and np.count_nonzero(zeros_r) == 1
