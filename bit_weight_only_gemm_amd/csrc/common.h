@@ -9,8 +9,8 @@
 //  * fp16: the code is turned into the fp16 value 1024 + q by OR-ing it into
 //    the significand of 1024.0 (bits 0x6400 | q); subtracting 1024 + z is then
 //    exact, and one packed fp16 multiply by s rounds the exact product once.
-//  * bf16: there is no packed bf16 add on gfx950, so each code goes to fp32
-//    (v_cvt_f32_ubyte*), (q - z) * s is formed exactly in fp32 and
+//  * bf16: there is no packed bf16 add on gfx950; (q - z) is formed exactly in
+//    fp16 as above, widened, multiplied by s in fp32 (exact) and
 //    v_cvt_pk_bf16_f32 rounds two results at a time.
 //
 // Repacked word format: a 32-bit word holds the 8 codes of one column for 8
@@ -32,6 +32,22 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
+
+// 0x64006400 (two fp16 1024.0) held in a VGPR: a literal cannot be an operand
+// of the 3-operand v_and_or_b32 on gfx9, so without this the compiler splits
+// the nibble insert into v_and_b32 + v_or_b32.
+#ifndef W4A16_MAGIC_REG
+#define W4A16_MAGIC_REG 1
+#endif
+__device__ __forceinline__ uint32_t opaque_magic() {
+#if W4A16_MAGIC_REG
+  uint32_t m;
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(m));
+  return m;
+#else
+  return 0x64006400u;
+#endif
+}
 
 // 8-element MFMA operand type for a dtype.
 template <int DT> struct Op;
@@ -58,17 +74,27 @@ template <int DT> struct QParam;
 template <> struct QParam<DT_F16> {
   half2_t hz;  // (1024 + z) in both halves
   half2_t s2;  // s in both halves
+  uint32_t magic;  // 0x64006400 in a register, so the nibble insert is one v_and_or_b32
   __device__ __forceinline__ void set(uint32_t scale_bits, uint32_t z) {
+    magic = opaque_magic();
     uint32_t hzb = 0x6400u | z;
     hz = __builtin_bit_cast(half2_t, hzb | (hzb << 16));
     s2 = __builtin_bit_cast(half2_t, scale_bits | (scale_bits << 16));
   }
 };
 template <> struct QParam<DT_BF16> {
-  float zf, sf;
+  half2_t hz;  // (1024 + z) in both halves
+  float sf;    // s
+  float nz;    // -0.0, opaque to the compiler so that the fma below stays an fma
+  uint32_t magic;  // 0x64006400 in a register, so the nibble insert is one v_and_or_b32
   __device__ __forceinline__ void set(uint32_t scale_bits, uint32_t z) {
-    zf = (float)z;
+    magic = opaque_magic();
+    uint32_t hzb = 0x6400u | z;
+    hz = __builtin_bit_cast(half2_t, hzb | (hzb << 16));
     sf = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits);
+    uint32_t m;
+    asm("v_mov_b32 %0, 0x80000000" : "=v"(m));
+    nz = __builtin_bit_cast(float, m);
   }
 };
 
@@ -77,30 +103,50 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t w, const QParam<DT_F16>
   half2_t r[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;  // (1024+q_2i, 1024+q_2i+1)
+    uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;  // (1024+q_2i, 1024+q_2i+1)
     r[i] = (__builtin_bit_cast(half2_t, t) - p.hz) * p.s2;       // exact sub, one rounding
   }
   return half8_t{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
 }
 
 __device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, const QParam<DT_BF16>& p) {
-  // nibble slot s holds element e with s = (e >> 1) + 4 (e & 1):
-  //   lo = w & 0x0F0F0F0F  bytes = slots 0, 2, 4, 6 = elements 0, 4, 1, 5
-  //   hi = (w >> 4) & ...  bytes = slots 1, 3, 5, 7 = elements 2, 6, 3, 7
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  float f[8];
-  f[0] = (float)(lo & 0xFFu);
-  f[1] = (float)((lo >> 16) & 0xFFu);
-  f[2] = (float)(hi & 0xFFu);
-  f[3] = (float)((hi >> 16) & 0xFFu);
-  f[4] = (float)((lo >> 8) & 0xFFu);
-  f[5] = (float)((lo >> 24) & 0xFFu);
-  f[6] = (float)((hi >> 8) & 0xFFu);
-  f[7] = (float)((hi >> 24) & 0xFFu);
+  // (q - z) exactly in fp16 as on the fp16 path, then the exact fp32 product
+  // with s as fma(q - z, s, -0) (v_fma_mix widens the fp16 half in place;
+  // adding -0 keeps every signed zero of the plain product) and the one
+  // rounding to bf16.
   bf16x8_t out;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = (__bf16)((f[e] - p.zf) * p.sf);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;
+    const half2_t d = __builtin_bit_cast(half2_t, t) - p.hz;
+    out[2 * i] = (__bf16)__builtin_fmaf((float)d[0], p.sf, p.nz);
+    out[2 * i + 1] = (__bf16)__builtin_fmaf((float)d[1], p.sf, p.nz);
+  }
   return out;
+}
+
+// ---- raw buffer loads (gfx9-family descriptors).  A load whose per-lane
+// offset is at or past the descriptor's byte range returns 0, which is how
+// kernels read rows past M, codes past a tail and padding without branches;
+// every kernel keeps the in-range part of an address in the per-lane offset
+// and only a wave-uniform, in-range tile step in the scalar offset.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+// A per-lane offset past every descriptor's range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ u32x4_t bld128(rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bld32(rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bld16(rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
 // Round an fp32 value to the 16-bit output type and return its bits.

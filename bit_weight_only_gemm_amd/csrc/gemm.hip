@@ -41,6 +41,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace w4a16 {
 
@@ -52,25 +53,6 @@ constexpr int RUN = 8;                  // K tiles per meta run and ring pass
 
 enum { AM_PACKED = 0, AM_FULL = 1 };
 
-// Buffer resource word 3 for gfx9-family (CDNA) raw buffers.
-constexpr int kRsrcWord3 = 0x00020000;
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// A per-lane buffer offset past every descriptor's range: the load returns 0.
-// (Only the per-lane offset is relied on for range checks.)
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRsrcWord3);
-}
-__device__ __forceinline__ u32x4_t bld128(rsrc_t r, uint32_t voff, int soff) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint32_t bld32(rsrc_t r, uint32_t voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-
 // Timing events for the next main-kernel launch on this host thread (set by
 // w4a16_set_timing_events; consumed by one launch).
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
@@ -78,17 +60,6 @@ thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 void set_timing_events(hipEvent_t a, hipEvent_t b) {
   t_ev_start = a;
   t_ev_stop = b;
-}
-
-template <typename K, typename... Args>
-static void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
-  if (t_ev_start || t_ev_stop) {
-    hipEvent_t a = t_ev_start, b = t_ev_stop;
-    t_ev_start = t_ev_stop = nullptr;
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, a, b, 0, args...);
-  } else {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
-  }
 }
 
 // Multiply-accumulate the 4 MFMA steps of one K tile given its 4 B operands.
@@ -470,7 +441,7 @@ static void launch_int4_v(const void* x, const void* codes_r, const void* scales
                           const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  launch_timed(int4_decode_kernel<DT, MT, AM>, grid, dim3(64 * DW), stream, (const uint16_t*)x,
+  launch_timed(int4_decode_kernel<DT, MT, AM>, grid, dim3(64 * DW), 0, stream, (const uint16_t*)x,
                (const uint8_t*)codes_r, (const uint8_t*)scales_r, (const uint8_t*)zeros_r,
                (uint16_t*)out, (int)M, (int)N, (int)K, (int)(K / 128));
 }
@@ -502,7 +473,9 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
                        (const uint16_t*)x, perm, (uint16_t*)workspace, (int)M, (int)K);
     xa = workspace;
   }
-  if (dtype == DT_F16)
+  if (M >= kPrefillMinM)
+    launch_int4_prefill(xa, codes_r, scales_r, zeros_r, out, M, N, K, dtype, stream);
+  else if (dtype == DT_F16)
     launch_int4_dt<DT_F16>(xa, codes_r, scales_r, zeros_r, out, M, N, K, stream);
   else
     launch_int4_dt<DT_BF16>(xa, codes_r, scales_r, zeros_r, out, M, N, K, stream);
@@ -514,7 +487,7 @@ static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, con
                          const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), stream,
+  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), 0, stream,
                (const uint16_t*)x, q, aq, asc, L, (uint16_t*)out, (int)M, (int)N, (int)K,
                (int)ceil_div(K, 128));
 }

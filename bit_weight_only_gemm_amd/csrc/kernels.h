@@ -40,6 +40,15 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
                             const void* zeros_r, const int32_t* perm, void* out, int64_t M,
                             int64_t N, int64_t K, int dtype, void* workspace,
                             int64_t workspace_bytes, hipStream_t stream);
+// Rows from which w4a16_gemm uses the LDS-staged prefill kernel.
+#ifndef W4A16_PREFILL_MIN_M
+#define W4A16_PREFILL_MIN_M 256
+#endif
+constexpr int64_t kPrefillMinM = W4A16_PREFILL_MIN_M;
+void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
+                         const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
+                         int dtype, hipStream_t stream);
+
 hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,
                            int64_t N, int64_t K, int dtype, void* workspace,

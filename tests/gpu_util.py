@@ -53,8 +53,8 @@ def gpu_int4_pack(W, gi):
 
 
 def oracle_int4_rows(W, gi, rows, dtype):
-    """Oracle dequantized weights for a subset of output rows, in the
-    permuted column order the repacked layout uses (rows are independent)."""
+    """Oracle dequantized weights [len(rows), K] for a subset of output rows,
+    in the original input-column order (rows are quantized independently)."""
     q, s, z = int4.quantize_rtn_int4(W[rows], 128, gi)
     wd = int4.dequant_codes(q, s, z, gi, 128, dtype)
     return wd

@@ -1,0 +1,86 @@
+"""Parity of the large-M (prefill) INT4 kernel with the oracle.
+
+w4a16_gemm switches to the LDS-staged kernel for M >= 256 rows; these cases
+cover several 256 x 256 workgroup tiles, ragged row blocks (M % 256 != 0),
+a panel count that is not a multiple of 4 (N = 320 -> 5 panels), act-order,
+bf16 with outlier channels, and exact one-hot probes through the kernel.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_gemm_amd as w4
+from bit_weight_only_gemm_amd import synth
+from oracle.gemm import TOL
+from gpu_util import (say, bits_to_tensor, tensor_bits, int4_inputs, gpu_int4_pack,
+                      oracle_int4_rows, compare_gemm)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemm(tag, M, N, K, dtype, act=False, outliers=False):
+    W, gi, _ = int4_inputs(tag, N, K, act_order=act)
+    x32 = synth.activations(tag + "/x", M, K)
+    if outliers:
+        x32 = synth.with_outliers(x32, synth.outlier_channels(tag + "/outl", K))
+    xb = synth.to_bits(x32, dtype)
+    _, packed = gpu_int4_pack(W, gi)
+    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed)
+    torch.cuda.synchronize()
+    return y, xb, W, gi, packed
+
+
+@pytest.mark.parametrize("M", [256, 257, 600])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_ragged(M, dtype):
+    N, K = 320, 640
+    say("prefill", M, dtype)
+    y, xb, W, gi, _ = _gemm("gpu/pf/%d" % M, M, N, K, dtype)
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    assert compare_gemm(y, xb, wd, dtype) <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_act_order(dtype):
+    M, N, K = 300, 512, 1024
+    say("prefill act", dtype)
+    y, xb, W, gi, _ = _gemm("gpu/pf/act", M, N, K, dtype, act=True)
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    assert compare_gemm(y, xb, wd, dtype) <= TOL
+
+
+def test_prefill_bf16_outlier_channels_sampled_columns():
+    # bf16 activations with 1 % of input channels x20, several K tiles and
+    # row blocks; the oracle checks every 5th output column
+    M, N, K = 1024, 1280, 2560
+    say("prefill outliers")
+    y, xb, W, gi, _ = _gemm("gpu/pf/outl", M, N, K, "bf16", outliers=True)
+    cols = np.arange(0, N, 5)
+    wd = oracle_int4_rows(W, gi, cols, "bf16")
+    assert compare_gemm(y, xb, wd, "bf16", cols=cols) <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_onehot_exact(dtype):
+    # 256 one-hot rows: every output equals one dequantized weight bit for bit
+    N, K = 320, 512
+    W, gi, _ = int4_inputs("gpu/pf/onehot", N, K, act_order=True)
+    _, packed = gpu_int4_pack(W, gi)
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    M = 256
+    ks = (np.arange(M) * 37) % K
+    x = np.zeros((M, K), dtype=np.float32)
+    x[np.arange(M), ks] = 1.0
+    y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, dtype), dtype), packed))
+    assert np.array_equal(y, wd[:, ks].T)
+
+
+def test_prefill_deterministic():
+    M, N, K = 512, 256, 1024
+    W, gi, _ = int4_inputs("gpu/pf/det", N, K)
+    _, packed = gpu_int4_pack(W, gi)
+    x = bits_to_tensor(synth.to_bf16_bits(synth.activations("gpu/pf/det/x", M, K)), "bf16")
+    y1 = tensor_bits(w4.w4a16_gemm(x, packed))
+    y2 = tensor_bits(w4.w4a16_gemm(x, packed))
+    assert np.array_equal(y1, y2)
