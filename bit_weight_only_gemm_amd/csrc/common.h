@@ -98,31 +98,33 @@ template <> struct QParam<DT_BF16> {
   }
 };
 
-// Exact dequantization of one repacked word into an 8-element MFMA operand.
-__device__ __forceinline__ half8_t dequant_word(uint32_t w, const QParam<DT_F16>& p) {
-  half2_t r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;  // (1024+q_2i, 1024+q_2i+1)
-    r[i] = (__builtin_bit_cast(half2_t, t) - p.hz) * p.s2;       // exact sub, one rounding
-  }
-  return half8_t{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+// Exact dequantization of element pair i (elements 2i, 2i + 1, nibble slots
+// i and i + 4) of one repacked word, returned as two packed 16-bit values.
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QParam<DT_F16>& p) {
+  const uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;  // (1024+q_2i, 1024+q_2i+1)
+  const half2_t r = (__builtin_bit_cast(half2_t, t) - p.hz) * p.s2;  // exact sub, one rounding
+  return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ bf16x8_t dequant_word(uint32_t w, const QParam<DT_BF16>& p) {
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QParam<DT_BF16>& p) {
   // (q - z) exactly in fp16 as on the fp16 path, then the exact fp32 product
   // with s as fma(q - z, s, -0) (v_fma_mix widens the fp16 half in place;
   // adding -0 keeps every signed zero of the plain product) and the one
   // rounding to bf16.
-  bf16x8_t out;
+  const uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;
+  const half2_t d = __builtin_bit_cast(half2_t, t) - p.hz;
+  const bf16x2_t r = {(__bf16)__builtin_fmaf((float)d[0], p.sf, p.nz),
+                      (__bf16)__builtin_fmaf((float)d[1], p.sf, p.nz)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Exact dequantization of one repacked word into an 8-element MFMA operand.
+template <int DT>
+__device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const QParam<DT>& p) {
+  u32x4_t r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;
-    const half2_t d = __builtin_bit_cast(half2_t, t) - p.hz;
-    out[2 * i] = (__bf16)__builtin_fmaf((float)d[0], p.sf, p.nz);
-    out[2 * i + 1] = (__bf16)__builtin_fmaf((float)d[1], p.sf, p.nz);
-  }
-  return out;
+  for (int i = 0; i < 4; ++i) r[i] = dequant_pair(w, i, p);
+  return __builtin_bit_cast(typename Op<DT>::vec, r);
 }
 
 // ---- raw buffer loads (gfx9-family descriptors).  A load whose per-lane

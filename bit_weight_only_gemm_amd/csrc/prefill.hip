@@ -5,20 +5,26 @@
 // M large enough that the multiply, not the weight stream, bounds the call.
 //
 //  * One workgroup computes a 256 x 256 output tile with 4 waves; wave w owns
-//    the 64-column panel 4 bx + w for all 256 rows (16 x 4 MFMA tiles of
-//    16 x 16, fp32 accumulators).
+//    the 64-column panel 4 bx + w for all 256 rows: 8 x 2 tiles of 32 x 32 on
+//    v_mfma_f32_32x32x16_{f16,bf16} (on gfx950 this shape sustains a much
+//    higher fraction of the matrix peak than 16x16x32), fp32 accumulators.
 //  * Activations: each K tile (128 inputs) of the 256 rows is loaded once per
-//    workgroup, 16 bytes per lane, and staged in LDS (64 KB per stage, two
-//    stages); the 16-byte chunk q of row r sits at chunk position q ^ (r & 15)
-//    of its 256-byte LDS row, so the MFMA operand reads (16 rows, one chunk
-//    each) hit distinct banks.
-//  * Weights: the repacked code tile is already the B operand layout of
-//    v_mfma_f32_16x16x32, so each wave loads its 4 column tiles straight into
-//    registers (one 16-byte load per lane each) and dequantizes them exactly
-//    with the routine of the dequant export.  Each weight is therefore read
-//    and dequantized once per workgroup, and B never passes through LDS.
+//    workgroup straight from HBM into LDS (buffer loads with an LDS
+//    destination, 16 bytes per lane; 64 KB per stage, two stages).  The
+//    16-byte chunk q of row r sits at chunk position q ^ (r & 15) of its
+//    256-byte LDS row, so the operand reads (32 rows x 2 chunks) hit distinct
+//    banks.
+//  * Weights: the repacked 1 KB code tiles (16 columns x 128 inputs) are read
+//    straight into registers.  The B operand of a 32 x 32 x 16 step is 8
+//    codes (one 32-bit word) per lane: column l & 31, inputs 8 (l >> 5) + e
+//    of the step.  Lane l therefore loads the 16 bytes that repacked lane
+//    (l & 15) + 16 (2 h2 + (l >> 5)) of column tile 2 g + ((l & 31) >> 4)
+//    holds, for h2 = 0 (even steps) and 1 (odd steps): word j of those is the
+//    operand of step 2 j + h2.  Each weight is read and dequantized exactly
+//    (the routine of the dequant export) once per workgroup; B never passes
+//    through LDS.
 //  * The loads of K tile t + 1 are issued before the MFMAs of tile t and land
-//    in the other LDS stage after them; one barrier per K tile.
+//    in the other LDS stage; one barrier per K tile.
 #include "common.h"
 #include "kernels.h"
 #include "launch.h"
@@ -27,12 +33,46 @@ namespace w4a16 {
 
 constexpr int PF_WAVES = 4;                  // waves per workgroup
 constexpr int PF_BM = 256;                   // rows per workgroup
-constexpr int PF_MT = PF_BM / 16;            // 16-row MFMA tiles per wave
+constexpr int PF_MT = PF_BM / 32;            // 32-row MFMA tiles per wave
 constexpr int PF_ROWB = 256;                 // LDS bytes of one row of a K tile
 constexpr int PF_STAGE = PF_BM * PF_ROWB;    // 64 KB
 constexpr int PF_ALD = PF_BM * 16 / (64 * PF_WAVES);  // 16-byte A chunks per thread
 
+#ifndef W4A16_PF_APF
+#define W4A16_PF_APF 1
+#endif
+#ifndef W4A16_PF_SGB
+#define W4A16_PF_SGB 1
+#endif
+
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
 template <int DT>
+__device__ __forceinline__ float16_t mfma32x32x16(const typename Op<DT>::vec& a,
+                                                  const typename Op<DT>::vec& b,
+                                                  const float16_t& c);
+template <>
+__device__ __forceinline__ float16_t mfma32x32x16<DT_F16>(const half8_t& a, const half8_t& b,
+                                                          const float16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ float16_t mfma32x32x16<DT_BF16>(const bf16x8_t& a, const bf16x8_t& b,
+                                                           const float16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
+// lds + 16 l (the LDS base is wave-uniform).
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// TAIL: the row block may hold fewer than 256 rows; the row of each load is
+// then part of the per-lane offset so that rows past M read 0.  Full blocks
+// put it in the scalar offset (fewer registers).
+template <int DT, bool TAIL>
 __global__ void __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
 int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
@@ -43,130 +83,196 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row0 = blockIdx.y * PF_BM;
+  const int row0 = (TAIL ? M / PF_BM : blockIdx.y) * PF_BM;
   const int p = blockIdx.x * PF_WAVES + wave;  // this wave's 64-column panel
   const int KT8 = (KT + 7) >> 3;
+  const int i16 = lane & 15, h = lane >> 5;
 
-  // ---- activations: rows row0 .. row0 + vrows - 1 of x; rows past M read 0
+  // ---- activations: rows row0 .. row0 + vrows - 1 of x; rows past M read 0.
+  // Instruction i of wave w fills the 1 KB LDS block 4 i + w (rows
+  // 16 i + 4 w .. + 3), lane l writing position (l & 15) of row
+  // 16 i + 4 w + (l >> 4), which holds chunk (l & 15) ^ (row & 15): the
+  // swizzle is applied on the global side.
   const int vrows = min(PF_BM, M - row0);
   const rsrc_t rx = make_rsrc(x + (size_t)row0 * K, (uint32_t)vrows * (uint32_t)K * 2u);
-  // thread's chunks: row i * 16 + ar, chunk aq (i = 0 .. PF_ALD - 1)
-  const int aq = tid & 15, ar = tid >> 4;
   const uint32_t arow_bytes = (uint32_t)K * 2u;
-  const uint32_t avoff = (uint32_t)ar * arow_bytes + (uint32_t)aq * 16u;
+  const int arow0 = 4 * wave + (lane >> 4);  // row & 15 of every instruction's row
+  const uint32_t avoff = (uint32_t)arow0 * arow_bytes + (uint32_t)((i16 ^ arow0) << 4);
   const uint32_t astride = 16u * arow_bytes;
-  const int aw = ar * PF_ROWB + ((aq ^ ar) << 4);  // (i * 16 + ar) & 15 == ar
 
-  // ---- weights of panel p (all loads return 0 for a panel past the last)
+  // ---- weights of panel p (all loads return 0 for a panel past the last).
+  // Column group g (32 columns): column tile 2 g + ((l & 31) >> 4), entry
+  // l & 15 of its meta.
   const bool pv = p < NP;
   const size_t pp = pv ? (size_t)p : 0;
   const rsrc_t rc = make_rsrc(codes + pp * KT * 4096, pv ? (uint32_t)KT * 4096u : 0u);
   const rsrc_t rs = make_rsrc(scales + pp * KT8 * 1024, pv ? (uint32_t)KT8 * 1024u : 0u);
   const rsrc_t rz = make_rsrc(zeros + pp * KT8 * 256, pv ? (uint32_t)KT8 * 256u : 0u);
-  const int i16 = lane & 15;
+  uint32_t vcode[2][2], vmeta[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int ct = 2 * g + ((lane & 31) >> 4);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      vcode[g][h2] = (uint32_t)(ct * 1024 + (i16 + 16 * (2 * h2 + h)) * 16);
+    vmeta[g] = (uint32_t)(ct * 16 + i16);
+  }
 
-  float4_t acc[PF_MT][4];
+  float16_t acc[PF_MT][2];
 #pragma unroll
   for (int m = 0; m < PF_MT; ++m)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[m][c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < 2; ++g) acc[m][g] = float16_t{};
 
-  u32x4_t ast[PF_ALD];
-  u32x4_t cw[4], cn[4];
-  uint32_t sc[4], zz[4], sn[4], zn[4];
+  u32x4_t cw[2][2], cn[2][2];
+  uint32_t sc[2], zz[2], sn[2], zn[2];
 
   // ---- prologue: K tile 0
 #pragma unroll
-  for (int i = 0; i < PF_ALD; ++i) ast[i] = bld128(rx, avoff + (uint32_t)i * astride, 0);
+  for (int g = 0; g < 2; ++g) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    cw[c] = bld128(rc, (uint32_t)(c * 1024 + lane * 16), 0);
-    sc[c] = bld16(rs, (uint32_t)((c * 16 + i16) * 16), 0);
-    zz[c] = bld32(rz, (uint32_t)((c * 16 + i16) * 4), 0);
+    for (int h2 = 0; h2 < 2; ++h2) cw[g][h2] = bld128(rc, vcode[g][h2], 0);
+    sc[g] = bld16(rs, vmeta[g] * 16u, 0);
+    zz[g] = bld32(rz, vmeta[g] * 4u, 0);
   }
 #pragma unroll
-  for (int i = 0; i < PF_ALD; ++i) *(u32x4_t*)(As + aw + i * 16 * PF_ROWB) = ast[i];
+  for (int i = 0; i < PF_ALD; ++i)
+    lds_dma16(rx, As + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
+              TAIL ? 0 : (int)((uint32_t)i * astride));
   __syncthreads();
 
   for (int t = 0; t < KT; ++t) {
-    // ---- issue K tile t + 1 (the last tile is re-read on the final pass)
+    // ---- issue K tile t + 1 (the last tile is re-read on the final pass);
+    // its activations go to LDS stage (t + 1) & 1, last read before the
+    // previous barrier
     const int tn = min(t + 1, KT - 1);
 #pragma unroll
-    for (int i = 0; i < PF_ALD; ++i)
-      ast[i] = bld128(rx, avoff + (uint32_t)i * astride, tn * 256);
+    for (int g = 0; g < 2; ++g) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      cn[c] = bld128(rc, (uint32_t)(c * 1024 + lane * 16), tn * 4096);
-      sn[c] = bld16(rs, (uint32_t)((c * 16 + i16) * 16), (tn >> 3) * 1024 + (tn & 7) * 2);
-      zn[c] = bld32(rz, (uint32_t)((c * 16 + i16) * 4), (tn >> 3) * 256);
+      for (int h2 = 0; h2 < 2; ++h2) cn[g][h2] = bld128(rc, vcode[g][h2], tn * 4096);
+      sn[g] = bld16(rs, vmeta[g] * 16u, (tn >> 3) * 1024 + (tn & 7) * 2);
+      zn[g] = bld32(rz, vmeta[g] * 4u, (tn >> 3) * 256);
     }
+    uint8_t* sw = As + ((t + 1) & 1) * PF_STAGE;
+#pragma unroll
+    for (int i = 0; i < PF_ALD; ++i)
+      lds_dma16(rx, sw + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
+                TAIL ? tn * 256 : (int)((uint32_t)i * astride) + tn * 256);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- K tile t from LDS stage t & 1
-    QParam<DT> qp[4];
+    // ---- K tile t from LDS stage t & 1: 8 steps of 16 inputs.  Per step the
+    // operand reads come first; the dequant of the next step's B operand is
+    // spread between the step's MFMAs (each 32 x 32 x 16 MFMA keeps the matrix
+    // pipe busy long enough to issue several VALU instructions behind it).
+    QParam<DT> qp[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qp[c].set(sc[c] & 0xFFFFu, (zz[c] >> (4 * (t & 7))) & 0xFu);
+    for (int g = 0; g < 2; ++g) qp[g].set(sc[g] & 0xFFFFu, (zz[g] >> (4 * (t & 7))) & 0xFu);
     const uint8_t* st = As + (t & 1) * PF_STAGE;
+    auto read_step = [&](int s, vec (&a)[PF_MT]) {
+      const int q = 2 * s + h;  // 8-element chunk of this lane's inputs
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      vec b[4];
+      for (int m = 0; m < PF_MT; ++m)
+        a[m] = *(const vec*)(st + (m * 32 + (lane & 31)) * PF_ROWB + ((q ^ i16) << 4));
+    };
+    vec b[2], a[PF_MT];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) b[c] = dequant_word(cw[c][j], qp[c]);
-      const int q = 4 * j + (lane >> 4);  // chunk of step j for this lane's K group
+    for (int g = 0; g < 2; ++g) b[g] = dequant_word(cw[g][0][0], qp[g]);
+    read_step(0, a);
 #pragma unroll
-      for (int m = 0; m < PF_MT; ++m) {
-        const vec a = *(const vec*)(st + (m * 16 + i16) * PF_ROWB + ((q ^ i16) << 4));
+    for (int s = 0; s < 8; ++s) {
+      vec bn[2], an[PF_MT];
+      if (s < 7) {
+        const int sn1 = s + 1;
+#if W4A16_PF_APF
+        read_step(sn1, an);
+#endif
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[m][c] = mfma16x16x32<DT>(a, b[c], acc[m][c]);
+        for (int g = 0; g < 2; ++g) bn[g] = dequant_word(cw[g][sn1 & 1][sn1 >> 1], qp[g]);
+      }
+#pragma unroll
+      for (int m = 0; m < PF_MT; ++m)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) acc[m][g] = mfma32x32x16<DT>(a[m], b[g], acc[m][g]);
+#if W4A16_PF_SGB
+      if (s < 7) {
+#pragma unroll
+        for (int k = 0; k < 2 * PF_MT; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+#if W4A16_PF_APF
+          if (k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+#endif
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
+        }
+      }
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 7) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) b[g] = bn[g];
+#if W4A16_PF_APF
+#pragma unroll
+        for (int m = 0; m < PF_MT; ++m) a[m] = an[m];
+#else
+        read_step(s + 1, a);
+        __builtin_amdgcn_sched_barrier(0);
+#endif
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    // ---- stage K tile t + 1 (stage (t + 1) & 1 was last read before the
-    // previous barrier)
-    uint8_t* sw = As + ((t + 1) & 1) * PF_STAGE;
 #pragma unroll
-    for (int i = 0; i < PF_ALD; ++i) *(u32x4_t*)(sw + aw + i * 16 * PF_ROWB) = ast[i];
+    for (int g = 0; g < 2; ++g) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      cw[c] = cn[c];
-      sc[c] = sn[c];
-      zz[c] = zn[c];
+      for (int h2 = 0; h2 < 2; ++h2) cw[g][h2] = cn[g][h2];
+      sc[g] = sn[g];
+      zz[g] = zn[g];
     }
-    __syncthreads();
+    __syncthreads();  // the LDS writes of tile t + 1 are complete (vmcnt) and visible
   }
 
-  // ---- epilogue: element e of lane l is row 4 (l >> 4) + e, column l & 15
+  // ---- epilogue: register r of lane l is row (r & 3) + 4 (l >> 5) + 8 (r >> 2),
+  // column l & 31 of the 32 x 32 tile
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int col = p * 64 + c * 16 + i16;
+  for (int g = 0; g < 2; ++g) {
+    const int col = p * 64 + g * 32 + (lane & 31);
     if (col < N) {
 #pragma unroll
       for (int m = 0; m < PF_MT; ++m) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = row0 + m * 16 + 4 * (lane >> 4) + e;
-          if (row < M) out[(size_t)row * N + col] = round16<DT>(acc[m][c][e]);
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + m * 32 + (r & 3) + 4 * h + 8 * (r >> 2);
+          if (row < M) out[(size_t)row * N + col] = round16<DT>(acc[m][g][r]);
         }
       }
     }
   }
 }
 
+template <int DT>
+static void launch_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
+                              const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream) {
+  const int64_t NP = ceil_div(N, 64);
+  const int KT = (int)(K / 128);
+  const unsigned gx = (unsigned)ceil_div(NP, PF_WAVES);
+  const int64_t full = M / PF_BM;
+  if (full > 0)
+    launch_timed(int4_prefill_kernel<DT, false>, dim3(gx, (unsigned)full), dim3(64 * PF_WAVES), 0,
+                 stream, (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
+                 (const uint8_t*)zeros_r, (uint16_t*)out, (int)M, (int)N, (int)K, KT, (int)NP);
+  if (M % PF_BM)
+    hipLaunchKernelGGL((int4_prefill_kernel<DT, true>), dim3(gx, 1), dim3(64 * PF_WAVES), 0, stream,
+                       (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
+                       (const uint8_t*)zeros_r, (uint16_t*)out, (int)M, (int)N, (int)K, KT,
+                       (int)NP);
+}
+
 void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
                          const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
                          int dtype, hipStream_t stream) {
-  const int64_t NP = ceil_div(N, 64);
-  const dim3 grid((unsigned)ceil_div(NP, PF_WAVES), (unsigned)ceil_div(M, PF_BM));
-  const int KT = (int)(K / 128);
   if (dtype == DT_F16)
-    launch_timed(int4_prefill_kernel<DT_F16>, grid, dim3(64 * PF_WAVES), 0, stream,
-                 (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
-                 (const uint8_t*)zeros_r, (uint16_t*)out, (int)M, (int)N, (int)K, KT, (int)NP);
+    launch_prefill_dt<DT_F16>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
   else
-    launch_timed(int4_prefill_kernel<DT_BF16>, grid, dim3(64 * PF_WAVES), 0, stream,
-                 (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
-                 (const uint8_t*)zeros_r, (uint16_t*)out, (int)M, (int)N, (int)K, KT, (int)NP);
+    launch_prefill_dt<DT_BF16>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
 }
 
 }  // namespace w4a16
