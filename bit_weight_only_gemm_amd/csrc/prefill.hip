@@ -38,6 +38,10 @@ constexpr int PF_ROWB = 256;                 // LDS bytes of one row of a K tile
 constexpr int PF_STAGE = PF_BM * PF_ROWB;    // 64 KB
 constexpr int PF_ALD = PF_BM * 16 / (64 * PF_WAVES);  // 16-byte A chunks per thread
 
+#ifndef W4A16_PF_DMA_STEPS
+#define W4A16_PF_DMA_STEPS 8
+#endif
+constexpr int PF_DMA_STEPS = W4A16_PF_DMA_STEPS;  // steps the activation loads spread over
 #ifndef W4A16_PF_APF
 #define W4A16_PF_APF 1
 #endif
@@ -154,10 +158,13 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
       zn[g] = bld32(rz, vmeta[g] * 4u, (tn >> 3) * 256);
     }
     uint8_t* sw = As + ((t + 1) & 1) * PF_STAGE;
-#pragma unroll
-    for (int i = 0; i < PF_ALD; ++i)
+    // the activation loads of tile t + 1 are spread over the first
+    // PF_DMA_STEPS steps of tile t (a burst of them stalls the issuing waves
+    // behind the address queue)
+    auto issue_dma = [&](int i) {
       lds_dma16(rx, sw + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
                 TAIL ? tn * 256 : (int)((uint32_t)i * astride) + tn * 256);
+    };
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- K tile t from LDS stage t & 1: 8 steps of 16 inputs.  Per step the
@@ -181,6 +188,11 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       vec bn[2], an[PF_MT];
+      constexpr int DPS = PF_ALD / PF_DMA_STEPS;  // activation loads per step
+      if (s < PF_DMA_STEPS) {
+#pragma unroll
+        for (int i = 0; i < DPS; ++i) issue_dma(s * DPS + i);
+      }
       if (s < 7) {
         const int sn1 = s + 1;
 #if W4A16_PF_APF
@@ -198,6 +210,8 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 #pragma unroll
         for (int k = 0; k < 2 * PF_MT; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          if (s < PF_DMA_STEPS && k < PF_ALD / PF_DMA_STEPS)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one activation load
 #if W4A16_PF_APF
           if (k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
 #endif
