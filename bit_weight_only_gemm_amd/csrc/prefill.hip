@@ -188,11 +188,11 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       vec bn[2], an[PF_MT];
-      constexpr int DPS = PF_ALD / PF_DMA_STEPS;  // activation loads per step
-      if (s < PF_DMA_STEPS) {
+      // loads i with i * PF_DMA_STEPS / PF_ALD == s go out in step s
+      const int i0 = (s * PF_ALD + PF_DMA_STEPS - 1) / PF_DMA_STEPS;
+      const int i1 = ((s + 1) * PF_ALD + PF_DMA_STEPS - 1) / PF_DMA_STEPS;
 #pragma unroll
-        for (int i = 0; i < DPS; ++i) issue_dma(s * DPS + i);
-      }
+      for (int i = i0; i < i1 && i < PF_ALD; ++i) issue_dma(i);
       if (s < 7) {
         const int sn1 = s + 1;
 #if W4A16_PF_APF
@@ -210,7 +210,7 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 #pragma unroll
         for (int k = 0; k < 2 * PF_MT; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          if (s < PF_DMA_STEPS && k < PF_ALD / PF_DMA_STEPS)
+          if (k < i1 - i0 && i0 < PF_ALD)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one activation load
 #if W4A16_PF_APF
           if (k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
