@@ -197,7 +197,8 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
   if (int s = check_ptrs({x, codes_r, scales_r, zeros_r, out})) return s;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
   if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
-  if (perm && (!workspace || workspace_bytes < int4_workspace_bytes(M, N, K)))
+  const int64_t need = perm ? int4_workspace_bytes(M, N, K) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
   return hip_status(launch_int4_gemm(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, dtype,
                                      workspace, workspace_bytes, (hipStream_t)stream));

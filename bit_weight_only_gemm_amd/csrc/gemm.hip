@@ -51,7 +51,17 @@ namespace w4a16 {
 constexpr int DW = W4A16_DECODE_WAVES;  // waves per decode workgroup
 constexpr int RUN = 8;                  // K tiles per meta run and ring pass
 
-enum { AM_PACKED = 0, AM_FULL = 1 };
+// Activation modes.  PACKED: M <= 4, one 16-byte load per lane and K tile
+// carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
+// tile.  XLDS / XGATHER: PACKED with the M rows of x staged in LDS once per
+// workgroup (and, for XGATHER, the act-order permutation too: the operand is
+// gathered from LDS, x[m][perm[k]], so no separate permutation pass runs).
+enum { AM_PACKED = 0, AM_FULL = 1, AM_XLDS = 2, AM_XGATHER = 3 };
+constexpr bool is_packed(int am) { return am != AM_FULL; }
+
+// Largest LDS footprint of the staged activations (+ permutation): with the
+// reduction buffer, two workgroups still fit a CU's 160 KB.
+constexpr int64_t kMaxXlds = 72 * 1024;
 
 // Timing events for the next main-kernel launch on this host thread (set by
 // w4a16_set_timing_events; consumed by one launch).
@@ -69,7 +79,7 @@ __device__ __forceinline__ void mma_tile(const typename Op<DT>::vec b[4],
                                          float4_t (&acc)[NACC]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if constexpr (AM == AM_PACKED) {
+    if constexpr (is_packed(AM)) {
       acc[j] = mfma16x16x32<DT>(a[0], b[j], acc[j]);
     } else {
 #pragma unroll
@@ -238,11 +248,45 @@ struct Nf4W {
 // step j of batch row m.  FULL: MT x 4 vectors (row tile m, step j), lane row
 // r = batch row.  Rows >= M read 0 through the descriptor range; k >= K (only
 // in a half NF4 tile) uses an out-of-range offset.
+// Staged activations in LDS: x rows [M][K] at xl, the permutation int32[K] at
+// pl (XGATHER), 16 zero bytes at zoff (for the inputs past K of a half NF4
+// tile).
+struct XLds {
+  const uint8_t* xl;
+  const int32_t* pl;
+  uint32_t zoff;
+  int M;
+};
+
 template <int DT, int AM, int MT, int NA, class WP>
 __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
-                                       typename Op<DT>::vec (&a)[NA]) {
+                                       typename Op<DT>::vec (&a)[NA], const XLds& xs) {
+  typedef typename Op<DT>::vec vec;
   const int r = lane & 15, b = lane >> 4;
-  if constexpr (AM == AM_PACKED) {
+  if constexpr (AM == AM_XLDS || AM == AM_XGATHER) {
+    // rows m >= M only feed output rows that are never stored, so they read
+    // row M - 1 instead of zeros
+    const int j = r >> 2, m = min(r & 3, xs.M - 1);
+    const int kg = t * 128 + WP::xk(j, b);
+    if constexpr (AM == AM_XLDS) {
+      uint32_t off = ((uint32_t)m * (uint32_t)K + (uint32_t)kg) * 2u;
+      if constexpr (WP::kRaggedK) off = kg < K ? off : xs.zoff;
+      a[0] = *(const vec*)(xs.xl + off);
+    } else {
+      const u32x4_t p0 = *(const u32x4_t*)(xs.pl + kg);
+      const u32x4_t p1 = *(const u32x4_t*)(xs.pl + kg + 4);
+      const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = *(const uint16_t*)(row + p0[e] * 2u);
+        v[4 + e] = *(const uint16_t*)(row + p1[e] * 2u);
+      }
+      const u32x4_t w = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                         v[6] | (v[7] << 16)};
+      a[0] = __builtin_bit_cast(vec, w);
+    }
+  } else if constexpr (AM == AM_PACKED) {
     const int j = r >> 2, m = r & 3;
     const int kin = WP::xk(j, b);
     uint32_t off = (uint32_t)m * (uint32_t)K * 2u + (uint32_t)kin * 2u;
@@ -263,13 +307,40 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
   }
 }
 
+// Bytes of LDS the staged activations (+ permutation) take: x rows, the
+// permutation, 16 zero bytes, each region rounded up to whole 1 KB blocks.
+__host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
+  return (uint32_t)((M * K * 2 + 1023) / 1024 * 1024);
+}
+__host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool gather) {
+  return xlds_x_bytes(M, K) + (gather ? (uint32_t)((K * 4 + 1023) / 1024 * 1024) : 0u) + 16u;
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
+// lds + 16 l (the LDS base is wave-uniform).
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Copy `bytes` (rounded up to 1 KB; the tail reads 0 through the descriptor
+// range) from `src` to LDS, 1 KB per wave instruction.
+__device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8_t* lds,
+                                          int wave, int lane) {
+  const rsrc_t r = make_rsrc(src, bytes);
+  const int nblk = (int)((bytes + 1023) / 1024);
+  for (int blk = wave; blk < nblk; blk += DW)
+    lds_dma16(r, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), 0);
+}
+
 template <int DT, int MT, int AM, class WP>
 __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& wp,
                                             uint16_t* __restrict__ out, int M, int N, int K,
-                                            int KT, float* red) {
-  constexpr int NA = AM == AM_PACKED ? 1 : MT * 4;                 // A vectors per tile
-  constexpr int NACC = AM == AM_PACKED ? 4 : MT;                   // accumulator tiles
-  constexpr int PA = AM == AM_PACKED ? RUN : (MT == 1 ? 2 : 1);    // A ring depth
+                                            int KT, float* red, const int32_t* perm,
+                                            uint8_t* xlds) {
+  constexpr int NA = is_packed(AM) ? 1 : MT * 4;                   // A vectors per tile
+  constexpr int NACC = is_packed(AM) ? 4 : MT;                     // accumulator tiles
+  constexpr int PA = is_packed(AM) ? RUN : (MT == 1 ? 2 : 1);      // A ring depth
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ct = blockIdx.x;
@@ -286,37 +357,49 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
 #pragma unroll
   for (int q = 0; q < NACC; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Ring of RUN tiles: slot s holds tile i + s of the current pass.  All
-  // loads are issued from one program point: the first pass (i = -RUN) only
-  // fills the ring; later passes compute slot s and refill it with tile
-  // i + s + RUN (clamped into range: the tail re-reads the last tile from
-  // cache, and slots past the wave's range are not computed).  The meta of a
-  // run is double-buffered.  Scheduling barriers keep slot order in the
-  // instruction stream so each slot's wait covers only its own loads.
+  // Ring of RUN tiles: slot s holds tile i + s of the current pass.  The
+  // fill (tiles 0 .. RUN - 1 and the first run's meta) is issued first; each
+  // pass then computes slot s and refills it with tile i + s + RUN (clamped
+  // into range: the tail re-reads the last tile from cache, and slots past
+  // the wave's range are not computed).  The meta of a run is double-buffered.
+  // Scheduling barriers keep slot order in the instruction stream so each
+  // slot's wait covers only its own loads.
+  u32x4_t ring[RUN];
+  typename Op<DT>::vec ra[PA][NA];
+  typename WP::Meta mc, mn = WP::zero_meta();
+  XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), 0u, M};
   if (n > 0) {
-    u32x4_t ring[RUN];
-    typename Op<DT>::vec ra[PA][NA];
+    mn = wp.load_meta(r0);
 #pragma unroll
-    for (int s = 0; s < RUN; ++s) ring[s] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int s = 0; s < RUN; ++s) ring[s] = wp.load_codes(t0 + min(s, n - 1), lane);
+  }
+  if constexpr (AM == AM_XLDS || AM == AM_XGATHER) {
+    // every wave takes part in staging the M rows of x (and the permutation)
+    // while its first code tiles are in flight
+    xs.zoff = xlds_bytes(M, K, AM == AM_XGATHER) - 16u;
+    stage_lds(x, (uint32_t)(M * K * 2), xlds, wave, lane);
+    if constexpr (AM == AM_XGATHER)
+      stage_lds(perm, (uint32_t)(K * 4), xlds + xlds_x_bytes(M, K), wave, lane);
+    if (threadIdx.x == 0) *(u32x4_t*)(xlds + xs.zoff) = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+  if (n > 0) {
 #pragma unroll
-    for (int s = 0; s < PA; ++s)
-#pragma unroll
-      for (int q = 0; q < NA; ++q) ra[s][q] = typename Op<DT>::vec{};
-    typename WP::Meta mc, mn = WP::zero_meta();
-    for (int i = -RUN; i < n; i += RUN) {
+    for (int s = 0; s < PA; ++s) load_a<DT, AM, MT, NA, WP>(rx, K, t0 + min(s, n - 1), lane, ra[s], xs);
+    for (int i = 0; i < n; i += RUN) {
       mc = mn;
       mn = wp.load_meta(r0 + min(i / RUN + 1, (n - 1) / RUN));
 #pragma unroll
       for (int s = 0; s < RUN; ++s) {
         const int sa = s % PA;
-        if (i + s >= 0 && i + s < n) {  // wave-uniform
+        if (i + s < n) {  // wave-uniform
           typename Op<DT>::vec b[4];
           wp.operands(ring[s], s, mc, b);
           mma_tile<DT, AM, MT, NA, NACC>(b, ra[sa], acc);
         }
         __builtin_amdgcn_sched_barrier(0);
         ring[s] = wp.load_codes(t0 + min(i + s + RUN, n - 1), lane);
-        load_a<DT, AM, MT, NA, WP>(rx, K, t0 + max(0, min(i + s + PA, n - 1)), lane, ra[sa]);
+        load_a<DT, AM, MT, NA, WP>(rx, K, t0 + min(i + s + PA, n - 1), lane, ra[sa], xs);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -325,7 +408,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
   // ---- v_mfma_f32_16x16x32 result layout: element e of lane l is row
   // 4 (l >> 4) + e, column l & 15 of the 16x16 tile.
   float4_t res[MT];
-  if constexpr (AM == AM_PACKED) {
+  if constexpr (is_packed(AM)) {
     // rows 4g .. 4g+3 of step tile acc[g] (g = lane group) are batch rows
     // 0..3 of step g: take them and add the 4 lane groups (a shuffle
     // reduction across the wave); lane group 0 then holds rows 0..3.
@@ -373,14 +456,16 @@ template <int DT, int MT, int AM>
 __global__ void __launch_bounds__(64 * DW)
 int4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                    const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                   uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+                   const int32_t* __restrict__ perm, uint16_t* __restrict__ out, int M, int N,
+                   int K, int KT) {
   __shared__ float red[DW * MT * 64 * 4];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
   Int4W<DT> wp;
   wp.codes = codes;
   wp.scales = scales;
   wp.zeros = zeros;
   wp.KT = KT;
-  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red);
+  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red, perm, xlds);
 }
 
 template <int DT, int MT, int AM, bool BATCH>
@@ -392,12 +477,13 @@ nf4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
   __syncthreads();
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
   Nf4W<DT, BATCH> wp;
   wp.q = q;
   wp.aq = aq;
   wp.asc = asc;
   wp.lut = lut;
-  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red);
+  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red, nullptr, xlds);
 }
 
 // x_p[m, k] = x[m, perm[k]]: one thread per 8 consecutive permuted columns.
@@ -421,15 +507,26 @@ permute_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ per
 }
 
 // ---------------------------------------------------------------- planning --
-int64_t int4_workspace_bytes(int64_t M, int64_t /*N*/, int64_t K) {
-  // room for the permuted activations of an act-order weight
-  return ceil_div(M * K * 2, 256) * 256;
+
+// Raise a kernel's dynamic LDS limit to kMaxXlds (once per kernel; the call
+// is idempotent, so a race between host threads is harmless).
+static void allow_dynamic_lds(const void* kernel) {
+  static thread_local const void* done[32];
+  static thread_local int ndone = 0;
+  for (int i = 0; i < ndone; ++i)
+    if (done[i] == kernel) return;
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxXlds);
+  if (ndone < 32) done[ndone++] = kernel;
 }
 
-// Activation mode and row tiles per workgroup row block for M rows.
-static int pick_mode(int64_t M, int* mt) {
+// Activation mode and row tiles per workgroup row block for M rows; gather:
+// an act-order permutation is to be applied.
+static int pick_mode(int64_t M, int64_t K, bool gather, int* mt) {
   if (M <= 4) {
     *mt = 1;
+    // staging x alone in LDS does not beat per-tile loads; the gather pays
+    // for itself by saving the separate permutation pass
+    if (gather && xlds_bytes((int)M, (int)K, true) <= kMaxXlds) return AM_XGATHER;
     return AM_PACKED;
   }
   *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -438,36 +535,46 @@ static int pick_mode(int64_t M, int* mt) {
 
 template <int DT, int MT, int AM>
 static void launch_int4_v(const void* x, const void* codes_r, const void* scales_r,
-                          const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
-                          hipStream_t stream) {
+                          const void* zeros_r, const int32_t* perm, void* out, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  launch_timed(int4_decode_kernel<DT, MT, AM>, grid, dim3(64 * DW), 0, stream, (const uint16_t*)x,
-               (const uint8_t*)codes_r, (const uint8_t*)scales_r, (const uint8_t*)zeros_r,
-               (uint16_t*)out, (int)M, (int)N, (int)K, (int)(K / 128));
+  const size_t lds = (AM == AM_XLDS || AM == AM_XGATHER)
+                         ? xlds_bytes((int)M, (int)K, AM == AM_XGATHER)
+                         : 0;
+  if (lds) allow_dynamic_lds((const void*)int4_decode_kernel<DT, MT, AM>);
+  launch_timed(int4_decode_kernel<DT, MT, AM>, grid, dim3(64 * DW), lds, stream,
+               (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
+               (const uint8_t*)zeros_r, perm, (uint16_t*)out, (int)M, (int)N, (int)K,
+               (int)(K / 128));
 }
 
 template <int DT>
-static void launch_int4_dt(const void* x, const void* codes_r, const void* scales_r,
-                           const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
-                           hipStream_t stream) {
-  int mt;
-  const int am = pick_mode(M, &mt);
-  if (am == AM_PACKED)
-    launch_int4_v<DT, 1, AM_PACKED>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+static void launch_int4_dt(int am, int mt, const void* x, const void* codes_r,
+                           const void* scales_r, const void* zeros_r, const int32_t* perm,
+                           void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (am == AM_XGATHER)
+    launch_int4_v<DT, 1, AM_XGATHER>(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
+  else if (am == AM_XLDS)
+    launch_int4_v<DT, 1, AM_XLDS>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
+  else if (am == AM_PACKED)
+    launch_int4_v<DT, 1, AM_PACKED>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
   else if (mt == 1)
-    launch_int4_v<DT, 1, AM_FULL>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+    launch_int4_v<DT, 1, AM_FULL>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
   else if (mt == 2)
-    launch_int4_v<DT, 2, AM_FULL>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+    launch_int4_v<DT, 2, AM_FULL>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
   else
-    launch_int4_v<DT, 4, AM_FULL>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+    launch_int4_v<DT, 4, AM_FULL>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
 }
 
 hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scales_r,
                             const void* zeros_r, const int32_t* perm, void* out, int64_t M,
                             int64_t N, int64_t K, int dtype, void* workspace,
                             int64_t /*workspace_bytes*/, hipStream_t stream) {
+  int mt = 1;
+  const int am = M >= kPrefillMinM ? AM_FULL : pick_mode(M, K, perm != nullptr, &mt);
   const void* xa = x;
-  if (perm) {
+  if (perm && am != AM_XGATHER) {
+    // the activations are permuted once into the workspace
     const int64_t n8 = M * (K / 8);
     hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, stream,
                        (const uint16_t*)x, perm, (uint16_t*)workspace, (int)M, (int)K);
@@ -476,10 +583,18 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
   if (M >= kPrefillMinM)
     launch_int4_prefill(xa, codes_r, scales_r, zeros_r, out, M, N, K, dtype, stream);
   else if (dtype == DT_F16)
-    launch_int4_dt<DT_F16>(xa, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+    launch_int4_dt<DT_F16>(am, mt, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
   else
-    launch_int4_dt<DT_BF16>(xa, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+    launch_int4_dt<DT_BF16>(am, mt, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
   return hipGetLastError();
+}
+
+int64_t int4_workspace_bytes(int64_t M, int64_t /*N*/, int64_t K) {
+  // room for the permuted activations of an act-order weight, unless the
+  // kernel gathers them itself
+  int mt;
+  if (M < kPrefillMinM && pick_mode(M, K, true, &mt) == AM_XGATHER) return 0;
+  return ceil_div(M * K * 2, 256) * 256;
 }
 
 template <int DT, int MT, int AM, bool BATCH>
@@ -487,7 +602,9 @@ static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, con
                          const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), 0, stream,
+  const size_t lds = AM == AM_XLDS ? xlds_bytes((int)M, (int)K, false) : 0;
+  if (lds) allow_dynamic_lds((const void*)nf4_decode_kernel<DT, MT, AM, BATCH>);
+  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), lds, stream,
                (const uint16_t*)x, q, aq, asc, L, (uint16_t*)out, (int)M, (int)N, (int)K,
                (int)ceil_div(K, 128));
 }
@@ -497,8 +614,10 @@ static void launch_nf4_dt(const void* x, const uint8_t* q, const uint8_t* aq, co
                           const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream) {
   int mt;
-  const int am = pick_mode(M, &mt);
-  if (am == AM_PACKED)
+  const int am = pick_mode(M, K, false, &mt);
+  if (am == AM_XLDS)
+    launch_nf4_v<DT, 1, AM_XLDS, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+  else if (am == AM_PACKED)
     launch_nf4_v<DT, 1, AM_PACKED, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
   else if (mt == 1)
     launch_nf4_v<DT, 1, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);

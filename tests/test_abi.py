@@ -77,6 +77,13 @@ def test_gemm_validation_without_gpu():
     assert need >= 16 * 4096 * 2
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, FAKE, need - 16, NULL) == 5
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, NULL, 0, NULL) == 5
+    # M <= 4 with x and perm small enough to stage on chip: gathered in the
+    # kernel, no workspace
+    assert L.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
+    assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) == 0
+    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) == 0
+    assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) >= 4 * 11008 * 2
+    assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 5 * 4096 * 2
 
 
 def test_nf4_validation_without_gpu():

@@ -130,11 +130,30 @@ def test_gemm_long_k_sampled_columns(act):
 
 
 def test_gemm_perm_requires_workspace():
+    # M > 4: the activations are permuted into the workspace first
     W, gi, _ = int4_inputs("gpu/gemm/nows", 64, 256, act_order=True)
     _, packed = gpu_int4_pack(W, gi)
-    x = bits_to_tensor(synth.to_f16_bits(synth.activations("gpu/gemm/nows/x", 2, 256)), "f16")
+    x = bits_to_tensor(synth.to_f16_bits(synth.activations("gpu/gemm/nows/x", 8, 256)), "f16")
     with pytest.raises(w4.W4A16Error):
         w4.w4a16_gemm(x, packed, use_workspace=False)
+
+
+@pytest.mark.parametrize("M,K", [(1, 512), (2, 1024), (3, 2048), (4, 4096), (1, 11008),
+                                 (4, 11008)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_gemm_act_order_small_m(M, K, dtype):
+    # M <= 4: the kernel gathers x[:, perm] from on-chip staging without a
+    # workspace when it fits (the last case does not: permuted through the
+    # workspace); sampled columns at the larger K
+    N = 96
+    say("act-order small M", M, K, dtype)
+    W, gi, _ = int4_inputs("gpu/gemm/gather/%d" % K, N, K, act_order=True)
+    xb = synth.to_bits(synth.activations("gpu/gemm/gather/x/%d/%d" % (M, K), M, K), dtype)
+    _, packed = gpu_int4_pack(W, gi)
+    need = w4.w4a16_workspace_bytes(M, N, K)
+    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed, use_workspace=need > 0)
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    assert compare_gemm(y, xb, wd, dtype) <= TOL
 
 
 def test_gemm_deterministic_and_scaling_exact():
