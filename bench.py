@@ -48,9 +48,13 @@ def call_bytes(M, K, N):
     return weight_bytes(K, N, perm=False) + 2 * M * K + 2 * M * N
 
 
-def kernel_name(M):
-    """Decode-kernel instantiation the library picks for M rows (f16)."""
+def kernel_name(M, K, N):
+    """Decode-kernel instantiation the library picks for an act-order call
+    with M rows (f16): the in-kernel gather needs no workspace."""
+    import bit_weight_only_gemm_amd as w4
     if M <= 4:
+        if w4.w4a16_workspace_bytes(M, N, K) == 0:
+            return "int4_decode_kernel<f16, MT=1, xgather>"
         return "int4_decode_kernel<f16, MT=1, packed>"
     mt = 1 if M <= 16 else (2 if M <= 32 else 4)
     return "int4_decode_kernel<f16, MT=%d, full>" % mt
@@ -62,6 +66,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-nf4", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run each decode call of the workload once, then a 256 MiB device copy "
+                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), and exit")
     ap.add_argument("--min-rotation-mb", type=float, default=512.0)
     return ap.parse_args()
 
@@ -79,6 +88,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = _lib.load()
+    if args.pmc_probe:
+        pmc_probe(L, dev)
+        return
     stream = torch.cuda.Stream()          # graphs are captured on a non-default stream
     torch.cuda.set_stream(stream)
     sptr = ctypes.c_void_p(stream.cuda_stream)
@@ -196,7 +208,7 @@ def main():
     # the dominant kernel: the instantiation with the most time per step
     groups = {}
     for j, (K, N, M, _) in enumerate(rot[0]):
-        groups.setdefault(kernel_name(M), []).append(j)
+        groups.setdefault(kernel_name(M, K, N), []).append(j)
     dom = max(groups, key=lambda g: dur[:, groups[g]].sum())
     dj = groups[dom]
     avg_launch_s = float(dur[:, dj].mean())
@@ -205,7 +217,8 @@ def main():
     per_point = []
     for j, (K, N, M, _) in enumerate(rot[0]):
         d = float(dur[:, j].mean())
-        per_point.append({"M": M, "K": K, "N": N, "kernel": kernel_name(M), "us": round(d * 1e6, 2),
+        per_point.append({"M": M, "K": K, "N": N, "kernel": kernel_name(M, K, N),
+                          "us": round(d * 1e6, 2),
                           "weight_GBps": round(weight_bytes(K, N) / d / 1e9, 1),
                           "pct_hbm": round(100 * call_bytes(M, K, N) / d / 1e9 / HBM_PEAK_GBS, 1)})
 
@@ -227,7 +240,8 @@ def main():
             "workload": "Llama-2-7B-shaped decode GEMMs, GPTQ act-order int4 G=128: "
                         "(K,N) in {(4096,4096),(4096,11008),(11008,4096)} x M in {1,4,16}",
             "gemm_calls_per_step": nper,
-            "step_timing": "HIP graph replay per step (GEMM + act-order permutation kernels)",
+            "step_timing": "HIP graph replay per step (the GEMM kernels, plus the act-order "
+                           "permutation pass where the kernel does not gather itself)",
             "weight_rotation_copies": R,
             "tflops": round(step_flops / step_s / 1e12, 3),
             "pct_hbm_step": round(100 * step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 1),
@@ -242,7 +256,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
             "timing": "hipExtLaunchKernel start/stop events on every launch of this kernel "
                       "in K eager steps, on the stream it runs on",
@@ -250,12 +264,198 @@ def main():
         },
         "points": per_point,
     }
+    timer = KernelTimer(L, hip)
+    del rot, calls, graphs, base
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(L, timer, sptr)
+    if not args.no_nf4:
+        result["nf4"] = bench_nf4(L, timer, sptr)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(calls, rot, xs, outs)
+        result["cpu_baseline"] = cpu_baseline(xs, outs)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(calls, rot, xs, outs):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "int4_decode_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_only_gemm_amd", "csrc", f)
+                  for f in ("gemm.hip", "common.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None
+    when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def pmc_probe(L, dev):
+    """Each decode call of the workload once (act-order, one weight copy),
+    then a 256 MiB device-to-device copy whose byte count calibrates the
+    counters."""
+    import torch
+    import bit_weight_only_gemm_amd as w4
+    from bit_weight_only_gemm_amd import synth
+    for K, N in SHAPES:
+        W = torch.from_numpy(synth.weights("C2/W/%dx%d" % (K, N), N, K)).to(dev)
+        gi = torch.from_numpy(synth.act_order_gidx("C2/gidx/%dx%d" % (K, N), K, G)).to(dev)
+        qw, sc, qz = w4.w4a16_quantize_rtn(W, G, g_idx=gi)
+        p = w4.w4a16_repack(qw, sc, qz, gi)
+        del W, qw, sc, qz
+        for M in MS:
+            xb = synth.to_f16_bits(synth.activations("C2/x/%dx%d" % (M, K), M, K))
+            x = torch.from_numpy(xb.view(np.int16)).view(torch.float16).to(dev)
+            w4.w4a16_gemm(x, p)
+            torch.cuda.synchronize()
+            print("call M=%d K=%d N=%d kernel=%s algorithmic_bytes=%d"
+                  % (M, K, N, kernel_name(M, K, N), call_bytes(M, K, N)), flush=True)
+    src = torch.ones(64 * 2**20, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copy bytes_read=%d bytes_written=%d" % (src.numel() * 4, dst.numel() * 4), flush=True)
+
+
+class KernelTimer:
+    """Durations of the library's main kernel launch, from hipExtLaunchKernel
+    start/stop events (w4a16_set_timing_events) on the stream it runs on."""
+
+    def __init__(self, L, hip):
+        self.L, self.hip = L, hip
+        self.ev = (ctypes.c_void_p * 2)()
+        for k in range(2):
+            if hip.hipEventCreate(ctypes.byref(self.ev, k * ctypes.sizeof(ctypes.c_void_p))):
+                raise RuntimeError("hipEventCreate failed")
+
+    def time(self, call, reps, warm=3):
+        import torch
+        ts = []
+        ms = ctypes.c_float(0.0)
+        for r in range(warm + reps):
+            self.L.w4a16_set_timing_events(ctypes.c_void_p(self.ev[0]), ctypes.c_void_p(self.ev[1]))
+            if call() != 0:
+                raise RuntimeError("library call failed")
+            torch.cuda.synchronize()
+            self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[0]),
+                                         ctypes.c_void_p(self.ev[1]))
+            if r >= warm:
+                ts.append(ms.value * 1e-3)
+        return float(np.median(ts))
+
+
+PREFILL_SHAPES = [(5120, 7168), (5120, 5120), (5120, 55296), (27648, 5120)]   # (K, N)
+
+
+def bench_prefill(L, timer, sptr, M=2048):
+    """Qwen2.5-32B-shaped prefill layers at M = 2048 tokens, bf16 activations
+    ~N(0,1) with 1 % of the input channels x20, RTN int4 G=128 weights:
+    median kernel time of the fused kernel, and dense bf16 torch.matmul of
+    the dequantized weights (the practical matrix-core ceiling) beside it."""
+    import torch
+    import bit_weight_only_gemm_amd as w4
+    from bit_weight_only_gemm_amd import synth
+    dev = torch.device("cuda:0")
+    pts = []
+    for K, N in PREFILL_SHAPES:
+        W = torch.from_numpy(synth.weights("C4/W/%dx%d" % (K, N), N, K)).to(dev)
+        qw, sc, qz = w4.w4a16_quantize_rtn(W, G)
+        p = w4.w4a16_repack(qw, sc, qz, None)
+        del W, qw, sc, qz
+        x32 = synth.activations("C4/x/%dx%d" % (M, K), M, K)
+        x32 = synth.with_outliers(x32, synth.outlier_channels("C4/outl/%d" % K, K))
+        x = torch.from_numpy(synth.to_bf16_bits(x32).view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        a = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(p["codes"].data_ptr()),
+             ctypes.c_void_p(p["scales"].data_ptr()), ctypes.c_void_p(p["zeros"].data_ptr()),
+             None, G, ctypes.c_void_p(y.data_ptr()), M, N, K, w4.BF16, None, 0, sptr)
+        for _ in range(20):          # clocks up before the first timed shape
+            L.w4a16_gemm(*a)
+        t = timer.time(lambda: L.w4a16_gemm(*a), 10)
+        wd = w4.w4a16_dequant(p, torch.bfloat16)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            torch.matmul(x, wd.t())
+        e0.record()
+        for _ in range(10):
+            torch.matmul(x, wd.t())
+        e1.record()
+        torch.cuda.synchronize()
+        td = e0.elapsed_time(e1) * 1e-3 / 10
+        fl = 2.0 * M * N * K
+        pts.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 1),
+                    "tflops": round(fl / t / 1e12, 1),
+                    "pct_mfma": round(100 * fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
+                    "dense_bf16_matmul_tflops": round(fl / td / 1e12, 1)})
+        del p, x, y, wd
+        torch.cuda.empty_cache()
+    best = max(pts, key=lambda q: q["tflops"])
+    tot_fl = sum(2.0 * q["M"] * q["N"] * q["K"] for q in pts)
+    tot_t = sum(q["us"] for q in pts) * 1e-6
+    return {"workload": "Qwen2.5-32B-shaped prefill, int4 G=128, bf16 x with 1% outlier "
+                        "channels x20, M=2048",
+            "kernel": "int4_prefill_kernel<bf16>",
+            "tflops_all_shapes": round(tot_fl / tot_t / 1e12, 1),
+            "roofline": {"bound": "mfma", "achieved": best["tflops"],
+                         "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(best["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                         "shape": [best["M"], best["K"], best["N"]]},
+            "points": pts}
+
+
+def bench_nf4(L, timer, sptr, K=8192, N=28672):
+    """The NF4 projection: W [28672, 8192] ~N(0, 0.02), blocksize 64, double
+    quant over 256 blocks, bf16 x ~N(0,1) at M in {1, 32}; 4 rotating weight
+    copies so the weights stream from HBM."""
+    import torch
+    import bit_weight_only_gemm_amd as w4
+    from bit_weight_only_gemm_amd import synth
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(synth.weights("C5/W/%dx%d" % (K, N), N, K)).to(dev)
+    p0 = w4.nf4_quantize(W)
+    del W
+    ps = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in p0.items()}
+          for _ in range(4)]
+    wb = K * N // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256)
+    pts = []
+    for M in (1, 32):
+        xb = synth.to_bf16_bits(synth.activations("C5/x/%d" % M, M, K))
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        k = [0]
+
+        def call():
+            p = ps[k[0] % 4]
+            k[0] += 1
+            return L.nf4_gemm(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(p["qweight"].data_ptr()),
+                              ctypes.c_void_p(p["absmax_q"].data_ptr()),
+                              ctypes.c_void_p(p["absmax_scale"].data_ptr()), 64,
+                              ctypes.c_void_p(y.data_ptr()), M, N, K, w4.BF16, None, 0, sptr)
+        t = timer.time(call, 20)
+        byt = wb + 2 * M * K + 2 * M * N
+        pts.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 2),
+                    "weight_GBps": round(wb / t / 1e9, 1),
+                    "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1)})
+    return {"workload": "NF4 28672x8192, blocksize 64, double quant 256, bf16",
+            "kernel": "nf4_decode_kernel<bf16>", "points": pts}
+
+
+def cpu_baseline(xs, outs):
     """The oracle, as it stands, on one whole step (all 9 calls) of the same
     workload: unpack + dequant + fp64 product per call, on this host."""
     import torch
@@ -275,7 +475,7 @@ def cpu_baseline(calls, rot, xs, outs):
     wbytes = 0
     worst = 0.0
     t_total = 0.0
-    for K, N, M, _ in rot[0]:
+    for K, N, M in [(K, N, M) for K, N in SHAPES for M in MS]:
         qw, s, qz, gi = packed[(K, N)]
         xb = xs[(M, K)].view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()

@@ -53,10 +53,10 @@ constexpr int RUN = 8;                  // K tiles per meta run and ring pass
 
 // Activation modes.  PACKED: M <= 4, one 16-byte load per lane and K tile
 // carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
-// tile.  XLDS / XGATHER: PACKED with the M rows of x staged in LDS once per
-// workgroup (and, for XGATHER, the act-order permutation too: the operand is
-// gathered from LDS, x[m][perm[k]], so no separate permutation pass runs).
-enum { AM_PACKED = 0, AM_FULL = 1, AM_XLDS = 2, AM_XGATHER = 3 };
+// tile.  XGATHER: PACKED for an act-order weight, with the M rows of x and
+// the permutation staged in LDS once per workgroup; the operand is gathered
+// from LDS, x[m][perm[k]], so no separate permutation pass runs.
+enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2 };
 constexpr bool is_packed(int am) { return am != AM_FULL; }
 
 // Largest LDS footprint of the staged activations (+ permutation): with the
@@ -249,12 +249,10 @@ struct Nf4W {
 // r = batch row.  Rows >= M read 0 through the descriptor range; k >= K (only
 // in a half NF4 tile) uses an out-of-range offset.
 // Staged activations in LDS: x rows [M][K] at xl, the permutation int32[K] at
-// pl (XGATHER), 16 zero bytes at zoff (for the inputs past K of a half NF4
-// tile).
+// pl.
 struct XLds {
   const uint8_t* xl;
   const int32_t* pl;
-  uint32_t zoff;
   int M;
 };
 
@@ -263,16 +261,12 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
                                        typename Op<DT>::vec (&a)[NA], const XLds& xs) {
   typedef typename Op<DT>::vec vec;
   const int r = lane & 15, b = lane >> 4;
-  if constexpr (AM == AM_XLDS || AM == AM_XGATHER) {
+  if constexpr (AM == AM_XGATHER) {
     // rows m >= M only feed output rows that are never stored, so they read
-    // row M - 1 instead of zeros
+    // row M - 1 instead of zeros (K % 128 == 0: no half tiles)
     const int j = r >> 2, m = min(r & 3, xs.M - 1);
     const int kg = t * 128 + WP::xk(j, b);
-    if constexpr (AM == AM_XLDS) {
-      uint32_t off = ((uint32_t)m * (uint32_t)K + (uint32_t)kg) * 2u;
-      if constexpr (WP::kRaggedK) off = kg < K ? off : xs.zoff;
-      a[0] = *(const vec*)(xs.xl + off);
-    } else {
+    {
       const u32x4_t p0 = *(const u32x4_t*)(xs.pl + kg);
       const u32x4_t p1 = *(const u32x4_t*)(xs.pl + kg + 4);
       const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
@@ -307,13 +301,13 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
   }
 }
 
-// Bytes of LDS the staged activations (+ permutation) take: x rows, the
-// permutation, 16 zero bytes, each region rounded up to whole 1 KB blocks.
+// Bytes of LDS the staged activations and permutation take, each region
+// rounded up to whole 1 KB blocks.
 __host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
   return (uint32_t)((M * K * 2 + 1023) / 1024 * 1024);
 }
-__host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool gather) {
-  return xlds_x_bytes(M, K) + (gather ? (uint32_t)((K * 4 + 1023) / 1024 * 1024) : 0u) + 16u;
+__host__ __device__ constexpr uint32_t xlds_bytes(int M, int K) {
+  return xlds_x_bytes(M, K) + (uint32_t)((K * 4 + 1023) / 1024 * 1024);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
@@ -367,20 +361,17 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
   u32x4_t ring[RUN];
   typename Op<DT>::vec ra[PA][NA];
   typename WP::Meta mc, mn = WP::zero_meta();
-  XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), 0u, M};
+  XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), M};
   if (n > 0) {
     mn = wp.load_meta(r0);
 #pragma unroll
     for (int s = 0; s < RUN; ++s) ring[s] = wp.load_codes(t0 + min(s, n - 1), lane);
   }
-  if constexpr (AM == AM_XLDS || AM == AM_XGATHER) {
-    // every wave takes part in staging the M rows of x (and the permutation)
+  if constexpr (AM == AM_XGATHER) {
+    // every wave takes part in staging the M rows of x and the permutation
     // while its first code tiles are in flight
-    xs.zoff = xlds_bytes(M, K, AM == AM_XGATHER) - 16u;
     stage_lds(x, (uint32_t)(M * K * 2), xlds, wave, lane);
-    if constexpr (AM == AM_XGATHER)
-      stage_lds(perm, (uint32_t)(K * 4), xlds + xlds_x_bytes(M, K), wave, lane);
-    if (threadIdx.x == 0) *(u32x4_t*)(xlds + xs.zoff) = u32x4_t{0u, 0u, 0u, 0u};
+    stage_lds(perm, (uint32_t)(K * 4), xlds + xlds_x_bytes(M, K), wave, lane);
     __syncthreads();
   }
   if (n > 0) {
@@ -526,7 +517,7 @@ static int pick_mode(int64_t M, int64_t K, bool gather, int* mt) {
     *mt = 1;
     // staging x alone in LDS does not beat per-tile loads; the gather pays
     // for itself by saving the separate permutation pass
-    if (gather && xlds_bytes((int)M, (int)K, true) <= kMaxXlds) return AM_XGATHER;
+    if (gather && xlds_bytes((int)M, (int)K) <= kMaxXlds) return AM_XGATHER;
     return AM_PACKED;
   }
   *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -538,9 +529,7 @@ static void launch_int4_v(const void* x, const void* codes_r, const void* scales
                           const void* zeros_r, const int32_t* perm, void* out, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  const size_t lds = (AM == AM_XLDS || AM == AM_XGATHER)
-                         ? xlds_bytes((int)M, (int)K, AM == AM_XGATHER)
-                         : 0;
+  const size_t lds = AM == AM_XGATHER ? xlds_bytes((int)M, (int)K) : 0;
   if (lds) allow_dynamic_lds((const void*)int4_decode_kernel<DT, MT, AM>);
   launch_timed(int4_decode_kernel<DT, MT, AM>, grid, dim3(64 * DW), lds, stream,
                (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
@@ -554,8 +543,6 @@ static void launch_int4_dt(int am, int mt, const void* x, const void* codes_r,
                            void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (am == AM_XGATHER)
     launch_int4_v<DT, 1, AM_XGATHER>(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
-  else if (am == AM_XLDS)
-    launch_int4_v<DT, 1, AM_XLDS>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
   else if (am == AM_PACKED)
     launch_int4_v<DT, 1, AM_PACKED>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
   else if (mt == 1)
@@ -602,9 +589,7 @@ static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, con
                          const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  const size_t lds = AM == AM_XLDS ? xlds_bytes((int)M, (int)K, false) : 0;
-  if (lds) allow_dynamic_lds((const void*)nf4_decode_kernel<DT, MT, AM, BATCH>);
-  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), lds, stream,
+  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), 0, stream,
                (const uint16_t*)x, q, aq, asc, L, (uint16_t*)out, (int)M, (int)N, (int)K,
                (int)ceil_div(K, 128));
 }
@@ -615,9 +600,7 @@ static void launch_nf4_dt(const void* x, const uint8_t* q, const uint8_t* aq, co
                           hipStream_t stream) {
   int mt;
   const int am = pick_mode(M, K, false, &mt);
-  if (am == AM_XLDS)
-    launch_nf4_v<DT, 1, AM_XLDS, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
-  else if (am == AM_PACKED)
+  if (am == AM_PACKED)
     launch_nf4_v<DT, 1, AM_PACKED, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
   else if (mt == 1)
     launch_nf4_v<DT, 1, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
