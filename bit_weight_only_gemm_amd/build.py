@@ -28,9 +28,16 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  The decode kernels keep their few accumulator tiles in
+# ordinary VGPRs (MFMA with VGPR destination): with accumulation registers the
+# compiler copies them back to VGPRs after every tile.  The prefill kernel's
+# 256 accumulators need the accumulation registers and keeps the default.
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
