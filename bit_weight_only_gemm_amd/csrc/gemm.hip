@@ -83,7 +83,12 @@ __device__ __forceinline__ void mma_tile(const typename Op<DT>::vec b[4],
       acc[j] = mfma16x16x32<DT>(a[0], b[j], acc[j]);
     } else {
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = mfma16x16x32<DT>(a[m * 4 + j], b[j], acc[m]);
+      for (int m = 0; m < MT; ++m) {
+        // NACC / MT accumulators per row tile take the steps in turn, so that
+        // consecutive MFMAs do not wait on each other's results
+        constexpr int PER = NACC / MT;
+        acc[m * PER + j % PER] = mfma16x16x32<DT>(a[m * 4 + j], b[j], acc[m * PER + j % PER]);
+      }
     }
   }
 }
@@ -333,7 +338,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
                                             int KT, float* red, const int32_t* perm,
                                             uint8_t* xlds) {
   constexpr int NA = is_packed(AM) ? 1 : MT * 4;                   // A vectors per tile
-  constexpr int NACC = is_packed(AM) ? 4 : MT;                     // accumulator tiles
+  constexpr int NACC = is_packed(AM) ? 4 : MT * (MT == 1 ? 4 : (MT == 2 ? 2 : 1));  // acc tiles
   constexpr int PA = is_packed(AM) ? RUN : (MT == 1 ? 2 : 1);      // A ring depth
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -412,8 +417,18 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
     }
     res[0] = g == 0 ? v : float4_t{0.f, 0.f, 0.f, 0.f};
   } else {
+    constexpr int PER = NACC / MT;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) res[m] = acc[m];
+    for (int m = 0; m < MT; ++m) {
+      res[m] = acc[m * PER];
+#pragma unroll
+      for (int q = 1; q < PER; ++q) {
+        res[m][0] += acc[m * PER + q][0];
+        res[m][1] += acc[m * PER + q][1];
+        res[m][2] += acc[m * PER + q][2];
+        res[m][3] += acc[m * PER + q][3];
+      }
+    }
   }
 
   // ---- wave partials -> LDS, summed in wave order
