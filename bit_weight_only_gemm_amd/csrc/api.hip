@@ -36,6 +36,11 @@ int check_ptrs(std::initializer_list<const void*> required) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+// The launchers report hipGetLastError() after their launches; an error an
+// earlier runtime call of the caller left pending is cleared first so that it
+// is not reported as this call's failure.
+void clear_pending_error() { (void)hipGetLastError(); }
+
 // ---- NF4 codebook, computed here from its closed form (independent of any
 // table elsewhere): Phi^-1 by Newton iteration on erfc in double precision.
 double norm_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
@@ -155,6 +160,7 @@ int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm
   if ((g_idx == nullptr) != (perm == nullptr)) return W4A16_ERR_INVALID_ARG;
   if (int s = check_ptrs({W, qweight, scales, qzeros})) return s;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
+  clear_pending_error();
   return hip_status(launch_rtn_int4(W, perm, N, K, qweight, scales, qzeros, (hipStream_t)stream));
 }
 
@@ -170,6 +176,7 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
     if (!perm) return W4A16_ERR_INVALID_ARG;
     if (int s = w4a16_make_perm(g_idx, K, group_size, perm, &used, stream)) return s;
   }
+  clear_pending_error();
   if (int s = hip_status(launch_repack(qweight, scales, qzeros, used ? perm : nullptr, K, N,
                                        codes_r, scales_r, zeros_r, (hipStream_t)stream)))
     return s;
@@ -200,6 +207,7 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
   const int64_t need = perm ? int4_workspace_bytes(M, N, K) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
+  clear_pending_error();
   return hip_status(launch_int4_gemm(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, dtype,
                                      workspace, workspace_bytes, (hipStream_t)stream));
 }
@@ -209,6 +217,7 @@ int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r
   if (int s = validate_int4_shape(K, N, group_size)) return s;
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({codes_r, scales_r, zeros_r, w_out})) return s;
+  clear_pending_error();
   return hip_status(
       launch_dequant_int4(codes_r, scales_r, zeros_r, K, N, dtype, w_out, (hipStream_t)stream));
 }
@@ -231,6 +240,7 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_
                  uint8_t* absmax_q, float* absmax_scale, void* stream) {
   if (int s = validate_nf4_shape(N, K, blocksize)) return s;
   if (int s = check_ptrs({W, qweight, absmax_q, absmax_scale})) return s;
+  clear_pending_error();
   return hip_status(launch_nf4_quant(W, N, K, codebook(), qweight, absmax_q, absmax_scale,
                                      (hipStream_t)stream));
 }
@@ -251,6 +261,7 @@ int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
   if (int s = check_ptrs({x, qweight, absmax_q, absmax_scale, out})) return s;
   if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
   (void)workspace_bytes;
+  clear_pending_error();
   return hip_status(launch_nf4_gemm(x, qweight, absmax_q, absmax_scale, codebook(), out, M, N, K,
                                     dtype, workspace, workspace_bytes, (hipStream_t)stream));
 }
@@ -261,6 +272,7 @@ int nf4_dequant(const uint8_t* qweight, const uint8_t* absmax_q, const float* ab
   if (int s = validate_nf4_shape(N, K, blocksize)) return s;
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({qweight, absmax_q, absmax_scale, w_out})) return s;
+  clear_pending_error();
   return hip_status(launch_dequant_nf4(qweight, absmax_q, absmax_scale, N, K, dtype, codebook(),
                                        w_out, (hipStream_t)stream));
 }
