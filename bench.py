@@ -381,9 +381,12 @@ def bench_prefill(L, timer, sptr, M=2048):
         x32 = synth.with_outliers(x32, synth.outlier_channels("C4/outl/%d" % K, K))
         x = torch.from_numpy(synth.to_bf16_bits(x32).view(np.int16)).view(torch.bfloat16).to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsb = w4.w4a16_workspace_bytes(M, N, K)
+        ws = w4.workspace(wsb, dev)
         a = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(p["codes"].data_ptr()),
              ctypes.c_void_p(p["scales"].data_ptr()), ctypes.c_void_p(p["zeros"].data_ptr()),
-             None, G, ctypes.c_void_p(y.data_ptr()), M, N, K, w4.BF16, None, 0, sptr)
+             None, G, ctypes.c_void_p(y.data_ptr()), M, N, K, w4.BF16,
+             ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb, sptr)
         for _ in range(20):          # clocks up before the first timed shape
             L.w4a16_gemm(*a)
         t = timer.time(lambda: L.w4a16_gemm(*a), 10)
@@ -402,7 +405,7 @@ def bench_prefill(L, timer, sptr, M=2048):
                     "tflops": round(fl / t / 1e12, 1),
                     "pct_mfma": round(100 * fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
                     "dense_bf16_matmul_tflops": round(fl / td / 1e12, 1)})
-        del p, x, y, wd
+        del p, x, y, wd, ws
         torch.cuda.empty_cache()
     best = max(pts, key=lambda q: q["tflops"])
     tot_fl = sum(2.0 * q["M"] * q["N"] * q["K"] for q in pts)

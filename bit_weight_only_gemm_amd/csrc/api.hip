@@ -186,7 +186,7 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
 
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (M <= 0 || validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
-  return int4_workspace_bytes(M, N, K);
+  return int4_workspace_bytes(M, N, K, true);
 }
 
 int w4a16_set_timing_events(void* start_event, void* stop_event) {
@@ -204,7 +204,7 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
   if (int s = check_ptrs({x, codes_r, scales_r, zeros_r, out})) return s;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
   if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
-  const int64_t need = perm ? int4_workspace_bytes(M, N, K) : 0;
+  const int64_t need = int4_workspace_bytes(M, N, K, perm != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
   clear_pending_error();

@@ -568,6 +568,19 @@ static void launch_int4_dt(int am, int mt, const void* x, const void* codes_r,
     launch_int4_v<DT, 4, AM_FULL>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
 }
 
+// Workspace layout: the permuted activations (when the activations are
+// permuted in a separate pass), then the prefill split-K partials (when the
+// prefill kernel splits K).
+static int64_t xperm_bytes(int64_t M, int64_t K, bool perm) {
+  int mt;
+  if (!perm || (M < kPrefillMinM && pick_mode(M, K, true, &mt) == AM_XGATHER)) return 0;
+  return ceil_div(M * K * 2, 256) * 256;
+}
+
+int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm) {
+  return xperm_bytes(M, K, perm) + (M >= kPrefillMinM ? prefill_workspace_bytes(M, N, K) : 0);
+}
+
 hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scales_r,
                             const void* zeros_r, const int32_t* perm, void* out, int64_t M,
                             int64_t N, int64_t K, int dtype, void* workspace,
@@ -575,7 +588,8 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
   int mt = 1;
   const int am = M >= kPrefillMinM ? AM_FULL : pick_mode(M, K, perm != nullptr, &mt);
   const void* xa = x;
-  if (perm && am != AM_XGATHER) {
+  const int64_t xb = xperm_bytes(M, K, perm != nullptr);
+  if (xb > 0) {
     // the activations are permuted once into the workspace
     const int64_t n8 = M * (K / 8);
     hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, stream,
@@ -583,7 +597,8 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
     xa = workspace;
   }
   if (M >= kPrefillMinM)
-    launch_int4_prefill(xa, codes_r, scales_r, zeros_r, out, M, N, K, dtype, stream);
+    launch_int4_prefill(xa, codes_r, scales_r, zeros_r, out, (uint8_t*)workspace + xb, M, N, K,
+                        dtype, stream);
   else if (dtype == DT_F16)
     launch_int4_dt<DT_F16>(am, mt, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
   else
@@ -591,13 +606,7 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
   return hipGetLastError();
 }
 
-int64_t int4_workspace_bytes(int64_t M, int64_t /*N*/, int64_t K) {
-  // room for the permuted activations of an act-order weight, unless the
-  // kernel gathers them itself
-  int mt;
-  if (M < kPrefillMinM && pick_mode(M, K, true, &mt) == AM_XGATHER) return 0;
-  return ceil_div(M * K * 2, 256) * 256;
-}
+
 
 template <int DT, int MT, int AM, bool BATCH>
 static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, const float* asc,

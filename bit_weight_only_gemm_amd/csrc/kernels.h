@@ -13,9 +13,12 @@ struct Nf4Table {
   float v[16];
 };
 
-// Workspace bytes the INT4 GEMM needs at this shape when a column permutation
-// is given (room for the permuted activations); 0 otherwise.
-int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Workspace bytes the INT4 GEMM needs at this shape, with or without a column
+// permutation: room for the permuted activations (when they are permuted in a
+// separate pass) and for the prefill kernel's split-K partials.
+int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm);
+// Bytes of the prefill kernel's split-K partials at this shape (0: no split).
+int64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // Attach HIP timing events to the next main GEMM kernel launched by the
 // calling host thread (hipExtLaunchKernel start/stop events).
@@ -42,12 +45,12 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
                             int64_t workspace_bytes, hipStream_t stream);
 // Rows from which w4a16_gemm uses the LDS-staged prefill kernel.
 #ifndef W4A16_PREFILL_MIN_M
-#define W4A16_PREFILL_MIN_M 256
+#define W4A16_PREFILL_MIN_M 64
 #endif
 constexpr int64_t kPrefillMinM = W4A16_PREFILL_MIN_M;
 void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
-                         const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
-                         int dtype, hipStream_t stream);
+                         const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
+                         int64_t K, int dtype, hipStream_t stream);
 
 hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,

@@ -32,11 +32,9 @@
 namespace w4a16 {
 
 constexpr int PF_WAVES = 4;                  // waves per workgroup
-constexpr int PF_BM = 256;                   // rows per workgroup
-constexpr int PF_MT = PF_BM / 32;            // 32-row MFMA tiles per wave
 constexpr int PF_ROWB = 256;                 // LDS bytes of one row of a K tile
-constexpr int PF_STAGE = PF_BM * PF_ROWB;    // 64 KB
-constexpr int PF_ALD = PF_BM * 16 / (64 * PF_WAVES);  // 16-byte A chunks per thread
+// Rows per workgroup BM in {64, 128, 256}: BM / 32 MFMA row tiles per wave,
+// an LDS stage of BM x 256 bytes, BM / 16 16-byte activation loads per lane.
 
 #ifndef W4A16_PF_DMA_STEPS
 #define W4A16_PF_DMA_STEPS 8
@@ -76,18 +74,27 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff,
 // TAIL: the row block may hold fewer than 256 rows; the row of each load is
 // then part of the per-lane offset so that rows past M read 0.  Full blocks
 // put it in the scalar offset (fewer registers).
-template <int DT, bool TAIL>
+// Split-K: workgroup z of S takes K tiles [z KT / S, (z + 1) KT / S) and, when
+// S > 1, writes its fp32 partial tile to part[z][M][N] for split_reduce_kernel.
+template <int DT, int BM, bool TAIL>
 __global__ void __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
 int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                    uint16_t* __restrict__ out, int M, int N, int K, int KT, int NP) {
+                    uint16_t* __restrict__ out, float* __restrict__ part, int M, int N, int K,
+                    int KT, int NP, int S) {
   typedef typename Op<DT>::vec vec;
+  constexpr int PF_BM = BM;
+  constexpr int PF_MT = BM / 32;
+  constexpr int PF_STAGE = BM * PF_ROWB;
+  constexpr int PF_ALD = BM * 16 / (64 * PF_WAVES);
   __shared__ __attribute__((aligned(16))) uint8_t As[2 * PF_STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = (TAIL ? M / PF_BM : blockIdx.y) * PF_BM;
+  const int z = blockIdx.z;
+  const int tb = (int)((int64_t)z * KT / S), te = (int)((int64_t)(z + 1) * KT / S);
   const int p = blockIdx.x * PF_WAVES + wave;  // this wave's 64-column panel
   const int KT8 = (KT + 7) >> 3;
   const int i16 = lane & 15, h = lane >> 5;
@@ -135,21 +142,21 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) cw[g][h2] = bld128(rc, vcode[g][h2], 0);
-    sc[g] = bld16(rs, vmeta[g] * 16u, 0);
-    zz[g] = bld32(rz, vmeta[g] * 4u, 0);
+    for (int h2 = 0; h2 < 2; ++h2) cw[g][h2] = bld128(rc, vcode[g][h2], tb * 4096);
+    sc[g] = bld16(rs, vmeta[g] * 16u, (tb >> 3) * 1024 + (tb & 7) * 2);
+    zz[g] = bld32(rz, vmeta[g] * 4u, (tb >> 3) * 256);
   }
 #pragma unroll
   for (int i = 0; i < PF_ALD; ++i)
     lds_dma16(rx, As + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
-              TAIL ? 0 : (int)((uint32_t)i * astride));
+              TAIL ? tb * 256 : (int)((uint32_t)i * astride) + tb * 256);
   __syncthreads();
 
-  for (int t = 0; t < KT; ++t) {
+  for (int t = tb; t < te; ++t) {
     // ---- issue K tile t + 1 (the last tile is re-read on the final pass);
-    // its activations go to LDS stage (t + 1) & 1, last read before the
+    // its activations go to LDS stage (t - tb + 1) & 1, last read before the
     // previous barrier
-    const int tn = min(t + 1, KT - 1);
+    const int tn = min(t + 1, te - 1);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
@@ -157,7 +164,7 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
       sn[g] = bld16(rs, vmeta[g] * 16u, (tn >> 3) * 1024 + (tn & 7) * 2);
       zn[g] = bld32(rz, vmeta[g] * 4u, (tn >> 3) * 256);
     }
-    uint8_t* sw = As + ((t + 1) & 1) * PF_STAGE;
+    uint8_t* sw = As + ((t - tb + 1) & 1) * PF_STAGE;
     // the activation loads of tile t + 1 are spread over the first
     // PF_DMA_STEPS steps of tile t (a burst of them stalls the issuing waves
     // behind the address queue)
@@ -174,7 +181,7 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     QParam<DT> qp[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) qp[g].set(sc[g] & 0xFFFFu, (zz[g] >> (4 * (t & 7))) & 0xFu);
-    const uint8_t* st = As + (t & 1) * PF_STAGE;
+    const uint8_t* st = As + ((t - tb) & 1) * PF_STAGE;
     auto read_step = [&](int s, vec (&a)[PF_MT]) {
       const int q = 2 * s + h;  // 8-element chunk of this lane's inputs
 #pragma unroll
@@ -245,6 +252,7 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 
   // ---- epilogue: register r of lane l is row (r & 3) + 4 (l >> 5) + 8 (r >> 2),
   // column l & 31 of the 32 x 32 tile
+  float* pz = part + (size_t)z * M * N;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int col = p * 64 + g * 32 + (lane & 31);
@@ -254,39 +262,119 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + m * 32 + (r & 3) + 4 * h + 8 * (r >> 2);
-          if (row < M) out[(size_t)row * N + col] = round16<DT>(acc[m][g][r]);
+          if (row < M) {
+            if (S == 1)
+              out[(size_t)row * N + col] = round16<DT>(acc[m][g][r]);
+            else
+              pz[(size_t)row * N + col] = acc[m][g][r];
+          }
         }
       }
     }
   }
 }
 
+// out = round16(sum_z part[z]) over the S split-K partials, added in z order
+// (bitwise reproducible); 4 consecutive outputs per thread.
 template <int DT>
-static void launch_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
-                              const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
-                              hipStream_t stream) {
+__global__ void __launch_bounds__(256)
+split_reduce_kernel(const float* __restrict__ part, int S, int64_t MN, uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= MN) return;
+  float4_t s = *(const float4_t*)(part + i);
+  for (int z = 1; z < S; ++z) {
+    const float4_t v = *(const float4_t*)(part + (size_t)z * MN + i);
+    s[0] += v[0];
+    s[1] += v[1];
+    s[2] += v[2];
+    s[3] += v[3];
+  }
+  const uint32_t lo = (uint32_t)round16<DT>(s[0]) | ((uint32_t)round16<DT>(s[1]) << 16);
+  const uint32_t hi = (uint32_t)round16<DT>(s[2]) | ((uint32_t)round16<DT>(s[3]) << 16);
+  *(uint2*)(out + i) = make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------- planning --
+// Rows per workgroup for M, and the split of K that fills the GPU best: a
+// simple model of the call time (rounds of workgroups on 256 CUs x K tiles per
+// workgroup x per-tile MFMA time, plus the partials' round trip through HBM).
+struct PrefillPlan {
+  int bm, splits;
+};
+
+static PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K) {
+  PrefillPlan pl;
+  pl.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+  const int64_t tiles = ceil_div(ceil_div(N, 64), (int64_t)PF_WAVES) * ceil_div(M, (int64_t)pl.bm);
+  const int64_t KT = K / 128;
+  const double t_tile = 3.4e-6 * pl.bm / 256.0;  // one K tile of a workgroup
+  double best = 0;
+  pl.splits = 1;
+  for (int S = 1; S <= 16 && S <= KT; ++S) {
+    double t = (double)ceil_div(tiles * S, (int64_t)256) * (double)ceil_div(KT, (int64_t)S) * t_tile;
+    if (S > 1) t += (double)(S * 4 + 2) * M * N / 4.0e12 + 2e-6;
+    if (S == 1 || t < best * 0.97) {
+      best = t;
+      pl.splits = S;
+    }
+  }
+  return pl;
+}
+
+int64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const PrefillPlan pl = plan_prefill(M, N, K);
+  return pl.splits > 1 ? ceil_div((int64_t)pl.splits * M * N * 4, 256) * 256 : 0;
+}
+
+template <int DT, int BM>
+static void launch_prefill_bm(const void* x, const void* codes_r, const void* scales_r,
+                              const void* zeros_r, void* out, float* part, int S, int64_t M,
+                              int64_t N, int64_t K, hipStream_t stream) {
   const int64_t NP = ceil_div(N, 64);
   const int KT = (int)(K / 128);
   const unsigned gx = (unsigned)ceil_div(NP, PF_WAVES);
-  const int64_t full = M / PF_BM;
-  if (full > 0)
-    launch_timed(int4_prefill_kernel<DT, false>, dim3(gx, (unsigned)full), dim3(64 * PF_WAVES), 0,
-                 stream, (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
-                 (const uint8_t*)zeros_r, (uint16_t*)out, (int)M, (int)N, (int)K, KT, (int)NP);
+  const int64_t full = M / BM;
   // the timing events (if set) go to the first launch
-  if (M % PF_BM)
-    launch_timed(int4_prefill_kernel<DT, true>, dim3(gx, 1), dim3(64 * PF_WAVES), 0, stream,
-                 (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
-                 (const uint8_t*)zeros_r, (uint16_t*)out, (int)M, (int)N, (int)K, KT, (int)NP);
+  if (full > 0)
+    launch_timed(int4_prefill_kernel<DT, BM, false>, dim3(gx, (unsigned)full, (unsigned)S),
+                 dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
+                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, (uint16_t*)out, part, (int)M,
+                 (int)N, (int)K, KT, (int)NP, S);
+  if (M % BM)
+    launch_timed(int4_prefill_kernel<DT, BM, true>, dim3(gx, 1, (unsigned)S),
+                 dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
+                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, (uint16_t*)out, part, (int)M,
+                 (int)N, (int)K, KT, (int)NP, S);
+  if (S > 1) {
+    const int64_t MN = M * N;
+    hipLaunchKernelGGL(split_reduce_kernel<DT>, dim3((unsigned)ceil_div(MN / 4, (int64_t)256)),
+                       dim3(256), 0, stream, (const float*)part, S, MN, (uint16_t*)out);
+  }
+}
+
+template <int DT>
+static void launch_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
+                              const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
+                              int64_t K, hipStream_t stream) {
+  const PrefillPlan pl = plan_prefill(M, N, K);
+  float* part = (float*)ws;
+  if (pl.bm == 64)
+    launch_prefill_bm<DT, 64>(x, codes_r, scales_r, zeros_r, out, part, pl.splits, M, N, K, stream);
+  else if (pl.bm == 128)
+    launch_prefill_bm<DT, 128>(x, codes_r, scales_r, zeros_r, out, part, pl.splits, M, N, K,
+                               stream);
+  else
+    launch_prefill_bm<DT, 256>(x, codes_r, scales_r, zeros_r, out, part, pl.splits, M, N, K,
+                               stream);
 }
 
 void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
-                         const void* zeros_r, void* out, int64_t M, int64_t N, int64_t K,
-                         int dtype, hipStream_t stream) {
+                         const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
+                         int64_t K, int dtype, hipStream_t stream) {
   if (dtype == DT_F16)
-    launch_prefill_dt<DT_F16>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+    launch_prefill_dt<DT_F16>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, stream);
   else
-    launch_prefill_dt<DT_BF16>(x, codes_r, scales_r, zeros_r, out, M, N, K, stream);
+    launch_prefill_dt<DT_BF16>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, stream);
 }
 
 }  // namespace w4a16

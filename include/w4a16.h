@@ -147,10 +147,11 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
                  int32_t* perm_used_host, void* stream);
 
 /*
- * Workspace bytes w4a16_gemm needs at this shape when it is given a column
- * permutation `perm` (room for the permuted activations x[:, perm]); 0 where
- * the kernel gathers x[:, perm] itself (M <= 4 and M*K*2 + K*4 bytes fit its
- * on-chip staging, about 64 KB).  Without a permutation no workspace is used.
+ * Workspace bytes w4a16_gemm needs at this shape (covering calls with a
+ * column permutation): room for the permuted activations x[:, perm] (none
+ * where the kernel gathers x[:, perm] itself: M <= 4 with M*K*2 + K*4 bytes
+ * within its on-chip staging, about 72 KB) plus, for M >= 64, the fp32
+ * partials S*M*N*4 of the large-M kernel when it splits K over S workgroups.
  * Calls that overlap in time must not share a workspace.
  */
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
@@ -165,9 +166,10 @@ int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_siz
  *   perm   int32 [K] from w4a16_repack (or NULL for identity).
  *   codes_r, scales_r, zeros_r from w4a16_repack.
  *   dtype  W4A16_F16 or W4A16_BF16 (activations and output).
- *   workspace / workspace_bytes: required when perm is given and
- *          w4a16_workspace_bytes(M, N, K, 128) > 0 (at least that many bytes;
- *          W4A16_ERR_WORKSPACE otherwise), else ignored.
+ *   workspace / workspace_bytes: required when the call needs one (a
+ *          permutation the kernel does not gather itself, or a split of K);
+ *          w4a16_workspace_bytes(M, N, K, 128) bytes always suffice
+ *          (W4A16_ERR_WORKSPACE when too small), else ignored.
  * Constraints: M >= 1, K % 128 == 0, N % 8 == 0, group_size == 128.
  * Async on `stream`.  Results are bitwise reproducible run to run (the split of
  * K over a workgroup's waves is reduced in a fixed order).

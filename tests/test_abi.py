@@ -84,6 +84,11 @@ def test_gemm_validation_without_gpu():
     assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) == 0
     assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) >= 4 * 11008 * 2
     assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 5 * 4096 * 2
+    # a prefill-sized call that splits K needs room for fp32 partials even
+    # without a permutation
+    need = L.w4a16_workspace_bytes(64, 5120, 5120, 128)
+    assert need >= 2 * 64 * 5120 * 4
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 64, 5120, 5120, 0, NULL, 0, NULL) == 5
 
 
 def test_nf4_validation_without_gpu():

@@ -1,9 +1,11 @@
 """Parity of the large-M (prefill) INT4 kernel with the oracle.
 
-w4a16_gemm switches to the LDS-staged kernel for M >= 256 rows; these cases
-cover several 256 x 256 workgroup tiles, ragged row blocks (M % 256 != 0),
-a panel count that is not a multiple of 4 (N = 320 -> 5 panels), act-order,
-bf16 with outlier channels, and exact one-hot probes through the kernel.
+w4a16_gemm switches to the LDS-staged kernel for M >= 64 rows (64-, 128- or
+256-row workgroup tiles, K split over workgroups with an ordered reduction of
+fp32 partials when that fills the GPU better); these cases cover several
+workgroup tiles, ragged row blocks, a panel count that is not a multiple of 4
+(N = 320 -> 5 panels), act-order, split K, bf16 with outlier channels, and
+exact one-hot probes through the kernel.
 """
 
 import numpy as np
@@ -84,3 +86,43 @@ def test_prefill_deterministic():
     y1 = tensor_bits(w4.w4a16_gemm(x, packed))
     y2 = tensor_bits(w4.w4a16_gemm(x, packed))
     assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("M", [64, 65, 100, 128, 129, 200])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mid_m_split_k(M, dtype):
+    # small row counts: 64/128-row tiles and, for so few workgroups, K split
+    # over workgroups (partials through the workspace)
+    N, K = 320, 2560
+    say("mid M", M, dtype, "workspace", w4.w4a16_workspace_bytes(M, N, K))
+    y, xb, W, gi, _ = _gemm("gpu/pf/mid/%d" % M, M, N, K, dtype)
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    assert compare_gemm(y, xb, wd, dtype) <= TOL
+
+
+def test_mid_m_act_order_and_determinism():
+    M, N, K = 96, 256, 3072
+    W, gi, _ = int4_inputs("gpu/pf/midact", N, K, act_order=True)
+    _, packed = gpu_int4_pack(W, gi)
+    xb = synth.to_f16_bits(synth.activations("gpu/pf/midact/x", M, K))
+    y1 = w4.w4a16_gemm(bits_to_tensor(xb, "f16"), packed)
+    y2 = w4.w4a16_gemm(bits_to_tensor(xb, "f16"), packed)
+    assert np.array_equal(tensor_bits(y1), tensor_bits(y2))
+    wd = oracle_int4_rows(W, gi, np.arange(N), "f16")
+    assert compare_gemm(y1, xb, wd, "f16") <= TOL
+
+
+def test_mid_m_onehot_exact_through_split_k():
+    # one-hot rows through the split-K path: each output is one weight plus
+    # exact zeros from the other splits
+    N, K = 256, 4096
+    W, gi, _ = int4_inputs("gpu/pf/midonehot", N, K)
+    _, packed = gpu_int4_pack(W, gi)
+    wd = oracle_int4_rows(W, gi, np.arange(N), "bf16")
+    M = 64
+    ks = (np.arange(M) * 61) % K
+    x = np.zeros((M, K), dtype=np.float32)
+    x[np.arange(M), ks] = 1.0
+    assert w4.w4a16_workspace_bytes(M, N, K) > 0          # this shape splits K
+    y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, "bf16"), "bf16"), packed))
+    assert np.array_equal(y, wd[:, ks].T)
