@@ -571,14 +571,15 @@ static void launch_int4_dt(int am, int mt, const void* x, const void* codes_r,
 // Workspace layout: the permuted activations (when the activations are
 // permuted in a separate pass), then the prefill split-K partials (when the
 // prefill kernel splits K).
-static int64_t xperm_bytes(int64_t M, int64_t K, bool perm) {
+static int64_t xperm_bytes(int64_t M, int64_t N, int64_t K, bool perm) {
   int mt;
-  if (!perm || (M < kPrefillMinM && pick_mode(M, K, true, &mt) == AM_XGATHER)) return 0;
+  if (!perm || (!use_prefill(M, N, K) && pick_mode(M, K, true, &mt) == AM_XGATHER)) return 0;
   return ceil_div(M * K * 2, 256) * 256;
 }
 
 int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm) {
-  return xperm_bytes(M, K, perm) + (M >= kPrefillMinM ? prefill_workspace_bytes(M, N, K) : 0);
+  return xperm_bytes(M, N, K, perm) +
+         (use_prefill(M, N, K) ? prefill_workspace_bytes(M, N, K) : 0);
 }
 
 hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scales_r,
@@ -586,9 +587,10 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
                             int64_t N, int64_t K, int dtype, void* workspace,
                             int64_t /*workspace_bytes*/, hipStream_t stream) {
   int mt = 1;
-  const int am = M >= kPrefillMinM ? AM_FULL : pick_mode(M, K, perm != nullptr, &mt);
+  const bool pf = use_prefill(M, N, K);
+  const int am = pf ? AM_FULL : pick_mode(M, K, perm != nullptr, &mt);
   const void* xa = x;
-  const int64_t xb = xperm_bytes(M, K, perm != nullptr);
+  const int64_t xb = xperm_bytes(M, N, K, perm != nullptr);
   if (xb > 0) {
     // the activations are permuted once into the workspace
     const int64_t n8 = M * (K / 8);
@@ -596,7 +598,7 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
                        (const uint16_t*)x, perm, (uint16_t*)workspace, (int)M, (int)K);
     xa = workspace;
   }
-  if (M >= kPrefillMinM)
+  if (pf)
     launch_int4_prefill(xa, codes_r, scales_r, zeros_r, out, (uint8_t*)workspace + xb, M, N, K,
                         dtype, stream);
   else if (dtype == DT_F16)

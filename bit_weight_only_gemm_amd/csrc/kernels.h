@@ -43,11 +43,13 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
                             const void* zeros_r, const int32_t* perm, void* out, int64_t M,
                             int64_t N, int64_t K, int dtype, void* workspace,
                             int64_t workspace_bytes, hipStream_t stream);
-// Rows from which w4a16_gemm uses the LDS-staged prefill kernel.
-#ifndef W4A16_PREFILL_MIN_M
-#define W4A16_PREFILL_MIN_M 64
-#endif
-constexpr int64_t kPrefillMinM = W4A16_PREFILL_MIN_M;
+// Whether w4a16_gemm runs the LDS-staged large-M kernel (activations shared
+// by a workgroup's 256 columns through LDS) rather than the skinny decode
+// kernel: from 32 rows, or from 12 rows on layers of 100 Mi weights and more
+// (measured crossovers on MI355X).
+inline bool use_prefill(int64_t M, int64_t N, int64_t K) {
+  return M >= 32 || (M >= 12 && N * K >= (int64_t)100 << 20);
+}
 void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
                          const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
                          int64_t K, int dtype, hipStream_t stream);

@@ -150,8 +150,9 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
  * Workspace bytes w4a16_gemm needs at this shape (covering calls with a
  * column permutation): room for the permuted activations x[:, perm] (none
  * where the kernel gathers x[:, perm] itself: M <= 4 with M*K*2 + K*4 bytes
- * within its on-chip staging, about 72 KB) plus, for M >= 64, the fp32
- * partials S*M*N*4 of the large-M kernel when it splits K over S workgroups.
+ * within its on-chip staging, about 72 KB) plus the fp32 partials S*M*N*4 of
+ * the large-M kernel (M >= 32, or M >= 12 on layers of 100 Mi weights and
+ * more) when it splits K over S workgroups.
  * Calls that overlap in time must not share a workspace.
  */
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);

@@ -1,6 +1,7 @@
 """Parity of the large-M (prefill) INT4 kernel with the oracle.
 
-w4a16_gemm switches to the LDS-staged kernel for M >= 64 rows (64-, 128- or
+w4a16_gemm switches to the LDS-staged kernel for M >= 32 rows, or 12 on big
+layers (64-, 128- or
 256-row workgroup tiles, K split over workgroups with an ordered reduction of
 fp32 partials when that fills the GPU better); these cases cover several
 workgroup tiles, ragged row blocks, a panel count that is not a multiple of 4
@@ -126,3 +127,14 @@ def test_mid_m_onehot_exact_through_split_k():
     assert w4.w4a16_workspace_bytes(M, N, K) > 0          # this shape splits K
     y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, "bf16"), "bf16"), packed))
     assert np.array_equal(y, wd[:, ks].T)
+
+
+def test_big_layer_m16_uses_large_m_kernel_sampled_columns():
+    # 16 rows on a 100 Mi-weight layer take the large-M kernel with split K;
+    # the oracle checks every 97th output column
+    M, N, K = 16, 20480, 5120
+    say("big layer M=16")
+    y, xb, W, gi, _ = _gemm("gpu/pf/big16", M, N, K, "bf16")
+    cols = np.arange(0, N, 97)
+    wd = oracle_int4_rows(W, gi, cols, "bf16")
+    assert compare_gemm(y, xb, wd, "bf16", cols=cols) <= TOL
