@@ -440,6 +440,9 @@ def bench_nf4(L, timer, sptr, K=8192, N=28672):
         xb = synth.to_bf16_bits(synth.activations("C5/x/%d" % M, M, K))
         x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsb = w4.nf4_workspace_bytes(M, N, K)
+        ws = w4.workspace(wsb, dev)
+        wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
         k = [0]
 
         def call():
@@ -448,14 +451,15 @@ def bench_nf4(L, timer, sptr, K=8192, N=28672):
             return L.nf4_gemm(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(p["qweight"].data_ptr()),
                               ctypes.c_void_p(p["absmax_q"].data_ptr()),
                               ctypes.c_void_p(p["absmax_scale"].data_ptr()), 64,
-                              ctypes.c_void_p(y.data_ptr()), M, N, K, w4.BF16, None, 0, sptr)
+                              ctypes.c_void_p(y.data_ptr()), M, N, K, w4.BF16, wsp, wsb, sptr)
         t = timer.time(call, 20)
         byt = wb + 2 * M * K + 2 * M * N
         pts.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 2),
                     "weight_GBps": round(wb / t / 1e9, 1),
                     "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1)})
     return {"workload": "NF4 28672x8192, blocksize 64, double quant 256, bf16",
-            "kernel": "nf4_decode_kernel<bf16>", "points": pts}
+            "kernel": "nf4_decode_kernel<bf16> (M=1), int4_prefill_kernel<bf16, NF4> (M=32)",
+            "points": pts}
 
 
 def cpu_baseline(xs, outs):

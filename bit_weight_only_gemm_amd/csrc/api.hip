@@ -247,8 +247,7 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_
 
 int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize) {
   if (M <= 0 || validate_nf4_shape(N, K, blocksize) != W4A16_OK) return -1;
-  (void)M;
-  return 0;
+  return nf4_workspace_bytes_for(M, N, K);
 }
 
 int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
@@ -260,7 +259,8 @@ int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({x, qweight, absmax_q, absmax_scale, out})) return s;
   if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
-  (void)workspace_bytes;
+  const int64_t need = nf4_workspace_bytes_for(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return W4A16_ERR_WORKSPACE;
   clear_pending_error();
   return hip_status(launch_nf4_gemm(x, qweight, absmax_q, absmax_scale, codebook(), out, M, N, K,
                                     dtype, workspace, workspace_bytes, (hipStream_t)stream));

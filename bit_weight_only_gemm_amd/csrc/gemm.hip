@@ -636,10 +636,19 @@ static void launch_nf4_dt(const void* x, const uint8_t* q, const uint8_t* aq, co
     launch_nf4_v<DT, 4, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
 }
 
+int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K) {
+  return nf4_use_prefill(M, N, K) ? prefill_workspace_bytes(M, N, K) : 0;
+}
+
 hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,
-                           int64_t N, int64_t K, int dtype, void* /*workspace*/,
+                           int64_t N, int64_t K, int dtype, void* workspace,
                            int64_t /*workspace_bytes*/, hipStream_t stream) {
+  if (nf4_use_prefill(M, N, K)) {
+    launch_nf4_prefill(x, qweight, absmax_q, absmax_scale, L, out, workspace, M, N, K, dtype,
+                       stream);
+    return hipGetLastError();
+  }
   const bool batch = K % 1024 == 0;
   if (dtype == DT_F16) {
     if (batch)

@@ -54,6 +54,18 @@ void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_
                          const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
                          int64_t K, int dtype, hipStream_t stream);
 
+void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
+                        const float* absmax_scale, const Nf4Table& L, void* out, void* ws,
+                        int64_t M, int64_t N, int64_t K, int dtype, hipStream_t stream);
+// Whether nf4_gemm runs the large-M kernel at this shape (its codebook
+// dequant costs about twice the INT4 one, so the crossover is later: from 64
+// rows, or 32 on layers of 32 Mi weights and more), and the workspace bytes
+// it then needs.
+inline bool nf4_use_prefill(int64_t M, int64_t N, int64_t K) {
+  return K % 128 == 0 && (M >= 64 || (M >= 32 && N * K >= (int64_t)32 << 20));
+}
+int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K);
+
 hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,
                            int64_t N, int64_t K, int dtype, void* workspace,

@@ -76,13 +76,26 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff,
 // put it in the scalar offset (fewer registers).
 // Split-K: workgroup z of S takes K tiles [z KT / S, (z + 1) KT / S) and, when
 // S > 1, writes its fp32 partial tile to part[z][M][N] for split_reduce_kernel.
-template <int DT, int BM, bool TAIL>
+//
+// Weight formats (FMT): INT4 reads the repacked tiles as above.  NF4 reads the
+// canonical layout (row n: K / 2 bytes, element 2 j in the low nibble of byte
+// j): for K tile t, lane l loads the 32 bytes holding inputs
+// 128 t + 64 (l >> 5) .. + 63 of its column, one 64-element absmax block, and
+// word j of them is the B operand of step j; the activation operand of step j
+// is then chunk 8 (l >> 5) + j of the tile (the K order inside a tile is the
+// same permutation on both sides).  Dequant: w = round16(L[c] * a'), a' =
+// absmax_q * absmax_scale, L from LDS.  NF4 here needs K % 128 == 0.
+enum { FMT_INT4 = 0, FMT_NF4 = 1 };
+
+template <int DT, int BM, bool TAIL, int FMT>
 __global__ void __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
 int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                    uint16_t* __restrict__ out, float* __restrict__ part, int M, int N, int K,
-                    int KT, int NP, int S) {
+                    Nf4Table L, uint16_t* __restrict__ out, float* __restrict__ part, int M,
+                    int N, int K, int KT, int NP, int S) {
   typedef typename Op<DT>::vec vec;
+  __shared__ float lut[16];
+  if (FMT == FMT_NF4 && threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
   constexpr int PF_BM = BM;
   constexpr int PF_MT = BM / 32;
   constexpr int PF_STAGE = BM * PF_ROWB;
@@ -116,18 +129,50 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   // l & 15 of its meta.
   const bool pv = p < NP;
   const size_t pp = pv ? (size_t)p : 0;
-  const rsrc_t rc = make_rsrc(codes + pp * KT * 4096, pv ? (uint32_t)KT * 4096u : 0u);
-  const rsrc_t rs = make_rsrc(scales + pp * KT8 * 1024, pv ? (uint32_t)KT8 * 1024u : 0u);
-  const rsrc_t rz = make_rsrc(zeros + pp * KT8 * 256, pv ? (uint32_t)KT8 * 256u : 0u);
-  uint32_t vcode[2][2], vmeta[2];
+  rsrc_t rc, rs, rz;
+  uint32_t vcode[2][2], vmeta[2], gblk[2];
+  if constexpr (FMT == FMT_INT4) {
+    rc = make_rsrc(codes + pp * KT * 4096, pv ? (uint32_t)KT * 4096u : 0u);
+    rs = make_rsrc(scales + pp * KT8 * 1024, pv ? (uint32_t)KT8 * 1024u : 0u);
+    rz = make_rsrc(zeros + pp * KT8 * 256, pv ? (uint32_t)KT8 * 256u : 0u);
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int ct = 2 * g + ((lane & 31) >> 4);
+    for (int g = 0; g < 2; ++g) {
+      const int ct = 2 * g + ((lane & 31) >> 4);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-      vcode[g][h2] = (uint32_t)(ct * 1024 + (i16 + 16 * (2 * h2 + h)) * 16);
-    vmeta[g] = (uint32_t)(ct * 16 + i16);
+      for (int h2 = 0; h2 < 2; ++h2)
+        vcode[g][h2] = (uint32_t)(ct * 1024 + (i16 + 16 * (2 * h2 + h)) * 16);
+      vmeta[g] = (uint32_t)(ct * 16 + i16);
+    }
+  } else {
+    // rows of this panel (N % 16 == 0; rows past N read 0 -> a' = 0)
+    const int nrows = pv ? min(64, N - p * 64) : 0;
+    const uint32_t Kb = (uint32_t)K / 2u, Kblk = (uint32_t)K / 64u;
+    rc = make_rsrc(codes + pp * 64 * Kb, (uint32_t)nrows * Kb);
+    rs = make_rsrc(scales + pp * 64 * Kblk, (uint32_t)nrows * Kblk);
+    rz = make_rsrc(zeros, (uint32_t)(((int64_t)N * Kblk + 255) / 256 * 4));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int c = 32 * g + (lane & 31);
+      vcode[g][0] = (uint32_t)c * Kb + 32u * (uint32_t)h;
+      vcode[g][1] = vcode[g][0] + 16u;
+      vmeta[g] = (uint32_t)c * Kblk + (uint32_t)h;
+      gblk[g] = (uint32_t)(pp * 64 + c) * Kblk + (uint32_t)h;
+    }
   }
+  // the weights and meta of K tile t for column group g
+  auto load_w = [&](int t, int g, u32x4_t (&w)[2], uint32_t& sa, uint32_t& za) {
+    if constexpr (FMT == FMT_INT4) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) w[h2] = bld128(rc, vcode[g][h2], t * 4096);
+      sa = bld16(rs, vmeta[g] * 16u, (t >> 3) * 1024 + (t & 7) * 2);
+      za = bld32(rz, vmeta[g] * 4u, (t >> 3) * 256);
+    } else {
+      w[0] = bld128(rc, vcode[g][0], t * 64);
+      w[1] = bld128(rc, vcode[g][1], t * 64);
+      sa = __builtin_amdgcn_raw_buffer_load_b8(rs, vmeta[g], 2 * t, 0);
+      za = bld32(rz, ((gblk[g] + 2u * (uint32_t)t) >> 8) * 4u, 0);
+    }
+  };
 
   float16_t acc[PF_MT][2];
 #pragma unroll
@@ -140,12 +185,7 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
 
   // ---- prologue: K tile 0
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) cw[g][h2] = bld128(rc, vcode[g][h2], tb * 4096);
-    sc[g] = bld16(rs, vmeta[g] * 16u, (tb >> 3) * 1024 + (tb & 7) * 2);
-    zz[g] = bld32(rz, vmeta[g] * 4u, (tb >> 3) * 256);
-  }
+  for (int g = 0; g < 2; ++g) load_w(tb, g, cw[g], sc[g], zz[g]);
 #pragma unroll
   for (int i = 0; i < PF_ALD; ++i)
     lds_dma16(rx, As + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
@@ -158,12 +198,7 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     // previous barrier
     const int tn = min(t + 1, te - 1);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) cn[g][h2] = bld128(rc, vcode[g][h2], tn * 4096);
-      sn[g] = bld16(rs, vmeta[g] * 16u, (tn >> 3) * 1024 + (tn & 7) * 2);
-      zn[g] = bld32(rz, vmeta[g] * 4u, (tn >> 3) * 256);
-    }
+    for (int g = 0; g < 2; ++g) load_w(tn, g, cn[g], sn[g], zn[g]);
     uint8_t* sw = As + ((t - tb + 1) & 1) * PF_STAGE;
     // the activation loads of tile t + 1 are spread over the first
     // PF_DMA_STEPS steps of tile t (a burst of them stalls the issuing waves
@@ -179,18 +214,41 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     // spread between the step's MFMAs (each 32 x 32 x 16 MFMA keeps the matrix
     // pipe busy long enough to issue several VALU instructions behind it).
     QParam<DT> qp[2];
+    float ap[2];  // NF4: a' of this lane's block
 #pragma unroll
-    for (int g = 0; g < 2; ++g) qp[g].set(sc[g] & 0xFFFFu, (zz[g] >> (4 * (t & 7))) & 0xFu);
+    for (int g = 0; g < 2; ++g) {
+      if constexpr (FMT == FMT_INT4)
+        qp[g].set(sc[g] & 0xFFFFu, (zz[g] >> (4 * (t & 7))) & 0xFu);
+      else
+        ap[g] = (float)(sc[g] & 0xFFu) * __builtin_bit_cast(float, zz[g]);
+    }
+    // B operand of step s for column group g
+    auto operand = [&](int s, int g) -> vec {
+      if constexpr (FMT == FMT_INT4) {
+        return dequant_word(cw[g][s & 1][s >> 1], qp[g]);
+      } else {
+        const uint32_t w = cw[g][s >> 2][s & 3];
+        vec v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = lut[(w >> (4 * e)) & 0xFu] * ap[g];
+          if constexpr (DT == DT_F16) v[e] = (_Float16)f;
+          else v[e] = (__bf16)f;
+        }
+        return v;
+      }
+    };
     const uint8_t* st = As + ((t - tb) & 1) * PF_STAGE;
     auto read_step = [&](int s, vec (&a)[PF_MT]) {
-      const int q = 2 * s + h;  // 8-element chunk of this lane's inputs
+      // 8-element chunk of this lane's inputs in step s
+      const int q = FMT == FMT_INT4 ? 2 * s + h : 8 * h + s;
 #pragma unroll
       for (int m = 0; m < PF_MT; ++m)
         a[m] = *(const vec*)(st + (m * 32 + (lane & 31)) * PF_ROWB + ((q ^ i16) << 4));
     };
     vec b[2], a[PF_MT];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) b[g] = dequant_word(cw[g][0][0], qp[g]);
+    for (int g = 0; g < 2; ++g) b[g] = operand(0, g);
     read_step(0, a);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -206,7 +264,7 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
         read_step(sn1, an);
 #endif
 #pragma unroll
-        for (int g = 0; g < 2; ++g) bn[g] = dequant_word(cw[g][sn1 & 1][sn1 >> 1], qp[g]);
+        for (int g = 0; g < 2; ++g) bn[g] = operand(sn1, g);
       }
 #pragma unroll
       for (int m = 0; m < PF_MT; ++m)
@@ -326,25 +384,25 @@ int64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return pl.splits > 1 ? ceil_div((int64_t)pl.splits * M * N * 4, 256) * 256 : 0;
 }
 
-template <int DT, int BM>
+template <int DT, int BM, int FMT>
 static void launch_prefill_bm(const void* x, const void* codes_r, const void* scales_r,
-                              const void* zeros_r, void* out, float* part, int S, int64_t M,
-                              int64_t N, int64_t K, hipStream_t stream) {
+                              const void* zeros_r, const Nf4Table& L, void* out, float* part,
+                              int S, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t NP = ceil_div(N, 64);
   const int KT = (int)(K / 128);
   const unsigned gx = (unsigned)ceil_div(NP, PF_WAVES);
   const int64_t full = M / BM;
   // the timing events (if set) go to the first launch
   if (full > 0)
-    launch_timed(int4_prefill_kernel<DT, BM, false>, dim3(gx, (unsigned)full, (unsigned)S),
+    launch_timed(int4_prefill_kernel<DT, BM, false, FMT>, dim3(gx, (unsigned)full, (unsigned)S),
                  dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
-                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, (uint16_t*)out, part, (int)M,
-                 (int)N, (int)K, KT, (int)NP, S);
+                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, L, (uint16_t*)out, part,
+                 (int)M, (int)N, (int)K, KT, (int)NP, S);
   if (M % BM)
-    launch_timed(int4_prefill_kernel<DT, BM, true>, dim3(gx, 1, (unsigned)S),
+    launch_timed(int4_prefill_kernel<DT, BM, true, FMT>, dim3(gx, 1, (unsigned)S),
                  dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
-                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, (uint16_t*)out, part, (int)M,
-                 (int)N, (int)K, KT, (int)NP, S);
+                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, L, (uint16_t*)out, part,
+                 (int)M, (int)N, (int)K, KT, (int)NP, S);
   if (S > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(split_reduce_kernel<DT>, dim3((unsigned)ceil_div(MN / 4, (int64_t)256)),
@@ -352,29 +410,44 @@ static void launch_prefill_bm(const void* x, const void* codes_r, const void* sc
   }
 }
 
-template <int DT>
+template <int DT, int FMT>
 static void launch_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
-                              const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
-                              int64_t K, hipStream_t stream) {
+                              const void* zeros_r, const Nf4Table& L, void* out, void* ws,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const PrefillPlan pl = plan_prefill(M, N, K);
   float* part = (float*)ws;
   if (pl.bm == 64)
-    launch_prefill_bm<DT, 64>(x, codes_r, scales_r, zeros_r, out, part, pl.splits, M, N, K, stream);
+    launch_prefill_bm<DT, 64, FMT>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M, N,
+                                   K, stream);
   else if (pl.bm == 128)
-    launch_prefill_bm<DT, 128>(x, codes_r, scales_r, zeros_r, out, part, pl.splits, M, N, K,
-                               stream);
+    launch_prefill_bm<DT, 128, FMT>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M, N,
+                                    K, stream);
   else
-    launch_prefill_bm<DT, 256>(x, codes_r, scales_r, zeros_r, out, part, pl.splits, M, N, K,
-                               stream);
+    launch_prefill_bm<DT, 256, FMT>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M, N,
+                                    K, stream);
 }
 
 void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
                          const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
                          int64_t K, int dtype, hipStream_t stream) {
+  const Nf4Table none{};
   if (dtype == DT_F16)
-    launch_prefill_dt<DT_F16>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, stream);
+    launch_prefill_dt<DT_F16, FMT_INT4>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N, K,
+                                        stream);
   else
-    launch_prefill_dt<DT_BF16>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, stream);
+    launch_prefill_dt<DT_BF16, FMT_INT4>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N, K,
+                                         stream);
+}
+
+void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
+                        const float* absmax_scale, const Nf4Table& L, void* out, void* ws,
+                        int64_t M, int64_t N, int64_t K, int dtype, hipStream_t stream) {
+  if (dtype == DT_F16)
+    launch_prefill_dt<DT_F16, FMT_NF4>(x, qweight, absmax_q, absmax_scale, L, out, ws, M, N, K,
+                                       stream);
+  else
+    launch_prefill_dt<DT_BF16, FMT_NF4>(x, qweight, absmax_q, absmax_scale, L, out, ws, M, N, K,
+                                        stream);
 }
 
 }  // namespace w4a16

@@ -216,7 +216,11 @@ int nf4_codebook(float* out16_host);
 int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_t* qweight,
                  uint8_t* absmax_q, float* absmax_scale, void* stream);
 
-/* Workspace bytes nf4_gemm needs at this shape (currently always 0). */
+/*
+ * Workspace bytes nf4_gemm needs at this shape: the fp32 split-K partials of
+ * the large-M kernel (K % 128 == 0 and M >= 64, or M >= 32 on layers of 32 Mi
+ * weights and more) when it splits K; 0 otherwise.
+ */
 int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
 
 /*
@@ -226,7 +230,9 @@ int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
  *   w[n, k] = round_dtype(fp32(L[c] * a')),  a' = fp32(fp32(absmax_q[b]) *
  *   absmax_scale[b / 256]),  b = (n*K + k) / blocksize.
  *   x [M, K] and out [M, N] row-major in dtype; qweight/absmax as nf4_quantize.
- * Constraints: M >= 1, blocksize == 64, K % 64 == 0, N % 16 == 0.  Async.
+ * Constraints: M >= 1, blocksize == 64, K % 64 == 0, N % 16 == 0.
+ * workspace: at least nf4_workspace_bytes(M, N, K, 64) bytes when that is > 0
+ * (W4A16_ERR_WORKSPACE otherwise).  Async.
  */
 int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
              const float* absmax_scale, int32_t blocksize, void* out, int64_t M, int64_t N,

@@ -106,3 +106,35 @@ def test_nf4_gemm_onehot_exact_k1024():
     y = tensor_bits(w4.nf4_gemm(bits_to_tensor(synth.to_f16_bits(x), "f16"), p))
     for r, k in enumerate(ks):
         assert np.array_equal(y[r], wd[:, k]), k
+
+
+@pytest.mark.parametrize("M", [12, 32, 64, 96, 300])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nf4_gemm_large_m(M, dtype):
+    # the large-M kernel (K % 128 == 0): 32 x 32 MFMA tiles with the NF4 codes
+    # read from the canonical layout, split K where the grid is small
+    N, K = 160, 2048
+    say("nf4 large M", M, dtype, "workspace", w4.nf4_workspace_bytes(M, N, K))
+    W = synth.weights("gpu/nf4L/W", N, K)
+    xb = synth.to_bits(synth.activations("gpu/nf4L/x/%d" % M, M, K), dtype)
+    p = _pack(W)
+    y = w4.nf4_gemm(bits_to_tensor(xb, dtype), p)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)
+    assert compare_gemm(y, xb, wd, dtype) <= TOL
+
+
+def test_nf4_large_m_onehot_exact():
+    N, K = 96, 1024
+    W = synth.weights("gpu/nf4L/onehot", N, K)
+    p = _pack(W)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, "bf16")
+    M = 64
+    ks = (np.arange(M) * 37 + 5) % K
+    x = np.zeros((M, K), dtype=np.float32)
+    x[np.arange(M), ks] = 1.0
+    y = tensor_bits(w4.nf4_gemm(bits_to_tensor(synth.to_bf16_bits(x), "bf16"), p))
+    assert np.array_equal(y, wd[:, ks].T)
