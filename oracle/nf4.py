@@ -21,7 +21,7 @@ construction: 8 positive levels at Phi^-1 of 8 equal steps from 1/2 to delta,
 divided by Phi^-1(delta) so the range is [-1, 1], with
 delta = ((1 - 1/30) + (1 - 1/32)) / 2.  Levels are rounded once to fp32.
 
-Other readings (listed in the design doc):
+Other readings taken where the pages are silent:
 * a block is 64 consecutive elements of row-major W [N, K] (K % 64 == 0);
 * code = argmin_i |w/absmax - L_i| with w/absmax and the distances in fp32;
   ties go to the lower index; an all-zero block gives code 7 (L_7 = 0);

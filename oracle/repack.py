@@ -6,7 +6,8 @@ for byte, and so that ``unrepack_ref(repack_ref(.))`` pins it as a bijection.
 The point of repacking once, offline, is the one [P5] "关键数据解读" item 4
 makes: a format whose layout is translated on every run is slow.
 
-Layout (G = 128, KT = K / G, NP = ceil(N / 64)):
+Layout (K tiles of 128 inputs, KT = K / 128, NP = ceil(N / 64); group size G
+in {32, 64} or a multiple of 128 that divides K, G = K being per-channel):
 
 * Column permutation.  If ``g_idx`` is given and is not the trivial
   k // G map, ``perm`` = stable argsort(g_idx): permuted column k' is original
@@ -16,11 +17,17 @@ Layout (G = 128, KT = K / G, NP = ceil(N / 64)):
   permuted column k' = 128t + 32j + 8b + e, the code sits in lane l = i + 16b,
   32-bit word j of that lane's 16 bytes (little endian), at nibble slot
   (e >> 1) + 4 * (e & 1).  Columns n >= N are zero padding.
-* Scales, in runs of 8 groups (KT8 = ceil(KT / 8)): fp16 [NP][KT8][4][16][8],
-  entry [p][g][c][i][s] = scale of column 64p + 16c + i in group 8g + s
-  (0 for padding columns and for groups >= KT).
-* Zeros: uint32 [NP][KT8][4][16], bits [4s, 4s + 4) of [p][g][c][i] = zero
-  of column 64p + 16c + i in group 8g + s (0 for padding).
+* Meta units: U = 128 / G units per K tile when G < 128 (unit u of tile t
+  covers permuted columns 128t + uG ..; word j of a lane lies in unit
+  jU / 4), else U = 1 and the unit of tile t carries the scale and zero of the
+  group holding columns 128t .. 128t + 127 (repeated on each tile of a group
+  that spans several).  Units are numbered v = tU + u.
+* Scales, in runs of 8 tiles (KT8 = ceil(KT / 8)): fp16 [NP][KT8][4][16][8U],
+  entry [p][g][c][i][r] = scale of column 64p + 16c + i in unit 8Ug + r
+  (0 for padding columns and for units past the last tile).
+* Zeros: uint32 [NP][KT8][4][16][U], bits [4e, 4e + 4) of word w of
+  [p][g][c][i] = zero of column 64p + 16c + i in unit 8Ug + 8w + e (0 for
+  padding).  A symmetric weight (no zeros) has no zeros array.
 """
 
 import numpy as np
@@ -28,10 +35,27 @@ import numpy as np
 from .int4 import unpack_qweight, unpack_qzeros, default_g_idx
 
 GROUP = 128
+TILE = 128
 
 
 def nibble_slot(e):
     return (e >> 1) + 4 * (e & 1)
+
+
+def valid_group_size(K, G):
+    return K % TILE == 0 and (G in (32, 64) or (G > 0 and G % TILE == 0 and K % G == 0))
+
+
+def units_per_tile(G):
+    return TILE // G if G < TILE else 1
+
+
+def unit_groups(K, G):
+    """Group (in permuted column order) of every meta unit v = t U + u."""
+    U, KT = units_per_tile(G), K // TILE
+    t = np.arange(KT)[:, None]
+    u = np.arange(U)[None, :]
+    return ((TILE * t + u * min(G, TILE)) // G).reshape(-1)
 
 
 def canonical_perm(g_idx, K, group_size=GROUP):
@@ -45,24 +69,24 @@ def canonical_perm(g_idx, K, group_size=GROUP):
 
 
 def repack_ref(qweight, scales, qzeros, g_idx=None, group_size=GROUP):
-    """Canonical GPTQ-style tensors -> (codes_r, scales_r, zeros_r, perm)."""
-    assert group_size == GROUP
+    """Canonical GPTQ-style tensors -> (codes_r, scales_r, zeros_r, perm).
+
+    ``qzeros=None`` (symmetric) gives zeros_r = None."""
+    G = int(group_size)
     q = unpack_qweight(qweight)                      # [N, K]
     N, K = q.shape
-    z = unpack_qzeros(qzeros)[:, :N]                 # [KT, N]
-    s = np.asarray(scales, dtype=np.float16)         # [KT, N]
-    KT = K // GROUP
+    assert valid_group_size(K, G)
+    s = np.asarray(scales, dtype=np.float16)         # [K/G, N]
+    z = None if qzeros is None else unpack_qzeros(qzeros)[:, :N]
+    KT = K // TILE
+    U = units_per_tile(G)
     NP = (N + 63) // 64
-    perm = canonical_perm(g_idx, K, group_size)
+    perm = canonical_perm(g_idx, K, G)
     if perm is not None:
         q = q[:, perm]
     Np = NP * 64
     qp = np.zeros((Np, K), dtype=np.uint8)
     qp[:N] = q
-    zp = np.zeros((KT, Np), dtype=np.uint8)
-    zp[:, :N] = z
-    sp = np.zeros((KT, Np), dtype=np.float16)
-    sp[:, :N] = s
 
     # qp[n, k'] with n = 64p + 16c + i and k' = 128t + 32j + 8b + e
     v = qp.reshape(NP, 4, 16, KT, 4, 4, 8).astype(np.uint32)   # p c i t j b e
@@ -74,23 +98,31 @@ def repack_ref(qweight, scales, qzeros, g_idx=None, group_size=GROUP):
     codes_r = np.ascontiguousarray(words).view(np.uint8).reshape(-1)
 
     KT8 = (KT + 7) // 8
-    sp8 = np.zeros((KT8 * 8, Np), dtype=np.float16)
-    sp8[:KT] = sp
-    zp8 = np.zeros((KT8 * 8, Np), dtype=np.uint32)
-    zp8[:KT] = zp
-    # [g s][p c i] -> [p][g][c][i][s]
-    scales_r = sp8.reshape(KT8, 8, NP, 4, 16).transpose(2, 0, 3, 4, 1).copy()
-    zz = zp8.reshape(KT8, 8, NP, 4, 16).transpose(2, 0, 3, 4, 1)          # p g c i s
-    zeros_r = np.zeros((NP, KT8, 4, 16), dtype=np.uint32)
-    for t8 in range(8):
-        zeros_r |= zz[..., t8] << np.uint32(4 * t8)
-    return codes_r, scales_r.reshape(-1), zeros_r.reshape(-1), perm
+    V8 = KT8 * 8 * U                                  # units incl. the last run's padding
+    ug = unit_groups(K, G)                            # [KT * U]
+    su = np.zeros((V8, Np), dtype=np.float16)
+    su[:KT * U, :N] = s[ug]
+    # [g r][p c i] -> [p][g][c][i][r]
+    scales_r = su.reshape(KT8, 8 * U, NP, 4, 16).transpose(2, 0, 3, 4, 1).copy().reshape(-1)
+    zeros_r = None
+    if z is not None:
+        zu = np.zeros((V8, Np), dtype=np.uint32)
+        zu[:KT * U, :N] = z[ug]
+        zz = zu.reshape(KT8, U, 8, NP, 4, 16).transpose(3, 0, 4, 5, 1, 2)   # p g c i w e
+        zr = np.zeros((NP, KT8, 4, 16, U), dtype=np.uint32)
+        for e in range(8):
+            zr |= zz[..., e] << np.uint32(4 * e)
+        zeros_r = zr.reshape(-1)
+    return codes_r, scales_r, zeros_r, perm
 
 
-def unrepack_ref(codes_r, scales_r, zeros_r, K, N):
+def unrepack_ref(codes_r, scales_r, zeros_r, K, N, group_size=GROUP):
     """Inverse of the tile layout: -> (codes [N, K] in permuted column order,
-    scales fp16 [KT, N], zeros uint8 [KT, N])."""
-    KT = K // GROUP
+    scales fp16 [K/G, N], zeros uint8 [K/G, N] or None).  Raises if the units
+    of one group disagree."""
+    G = int(group_size)
+    KT = K // TILE
+    U = units_per_tile(G)
     NP = (N + 63) // 64
     words = np.asarray(codes_r, dtype=np.uint8).view(np.uint32).reshape(NP, KT, 4, 4, 16, 4)
     # p t c b i j -> p c i t j b
@@ -100,11 +132,23 @@ def unrepack_ref(codes_r, scales_r, zeros_r, K, N):
         v[..., e] = (words >> np.uint32(4 * nibble_slot(e))) & np.uint32(0xF)
     q = v.reshape(NP * 64, K)[:N]
     KT8 = (KT + 7) // 8
-    s8 = np.asarray(scales_r, dtype=np.float16).reshape(NP, KT8, 4, 16, 8)
-    s = s8.transpose(1, 4, 0, 2, 3).reshape(KT8 * 8, NP * 64)[:KT, :N]
-    zr = np.asarray(zeros_r, dtype=np.uint32).reshape(NP, KT8, 4, 16)
-    z8 = np.zeros((NP, KT8, 4, 16, 8), dtype=np.uint8)
-    for t8 in range(8):
-        z8[..., t8] = (zr >> np.uint32(4 * t8)) & np.uint32(0xF)
-    z = z8.transpose(1, 4, 0, 2, 3).reshape(KT8 * 8, NP * 64)[:KT, :N]
-    return q.copy(), s.copy(), z.copy()
+    ug = unit_groups(K, G)
+
+    def from_units(units):                           # [KT * U, N] -> [K / G, N]
+        out = units[np.searchsorted(ug, np.arange(K // G))]
+        if not np.array_equal(units, out[ug]):
+            raise ValueError("meta units of one group disagree")
+        return out
+
+    su = np.asarray(scales_r, dtype=np.float16).reshape(NP, KT8, 4, 16, 8 * U)
+    su = su.transpose(1, 4, 0, 2, 3).reshape(KT8 * 8 * U, NP * 64)[:KT * U, :N]
+    s = from_units(su)
+    z = None
+    if zeros_r is not None:
+        zr = np.asarray(zeros_r, dtype=np.uint32).reshape(NP, KT8, 4, 16, U)
+        z8 = np.zeros((NP, KT8, 4, 16, U, 8), dtype=np.uint8)
+        for e in range(8):
+            z8[..., e] = (zr >> np.uint32(4 * e)) & np.uint32(0xF)
+        zu = z8.transpose(1, 4, 5, 0, 2, 3).reshape(KT8 * 8 * U, NP * 64)[:KT * U, :N]
+        z = from_units(zu)
+    return q.copy(), s.copy(), None if z is None else z.copy()

@@ -159,3 +159,97 @@ def test_repack_meta_addressing_single_group():
         idx = (((p * KT8 + g) * 4 + c) * 16 + i)
         assert scales_r[idx * 8 + s8] == np.float16(0.5) and np.count_nonzero(scales_r) == 1
         assert zeros_r[idx] == 0xD << (4 * s8) and np.count_nonzero(zeros_r) == 1
+
+
+# ------------------------------------------- repack: group sizes and symmetric (f2)
+
+@pytest.mark.parametrize("G,K", [(32, 512), (64, 1280), (256, 1024), (1280, 1280),
+                                 (2048, 2048)])
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("act_order", [False, True])
+def test_repack_group_sizes_bijection(G, K, sym, act_order):
+    N = 200
+    W = synth.weights(f"test/repack/G/{G}/{K}", N, K)
+    gi = synth.act_order_gidx(f"test/repack/G/g/{G}/{K}", K, G) if act_order else None
+    q, s, z = int4.quantize_rtn_int4(W, G, gi, sym=sym)
+    codes_r, scales_r, zeros_r, perm = repack.repack_ref(
+        int4.pack_qweight(q), s, None if sym else int4.pack_qzeros(z), gi, G)
+    U = repack.units_per_tile(G)
+    NP, KT8 = (N + 63) // 64, (K // 128 + 7) // 8
+    assert codes_r.size == NP * (K // 128) * 4096
+    assert scales_r.size == NP * KT8 * 512 * U
+    assert (zeros_r is None) == sym
+    if not sym:
+        assert zeros_r.size == NP * KT8 * 64 * U
+    # act-order with one group per row (G = K) is the trivial map: no perm
+    assert (perm is None) == (not act_order or G == K)
+    q2, s2, z2 = repack.unrepack_ref(codes_r, scales_r, zeros_r, K, N, G)
+    qp = q if perm is None else q[:, perm]
+    assert np.array_equal(q2, qp) and np.array_equal(s2, s)
+    assert (z2 is None) if sym else np.array_equal(z2, z)
+
+
+def test_units_per_tile_and_unit_groups_closed_form():
+    assert [repack.units_per_tile(G) for G in (32, 64, 128, 256, 4096)] == [4, 2, 1, 1, 1]
+    # word j of a lane covers permuted columns 128t + 32j + 8b + e: its unit
+    # j U / 4 must hold the group of every one of those columns
+    for G in (32, 64, 128, 256, 512):
+        K = 1024
+        U = repack.units_per_tile(G)
+        ug = repack.unit_groups(K, G)
+        assert ug.size == (K // 128) * U
+        for t in range(K // 128):
+            for j in range(4):
+                for b in range(4):
+                    for e in range(8):
+                        k = 128 * t + 32 * j + 8 * b + e
+                        assert ug[t * U + j * U // 4] == k // G
+
+
+@pytest.mark.parametrize("G", [32, 64, 256])
+def test_repack_meta_addressing_group_sizes(G):
+    # one nonzero scale / zero lands at the documented unit index and nibble,
+    # repeated on every tile of a group that spans several tiles
+    K, N = 2048, 128
+    KT, U = K // 128, repack.units_per_tile(G)
+    KT8 = (KT + 7) // 8
+    rr = np.random.default_rng(11 + G)
+    for _ in range(12):
+        n, g = int(rr.integers(N)), int(rr.integers(K // G))
+        s = np.zeros((K // G, N), np.float16)
+        z = np.zeros((K // G, N), np.uint8)
+        s[g, n] = 0.25
+        z[g, n] = 0xC
+        _, scales_r, zeros_r, _ = repack.repack_ref(
+            int4.pack_qweight(np.zeros((N, K), np.uint8)), s, int4.pack_qzeros(z), None, G)
+        p, c, i = n // 64, (n % 64) // 16, n % 16
+        if G < 128:
+            units = [g]                                    # unit v = t U + u = g
+        else:
+            units = list(range(g * G // 128, (g + 1) * G // 128))
+        want_z = {}
+        for v in units:
+            run, r = v // (8 * U), v % (8 * U)
+            base = ((p * KT8 + run) * 4 + c) * 16 + i
+            assert scales_r[base * 8 * U + r] == np.float16(0.25)
+            want_z[base * U + r // 8] = want_z.get(base * U + r // 8, 0) | 0xC << (4 * (r % 8))
+        assert np.count_nonzero(scales_r) == len(units)
+        assert set(np.nonzero(zeros_r)[0].tolist()) == set(want_z)
+        for w, v in want_z.items():
+            assert zeros_r[w] == v
+
+
+def test_symmetric_small_group_product_within_closed_form_bound():
+    # symmetric RTN with G = 32: every weight is within s/2 of its level
+    # (nothing clamps for |w| <= max|w|), plus the fp16 round of the level
+    M, N, K, G = 3, 16, 512, 32
+    W = synth.weights("test/gemm/bound/sym", N, K)
+    x = synth.to_f16_bits(synth.activations("test/gemm/bound/sym/x", M, K))
+    q, s, _ = int4.quantize_rtn_int4(W, G, sym=True)
+    wd = int4.dequant_int4(int4.pack_qweight(q), s, None, None, G, "f16")
+    xf = fp.bits_to_f64(x, "f16")
+    y_ref = gemm.gemm_ref_bits(x, wd, "f16")
+    y_flt = gemm.gemm_ref_fp64(xf, W.astype(np.float64))
+    sk = s.astype(np.float64)[np.arange(K) // G].T
+    per_w = sk * 0.5 * (1 + 1e-6) + 2.0**-11 * np.abs(fp.bits_to_f64(wd, "f16")) + 1e-12
+    assert np.all(np.abs(y_ref - y_flt) <= np.abs(xf) @ per_w.T)

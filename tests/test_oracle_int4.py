@@ -198,3 +198,134 @@ def test_q_equal_z_gives_zero_product():
     s = np.full((K // G, N), 0.01, dtype=np.float16)
     wd = int4.dequant_int4(int4.pack_qweight(q), s, int4.pack_qzeros(z), None, G, "f16")
     assert not np.any(wd & 0x7FFF)
+
+
+# ------------------------------------------- group sizes and symmetric codes (P2, P3)
+
+def _fp16_scales(r, shape):
+    # fp16 values with at most 11 significant bits: 15 s and 7 s are exact in fp32
+    return (r.uniform(0.002, 0.05, size=shape).astype(np.float16)).astype(np.float32)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128, 256, 1024])
+def test_rtn_recovers_an_exact_grid_per_group(G):
+    # w = (q - z) s with every (row, group) holding codes 0 and 15: then
+    # (max - min) / 15 = s, rint(-min / s) = z and rint(w / s) + z = q exactly,
+    # so a wrong group boundary (a different s or z) cannot reproduce q, s, z
+    N, K = 6, 1024
+    r = np.random.default_rng(21 + G)
+    ng = K // G
+    s = _fp16_scales(r, (ng, N))
+    z = r.integers(0, 16, size=(ng, N))
+    q = r.integers(0, 16, size=(N, K))
+    for g in range(ng):
+        q[:, g * G] = 0
+        q[:, g * G + G - 1] = 15
+    gk = np.arange(K) // G
+    W = ((q - z[gk].T) * s[gk].T).astype(np.float32)
+    q2, s2, z2 = int4.quantize_rtn_int4(W, G)
+    assert np.array_equal(q2, q) and np.array_equal(z2, z)
+    assert np.array_equal(s2.astype(np.float32), s)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128, 1024])
+def test_symmetric_rtn_recovers_an_exact_grid(G):
+    # w = c s, c in [-7, 7] with |c| = 7 in every (row, group): max|w| / 7 = s
+    # and rint(w / s) = c exactly; the stored nibble is c + 8, no zeros
+    N, K = 5, 1024
+    r = np.random.default_rng(40 + G)
+    ng = K // G
+    s = _fp16_scales(r, (ng, N))
+    c = r.integers(-7, 8, size=(N, K))
+    for g in range(ng):
+        c[:, g * G + 3] = np.where(r.random(N) < 0.5, 7, -7)
+    gk = np.arange(K) // G
+    W = (c * s[gk].T).astype(np.float32)
+    q, s2, z = int4.quantize_rtn_int4(W, G, sym=True)
+    assert z is None
+    assert np.array_equal(q.astype(np.int64), c + 8)
+    assert np.array_equal(s2.astype(np.float32), s)
+
+
+def test_symmetric_rtn_is_odd():
+    # rint is symmetric and max|w| is sign-blind: negating W mirrors every code
+    # about the zero nibble 8 (codes stay in [1, 15]: -8 is never produced)
+    W = synth.weights("test/sym/odd", 16, 512)
+    q1, s1, _ = int4.quantize_rtn_int4(W, 64, sym=True)
+    q2, s2, _ = int4.quantize_rtn_int4(-W, 64, sym=True)
+    assert q1.min() >= 1 and q2.min() >= 1
+    assert np.array_equal(q2.astype(np.int64), 16 - q1.astype(np.int64))
+    assert np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("G", [32, 64])
+def test_symmetric_rtn_nearest_level_brute_force(G):
+    W = synth.weights(f"test/sym/brute/{G}", 4, 256)
+    q, s, _ = int4.quantize_rtn_int4(W, G, sym=True)
+    for n in range(4):
+        for k in range(0, 256, 5):
+            sf = np.float64(s[k // G, n])
+            levels = np.arange(-8, 8) * sf                 # nibbles 0..15
+            d = np.abs(levels - np.float64(W[n, k]))
+            assert d[q[n, k]] <= d.min() + 1e-6 * sf
+            # and the error bound of a rounding to a grid of step s
+            assert d[q[n, k]] <= 0.5 * sf * (1 + 1e-6)
+
+
+def test_symmetric_degenerate_and_zero_group():
+    W = np.zeros((2, 64), dtype=np.float32)
+    W[1, 5] = 3.5
+    q, s, _ = int4.quantize_rtn_int4(W, 32, sym=True)
+    assert float(s[0, 0]) == 1.0 and np.all(q[0] == 8)       # all-zero group: s = 1
+    assert float(s[0, 1]) == 0.5 and q[1, 5] == 15 and q[1, 4] == 8
+    assert float(s[1, 1]) == 1.0
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_symmetric_dequant_exact_and_mirrored(dtype):
+    # no zeros: w = (q - 8) s exactly rounded; nibble 8 is +0 and nibbles
+    # 8 + k and 8 - k give values of opposite sign and equal magnitude
+    scales = _scale_set()
+    scales = scales[np.isfinite(scales.astype(np.float32)) & (scales != 0)]
+    G = 16
+    K = G * len(scales)
+    q = np.tile(np.arange(16, dtype=np.uint8), (3, K // 16))
+    s = np.tile(scales[:, None], (1, 3)).astype(np.float16)
+    got = int4.dequant_int4(int4.pack_qweight(q), s, None, None, G, dtype)
+    for k in range(K):
+        sv = Fraction(float(scales[k // G]))
+        exact = Fraction(int(q[0, k]) - 8) * sv
+        if dtype == "f16":
+            want = int(_f16_of_exact(float(exact)))
+        else:
+            t = torch.tensor([float(exact)], dtype=torch.float64).to(torch.bfloat16)
+            want = int(t.view(torch.int16).numpy().view(np.uint16)[0])
+        if q[0, k] == 8:
+            want = 0 if float(scales[k // G]) > 0 else 0x8000
+        assert int(got[0, k]) == want, (k, int(q[0, k]), float(scales[k // G]))
+    for k0 in range(0, K, 16):
+        for d in range(1, 8):
+            a, b = int(got[0, k0 + 8 + d]), int(got[0, k0 + 8 - d])
+            assert a ^ b == 0x8000
+
+
+def test_symmetric_equals_asymmetric_with_zero_eight():
+    K, N, G = 256, 16, 64
+    W = synth.weights("test/sym/z8", N, K)
+    q, s, _ = int4.quantize_rtn_int4(W, G, sym=True)
+    z8 = np.full((K // G, N), 8, dtype=np.uint8)
+    a = int4.dequant_int4(int4.pack_qweight(q), s, None, None, G, "bf16")
+    b = int4.dequant_int4(int4.pack_qweight(q), s, int4.pack_qzeros(z8), None, G, "bf16")
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("sym", [False, True])
+def test_small_group_act_order_equals_contiguous_groups(sym):
+    K, N, G = 512, 16, 32
+    W = synth.weights(f"test/gidx/g32/{sym}", N, K)
+    gi = synth.act_order_gidx(f"test/gidx/g32/g/{sym}", K, G)
+    perm = np.argsort(gi, kind="stable")
+    q1, s1, z1 = int4.quantize_rtn_int4(W, G, gi, sym=sym)
+    q2, s2, z2 = int4.quantize_rtn_int4(W[:, perm], G, None, sym=sym)
+    assert np.array_equal(q1[:, perm], q2) and np.array_equal(s1, s2)
+    assert (z1 is None and z2 is None) if sym else np.array_equal(z1, z2)
