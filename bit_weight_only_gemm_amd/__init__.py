@@ -89,16 +89,25 @@ def w4a16_make_perm(g_idx, group_size=GROUP, stream=None):
     return perm, bool(nt.value)
 
 
-def w4a16_quantize_rtn(W, group_size=GROUP, g_idx=None, perm=None, stream=None):
-    """RTN group quantization of W [N, K] fp32 -> (qweight, scales, qzeros)."""
+def _group(K, group_size):
+    """The group size in elements (-1 is per-channel: one group of K)."""
+    return K if group_size == -1 else group_size
+
+
+def w4a16_quantize_rtn(W, group_size=GROUP, g_idx=None, perm=None, sym=False, stream=None):
+    """RTN group quantization of W [N, K] fp32 -> (qweight, scales, qzeros).
+
+    ``sym=True``: symmetric codes (zero point fixed, stored offset by 8) and
+    qzeros = None."""
     _need(W, torch.float32, "W")
     N, K = W.shape
+    G = _group(K, group_size)
     if g_idx is not None and perm is None:
         perm, _ = w4a16_make_perm(g_idx, group_size, stream)
     dev = W.device
     qweight = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
-    scales = torch.empty((K // group_size, N), dtype=torch.float16, device=dev)
-    qzeros = torch.empty((K // group_size, N // 8), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // G, N), dtype=torch.float16, device=dev)
+    qzeros = None if sym else torch.empty((K // G, N // 8), dtype=torch.int32, device=dev)
     _lib.check(_lib.lib().w4a16_quantize_rtn(_ptr(W), _ptr(g_idx), _ptr(perm), N, K, group_size,
                                              _ptr(qweight), _ptr(scales), _ptr(qzeros),
                                              _stream(stream)), "w4a16_quantize_rtn")
@@ -106,17 +115,21 @@ def w4a16_quantize_rtn(W, group_size=GROUP, g_idx=None, perm=None, stream=None):
 
 
 def w4a16_repack(qweight, scales, qzeros, g_idx=None, group_size=GROUP, stream=None):
-    """Repack canonical tensors; returns dict(codes, scales, zeros, perm, K, N)."""
+    """Repack canonical tensors; returns dict(codes, scales, zeros, perm, K, N, group_size).
+
+    ``qzeros=None`` is a symmetric weight: the result then has zeros = None."""
     _need(qweight, torch.int32, "qweight")
     K8, N = qweight.shape
     K = K8 * 8
-    _need(scales, torch.float16, "scales", (K // group_size) * N)
-    _need(qzeros, torch.int32, "qzeros", (K // group_size) * (N // 8))
+    G = _group(K, group_size)
+    _need(scales, torch.float16, "scales", (K // G) * N)
+    if qzeros is not None:
+        _need(qzeros, torch.int32, "qzeros", (K // G) * (N // 8))
     nc, ns, nz = w4a16_repacked_bytes(K, N, group_size)
     dev = qweight.device
     codes_r = torch.empty(nc, dtype=torch.uint8, device=dev)
     scales_r = torch.empty(ns // 2, dtype=torch.float16, device=dev)
-    zeros_r = torch.empty(nz // 4, dtype=torch.int32, device=dev)
+    zeros_r = None if qzeros is None else torch.empty(nz // 4, dtype=torch.int32, device=dev)
     perm = None
     if g_idx is not None:
         _need(g_idx, torch.int32, "g_idx", K)
@@ -147,7 +160,7 @@ def w4a16_gemm(x, packed, out=None, workspace=None, use_workspace=True, stream=N
     if use_workspace:
         need = w4a16_workspace_bytes(M, N, K, G)
         if workspace is None and need > 0:
-            workspace = _ws_cache(x.device, need)
+            workspace = _ws_cache(x.device, need, stream)
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     else:
         workspace = None
@@ -204,7 +217,7 @@ def nf4_gemm(x, nf4, out=None, workspace=None, use_workspace=True, stream=None):
     if use_workspace:
         need = nf4_workspace_bytes(M, N, K, bs)
         if workspace is None and need > 0:
-            workspace = _ws_cache(x.device, need)
+            workspace = _ws_cache(x.device, need, stream)
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     else:
         workspace = None
@@ -224,16 +237,18 @@ def nf4_dequant(nf4, dtype=torch.bfloat16, stream=None):
     return w
 
 
-# One zero-filled workspace per (device, stream), grown on demand.  Every
-# completed call leaves it zeroed, so it is reused across calls on a stream.
+# One workspace per (device, stream), grown on demand and reused by later
+# calls on that stream (calls on one stream run in order; the kernels write
+# every workspace byte they read, so its contents do not matter).
 _WS = {}
 
 
-def _ws_cache(device, nbytes):
-    key = (str(device), torch.cuda.current_stream().cuda_stream)
+def _ws_cache(device, nbytes, stream=None):
+    st = torch.cuda.current_stream() if stream is None else stream
+    key = (str(device), st.cuda_stream)
     cur = _WS.get(key)
     if cur is None or cur.numel() * 4 < nbytes:
-        torch.cuda.current_stream().synchronize()
+        st.synchronize()
         cur = workspace(max(nbytes, 1 << 20), device)
         _WS[key] = cur
     return cur

@@ -19,7 +19,6 @@ using namespace w4a16;
 
 namespace {
 
-constexpr int kGroup = 128;
 constexpr int64_t kMaxM = (int64_t)1 << 21;  // keeps the row-block grid dimension < 65536
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -77,11 +76,20 @@ const Nf4Table& codebook() {
   return cb.t;
 }
 
+// Group size G: 32, 64 or a multiple of 128 that divides K; -1 (or K) is
+// per-channel.  K is a whole number of 128-input tiles in every case.
+int64_t resolve_group(int64_t K, int32_t group_size) {
+  return group_size == -1 ? K : (int64_t)group_size;
+}
+
 int validate_int4_shape(int64_t K, int64_t N, int32_t group_size) {
   if (K <= 0 || N <= 0) return W4A16_ERR_INVALID_ARG;
-  if (group_size != kGroup) return W4A16_ERR_UNSUPPORTED;
-  if (K % kGroup != 0 || N % 8 != 0) return W4A16_ERR_INVALID_ARG;
+  if (K % 128 != 0 || N % 8 != 0) return W4A16_ERR_INVALID_ARG;
   if (K > (int64_t)1 << 30 || N > (int64_t)1 << 30) return W4A16_ERR_UNSUPPORTED;
+  const int64_t G = resolve_group(K, group_size);
+  if (G == 32 || G == 64) return W4A16_OK;
+  if (G <= 0 || G % 128 != 0) return W4A16_ERR_UNSUPPORTED;
+  if (K % G != 0) return W4A16_ERR_INVALID_ARG;
   return W4A16_OK;
 }
 
@@ -110,11 +118,12 @@ int w4a16_version(void) { return 1; }
 
 int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which) {
   if (validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
-  const int64_t NP = ceil_div(N, 64), KT = K / kGroup, KT8 = ceil_div(KT, 8);
+  const int64_t U = units_per_tile((int)resolve_group(K, group_size));
+  const int64_t NP = ceil_div(N, 64), KT = K / 128, KT8 = ceil_div(KT, 8);
   switch (which) {
     case W4A16_CODES: return NP * KT * 4096;
-    case W4A16_SCALES: return NP * KT8 * 1024;
-    case W4A16_ZEROS: return NP * KT8 * 256;
+    case W4A16_SCALES: return NP * KT8 * 1024 * U;
+    case W4A16_ZEROS: return NP * KT8 * 256 * U;
     default: return -1;
   }
 }
@@ -122,29 +131,28 @@ int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t w
 int w4a16_make_perm(const int32_t* g_idx, int64_t K, int32_t group_size, int32_t* perm,
                     int32_t* nontrivial_host, void* stream) {
   if (!nontrivial_host) return W4A16_ERR_INVALID_ARG;
-  if (K <= 0 || group_size != kGroup) return group_size != kGroup ? W4A16_ERR_UNSUPPORTED
-                                                                  : W4A16_ERR_INVALID_ARG;
-  if (K % kGroup != 0) return W4A16_ERR_INVALID_ARG;
+  if (int s = validate_int4_shape(K, 8, group_size)) return s;
   if (int s = check_ptrs({g_idx, perm})) return s;
+  const int64_t G = resolve_group(K, group_size);
   hipStream_t st = (hipStream_t)stream;
   std::vector<int32_t> g((size_t)K);
   if (hipMemcpyAsync(g.data(), g_idx, (size_t)K * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
     return W4A16_ERR_HIP;
-  const int64_t ng = K / kGroup;
+  const int64_t ng = K / G;
   std::vector<int64_t> count((size_t)ng, 0);
   bool trivial = true;
   for (int64_t k = 0; k < K; ++k) {
     if (g[k] < 0 || g[k] >= ng) return W4A16_ERR_BAD_GIDX;
     ++count[g[k]];
-    if (g[k] != k / kGroup) trivial = false;
+    if (g[k] != k / G) trivial = false;
   }
   for (int64_t c : count)
-    if (c != kGroup) return W4A16_ERR_BAD_GIDX;
+    if (c != G) return W4A16_ERR_BAD_GIDX;
   // stable counting sort: columns of group 0 in original order, then group 1, ...
   std::vector<int32_t> p((size_t)K);
   std::vector<int64_t> next((size_t)ng);
-  for (int64_t i = 0; i < ng; ++i) next[i] = i * kGroup;
+  for (int64_t i = 0; i < ng; ++i) next[i] = i * G;
   for (int64_t k = 0; k < K; ++k) p[next[g[k]]++] = (int32_t)k;
   if (hipMemcpyAsync(perm, p.data(), (size_t)K * 4, hipMemcpyHostToDevice, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
@@ -158,10 +166,12 @@ int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm
                        int32_t* qzeros, void* stream) {
   if (int s = validate_int4_shape(K, N, group_size)) return s;
   if ((g_idx == nullptr) != (perm == nullptr)) return W4A16_ERR_INVALID_ARG;
-  if (int s = check_ptrs({W, qweight, scales, qzeros})) return s;
+  if (int s = check_ptrs({W, qweight, scales})) return s;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
+  if (qzeros && !aligned16(qzeros)) return W4A16_ERR_MISALIGNED;
   clear_pending_error();
-  return hip_status(launch_rtn_int4(W, perm, N, K, qweight, scales, qzeros, (hipStream_t)stream));
+  return hip_status(launch_rtn_int4(W, perm, N, K, (int)resolve_group(K, group_size), qweight,
+                                    scales, qzeros, (hipStream_t)stream));
 }
 
 int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
@@ -170,7 +180,10 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
                  void* stream) {
   if (int s = validate_int4_shape(K, N, group_size)) return s;
   if (!perm_used_host) return W4A16_ERR_INVALID_ARG;
-  if (int s = check_ptrs({qweight, scales, qzeros, codes_r, scales_r, zeros_r})) return s;
+  // a symmetric weight has neither zeros nor repacked zeros
+  if ((qzeros == nullptr) != (zeros_r == nullptr)) return W4A16_ERR_INVALID_ARG;
+  if (int s = check_ptrs({qweight, scales, codes_r, scales_r})) return s;
+  if (qzeros && (!aligned16(qzeros) || !aligned16(zeros_r))) return W4A16_ERR_MISALIGNED;
   int32_t used = 0;
   if (g_idx) {
     if (!perm) return W4A16_ERR_INVALID_ARG;
@@ -178,7 +191,8 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
   }
   clear_pending_error();
   if (int s = hip_status(launch_repack(qweight, scales, qzeros, used ? perm : nullptr, K, N,
-                                       codes_r, scales_r, zeros_r, (hipStream_t)stream)))
+                                       (int)resolve_group(K, group_size), codes_r, scales_r,
+                                       zeros_r, (hipStream_t)stream)))
     return s;
   *perm_used_host = used;
   return W4A16_OK;
@@ -201,25 +215,29 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
   if (M <= 0 || M > kMaxM) return M <= 0 ? W4A16_ERR_INVALID_ARG : W4A16_ERR_UNSUPPORTED;
   if (int s = validate_int4_shape(K, N, group_size)) return s;
   if (int s = validate_dtype(dtype)) return s;
-  if (int s = check_ptrs({x, codes_r, scales_r, zeros_r, out})) return s;
+  if (int s = check_ptrs({x, codes_r, scales_r, out})) return s;
+  if (zeros_r && !aligned16(zeros_r)) return W4A16_ERR_MISALIGNED;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
   if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
   const int64_t need = int4_workspace_bytes(M, N, K, perm != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
   clear_pending_error();
-  return hip_status(launch_int4_gemm(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, dtype,
-                                     workspace, workspace_bytes, (hipStream_t)stream));
+  return hip_status(launch_int4_gemm(x, codes_r, scales_r, zeros_r, perm, out, M, N, K,
+                                     (int)resolve_group(K, group_size), dtype, workspace,
+                                     workspace_bytes, (hipStream_t)stream));
 }
 
 int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
                   int64_t N, int32_t group_size, int32_t dtype, void* w_out, void* stream) {
   if (int s = validate_int4_shape(K, N, group_size)) return s;
   if (int s = validate_dtype(dtype)) return s;
-  if (int s = check_ptrs({codes_r, scales_r, zeros_r, w_out})) return s;
+  if (int s = check_ptrs({codes_r, scales_r, w_out})) return s;
+  if (zeros_r && !aligned16(zeros_r)) return W4A16_ERR_MISALIGNED;
   clear_pending_error();
-  return hip_status(
-      launch_dequant_int4(codes_r, scales_r, zeros_r, K, N, dtype, w_out, (hipStream_t)stream));
+  return hip_status(launch_dequant_int4(codes_r, scales_r, zeros_r, K, N,
+                                        (int)resolve_group(K, group_size), dtype, w_out,
+                                        (hipStream_t)stream));
 }
 
 int nf4_codebook(float* out16_host) {

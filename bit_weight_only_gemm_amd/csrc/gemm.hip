@@ -96,19 +96,23 @@ __device__ __forceinline__ void mma_tile(const typename Op<DT>::vec b[4],
 // --------------------------------------------------------------- INT4 policy --
 // Column tile ct = 4p + c of panel p.  Word j of lane l covers K = 128t + 32j +
 // 8(l >> 4) + e, so lane-group b feeds x[row][128t + 32j + 8b ...] in step j.
-template <int DT>
+// U meta units per K tile (group size 128 / U, or >= 128 for U = 1); word j of
+// tile slot s uses unit r = sU + jU/4 of the run.  A symmetric weight has no
+// zeros (empty descriptor range, loads read 0) and zx turns each nibble into 8.
+template <int DT, int U>
 struct Int4W {
   static constexpr bool kRaggedK = false;  // K % 128 == 0 for this format
   const uint8_t* codes;
   const uint8_t* scales;
   const uint8_t* zeros;
   int KT;
+  uint32_t zx;  // kSymZeroXor for a symmetric weight, else 0
   rsrc_t rc, rs, rz;
   uint32_t voc, vos, voz;
   int c;
   struct Meta {
-    u32x4_t s;   // 8 fp16 scales of this lane's column, one per tile of the run
-    uint32_t z;  // 8 zero nibbles
+    u32x4_t s[U];   // 8U fp16 scales of this lane's column, unit r at half r
+    uint32_t z[U];  // 8U zero nibbles, unit r at nibble r & 7 of word r >> 3
   };
   __device__ __forceinline__ void init(int ct, int lane, int /*N*/, int /*K*/) {
     const int p = ct >> 2;
@@ -117,34 +121,56 @@ struct Int4W {
     const int KT8 = (KT + RUN - 1) / RUN;
     // one descriptor per array, based at this panel: offsets stay 32-bit
     rc = make_rsrc(codes + (size_t)p * KT * 4096, (uint32_t)KT * 4096u);
-    rs = make_rsrc(scales + (size_t)p * KT8 * 1024, (uint32_t)KT8 * 1024u);
-    rz = make_rsrc(zeros + (size_t)p * KT8 * 256, (uint32_t)KT8 * 256u);
+    rs = make_rsrc(scales + (size_t)p * KT8 * 1024 * U, (uint32_t)KT8 * 1024u * U);
+    rz = make_rsrc(zeros + (size_t)p * KT8 * 256 * U, zx ? 0u : (uint32_t)KT8 * 256u * U);
     voc = (uint32_t)(c * 1024 + lane * 16);
-    vos = (uint32_t)((c * 16 + i) * 16);
-    voz = (uint32_t)((c * 16 + i) * 4);
+    vos = (uint32_t)((c * 16 + i) * 16 * U);
+    voz = (uint32_t)((c * 16 + i) * 4 * U);
   }
   __device__ static __forceinline__ Meta zero_meta() {
     Meta m;
-    m.s = u32x4_t{0u, 0u, 0u, 0u};
-    m.z = 0u;
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      m.s[k] = u32x4_t{0u, 0u, 0u, 0u};
+      m.z[k] = 0u;
+    }
     return m;
   }
   __device__ __forceinline__ Meta load_meta(int run) const {
     Meta m;
-    m.s = bld128(rs, vos, run * 1024);
-    m.z = bld32(rz, voz, run * 256);
+#pragma unroll
+    for (int k = 0; k < U; ++k) m.s[k] = bld128(rs, vos + 16u * k, run * 1024 * U);
+    if constexpr (U == 1) {
+      m.z[0] = bld32(rz, voz, run * 256);
+    } else if constexpr (U == 2) {
+      const u32x2_t z = bld64(rz, voz, run * 512);
+      m.z[0] = z[0];
+      m.z[1] = z[1];
+    } else {
+      const u32x4_t z = bld128(rz, voz, run * 1024);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m.z[k] = z[k];
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) m.z[k] ^= zx;
     return m;
   }
   __device__ __forceinline__ u32x4_t load_codes(int t, int /*lane*/) const {
     return bld128(rc, voc, t * 4096);
   }
+  __device__ static __forceinline__ void unit_param(const Meta& m, int r, QParam<DT>& qp) {
+    qp.set((m.s[r >> 3][(r & 7) >> 1] >> (16 * (r & 1))) & 0xFFFFu,
+           (m.z[r >> 3] >> (4 * (r & 7))) & 0xFu);
+  }
   // B operands of tile slot s (0..7 within the run) from the exact dequant.
   __device__ __forceinline__ void operands(const u32x4_t& w, int s, const Meta& m,
                                            typename Op<DT>::vec b[4]) const {
     QParam<DT> qp;
-    qp.set((m.s[s >> 1] >> (16 * (s & 1))) & 0xFFFFu, (m.z >> (4 * s)) & 0xFu);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = dequant_word(w[j], qp);
+    for (int j = 0; j < 4; ++j) {
+      if (j * U % 4 == 0) unit_param(m, s * U + j * U / 4, qp);  // a new unit
+      b[j] = dequant_word(w[j], qp);
+    }
   }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }
 };
@@ -458,18 +484,19 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
   }
 }
 
-template <int DT, int MT, int AM>
+template <int DT, int MT, int AM, int U>
 __global__ void __launch_bounds__(64 * DW)
 int4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                    const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                   const int32_t* __restrict__ perm, uint16_t* __restrict__ out, int M, int N,
-                   int K, int KT) {
+                   uint32_t zx, const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
+                   int M, int N, int K, int KT) {
   __shared__ float red[DW * MT * 64 * 4];
   extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
-  Int4W<DT> wp;
+  Int4W<DT, U> wp;
   wp.codes = codes;
   wp.scales = scales;
   wp.zeros = zeros;
+  wp.zx = zx;
   wp.KT = KT;
   decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red, perm, xlds);
 }
@@ -539,33 +566,50 @@ static int pick_mode(int64_t M, int64_t K, bool gather, int* mt) {
   return AM_FULL;
 }
 
-template <int DT, int MT, int AM>
+template <int DT, int MT, int AM, int U>
 static void launch_int4_v(const void* x, const void* codes_r, const void* scales_r,
                           const void* zeros_r, const int32_t* perm, void* out, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
   const size_t lds = AM == AM_XGATHER ? xlds_bytes((int)M, (int)K) : 0;
-  if (lds) allow_dynamic_lds((const void*)int4_decode_kernel<DT, MT, AM>);
-  launch_timed(int4_decode_kernel<DT, MT, AM>, grid, dim3(64 * DW), lds, stream,
+  if (lds) allow_dynamic_lds((const void*)int4_decode_kernel<DT, MT, AM, U>);
+  // a symmetric weight: the zeros descriptor gets an empty range over a valid
+  // base and every zero nibble reads 0 ^ 8
+  const uint32_t zx = zeros_r ? 0u : kSymZeroXor;
+  launch_timed(int4_decode_kernel<DT, MT, AM, U>, grid, dim3(64 * DW), lds, stream,
                (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
-               (const uint8_t*)zeros_r, perm, (uint16_t*)out, (int)M, (int)N, (int)K,
-               (int)(K / 128));
+               (const uint8_t*)(zeros_r ? zeros_r : scales_r), zx, perm, (uint16_t*)out,
+               (int)M, (int)N, (int)K, (int)(K / 128));
+}
+
+template <int DT, int U>
+static void launch_int4_mode(int am, int mt, const void* x, const void* codes_r,
+                             const void* scales_r, const void* zeros_r, const int32_t* perm,
+                             void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (am == AM_XGATHER)
+    launch_int4_v<DT, 1, AM_XGATHER, U>(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
+  else if (am == AM_PACKED)
+    launch_int4_v<DT, 1, AM_PACKED, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K,
+                                       stream);
+  else if (mt == 1)
+    launch_int4_v<DT, 1, AM_FULL, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
+  else if (mt == 2)
+    launch_int4_v<DT, 2, AM_FULL, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
+  else
+    launch_int4_v<DT, 4, AM_FULL, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
 }
 
 template <int DT>
-static void launch_int4_dt(int am, int mt, const void* x, const void* codes_r,
+static void launch_int4_dt(int am, int mt, int G, const void* x, const void* codes_r,
                            const void* scales_r, const void* zeros_r, const int32_t* perm,
                            void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (am == AM_XGATHER)
-    launch_int4_v<DT, 1, AM_XGATHER>(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
-  else if (am == AM_PACKED)
-    launch_int4_v<DT, 1, AM_PACKED>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
-  else if (mt == 1)
-    launch_int4_v<DT, 1, AM_FULL>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
-  else if (mt == 2)
-    launch_int4_v<DT, 2, AM_FULL>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
+  const int U = units_per_tile(G);
+  if (U == 1)
+    launch_int4_mode<DT, 1>(am, mt, x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
+  else if (U == 2)
+    launch_int4_mode<DT, 2>(am, mt, x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
   else
-    launch_int4_v<DT, 4, AM_FULL>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
+    launch_int4_mode<DT, 4>(am, mt, x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
 }
 
 // Workspace layout: the permuted activations (when the activations are
@@ -584,7 +628,7 @@ int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm) {
 
 hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scales_r,
                             const void* zeros_r, const int32_t* perm, void* out, int64_t M,
-                            int64_t N, int64_t K, int dtype, void* workspace,
+                            int64_t N, int64_t K, int G, int dtype, void* workspace,
                             int64_t /*workspace_bytes*/, hipStream_t stream) {
   int mt = 1;
   const bool pf = use_prefill(M, N, K);
@@ -600,11 +644,12 @@ hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scal
   }
   if (pf)
     launch_int4_prefill(xa, codes_r, scales_r, zeros_r, out, (uint8_t*)workspace + xb, M, N, K,
-                        dtype, stream);
+                        G, dtype, stream);
   else if (dtype == DT_F16)
-    launch_int4_dt<DT_F16>(am, mt, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
+    launch_int4_dt<DT_F16>(am, mt, G, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
   else
-    launch_int4_dt<DT_BF16>(am, mt, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
+    launch_int4_dt<DT_BF16>(am, mt, G, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K,
+                            stream);
   return hipGetLastError();
 }
 

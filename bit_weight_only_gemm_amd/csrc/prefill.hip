@@ -87,12 +87,12 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff,
 // absmax_q * absmax_scale, L from LDS.  NF4 here needs K % 128 == 0.
 enum { FMT_INT4 = 0, FMT_NF4 = 1 };
 
-template <int DT, int BM, bool TAIL, int FMT>
+template <int DT, int BM, bool TAIL, int FMT, int U>
 __global__ void __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
 int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                     const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
-                    Nf4Table L, uint16_t* __restrict__ out, float* __restrict__ part, int M,
-                    int N, int K, int KT, int NP, int S) {
+                    uint32_t zx, Nf4Table L, uint16_t* __restrict__ out,
+                    float* __restrict__ part, int M, int N, int K, int KT, int NP, int S) {
   typedef typename Op<DT>::vec vec;
   __shared__ float lut[16];
   if (FMT == FMT_NF4 && threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
@@ -133,8 +133,8 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
   uint32_t vcode[2][2], vmeta[2], gblk[2];
   if constexpr (FMT == FMT_INT4) {
     rc = make_rsrc(codes + pp * KT * 4096, pv ? (uint32_t)KT * 4096u : 0u);
-    rs = make_rsrc(scales + pp * KT8 * 1024, pv ? (uint32_t)KT8 * 1024u : 0u);
-    rz = make_rsrc(zeros + pp * KT8 * 256, pv ? (uint32_t)KT8 * 256u : 0u);
+    rs = make_rsrc(scales + pp * KT8 * 1024 * U, pv ? (uint32_t)KT8 * 1024u * U : 0u);
+    rz = make_rsrc(zeros + pp * KT8 * 256 * U, pv && !zx ? (uint32_t)KT8 * 256u * U : 0u);
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int ct = 2 * g + ((lane & 31) >> 4);
@@ -159,17 +159,22 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
       gblk[g] = (uint32_t)(pp * 64 + c) * Kblk + (uint32_t)h;
     }
   }
-  // the weights and meta of K tile t for column group g
-  auto load_w = [&](int t, int g, u32x4_t (&w)[2], uint32_t& sa, uint32_t& za) {
+  // the weights and meta of K tile t for column group g.  INT4: sa holds the U
+  // scales of the tile (units (t & 7) U .. of the run, 2 U bytes), za the zero
+  // word holding their nibbles.
+  auto load_w = [&](int t, int g, u32x4_t (&w)[2], u32x2_t& sa, uint32_t& za) {
     if constexpr (FMT == FMT_INT4) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) w[h2] = bld128(rc, vcode[g][h2], t * 4096);
-      sa = bld16(rs, vmeta[g] * 16u, (t >> 3) * 1024 + (t & 7) * 2);
-      za = bld32(rz, vmeta[g] * 4u, (t >> 3) * 256);
+      const int sb = (t >> 3) * 1024 * U + (t & 7) * 2 * U;
+      if constexpr (U == 1) sa = u32x2_t{bld16(rs, vmeta[g] * 16u, sb), 0u};
+      else if constexpr (U == 2) sa = u32x2_t{bld32(rs, vmeta[g] * 32u, sb), 0u};
+      else sa = bld64(rs, vmeta[g] * 64u, sb);
+      za = bld32(rz, vmeta[g] * 4u * U, (t >> 3) * 256 * U + (((t & 7) * U) >> 3) * 4) ^ zx;
     } else {
       w[0] = bld128(rc, vcode[g][0], t * 64);
       w[1] = bld128(rc, vcode[g][1], t * 64);
-      sa = __builtin_amdgcn_raw_buffer_load_b8(rs, vmeta[g], 2 * t, 0);
+      sa = u32x2_t{__builtin_amdgcn_raw_buffer_load_b8(rs, vmeta[g], 2 * t, 0), 0u};
       za = bld32(rz, ((gblk[g] + 2u * (uint32_t)t) >> 8) * 4u, 0);
     }
   };
@@ -181,7 +186,8 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     for (int g = 0; g < 2; ++g) acc[m][g] = float16_t{};
 
   u32x4_t cw[2][2], cn[2][2];
-  uint32_t sc[2], zz[2], sn[2], zn[2];
+  u32x2_t sc[2], sn[2];
+  uint32_t zz[2], zn[2];
 
   // ---- prologue: K tile 0
 #pragma unroll
@@ -215,17 +221,27 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     // pipe busy long enough to issue several VALU instructions behind it).
     QParam<DT> qp[2];
     float ap[2];  // NF4: a' of this lane's block
+    const int zb = ((t & 7) * U) & 7;  // nibble of the tile's first unit
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      if constexpr (FMT == FMT_INT4)
-        qp[g].set(sc[g] & 0xFFFFu, (zz[g] >> (4 * (t & 7))) & 0xFu);
-      else
-        ap[g] = (float)(sc[g] & 0xFFu) * __builtin_bit_cast(float, zz[g]);
+      if constexpr (FMT == FMT_INT4) {
+        if constexpr (U == 1) qp[g].set(sc[g][0] & 0xFFFFu, (zz[g] >> (4 * zb)) & 0xFu);
+      } else {
+        ap[g] = (float)(sc[g][0] & 0xFFu) * __builtin_bit_cast(float, zz[g]);
+      }
     }
-    // B operand of step s for column group g
+    // B operand of step s for column group g: word j = s >> 1 of the tile,
+    // meta unit j U / 4 (U > 1: its parameters are formed at the step)
     auto operand = [&](int s, int g) -> vec {
       if constexpr (FMT == FMT_INT4) {
-        return dequant_word(cw[g][s & 1][s >> 1], qp[g]);
+        if constexpr (U == 1) {
+          return dequant_word(cw[g][s & 1][s >> 1], qp[g]);
+        } else {
+          const int u = (s >> 1) * U / 4;
+          QParam<DT> q;
+          q.set((sc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu, (zz[g] >> (4 * (zb + u))) & 0xFu);
+          return dequant_word(cw[g][s & 1][s >> 1], q);
+        }
       } else {
         const uint32_t w = cw[g][s >> 2][s & 3];
         vec v;
@@ -384,7 +400,7 @@ int64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return pl.splits > 1 ? ceil_div((int64_t)pl.splits * M * N * 4, 256) * 256 : 0;
 }
 
-template <int DT, int BM, int FMT>
+template <int DT, int BM, int FMT, int U>
 static void launch_prefill_bm(const void* x, const void* codes_r, const void* scales_r,
                               const void* zeros_r, const Nf4Table& L, void* out, float* part,
                               int S, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
@@ -392,17 +408,21 @@ static void launch_prefill_bm(const void* x, const void* codes_r, const void* sc
   const int KT = (int)(K / 128);
   const unsigned gx = (unsigned)ceil_div(NP, PF_WAVES);
   const int64_t full = M / BM;
+  // INT4 without zeros (symmetric): an empty zeros range over a valid base,
+  // every nibble read as 0 ^ 8
+  const uint32_t zx = (FMT == FMT_INT4 && !zeros_r) ? kSymZeroXor : 0u;
+  const uint8_t* zp = (const uint8_t*)(zeros_r ? zeros_r : scales_r);
   // the timing events (if set) go to the first launch
   if (full > 0)
-    launch_timed(int4_prefill_kernel<DT, BM, false, FMT>, dim3(gx, (unsigned)full, (unsigned)S),
-                 dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
-                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, L, (uint16_t*)out, part,
-                 (int)M, (int)N, (int)K, KT, (int)NP, S);
+    launch_timed(int4_prefill_kernel<DT, BM, false, FMT, U>,
+                 dim3(gx, (unsigned)full, (unsigned)S), dim3(64 * PF_WAVES), 0, stream,
+                 (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r, zp, zx, L,
+                 (uint16_t*)out, part, (int)M, (int)N, (int)K, KT, (int)NP, S);
   if (M % BM)
-    launch_timed(int4_prefill_kernel<DT, BM, true, FMT>, dim3(gx, 1, (unsigned)S),
+    launch_timed(int4_prefill_kernel<DT, BM, true, FMT, U>, dim3(gx, 1, (unsigned)S),
                  dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
-                 (const uint8_t*)scales_r, (const uint8_t*)zeros_r, L, (uint16_t*)out, part,
-                 (int)M, (int)N, (int)K, KT, (int)NP, S);
+                 (const uint8_t*)scales_r, zp, zx, L, (uint16_t*)out, part, (int)M, (int)N,
+                 (int)K, KT, (int)NP, S);
   if (S > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(split_reduce_kernel<DT>, dim3((unsigned)ceil_div(MN / 4, (int64_t)256)),
@@ -410,44 +430,58 @@ static void launch_prefill_bm(const void* x, const void* codes_r, const void* sc
   }
 }
 
-template <int DT, int FMT>
+template <int DT, int FMT, int U>
 static void launch_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
                               const void* zeros_r, const Nf4Table& L, void* out, void* ws,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const PrefillPlan pl = plan_prefill(M, N, K);
   float* part = (float*)ws;
   if (pl.bm == 64)
-    launch_prefill_bm<DT, 64, FMT>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M, N,
-                                   K, stream);
+    launch_prefill_bm<DT, 64, FMT, U>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
+                                      N, K, stream);
   else if (pl.bm == 128)
-    launch_prefill_bm<DT, 128, FMT>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M, N,
-                                    K, stream);
+    launch_prefill_bm<DT, 128, FMT, U>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
+                                       N, K, stream);
   else
-    launch_prefill_bm<DT, 256, FMT>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M, N,
-                                    K, stream);
+    launch_prefill_bm<DT, 256, FMT, U>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
+                                       N, K, stream);
+}
+
+template <int DT>
+static void launch_int4_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
+                                   const void* zeros_r, void* out, void* ws, int64_t M,
+                                   int64_t N, int64_t K, int G, hipStream_t stream) {
+  const Nf4Table none{};
+  const int U = units_per_tile(G);
+  if (U == 1)
+    launch_prefill_dt<DT, FMT_INT4, 1>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N, K,
+                                       stream);
+  else if (U == 2)
+    launch_prefill_dt<DT, FMT_INT4, 2>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N, K,
+                                       stream);
+  else
+    launch_prefill_dt<DT, FMT_INT4, 4>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N, K,
+                                       stream);
 }
 
 void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
                          const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
-                         int64_t K, int dtype, hipStream_t stream) {
-  const Nf4Table none{};
+                         int64_t K, int G, int dtype, hipStream_t stream) {
   if (dtype == DT_F16)
-    launch_prefill_dt<DT_F16, FMT_INT4>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N, K,
-                                        stream);
+    launch_int4_prefill_dt<DT_F16>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, G, stream);
   else
-    launch_prefill_dt<DT_BF16, FMT_INT4>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N, K,
-                                         stream);
+    launch_int4_prefill_dt<DT_BF16>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, G, stream);
 }
 
 void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                         const float* absmax_scale, const Nf4Table& L, void* out, void* ws,
                         int64_t M, int64_t N, int64_t K, int dtype, hipStream_t stream) {
   if (dtype == DT_F16)
-    launch_prefill_dt<DT_F16, FMT_NF4>(x, qweight, absmax_q, absmax_scale, L, out, ws, M, N, K,
-                                       stream);
+    launch_prefill_dt<DT_F16, FMT_NF4, 1>(x, qweight, absmax_q, absmax_scale, L, out, ws, M, N,
+                                          K, stream);
   else
-    launch_prefill_dt<DT_BF16, FMT_NF4>(x, qweight, absmax_q, absmax_scale, L, out, ws, M, N, K,
-                                        stream);
+    launch_prefill_dt<DT_BF16, FMT_NF4, 1>(x, qweight, absmax_q, absmax_scale, L, out, ws, M, N,
+                                           K, stream);
 }
 
 }  // namespace w4a16

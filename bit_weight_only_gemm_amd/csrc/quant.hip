@@ -27,55 +27,67 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
 }
 
 // ---------------------------------------------------------------- RTN INT4 --
-// One wave per (row n, group g); lane holds group members u = lane, lane + 64.
-// Codes are OR-ed into the zero-filled canonical qweight / qzeros words.
+// One wave per (row n, group g of G members); lane holds members u = lane +
+// 64 h, read twice (range, then codes).  Codes are OR-ed into the zero-filled
+// canonical qweight / qzeros words.  Asymmetric: s = fp16(fp32(max - min) / 15),
+// z = clip(rint(-min / s), 0, 15), q = clip(rint(w / s) + z, 0, 15).
+// Symmetric (qzeros == nullptr): s = fp16(fp32(max |w|) / 7),
+// q = clip(rint(w / s), -8, 7) + 8.  A group whose fp16 scale is 0 uses s = 1.
 __global__ void __launch_bounds__(256)
 rtn_int4_kernel(const float* __restrict__ W, const int32_t* __restrict__ perm, int64_t N,
-                int64_t K, uint32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
+                int64_t K, int G, uint32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
                 uint32_t* __restrict__ qzeros) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t ng = K / 128;
+  const int64_t ng = K / G;
   if (item >= N * ng) return;
   const int64_t g = item / N, n = item % N;  // n fastest across waves
-  int64_t k[2];
-  float w[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int64_t u = g * 128 + lane + 64 * h;
-    k[h] = perm ? (int64_t)perm[u] : u;
-    w[h] = W[n * K + k[h]];
+  const bool sym = qzeros == nullptr;
+  auto col = [&](int u) -> int64_t {
+    const int64_t k = g * G + u;
+    return perm ? (int64_t)perm[k] : k;
+  };
+  float mn = INFINITY, mx = -INFINITY;
+  for (int u = lane; u < G; u += 64) {
+    const float w = W[n * K + col(u)];
+    mn = fminf(mn, w);
+    mx = fmaxf(mx, sym ? fabsf(w) : w);
   }
-  const float mn = wave_min(fminf(w[0], w[1]));
-  const float mx = wave_max(fmaxf(w[0], w[1]));
-  _Float16 s16 = (_Float16)((mx - mn) / 15.0f);  // fp32 sub + correctly rounded div, RNE
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  _Float16 s16 = sym ? (_Float16)(mx / 7.0f)             // correctly rounded fp32 div, RNE
+                     : (_Float16)((mx - mn) / 15.0f);    // fp32 sub + div, RNE
   if (s16 == (_Float16)0.0f) s16 = (_Float16)1.0f;
   const float sf = (float)s16;
-  const float z = fminf(fmaxf(rintf(-mn / sf), 0.0f), 15.0f);
-  const uint32_t zi = (uint32_t)z;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float q = fminf(fmaxf(rintf(w[h] / sf) + z, 0.0f), 15.0f);
+  // symmetric: clip(rint(w / s), -8, 7) + 8 is the asymmetric formula with z = 8
+  const float z = sym ? 8.0f : fminf(fmaxf(rintf(-mn / sf), 0.0f), 15.0f);
+  for (int u = lane; u < G; u += 64) {
+    const int64_t k = col(u);
+    const float w = W[n * K + k];
+    const float q = fminf(fmaxf(rintf(w / sf) + z, 0.0f), 15.0f);
     const uint32_t qi = (uint32_t)q;
-    if (qi) atomicOr(&qweight[(k[h] >> 3) * N + n], qi << (4 * (k[h] & 7)));
+    if (qi) atomicOr(&qweight[(k >> 3) * N + n], qi << (4 * (k & 7)));
   }
   if (lane == 0) {
     scales[g * N + n] = __builtin_bit_cast(uint16_t, s16);
-    if (zi) atomicOr(&qzeros[g * (N >> 3) + (n >> 3)], zi << (4 * (n & 7)));
+    const uint32_t zi = (uint32_t)z;
+    if (!sym && zi) atomicOr(&qzeros[g * (N >> 3) + (n >> 3)], zi << (4 * (n & 7)));
   }
 }
 
-hipError_t launch_rtn_int4(const float* W, const int32_t* perm, int64_t N, int64_t K,
+hipError_t launch_rtn_int4(const float* W, const int32_t* perm, int64_t N, int64_t K, int G,
                            int32_t* qweight, uint16_t* scales, int32_t* qzeros,
                            hipStream_t stream) {
-  const int64_t nw = (K / 8) * N, nz = (K / 128) * (N / 8);
+  const int64_t nw = (K / 8) * N, nz = (K / G) * (N / 8);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(nw, 256), 65535)),
                      dim3(256), 0, stream, (uint32_t*)qweight, nw, 0u);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(nz, 256), 65535)),
-                     dim3(256), 0, stream, (uint32_t*)qzeros, nz, 0u);
-  const int64_t items = N * (K / 128);
+  if (qzeros)
+    hipLaunchKernelGGL(fill_u32_kernel,
+                       dim3((unsigned)std::min<int64_t>(ceil_div(nz, 256), 65535)), dim3(256), 0,
+                       stream, (uint32_t*)qzeros, nz, 0u);
+  const int64_t items = N * (K / G);
   hipLaunchKernelGGL(rtn_int4_kernel, dim3((unsigned)ceil_div(items, 4)), dim3(256), 0, stream,
-                     W, perm, N, K, (uint32_t*)qweight, scales, (uint32_t*)qzeros);
+                     W, perm, N, K, G, (uint32_t*)qweight, scales, (uint32_t*)qzeros);
   return hipGetLastError();
 }
 
@@ -160,13 +172,15 @@ repack_codes_kernel(const uint32_t* __restrict__ qweight, const int32_t* __restr
   codes_r[idx] = word;
 }
 
-// One thread per (panel p, run g of 8 groups, column tile c, column i): the 8
-// scales (16 bytes) and the 8 zero nibbles (one word) of that column.
+// One thread per (panel p, run g of 8 K tiles, column tile c, column i): the
+// 8 U scales (16 U bytes) and 8 U zero nibbles (U words) of that column, unit
+// r of the run being tile 8 g + r / U, unit r % U.
 __global__ void __launch_bounds__(256)
 repack_meta_kernel(const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
-                   int64_t K, int64_t N, int64_t NP, uint16_t* __restrict__ scales_r,
+                   int64_t K, int64_t N, int64_t NP, int G, uint16_t* __restrict__ scales_r,
                    uint32_t* __restrict__ zeros_r) {
   const int64_t KT = K / 128, KT8 = ceil_div(KT, 8);
+  const int U = units_per_tile(G), span = G < 128 ? G : 128;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= NP * KT8 * 64) return;
   const int i = (int)(idx & 15);
@@ -174,25 +188,29 @@ repack_meta_kernel(const uint16_t* __restrict__ scales, const uint32_t* __restri
   const int64_t pg = idx >> 6;
   const int64_t g = pg % KT8, p = pg / KT8;
   const int64_t n = p * 64 + c * 16 + i;
-  uint32_t zw = 0;
-  u32x4_t sv = {0u, 0u, 0u, 0u};
+  for (int w = 0; w < U; ++w) {
+    uint32_t zw = 0;
+    u32x4_t sv = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int64_t t = g * 8 + s;
-    uint32_t sb = 0, z = 0;
-    if (n < N && t < KT) {
-      sb = scales[t * N + n];
-      z = (qzeros[t * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
+    for (int e = 0; e < 8; ++e) {
+      const int64_t v = g * 8 * U + 8 * w + e;  // unit index
+      const int64_t t = v / U;
+      uint32_t sb = 0, z = 0;
+      if (n < N && t < KT) {
+        const int64_t grp = (128 * t + (v % U) * span) / G;
+        sb = scales[grp * N + n];
+        if (qzeros) z = (qzeros[grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
+      }
+      sv[e >> 1] |= sb << (16 * (e & 1));
+      zw |= z << (4 * e);
     }
-    sv[s >> 1] |= sb << (16 * (s & 1));
-    zw |= z << (4 * s);
+    *(u32x4_t*)(scales_r + (idx * U + w) * 8) = sv;
+    if (zeros_r) zeros_r[idx * U + w] = zw;
   }
-  *(u32x4_t*)(scales_r + idx * 8) = sv;
-  zeros_r[idx] = zw;
 }
 
 hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
-                         const int32_t* perm, int64_t K, int64_t N, void* codes_r,
+                         const int32_t* perm, int64_t K, int64_t N, int G, void* codes_r,
                          void* scales_r, void* zeros_r, hipStream_t stream) {
   const int64_t NP = ceil_div(N, 64), KT = K / 128;
   const int64_t words = NP * KT * 1024;
@@ -200,7 +218,7 @@ hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const i
                      stream, (const uint32_t*)qweight, perm, K, N, NP, (uint32_t*)codes_r);
   const int64_t metas = NP * ceil_div(KT, 8) * 64;
   hipLaunchKernelGGL(repack_meta_kernel, dim3((unsigned)ceil_div(metas, 256)), dim3(256), 0,
-                     stream, scales, (const uint32_t*)qzeros, K, N, NP, (uint16_t*)scales_r,
+                     stream, scales, (const uint32_t*)qzeros, K, N, NP, G, (uint16_t*)scales_r,
                      (uint32_t*)zeros_r);
   return hipGetLastError();
 }
@@ -212,8 +230,9 @@ template <int DT>
 __global__ void __launch_bounds__(256)
 dequant_int4_kernel(const uint32_t* __restrict__ codes_r, const uint16_t* __restrict__ scales_r,
                     const uint32_t* __restrict__ zeros_r, int64_t K, int64_t N, int64_t NP,
-                    uint16_t* __restrict__ w_out) {
+                    int G, uint16_t* __restrict__ w_out) {
   const int64_t KT = K / 128, KT8 = ceil_div(KT, 8);
+  const int U = units_per_tile(G);
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= NP * KT * 1024) return;
   const int j = (int)(idx & 3);
@@ -225,26 +244,28 @@ dequant_int4_kernel(const uint32_t* __restrict__ codes_r, const uint16_t* __rest
   const int64_t n = p * 64 + c * 16 + i;
   if (n >= N) return;
   const int64_t meta = ((p * KT8 + (t >> 3)) * 4 + c) * 16 + i;
+  const int r = (int)(t & 7) * U + j * U / 4;  // unit of word j within the run
+  const uint32_t z = zeros_r ? (zeros_r[meta * U + (r >> 3)] >> (4 * (r & 7))) & 0xFu : 8u;
   QParam<DT> qp;
-  qp.set(scales_r[meta * 8 + (t & 7)], (zeros_r[meta] >> (4 * (t & 7))) & 0xFu);
+  qp.set(scales_r[meta * 8 * U + r], z);
   const auto v = dequant_word(codes_r[idx], qp);
   const int64_t k = t * 128 + j * 32 + (lane >> 4) * 8;
   *(u32x4_t*)(w_out + n * K + k) = __builtin_bit_cast(u32x4_t, v);
 }
 
 hipError_t launch_dequant_int4(const void* codes_r, const void* scales_r, const void* zeros_r,
-                               int64_t K, int64_t N, int dtype, void* w_out,
+                               int64_t K, int64_t N, int G, int dtype, void* w_out,
                                hipStream_t stream) {
   const int64_t NP = ceil_div(N, 64), KT = K / 128;
   const dim3 grid((unsigned)ceil_div(NP * KT * 1024, 256));
   if (dtype == DT_F16)
     hipLaunchKernelGGL(dequant_int4_kernel<DT_F16>, grid, dim3(256), 0, stream,
                        (const uint32_t*)codes_r, (const uint16_t*)scales_r,
-                       (const uint32_t*)zeros_r, K, N, NP, (uint16_t*)w_out);
+                       (const uint32_t*)zeros_r, K, N, NP, G, (uint16_t*)w_out);
   else
     hipLaunchKernelGGL(dequant_int4_kernel<DT_BF16>, grid, dim3(256), 0, stream,
                        (const uint32_t*)codes_r, (const uint16_t*)scales_r,
-                       (const uint32_t*)zeros_r, K, N, NP, (uint16_t*)w_out);
+                       (const uint32_t*)zeros_r, K, N, NP, G, (uint16_t*)w_out);
   return hipGetLastError();
 }
 

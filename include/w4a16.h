@@ -5,8 +5,11 @@
  * weights Wq [N, K] (row = output channel) with fp32 accumulation, in two
  * weight formats:
  *
- *   INT4  group-wise asymmetric: per (column, group of 128 along K) an fp16
- *         scale and a 4-bit zero; optional act-order column map g_idx.
+ *   INT4  group-wise: per (column, group of G inputs along K) an fp16 scale
+ *         and, for asymmetric codes, a 4-bit zero (symmetric codes have none
+ *         and read as zero point 8); G = 128 by default, 32, 64, any multiple
+ *         of 128 dividing K, or K itself (per-channel); optional act-order
+ *         column map g_idx.
  *   NF4   block-wise normal-float: per 64-element block an absmax that is
  *         itself 8-bit quantized with one fp32 scale per 256 blocks.
  *
@@ -79,19 +82,31 @@ int w4a16_set_timing_events(void* start_event, void* stop_event);
 /* ------------------------------------------------------------------ INT4 --- */
 
 /*
- * Bytes of one array of the repacked INT4 layout for a [N, K] weight.
- * Group size must be 128; K % 128 == 0; N % 8 == 0.  Returns -1 on bad input.
+ * Group sizes (every INT4 entry point): group_size G in {32, 64}, or a
+ * multiple of 128 that divides K; -1 means per-channel (G = K, [P3] §2.2),
+ * as does G == K.  Smaller groups trade bytes for accuracy ([P3] §7.1,
+ * [P1] §3.1 node 3).  K % 128 == 0 and N % 8 == 0 always.  An unsupported G
+ * gives W4A16_ERR_UNSUPPORTED, a G that does not divide K
+ * W4A16_ERR_INVALID_ARG.
  *
- * Repacked layout (KT = K/128 groups, NP = ceil(N/64) panels of 64 columns):
+ * Bytes of one array of the repacked INT4 layout for a [N, K] weight
+ * (-1 on bad input; a symmetric weight has no zeros array).
+ *
+ * Repacked layout (KT = K/128 tiles of 128 inputs, NP = ceil(N/64) panels of
+ * 64 columns, U = 128/G meta units per tile for G < 128, else U = 1):
  *   codes  uint8 [NP][KT][4][64][16]: output column n = 64p + 16c + i and
  *          (permuted) input column k = 128t + 32j + 8b + e are stored in lane
  *          l = i + 16b, 32-bit little-endian word j of that lane's 16 bytes,
  *          nibble slot (e >> 1) + 4*(e & 1).  Padding columns are zero.
- *   scales fp16  [NP][KT8][4][16][8] (KT8 = ceil(KT/8)): entry [p][g][c][i][s]
- *          = scale(64p+16c+i, group 8g+s); zero for padding columns/groups.
- *   zeros  uint32 [NP][KT8][4][16]: bits [4s, 4s+4) = zero(64p+16c+i, 8g+s).
- *   (Runs of 8 groups let a decode wave fetch 8 groups' scales in one 16-byte
- *   load and their zeros in one dword.)
+ *   Meta unit v = tU + u of a column: for G < 128 the group (128t + uG)/G
+ *          (word j of a lane lies in unit tU + jU/4); for G >= 128 the group
+ *          holding tile t (repeated on each tile of a group).
+ *   scales fp16  [NP][KT8][4][16][8U] (KT8 = ceil(KT/8)): entry [p][g][c][i][r]
+ *          = scale(64p+16c+i, unit 8Ug+r); zero for padding columns/units.
+ *   zeros  uint32 [NP][KT8][4][16][U]: bits [4e, 4e+4) of word w =
+ *          zero(64p+16c+i, unit 8Ug+8w+e).
+ *   (Runs of 8 tiles let a decode wave fetch a run's scales in U 16-byte
+ *   loads and its zeros in one load of U dwords.)
  */
 int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which);
 
@@ -112,18 +127,23 @@ int w4a16_make_perm(const int32_t* g_idx, int64_t K, int32_t group_size, int32_t
 
 /*
  * Round-to-nearest group quantizer ([P4] "技术原理": RTN is the baseline GPTQ
- * improves on; [P3] §2.1 asymmetric with a zero point; [P3] §2.2 group-wise).
+ * improves on; [P3] §2.1 asymmetric with a zero point, or symmetric with the
+ * zero point fixed; [P3] §2.2 group-wise).
  * Per output row n and group g (the columns {perm[gG .. gG+G-1]} when perm is
  * given, else G consecutive columns):
- *   s = fp16(fp32(max - min) / 15)  (s = 1 if that rounds to 0);
- *   z = clip(rint(-min / s), 0, 15);  q = clip(rint(w / s) + z, 0, 15),
- * all decisions in fp32, rint = half to even.
+ *   asymmetric (qzeros given): s = fp16(fp32(max - min) / 15),
+ *     z = clip(rint(-min / s), 0, 15),  q = clip(rint(w / s) + z, 0, 15);
+ *   symmetric (qzeros NULL): s = fp16(fp32(max |w|) / 7),
+ *     q = clip(rint(w / s), -8, 7) + 8  (stored offset by 8; dequantized as
+ *     (q - 8) s, so +-max|w| map to +-7);
+ * s = 1 where the fp16 scale rounds to 0; all decisions in fp32, rint = half
+ * to even.
  *   W        fp32 [N, K] device (finite values).
  *   g_idx    int32 [K] or NULL; perm int32 [K] (from w4a16_make_perm) iff g_idx.
  *   qweight  int32 [K/8, N]: bits [4j,4j+4) of (i, n) = q(n, 8i+j), original order.
- *   scales   fp16 [K/G, N];  qzeros int32 [K/G, N/8]: bits [4j,4j+4) of
- *            (g, i) = z(g, 8i+j).
- * Constraints: G == 128, K % G == 0, N % 8 == 0.
+ *   scales   fp16 [K/G, N];  qzeros int32 [K/G, N/8] or NULL (symmetric):
+ *            bits [4j,4j+4) of (g, i) = z(g, 8i+j).
+ * Constraints: the group sizes above.
  */
 int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm,
                        int64_t N, int64_t K, int32_t group_size, int32_t* qweight,
@@ -132,13 +152,15 @@ int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm
 /*
  * Offline repack of canonical GPTQ-style tensors into the tile layout above
  * (pay the layout translation once, not per call: [P5] "关键数据解读" item 4).
- *   qweight int32 [K/8, N]; scales fp16 [K/G, N]; qzeros int32 [K/G, N/8].
+ *   qweight int32 [K/8, N]; scales fp16 [K/G, N]; qzeros int32 [K/G, N/8],
+ *           or NULL for a symmetric weight (then zeros_r must be NULL too).
  *   g_idx   int32 [K] or NULL.  When given, `perm` (int32 [K], required then)
  *           receives w4a16_make_perm's permutation (the identity for the
  *           trivial k/G map).  If g_idx is non-trivial the codes are stored in
  *           perm order and *perm_used_host is set to 1: pass `perm` to
  *           w4a16_gemm.  Otherwise *perm_used_host = 0: pass NULL.
  *   codes_r / scales_r / zeros_r: sized by w4a16_repacked_bytes.
+ * W4A16_ERR_INVALID_ARG when exactly one of qzeros, zeros_r is NULL.
  * BLOCKS when g_idx is non-NULL (host validation of g_idx); otherwise async.
  */
 int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
@@ -161,17 +183,19 @@ int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_siz
  * Fused dequantize-and-multiply, the method of [P5] "关键数据解读" item 1
  * (weights are never written back as 16-bit values):
  *   y[m, n] = sum_k x[m, perm[k]] * w[n, k],
- *   w[n, k] = round_dtype(fp32(q - z) * fp32(s))  (q, z, s of column n, group k/128),
+ *   w[n, k] = round_dtype(fp32(q - z) * fp32(s))  (q, z, s of column n and the
+ *             group of permuted column k; z = 8 when zeros_r is NULL),
  * with fp32 accumulation and one round-to-nearest-even to the output dtype.
  *   x      [M, K] row-major, dtype;  out [M, N] row-major, dtype.
  *   perm   int32 [K] from w4a16_repack (or NULL for identity).
- *   codes_r, scales_r, zeros_r from w4a16_repack.
+ *   codes_r, scales_r, zeros_r from w4a16_repack with the same group_size
+ *          (zeros_r NULL: a symmetric weight).
  *   dtype  W4A16_F16 or W4A16_BF16 (activations and output).
  *   workspace / workspace_bytes: required when the call needs one (a
  *          permutation the kernel does not gather itself, or a split of K);
- *          w4a16_workspace_bytes(M, N, K, 128) bytes always suffice
+ *          w4a16_workspace_bytes(M, N, K, group_size) bytes always suffice
  *          (W4A16_ERR_WORKSPACE when too small), else ignored.
- * Constraints: M >= 1, K % 128 == 0, N % 8 == 0, group_size == 128.
+ * Constraints: M >= 1 and the group sizes above.
  * Async on `stream`.  Results are bitwise reproducible run to run (the split of
  * K over a workgroup's waves is reduced in a fixed order).
  */

@@ -55,7 +55,18 @@ def test_repacked_bytes():
     assert L.w4a16_repacked_bytes(512, 200, 128, 0) == 4 * 4 * 4096   # N padded to 256
     assert L.w4a16_repacked_bytes(500, 256, 128, 0) == -1             # K % 128
     assert L.w4a16_repacked_bytes(512, 20, 128, 0) == -1              # N % 8
-    assert L.w4a16_repacked_bytes(512, 256, 64, 0) == -1              # G != 128
+    # group sizes: 32 / 64 give 4 / 2 meta units per tile, multiples of 128 one
+    assert L.w4a16_repacked_bytes(512, 256, 64, 0) == 4 * 4 * 4096
+    assert L.w4a16_repacked_bytes(512, 256, 64, 1) == 2 * L.w4a16_repacked_bytes(512, 256, 128, 1)
+    assert L.w4a16_repacked_bytes(512, 256, 32, 2) == 4 * L.w4a16_repacked_bytes(512, 256, 128, 2)
+    for G in (256, 512, -1):                                          # -1: per-channel
+        for w in (0, 1, 2):
+            assert L.w4a16_repacked_bytes(512, 256, G, w) == L.w4a16_repacked_bytes(512, 256, 128, w)
+    assert L.w4a16_repacked_bytes(512, 256, 96, 0) == -1              # unsupported G
+    assert L.w4a16_repacked_bytes(512, 256, 16, 0) == -1
+    assert L.w4a16_repacked_bytes(512, 256, 384, 0) == -1             # G does not divide K
+    assert L.w4a16_repacked_bytes(512, 256, 0, 0) == -1
+    assert L.w4a16_repacked_bytes(512, 256, -2, 0) == -1
 
 
 def test_gemm_validation_without_gpu():
@@ -64,8 +75,10 @@ def test_gemm_validation_without_gpu():
     assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 0, 256, 512, 0, NULL, 0, NULL) == 1
     # K not a multiple of the group size
     assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 500, 0, NULL, 0, NULL) == 1
-    # unsupported group size
-    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 64, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 2
+    # unsupported group sizes, and one that does not divide K
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 96, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 16, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 384, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 1
     # unknown dtype
     assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 512, 7, NULL, 0, NULL) == 1
     # NULL required pointer
@@ -106,8 +119,16 @@ def test_quantize_and_repack_validation_without_gpu():
     # g_idx given without a perm buffer
     assert L.w4a16_repack(FAKE, FAKE, FAKE, FAKE, 512, 256, 128, FAKE, FAKE, FAKE, NULL,
                           ctypes.byref(used), NULL) == 1
+    # symmetric weights: qzeros and zeros_r are both NULL or both given
+    assert L.w4a16_repack(FAKE, FAKE, NULL, NULL, 512, 256, 64, FAKE, FAKE, FAKE, NULL,
+                          ctypes.byref(used), NULL) == 1
+    assert L.w4a16_repack(FAKE, FAKE, FAKE, NULL, 512, 256, 64, FAKE, FAKE, NULL, NULL,
+                          ctypes.byref(used), NULL) == 1
+    assert L.w4a16_repack(FAKE, FAKE, NULL, NULL, 512, 256, 96, FAKE, FAKE, NULL, NULL,
+                          ctypes.byref(used), NULL) == 2
     # quantize: g_idx without perm
     assert L.w4a16_quantize_rtn(FAKE, FAKE, NULL, 256, 512, 128, FAKE, FAKE, FAKE, NULL) == 1
+    assert L.w4a16_quantize_rtn(FAKE, NULL, NULL, 256, 512, 48, FAKE, FAKE, NULL, NULL) == 2
     assert L.w4a16_set_timing_events(NULL, NULL) == 0
 
 
