@@ -219,29 +219,22 @@ int4_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ 
     // operand reads come first; the dequant of the next step's B operand is
     // spread between the step's MFMAs (each 32 x 32 x 16 MFMA keeps the matrix
     // pipe busy long enough to issue several VALU instructions behind it).
-    QParam<DT> qp[2];
     float ap[2];  // NF4: a' of this lane's block
     const int zb = ((t & 7) * U) & 7;  // nibble of the tile's first unit
+    if constexpr (FMT == FMT_NF4) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      if constexpr (FMT == FMT_INT4) {
-        if constexpr (U == 1) qp[g].set(sc[g][0] & 0xFFFFu, (zz[g] >> (4 * zb)) & 0xFu);
-      } else {
-        ap[g] = (float)(sc[g][0] & 0xFFu) * __builtin_bit_cast(float, zz[g]);
-      }
+      for (int g = 0; g < 2; ++g) ap[g] = (float)(sc[g][0] & 0xFFu) * __builtin_bit_cast(float, zz[g]);
     }
-    // B operand of step s for column group g: word j = s >> 1 of the tile,
-    // meta unit j U / 4 (U > 1: its parameters are formed at the step)
+    // B operand of step s for column group g: word j = s >> 1 of the tile, in
+    // meta unit j U / 4.  The unit's dequant parameters are formed at the step
+    // (a few VALU instructions between MFMAs); formed once per tile and held
+    // across it they made the small-M launches of this kernel markedly slower.
     auto operand = [&](int s, int g) -> vec {
       if constexpr (FMT == FMT_INT4) {
-        if constexpr (U == 1) {
-          return dequant_word(cw[g][s & 1][s >> 1], qp[g]);
-        } else {
-          const int u = (s >> 1) * U / 4;
-          QParam<DT> q;
-          q.set((sc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu, (zz[g] >> (4 * (zb + u))) & 0xFu);
-          return dequant_word(cw[g][s & 1][s >> 1], q);
-        }
+        const int u = (s >> 1) * U / 4;
+        QParam<DT> q;
+        q.set((sc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu, (zz[g] >> (4 * (zb + u))) & 0xFu);
+        return dequant_word(cw[g][s & 1][s >> 1], q);
       } else {
         const uint32_t w = cw[g][s >> 2][s & 3];
         vec v;
