@@ -253,3 +253,76 @@ def test_symmetric_small_group_product_within_closed_form_bound():
     sk = s.astype(np.float64)[np.arange(K) // G].T
     per_w = sk * 0.5 * (1 + 1e-6) + 2.0**-11 * np.abs(fp.bits_to_f64(wd, "f16")) + 1e-12
     assert np.all(np.abs(y_ref - y_flt) <= np.abs(xf) @ per_w.T)
+
+
+# ----------------------------------------------------- AWQ input scales (f4)
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_xscale_unit_scales_equal_plain_product(dtype):
+    M, N, K = 3, 16, 256
+    x = synth.to_bits(synth.activations("test/xs/unit/x", M, K), dtype)
+    w = synth.to_bits(synth.weights("test/xs/unit/w", N, K), dtype)
+    one = synth.to_bits(np.ones((1, K), np.float32), dtype)[0]
+    assert np.array_equal(gemm.gemm_ref_xscale_bits(x, one, w, dtype), gemm.gemm_ref_bits(x, w, dtype))
+
+
+def test_xscale_onehot_reads_weight_over_scale():
+    # x = e_k: y = (1 / s_k) * w[:, k] (the fp64 quotient x_k / s_k, then one
+    # fp64 product; every other term is an exact zero)
+    N, K = 8, 64
+    w = synth.to_f16_bits(synth.weights("test/xs/oh/w", N, K))
+    s = synth.to_f16_bits(synth.awq_scales("test/xs/oh/s", K)[None, :])[0]
+    for k in (0, 17, 63):
+        x = np.zeros((1, K), np.float32)
+        x[0, k] = 1.0
+        y = gemm.gemm_ref_xscale_bits(synth.to_f16_bits(x), s, w, "f16")
+        want = (1.0 / float(fp.bits_to_f64(s[k:k + 1], "f16")[0])) * fp.bits_to_f64(w[:, k], "f16")
+        assert np.array_equal(y[0], want)
+
+
+def test_xscale_power_of_two_scales_are_exact_shifts():
+    # s_k = 2^e_k: x / s is exact, so the product equals the plain product of
+    # the exactly rescaled activations
+    M, N, K = 2, 12, 128
+    r = np.random.default_rng(31)
+    e = r.integers(-3, 4, size=K)
+    s = synth.to_f16_bits((2.0 ** e).astype(np.float32)[None, :])[0]
+    x = synth.to_f16_bits(synth.activations("test/xs/p2/x", M, K))
+    w = synth.to_f16_bits(synth.weights("test/xs/p2/w", N, K))
+    xd = fp.bits_to_f64(x, "f16") * 2.0 ** -e[None, :]
+    assert np.array_equal(gemm.gemm_ref_xscale_bits(x, s, w, "f16"),
+                          gemm.gemm_ref_fp64(xd, fp.bits_to_f64(w, "f16")))
+
+
+def test_xscale_undoes_awq_weight_folding():
+    # the point of the scales: quantizing W' = W * s and dividing x by s gives
+    # x W^T back up to the quantization error; checked against the closed-form
+    # RTN bound with the per-channel factor 1 / s_k
+    M, N, K, G = 3, 32, 512, 128
+    W = synth.weights("test/xs/fold/W", N, K)
+    s32 = synth.awq_scales("test/xs/fold/s", K)
+    sb = synth.to_f16_bits(s32[None, :])[0]
+    sf = fp.bits_to_f64(sb, "f16")
+    Wf = (W.astype(np.float64) * sf[None, :]).astype(np.float32)
+    q, sc, z = int4.quantize_rtn_int4(Wf, G)
+    wd = int4.dequant_int4(int4.pack_qweight(q), sc, int4.pack_qzeros(z), None, G, "f16")
+    x = synth.to_f16_bits(synth.activations("test/xs/fold/x", M, K))
+    xf = fp.bits_to_f64(x, "f16")
+    y = gemm.gemm_ref_xscale_bits(x, sb, wd, "f16")
+    y_true = xf @ W.astype(np.float64).T
+    sk = sc.astype(np.float64)[np.arange(K) // G].T
+    per_w = (sk * (0.5 + 15 * 2.0**-11) + 2.0**-11 * np.abs(fp.bits_to_f64(wd, "f16"))
+             + 2.0**-23 * np.abs(Wf)) / sf[None, :] + 1e-12
+    assert np.all(np.abs(y - y_true) <= np.abs(xf) @ per_w.T)
+
+
+def test_xscale_gather_divides_by_original_channel():
+    M, N, K, G = 2, 8, 256, 128
+    gi = synth.act_order_gidx("test/xs/perm/g", K, G)
+    perm = repack.canonical_perm(gi, K, G)
+    x = synth.to_bits(synth.activations("test/xs/perm/x", M, K), "bf16")
+    s = synth.to_bits(synth.awq_scales("test/xs/perm/s", K)[None, :], "bf16")[0]
+    w = synth.to_bits(synth.weights("test/xs/perm/w", N, K), "bf16")     # permuted order
+    y = gemm.gemm_ref_xscale_bits(x, s, w, "bf16", perm=perm)
+    xs = fp.bits_to_f64(x, "bf16") / fp.bits_to_f64(s[None, :], "bf16")
+    assert np.array_equal(y, xs[:, perm] @ fp.bits_to_f64(w, "bf16").T)
