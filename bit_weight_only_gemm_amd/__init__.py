@@ -145,6 +145,18 @@ def w4a16_repack(qweight, scales, qzeros, g_idx=None, group_size=GROUP, stream=N
 
 def w4a16_gemm(x, packed, out=None, workspace=None, use_workspace=True, stream=None):
     """y = x @ dequant(W)^T for x [M, K] fp16/bf16 (weights from w4a16_repack)."""
+    return _int4_gemm(x, None, packed, out, workspace, use_workspace, stream)
+
+
+def w4a16_gemm_xscale(x, x_scale, packed, out=None, workspace=None, use_workspace=True,
+                      stream=None):
+    """y = (x / s) @ dequant(W)^T: AWQ input scales s [K] (x's dtype) applied
+    by the GEMM itself."""
+    _need(x_scale, x.dtype, "x_scale", packed["K"])
+    return _int4_gemm(x, x_scale, packed, out, workspace, use_workspace, stream)
+
+
+def _int4_gemm(x, x_scale, packed, out, workspace, use_workspace, stream):
     if x.dtype not in _DT:
         raise TypeError("x must be float16 or bfloat16")
     _need(x, x.dtype, "x")
@@ -164,10 +176,14 @@ def w4a16_gemm(x, packed, out=None, workspace=None, use_workspace=True, stream=N
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     else:
         workspace = None
-    _lib.check(_lib.lib().w4a16_gemm(_ptr(x), _ptr(packed["codes"]), _ptr(packed["scales"]),
-                                     _ptr(packed["zeros"]), _ptr(packed["perm"]), G, _ptr(out),
-                                     M, N, K, _DT[x.dtype], _ptr(workspace), ws_bytes,
-                                     _stream(stream)), "w4a16_gemm")
+    L = _lib.lib()
+    weights = (_ptr(packed["codes"]), _ptr(packed["scales"]), _ptr(packed["zeros"]),
+               _ptr(packed["perm"]), G, _ptr(out), M, N, K, _DT[x.dtype], _ptr(workspace),
+               ws_bytes, _stream(stream))
+    if x_scale is None:
+        _lib.check(L.w4a16_gemm(_ptr(x), *weights), "w4a16_gemm")
+    else:
+        _lib.check(L.w4a16_gemm_xscale(_ptr(x), _ptr(x_scale), *weights), "w4a16_gemm_xscale")
     return out
 
 

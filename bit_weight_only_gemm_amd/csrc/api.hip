@@ -200,7 +200,7 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
 
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
   if (M <= 0 || validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
-  return int4_workspace_bytes(M, N, K, true);
+  return int4_workspace_bytes(M, N, K, true, true);
 }
 
 int w4a16_set_timing_events(void* start_event, void* stop_event) {
@@ -208,24 +208,33 @@ int w4a16_set_timing_events(void* start_event, void* stop_event) {
   return W4A16_OK;
 }
 
-int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
-               const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
-               int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
-               void* stream) {
+int w4a16_gemm_xscale(const void* x, const void* x_scale, const void* codes_r,
+                      const void* scales_r, const void* zeros_r, const int32_t* perm,
+                      int32_t group_size, void* out, int64_t M, int64_t N, int64_t K,
+                      int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
   if (M <= 0 || M > kMaxM) return M <= 0 ? W4A16_ERR_INVALID_ARG : W4A16_ERR_UNSUPPORTED;
   if (int s = validate_int4_shape(K, N, group_size)) return s;
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({x, codes_r, scales_r, out})) return s;
   if (zeros_r && !aligned16(zeros_r)) return W4A16_ERR_MISALIGNED;
+  if (x_scale && !aligned16(x_scale)) return W4A16_ERR_MISALIGNED;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
   if (workspace && !aligned16(workspace)) return W4A16_ERR_MISALIGNED;
-  const int64_t need = int4_workspace_bytes(M, N, K, perm != nullptr);
+  const int64_t need = int4_workspace_bytes(M, N, K, perm != nullptr, x_scale != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
   clear_pending_error();
-  return hip_status(launch_int4_gemm(x, codes_r, scales_r, zeros_r, perm, out, M, N, K,
+  return hip_status(launch_int4_gemm(x, x_scale, codes_r, scales_r, zeros_r, perm, out, M, N, K,
                                      (int)resolve_group(K, group_size), dtype, workspace,
                                      workspace_bytes, (hipStream_t)stream));
+}
+
+int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
+               const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
+               int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
+               void* stream) {
+  return w4a16_gemm_xscale(x, nullptr, codes_r, scales_r, zeros_r, perm, group_size, out, M, N,
+                           K, dtype, workspace, workspace_bytes, stream);
 }
 
 int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,

@@ -128,6 +128,30 @@ __device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const Q
   return __builtin_bit_cast(typename Op<DT>::vec, r);
 }
 
+// AWQ input scaling of 16-bit activations: x / s as the fp32 product of x
+// with the fp32 reciprocal of s (v_rcp_f32, within 1 ulp), rounded once to
+// the activation type.  Shared by the decode kernel's staged rows and the
+// activation preparation pass, so both produce the same operand bits.
+template <int DT>
+__device__ __forceinline__ float f16bits_to_f32(uint16_t v) {
+  if constexpr (DT == DT_F16) return (float)__builtin_bit_cast(_Float16, v);
+  else return __builtin_bit_cast(float, (uint32_t)v << 16);
+}
+template <int DT>
+__device__ __forceinline__ float recip_scale(uint16_t s) {
+  return __builtin_amdgcn_rcpf(f16bits_to_f32<DT>(s));
+}
+template <int DT>
+__device__ __forceinline__ uint16_t mul_round16(uint16_t x, float r) {
+  const float f = f16bits_to_f32<DT>(x) * r;
+  if constexpr (DT == DT_F16) return __builtin_bit_cast(uint16_t, (_Float16)f);
+  else return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+template <int DT>
+__device__ __forceinline__ uint16_t div_scale1(uint16_t x, uint16_t s) {
+  return mul_round16<DT>(x, recip_scale<DT>(s));
+}
+
 // ---- raw buffer loads (gfx9-family descriptors).  A load whose per-lane
 // offset is at or past the descriptor's byte range returns 0, which is how
 // kernels read rows past M, codes past a tail and padding without branches;

@@ -17,9 +17,10 @@
 //    every wave64 vector-memory instruction costs the CU's load path about
 //    the same whatever its active lanes.  So per K tile a wave issues one
 //    16-byte-per-lane load of codes (a contiguous, coalesced 1 KB tile), the
-//    scales and zeros come once per run of 8 tiles (one 16-byte and one 4-byte
-//    load per lane), and for M <= 4 one 16-byte load per lane carries the
-//    activations of all 4 MFMA steps of the tile (see "packed" below).
+//    scales and zeros come once per run of 8 tiles (for G >= 128 one 16-byte
+//    and one 4-byte load per lane), and for M <= 4 one 16-byte load per lane
+//    carries the activations of all 4 MFMA steps of the tile (see "packed"
+//    below).
 //  * Each 32-bit code word is dequantized exactly into an 8-element MFMA
 //    operand (the routine the dequant export uses) and multiplied with
 //    v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation.
@@ -34,9 +35,14 @@
 //    divergent branch and no load result merges through a branch (either
 //    would make the compiler drain every outstanding load per tile); rows
 //    >= M read 0 through the descriptor range.
-//  * For an act-order weight the activations are first permuted once,
-//    x_p[:, k] = x[:, perm[k]], into the workspace by a small gather kernel, so
-//    the GEMM itself always streams contiguous rows.
+//  * Act-order permutation and AWQ input scales: for M <= 4 rows and a small
+//    enough grid every workgroup stages the rows (with the permutation and/or
+//    the scales) in LDS, divides them by the scales once and gathers
+//    x[m][perm[k]] from there; otherwise a small preparation kernel writes
+//    x[:, perm] / s into the workspace first and the GEMM streams contiguous
+//    rows.
+//  * Group sizes below 128 (U = 128 / G meta units per K tile) read U times the
+//    scales and zeros per run; a symmetric weight reads no zeros at all.
 #include <hip/hip_ext.h>
 
 #include "common.h"
@@ -55,13 +61,20 @@ constexpr int RUN = 8;                  // K tiles per meta run and ring pass
 // carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
 // tile.  XGATHER: PACKED for an act-order weight, with the M rows of x and
 // the permutation staged in LDS once per workgroup; the operand is gathered
-// from LDS, x[m][perm[k]], so no separate permutation pass runs.
-enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2 };
+// from LDS, x[m][perm[k]], so no separate permutation pass runs.  XSTAGED:
+// PACKED with the M rows of x staged in LDS and read from there (used with
+// AWQ input scales, below).  With input scales (XS) the staged rows are
+// divided by s in place, once per workgroup, before the loop: each x element
+// is scaled once per workgroup instead of once per use.
+enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3 };
 constexpr bool is_packed(int am) { return am != AM_FULL; }
+constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; }
 
-// Largest LDS footprint of the staged activations (+ permutation): with the
-// reduction buffer, two workgroups still fit a CU's 160 KB.
-constexpr int64_t kMaxXlds = 72 * 1024;
+// Largest LDS footprint of the staged activations (+ permutation, + input
+// scales) per workgroup: past it the staging costs more than the separate
+// preparation pass it saves (measured on MI355X), and it leaves room for
+// several workgroups per CU.
+constexpr int64_t kMaxXlds = 32 * 1024;
 
 // Timing events for the next main-kernel launch on this host thread (set by
 // w4a16_set_timing_events; consumed by one launch).
@@ -311,6 +324,10 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
                          v[6] | (v[7] << 16)};
       a[0] = __builtin_bit_cast(vec, w);
     }
+  } else if constexpr (AM == AM_XSTAGED) {
+    const int j = r >> 2, m = min(r & 3, xs.M - 1);
+    const uint32_t kg = (uint32_t)(t * 128 + WP::xk(j, b));
+    a[0] = *(const vec*)(xs.xl + ((uint32_t)m * (uint32_t)K + kg) * 2u);
   } else if constexpr (AM == AM_PACKED) {
     const int j = r >> 2, m = r & 3;
     const int kin = WP::xk(j, b);
@@ -334,11 +351,17 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
 
 // Bytes of LDS the staged activations and permutation take, each region
 // rounded up to whole 1 KB blocks.
+// Staged LDS layout: x rows [M][K], then (gather) the permutation int32[K],
+// then (input scales) s [K].
 __host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
   return (uint32_t)((M * K * 2 + 1023) / 1024 * 1024);
 }
-__host__ __device__ constexpr uint32_t xlds_bytes(int M, int K) {
-  return xlds_x_bytes(M, K) + (uint32_t)((K * 4 + 1023) / 1024 * 1024);
+__host__ __device__ constexpr uint32_t xlds_perm_bytes(int K, bool perm) {
+  return perm ? (uint32_t)((K * 4 + 1023) / 1024 * 1024) : 0u;
+}
+__host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool perm, bool xs) {
+  return xlds_x_bytes(M, K) + xlds_perm_bytes(K, perm) +
+         (xs ? (uint32_t)((K * 2 + 1023) / 1024 * 1024) : 0u);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
@@ -358,11 +381,16 @@ __device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8
     lds_dma16(r, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), 0);
 }
 
-template <int DT, int MT, int AM, class WP>
-__device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& wp,
+// XS: divide the staged activations by the AWQ input scales xsc [K] (staged
+// modes only).
+template <int DT, int MT, int AM, bool XS, class WP>
+__device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
+                                            const uint16_t* __restrict__ xsc, WP& wp,
                                             uint16_t* __restrict__ out, int M, int N, int K,
                                             int KT, float* red, const int32_t* perm,
                                             uint8_t* xlds) {
+  static_assert(!XS || is_staged(AM), "input scales are applied to staged rows");
+  static_assert(AM != AM_XSTAGED || XS, "rows are staged for input scales");
   constexpr int NA = is_packed(AM) ? 1 : MT * 4;                   // A vectors per tile
   constexpr int NACC = is_packed(AM) ? 4 : MT * (MT == 1 ? 4 : (MT == 2 ? 2 : 1));  // acc tiles
   constexpr int PA = is_packed(AM) ? RUN : (MT == 1 ? 2 : 1);      // A ring depth
@@ -398,12 +426,32 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
 #pragma unroll
     for (int s = 0; s < RUN; ++s) ring[s] = wp.load_codes(t0 + min(s, n - 1), lane);
   }
-  if constexpr (AM == AM_XGATHER) {
-    // every wave takes part in staging the M rows of x and the permutation
-    // while its first code tiles are in flight
+  if constexpr (is_staged(AM)) {
+    // every wave takes part in staging the M rows of x (and the permutation,
+    // and the input scales) while its first code tiles are in flight
+    const uint32_t xb = xlds_x_bytes(M, K), pb = xlds_perm_bytes(K, AM == AM_XGATHER);
     stage_lds(x, (uint32_t)(M * K * 2), xlds, wave, lane);
-    stage_lds(perm, (uint32_t)(K * 4), xlds + xlds_x_bytes(M, K), wave, lane);
+    if constexpr (AM == AM_XGATHER) stage_lds(perm, (uint32_t)(K * 4), xlds + xb, wave, lane);
+    if constexpr (XS) stage_lds(xsc, (uint32_t)(K * 2), xlds + xb + pb, wave, lane);
     __syncthreads();
+    if constexpr (XS) {
+      // x[m][k] / s[k] in place (original column order): a pair of columns per
+      // step, their reciprocals shared by the M rows
+      uint32_t* xw = (uint32_t*)xlds;
+      const uint32_t* sw = (const uint32_t*)(xlds + xb + pb);
+      const int half = K >> 1;
+      for (int kp = threadIdx.x; kp < half; kp += 64 * DW) {
+        const uint32_t sv = sw[kp];
+        const float r0 = recip_scale<DT>((uint16_t)(sv & 0xFFFFu));
+        const float r1 = recip_scale<DT>((uint16_t)(sv >> 16));
+        for (int m = 0; m < M; ++m) {
+          const uint32_t v = xw[m * half + kp];
+          xw[m * half + kp] = (uint32_t)mul_round16<DT>((uint16_t)(v & 0xFFFFu), r0) |
+                              ((uint32_t)mul_round16<DT>((uint16_t)(v >> 16), r1) << 16);
+        }
+      }
+      __syncthreads();
+    }
   }
   if (n > 0) {
 #pragma unroll
@@ -484,9 +532,10 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x, WP& 
   }
 }
 
-template <int DT, int MT, int AM, int U>
+template <int DT, int MT, int AM, int U, bool XS>
 __global__ void __launch_bounds__(64 * DW)
-int4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
+int4_decode_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ xsc,
+                   const uint8_t* __restrict__ codes,
                    const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
                    uint32_t zx, const int32_t* __restrict__ perm, uint16_t* __restrict__ out,
                    int M, int N, int K, int KT) {
@@ -498,7 +547,7 @@ int4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ c
   wp.zeros = zeros;
   wp.zx = zx;
   wp.KT = KT;
-  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red, perm, xlds);
+  decode_body<DT, MT, AM, XS>(x, xsc, wp, out, M, N, K, KT, red, perm, xlds);
 }
 
 template <int DT, int MT, int AM, bool BATCH>
@@ -516,26 +565,41 @@ nf4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
   wp.aq = aq;
   wp.asc = asc;
   wp.lut = lut;
-  decode_body<DT, MT, AM>(x, wp, out, M, N, K, KT, red, nullptr, xlds);
+  decode_body<DT, MT, AM, false>(x, nullptr, wp, out, M, N, K, KT, red, nullptr, xlds);
 }
 
-// x_p[m, k] = x[m, perm[k]]: one thread per 8 consecutive permuted columns.
+// Activation preparation pass: x_p[m, k] = x[m, perm[k]] (perm may be null:
+// identity), divided by the AWQ input scale s[perm[k]] when xsc is given (the
+// same rounding as the fused loads).  One thread per 8 consecutive columns.
+template <int DT>
 __global__ void __launch_bounds__(256)
-permute_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-                 uint16_t* __restrict__ xp, int M, int K) {
+prep_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+              const uint16_t* __restrict__ xsc, uint16_t* __restrict__ xp, int M, int K) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_row = K >> 3;
   if (idx >= (int64_t)M * per_row) return;
   const int64_t m = idx / per_row;
   const int k = (int)(idx - m * per_row) * 8;
   const uint16_t* xr = x + m * K;
-  const int4* pp = (const int4*)(perm + k);
-  const int4 p0 = pp[0], p1 = pp[1];
+  int src[8];
+  if (perm) {
+    const int4* pp = (const int4*)(perm + k);
+    const int4 p0 = pp[0], p1 = pp[1];
+    src[0] = p0.x; src[1] = p0.y; src[2] = p0.z; src[3] = p0.w;
+    src[4] = p1.x; src[5] = p1.y; src[6] = p1.z; src[7] = p1.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) src[e] = k + e;
+  }
+  uint32_t h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = xr[src[e]];
+    if (xsc) h[e] = div_scale1<DT>((uint16_t)h[e], xsc[src[e]]);
+  }
   u32x4_t v;
-  v[0] = (uint32_t)xr[p0.x] | ((uint32_t)xr[p0.y] << 16);
-  v[1] = (uint32_t)xr[p0.z] | ((uint32_t)xr[p0.w] << 16);
-  v[2] = (uint32_t)xr[p1.x] | ((uint32_t)xr[p1.y] << 16);
-  v[3] = (uint32_t)xr[p1.z] | ((uint32_t)xr[p1.w] << 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = h[2 * i] | (h[2 * i + 1] << 16);
   *(u32x4_t*)(xp + m * K + k) = v;
 }
 
@@ -552,108 +616,135 @@ static void allow_dynamic_lds(const void* kernel) {
   if (ndone < 32) done[ndone++] = kernel;
 }
 
-// Activation mode and row tiles per workgroup row block for M rows; gather:
-// an act-order permutation is to be applied.
-static int pick_mode(int64_t M, int64_t K, bool gather, int* mt) {
+// Largest total of staged bytes (workgroups x bytes each) for which staging
+// beats a separate preparation pass: every workgroup copies the rows (and the
+// permutation and scales) from L2, so the cost grows with the grid, while the
+// pass costs about one launch (measured crossover on MI355X: staging saves
+// ~1 us on 4096 x 4096 layers and costs ~10 us on 5120 x 55296 ones).
+constexpr int64_t kMaxStagedTotal = (int64_t)12 << 20;
+
+// Activation mode and row tiles per workgroup row block for M rows of a
+// [N, K] layer; gather: an act-order permutation is to be applied, xs: AWQ
+// input scales.  For M <= 4 both are done on the rows staged in LDS when they
+// fit and the grid is small enough (staging x alone does not beat per-tile
+// loads).  Otherwise the caller prepares x first.
+static int pick_mode(int64_t M, int64_t N, int64_t K, bool gather, bool xs, int* mt) {
   if (M <= 4) {
     *mt = 1;
-    // staging x alone in LDS does not beat per-tile loads; the gather pays
-    // for itself by saving the separate permutation pass
-    if (gather && xlds_bytes((int)M, (int)K) <= kMaxXlds) return AM_XGATHER;
+    const int64_t b = xlds_bytes((int)M, (int)K, gather, xs);
+    if ((gather || xs) && b <= kMaxXlds && ceil_div(N, 16) * b <= kMaxStagedTotal)
+      return gather ? AM_XGATHER : AM_XSTAGED;
     return AM_PACKED;
   }
   *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   return AM_FULL;
 }
 
-template <int DT, int MT, int AM, int U>
-static void launch_int4_v(const void* x, const void* codes_r, const void* scales_r,
-                          const void* zeros_r, const int32_t* perm, void* out, int64_t M,
-                          int64_t N, int64_t K, hipStream_t stream) {
-  const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  const size_t lds = AM == AM_XGATHER ? xlds_bytes((int)M, (int)K) : 0;
-  if (lds) allow_dynamic_lds((const void*)int4_decode_kernel<DT, MT, AM, U>);
+// One decode launch.  a: the call's arguments (xsc non-null only when the
+// kernel scales the activations itself).
+struct DecodeArgs {
+  const void *x, *xsc, *codes, *scales, *zeros;
+  const int32_t* perm;
+  void* out;
+  int64_t M, N, K;
+  hipStream_t stream;
+};
+
+template <int DT, int MT, int AM, int U, bool XS>
+static void launch_int4_v(const DecodeArgs& a) {
+  const dim3 grid((unsigned)ceil_div(a.N, 16), (unsigned)ceil_div(a.M, 16 * MT));
+  const size_t lds =
+      is_staged(AM) ? xlds_bytes((int)a.M, (int)a.K, AM == AM_XGATHER, XS) : 0;
+  if (lds) allow_dynamic_lds((const void*)int4_decode_kernel<DT, MT, AM, U, XS>);
   // a symmetric weight: the zeros descriptor gets an empty range over a valid
   // base and every zero nibble reads 0 ^ 8
-  const uint32_t zx = zeros_r ? 0u : kSymZeroXor;
-  launch_timed(int4_decode_kernel<DT, MT, AM, U>, grid, dim3(64 * DW), lds, stream,
-               (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r,
-               (const uint8_t*)(zeros_r ? zeros_r : scales_r), zx, perm, (uint16_t*)out,
-               (int)M, (int)N, (int)K, (int)(K / 128));
+  const uint32_t zx = a.zeros ? 0u : kSymZeroXor;
+  launch_timed(int4_decode_kernel<DT, MT, AM, U, XS>, grid, dim3(64 * DW), lds, a.stream,
+               (const uint16_t*)a.x, (const uint16_t*)a.xsc, (const uint8_t*)a.codes,
+               (const uint8_t*)a.scales, (const uint8_t*)(a.zeros ? a.zeros : a.scales), zx,
+               AM == AM_XGATHER ? a.perm : nullptr, (uint16_t*)a.out, (int)a.M, (int)a.N,
+               (int)a.K, (int)(a.K / 128));
 }
 
-template <int DT, int U>
-static void launch_int4_mode(int am, int mt, const void* x, const void* codes_r,
-                             const void* scales_r, const void* zeros_r, const int32_t* perm,
-                             void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (am == AM_XGATHER)
-    launch_int4_v<DT, 1, AM_XGATHER, U>(x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
-  else if (am == AM_PACKED)
-    launch_int4_v<DT, 1, AM_PACKED, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K,
-                                       stream);
-  else if (mt == 1)
-    launch_int4_v<DT, 1, AM_FULL, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
-  else if (mt == 2)
-    launch_int4_v<DT, 2, AM_FULL, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
-  else
-    launch_int4_v<DT, 4, AM_FULL, U>(x, codes_r, scales_r, zeros_r, nullptr, out, M, N, K, stream);
+template <int DT, int U, bool XS>
+static void launch_int4_mode(int am, int mt, const DecodeArgs& a) {
+  if (am == AM_XGATHER) return launch_int4_v<DT, 1, AM_XGATHER, U, XS>(a);
+  if constexpr (XS) {
+    launch_int4_v<DT, 1, AM_XSTAGED, U, true>(a);  // the only other mode that scales
+  } else {
+    if (am == AM_PACKED) launch_int4_v<DT, 1, AM_PACKED, U, false>(a);
+    else if (mt == 1) launch_int4_v<DT, 1, AM_FULL, U, false>(a);
+    else if (mt == 2) launch_int4_v<DT, 2, AM_FULL, U, false>(a);
+    else launch_int4_v<DT, 4, AM_FULL, U, false>(a);
+  }
 }
 
-template <int DT>
-static void launch_int4_dt(int am, int mt, int G, const void* x, const void* codes_r,
-                           const void* scales_r, const void* zeros_r, const int32_t* perm,
-                           void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+template <int DT, bool XS>
+static void launch_int4_dt(int am, int mt, int G, const DecodeArgs& a) {
   const int U = units_per_tile(G);
-  if (U == 1)
-    launch_int4_mode<DT, 1>(am, mt, x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
-  else if (U == 2)
-    launch_int4_mode<DT, 2>(am, mt, x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
-  else
-    launch_int4_mode<DT, 4>(am, mt, x, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
+  if (U == 1) launch_int4_mode<DT, 1, XS>(am, mt, a);
+  else if (U == 2) launch_int4_mode<DT, 2, XS>(am, mt, a);
+  else launch_int4_mode<DT, 4, XS>(am, mt, a);
 }
 
-// Workspace layout: the permuted activations (when the activations are
-// permuted in a separate pass), then the prefill split-K partials (when the
-// prefill kernel splits K).
-static int64_t xperm_bytes(int64_t M, int64_t N, int64_t K, bool perm) {
+// Workspace layout: the prepared activations (when they are permuted and/or
+// divided by the AWQ input scales in a separate pass), then the large-M
+// kernel's split-K partials (when it splits K).  The decode kernel gathers and
+// scales M <= 4 rows itself when they fit on chip; other decode calls and the
+// large-M kernel (whose activations go from memory straight into LDS) use the
+// pass.
+static int64_t xprep_bytes(int64_t M, int64_t N, int64_t K, bool perm, bool xs) {
+  if (!perm && !xs) return 0;
+  const int64_t bytes = ceil_div(M * K * 2, 256) * 256;
+  if (use_prefill(M, N, K)) return bytes;
   int mt;
-  if (!perm || (!use_prefill(M, N, K) && pick_mode(M, K, true, &mt) == AM_XGATHER)) return 0;
-  return ceil_div(M * K * 2, 256) * 256;
+  return is_staged(pick_mode(M, N, K, perm, xs, &mt)) ? 0 : bytes;
 }
 
-int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm) {
-  return xperm_bytes(M, N, K, perm) +
+int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm, bool xs) {
+  return xprep_bytes(M, N, K, perm, xs) +
          (use_prefill(M, N, K) ? prefill_workspace_bytes(M, N, K) : 0);
 }
 
-hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scales_r,
-                            const void* zeros_r, const int32_t* perm, void* out, int64_t M,
-                            int64_t N, int64_t K, int G, int dtype, void* workspace,
-                            int64_t /*workspace_bytes*/, hipStream_t stream) {
+hipError_t launch_int4_gemm(const void* x, const void* xsc, const void* codes_r,
+                            const void* scales_r, const void* zeros_r, const int32_t* perm,
+                            void* out, int64_t M, int64_t N, int64_t K, int G, int dtype,
+                            void* workspace, int64_t /*workspace_bytes*/, hipStream_t stream) {
   int mt = 1;
   const bool pf = use_prefill(M, N, K);
-  const int am = pf ? AM_FULL : pick_mode(M, K, perm != nullptr, &mt);
+  const int64_t xb = xprep_bytes(M, N, K, perm != nullptr, xsc != nullptr);
   const void* xa = x;
-  const int64_t xb = xperm_bytes(M, N, K, perm != nullptr);
   if (xb > 0) {
-    // the activations are permuted once into the workspace
+    // the activations are prepared once into the workspace
     const int64_t n8 = M * (K / 8);
-    hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)ceil_div(n8, 256)), dim3(256), 0, stream,
-                       (const uint16_t*)x, perm, (uint16_t*)workspace, (int)M, (int)K);
+    const dim3 grid((unsigned)ceil_div(n8, 256));
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(prep_x_kernel<DT_F16>, grid, dim3(256), 0, stream, (const uint16_t*)x,
+                         perm, (const uint16_t*)xsc, (uint16_t*)workspace, (int)M, (int)K);
+    else
+      hipLaunchKernelGGL(prep_x_kernel<DT_BF16>, grid, dim3(256), 0, stream, (const uint16_t*)x,
+                         perm, (const uint16_t*)xsc, (uint16_t*)workspace, (int)M, (int)K);
     xa = workspace;
   }
-  if (pf)
+  if (pf) {
     launch_int4_prefill(xa, codes_r, scales_r, zeros_r, out, (uint8_t*)workspace + xb, M, N, K,
                         G, dtype, stream);
-  else if (dtype == DT_F16)
-    launch_int4_dt<DT_F16>(am, mt, G, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K, stream);
-  else
-    launch_int4_dt<DT_BF16>(am, mt, G, xa, codes_r, scales_r, zeros_r, perm, out, M, N, K,
-                            stream);
+    return hipGetLastError();
+  }
+  // what the decode kernel still has to do itself
+  const bool gather = perm && xb == 0, scale = xsc && xb == 0;
+  const int am = pick_mode(M, N, K, gather, scale, &mt);
+  const DecodeArgs a{xa, scale ? xsc : nullptr, codes_r, scales_r, zeros_r,
+                     gather ? perm : nullptr, out, M, N, K, stream};
+  if (dtype == DT_F16) {
+    if (scale) launch_int4_dt<DT_F16, true>(am, mt, G, a);
+    else launch_int4_dt<DT_F16, false>(am, mt, G, a);
+  } else {
+    if (scale) launch_int4_dt<DT_BF16, true>(am, mt, G, a);
+    else launch_int4_dt<DT_BF16, false>(am, mt, G, a);
+  }
   return hipGetLastError();
 }
-
-
 
 template <int DT, int MT, int AM, bool BATCH>
 static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, const float* asc,
@@ -670,7 +761,7 @@ static void launch_nf4_dt(const void* x, const uint8_t* q, const uint8_t* aq, co
                           const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream) {
   int mt;
-  const int am = pick_mode(M, K, false, &mt);
+  const int am = pick_mode(M, N, K, false, false, &mt);
   if (am == AM_PACKED)
     launch_nf4_v<DT, 1, AM_PACKED, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
   else if (mt == 1)

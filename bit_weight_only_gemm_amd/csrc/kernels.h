@@ -25,9 +25,10 @@ __host__ __device__ constexpr int units_per_tile(int G) { return G < 128 ? 128 /
 constexpr uint32_t kSymZeroXor = 0x88888888u;
 
 // Workspace bytes the INT4 GEMM needs at this shape, with or without a column
-// permutation: room for the permuted activations (when they are permuted in a
-// separate pass) and for the prefill kernel's split-K partials.
-int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm);
+// permutation and AWQ input scales: room for the prepared activations (when
+// they are permuted and/or scaled in a separate pass) and for the prefill
+// kernel's split-K partials.
+int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm, bool xs);
 // Bytes of the prefill kernel's split-K partials at this shape (0: no split).
 int64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -54,9 +55,11 @@ hipError_t launch_dequant_nf4(const uint8_t* qweight, const uint8_t* absmax_q,
                               const float* absmax_scale, int64_t N, int64_t K, int dtype,
                               const Nf4Table& L, void* w_out, hipStream_t stream);
 
-hipError_t launch_int4_gemm(const void* x, const void* codes_r, const void* scales_r,
-                            const void* zeros_r, const int32_t* perm, void* out, int64_t M,
-                            int64_t N, int64_t K, int G, int dtype, void* workspace,
+// xsc: AWQ input scales s [K] (activation dtype) or nullptr.
+hipError_t launch_int4_gemm(const void* x, const void* xsc, const void* codes_r,
+                            const void* scales_r, const void* zeros_r, const int32_t* perm,
+                            void* out, int64_t M, int64_t N, int64_t K, int G, int dtype,
+                            void* workspace,
                             int64_t workspace_bytes, hipStream_t stream);
 // Whether w4a16_gemm runs the LDS-staged large-M kernel (activations shared
 // by a workgroup's 256 columns through LDS) rather than the skinny decode

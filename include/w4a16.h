@@ -169,12 +169,16 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
                  int32_t* perm_used_host, void* stream);
 
 /*
- * Workspace bytes w4a16_gemm needs at this shape (covering calls with a
- * column permutation): room for the permuted activations x[:, perm] (none
- * where the kernel gathers x[:, perm] itself: M <= 4 with M*K*2 + K*4 bytes
- * within its on-chip staging, about 72 KB) plus the fp32 partials S*M*N*4 of
- * the large-M kernel (M >= 32, or M >= 12 on layers of 100 Mi weights and
- * more) when it splits K over S workgroups.
+ * Workspace bytes w4a16_gemm and w4a16_gemm_xscale need at this shape
+ * (covering calls with a column permutation and with input scales): room for
+ * the prepared activations M*K*2 where a separate pass writes x[:, perm]
+ * and/or x / s, plus the fp32 partials S*M*N*4 of the large-M kernel (M >= 32,
+ * or M >= 12 on layers of 100 Mi weights and more) when it splits K over S
+ * workgroups.  A given call may need less, or nothing: no pass runs where
+ * the decode kernel gathers x[:, perm] and/or divides by s itself (M <= 4,
+ * the rows, the permutation and the scales staged on chip: at most 32 KB per
+ * workgroup and 12 MiB over its grid of N/16 workgroups); each call
+ * validates what it needs.
  * Calls that overlap in time must not share a workspace.
  */
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
@@ -203,6 +207,26 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
                const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
                int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
                void* stream);
+
+/*
+ * w4a16_gemm with AWQ input scales ([P3] §4.1: the weights of salient input
+ * channels are scaled up by s_k before quantization and the activations
+ * divided by s_k; here the division is applied by the GEMM, so callers pass
+ * the raw activations):
+ *   y[m, n] = sum_k (x[m, perm[k]] / s[perm[k]]) * w[n, k].
+ *   x_scale  s [K] in the activation dtype (finite, non-zero), indexed by
+ *            original input channel; NULL makes the call w4a16_gemm.
+ * Each x / s is formed as x * (fp32 reciprocal of s, within 1 ulp) and rounded
+ * once to the activation dtype before the multiply.  For M <= 4 rows that the
+ * decode kernel stages on chip (see w4a16_workspace_bytes) every workgroup
+ * divides its staged copy once; otherwise a preparation pass writes x / s
+ * (permuted) into the workspace first.  Other arguments, constraints and the workspace rule as for
+ * w4a16_gemm (w4a16_workspace_bytes covers these calls too).
+ */
+int w4a16_gemm_xscale(const void* x, const void* x_scale, const void* codes_r,
+                      const void* scales_r, const void* zeros_r, const int32_t* perm,
+                      int32_t group_size, void* out, int64_t M, int64_t N, int64_t K,
+                      int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * Test/debug export: the dequantized weight matrix w [N, K] (dtype), in the

@@ -90,13 +90,28 @@ def test_gemm_validation_without_gpu():
     assert need >= 16 * 4096 * 2
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, FAKE, need - 16, NULL) == 5
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, NULL, 0, NULL) == 5
-    # M <= 4 with x and perm small enough to stage on chip: gathered in the
-    # kernel, no workspace
+    # the size covers every call at a shape, with or without a permutation and
+    # AWQ input scales: M <= 4 rows (with the permutation and the scales) that
+    # the decode kernel stages on chip need no workspace (up to 32 KB per
+    # workgroup and 12 MiB over the grid: 256 x 24 KB here) ...
     assert L.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
-    assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) == 0
-    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) == 0
+    # ... larger ones are prepared in a pass: M * K * 2 bytes
+    assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) >= 4 * 4096 * 2     # 256 x 56 KB
+    assert L.w4a16_workspace_bytes(1, 55296, 5120, 128) >= 5120 * 2        # 3456 workgroups
+    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) >= 11008 * 2
     assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) >= 4 * 11008 * 2
     assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 5 * 4096 * 2
+    # w4a16_gemm_xscale validates what the call needs (each case below fails
+    # before any launch)
+    xs = L.w4a16_gemm_xscale
+    # scales with rows that do not fit on chip, and with M > 4: a pass
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 4, 4096, 11008, 0, NULL, 0, NULL) == 5
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 4, 4096, 11008, 0, NULL, 0, NULL) == 5
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 8, 4096, 4096, 0, NULL, 0, NULL) == 5
+    assert xs(FAKE, ODD, FAKE, FAKE, FAKE, NULL, 128, FAKE, 2, 4096, 4096, 0, NULL, 0, NULL) == 3
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 96, FAKE, 2, 4096, 4096, 0, NULL, 0, NULL) == 2
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 64, 5120, 5120, 0, NULL, 0,
+              NULL) == 5
     # a prefill-sized call that splits K needs room for fp32 partials even
     # without a permutation
     need = L.w4a16_workspace_bytes(64, 5120, 5120, 128)
