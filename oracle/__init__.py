@@ -21,6 +21,7 @@ Modules
 -------
 fp     -- IEEE rounding helpers (fp32 -> bf16 round-to-nearest-even by bit ops).
 int4   -- RTN group quantizer, GPTQ-style packing/unpacking, int4 dequant.
+intb   -- the same at 3, 4 or 8 bits (bit-stream packing of 32-code runs).
 nf4    -- NF4 codebook (closed form), block quantizer, double quant, dequant.
 gemm   -- fp64 reference product and the relative-error score.
 repack -- reference implementation of the repacked tile layout and its inverse.
@@ -31,4 +32,4 @@ library routines.  Bit-compatibility with third-party checkpoints or libraries
 is "parity unpinned": the pages give no byte layout for them.
 """
 
-from . import fp, int4, nf4, gemm, repack  # noqa: F401
+from . import fp, int4, intb, nf4, gemm, repack  # noqa: F401

@@ -152,3 +152,135 @@ def unrepack_ref(codes_r, scales_r, zeros_r, K, N, group_size=GROUP):
         zu = z8.transpose(1, 4, 5, 0, 2, 3).reshape(KT8 * 8 * U, NP * 64)[:KT * U, :N]
         z = from_units(zu)
     return q.copy(), s.copy(), None if z is None else z.copy()
+
+
+# --------------------------------------------------- 3- and 8-bit tile layouts
+#
+# The same tiles (16 columns x 128 permuted inputs, lane l = i + 16b holding
+# inputs 128t + 32j + 8b + e of column i for the 4 MFMA steps j), with the
+# lane's 32 codes in b-bit form:
+#
+# * b = 4: as above (4 dwords, dword j, nibble slot (e >> 1) + 4(e & 1)).
+# * b = 8: 8 dwords per lane in two halves h = j >> 1 of 16 bytes each; the
+#   tile is uint8 [2][64][16] (so each half of the tile is 1 KB contiguous).
+#   Code (j, e) sits in dword 2(j & 1) + (e >> 2) of half j >> 1, at byte slot
+#   ((e & 3) >> 1) + 2(e & 1): a dword holds elements [e0, e2, e1, e3] so that
+#   (d >> 8r) & 0x00FF00FF is the element pair (2r, 2r + 1).
+# * b = 3: 3 dwords per lane (tile uint8 [64][12]).  The low 2 bits of code
+#   (j, e) sit in dword j >> 1 at bit 16(e & 1) + 2(4(j & 1) + (e >> 1)); its
+#   high bit in dword 2 at bit 16(e & 1) + 4j + (e >> 1).
+#
+# Zeros: 4-bit fields (b <= 4, as above) or 8-bit fields (b = 8: U x 2 dwords
+# per (panel, run, column), unit r of the run at byte r).  Scales as above.
+
+TILE_DWORDS = {3: 3, 4: 4, 8: 8}
+
+
+def _code_parts(bits, j, e):
+    """[(dword index within the lane's tile dwords, bit shift, value bits)]
+    for code (j, e): value bits = (mask, right shift) applied to the code."""
+    if bits == 4:
+        return [(j, 4 * nibble_slot(e), (0xF, 0))]
+    if bits == 8:
+        return [(4 * (j >> 1) + 2 * (j & 1) + (e >> 2), 8 * (((e & 3) >> 1) + 2 * (e & 1)),
+                 (0xFF, 0))]
+    return [(j >> 1, 16 * (e & 1) + 2 * (4 * (j & 1) + (e >> 1)), (0x3, 0)),
+            (2, 16 * (e & 1) + 4 * j + (e >> 1), (0x1, 2))]
+
+
+def _lane_dwords_to_bytes(words, bits):
+    """words [NP, KT, 4, 64, D] -> the tile byte order of ``bits``."""
+    if bits == 8:   # [.., 64, 2 halves, 4] -> [.., 2, 64, 4]
+        words = words.reshape(words.shape[:-1] + (2, 4)).swapaxes(-3, -2)
+    return np.ascontiguousarray(words).view(np.uint8).reshape(-1)
+
+
+def _bytes_to_lane_dwords(codes_r, bits, NP, KT):
+    D = TILE_DWORDS[bits]
+    w = np.asarray(codes_r, dtype=np.uint8).view(np.uint32)
+    if bits == 8:
+        return w.reshape(NP, KT, 4, 2, 64, 4).swapaxes(-3, -2).reshape(NP, KT, 4, 64, 8)
+    return w.reshape(NP, KT, 4, 64, D)
+
+
+def repack_ref_bits(qweight, scales, qzeros, bits, g_idx=None, group_size=GROUP):
+    """b-bit canonical tensors (``intb`` packing) -> (codes_r, scales_r, zeros_r, perm)."""
+    from .intb import unpack_qweight as unpack_b, unpack_qzeros as unpack_zb
+    G = int(group_size)
+    q = unpack_b(qweight, bits)
+    N, K = q.shape
+    assert valid_group_size(K, G)
+    s = np.asarray(scales, dtype=np.float16)
+    z = None if qzeros is None else unpack_zb(qzeros, bits)[:, :N]
+    KT, U, NP = K // TILE, units_per_tile(G), (N + 63) // 64
+    perm = canonical_perm(g_idx, K, G)
+    if perm is not None:
+        q = q[:, perm]
+    Np = NP * 64
+    qp = np.zeros((Np, K), dtype=np.uint8)
+    qp[:N] = q
+    v = qp.reshape(NP, 4, 16, KT, 4, 4, 8).astype(np.uint32)        # p c i t j b e
+    words = np.zeros((NP, KT, 4, 4, 16, TILE_DWORDS[bits]), dtype=np.uint32)  # p t c b i d
+    for j in range(4):
+        for e in range(8):
+            code = v[:, :, :, :, j, :, e].transpose(0, 3, 1, 4, 2)     # p t c b i
+            for d, sh, (mask, rs) in _code_parts(bits, j, e):
+                words[..., d] |= ((code >> np.uint32(rs)) & np.uint32(mask)) << np.uint32(sh)
+    codes_r = _lane_dwords_to_bytes(words.reshape(NP, KT, 4, 64, TILE_DWORDS[bits]), bits)
+
+    KT8 = (KT + 7) // 8
+    V8 = KT8 * 8 * U
+    ug = unit_groups(K, G)
+    su = np.zeros((V8, Np), dtype=np.float16)
+    su[:KT * U, :N] = s[ug]
+    scales_r = su.reshape(KT8, 8 * U, NP, 4, 16).transpose(2, 0, 3, 4, 1).copy().reshape(-1)
+    zeros_r = None
+    if z is not None:
+        zu = np.zeros((V8, Np), dtype=np.uint32)
+        zu[:KT * U, :N] = z[ug]
+        per, width = (4, 8) if bits == 8 else (8, 4)                  # fields per dword, bits
+        nw = 8 * U // per
+        zz = zu.reshape(KT8, nw, per, NP, 4, 16).transpose(3, 0, 4, 5, 1, 2)   # p g c i w f
+        zr = np.zeros((NP, KT8, 4, 16, nw), dtype=np.uint32)
+        for f in range(per):
+            zr |= zz[..., f] << np.uint32(width * f)
+        zeros_r = zr.reshape(-1)
+    return codes_r, scales_r, zeros_r, perm
+
+
+def unrepack_ref_bits(codes_r, scales_r, zeros_r, K, N, bits, group_size=GROUP):
+    """Inverse of repack_ref_bits: (codes [N, K] permuted order, scales [K/G, N],
+    zeros [K/G, N] or None)."""
+    G = int(group_size)
+    KT, U, NP = K // TILE, units_per_tile(G), (N + 63) // 64
+    words = _bytes_to_lane_dwords(codes_r, bits, NP, KT).reshape(NP, KT, 4, 4, 16, -1)
+    v = np.zeros((NP, 4, 16, KT, 4, 4, 8), dtype=np.uint8)            # p c i t j b e
+    for j in range(4):
+        for e in range(8):
+            code = np.zeros((NP, KT, 4, 4, 16), dtype=np.uint32)
+            for d, sh, (mask, rs) in _code_parts(bits, j, e):
+                code |= ((words[..., d] >> np.uint32(sh)) & np.uint32(mask)) << np.uint32(rs)
+            v[:, :, :, :, j, :, e] = code.transpose(0, 2, 4, 1, 3)
+    q = v.reshape(NP * 64, K)[:N]
+    KT8 = (KT + 7) // 8
+    ug = unit_groups(K, G)
+
+    def from_units(units):
+        out = units[np.searchsorted(ug, np.arange(K // G))]
+        if not np.array_equal(units, out[ug]):
+            raise ValueError("meta units of one group disagree")
+        return out
+
+    su = np.asarray(scales_r, dtype=np.float16).reshape(NP, KT8, 4, 16, 8 * U)
+    s = from_units(su.transpose(1, 4, 0, 2, 3).reshape(KT8 * 8 * U, NP * 64)[:KT * U, :N])
+    z = None
+    if zeros_r is not None:
+        per, width = (4, 8) if bits == 8 else (8, 4)
+        nw = 8 * U // per
+        zr = np.asarray(zeros_r, dtype=np.uint32).reshape(NP, KT8, 4, 16, nw)
+        zf = np.zeros((NP, KT8, 4, 16, nw, per), dtype=np.uint8)
+        for f in range(per):
+            zf[..., f] = (zr >> np.uint32(width * f)) & np.uint32((1 << width) - 1)
+        zu = zf.transpose(1, 4, 5, 0, 2, 3).reshape(KT8 * 8 * U, NP * 64)[:KT * U, :N]
+        z = from_units(zu)
+    return q.copy(), s.copy(), z
