@@ -57,9 +57,12 @@ def w4a16_set_timing_events(start_event, stop_event):
                "w4a16_set_timing_events")
 
 
-def w4a16_repacked_bytes(K, N, group_size=GROUP):
+def w4a16_repacked_bytes(K, N, group_size=GROUP, bits=4):
     L = _lib.lib()
-    out = [L.w4a16_repacked_bytes(K, N, group_size, w) for w in (0, 1, 2)]
+    if bits == 4:
+        out = [L.w4a16_repacked_bytes(K, N, group_size, w) for w in (0, 1, 2)]
+    else:
+        out = [L.w4a16_repacked_bytes_bits(K, N, group_size, bits, w) for w in (0, 1, 2)]
     if min(out) < 0:
         raise W4A16Error("w4a16_repacked_bytes: invalid shape K=%d N=%d G=%d" % (K, N, group_size))
     return tuple(out)
@@ -94,38 +97,47 @@ def _group(K, group_size):
     return K if group_size == -1 else group_size
 
 
-def w4a16_quantize_rtn(W, group_size=GROUP, g_idx=None, perm=None, sym=False, stream=None):
-    """RTN group quantization of W [N, K] fp32 -> (qweight, scales, qzeros).
+def w4a16_quantize_rtn(W, group_size=GROUP, g_idx=None, perm=None, sym=False, bits=4,
+                       stream=None):
+    """RTN group quantization of W [N, K] fp32 -> (qweight, scales, qzeros), with
+    ``bits``-bit codes (3, 4 or 8) in the canonical packing.
 
-    ``sym=True``: symmetric codes (zero point fixed, stored offset by 8) and
-    qzeros = None."""
+    ``sym=True``: symmetric codes (zero point fixed, stored offset by
+    2^(bits-1)) and qzeros = None."""
     _need(W, torch.float32, "W")
     N, K = W.shape
     G = _group(K, group_size)
     if g_idx is not None and perm is None:
         perm, _ = w4a16_make_perm(g_idx, group_size, stream)
     dev = W.device
-    qweight = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    qweight = torch.empty((K * bits // 32, N), dtype=torch.int32, device=dev)
     scales = torch.empty((K // G, N), dtype=torch.float16, device=dev)
-    qzeros = None if sym else torch.empty((K // G, N // 8), dtype=torch.int32, device=dev)
-    _lib.check(_lib.lib().w4a16_quantize_rtn(_ptr(W), _ptr(g_idx), _ptr(perm), N, K, group_size,
-                                             _ptr(qweight), _ptr(scales), _ptr(qzeros),
-                                             _stream(stream)), "w4a16_quantize_rtn")
+    qzeros = (None if sym else
+              torch.empty((K // G, N * bits // 32), dtype=torch.int32, device=dev))
+    L = _lib.lib()
+    args = (_ptr(qweight), _ptr(scales), _ptr(qzeros), _stream(stream))
+    if bits == 4:
+        _lib.check(L.w4a16_quantize_rtn(_ptr(W), _ptr(g_idx), _ptr(perm), N, K, group_size,
+                                        *args), "w4a16_quantize_rtn")
+    else:
+        _lib.check(L.w4a16_quantize_rtn_bits(_ptr(W), _ptr(g_idx), _ptr(perm), N, K, group_size,
+                                             bits, *args), "w4a16_quantize_rtn_bits")
     return qweight, scales, qzeros
 
 
-def w4a16_repack(qweight, scales, qzeros, g_idx=None, group_size=GROUP, stream=None):
-    """Repack canonical tensors; returns dict(codes, scales, zeros, perm, K, N, group_size).
+def w4a16_repack(qweight, scales, qzeros, g_idx=None, group_size=GROUP, bits=4, stream=None):
+    """Repack canonical tensors of ``bits``-bit codes; returns dict(codes, scales,
+    zeros, perm, K, N, group_size, bits).
 
     ``qzeros=None`` is a symmetric weight: the result then has zeros = None."""
     _need(qweight, torch.int32, "qweight")
-    K8, N = qweight.shape
-    K = K8 * 8
+    Kw, N = qweight.shape
+    K = Kw * 32 // bits
     G = _group(K, group_size)
     _need(scales, torch.float16, "scales", (K // G) * N)
     if qzeros is not None:
-        _need(qzeros, torch.int32, "qzeros", (K // G) * (N // 8))
-    nc, ns, nz = w4a16_repacked_bytes(K, N, group_size)
+        _need(qzeros, torch.int32, "qzeros", (K // G) * (N * bits // 32))
+    nc, ns, nz = w4a16_repacked_bytes(K, N, group_size, bits)
     dev = qweight.device
     codes_r = torch.empty(nc, dtype=torch.uint8, device=dev)
     scales_r = torch.empty(ns // 2, dtype=torch.float16, device=dev)
@@ -135,12 +147,17 @@ def w4a16_repack(qweight, scales, qzeros, g_idx=None, group_size=GROUP, stream=N
         _need(g_idx, torch.int32, "g_idx", K)
         perm = torch.empty(K, dtype=torch.int32, device=dev)
     used = ctypes.c_int32(0)
-    _lib.check(_lib.lib().w4a16_repack(_ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(g_idx), K, N,
-                                       group_size, _ptr(codes_r), _ptr(scales_r), _ptr(zeros_r),
-                                       _ptr(perm), ctypes.byref(used), _stream(stream)),
-               "w4a16_repack")
+    L = _lib.lib()
+    head = (_ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(g_idx), K, N, group_size)
+    tail = (_ptr(codes_r), _ptr(scales_r), _ptr(zeros_r), _ptr(perm), ctypes.byref(used),
+            _stream(stream))
+    if bits == 4:
+        _lib.check(L.w4a16_repack(*head, *tail), "w4a16_repack")
+    else:
+        _lib.check(L.w4a16_repack_bits(*head, bits, *tail), "w4a16_repack_bits")
     return {"codes": codes_r, "scales": scales_r, "zeros": zeros_r,
-            "perm": perm if used.value else None, "K": K, "N": N, "group_size": group_size}
+            "perm": perm if used.value else None, "K": K, "N": N, "group_size": group_size,
+            "bits": bits}
 
 
 def w4a16_gemm(x, packed, out=None, workspace=None, use_workspace=True, stream=None):
@@ -177,13 +194,17 @@ def _int4_gemm(x, x_scale, packed, out, workspace, use_workspace, stream):
     else:
         workspace = None
     L = _lib.lib()
-    weights = (_ptr(packed["codes"]), _ptr(packed["scales"]), _ptr(packed["zeros"]),
-               _ptr(packed["perm"]), G, _ptr(out), M, N, K, _DT[x.dtype], _ptr(workspace),
-               ws_bytes, _stream(stream))
-    if x_scale is None:
-        _lib.check(L.w4a16_gemm(_ptr(x), *weights), "w4a16_gemm")
+    bits = packed.get("bits", 4)
+    wts = (_ptr(packed["codes"]), _ptr(packed["scales"]), _ptr(packed["zeros"]),
+           _ptr(packed["perm"]), G)
+    rest = (_ptr(out), M, N, K, _DT[x.dtype], _ptr(workspace), ws_bytes, _stream(stream))
+    if bits != 4:
+        _lib.check(L.w4a16_gemm_bits(_ptr(x), _ptr(x_scale), *wts, bits, *rest),
+                   "w4a16_gemm_bits")
+    elif x_scale is None:
+        _lib.check(L.w4a16_gemm(_ptr(x), *wts, *rest), "w4a16_gemm")
     else:
-        _lib.check(L.w4a16_gemm_xscale(_ptr(x), _ptr(x_scale), *weights), "w4a16_gemm_xscale")
+        _lib.check(L.w4a16_gemm_xscale(_ptr(x), _ptr(x_scale), *wts, *rest), "w4a16_gemm_xscale")
     return out
 
 
@@ -191,9 +212,15 @@ def w4a16_dequant(packed, dtype=torch.float16, stream=None):
     """Dequantized weights [N, K] (permuted column order) via the device routine."""
     K, N = packed["K"], packed["N"]
     w = torch.empty((N, K), dtype=dtype, device=packed["codes"].device)
-    _lib.check(_lib.lib().w4a16_dequant(_ptr(packed["codes"]), _ptr(packed["scales"]),
-                                        _ptr(packed["zeros"]), K, N, packed["group_size"],
-                                        _DT[dtype], _ptr(w), _stream(stream)), "w4a16_dequant")
+    bits = packed.get("bits", 4)
+    arrays = (_ptr(packed["codes"]), _ptr(packed["scales"]), _ptr(packed["zeros"]), K, N,
+              packed["group_size"])
+    if bits == 4:
+        _lib.check(_lib.lib().w4a16_dequant(*arrays, _DT[dtype], _ptr(w), _stream(stream)),
+                   "w4a16_dequant")
+    else:
+        _lib.check(_lib.lib().w4a16_dequant_bits(*arrays, bits, _DT[dtype], _ptr(w),
+                                                 _stream(stream)), "w4a16_dequant_bits")
     return w
 
 

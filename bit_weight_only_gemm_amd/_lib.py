@@ -27,6 +27,13 @@ SIGNATURES = {
     "w4a16_gemm_xscale": (_c.c_int, [_p, _p, _p, _p, _p, _p, _i32, _p, _i64, _i64, _i64, _i32, _p,
                                      _i64, _p]),
     "w4a16_dequant": (_c.c_int, [_p, _p, _p, _i64, _i64, _i32, _i32, _p, _p]),
+    "w4a16_repacked_bytes_bits": (_i64, [_i64, _i64, _i32, _i32, _i32]),
+    "w4a16_quantize_rtn_bits": (_c.c_int, [_p, _p, _p, _i64, _i64, _i32, _i32, _p, _p, _p, _p]),
+    "w4a16_repack_bits": (_c.c_int, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p,
+                                     _p]),
+    "w4a16_gemm_bits": (_c.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _i64, _i64, _i64, _i32,
+                                   _p, _i64, _p]),
+    "w4a16_dequant_bits": (_c.c_int, [_p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p, _p]),
     "nf4_codebook": (_c.c_int, [_p]),
     "nf4_quantize": (_c.c_int, [_p, _i64, _i64, _i32, _p, _p, _p, _p]),
     "nf4_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "prefill.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_b3.hip", "gemm_b8.hip", "prefill.hip",
+           "prefill_b3.hip", "prefill_b8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -32,7 +33,8 @@ FLAGS = [
 # ordinary VGPRs (MFMA with VGPR destination): with accumulation registers the
 # compiler copies them back to VGPRs after every tile.  The prefill kernel's
 # 256 accumulators need the accumulation registers and keeps the default.
-EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+_DECODE = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"gemm.hip": _DECODE, "gemm_b3.hip": _DECODE, "gemm_b8.hip": _DECODE}
 
 
 def _compile(src):

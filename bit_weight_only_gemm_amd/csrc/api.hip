@@ -93,6 +93,15 @@ int validate_int4_shape(int64_t K, int64_t N, int32_t group_size) {
   return W4A16_OK;
 }
 
+// Code widths: 3, 4 or 8 bits.  3-bit zeros pack in runs of 32 columns, so a
+// call that reads or writes canonical 3-bit zeros needs N % 32 == 0.
+int validate_bits(int32_t bits) {
+  return (bits == 3 || bits == 4 || bits == 8) ? W4A16_OK : W4A16_ERR_UNSUPPORTED;
+}
+int validate_zero_rows(int64_t N, int32_t bits, bool zeros) {
+  return (zeros && bits == 3 && N % 32 != 0) ? W4A16_ERR_INVALID_ARG : W4A16_OK;
+}
+
 int validate_dtype(int32_t dtype) {
   return (dtype == W4A16_F16 || dtype == W4A16_BF16) ? W4A16_OK : W4A16_ERR_INVALID_ARG;
 }
@@ -116,16 +125,22 @@ const char* w4a16_status_string(int status) {
 
 int w4a16_version(void) { return 1; }
 
-int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which) {
-  if (validate_int4_shape(K, N, group_size) != W4A16_OK) return -1;
+int64_t w4a16_repacked_bytes_bits(int64_t K, int64_t N, int32_t group_size, int32_t bits,
+                                  int32_t which) {
+  if (validate_int4_shape(K, N, group_size) != W4A16_OK || validate_bits(bits) != W4A16_OK)
+    return -1;
   const int64_t U = units_per_tile((int)resolve_group(K, group_size));
   const int64_t NP = ceil_div(N, 64), KT = K / 128, KT8 = ceil_div(KT, 8);
   switch (which) {
-    case W4A16_CODES: return NP * KT * 4096;
+    case W4A16_CODES: return NP * KT * 4 * 256 * bits;
     case W4A16_SCALES: return NP * KT8 * 1024 * U;
-    case W4A16_ZEROS: return NP * KT8 * 256 * U;
+    case W4A16_ZEROS: return NP * KT8 * 256 * U * (zero_field_bits(bits) / 4);
     default: return -1;
   }
+}
+
+int64_t w4a16_repacked_bytes(int64_t K, int64_t N, int32_t group_size, int32_t which) {
+  return w4a16_repacked_bytes_bits(K, N, group_size, 4, which);
 }
 
 int w4a16_make_perm(const int32_t* g_idx, int64_t K, int32_t group_size, int32_t* perm,
@@ -161,24 +176,35 @@ int w4a16_make_perm(const int32_t* g_idx, int64_t K, int32_t group_size, int32_t
   return W4A16_OK;
 }
 
-int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm, int64_t N,
-                       int64_t K, int32_t group_size, int32_t* qweight, uint16_t* scales,
-                       int32_t* qzeros, void* stream) {
+int w4a16_quantize_rtn_bits(const float* W, const int32_t* g_idx, const int32_t* perm,
+                            int64_t N, int64_t K, int32_t group_size, int32_t bits,
+                            int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream) {
   if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if (int s = validate_bits(bits)) return s;
+  if (int s = validate_zero_rows(N, bits, qzeros != nullptr)) return s;
   if ((g_idx == nullptr) != (perm == nullptr)) return W4A16_ERR_INVALID_ARG;
   if (int s = check_ptrs({W, qweight, scales})) return s;
   if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
   if (qzeros && !aligned16(qzeros)) return W4A16_ERR_MISALIGNED;
   clear_pending_error();
-  return hip_status(launch_rtn_int4(W, perm, N, K, (int)resolve_group(K, group_size), qweight,
-                                    scales, qzeros, (hipStream_t)stream));
+  return hip_status(launch_rtn_int(W, perm, N, K, (int)resolve_group(K, group_size), bits,
+                                   qweight, scales, qzeros, (hipStream_t)stream));
 }
 
-int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
-                 const int32_t* g_idx, int64_t K, int64_t N, int32_t group_size, void* codes_r,
-                 void* scales_r, void* zeros_r, int32_t* perm, int32_t* perm_used_host,
-                 void* stream) {
+int w4a16_quantize_rtn(const float* W, const int32_t* g_idx, const int32_t* perm, int64_t N,
+                       int64_t K, int32_t group_size, int32_t* qweight, uint16_t* scales,
+                       int32_t* qzeros, void* stream) {
+  return w4a16_quantize_rtn_bits(W, g_idx, perm, N, K, group_size, 4, qweight, scales, qzeros,
+                                 stream);
+}
+
+int w4a16_repack_bits(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                      const int32_t* g_idx, int64_t K, int64_t N, int32_t group_size,
+                      int32_t bits, void* codes_r, void* scales_r, void* zeros_r, int32_t* perm,
+                      int32_t* perm_used_host, void* stream) {
   if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if (int s = validate_bits(bits)) return s;
+  if (int s = validate_zero_rows(N, bits, qzeros != nullptr)) return s;
   if (!perm_used_host) return W4A16_ERR_INVALID_ARG;
   // a symmetric weight has neither zeros nor repacked zeros
   if ((qzeros == nullptr) != (zeros_r == nullptr)) return W4A16_ERR_INVALID_ARG;
@@ -191,11 +217,19 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
   }
   clear_pending_error();
   if (int s = hip_status(launch_repack(qweight, scales, qzeros, used ? perm : nullptr, K, N,
-                                       (int)resolve_group(K, group_size), codes_r, scales_r,
-                                       zeros_r, (hipStream_t)stream)))
+                                       (int)resolve_group(K, group_size), bits, codes_r,
+                                       scales_r, zeros_r, (hipStream_t)stream)))
     return s;
   *perm_used_host = used;
   return W4A16_OK;
+}
+
+int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                 const int32_t* g_idx, int64_t K, int64_t N, int32_t group_size, void* codes_r,
+                 void* scales_r, void* zeros_r, int32_t* perm, int32_t* perm_used_host,
+                 void* stream) {
+  return w4a16_repack_bits(qweight, scales, qzeros, g_idx, K, N, group_size, 4, codes_r,
+                           scales_r, zeros_r, perm, perm_used_host, stream);
 }
 
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size) {
@@ -208,12 +242,14 @@ int w4a16_set_timing_events(void* start_event, void* stop_event) {
   return W4A16_OK;
 }
 
-int w4a16_gemm_xscale(const void* x, const void* x_scale, const void* codes_r,
-                      const void* scales_r, const void* zeros_r, const int32_t* perm,
-                      int32_t group_size, void* out, int64_t M, int64_t N, int64_t K,
-                      int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+int w4a16_gemm_bits(const void* x, const void* x_scale, const void* codes_r,
+                    const void* scales_r, const void* zeros_r, const int32_t* perm,
+                    int32_t group_size, int32_t bits, void* out, int64_t M, int64_t N,
+                    int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                    void* stream) {
   if (M <= 0 || M > kMaxM) return M <= 0 ? W4A16_ERR_INVALID_ARG : W4A16_ERR_UNSUPPORTED;
   if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if (int s = validate_bits(bits)) return s;
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({x, codes_r, scales_r, out})) return s;
   if (zeros_r && !aligned16(zeros_r)) return W4A16_ERR_MISALIGNED;
@@ -224,29 +260,45 @@ int w4a16_gemm_xscale(const void* x, const void* x_scale, const void* codes_r,
   if (need > 0 && (!workspace || workspace_bytes < need))
     return W4A16_ERR_WORKSPACE;
   clear_pending_error();
-  return hip_status(launch_int4_gemm(x, x_scale, codes_r, scales_r, zeros_r, perm, out, M, N, K,
-                                     (int)resolve_group(K, group_size), dtype, workspace,
-                                     workspace_bytes, (hipStream_t)stream));
+  return hip_status(launch_int_gemm(x, x_scale, codes_r, scales_r, zeros_r, perm, out, M, N, K,
+                                    (int)resolve_group(K, group_size), bits, dtype, workspace,
+                                    workspace_bytes, (hipStream_t)stream));
+}
+
+int w4a16_gemm_xscale(const void* x, const void* x_scale, const void* codes_r,
+                      const void* scales_r, const void* zeros_r, const int32_t* perm,
+                      int32_t group_size, void* out, int64_t M, int64_t N, int64_t K,
+                      int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  return w4a16_gemm_bits(x, x_scale, codes_r, scales_r, zeros_r, perm, group_size, 4, out, M, N,
+                         K, dtype, workspace, workspace_bytes, stream);
 }
 
 int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
                const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
                int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
                void* stream) {
-  return w4a16_gemm_xscale(x, nullptr, codes_r, scales_r, zeros_r, perm, group_size, out, M, N,
-                           K, dtype, workspace, workspace_bytes, stream);
+  return w4a16_gemm_bits(x, nullptr, codes_r, scales_r, zeros_r, perm, group_size, 4, out, M, N,
+                         K, dtype, workspace, workspace_bytes, stream);
 }
 
-int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
-                  int64_t N, int32_t group_size, int32_t dtype, void* w_out, void* stream) {
+int w4a16_dequant_bits(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
+                       int64_t N, int32_t group_size, int32_t bits, int32_t dtype, void* w_out,
+                       void* stream) {
   if (int s = validate_int4_shape(K, N, group_size)) return s;
+  if (int s = validate_bits(bits)) return s;
   if (int s = validate_dtype(dtype)) return s;
   if (int s = check_ptrs({codes_r, scales_r, w_out})) return s;
   if (zeros_r && !aligned16(zeros_r)) return W4A16_ERR_MISALIGNED;
   clear_pending_error();
-  return hip_status(launch_dequant_int4(codes_r, scales_r, zeros_r, K, N,
-                                        (int)resolve_group(K, group_size), dtype, w_out,
-                                        (hipStream_t)stream));
+  return hip_status(launch_dequant_int(codes_r, scales_r, zeros_r, K, N,
+                                       (int)resolve_group(K, group_size), bits, dtype, w_out,
+                                       (hipStream_t)stream));
+}
+
+int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
+                  int64_t N, int32_t group_size, int32_t dtype, void* w_out, void* stream) {
+  return w4a16_dequant_bits(codes_r, scales_r, zeros_r, K, N, group_size, 4, dtype, w_out,
+                            stream);
 }
 
 int nf4_codebook(float* out16_host) {

@@ -99,32 +99,95 @@ template <> struct QParam<DT_BF16> {
   }
 };
 
-// Exact dequantization of element pair i (elements 2i, 2i + 1, nibble slots
-// i and i + 4) of one repacked word, returned as two packed 16-bit values.
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QParam<DT_F16>& p) {
-  const uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;  // (1024+q_2i, 1024+q_2i+1)
+// Exact dequantization of a pair of codes held in the low bits of the two
+// 16-bit halves of f (codes < 1024): 0x6400 | q is the fp16 value 1024 + q,
+// so (1024 + q) - (1024 + z) = q - z exactly, then one rounding of (q - z) s.
+// Returned as two packed 16-bit values.
+__device__ __forceinline__ uint32_t dequant_fields(uint32_t f, const QParam<DT_F16>& p) {
+  const uint32_t t = f | p.magic;                                     // (1024+q_lo, 1024+q_hi)
   const half2_t r = (__builtin_bit_cast(half2_t, t) - p.hz) * p.s2;  // exact sub, one rounding
   return __builtin_bit_cast(uint32_t, r);
 }
 
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QParam<DT_BF16>& p) {
+__device__ __forceinline__ uint32_t dequant_fields(uint32_t f, const QParam<DT_BF16>& p) {
   // (q - z) exactly in fp16 as on the fp16 path, then the exact fp32 product
   // with s as fma(q - z, s, -0) (v_fma_mix widens the fp16 half in place;
   // adding -0 keeps every signed zero of the plain product) and the one
   // rounding to bf16.
-  const uint32_t t = ((w >> (4 * i)) & 0x000F000Fu) | p.magic;
+  const uint32_t t = f | p.magic;
   const half2_t d = __builtin_bit_cast(half2_t, t) - p.hz;
   const bf16x2_t r = {(__bf16)__builtin_fmaf((float)d[0], p.sf, p.nz),
                       (__bf16)__builtin_fmaf((float)d[1], p.sf, p.nz)};
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Exact dequantization of one repacked word into an 8-element MFMA operand.
+// Element pair i (elements 2i, 2i + 1, nibble slots i and i + 4) of one
+// repacked 4-bit word.
+template <class QP>
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QP& p) {
+  return dequant_fields((w >> (4 * i)) & 0x000F000Fu, p);
+}
+
+// Exact dequantization of one repacked 4-bit word into an 8-element MFMA operand.
 template <int DT>
 __device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const QParam<DT>& p) {
   u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = dequant_pair(w, i, p);
+  return __builtin_bit_cast(typename Op<DT>::vec, r);
+}
+
+// ---- b-bit integer codes.  One lane's codes of one K tile (32 codes: the 8
+// inputs of each of the 4 MFMA steps j) in the repacked form of each width:
+//  * 4 bits: 4 dwords, dword j = step j, nibble slot (e >> 1) + 4 (e & 1).
+//  * 8 bits: 8 dwords (two 16-byte halves, half j >> 1); step j is dwords
+//    2 (j & 1) and 2 (j & 1) + 1 of its half, each holding elements
+//    [e0, e2, e1, e3] of its 4 so that (d >> 8 r) & 0x00FF00FF is a pair.
+//  * 3 bits: 3 dwords; the low 2 bits of code (j, e) at bit 16 (e & 1) +
+//    2 (4 (j & 1) + (e >> 1)) of dword j >> 1, its high bit at bit
+//    16 (e & 1) + 4 j + (e >> 1) of dword 2.
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+template <int BITS> struct Codes;
+template <> struct Codes<4> { u32x4_t w; };
+template <> struct Codes<3> { u32x3_t w; };
+template <> struct Codes<8> { u32x4_t lo, hi; };
+
+// Width of a repacked zero field, and the XOR that turns the zero fields a
+// symmetric weight reads as 0 into its implicit zero 2^(b-1).
+__host__ __device__ constexpr int zero_field_bits(int bits) { return bits == 8 ? 8 : 4; }
+__host__ __device__ constexpr uint32_t sym_zero_xor(int bits) {
+  return bits == 8 ? 0x80808080u : bits == 4 ? 0x88888888u : 0x44444444u;
+}
+
+// The 8-element B operand of MFMA step j (0..3) from a lane's codes.
+template <int DT>
+__device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<4>& c, int j,
+                                                             const QParam<DT>& p) {
+  return dequant_word<DT>(c.w[j], p);
+}
+template <int DT>
+__device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<8>& c, int j,
+                                                             const QParam<DT>& p) {
+  const u32x4_t h = (j >> 1) ? c.hi : c.lo;
+  const uint32_t a = h[2 * (j & 1)], b = h[2 * (j & 1) + 1];
+  u32x4_t r;
+  r[0] = dequant_fields(a & 0x00FF00FFu, p);
+  r[1] = dequant_fields((a >> 8) & 0x00FF00FFu, p);
+  r[2] = dequant_fields(b & 0x00FF00FFu, p);
+  r[3] = dequant_fields((b >> 8) & 0x00FF00FFu, p);
+  return __builtin_bit_cast(typename Op<DT>::vec, r);
+}
+template <int DT>
+__device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<3>& c, int j,
+                                                             const QParam<DT>& p) {
+  const uint32_t lo = c.w[j >> 1], hi = c.w[2];
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t f = ((lo >> (8 * (j & 1) + 2 * i)) & 0x00030003u) |
+                       (((hi >> (4 * j + i)) & 0x00010001u) << 2);
+    r[i] = dequant_fields(f, p);
+  }
   return __builtin_bit_cast(typename Op<DT>::vec, r);
 }
 
@@ -168,6 +231,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ u32x4_t bld128(rsrc_t r, uint32_t voff, int soff) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x3_t bld96(rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0));
 }
 __device__ __forceinline__ u32x2_t bld64(rsrc_t r, uint32_t voff, int soff) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));

@@ -1,0 +1,644 @@
+// decode.h -- the skinny-M (decode) fused dequantize-and-multiply kernel
+// templates, shared by the translation units that instantiate them (one per
+// weight code width, compiled in parallel).  See gemm.hip for the design.
+#pragma once
+#include <hip/hip_ext.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "launch.h"
+
+namespace w4a16 {
+
+#ifndef W4A16_DECODE_WAVES
+#define W4A16_DECODE_WAVES 4
+#endif
+constexpr int DW = W4A16_DECODE_WAVES;  // waves per decode workgroup
+constexpr int RUN = 8;                  // K tiles per meta run and ring pass
+
+// Activation modes.  PACKED: M <= 4, one 16-byte load per lane and K tile
+// carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
+// tile.  XGATHER: PACKED for an act-order weight, with the M rows of x and
+// the permutation staged in LDS once per workgroup; the operand is gathered
+// from LDS, x[m][perm[k]], so no separate permutation pass runs.  XSTAGED:
+// PACKED with the M rows of x staged in LDS and read from there (used with
+// AWQ input scales, below).  With input scales (XS) the staged rows are
+// divided by s in place, once per workgroup, before the loop: each x element
+// is scaled once per workgroup instead of once per use.
+enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3 };
+constexpr bool is_packed(int am) { return am != AM_FULL; }
+constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; }
+
+// Largest LDS footprint of the staged activations (+ permutation, + input
+// scales) per workgroup: past it the staging costs more than the separate
+// preparation pass it saves (measured on MI355X), and it leaves room for
+// several workgroups per CU.
+constexpr int64_t kMaxXlds = 32 * 1024;
+
+// Multiply-accumulate the 4 MFMA steps of one K tile given its 4 B operands.
+template <int DT, int AM, int MT, int NA, int NACC>
+__device__ __forceinline__ void mma_tile(const typename Op<DT>::vec b[4],
+                                         const typename Op<DT>::vec (&a)[NA],
+                                         float4_t (&acc)[NACC]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (is_packed(AM)) {
+      acc[j] = mfma16x16x32<DT>(a[0], b[j], acc[j]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        // NACC / MT accumulators per row tile take the steps in turn, so that
+        // consecutive MFMAs do not wait on each other's results
+        constexpr int PER = NACC / MT;
+        acc[m * PER + j % PER] = mfma16x16x32<DT>(a[m * 4 + j], b[j], acc[m * PER + j % PER]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------ b-bit integer policy --
+// Column tile ct = 4p + c of panel p.  Word j of lane l covers K = 128t + 32j +
+// 8(l >> 4) + e, so lane-group b feeds x[row][128t + 32j + 8b ...] in step j.
+// BITS-bit codes (3, 4 or 8; the Codes<BITS> forms of common.h): a column
+// tile's K tile is 256 BITS bytes, lane l's codes at 12 l (3 bits), 16 l
+// (4 bits) or 16 l and 1024 + 16 l (8 bits).  U meta units per K tile (group
+// size 128 / U, or >= 128 for U = 1); word j of tile slot s uses unit
+// r = sU + jU/4 of the run.  Zero fields are 4 bits wide (8 for 8-bit codes).
+// A symmetric weight has no zeros (empty descriptor range, loads read 0) and
+// zx turns each field into the implicit zero 2^(BITS-1).
+template <int DT, int U, int BITS>
+struct IntW {
+  static constexpr bool kRaggedK = false;  // K % 128 == 0 for this format
+  static constexpr int kTile = 256 * BITS;                 // bytes per column tile, K tile
+  static constexpr int kZW = zero_field_bits(BITS);        // zero field width
+  static constexpr int kZWords = U * kZW / 4;              // zero dwords per column and run
+  typedef Codes<BITS> CodeT;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const uint8_t* zeros;
+  int KT;
+  uint32_t zx;  // sym_zero_xor(BITS) for a symmetric weight, else 0
+  rsrc_t rc, rs, rz;
+  uint32_t voc, vos, voz;
+  int c;
+  struct Meta {
+    u32x4_t s[U];          // 8U fp16 scales of this lane's column, unit r at half r
+    uint32_t z[kZWords];   // 8U zero fields, unit r at field r of the array
+  };
+  __device__ __forceinline__ void init(int ct, int lane, int /*N*/, int /*K*/) {
+    const int p = ct >> 2;
+    c = ct & 3;
+    const int i = lane & 15;
+    const int KT8 = (KT + RUN - 1) / RUN;
+    // one descriptor per array, based at this panel: offsets stay 32-bit
+    rc = make_rsrc(codes + (size_t)p * KT * 4 * kTile, (uint32_t)KT * 4u * kTile);
+    rs = make_rsrc(scales + (size_t)p * KT8 * 1024 * U, (uint32_t)KT8 * 1024u * U);
+    rz = make_rsrc(zeros + (size_t)p * KT8 * 256 * kZWords,
+                   zx ? 0u : (uint32_t)KT8 * 256u * kZWords);
+    voc = (uint32_t)(c * kTile + lane * (BITS == 3 ? 12 : 16));
+    vos = (uint32_t)((c * 16 + i) * 16 * U);
+    voz = (uint32_t)((c * 16 + i) * 4 * kZWords);
+  }
+  __device__ static __forceinline__ Meta zero_meta() {
+    Meta m;
+#pragma unroll
+    for (int k = 0; k < U; ++k) m.s[k] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kZWords; ++k) m.z[k] = 0u;
+    return m;
+  }
+  __device__ __forceinline__ Meta load_meta(int run) const {
+    Meta m;
+#pragma unroll
+    for (int k = 0; k < U; ++k) m.s[k] = bld128(rs, vos + 16u * k, run * 1024 * U);
+    const int zs = run * 256 * kZWords;
+    if constexpr (kZWords == 1) {
+      m.z[0] = bld32(rz, voz, zs);
+    } else if constexpr (kZWords == 2) {
+      const u32x2_t z = bld64(rz, voz, zs);
+      m.z[0] = z[0];
+      m.z[1] = z[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < kZWords / 4; ++h) {
+        const u32x4_t z = bld128(rz, voz + 16u * h, zs);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m.z[4 * h + k] = z[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kZWords; ++k) m.z[k] ^= zx;
+    return m;
+  }
+  __device__ __forceinline__ CodeT load_codes(int t, int /*lane*/) const {
+    CodeT w;
+    if constexpr (BITS == 4) {
+      w.w = bld128(rc, voc, t * 4 * kTile);
+    } else if constexpr (BITS == 3) {
+      w.w = bld96(rc, voc, t * 4 * kTile);
+    } else {
+      w.lo = bld128(rc, voc, t * 4 * kTile);
+      w.hi = bld128(rc, voc + 1024u, t * 4 * kTile);
+    }
+    return w;
+  }
+  __device__ static __forceinline__ void unit_param(const Meta& m, int r, QParam<DT>& qp) {
+    constexpr int per = 32 / kZW;  // fields per dword
+    qp.set((m.s[r >> 3][(r & 7) >> 1] >> (16 * (r & 1))) & 0xFFFFu,
+           (m.z[r / per] >> (kZW * (r % per))) & ((1u << kZW) - 1u));
+  }
+  // B operands of tile slot s (0..7 within the run) from the exact dequant.
+  __device__ __forceinline__ void operands(const CodeT& w, int s, const Meta& m,
+                                           typename Op<DT>::vec b[4]) const {
+    QParam<DT> qp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j * U % 4 == 0) unit_param(m, s * U + j * U / 4, qp);  // a new unit
+      b[j] = dequant_step<DT>(w, j, qp);
+    }
+  }
+  __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }
+};
+
+// ---------------------------------------------------------------- NF4 policy --
+// Raw layout: row n of qweight holds K/2 bytes, element 2j in the low nibble of
+// byte j.  Lane (column n = 16 ct + (l & 15), group b = l >> 4) loads 16 bytes =
+// elements 128t + 32b .. +31 of its row, all in one 64-element absmax block;
+// word j feeds MFMA step j.  Dequant is the definition: a' = fp32(absmax_q) *
+// absmax_scale, w = round16(fp32(L[c] * a')), L from a 16-entry LDS table.
+// BATCH (K % 1024 == 0): the 16 absmax bytes of a run of 8 tiles of a row are
+// one aligned 16-byte load and share one double-quant scale (a run of 16
+// blocks never straddles a group of 256); otherwise they are loaded per tile.
+template <int DT, bool BATCH>
+struct Nf4W {
+  static constexpr bool kRaggedK = true;  // K % 64 == 0 only: a last tile may be half
+  typedef u32x4_t CodeT;
+  const uint8_t* q;
+  const uint8_t* aq;
+  const float* asc;
+  const float* lut;
+  int N, K;
+  rsrc_t rq, raq, ras;
+  int kb;
+  uint32_t voq, vob, blk0;
+  struct Meta {
+    // BATCH: a16 = 16 absmax codes of the run, sc = its double-quant scale.
+    // otherwise: a[s] = dequantized absmax of tile slot s for this lane.
+    u32x4_t a16;
+    float sc;
+    float a[BATCH ? 1 : RUN];
+  };
+  __device__ __forceinline__ void init(int ct, int lane, int N_, int K_) {
+    N = N_;
+    K = K_;
+    const size_t n0 = (size_t)ct * 16;
+    const int nloc = lane & 15;
+    kb = lane >> 4;
+    rq = make_rsrc(q + n0 * (K >> 1), 16u * (uint32_t)(K >> 1));
+    raq = make_rsrc(aq + n0 * (K >> 6), 16u * (uint32_t)(K >> 6));
+    const size_t nblocks = (size_t)N * (K >> 6);
+    ras = make_rsrc(asc, (uint32_t)(((nblocks + 255) >> 8) * 4));
+    blk0 = (uint32_t)(n0 * (K >> 6));
+    voq = (uint32_t)(nloc * (K >> 1) + 16 * kb);
+    vob = (uint32_t)(nloc * (K >> 6));
+  }
+  __device__ static __forceinline__ Meta zero_meta() {
+    Meta m;
+    m.a16 = u32x4_t{0u, 0u, 0u, 0u};
+    m.sc = 0.0f;
+#pragma unroll
+    for (int s = 0; s < (BATCH ? 1 : RUN); ++s) m.a[s] = 0.0f;
+    return m;
+  }
+  __device__ __forceinline__ Meta load_meta(int run) const {
+    Meta m = zero_meta();
+    if constexpr (BATCH) {
+      m.a16 = bld128(raq, vob + (uint32_t)(16 * run), 0);
+      m.sc = __builtin_bit_cast(float, bld32(ras, ((blk0 + vob + 16u * run) >> 8) * 4u, 0));
+    } else {
+#pragma unroll
+      for (int s = 0; s < RUN; ++s) {
+        // block of (row, tile 8 run + s, lane group); reads past the row meet
+        // zero activations
+        const uint32_t bl = vob + (uint32_t)(2 * (RUN * run + s) + (kb >> 1));
+        const uint32_t qa = __builtin_amdgcn_raw_buffer_load_b8(raq, bl, 0, 0);
+        const float sa = __builtin_bit_cast(float, bld32(ras, ((blk0 + bl) >> 8) * 4u, 0));
+        m.a[s] = (float)qa * sa;
+      }
+    }
+    return m;
+  }
+  // t is a valid K tile.  In a half-filled last tile the lanes past K use an
+  // out-of-range per-lane offset and read zeros.
+  __device__ __forceinline__ u32x4_t load_codes(int t, int /*lane*/) const {
+    const uint32_t vq = (t * 128 + 32 * kb < K) ? voq : kOutOfRange;
+    return bld128(rq, vq, t * 64);
+  }
+  __device__ __forceinline__ void operands(const u32x4_t& w4, int s, const Meta& m,
+                                           typename Op<DT>::vec b[4]) const {
+    float a;
+    if constexpr (BATCH) {
+      // absmax code of block 2 s + (b >> 1) of the run: byte 2 (s & 1) + (b >> 1)
+      // of word s >> 1
+      const uint32_t qa = (m.a16[s >> 1] >> (16 * (s & 1) + 8 * (kb >> 1))) & 0xFFu;
+      a = (float)qa * m.sc;
+    } else {
+      a = m.a[s];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = w4[j];
+      typename Op<DT>::vec v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = lut[(w >> (4 * e)) & 0xFu] * a;
+        if constexpr (DT == DT_F16) v[e] = (_Float16)f;
+        else v[e] = (__bf16)f;
+      }
+      b[j] = v;
+    }
+  }
+  __device__ static __forceinline__ int xk(int j, int b) { return 32 * b + 8 * j; }
+};
+
+// Activations of one K tile.  PACKED: one vector, lane row r = 4 j + m holds
+// step j of batch row m.  FULL: MT x 4 vectors (row tile m, step j), lane row
+// r = batch row.  Rows >= M read 0 through the descriptor range; k >= K (only
+// in a half NF4 tile) uses an out-of-range offset.
+// Staged activations in LDS: x rows [M][K] at xl, the permutation int32[K] at
+// pl.
+struct XLds {
+  const uint8_t* xl;
+  const int32_t* pl;
+  int M;
+};
+
+template <int DT, int AM, int MT, int NA, class WP>
+__device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
+                                       typename Op<DT>::vec (&a)[NA], const XLds& xs) {
+  typedef typename Op<DT>::vec vec;
+  const int r = lane & 15, b = lane >> 4;
+  if constexpr (AM == AM_XGATHER) {
+    // rows m >= M only feed output rows that are never stored, so they read
+    // row M - 1 instead of zeros (K % 128 == 0: no half tiles)
+    const int j = r >> 2, m = min(r & 3, xs.M - 1);
+    const int kg = t * 128 + WP::xk(j, b);
+    {
+      const u32x4_t p0 = *(const u32x4_t*)(xs.pl + kg);
+      const u32x4_t p1 = *(const u32x4_t*)(xs.pl + kg + 4);
+      const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = *(const uint16_t*)(row + p0[e] * 2u);
+        v[4 + e] = *(const uint16_t*)(row + p1[e] * 2u);
+      }
+      const u32x4_t w = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                         v[6] | (v[7] << 16)};
+      a[0] = __builtin_bit_cast(vec, w);
+    }
+  } else if constexpr (AM == AM_XSTAGED) {
+    const int j = r >> 2, m = min(r & 3, xs.M - 1);
+    const uint32_t kg = (uint32_t)(t * 128 + WP::xk(j, b));
+    a[0] = *(const vec*)(xs.xl + ((uint32_t)m * (uint32_t)K + kg) * 2u);
+  } else if constexpr (AM == AM_PACKED) {
+    const int j = r >> 2, m = r & 3;
+    const int kin = WP::xk(j, b);
+    uint32_t off = (uint32_t)m * (uint32_t)K * 2u + (uint32_t)kin * 2u;
+    if constexpr (WP::kRaggedK) off = (t * 128 + kin < K) ? off : kOutOfRange;
+    a[0] = __builtin_bit_cast(typename Op<DT>::vec, bld128(rx, off, t * 256));
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint32_t rowoff = (uint32_t)(m * 16 + r) * (uint32_t)K * 2u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kin = WP::xk(j, b);
+        uint32_t off = rowoff + (uint32_t)kin * 2u;
+        if constexpr (WP::kRaggedK) off = (t * 128 + kin < K) ? off : kOutOfRange;
+        a[m * 4 + j] = __builtin_bit_cast(typename Op<DT>::vec, bld128(rx, off, t * 256));
+      }
+    }
+  }
+}
+
+// Bytes of LDS the staged activations and permutation take, each region
+// rounded up to whole 1 KB blocks.
+// Staged LDS layout: x rows [M][K], then (gather) the permutation int32[K],
+// then (input scales) s [K].
+__host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
+  return (uint32_t)((M * K * 2 + 1023) / 1024 * 1024);
+}
+__host__ __device__ constexpr uint32_t xlds_perm_bytes(int K, bool perm) {
+  return perm ? (uint32_t)((K * 4 + 1023) / 1024 * 1024) : 0u;
+}
+__host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool perm, bool xs) {
+  return xlds_x_bytes(M, K) + xlds_perm_bytes(K, perm) +
+         (xs ? (uint32_t)((K * 2 + 1023) / 1024 * 1024) : 0u);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
+// lds + 16 l (the LDS base is wave-uniform).
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Copy `bytes` (rounded up to 1 KB; the tail reads 0 through the descriptor
+// range) from `src` to LDS, 1 KB per wave instruction.
+__device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8_t* lds,
+                                          int wave, int lane) {
+  const rsrc_t r = make_rsrc(src, bytes);
+  const int nblk = (int)((bytes + 1023) / 1024);
+  for (int blk = wave; blk < nblk; blk += DW)
+    lds_dma16(r, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), 0);
+}
+
+// XS: divide the staged activations by the AWQ input scales xsc [K] (staged
+// modes only).
+template <int DT, int MT, int AM, bool XS, class WP>
+__device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
+                                            const uint16_t* __restrict__ xsc, WP& wp,
+                                            uint16_t* __restrict__ out, int M, int N, int K,
+                                            int KT, float* red, const int32_t* perm,
+                                            uint8_t* xlds) {
+  static_assert(!XS || is_staged(AM), "input scales are applied to staged rows");
+  static_assert(AM != AM_XSTAGED || XS, "rows are staged for input scales");
+  constexpr int NA = is_packed(AM) ? 1 : MT * 4;                   // A vectors per tile
+  constexpr int NACC = is_packed(AM) ? 4 : MT * (MT == 1 ? 4 : (MT == 2 ? 2 : 1));  // acc tiles
+  constexpr int PA = is_packed(AM) ? RUN : (MT == 1 ? 2 : 1);      // A ring depth
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ct = blockIdx.x;
+  const int row0 = blockIdx.y * 16 * MT;
+  wp.init(ct, lane, N, K);
+  const int nrun = (KT + RUN - 1) / RUN;
+  const int r0 = (nrun * wave) / DW, r1 = (nrun * (wave + 1)) / DW;
+  const int t0 = r0 * RUN;
+  const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
+  const int vrows = min(16 * MT, M - row0);
+  const rsrc_t rx = make_rsrc(x + (size_t)row0 * K, (uint32_t)vrows * (uint32_t)K * 2u);
+
+  float4_t acc[NACC];
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Ring of RUN tiles: slot s holds tile i + s of the current pass.  The
+  // fill (tiles 0 .. RUN - 1 and the first run's meta) is issued first; each
+  // pass then computes slot s and refills it with tile i + s + RUN (clamped
+  // into range: the tail re-reads the last tile from cache, and slots past
+  // the wave's range are not computed).  The meta of a run is double-buffered.
+  // Scheduling barriers keep slot order in the instruction stream so each
+  // slot's wait covers only its own loads.
+  typename WP::CodeT ring[RUN];
+  typename Op<DT>::vec ra[PA][NA];
+  typename WP::Meta mc, mn = WP::zero_meta();
+  XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), M};
+  if (n > 0) {
+    mn = wp.load_meta(r0);
+#pragma unroll
+    for (int s = 0; s < RUN; ++s) ring[s] = wp.load_codes(t0 + min(s, n - 1), lane);
+  }
+  if constexpr (is_staged(AM)) {
+    // every wave takes part in staging the M rows of x (and the permutation,
+    // and the input scales) while its first code tiles are in flight
+    const uint32_t xb = xlds_x_bytes(M, K), pb = xlds_perm_bytes(K, AM == AM_XGATHER);
+    stage_lds(x, (uint32_t)(M * K * 2), xlds, wave, lane);
+    if constexpr (AM == AM_XGATHER) stage_lds(perm, (uint32_t)(K * 4), xlds + xb, wave, lane);
+    if constexpr (XS) stage_lds(xsc, (uint32_t)(K * 2), xlds + xb + pb, wave, lane);
+    __syncthreads();
+    if constexpr (XS) {
+      // x[m][k] / s[k] in place (original column order): a pair of columns per
+      // step, their reciprocals shared by the M rows
+      uint32_t* xw = (uint32_t*)xlds;
+      const uint32_t* sw = (const uint32_t*)(xlds + xb + pb);
+      const int half = K >> 1;
+      for (int kp = threadIdx.x; kp < half; kp += 64 * DW) {
+        const uint32_t sv = sw[kp];
+        const float r0 = recip_scale<DT>((uint16_t)(sv & 0xFFFFu));
+        const float r1 = recip_scale<DT>((uint16_t)(sv >> 16));
+        for (int m = 0; m < M; ++m) {
+          const uint32_t v = xw[m * half + kp];
+          xw[m * half + kp] = (uint32_t)mul_round16<DT>((uint16_t)(v & 0xFFFFu), r0) |
+                              ((uint32_t)mul_round16<DT>((uint16_t)(v >> 16), r1) << 16);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (n > 0) {
+#pragma unroll
+    for (int s = 0; s < PA; ++s) load_a<DT, AM, MT, NA, WP>(rx, K, t0 + min(s, n - 1), lane, ra[s], xs);
+    for (int i = 0; i < n; i += RUN) {
+      mc = mn;
+      mn = wp.load_meta(r0 + min(i / RUN + 1, (n - 1) / RUN));
+#pragma unroll
+      for (int s = 0; s < RUN; ++s) {
+        const int sa = s % PA;
+        if (i + s < n) {  // wave-uniform
+          typename Op<DT>::vec b[4];
+          wp.operands(ring[s], s, mc, b);
+          mma_tile<DT, AM, MT, NA, NACC>(b, ra[sa], acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        ring[s] = wp.load_codes(t0 + min(i + s + RUN, n - 1), lane);
+        load_a<DT, AM, MT, NA, WP>(rx, K, t0 + min(i + s + PA, n - 1), lane, ra[sa], xs);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- v_mfma_f32_16x16x32 result layout: element e of lane l is row
+  // 4 (l >> 4) + e, column l & 15 of the 16x16 tile.
+  float4_t res[MT];
+  if constexpr (is_packed(AM)) {
+    // rows 4g .. 4g+3 of step tile acc[g] (g = lane group) are batch rows
+    // 0..3 of step g: take them and add the 4 lane groups (a shuffle
+    // reduction across the wave); lane group 0 then holds rows 0..3.
+    const int g = lane >> 4;
+    float4_t v = g == 0 ? acc[0] : (g == 1 ? acc[1] : (g == 2 ? acc[2] : acc[3]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] += __shfl_xor(v[e], 16, 64);
+      v[e] += __shfl_xor(v[e], 32, 64);
+    }
+    res[0] = g == 0 ? v : float4_t{0.f, 0.f, 0.f, 0.f};
+  } else {
+    constexpr int PER = NACC / MT;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      res[m] = acc[m * PER];
+#pragma unroll
+      for (int q = 1; q < PER; ++q) {
+        res[m][0] += acc[m * PER + q][0];
+        res[m][1] += acc[m * PER + q][1];
+        res[m][2] += acc[m * PER + q][2];
+        res[m][3] += acc[m * PER + q][3];
+      }
+    }
+  }
+
+  // ---- wave partials -> LDS, summed in wave order
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+    *(float4_t*)(red + ((wave * MT + m) * 64 + lane) * 4) = res[m];
+  __syncthreads();
+  if (wave < MT) {
+    const int m = wave;
+    float4_t s = *(const float4_t*)(red + ((0 * MT + m) * 64 + lane) * 4);
+#pragma unroll
+    for (int w = 1; w < DW; ++w) {
+      const float4_t v = *(const float4_t*)(red + ((w * MT + m) * 64 + lane) * 4);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+    const int col = ct * 16 + (lane & 15);
+    if (col < N) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + m * 16 + 4 * (lane >> 4) + e;
+        if (row < M) out[(size_t)row * N + col] = round16<DT>(s[e]);
+      }
+    }
+  }
+}
+
+template <int DT, int MT, int AM, int U, bool XS, int BITS>
+__global__ void __launch_bounds__(64 * DW)
+intb_decode_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ xsc,
+                   const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                   const uint8_t* __restrict__ zeros, uint32_t zx,
+                   const int32_t* __restrict__ perm, uint16_t* __restrict__ out, int M, int N,
+                   int K, int KT) {
+  __shared__ float red[DW * MT * 64 * 4];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+  IntW<DT, U, BITS> wp;
+  wp.codes = codes;
+  wp.scales = scales;
+  wp.zeros = zeros;
+  wp.zx = zx;
+  wp.KT = KT;
+  decode_body<DT, MT, AM, XS>(x, xsc, wp, out, M, N, K, KT, red, perm, xlds);
+}
+
+template <int DT, int MT, int AM, bool BATCH>
+__global__ void __launch_bounds__(64 * DW)
+nf4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
+                  const uint8_t* __restrict__ aq, const float* __restrict__ asc, Nf4Table L,
+                  uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+  __shared__ float red[DW * MT * 64 * 4];
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
+  __syncthreads();
+  extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
+  Nf4W<DT, BATCH> wp;
+  wp.q = q;
+  wp.aq = aq;
+  wp.asc = asc;
+  wp.lut = lut;
+  decode_body<DT, MT, AM, false>(x, nullptr, wp, out, M, N, K, KT, red, nullptr, xlds);
+}
+
+// ---------------------------------------------------------------- planning --
+
+// Raise a kernel's dynamic LDS limit to kMaxXlds (once per kernel; the call
+// is idempotent, so a race between host threads is harmless).
+static void allow_dynamic_lds(const void* kernel) {
+  static thread_local const void* done[32];
+  static thread_local int ndone = 0;
+  for (int i = 0; i < ndone; ++i)
+    if (done[i] == kernel) return;
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxXlds);
+  if (ndone < 32) done[ndone++] = kernel;
+}
+
+// Largest total of staged bytes (workgroups x bytes each) for which staging
+// beats a separate preparation pass: every workgroup copies the rows (and the
+// permutation and scales) from L2, so the cost grows with the grid, while the
+// pass costs about one launch (measured crossover on MI355X: staging saves
+// ~1 us on 4096 x 4096 layers and costs ~10 us on 5120 x 55296 ones).
+constexpr int64_t kMaxStagedTotal = (int64_t)12 << 20;
+
+// Activation mode and row tiles per workgroup row block for M rows of a
+// [N, K] layer; gather: an act-order permutation is to be applied, xs: AWQ
+// input scales.  For M <= 4 both are done on the rows staged in LDS when they
+// fit and the grid is small enough (staging x alone does not beat per-tile
+// loads).  Otherwise the caller prepares x first.
+static int pick_mode(int64_t M, int64_t N, int64_t K, bool gather, bool xs, int* mt) {
+  if (M <= 4) {
+    *mt = 1;
+    const int64_t b = xlds_bytes((int)M, (int)K, gather, xs);
+    if ((gather || xs) && b <= kMaxXlds && ceil_div(N, 16) * b <= kMaxStagedTotal)
+      return gather ? AM_XGATHER : AM_XSTAGED;
+    return AM_PACKED;
+  }
+  *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  return AM_FULL;
+}
+
+// One decode launch.  a: the call's arguments (xsc non-null only when the
+// kernel scales the activations itself).
+struct DecodeArgs {
+  const void *x, *xsc, *codes, *scales, *zeros;
+  const int32_t* perm;
+  void* out;
+  int64_t M, N, K;
+  hipStream_t stream;
+};
+
+template <int DT, int MT, int AM, int U, bool XS, int BITS>
+static void launch_intb_v(const DecodeArgs& a) {
+  const dim3 grid((unsigned)ceil_div(a.N, 16), (unsigned)ceil_div(a.M, 16 * MT));
+  const size_t lds =
+      is_staged(AM) ? xlds_bytes((int)a.M, (int)a.K, AM == AM_XGATHER, XS) : 0;
+  if (lds) allow_dynamic_lds((const void*)intb_decode_kernel<DT, MT, AM, U, XS, BITS>);
+  // a symmetric weight: the zeros descriptor gets an empty range over a valid
+  // base and every zero field reads 0 ^ 2^(BITS-1)
+  const uint32_t zx = a.zeros ? 0u : sym_zero_xor(BITS);
+  launch_timed(intb_decode_kernel<DT, MT, AM, U, XS, BITS>, grid, dim3(64 * DW), lds, a.stream,
+               (const uint16_t*)a.x, (const uint16_t*)a.xsc, (const uint8_t*)a.codes,
+               (const uint8_t*)a.scales, (const uint8_t*)(a.zeros ? a.zeros : a.scales), zx,
+               AM == AM_XGATHER ? a.perm : nullptr, (uint16_t*)a.out, (int)a.M, (int)a.N,
+               (int)a.K, (int)(a.K / 128));
+}
+
+template <int DT, int U, bool XS, int BITS>
+static void launch_intb_mode(int am, int mt, const DecodeArgs& a) {
+  if (am == AM_XGATHER) return launch_intb_v<DT, 1, AM_XGATHER, U, XS, BITS>(a);
+  if constexpr (XS) {
+    launch_intb_v<DT, 1, AM_XSTAGED, U, true, BITS>(a);  // the only other mode that scales
+  } else {
+    if (am == AM_PACKED) launch_intb_v<DT, 1, AM_PACKED, U, false, BITS>(a);
+    else if (mt == 1) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);
+    else if (mt == 2) launch_intb_v<DT, 2, AM_FULL, U, false, BITS>(a);
+    else launch_intb_v<DT, 4, AM_FULL, U, false, BITS>(a);
+  }
+}
+
+template <int DT, bool XS, int BITS>
+static void launch_intb_dt(int am, int mt, int G, const DecodeArgs& a) {
+  const int U = units_per_tile(G);
+  if (U == 1) launch_intb_mode<DT, 1, XS, BITS>(am, mt, a);
+  else if (U == 2) launch_intb_mode<DT, 2, XS, BITS>(am, mt, a);
+  else launch_intb_mode<DT, 4, XS, BITS>(am, mt, a);
+}
+
+// One decode launch of BITS-bit codes (instantiated once per width, each in
+// its own translation unit).
+template <int BITS>
+void launch_intb_decode(int dtype, bool xs, int am, int mt, int G, const DecodeArgs& a) {
+  if (dtype == DT_F16) {
+    if (xs) launch_intb_dt<DT_F16, true, BITS>(am, mt, G, a);
+    else launch_intb_dt<DT_F16, false, BITS>(am, mt, G, a);
+  } else {
+    if (xs) launch_intb_dt<DT_BF16, true, BITS>(am, mt, G, a);
+    else launch_intb_dt<DT_BF16, false, BITS>(am, mt, G, a);
+  }
+}
+extern template void launch_intb_decode<3>(int, bool, int, int, int, const DecodeArgs&);
+extern template void launch_intb_decode<4>(int, bool, int, int, int, const DecodeArgs&);
+extern template void launch_intb_decode<8>(int, bool, int, int, int, const DecodeArgs&);
+
+}  // namespace w4a16

@@ -20,9 +20,6 @@ struct Nf4Table {
 // for G >= 128 the single unit of tile t repeats the scale and zero of the
 // group that holds the tile.
 __host__ __device__ constexpr int units_per_tile(int G) { return G < 128 ? 128 / G : 1; }
-// A symmetric weight has no zeros: its zero loads read 0 through an empty
-// buffer range and this XOR turns every nibble into the implicit zero 8.
-constexpr uint32_t kSymZeroXor = 0x88888888u;
 
 // Workspace bytes the INT4 GEMM needs at this shape, with or without a column
 // permutation and AWQ input scales: room for the prepared activations (when
@@ -36,30 +33,31 @@ int64_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
 // calling host thread (hipExtLaunchKernel start/stop events).
 void set_timing_events(hipEvent_t start, hipEvent_t stop);
 
-// qzeros == nullptr: symmetric codes (no zeros).
-hipError_t launch_rtn_int4(const float* W, const int32_t* perm, int64_t N, int64_t K, int G,
-                           int32_t* qweight, uint16_t* scales, int32_t* qzeros,
-                           hipStream_t stream);
+// bits-bit RTN codes (3, 4 or 8) in the canonical packing; qzeros == nullptr:
+// symmetric codes (no zeros).
+hipError_t launch_rtn_int(const float* W, const int32_t* perm, int64_t N, int64_t K, int G,
+                          int bits, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+                          hipStream_t stream);
 hipError_t launch_nf4_quant(const float* W, int64_t N, int64_t K, const Nf4Table& L,
                             uint8_t* qweight, uint8_t* absmax_q, float* absmax_scale,
                             hipStream_t stream);
 // In the repack, dequant and GEMM launchers zeros == nullptr (qzeros,
 // zeros_r) is a symmetric weight.
 hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
-                         const int32_t* perm, int64_t K, int64_t N, int G, void* codes_r,
-                         void* scales_r, void* zeros_r, hipStream_t stream);
-hipError_t launch_dequant_int4(const void* codes_r, const void* scales_r, const void* zeros_r,
-                               int64_t K, int64_t N, int G, int dtype, void* w_out,
-                               hipStream_t stream);
+                         const int32_t* perm, int64_t K, int64_t N, int G, int bits,
+                         void* codes_r, void* scales_r, void* zeros_r, hipStream_t stream);
+hipError_t launch_dequant_int(const void* codes_r, const void* scales_r, const void* zeros_r,
+                              int64_t K, int64_t N, int G, int bits, int dtype, void* w_out,
+                              hipStream_t stream);
 hipError_t launch_dequant_nf4(const uint8_t* qweight, const uint8_t* absmax_q,
                               const float* absmax_scale, int64_t N, int64_t K, int dtype,
                               const Nf4Table& L, void* w_out, hipStream_t stream);
 
-// xsc: AWQ input scales s [K] (activation dtype) or nullptr.
-hipError_t launch_int4_gemm(const void* x, const void* xsc, const void* codes_r,
-                            const void* scales_r, const void* zeros_r, const int32_t* perm,
-                            void* out, int64_t M, int64_t N, int64_t K, int G, int dtype,
-                            void* workspace,
+// xsc: AWQ input scales s [K] (activation dtype) or nullptr; bits: 3, 4 or 8.
+hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
+                           const void* scales_r, const void* zeros_r, const int32_t* perm,
+                           void* out, int64_t M, int64_t N, int64_t K, int G, int bits,
+                           int dtype, void* workspace,
                             int64_t workspace_bytes, hipStream_t stream);
 // Whether w4a16_gemm runs the LDS-staged large-M kernel (activations shared
 // by a workgroup's 256 columns through LDS) rather than the skinny decode
@@ -68,9 +66,9 @@ hipError_t launch_int4_gemm(const void* x, const void* xsc, const void* codes_r,
 inline bool use_prefill(int64_t M, int64_t N, int64_t K) {
   return M >= 32 || (M >= 12 && N * K >= (int64_t)100 << 20);
 }
-void launch_int4_prefill(const void* x, const void* codes_r, const void* scales_r,
-                         const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
-                         int64_t K, int G, int dtype, hipStream_t stream);
+void launch_int_prefill(const void* x, const void* codes_r, const void* scales_r,
+                        const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
+                        int64_t K, int G, int bits, int dtype, hipStream_t stream);
 
 void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                         const float* absmax_scale, const Nf4Table& L, void* out, void* ws,

@@ -1,0 +1,457 @@
+// prefill.h -- the large-M fused dequantize-and-multiply kernel template and
+// its launchers, shared by the translation units that instantiate them (one
+// per weight code width, compiled in parallel).  See prefill.hip for the
+// design.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+#include "launch.h"
+
+namespace w4a16 {
+
+
+constexpr int PF_WAVES = 4;                  // waves per workgroup
+constexpr int PF_ROWB = 256;                 // LDS bytes of one row of a K tile
+// Rows per workgroup BM in {64, 128, 256}: BM / 32 MFMA row tiles per wave,
+// an LDS stage of BM x 256 bytes, BM / 16 16-byte activation loads per lane.
+
+#ifndef W4A16_PF_DMA_STEPS
+#define W4A16_PF_DMA_STEPS 8
+#endif
+constexpr int PF_DMA_STEPS = W4A16_PF_DMA_STEPS;  // steps the activation loads spread over
+#ifndef W4A16_PF_APF
+#define W4A16_PF_APF 1
+#endif
+#ifndef W4A16_PF_SGB
+#define W4A16_PF_SGB 1
+#endif
+
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+template <int DT>
+__device__ __forceinline__ float16_t mfma32x32x16(const typename Op<DT>::vec& a,
+                                                  const typename Op<DT>::vec& b,
+                                                  const float16_t& c);
+template <>
+__device__ __forceinline__ float16_t mfma32x32x16<DT_F16>(const half8_t& a, const half8_t& b,
+                                                          const float16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ float16_t mfma32x32x16<DT_BF16>(const bf16x8_t& a, const bf16x8_t& b,
+                                                           const float16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
+// lds + 16 l (the LDS base is wave-uniform).
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// TAIL: the row block may hold fewer than 256 rows; the row of each load is
+// then part of the per-lane offset so that rows past M read 0.  Full blocks
+// put it in the scalar offset (fewer registers).
+// Split-K: workgroup z of S takes K tiles [z KT / S, (z + 1) KT / S) and, when
+// S > 1, writes its fp32 partial tile to part[z][M][N] for split_reduce_kernel.
+//
+// Weight formats (FMT): INT4 reads the repacked tiles as above.  NF4 reads the
+// canonical layout (row n: K / 2 bytes, element 2 j in the low nibble of byte
+// j): for K tile t, lane l loads the 32 bytes holding inputs
+// 128 t + 64 (l >> 5) .. + 63 of its column, one 64-element absmax block, and
+// word j of them is the B operand of step j; the activation operand of step j
+// is then chunk 8 (l >> 5) + j of the tile (the K order inside a tile is the
+// same permutation on both sides).  Dequant: w = round16(L[c] * a'), a' =
+// absmax_q * absmax_scale, L from LDS.  NF4 here needs K % 128 == 0.
+enum { FMT_INT4 = 0, FMT_NF4 = 1 };
+
+// INT codes of BITS bits (3, 4 or 8; the Codes<BITS> forms of common.h): a
+// column tile's K tile is 256 BITS bytes, repacked lane r's codes at 12 r
+// (3 bits), 16 r (4 bits), or 16 r and 1024 + 16 r (8 bits).
+template <int DT, int BM, bool TAIL, int FMT, int U, int BITS>
+__global__ void __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per_eu(1, 1)))
+wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
+                  const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                  uint32_t zx, Nf4Table L, uint16_t* __restrict__ out,
+                  float* __restrict__ part, int M, int N, int K, int KT, int NP, int S) {
+  typedef typename Op<DT>::vec vec;
+  typedef Codes<FMT == FMT_NF4 ? 4 : BITS> CT;     // NF4: its 16-byte loads as Codes<4>
+  constexpr int kTile = 256 * BITS;                 // INT: bytes per column tile, K tile
+  constexpr int kZW = zero_field_bits(BITS);        // INT: zero field width
+  constexpr int kZWords = U * kZW / 4;              // INT: zero dwords per column and run
+  __shared__ float lut[16];
+  if (FMT == FMT_NF4 && threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
+  constexpr int PF_BM = BM;
+  constexpr int PF_MT = BM / 32;
+  constexpr int PF_STAGE = BM * PF_ROWB;
+  constexpr int PF_ALD = BM * 16 / (64 * PF_WAVES);
+  __shared__ __attribute__((aligned(16))) uint8_t As[2 * PF_STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = (TAIL ? M / PF_BM : blockIdx.y) * PF_BM;
+  const int z = blockIdx.z;
+  const int tb = (int)((int64_t)z * KT / S), te = (int)((int64_t)(z + 1) * KT / S);
+  const int p = blockIdx.x * PF_WAVES + wave;  // this wave's 64-column panel
+  const int KT8 = (KT + 7) >> 3;
+  const int i16 = lane & 15, h = lane >> 5;
+
+  // ---- activations: rows row0 .. row0 + vrows - 1 of x; rows past M read 0.
+  // Instruction i of wave w fills the 1 KB LDS block 4 i + w (rows
+  // 16 i + 4 w .. + 3), lane l writing position (l & 15) of row
+  // 16 i + 4 w + (l >> 4), which holds chunk (l & 15) ^ (row & 15): the
+  // swizzle is applied on the global side.
+  const int vrows = min(PF_BM, M - row0);
+  const rsrc_t rx = make_rsrc(x + (size_t)row0 * K, (uint32_t)vrows * (uint32_t)K * 2u);
+  const uint32_t arow_bytes = (uint32_t)K * 2u;
+  const int arow0 = 4 * wave + (lane >> 4);  // row & 15 of every instruction's row
+  const uint32_t avoff = (uint32_t)arow0 * arow_bytes + (uint32_t)((i16 ^ arow0) << 4);
+  const uint32_t astride = 16u * arow_bytes;
+
+  // ---- weights of panel p (all loads return 0 for a panel past the last).
+  // Column group g (32 columns): column tile 2 g + ((l & 31) >> 4), entry
+  // l & 15 of its meta.
+  const bool pv = p < NP;
+  const size_t pp = pv ? (size_t)p : 0;
+  rsrc_t rc, rs, rz;
+  uint32_t vcode[2][2], vmeta[2], gblk[2];
+  if constexpr (FMT == FMT_INT4) {
+    rc = make_rsrc(codes + pp * KT * 4 * kTile, pv ? (uint32_t)KT * 4u * kTile : 0u);
+    rs = make_rsrc(scales + pp * KT8 * 1024 * U, pv ? (uint32_t)KT8 * 1024u * U : 0u);
+    rz = make_rsrc(zeros + pp * KT8 * 256 * kZWords,
+                   pv && !zx ? (uint32_t)KT8 * 256u * kZWords : 0u);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int ct = 2 * g + ((lane & 31) >> 4);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        vcode[g][h2] =
+            (uint32_t)(ct * kTile + (i16 + 16 * (2 * h2 + h)) * (BITS == 3 ? 12 : 16));
+      vmeta[g] = (uint32_t)(ct * 16 + i16);
+    }
+  } else {
+    // rows of this panel (N % 16 == 0; rows past N read 0 -> a' = 0)
+    const int nrows = pv ? min(64, N - p * 64) : 0;
+    const uint32_t Kb = (uint32_t)K / 2u, Kblk = (uint32_t)K / 64u;
+    rc = make_rsrc(codes + pp * 64 * Kb, (uint32_t)nrows * Kb);
+    rs = make_rsrc(scales + pp * 64 * Kblk, (uint32_t)nrows * Kblk);
+    rz = make_rsrc(zeros, (uint32_t)(((int64_t)N * Kblk + 255) / 256 * 4));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int c = 32 * g + (lane & 31);
+      vcode[g][0] = (uint32_t)c * Kb + 32u * (uint32_t)h;
+      vcode[g][1] = vcode[g][0] + 16u;
+      vmeta[g] = (uint32_t)c * Kblk + (uint32_t)h;
+      gblk[g] = (uint32_t)(pp * 64 + c) * Kblk + (uint32_t)h;
+    }
+  }
+  // the weights and meta of K tile t for column group g.  INT: sa holds the U
+  // scales of the tile (units (t & 7) U .. of the run, 2 U bytes), za the zero
+  // dword holding their fields.
+  auto load_w = [&](int t, int g, CT (&w)[2], u32x2_t& sa, uint32_t& za) {
+    if constexpr (FMT == FMT_INT4) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        if constexpr (BITS == 4) {
+          w[h2].w = bld128(rc, vcode[g][h2], t * 4 * kTile);
+        } else if constexpr (BITS == 3) {
+          w[h2].w = bld96(rc, vcode[g][h2], t * 4 * kTile);
+        } else {
+          w[h2].lo = bld128(rc, vcode[g][h2], t * 4 * kTile);
+          w[h2].hi = bld128(rc, vcode[g][h2] + 1024u, t * 4 * kTile);
+        }
+      }
+      const int sb = (t >> 3) * 1024 * U + (t & 7) * 2 * U;
+      if constexpr (U == 1) sa = u32x2_t{bld16(rs, vmeta[g] * 16u, sb), 0u};
+      else if constexpr (U == 2) sa = u32x2_t{bld32(rs, vmeta[g] * 32u, sb), 0u};
+      else sa = bld64(rs, vmeta[g] * 64u, sb);
+      za = bld32(rz, vmeta[g] * 4u * kZWords,
+                 (t >> 3) * 256 * kZWords + (((t & 7) * U * kZW) >> 5) * 4) ^ zx;
+    } else {
+      w[0].w = bld128(rc, vcode[g][0], t * 64);
+      w[1].w = bld128(rc, vcode[g][1], t * 64);
+      sa = u32x2_t{__builtin_amdgcn_raw_buffer_load_b8(rs, vmeta[g], 2 * t, 0), 0u};
+      za = bld32(rz, ((gblk[g] + 2u * (uint32_t)t) >> 8) * 4u, 0);
+    }
+  };
+
+  float16_t acc[PF_MT][2];
+#pragma unroll
+  for (int m = 0; m < PF_MT; ++m)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) acc[m][g] = float16_t{};
+
+  CT cw[2][2], cn[2][2];
+  u32x2_t sc[2], sn[2];
+  uint32_t zz[2], zn[2];
+
+  // ---- prologue: K tile 0
+#pragma unroll
+  for (int g = 0; g < 2; ++g) load_w(tb, g, cw[g], sc[g], zz[g]);
+#pragma unroll
+  for (int i = 0; i < PF_ALD; ++i)
+    lds_dma16(rx, As + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
+              TAIL ? tb * 256 : (int)((uint32_t)i * astride) + tb * 256);
+  __syncthreads();
+
+  for (int t = tb; t < te; ++t) {
+    // ---- issue K tile t + 1 (the last tile is re-read on the final pass);
+    // its activations go to LDS stage (t - tb + 1) & 1, last read before the
+    // previous barrier
+    const int tn = min(t + 1, te - 1);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) load_w(tn, g, cn[g], sn[g], zn[g]);
+    uint8_t* sw = As + ((t - tb + 1) & 1) * PF_STAGE;
+    // the activation loads of tile t + 1 are spread over the first
+    // PF_DMA_STEPS steps of tile t (a burst of them stalls the issuing waves
+    // behind the address queue)
+    auto issue_dma = [&](int i) {
+      lds_dma16(rx, sw + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
+                TAIL ? tn * 256 : (int)((uint32_t)i * astride) + tn * 256);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- K tile t from LDS stage t & 1: 8 steps of 16 inputs.  Per step the
+    // operand reads come first; the dequant of the next step's B operand is
+    // spread between the step's MFMAs (each 32 x 32 x 16 MFMA keeps the matrix
+    // pipe busy long enough to issue several VALU instructions behind it).
+    float ap[2];  // NF4: a' of this lane's block
+    const int zb = ((t & 7) * U) % (32 / kZW);  // zero field of the tile's first unit
+    if constexpr (FMT == FMT_NF4) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) ap[g] = (float)(sc[g][0] & 0xFFu) * __builtin_bit_cast(float, zz[g]);
+    }
+    // B operand of step s for column group g: word j = s >> 1 of the tile, in
+    // meta unit j U / 4.  The unit's dequant parameters are formed at the step
+    // (a few VALU instructions between MFMAs); formed once per tile and held
+    // across it they made the small-M launches of this kernel markedly slower.
+    auto operand = [&](int s, int g) -> vec {
+      if constexpr (FMT == FMT_INT4) {
+        const int u = (s >> 1) * U / 4;
+        QParam<DT> q;
+        q.set((sc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
+              (zz[g] >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
+        return dequant_step<DT>(cw[g][s & 1], s >> 1, q);
+      } else {
+        const uint32_t w = cw[g][s >> 2].w[s & 3];
+        vec v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = lut[(w >> (4 * e)) & 0xFu] * ap[g];
+          if constexpr (DT == DT_F16) v[e] = (_Float16)f;
+          else v[e] = (__bf16)f;
+        }
+        return v;
+      }
+    };
+    const uint8_t* st = As + ((t - tb) & 1) * PF_STAGE;
+    auto read_step = [&](int s, vec (&a)[PF_MT]) {
+      // 8-element chunk of this lane's inputs in step s
+      const int q = FMT == FMT_INT4 ? 2 * s + h : 8 * h + s;
+#pragma unroll
+      for (int m = 0; m < PF_MT; ++m)
+        a[m] = *(const vec*)(st + (m * 32 + (lane & 31)) * PF_ROWB + ((q ^ i16) << 4));
+    };
+    vec b[2], a[PF_MT];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) b[g] = operand(0, g);
+    read_step(0, a);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      vec bn[2], an[PF_MT];
+      // loads i with i * PF_DMA_STEPS / PF_ALD == s go out in step s
+      const int i0 = (s * PF_ALD + PF_DMA_STEPS - 1) / PF_DMA_STEPS;
+      const int i1 = ((s + 1) * PF_ALD + PF_DMA_STEPS - 1) / PF_DMA_STEPS;
+#pragma unroll
+      for (int i = i0; i < i1 && i < PF_ALD; ++i) issue_dma(i);
+      if (s < 7) {
+        const int sn1 = s + 1;
+#if W4A16_PF_APF
+        read_step(sn1, an);
+#endif
+#pragma unroll
+        for (int g = 0; g < 2; ++g) bn[g] = operand(sn1, g);
+      }
+#pragma unroll
+      for (int m = 0; m < PF_MT; ++m)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) acc[m][g] = mfma32x32x16<DT>(a[m], b[g], acc[m][g]);
+#if W4A16_PF_SGB
+      if (s < 7) {
+#pragma unroll
+        for (int k = 0; k < 2 * PF_MT; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          if (k < i1 - i0 && i0 < PF_ALD)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one activation load
+#if W4A16_PF_APF
+          if (k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+#endif
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
+        }
+      }
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 7) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) b[g] = bn[g];
+#if W4A16_PF_APF
+#pragma unroll
+        for (int m = 0; m < PF_MT; ++m) a[m] = an[m];
+#else
+        read_step(s + 1, a);
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) cw[g][h2] = cn[g][h2];
+      sc[g] = sn[g];
+      zz[g] = zn[g];
+    }
+    __syncthreads();  // the LDS writes of tile t + 1 are complete (vmcnt) and visible
+  }
+
+  // ---- epilogue: register r of lane l is row (r & 3) + 4 (l >> 5) + 8 (r >> 2),
+  // column l & 31 of the 32 x 32 tile
+  float* pz = part + (size_t)z * M * N;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int col = p * 64 + g * 32 + (lane & 31);
+    if (col < N) {
+#pragma unroll
+      for (int m = 0; m < PF_MT; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + m * 32 + (r & 3) + 4 * h + 8 * (r >> 2);
+          if (row < M) {
+            if (S == 1)
+              out[(size_t)row * N + col] = round16<DT>(acc[m][g][r]);
+            else
+              pz[(size_t)row * N + col] = acc[m][g][r];
+          }
+        }
+      }
+    }
+  }
+}
+
+// out = round16(sum_z part[z]) over the S split-K partials, added in z order
+// (bitwise reproducible); 4 consecutive outputs per thread.
+template <int DT>
+__global__ void __launch_bounds__(256)
+split_reduce_kernel(const float* __restrict__ part, int S, int64_t MN, uint16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= MN) return;
+  float4_t s = *(const float4_t*)(part + i);
+  for (int z = 1; z < S; ++z) {
+    const float4_t v = *(const float4_t*)(part + (size_t)z * MN + i);
+    s[0] += v[0];
+    s[1] += v[1];
+    s[2] += v[2];
+    s[3] += v[3];
+  }
+  const uint32_t lo = (uint32_t)round16<DT>(s[0]) | ((uint32_t)round16<DT>(s[1]) << 16);
+  const uint32_t hi = (uint32_t)round16<DT>(s[2]) | ((uint32_t)round16<DT>(s[3]) << 16);
+  *(uint2*)(out + i) = make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------- planning --
+// Rows per workgroup for M, and the split of K that fills the GPU best: a
+// simple model of the call time (rounds of workgroups on 256 CUs x K tiles per
+// workgroup x per-tile MFMA time, plus the partials' round trip through HBM).
+struct PrefillPlan {
+  int bm, splits;
+};
+
+PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K);
+
+template <int DT, int BM, int FMT, int U, int BITS>
+static void launch_prefill_bm(const void* x, const void* codes_r, const void* scales_r,
+                              const void* zeros_r, const Nf4Table& L, void* out, float* part,
+                              int S, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t NP = ceil_div(N, 64);
+  const int KT = (int)(K / 128);
+  const unsigned gx = (unsigned)ceil_div(NP, PF_WAVES);
+  const int64_t full = M / BM;
+  // INT codes without zeros (symmetric): an empty zeros range over a valid
+  // base, every zero field read as 0 ^ 2^(BITS-1)
+  const uint32_t zx = (FMT == FMT_INT4 && !zeros_r) ? sym_zero_xor(BITS) : 0u;
+  const uint8_t* zp = (const uint8_t*)(zeros_r ? zeros_r : scales_r);
+  // the timing events (if set) go to the first launch
+  if (full > 0)
+    launch_timed(wq_prefill_kernel<DT, BM, false, FMT, U, BITS>,
+                 dim3(gx, (unsigned)full, (unsigned)S), dim3(64 * PF_WAVES), 0, stream,
+                 (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r, zp, zx, L,
+                 (uint16_t*)out, part, (int)M, (int)N, (int)K, KT, (int)NP, S);
+  if (M % BM)
+    launch_timed(wq_prefill_kernel<DT, BM, true, FMT, U, BITS>, dim3(gx, 1, (unsigned)S),
+                 dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
+                 (const uint8_t*)scales_r, zp, zx, L, (uint16_t*)out, part, (int)M, (int)N,
+                 (int)K, KT, (int)NP, S);
+  if (S > 1) {
+    const int64_t MN = M * N;
+    hipLaunchKernelGGL(split_reduce_kernel<DT>, dim3((unsigned)ceil_div(MN / 4, (int64_t)256)),
+                       dim3(256), 0, stream, (const float*)part, S, MN, (uint16_t*)out);
+  }
+}
+
+template <int DT, int FMT, int U, int BITS>
+static void launch_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
+                              const void* zeros_r, const Nf4Table& L, void* out, void* ws,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const PrefillPlan pl = plan_prefill(M, N, K);
+  float* part = (float*)ws;
+  if (pl.bm == 64)
+    launch_prefill_bm<DT, 64, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
+                                      N, K, stream);
+  else if (pl.bm == 128)
+    launch_prefill_bm<DT, 128, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
+                                       N, K, stream);
+  else
+    launch_prefill_bm<DT, 256, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
+                                       N, K, stream);
+}
+
+template <int DT, int BITS>
+static void launch_intb_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
+                                   const void* zeros_r, void* out, void* ws, int64_t M,
+                                   int64_t N, int64_t K, int G, hipStream_t stream) {
+  const Nf4Table none{};
+  const int U = units_per_tile(G);
+  if (U == 1)
+    launch_prefill_dt<DT, FMT_INT4, 1, BITS>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N,
+                                             K, stream);
+  else if (U == 2)
+    launch_prefill_dt<DT, FMT_INT4, 2, BITS>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N,
+                                             K, stream);
+  else
+    launch_prefill_dt<DT, FMT_INT4, 4, BITS>(x, codes_r, scales_r, zeros_r, none, out, ws, M, N,
+                                             K, stream);
+}
+
+// The large-M kernel for BITS-bit codes (instantiated once per width, each in
+// its own translation unit).
+template <int BITS>
+void launch_intb_prefill(const void* x, const void* codes_r, const void* scales_r,
+                         const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
+                         int64_t K, int G, int dtype, hipStream_t stream) {
+  if (dtype == DT_F16)
+    launch_intb_prefill_dt<DT_F16, BITS>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, G,
+                                         stream);
+  else
+    launch_intb_prefill_dt<DT_BF16, BITS>(x, codes_r, scales_r, zeros_r, out, ws, M, N, K, G,
+                                          stream);
+}
+#define W4A16_PREFILL_ARGS \
+  const void*, const void*, const void*, const void*, void*, void*, int64_t, int64_t, int64_t, \
+      int, int, hipStream_t
+extern template void launch_intb_prefill<3>(W4A16_PREFILL_ARGS);
+extern template void launch_intb_prefill<4>(W4A16_PREFILL_ARGS);
+extern template void launch_intb_prefill<8>(W4A16_PREFILL_ARGS);
+
+}  // namespace w4a16

@@ -26,23 +26,70 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v)
   for (; i < n; i += stride) p[i] = v;
 }
 
-// ---------------------------------------------------------------- RTN INT4 --
+// ------------------------------------------------- canonical b-bit packing --
+// GPTQ style: each run of L = 32 / gcd(b, 32) consecutive codes (8 at 4 bits,
+// 4 at 8 bits, 32 at 3 bits) is a little-endian bit stream of L b / 32 words,
+// code e at bits [b e, b e + b); qweight runs along K (word row = run word,
+// column n), qzeros runs along N within each group row.
+__host__ __device__ constexpr int run_codes(int bits) { return bits == 3 ? 32 : 32 / bits; }
+
+struct BitPos {
+  int64_t word;  // run word index along the packed dimension
+  int sh;        // bit position in that word (the code continues in word + 1 when sh + b > 32)
+};
+__device__ __forceinline__ BitPos bit_pos(int64_t i, int bits) {
+  const int L = run_codes(bits), nw = L * bits / 32;
+  const int pos = bits * (int)(i % L);
+  return BitPos{(i / L) * nw + pos / 32, pos % 32};
+}
+
+// code (n, k) of a canonical qweight [K b / 32, N]
+__device__ __forceinline__ uint32_t canon_code(const uint32_t* __restrict__ qw, int64_t N,
+                                               int64_t n, int64_t k, int bits) {
+  const BitPos bp = bit_pos(k, bits);
+  uint32_t v = qw[bp.word * N + n] >> bp.sh;
+  if (bp.sh + bits > 32) v |= qw[(bp.word + 1) * N + n] << (32 - bp.sh);
+  return v & ((1u << bits) - 1u);
+}
+
+// zero (g, n) of a canonical qzeros [K/G, N b / 32]
+__device__ __forceinline__ uint32_t canon_zero(const uint32_t* __restrict__ qz, int64_t N,
+                                               int64_t g, int64_t n, int bits) {
+  const BitPos bp = bit_pos(n, bits);
+  const uint32_t* row = qz + g * (N * bits / 32);
+  uint32_t v = row[bp.word] >> bp.sh;
+  if (bp.sh + bits > 32) v |= row[bp.word + 1] << (32 - bp.sh);
+  return v & ((1u << bits) - 1u);
+}
+
+// OR a code into a canonical packed array (its word row stride is `stride`).
+__device__ __forceinline__ void canon_or(uint32_t* __restrict__ base, int64_t stride,
+                                         int64_t col, int64_t i, uint32_t q, int bits) {
+  if (!q) return;
+  const BitPos bp = bit_pos(i, bits);
+  atomicOr(&base[bp.word * stride + col], q << bp.sh);
+  if (bp.sh + bits > 32) atomicOr(&base[(bp.word + 1) * stride + col], q >> (32 - bp.sh));
+}
+
+// ------------------------------------------------------------------ RTN INT --
 // One wave per (row n, group g of G members); lane holds members u = lane +
 // 64 h, read twice (range, then codes).  Codes are OR-ed into the zero-filled
-// canonical qweight / qzeros words.  Asymmetric: s = fp16(fp32(max - min) / 15),
-// z = clip(rint(-min / s), 0, 15), q = clip(rint(w / s) + z, 0, 15).
-// Symmetric (qzeros == nullptr): s = fp16(fp32(max |w|) / 7),
-// q = clip(rint(w / s), -8, 7) + 8.  A group whose fp16 scale is 0 uses s = 1.
+// canonical qweight / qzeros words.  With qmax = 2^b - 1:
+// asymmetric: s = fp16(fp32(max - min) / qmax), z = clip(rint(-min / s), 0, qmax),
+// q = clip(rint(w / s) + z, 0, qmax).  Symmetric (qzeros == nullptr): s =
+// fp16(fp32(max |w|) / (2^(b-1) - 1)), q = clip(rint(w / s), -2^(b-1),
+// 2^(b-1) - 1) + 2^(b-1).  A group whose fp16 scale is 0 uses s = 1.
 __global__ void __launch_bounds__(256)
-rtn_int4_kernel(const float* __restrict__ W, const int32_t* __restrict__ perm, int64_t N,
-                int64_t K, int G, uint32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
-                uint32_t* __restrict__ qzeros) {
+rtn_int_kernel(const float* __restrict__ W, const int32_t* __restrict__ perm, int64_t N,
+               int64_t K, int G, int bits, uint32_t* __restrict__ qweight,
+               uint16_t* __restrict__ scales, uint32_t* __restrict__ qzeros) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t ng = K / G;
   if (item >= N * ng) return;
   const int64_t g = item / N, n = item % N;  // n fastest across waves
   const bool sym = qzeros == nullptr;
+  const float qmax = (float)((1 << bits) - 1), half = (float)(1 << (bits - 1));
   auto col = [&](int u) -> int64_t {
     const int64_t k = g * G + u;
     return perm ? (int64_t)perm[k] : k;
@@ -55,30 +102,28 @@ rtn_int4_kernel(const float* __restrict__ W, const int32_t* __restrict__ perm, i
   }
   mn = wave_min(mn);
   mx = wave_max(mx);
-  _Float16 s16 = sym ? (_Float16)(mx / 7.0f)             // correctly rounded fp32 div, RNE
-                     : (_Float16)((mx - mn) / 15.0f);    // fp32 sub + div, RNE
+  _Float16 s16 = sym ? (_Float16)(mx / (half - 1.0f))   // correctly rounded fp32 div, RNE
+                     : (_Float16)((mx - mn) / qmax);    // fp32 sub + div, RNE
   if (s16 == (_Float16)0.0f) s16 = (_Float16)1.0f;
   const float sf = (float)s16;
-  // symmetric: clip(rint(w / s), -8, 7) + 8 is the asymmetric formula with z = 8
-  const float z = sym ? 8.0f : fminf(fmaxf(rintf(-mn / sf), 0.0f), 15.0f);
+  // symmetric: clip(rint(w / s), -h, h - 1) + h is the asymmetric formula with z = h
+  const float z = sym ? half : fminf(fmaxf(rintf(-mn / sf), 0.0f), qmax);
   for (int u = lane; u < G; u += 64) {
     const int64_t k = col(u);
     const float w = W[n * K + k];
-    const float q = fminf(fmaxf(rintf(w / sf) + z, 0.0f), 15.0f);
-    const uint32_t qi = (uint32_t)q;
-    if (qi) atomicOr(&qweight[(k >> 3) * N + n], qi << (4 * (k & 7)));
+    const float q = fminf(fmaxf(rintf(w / sf) + z, 0.0f), qmax);
+    canon_or(qweight, N, n, k, (uint32_t)q, bits);
   }
   if (lane == 0) {
     scales[g * N + n] = __builtin_bit_cast(uint16_t, s16);
-    const uint32_t zi = (uint32_t)z;
-    if (!sym && zi) atomicOr(&qzeros[g * (N >> 3) + (n >> 3)], zi << (4 * (n & 7)));
+    if (!sym) canon_or(qzeros + g * (N * bits / 32), 1, 0, n, (uint32_t)z, bits);
   }
 }
 
-hipError_t launch_rtn_int4(const float* W, const int32_t* perm, int64_t N, int64_t K, int G,
-                           int32_t* qweight, uint16_t* scales, int32_t* qzeros,
-                           hipStream_t stream) {
-  const int64_t nw = (K / 8) * N, nz = (K / G) * (N / 8);
+hipError_t launch_rtn_int(const float* W, const int32_t* perm, int64_t N, int64_t K, int G,
+                          int bits, int32_t* qweight, uint16_t* scales, int32_t* qzeros,
+                          hipStream_t stream) {
+  const int64_t nw = (K * bits / 32) * N, nz = (K / G) * (N * bits / 32);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(nw, 256), 65535)),
                      dim3(256), 0, stream, (uint32_t*)qweight, nw, 0u);
   if (qzeros)
@@ -86,8 +131,8 @@ hipError_t launch_rtn_int4(const float* W, const int32_t* perm, int64_t N, int64
                        dim3((unsigned)std::min<int64_t>(ceil_div(nz, 256), 65535)), dim3(256), 0,
                        stream, (uint32_t*)qzeros, nz, 0u);
   const int64_t items = N * (K / G);
-  hipLaunchKernelGGL(rtn_int4_kernel, dim3((unsigned)ceil_div(items, 4)), dim3(256), 0, stream,
-                     W, perm, N, K, G, (uint32_t*)qweight, scales, (uint32_t*)qzeros);
+  hipLaunchKernelGGL(rtn_int_kernel, dim3((unsigned)ceil_div(items, 4)), dim3(256), 0, stream,
+                     W, perm, N, K, G, bits, (uint32_t*)qweight, scales, (uint32_t*)qzeros);
   return hipGetLastError();
 }
 
@@ -145,42 +190,74 @@ hipError_t launch_nf4_quant(const float* W, int64_t N, int64_t K, const Nf4Table
 }
 
 // --------------------------------------------------------------------- repack --
+// Dwords per lane of one repacked tile (16 columns x 128 inputs) at b bits.
+__host__ __device__ constexpr int tile_lane_dwords(int bits) { return bits == 3 ? 3 : bits == 4 ? 4 : 8; }
+
 // One thread per 32-bit output word of the code tiles (coalesced writes).
+// Tile (p, t, c) holds 64 lanes x D dwords: [64][D] at 3 and 4 bits,
+// [2 halves][64][4] at 8 bits; lane l = i + 16 b of column 64p + 16c + i.
+// The codes of each lane dword (Codes<b> forms of common.h) are read from
+// the canonical array through the permutation.
 __global__ void __launch_bounds__(256)
 repack_codes_kernel(const uint32_t* __restrict__ qweight, const int32_t* __restrict__ perm,
-                    int64_t K, int64_t N, int64_t NP, uint32_t* __restrict__ codes_r) {
+                    int64_t K, int64_t N, int64_t NP, int bits, uint32_t* __restrict__ codes_r) {
   const int64_t KT = K / 128;
-  const int64_t total = NP * KT * 4 * 64 * 4;
+  const int D = tile_lane_dwords(bits);
+  const int64_t per_tile = 64 * D;
+  const int64_t total = NP * KT * 4 * per_tile;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int j = (int)(idx & 3);
-  const int lane = (int)((idx >> 2) & 63);
-  const int c = (int)((idx >> 8) & 3);
-  const int64_t pt = idx >> 10;  // p * KT + t
+  const int w = (int)(idx % per_tile);
+  const int c = (int)((idx / per_tile) & 3);
+  const int64_t pt = idx / per_tile / 4;  // p * KT + t
   const int64_t t = pt % KT, p = pt / KT;
+  int lane, d;
+  if (bits == 8) {
+    lane = (w >> 2) & 63;
+    d = 4 * (w >> 8) + (w & 3);
+  } else {
+    lane = w / D;
+    d = w % D;
+  }
   const int64_t n = p * 64 + c * 16 + (lane & 15);
+  const int b = lane >> 4;
   uint32_t word = 0;
   if (n < N) {
-    const int64_t kb = t * 128 + j * 32 + (lane >> 4) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t k = perm ? (int64_t)perm[kb + e] : kb + e;
-      const uint32_t q = (qweight[(k >> 3) * N + n] >> (4 * (k & 7))) & 0xFu;
-      word |= q << (4 * ((e >> 1) + 4 * (e & 1)));
+    auto code = [&](int j, int e) -> uint32_t {
+      const int64_t kp = t * 128 + 32 * j + 8 * b + e;  // permuted input
+      return canon_code(qweight, N, n, perm ? (int64_t)perm[kp] : kp, bits);
+    };
+    if (bits == 4) {
+      for (int e = 0; e < 8; ++e) word |= code(d, e) << (4 * ((e >> 1) + 4 * (e & 1)));
+    } else if (bits == 8) {
+      const int h = d >> 2, dd = d & 3;
+      const int j = 2 * h + (dd >> 1);
+      for (int e4 = 0; e4 < 4; ++e4)
+        word |= code(j, 4 * (dd & 1) + e4) << (8 * ((e4 >> 1) + 2 * (e4 & 1)));
+    } else if (d < 2) {  // 3 bits: low 2 bits of steps 2d, 2d + 1
+      for (int jj = 0; jj < 2; ++jj)
+        for (int e = 0; e < 8; ++e)
+          word |= (code(2 * d + jj, e) & 3u) << (16 * (e & 1) + 2 * (4 * jj + (e >> 1)));
+    } else {             // 3 bits: high bits of all 4 steps
+      for (int j = 0; j < 4; ++j)
+        for (int e = 0; e < 8; ++e)
+          word |= (code(j, e) >> 2) << (16 * (e & 1) + 4 * j + (e >> 1));
     }
   }
   codes_r[idx] = word;
 }
 
 // One thread per (panel p, run g of 8 K tiles, column tile c, column i): the
-// 8 U scales (16 U bytes) and 8 U zero nibbles (U words) of that column, unit
-// r of the run being tile 8 g + r / U, unit r % U.
+// 8 U scales (16 U bytes) and 8 U zero fields of that column, unit r of the
+// run being tile 8 g + r / U, unit r % U.  Zero fields are 4 bits wide (8 at
+// 8 bits): U or 2U dwords.
 __global__ void __launch_bounds__(256)
 repack_meta_kernel(const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
-                   int64_t K, int64_t N, int64_t NP, int G, uint16_t* __restrict__ scales_r,
-                   uint32_t* __restrict__ zeros_r) {
+                   int64_t K, int64_t N, int64_t NP, int G, int bits,
+                   uint16_t* __restrict__ scales_r, uint32_t* __restrict__ zeros_r) {
   const int64_t KT = K / 128, KT8 = ceil_div(KT, 8);
   const int U = units_per_tile(G), span = G < 128 ? G : 128;
+  const int zw = zero_field_bits(bits), per = 32 / zw, nzw = 8 * U / per;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= NP * KT8 * 64) return;
   const int i = (int)(idx & 15);
@@ -189,50 +266,57 @@ repack_meta_kernel(const uint16_t* __restrict__ scales, const uint32_t* __restri
   const int64_t g = pg % KT8, p = pg / KT8;
   const int64_t n = p * 64 + c * 16 + i;
   for (int w = 0; w < U; ++w) {
-    uint32_t zw = 0;
     u32x4_t sv = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int64_t v = g * 8 * U + 8 * w + e;  // unit index
       const int64_t t = v / U;
-      uint32_t sb = 0, z = 0;
-      if (n < N && t < KT) {
-        const int64_t grp = (128 * t + (v % U) * span) / G;
-        sb = scales[grp * N + n];
-        if (qzeros) z = (qzeros[grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 0xFu;
-      }
+      uint32_t sb = 0;
+      if (n < N && t < KT) sb = scales[((128 * t + (v % U) * span) / G) * N + n];
       sv[e >> 1] |= sb << (16 * (e & 1));
-      zw |= z << (4 * e);
     }
     *(u32x4_t*)(scales_r + (idx * U + w) * 8) = sv;
-    if (zeros_r) zeros_r[idx * U + w] = zw;
+  }
+  if (!zeros_r) return;
+  for (int w = 0; w < nzw; ++w) {
+    uint32_t zv = 0;
+    for (int f = 0; f < per; ++f) {
+      const int64_t v = g * 8 * U + per * w + f;
+      const int64_t t = v / U;
+      if (n < N && t < KT)
+        zv |= canon_zero(qzeros, N, (128 * t + (v % U) * span) / G, n, bits) << (zw * f);
+    }
+    zeros_r[idx * nzw + w] = zv;
   }
 }
 
 hipError_t launch_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
-                         const int32_t* perm, int64_t K, int64_t N, int G, void* codes_r,
-                         void* scales_r, void* zeros_r, hipStream_t stream) {
+                         const int32_t* perm, int64_t K, int64_t N, int G, int bits,
+                         void* codes_r, void* scales_r, void* zeros_r, hipStream_t stream) {
   const int64_t NP = ceil_div(N, 64), KT = K / 128;
-  const int64_t words = NP * KT * 1024;
+  const int64_t words = NP * KT * 4 * 64 * tile_lane_dwords(bits);
   hipLaunchKernelGGL(repack_codes_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0,
-                     stream, (const uint32_t*)qweight, perm, K, N, NP, (uint32_t*)codes_r);
+                     stream, (const uint32_t*)qweight, perm, K, N, NP, bits,
+                     (uint32_t*)codes_r);
   const int64_t metas = NP * ceil_div(KT, 8) * 64;
   hipLaunchKernelGGL(repack_meta_kernel, dim3((unsigned)ceil_div(metas, 256)), dim3(256), 0,
-                     stream, scales, (const uint32_t*)qzeros, K, N, NP, G, (uint16_t*)scales_r,
-                     (uint32_t*)zeros_r);
+                     stream, scales, (const uint32_t*)qzeros, K, N, NP, G, bits,
+                     (uint16_t*)scales_r, (uint32_t*)zeros_r);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ dequant exports --
-// INT4: one thread per repacked word, through the same dequant_word routine
-// the GEMM kernels use; writes 8 consecutive elements (16 bytes) of w [N, K].
-template <int DT>
+// b-bit integer codes: one thread per (tile, lane, step j): the lane's codes
+// and the unit's scale and zero through the same dequant_step routine the
+// GEMM kernels use; writes 8 consecutive elements (16 bytes) of w [N, K].
+template <int DT, int BITS>
 __global__ void __launch_bounds__(256)
-dequant_int4_kernel(const uint32_t* __restrict__ codes_r, const uint16_t* __restrict__ scales_r,
-                    const uint32_t* __restrict__ zeros_r, int64_t K, int64_t N, int64_t NP,
-                    int G, uint16_t* __restrict__ w_out) {
+dequant_int_kernel(const uint8_t* __restrict__ codes_r, const uint16_t* __restrict__ scales_r,
+                   const uint32_t* __restrict__ zeros_r, int64_t K, int64_t N, int64_t NP,
+                   int G, uint16_t* __restrict__ w_out) {
+  constexpr int kTile = 256 * BITS, kZW = zero_field_bits(BITS), per = 32 / kZW;
   const int64_t KT = K / 128, KT8 = ceil_div(KT, 8);
-  const int U = units_per_tile(G);
+  const int U = units_per_tile(G), nzw = 8 * U / per;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= NP * KT * 1024) return;
   const int j = (int)(idx & 3);
@@ -243,29 +327,52 @@ dequant_int4_kernel(const uint32_t* __restrict__ codes_r, const uint16_t* __rest
   const int i = lane & 15;
   const int64_t n = p * 64 + c * 16 + i;
   if (n >= N) return;
+  const uint8_t* tile = codes_r + (pt * 4 + c) * kTile;
+  Codes<BITS> w;
+  if constexpr (BITS == 4) {
+    w.w = *(const u32x4_t*)(tile + lane * 16);
+  } else if constexpr (BITS == 3) {
+    const uint32_t* q = (const uint32_t*)(tile + lane * 12);
+    w.w = u32x3_t{q[0], q[1], q[2]};
+  } else {
+    w.lo = *(const u32x4_t*)(tile + lane * 16);
+    w.hi = *(const u32x4_t*)(tile + 1024 + lane * 16);
+  }
   const int64_t meta = ((p * KT8 + (t >> 3)) * 4 + c) * 16 + i;
-  const int r = (int)(t & 7) * U + j * U / 4;  // unit of word j within the run
-  const uint32_t z = zeros_r ? (zeros_r[meta * U + (r >> 3)] >> (4 * (r & 7))) & 0xFu : 8u;
+  const int r = (int)(t & 7) * U + j * U / 4;  // unit of step j within the run
+  const uint32_t z = zeros_r ? (zeros_r[meta * nzw + r / per] >> (kZW * (r % per))) &
+                                   ((1u << kZW) - 1u)
+                             : (1u << (BITS - 1));
   QParam<DT> qp;
   qp.set(scales_r[meta * 8 * U + r], z);
-  const auto v = dequant_word(codes_r[idx], qp);
+  const auto v = dequant_step<DT>(w, j, qp);
   const int64_t k = t * 128 + j * 32 + (lane >> 4) * 8;
   *(u32x4_t*)(w_out + n * K + k) = __builtin_bit_cast(u32x4_t, v);
 }
 
-hipError_t launch_dequant_int4(const void* codes_r, const void* scales_r, const void* zeros_r,
-                               int64_t K, int64_t N, int G, int dtype, void* w_out,
-                               hipStream_t stream) {
+template <int DT>
+static void launch_dequant_int_dt(const void* codes_r, const void* scales_r, const void* zeros_r,
+                                  int64_t K, int64_t N, int G, int bits, void* w_out,
+                                  hipStream_t stream) {
   const int64_t NP = ceil_div(N, 64), KT = K / 128;
   const dim3 grid((unsigned)ceil_div(NP * KT * 1024, 256));
+  auto args = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, (const uint8_t*)codes_r,
+                       (const uint16_t*)scales_r, (const uint32_t*)zeros_r, K, N, NP, G,
+                       (uint16_t*)w_out);
+  };
+  if (bits == 4) args(dequant_int_kernel<DT, 4>);
+  else if (bits == 3) args(dequant_int_kernel<DT, 3>);
+  else args(dequant_int_kernel<DT, 8>);
+}
+
+hipError_t launch_dequant_int(const void* codes_r, const void* scales_r, const void* zeros_r,
+                              int64_t K, int64_t N, int G, int bits, int dtype, void* w_out,
+                              hipStream_t stream) {
   if (dtype == DT_F16)
-    hipLaunchKernelGGL(dequant_int4_kernel<DT_F16>, grid, dim3(256), 0, stream,
-                       (const uint32_t*)codes_r, (const uint16_t*)scales_r,
-                       (const uint32_t*)zeros_r, K, N, NP, G, (uint16_t*)w_out);
+    launch_dequant_int_dt<DT_F16>(codes_r, scales_r, zeros_r, K, N, G, bits, w_out, stream);
   else
-    hipLaunchKernelGGL(dequant_int4_kernel<DT_BF16>, grid, dim3(256), 0, stream,
-                       (const uint32_t*)codes_r, (const uint16_t*)scales_r,
-                       (const uint32_t*)zeros_r, K, N, NP, G, (uint16_t*)w_out);
+    launch_dequant_int_dt<DT_BF16>(codes_r, scales_r, zeros_r, K, N, G, bits, w_out, stream);
   return hipGetLastError();
 }
 

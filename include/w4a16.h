@@ -236,6 +236,59 @@ int w4a16_gemm_xscale(const void* x, const void* x_scale, const void* codes_r,
 int w4a16_dequant(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
                   int64_t N, int32_t group_size, int32_t dtype, void* w_out, void* stream);
 
+/* ------------------------------------------------- 3- and 8-bit integers --- */
+
+/*
+ * The INT4 entry points above for b-bit integer codes, b = `bits` in
+ * {3, 4, 8} (b = 4 is the entry point without the suffix): weight-only
+ * quantization at 8 bits trades little accuracy for half the 4-bit saving,
+ * at 3 bits more saving for visible loss ([P3] §2.3; the GPTQ-3bit and
+ * AWQ-3bit rows of [P1] §4.1; [P4] "量化效果PK", 3-bit codes with groups of
+ * 128, and "部署实战", the bit-width option).  Everything else -- group
+ * sizes, symmetric codes (implicit zero 2^(b-1)), act-order, AWQ input
+ * scales, workspace, dtypes, errors -- is as for 4 bits.  bits outside
+ * {3, 4, 8}: W4A16_ERR_UNSUPPORTED.
+ *
+ * Canonical tensors (GPTQ style, original column order): codes in
+ * [0, 2^b - 1]; qweight int32 [K b / 32, N], qzeros int32 [K/G, N b / 32]
+ * (asymmetric only).  Each run of 32 consecutive codes along K (qweight) or
+ * N (qzeros) is a little-endian bit stream of b words, code e at bits
+ * [b e, b e + b); at b = 3 codes 10 and 21 of a run straddle words, and a
+ * call that reads or writes 3-bit qzeros needs N % 32 == 0
+ * (W4A16_ERR_INVALID_ARG).  RTN as above with 2^b - 1 levels: s =
+ * fp16(fp32(max - min) / (2^b - 1)), or s = fp16(fp32(max |w|) /
+ * (2^(b-1) - 1)) for symmetric codes.
+ *
+ * Repacked layout: the tiles of the INT4 layout with each lane's 32 codes in
+ * b-bit form (a column tile's K tile is 256 b bytes):
+ *   b = 8  uint8 [NP][KT][4][2][64][16]: code (j, e) of lane l in half j >> 1,
+ *          dword 2 (j & 1) + (e >> 2) of the lane's 16 bytes, byte slot
+ *          ((e & 3) >> 1) + 2 (e & 1).
+ *   b = 3  uint8 [NP][KT][4][64][12]: the low 2 bits of code (j, e) at bit
+ *          16 (e & 1) + 2 (4 (j & 1) + (e >> 1)) of dword j >> 1, its high
+ *          bit at bit 16 (e & 1) + 4 j + (e >> 1) of dword 2.
+ *   scales as for 4 bits; zeros in 4-bit fields for b = 3 (as for 4 bits) and
+ *   8-bit fields for b = 8 (uint32 [NP][KT8][4][16][2U], unit r of a run at
+ *   byte r).
+ */
+int64_t w4a16_repacked_bytes_bits(int64_t K, int64_t N, int32_t group_size, int32_t bits,
+                                  int32_t which);
+int w4a16_quantize_rtn_bits(const float* W, const int32_t* g_idx, const int32_t* perm,
+                            int64_t N, int64_t K, int32_t group_size, int32_t bits,
+                            int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
+int w4a16_repack_bits(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                      const int32_t* g_idx, int64_t K, int64_t N, int32_t group_size,
+                      int32_t bits, void* codes_r, void* scales_r, void* zeros_r, int32_t* perm,
+                      int32_t* perm_used_host, void* stream);
+int w4a16_gemm_bits(const void* x, const void* x_scale, const void* codes_r,
+                    const void* scales_r, const void* zeros_r, const int32_t* perm,
+                    int32_t group_size, int32_t bits, void* out, int64_t M, int64_t N,
+                    int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                    void* stream);
+int w4a16_dequant_bits(const void* codes_r, const void* scales_r, const void* zeros_r, int64_t K,
+                       int64_t N, int32_t group_size, int32_t bits, int32_t dtype, void* w_out,
+                       void* stream);
+
 /* ------------------------------------------------------------------- NF4 --- */
 
 /*

@@ -152,3 +152,38 @@ def test_library_codebook_equals_oracle_codebook():
     assert L.nf4_codebook(ctypes.cast(buf, ctypes.c_void_p)) == 0
     got = np.frombuffer(buf, dtype=np.float32)
     assert np.array_equal(got.view(np.uint32), nf4.nf4_codebook().view(np.uint32))
+
+
+def test_bits_entry_points_validation_without_gpu():
+    rb = L.w4a16_repacked_bytes_bits
+    # 256 b bytes per 16 x 128 tile; scales as at 4 bits; zeros twice as wide at 8 bits
+    for bits in (3, 4, 8):
+        assert rb(4096, 4096, 128, bits, 0) == 4096 * 4096 * bits // 8
+        assert rb(4096, 4096, 128, bits, 1) == L.w4a16_repacked_bytes(4096, 4096, 128, 1)
+    assert rb(4096, 4096, 128, 8, 2) == 2 * L.w4a16_repacked_bytes(4096, 4096, 128, 2)
+    assert rb(4096, 4096, 128, 3, 2) == L.w4a16_repacked_bytes(4096, 4096, 128, 2)
+    assert rb(4096, 4096, 32, 8, 2) == 8 * L.w4a16_repacked_bytes(4096, 4096, 128, 2)
+    for bits in (0, 2, 5, 16):
+        assert rb(4096, 4096, 128, bits, 0) == -1
+    used = ctypes.c_int32(0)
+    # unsupported widths, before anything else is looked at
+    assert L.w4a16_repack_bits(FAKE, FAKE, FAKE, NULL, 512, 256, 128, 5, FAKE, FAKE, FAKE, NULL,
+                               ctypes.byref(used), NULL) == 2
+    assert L.w4a16_quantize_rtn_bits(FAKE, NULL, NULL, 256, 512, 128, 2, FAKE, FAKE, FAKE,
+                                     NULL) == 2
+    assert L.w4a16_gemm_bits(FAKE, NULL, FAKE, FAKE, FAKE, NULL, 128, 6, FAKE, 1, 256, 512, 0,
+                             NULL, 0, NULL) == 2
+    assert L.w4a16_dequant_bits(FAKE, FAKE, FAKE, 512, 256, 128, 7, 0, FAKE, NULL) == 2
+    # 3-bit zeros pack in runs of 32 columns: N = 200 is refused with zeros ...
+    assert L.w4a16_repack_bits(FAKE, FAKE, FAKE, NULL, 512, 200, 128, 3, FAKE, FAKE, FAKE, NULL,
+                               ctypes.byref(used), NULL) == 1
+    assert L.w4a16_quantize_rtn_bits(FAKE, NULL, NULL, 200, 512, 128, 3, FAKE, FAKE, FAKE,
+                                     NULL) == 1
+    # ... and a symmetric repack without zeros_r passes validation up to the
+    # pointer checks (misaligned codes_r here, so nothing is launched)
+    assert L.w4a16_repack_bits(FAKE, FAKE, NULL, NULL, 512, 200, 128, 3, ODD, FAKE, NULL, NULL,
+                               ctypes.byref(used), NULL) == 3
+    # the 8-bit GEMM validates like the 4-bit one
+    assert L.w4a16_workspace_bytes(64, 5120, 5120, 128) > 0        # split K: partials
+    assert L.w4a16_gemm_bits(FAKE, NULL, FAKE, FAKE, FAKE, NULL, 128, 8, FAKE, 64, 5120, 5120, 0,
+                             NULL, 0, NULL) == 5
