@@ -58,10 +58,10 @@ def kernel_name(M, K, N):
     if M <= 4:
         staged = kb(M * K * 2) + kb(K * 4)
         if staged <= 32 * 1024 and ((N + 15) // 16) * staged <= 12 << 20:
-            return "int4_decode_kernel<f16, MT=1, xgather>"
-        return "int4_decode_kernel<f16, MT=1, packed>"
+            return "intb_decode_kernel<f16, MT=1, xgather, 4-bit>"
+        return "intb_decode_kernel<f16, MT=1, packed, 4-bit>"
     mt = 1 if M <= 16 else (2 if M <= 32 else 4)
-    return "int4_decode_kernel<f16, MT=%d, full>" % mt
+    return "intb_decode_kernel<f16, MT=%d, full, 4-bit>" % mt
 
 
 def parse():
@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-nf4", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run each decode call of the workload once, then a 256 MiB device copy "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), and exit")
@@ -295,6 +296,8 @@ def main():
         result["prefill"] = bench_prefill(L, timer, sptr)
     if not args.no_nf4:
         result["nf4"] = bench_nf4(L, timer, sptr)
+    if not args.no_variants:
+        result["variants"] = bench_variants()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs, outs)
     print(json.dumps(result), flush=True)
@@ -302,7 +305,7 @@ def main():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "int4_decode_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_only_gemm_amd", "csrc", f)
-                  for f in ("gemm.hip", "common.h")]
+                  for f in ("gemm.hip", "decode.h", "common.h")]
 
 
 def kernel_source_hash():
@@ -436,12 +439,99 @@ def bench_prefill(L, timer, sptr, M=2048):
     tot_t = sum(q["us"] for q in pts) * 1e-6
     return {"workload": "Qwen2.5-32B-shaped prefill, int4 G=128, bf16 x with 1% outlier "
                         "channels x20, M=2048",
-            "kernel": "int4_prefill_kernel<bf16>",
+            "kernel": "wq_prefill_kernel<bf16, INT 4-bit>",
             "tflops_all_shapes": round(tot_fl / tot_t / 1e12, 1),
             "roofline": {"bound": "mfma", "achieved": best["tflops"],
                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(best["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                          "shape": [best["M"], best["K"], best["N"]]},
+            "points": pts}
+
+
+VARIANTS = [  # (label, bits, group size (-1: per-channel), symmetric, AWQ input scales)
+    ("int4 G=128 asym", 4, 128, False, False),
+    ("int4 G=64 sym", 4, 64, True, False),
+    ("int4 G=32 asym", 4, 32, False, False),
+    ("int4 per-channel sym", 4, -1, True, False),
+    ("int4 G=128 asym + AWQ input scales", 4, 128, False, True),
+    ("int3 G=128 asym", 3, 128, False, False),
+    ("int8 G=128 asym", 8, 128, False, False),
+]
+
+
+def variant_weight_bytes(K, N, bits, G, sym):
+    """Algorithmic bytes of a weight: codes + fp16 scales + zero fields per
+    group (per 128-input tile for G >= 128: the repacked meta repeats per tile)."""
+    g = min(K if G == -1 else G, 128)
+    zbits = 8 if bits == 8 else 4
+    return K * N * bits // 8 + 2 * N * K // g + (0 if sym else N * K // g * zbits // 8)
+
+
+def bench_variants(K=5120, N=55296, Ms=(1, 2048)):
+    """The format variants on the 5120 x 55296 layer (bf16 activations): group
+    sizes, symmetric codes, 3- and 8-bit codes and AWQ input scales.  Whole
+    calls (any preparation pass included) timed by HIP-graph replay of 10
+    calls over rotating weight copies (>= 512 MB)."""
+    import torch
+    import bit_weight_only_gemm_amd as w4
+    from bit_weight_only_gemm_amd import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    W = torch.from_numpy(synth.weights("C6/W/%dx%d" % (K, N), N, K)).to(dev)
+    s_awq = torch.from_numpy(synth.to_bf16_bits(synth.awq_scales("C6/s/%d" % K, K)[None, :])[0]
+                             .view(np.int16)).view(torch.bfloat16).to(dev)
+    pts = []
+    for label, bits, G, sym, xs in VARIANTS:
+        qw, sc, qz = w4.w4a16_quantize_rtn(W, G, sym=sym, bits=bits)
+        p0 = w4.w4a16_repack(qw, sc, qz, None, G, bits=bits)
+        del qw, sc, qz
+        wb = variant_weight_bytes(K, N, bits, G, sym)
+        R = max(2, int(np.ceil(512e6 / wb)))
+        ps = [p0] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in p0.items()}
+                     for _ in range(R - 1)]
+        for M in Ms:
+            x32 = synth.activations("C6/x/%d" % M, M, K)
+            x = torch.from_numpy(synth.to_bf16_bits(x32).view(np.int16)).view(torch.bfloat16).to(dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = w4.workspace(w4.w4a16_workspace_bytes(M, N, K, G), dev)
+
+            def call(p):
+                if xs:
+                    w4.w4a16_gemm_xscale(x, s_awq, p, out=y, workspace=ws)
+                else:
+                    w4.w4a16_gemm(x, p, out=y, workspace=ws)
+            for r in range(3):
+                call(ps[r % R])
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(10):
+                    call(ps[r % R])
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / 50
+            pt = {"variant": label, "bits": bits, "group_size": G, "symmetric": sym,
+                  "awq_input_scales": xs, "M": M, "us": round(t * 1e6, 2)}
+            if M >= 1024:
+                fl = 2.0 * M * N * K
+                pt.update(tflops=round(fl / t / 1e12, 1),
+                          pct_mfma=round(100 * fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 1))
+            else:
+                byt = wb + 2 * M * K + 2 * M * N
+                pt.update(weight_bytes=wb, GBps=round(byt / t / 1e9, 1),
+                          pct_hbm=round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1))
+            pts.append(pt)
+            del x, y, ws, g
+        del ps, p0
+        torch.cuda.empty_cache()
+    return {"workload": "5120 x 55296 layer, bf16 activations ~N(0,1), RTN weights of each "
+                        "format; whole calls by HIP-graph replay",
             "points": pts}
 
 
@@ -482,7 +572,7 @@ def bench_nf4(L, timer, sptr, K=8192, N=28672):
                     "weight_GBps": round(wb / t / 1e9, 1),
                     "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1)})
     return {"workload": "NF4 28672x8192, blocksize 64, double quant 256, bf16",
-            "kernel": "nf4_decode_kernel<bf16> (M=1), int4_prefill_kernel<bf16, NF4> (M=32)",
+            "kernel": "nf4_decode_kernel<bf16> (M=1), wq_prefill_kernel<bf16, NF4> (M=32)",
             "points": pts}
 
 
