@@ -87,12 +87,14 @@ template <> struct QParam<DT_BF16> {
   half2_t hz;  // (1024 + z) in both halves
   float sf;    // s
   float nz;    // -0.0, opaque to the compiler so that the fma below stays an fma
+  float nc;    // -(1024 + z) s, exact in fp32 (an 11-bit integer times an 11-bit significand)
   uint32_t magic;  // 0x64006400 in a register, so the nibble insert is one v_and_or_b32
   __device__ __forceinline__ void set(uint32_t scale_bits, uint32_t z) {
     magic = opaque_magic();
     uint32_t hzb = 0x6400u | z;
     hz = __builtin_bit_cast(half2_t, hzb | (hzb << 16));
     sf = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits);
+    nc = -(float)(1024u + z) * sf;
     uint32_t m;
     asm("v_mov_b32 %0, 0x80000000" : "=v"(m));
     nz = __builtin_bit_cast(float, m);
@@ -103,37 +105,55 @@ template <> struct QParam<DT_BF16> {
 // 16-bit halves of f (codes < 1024): 0x6400 | q is the fp16 value 1024 + q,
 // so (1024 + q) - (1024 + z) = q - z exactly, then one rounding of (q - z) s.
 // Returned as two packed 16-bit values.
+//
+// ZS (zero sign): the bf16 form below keeps the IEEE sign of an exactly-zero
+// product ((q - z) s = -0 when q == z and s is negative or -0).  The GEMM
+// kernels use ZS = false, a cheaper form whose only difference is +0 there:
+// their fp32 accumulators start at +0, and a sum of signed zeros with a +0
+// term is +0, so no output can tell the two apart.  The dequant export, which
+// is compared bit for bit, uses ZS = true.
+template <bool ZS = true>
 __device__ __forceinline__ uint32_t dequant_fields(uint32_t f, const QParam<DT_F16>& p) {
   const uint32_t t = f | p.magic;                                     // (1024+q_lo, 1024+q_hi)
   const half2_t r = (__builtin_bit_cast(half2_t, t) - p.hz) * p.s2;  // exact sub, one rounding
   return __builtin_bit_cast(uint32_t, r);
 }
 
+template <bool ZS = true>
 __device__ __forceinline__ uint32_t dequant_fields(uint32_t f, const QParam<DT_BF16>& p) {
-  // (q - z) exactly in fp16 as on the fp16 path, then the exact fp32 product
-  // with s as fma(q - z, s, -0) (v_fma_mix widens the fp16 half in place;
-  // adding -0 keeps every signed zero of the plain product) and the one
-  // rounding to bf16.
   const uint32_t t = f | p.magic;
-  const half2_t d = __builtin_bit_cast(half2_t, t) - p.hz;
-  const bf16x2_t r = {(__bf16)__builtin_fmaf((float)d[0], p.sf, p.nz),
-                      (__bf16)__builtin_fmaf((float)d[1], p.sf, p.nz)};
-  return __builtin_bit_cast(uint32_t, r);
+  if constexpr (ZS) {
+    // (q - z) exactly in fp16 as on the fp16 path, then the exact fp32
+    // product with s as fma(q - z, s, -0) (v_fma_mix widens the fp16 half in
+    // place; adding -0 keeps every signed zero of the plain product) and the
+    // one rounding to bf16.
+    const half2_t d = __builtin_bit_cast(half2_t, t) - p.hz;
+    const bf16x2_t r = {(__bf16)__builtin_fmaf((float)d[0], p.sf, p.nz),
+                        (__bf16)__builtin_fmaf((float)d[1], p.sf, p.nz)};
+    return __builtin_bit_cast(uint32_t, r);
+  } else {
+    // (1024 + q) s - (1024 + z) s in one fma: both products are exact in fp32
+    // and so is their difference (q - z) s, which is then rounded once to bf16
+    const half2_t th = __builtin_bit_cast(half2_t, t);
+    const bf16x2_t r = {(__bf16)__builtin_fmaf((float)th[0], p.sf, p.nc),
+                        (__bf16)__builtin_fmaf((float)th[1], p.sf, p.nc)};
+    return __builtin_bit_cast(uint32_t, r);
+  }
 }
 
 // Element pair i (elements 2i, 2i + 1, nibble slots i and i + 4) of one
 // repacked 4-bit word.
-template <class QP>
+template <bool ZS = true, class QP>
 __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QP& p) {
-  return dequant_fields((w >> (4 * i)) & 0x000F000Fu, p);
+  return dequant_fields<ZS>((w >> (4 * i)) & 0x000F000Fu, p);
 }
 
 // Exact dequantization of one repacked 4-bit word into an 8-element MFMA operand.
-template <int DT>
+template <int DT, bool ZS = true>
 __device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const QParam<DT>& p) {
   u32x4_t r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = dequant_pair(w, i, p);
+  for (int i = 0; i < 4; ++i) r[i] = dequant_pair<ZS>(w, i, p);
   return __builtin_bit_cast(typename Op<DT>::vec, r);
 }
 
@@ -160,24 +180,24 @@ __host__ __device__ constexpr uint32_t sym_zero_xor(int bits) {
 }
 
 // The 8-element B operand of MFMA step j (0..3) from a lane's codes.
-template <int DT>
+template <int DT, bool ZS = true>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<4>& c, int j,
                                                              const QParam<DT>& p) {
-  return dequant_word<DT>(c.w[j], p);
+  return dequant_word<DT, ZS>(c.w[j], p);
 }
-template <int DT>
+template <int DT, bool ZS = true>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<8>& c, int j,
                                                              const QParam<DT>& p) {
   const u32x4_t h = (j >> 1) ? c.hi : c.lo;
   const uint32_t a = h[2 * (j & 1)], b = h[2 * (j & 1) + 1];
   u32x4_t r;
-  r[0] = dequant_fields(a & 0x00FF00FFu, p);
-  r[1] = dequant_fields((a >> 8) & 0x00FF00FFu, p);
-  r[2] = dequant_fields(b & 0x00FF00FFu, p);
-  r[3] = dequant_fields((b >> 8) & 0x00FF00FFu, p);
+  r[0] = dequant_fields<ZS>(a & 0x00FF00FFu, p);
+  r[1] = dequant_fields<ZS>((a >> 8) & 0x00FF00FFu, p);
+  r[2] = dequant_fields<ZS>(b & 0x00FF00FFu, p);
+  r[3] = dequant_fields<ZS>((b >> 8) & 0x00FF00FFu, p);
   return __builtin_bit_cast(typename Op<DT>::vec, r);
 }
-template <int DT>
+template <int DT, bool ZS = true>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<3>& c, int j,
                                                              const QParam<DT>& p) {
   const uint32_t lo = c.w[j >> 1], hi = c.w[2];
@@ -186,7 +206,7 @@ __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<3>& c, 
   for (int i = 0; i < 4; ++i) {
     const uint32_t f = ((lo >> (8 * (j & 1) + 2 * i)) & 0x00030003u) |
                        (((hi >> (4 * j + i)) & 0x00010001u) << 2);
-    r[i] = dequant_fields(f, p);
+    r[i] = dequant_fields<ZS>(f, p);
   }
   return __builtin_bit_cast(typename Op<DT>::vec, r);
 }

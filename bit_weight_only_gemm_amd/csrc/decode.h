@@ -154,7 +154,7 @@ struct IntW {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (j * U % 4 == 0) unit_param(m, s * U + j * U / 4, qp);  // a new unit
-      b[j] = dequant_step<DT>(w, j, qp);
+      b[j] = dequant_step<DT, false>(w, j, qp);
     }
   }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }

@@ -233,7 +233,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
         QParam<DT> q;
         q.set((sc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
               (zz[g] >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
-        return dequant_step<DT>(cw[g][s & 1], s >> 1, q);
+        return dequant_step<DT, false>(cw[g][s & 1], s >> 1, q);
       } else {
         const uint32_t w = cw[g][s >> 2].w[s & 3];
         vec v;
