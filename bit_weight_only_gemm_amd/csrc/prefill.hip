@@ -35,10 +35,17 @@ namespace w4a16 {
 // Rows per workgroup for M, and the split of K that fills the GPU best: a
 // simple model of the call time (rounds of workgroups on 256 CUs x K tiles per
 // workgroup x per-tile MFMA time, plus the partials' round trip through HBM).
+//
+// For M > 128, when 256-row tiles need no split of K, 192-row tiles are taken
+// instead if they finish in fewer tile-times: a 192-row workgroup takes about
+// 0.83 of a 256-row one per K tile (measured on MI355X), and the smaller tile
+// fills a round that 256-row tiles leave partly idle -- e.g. 220 instead of
+// 160 workgroups on a 5120-column layer at M = 2048 (17 % faster there).
 PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K) {
   PrefillPlan pl;
   pl.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
-  const int64_t tiles = ceil_div(ceil_div(N, 64), (int64_t)PF_WAVES) * ceil_div(M, (int64_t)pl.bm);
+  const int64_t cols = ceil_div(ceil_div(N, 64), (int64_t)PF_WAVES);
+  const int64_t tiles = cols * ceil_div(M, (int64_t)pl.bm);
   const int64_t KT = K / 128;
   const double t_tile = 3.4e-6 * pl.bm / 256.0;  // one K tile of a workgroup
   double best = 0;
@@ -50,6 +57,11 @@ PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K) {
       best = t;
       pl.splits = S;
     }
+  }
+  if (pl.bm == 256 && pl.splits == 1) {
+    const double r256 = (double)ceil_div(tiles, (int64_t)256);
+    const double r192 = (double)ceil_div(cols * ceil_div(M, (int64_t)192), (int64_t)256);
+    if (r192 * 0.83 < r256 * 0.95) pl.bm = 192;
   }
   return pl;
 }
