@@ -49,12 +49,15 @@ def call_bytes(M, K, N):
 
 
 def kernel_name(M, K, N):
-    """Decode-kernel instantiation the library picks for an act-order call
-    with M rows (f16).  Mirrors its rule: M <= 4 rows are gathered in the
-    kernel when the staged rows + permutation take at most 32 KB per
-    workgroup and 12 MiB over the N/16 workgroups, else a preparation pass
-    permutes them first."""
+    """Kernel instantiation the library picks for an act-order call with M
+    rows (f16).  Mirrors its rules: the large-M kernel from 32 rows (12 on
+    layers of 24 Mi weights, 5 on layers of 100 Mi weights); otherwise the
+    decode kernel, where M <= 4 rows are gathered in the kernel when the
+    staged rows + permutation take at most 32 KB per workgroup and 12 MiB over
+    the N/16 workgroups, else a preparation pass permutes them first."""
     kb = lambda b: (b + 1023) // 1024 * 1024
+    if M >= 32 or (M >= 12 and N * K >= 24 << 20) or (M >= 5 and N * K >= 100 << 20):
+        return "wq_prefill_kernel<f16, INT 4-bit>"      # the large-M kernel
     if M <= 4:
         staged = kb(M * K * 2) + kb(K * 4)
         if staged <= 32 * 1024 and ((N + 15) // 16) * staged <= 12 << 20:

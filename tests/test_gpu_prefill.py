@@ -1,7 +1,7 @@
 """Parity of the large-M (prefill) INT4 kernel with the oracle.
 
-w4a16_gemm switches to the LDS-staged kernel for M >= 32 rows, or 12 on big
-layers (64-, 128- or
+w4a16_gemm switches to the LDS-staged kernel for M >= 32 rows, 12 on layers
+of 24 Mi weights and 5 on layers of 100 Mi weights (64-, 128-, 192- or
 256-row workgroup tiles, K split over workgroups with an ordered reduction of
 fp32 partials when that fills the GPU better); these cases cover several
 workgroup tiles, ragged row blocks, a panel count that is not a multiple of 4
@@ -138,3 +138,16 @@ def test_big_layer_m16_uses_large_m_kernel_sampled_columns():
     cols = np.arange(0, N, 97)
     wd = oracle_int4_rows(W, gi, cols, "bf16")
     assert compare_gemm(y, xb, wd, "bf16", cols=cols) <= TOL
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(5, 20480, 5120, "f16"), (12, 11008, 4096, "bf16"),
+                                         (11, 11008, 4096, "f16")])
+def test_kernel_crossover_rows_act_order_sampled_columns(M, N, K, dtype):
+    # the fewest rows that take the large-M kernel on a 100 Mi-weight layer
+    # (5) and on a 43 Mi-weight layer (12), and one row fewer on the latter
+    # (the decode kernel), act-order; every 61st output column
+    say("crossover", M, N, K, dtype)
+    y, xb, W, gi, _ = _gemm("gpu/pf/cross/%d" % M, M, N, K, dtype, act=True)
+    cols = np.arange(3, N, 61)
+    wd = oracle_int4_rows(W, gi, cols, dtype)
+    assert compare_gemm(y, xb, wd, dtype, cols=cols) <= TOL
