@@ -50,13 +50,16 @@ def call_bytes(M, K, N):
 
 def kernel_name(M, K, N):
     """Kernel instantiation the library picks for an act-order call with M
-    rows (f16).  Mirrors its rules: the large-M kernel from 32 rows (12 on
-    layers of 24 Mi weights, 5 on layers of 100 Mi weights); otherwise the
+    rows (f16).  Mirrors its rules: the large-M kernel from 32 rows (5 on
+    layers of 100 Mi weights; 16 on layers of 24 Mi weights with N >= 5120,
+    else 24); otherwise the
     decode kernel, where M <= 4 rows are gathered in the kernel when the
     staged rows + permutation take at most 32 KB per workgroup and 12 MiB over
     the N/16 workgroups, else a preparation pass permutes them first."""
     kb = lambda b: (b + 1023) // 1024 * 1024
-    if M >= 32 or (M >= 12 and N * K >= 24 << 20) or (M >= 5 and N * K >= 100 << 20):
+    w = N * K
+    if (M >= 32 or (w >= 100 << 20 and M >= 5)
+            or (w >= 24 << 20 and M >= (16 if N >= 5120 else 24))):
         return "wq_prefill_kernel<f16, INT 4-bit>"      # the large-M kernel
     if M <= 4:
         staged = kb(M * K * 2) + kb(K * 4)

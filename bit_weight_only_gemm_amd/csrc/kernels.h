@@ -61,14 +61,20 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
                             int64_t workspace_bytes, hipStream_t stream);
 // Whether w4a16_gemm runs the LDS-staged large-M kernel (activations shared
 // by a workgroup's 256 columns through LDS) rather than the skinny decode
-// kernel: from 32 rows, from 12 rows on layers of 24 Mi weights and more, and
-// from 5 rows on layers of 100 Mi weights and more (measured crossovers on
-// MI355X: e.g. 4096 x 11008 at M = 16 takes 15.7 us in the large-M kernel and
-// 19.0 in the decode kernel, 27648 x 5120 at M = 8 28.0 and 39.0; 4096 x 4096
-// stays faster in the decode kernel through M = 24).
+// kernel.  The decode kernel's time grows with every 16 rows; the large-M
+// kernel's hardly changes with M below 32 rows but carries the fixed cost of
+// its split-K reduction launch.  Measured whole-call crossovers on MI355X
+// (HIP graphs of calls over weight sets larger than the caches): from 5 rows
+// on layers of 100 Mi weights and more, from 16 rows on layers of 24 Mi weights
+// and more with N >= 5120 (4096 x 11008 at M = 16: 18.6 us against 20.9), from
+// 24 rows on such layers with fewer columns (11008 x 4096: decode faster
+// through M = 16), and from 32 rows otherwise.
 inline bool use_prefill(int64_t M, int64_t N, int64_t K) {
-  return M >= 32 || (M >= 12 && N * K >= (int64_t)24 << 20) ||
-         (M >= 5 && N * K >= (int64_t)100 << 20);
+  if (M >= 32) return true;
+  const int64_t w = N * K;
+  if (w >= (int64_t)100 << 20) return M >= 5;
+  if (w >= (int64_t)24 << 20) return M >= (N >= 5120 ? 16 : 24);
+  return false;
 }
 void launch_int_prefill(const void* x, const void* codes_r, const void* scales_r,
                         const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,

@@ -12,7 +12,7 @@ namespace w4a16 {
 
 constexpr int PF_WAVES = 4;                  // waves per workgroup
 constexpr int PF_ROWB = 256;                 // LDS bytes of one row of a K tile
-// Rows per workgroup BM in {64, 128, 192, 256}: BM / 32 MFMA row tiles per wave,
+// Rows per workgroup BM in {32, 64, 128, 192, 256}: BM / 32 MFMA row tiles per wave,
 // an LDS stage of BM x 256 bytes, BM / 16 16-byte activation loads per lane.
 
 #ifndef W4A16_PF_DMA_STEPS
@@ -406,7 +406,10 @@ static void launch_prefill_dt(const void* x, const void* codes_r, const void* sc
                               int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const PrefillPlan pl = plan_prefill(M, N, K);
   float* part = (float*)ws;
-  if (pl.bm == 64)
+  if (pl.bm == 32)
+    launch_prefill_bm<DT, 32, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
+                                      N, K, stream);
+  else if (pl.bm == 64)
     launch_prefill_bm<DT, 64, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
                                       N, K, stream);
   else if (pl.bm == 128)

@@ -43,7 +43,7 @@ namespace w4a16 {
 // 160 workgroups on a 5120-column layer at M = 2048 (17 % faster there).
 PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K) {
   PrefillPlan pl;
-  pl.bm = M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+  pl.bm = M <= 32 ? 32 : M <= 64 ? 64 : (M <= 128 ? 128 : 256);
   const int64_t cols = ceil_div(ceil_div(N, 64), (int64_t)PF_WAVES);
   const int64_t tiles = cols * ceil_div(M, (int64_t)pl.bm);
   const int64_t KT = K / 128;

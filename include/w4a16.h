@@ -172,9 +172,9 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
  * Workspace bytes w4a16_gemm and w4a16_gemm_xscale need at this shape
  * (covering calls with a column permutation and with input scales): room for
  * the prepared activations M*K*2 where a separate pass writes x[:, perm]
- * and/or x / s, plus the fp32 partials S*M*N*4 of the large-M kernel (M >= 32,
- * M >= 12 on layers of 24 Mi weights and more, M >= 5 on layers of 100 Mi
- * weights and more) when it splits K over S workgroups.  A given call may need less, or nothing: no pass runs where
+ * and/or x / s, plus the fp32 partials S*M*N*4 of the large-M kernel (M >= 32;
+ * M >= 5 on layers of 100 Mi weights and more; M >= 16, or 24 when N < 5120, on
+ * layers of 24 Mi weights and more) when it splits K over S workgroups.  A given call may need less, or nothing: no pass runs where
  * the decode kernel gathers x[:, perm] and/or divides by s itself (M <= 4,
  * the rows, the permutation and the scales staged on chip: at most 32 KB per
  * workgroup and 12 MiB over its grid of N/16 workgroups); each call

@@ -1,8 +1,8 @@
 """Parity of the large-M (prefill) INT4 kernel with the oracle.
 
-w4a16_gemm switches to the LDS-staged kernel for M >= 32 rows, 12 on layers
-of 24 Mi weights and 5 on layers of 100 Mi weights (64-, 128-, 192- or
-256-row workgroup tiles, K split over workgroups with an ordered reduction of
+w4a16_gemm switches to the LDS-staged kernel for M >= 32 rows, 5 on layers
+of 100 Mi weights and 16 or 24 on layers of 24 Mi weights (32-, 64-, 128-,
+192- or 256-row workgroup tiles, K split over workgroups with an ordered reduction of
 fp32 partials when that fills the GPU better); these cases cover several
 workgroup tiles, ragged row blocks, a panel count that is not a multiple of 4
 (N = 320 -> 5 panels), act-order, split K, bf16 with outlier channels, and
@@ -140,12 +140,14 @@ def test_big_layer_m16_uses_large_m_kernel_sampled_columns():
     assert compare_gemm(y, xb, wd, "bf16", cols=cols) <= TOL
 
 
-@pytest.mark.parametrize("M,N,K,dtype", [(5, 20480, 5120, "f16"), (12, 11008, 4096, "bf16"),
-                                         (11, 11008, 4096, "f16")])
+@pytest.mark.parametrize("M,N,K,dtype", [(5, 20480, 5120, "f16"), (16, 11008, 4096, "bf16"),
+                                         (15, 11008, 4096, "f16"), (24, 4096, 11008, "bf16"),
+                                         (23, 4096, 11008, "f16")])
 def test_kernel_crossover_rows_act_order_sampled_columns(M, N, K, dtype):
-    # the fewest rows that take the large-M kernel on a 100 Mi-weight layer
-    # (5) and on a 43 Mi-weight layer (12), and one row fewer on the latter
-    # (the decode kernel), act-order; every 61st output column
+    # the fewest rows that take the large-M kernel (32-row workgroup tiles)
+    # on a 100 Mi-weight layer (5) and on 43 Mi-weight layers (16 with 11008
+    # columns, 24 with 4096), and one row fewer (the decode kernel),
+    # act-order; every 61st output column
     say("crossover", M, N, K, dtype)
     y, xb, W, gi, _ = _gemm("gpu/pf/cross/%d" % M, M, N, K, dtype, act=True)
     cols = np.arange(3, N, 61)
