@@ -157,6 +157,35 @@ __device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const Q
   return __builtin_bit_cast(typename Op<DT>::vec, r);
 }
 
+// NF4 operand of one 32-bit code word (element e in nibble e): w = round16(L[c]
+// a') with the fp32 product, L a 16-entry fp32 table in LDS.  The table byte
+// offsets 4 c of the even and odd elements are formed for all four bytes at
+// once ((w << 2) and (w >> 2) masked to 0x3C per byte), so each lookup address
+// is a single byte extract.
+template <int DT>
+__device__ __forceinline__ typename Op<DT>::vec nf4_operand(uint32_t w, const float* lut,
+                                                           float a) {
+  uint32_t lo = (w << 2) & 0x3C3C3C3Cu, hi = (w >> 2) & 0x3C3C3C3Cu;
+  // opaque to the compiler, which would otherwise fold each extract back into
+  // a shift and a mask of w
+  asm("" : "+v"(lo), "+v"(hi));
+  const char* base = (const char*)lut;
+  typename Op<DT>::vec v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float f0 = *(const float*)(base + ((lo >> (8 * j)) & 0xFFu)) * a;
+    const float f1 = *(const float*)(base + ((hi >> (8 * j)) & 0xFFu)) * a;
+    if constexpr (DT == DT_F16) {
+      v[2 * j] = (_Float16)f0;
+      v[2 * j + 1] = (_Float16)f1;
+    } else {
+      v[2 * j] = (__bf16)f0;
+      v[2 * j + 1] = (__bf16)f1;
+    }
+  }
+  return v;
+}
+
 // ---- b-bit integer codes.  One lane's codes of one K tile (32 codes: the 8
 // inputs of each of the 4 MFMA steps j) in the repacked form of each width:
 //  * 4 bits: 4 dwords, dword j = step j, nibble slot (e >> 1) + 4 (e & 1).

@@ -246,17 +246,7 @@ struct Nf4W {
       a = m.a[s];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w = w4[j];
-      typename Op<DT>::vec v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = lut[(w >> (4 * e)) & 0xFu] * a;
-        if constexpr (DT == DT_F16) v[e] = (_Float16)f;
-        else v[e] = (__bf16)f;
-      }
-      b[j] = v;
-    }
+    for (int j = 0; j < 4; ++j) b[j] = nf4_operand<DT>(w4[j], lut, a);
   }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * b + 8 * j; }
 };

@@ -235,15 +235,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
               (zz[g] >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
         return dequant_step<DT, false>(cw[g][s & 1], s >> 1, q);
       } else {
-        const uint32_t w = cw[g][s >> 2].w[s & 3];
-        vec v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float f = lut[(w >> (4 * e)) & 0xFu] * ap[g];
-          if constexpr (DT == DT_F16) v[e] = (_Float16)f;
-          else v[e] = (__bf16)f;
-        }
-        return v;
+        return nf4_operand<DT>(cw[g][s >> 2].w[s & 3], lut, ap[g]);
       }
     };
     const uint8_t* st = As + ((t - tb) & 1) * PF_STAGE;
