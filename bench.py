@@ -186,12 +186,13 @@ def main():
     # ---- timed region, part 2: the same K steps launched eagerly with HIP
     # timing events attached to every GEMM kernel's own dispatch
     # (hipExtLaunchKernel start/stop), on the stream the kernels run on.  A
-    # dispatch's start event is taken when it is queued behind the kernel
-    # before it, so a GEMM launched right after the library's permutation pass
-    # would be charged that pass's tail: calls whose kernel does not gather x
-    # itself get their activations already permuted (perm = NULL), which runs
-    # the same kernel instantiation on the same data with nothing queued in
-    # front of it.  (The step time above includes the pass.)
+    # dispatch's start event is taken when it is queued, so a kernel queued
+    # behind another one would be charged that kernel's tail: calls whose
+    # kernel does not gather x itself get their activations already permuted
+    # (perm = NULL; the same kernel instantiation on the same data without the
+    # library's permutation pass in front of it), and the stream is drained
+    # after every call, before the next one is queued.  (The step time above
+    # includes the pass and runs the calls back to back.)
     hip = ctypes.CDLL("libamdhip64.so.7")
     nper = len(calls[0])
     tcalls = []
@@ -220,6 +221,8 @@ def main():
             L.w4a16_set_timing_events(ctypes.c_void_p(ev[2 * k]), ctypes.c_void_p(ev[2 * k + 1]))
             if L.w4a16_gemm(*a) != 0:
                 raise RuntimeError("w4a16_gemm failed")
+            if hip.hipStreamSynchronize(sptr) != 0:
+                raise RuntimeError("hipStreamSynchronize failed")
     torch.cuda.synchronize()
     ms = ctypes.c_float(0.0)
     dur = np.zeros((args.steps, nper))
@@ -290,7 +293,8 @@ def main():
             "traffic": measured_traffic(dom),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
             "timing": "hipExtLaunchKernel start/stop events on every launch of this kernel "
-                      "in K eager steps, on the stream it runs on",
+                      "in K eager steps, on the stream it runs on, the stream drained "
+                      "between calls",
             "algorithmic_bytes_per_launch": round(dom_bytes),
         },
         "points": per_point,
@@ -311,7 +315,7 @@ def main():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "int4_decode_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_only_gemm_amd", "csrc", f)
-                  for f in ("gemm.hip", "decode.h", "common.h")]
+                  for f in ("gemm.hip", "decode.h", "common.h", "prefill.h", "prefill.hip")]
 
 
 def kernel_source_hash():
@@ -338,7 +342,7 @@ def measured_traffic(kernel):
 
 
 def pmc_probe(L, dev):
-    """Each decode call of the workload once (act-order, one weight copy),
+    """Each GEMM call of the workload once (act-order, one weight copy),
     then a 256 MiB device-to-device copy whose byte count calibrates the
     counters."""
     import torch
