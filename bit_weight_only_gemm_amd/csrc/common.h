@@ -148,9 +148,27 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QP& p)
   return dequant_fields<ZS>((w >> (4 * i)) & 0x000F000Fu, p);
 }
 
-// Exact dequantization of one repacked 4-bit word into an 8-element MFMA operand.
-template <int DT, bool ZS = true>
-__device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const QParam<DT>& p) {
+// The codes alone as MFMA operand values, for kernels that apply the scale and
+// zero after summing over a group: 0x6400 | q is the fp16 value 1024 + q and
+// 0x4300 | q the bf16 value 128 + q (q < 128), both exact.  kOffset is that
+// 1024 or 128.
+template <int DT> struct RawQ {
+  static constexpr float kOffset = DT == DT_F16 ? 1024.0f : 128.0f;
+  uint32_t magic;  // in a register, so the insert is one v_and_or_b32
+  __device__ __forceinline__ RawQ() {
+    magic = DT == DT_F16 ? 0x64006400u : 0x43004300u;
+    asm("" : "+v"(magic));
+  }
+};
+template <bool ZS = true, int DT>
+__device__ __forceinline__ uint32_t dequant_fields(uint32_t f, const RawQ<DT>& p) {
+  return f | p.magic;
+}
+
+// Exact dequantization of one repacked 4-bit word into an 8-element MFMA operand
+// (with a RawQ: the codes alone).
+template <int DT, bool ZS = true, class QP>
+__device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const QP& p) {
   u32x4_t r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = dequant_pair<ZS>(w, i, p);
@@ -208,15 +226,16 @@ __host__ __device__ constexpr uint32_t sym_zero_xor(int bits) {
   return bits == 8 ? 0x80808080u : bits == 4 ? 0x88888888u : 0x44444444u;
 }
 
-// The 8-element B operand of MFMA step j (0..3) from a lane's codes.
-template <int DT, bool ZS = true>
+// The 8-element B operand of MFMA step j (0..3) from a lane's codes (p a
+// QParam, or a RawQ for the codes alone).
+template <int DT, bool ZS = true, class QP>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<4>& c, int j,
-                                                             const QParam<DT>& p) {
+                                                             const QP& p) {
   return dequant_word<DT, ZS>(c.w[j], p);
 }
-template <int DT, bool ZS = true>
+template <int DT, bool ZS = true, class QP>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<8>& c, int j,
-                                                             const QParam<DT>& p) {
+                                                             const QP& p) {
   const u32x4_t h = (j >> 1) ? c.hi : c.lo;
   const uint32_t a = h[2 * (j & 1)], b = h[2 * (j & 1) + 1];
   u32x4_t r;
@@ -226,9 +245,9 @@ __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<8>& c, 
   r[3] = dequant_fields<ZS>((b >> 8) & 0x00FF00FFu, p);
   return __builtin_bit_cast(typename Op<DT>::vec, r);
 }
-template <int DT, bool ZS = true>
+template <int DT, bool ZS = true, class QP>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<3>& c, int j,
-                                                             const QParam<DT>& p) {
+                                                             const QP& p) {
   const uint32_t lo = c.w[j >> 1], hi = c.w[2];
   u32x4_t r;
 #pragma unroll

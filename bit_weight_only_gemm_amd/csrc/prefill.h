@@ -25,6 +25,12 @@ constexpr int PF_DMA_STEPS = W4A16_PF_DMA_STEPS;  // steps the activation loads 
 #ifndef W4A16_PF_SGB
 #define W4A16_PF_SGB 1
 #endif
+#ifndef W4A16_PF_FOLD
+#define W4A16_PF_FOLD 1
+#endif
+#ifndef W4A16_PF_DEEP
+#define W4A16_PF_DEEP 1
+#endif
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
@@ -149,7 +155,8 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
   }
   // the weights and meta of K tile t for column group g.  INT: sa holds the U
   // scales of the tile (units (t & 7) U .. of the run, 2 U bytes), za the zero
-  // dword holding their fields.
+  // dword holding their fields (XORed with zx where they are used, so that no
+  // instruction needs a load's result before then).
   auto load_w = [&](int t, int g, CT (&w)[2], u32x2_t& sa, uint32_t& za) {
     if constexpr (FMT == FMT_INT4) {
 #pragma unroll
@@ -168,7 +175,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       else if constexpr (U == 2) sa = u32x2_t{bld32(rs, vmeta[g] * 32u, sb), 0u};
       else sa = bld64(rs, vmeta[g] * 64u, sb);
       za = bld32(rz, vmeta[g] * 4u * kZWords,
-                 (t >> 3) * 256 * kZWords + (((t & 7) * U * kZW) >> 5) * 4) ^ zx;
+                 (t >> 3) * 256 * kZWords + (((t & 7) * U * kZW) >> 5) * 4);
     } else {
       w[0].w = bld128(rc, vcode[g][0], t * 64);
       w[1].w = bld128(rc, vcode[g][1], t * 64);
@@ -182,35 +189,77 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
   for (int m = 0; m < PF_MT; ++m)
 #pragma unroll
     for (int g = 0; g < 2; ++g) acc[m][g] = float16_t{};
+  // FOLD (integer codes, one scale and zero per K tile, 32 rows): the B
+  // operands are the codes alone (RawQ: o + q, o = 1024 in fp16, 128 in
+  // bf16), summed over the tile into accT; accX sums the activation rows over
+  // the tile (an MFMA against ones).  At the end of the tile
+  //   acc += s (accT - (o + z) accX) = s sum_k x_k (q_k - z),
+  // one multiply-add pair per accumulator per tile in place of the scale and
+  // zero in every operand: the dequant VALU per weight drops to the insert.
+  // The result differs from dequant-then-multiply only by the rounding of
+  // each weight to 16 bits, which this form never does (a one-hot row still
+  // gives round16((q - z) s) exactly).
+  constexpr bool FOLD = W4A16_PF_FOLD && FMT == FMT_INT4 && U == 1 && BM == 32 &&
+                        !(BITS == 8 && DT == DT_BF16);
+  float16_t accT[FOLD ? PF_MT : 1][2], accX[FOLD ? PF_MT : 1];
+  const RawQ<DT> rq;
+  const vec ones = __builtin_bit_cast(
+      vec, DT == DT_F16 ? u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
+                        : u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-  CT cw[2][2], cn[2][2];
-  u32x2_t sc[2], sn[2];
-  uint32_t zz[2], zn[2];
+  // DEEP (32 rows): the weights of K tile t + 2 are in flight while
+  // tile t is computed (two tiles of latency cover; with few rows a tile's
+  // compute is short).  The weight registers are a ring of three slots, the
+  // tile loop unrolled by three so that no in-flight register is copied.  The
+  // activations of tile t + 1 are issued first, all at once (BM / 16 loads per
+  // lane), then the weights of tile t + 2; the wait before each barrier
+  // counts in issue order, so it leaves those kW loads pending (the barrier is
+  // a plain s_barrier: __syncthreads would wait for every load).
+  constexpr bool DEEP = W4A16_PF_DEEP && BM == 32;
+  constexpr int kW = 2 * ((FMT == FMT_NF4 ? 2 : (BITS == 8 ? 4 : 2)) + 2);  // loads per load_w pair
+  CT cw[DEEP ? 3 : 2][2][2];
+  u32x2_t sc[DEEP ? 3 : 2][2];
+  uint32_t zz[DEEP ? 3 : 2][2];
 
-  // ---- prologue: K tile 0
+  // ---- prologue: K tile tb (and, DEEP, the weights of tile tb + 1)
 #pragma unroll
-  for (int g = 0; g < 2; ++g) load_w(tb, g, cw[g], sc[g], zz[g]);
+  for (int g = 0; g < 2; ++g) load_w(tb, g, cw[0][g], sc[0][g], zz[0][g]);
+  if constexpr (DEEP) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) load_w(min(tb + 1, te - 1), g, cw[1][g], sc[1][g], zz[1][g]);
+  }
 #pragma unroll
   for (int i = 0; i < PF_ALD; ++i)
     lds_dma16(rx, As + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
               TAIL ? tb * 256 : (int)((uint32_t)i * astride) + tb * 256);
   __syncthreads();
 
-  for (int t = tb; t < te; ++t) {
+  // One K tile: compute tile t from the weight slot (cwc, scc, zzc) while the
+  // weights of tile t + 1 (t + 2 when DEEP) are loaded into (cwn, scn, zzn).
+  auto tile = [&](const int t, CT (&cwc)[2][2], u32x2_t (&scc)[2], uint32_t (&zzc)[2],
+                  CT (&cwn)[2][2], u32x2_t (&scn)[2], uint32_t (&zzn)[2]) {
     // ---- issue K tile t + 1 (the last tile is re-read on the final pass);
     // its activations go to LDS stage (t - tb + 1) & 1, last read before the
     // previous barrier
     const int tn = min(t + 1, te - 1);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) load_w(tn, g, cn[g], sn[g], zn[g]);
     uint8_t* sw = As + ((t - tb + 1) & 1) * PF_STAGE;
-    // the activation loads of tile t + 1 are spread over the first
-    // PF_DMA_STEPS steps of tile t (a burst of them stalls the issuing waves
-    // behind the address queue)
     auto issue_dma = [&](int i) {
       lds_dma16(rx, sw + (4 * i + wave) * 1024, TAIL ? avoff + (uint32_t)i * astride : avoff,
                 TAIL ? tn * 256 : (int)((uint32_t)i * astride) + tn * 256);
     };
+    if constexpr (DEEP) {
+#pragma unroll
+      for (int i = 0; i < PF_ALD; ++i) issue_dma(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) load_w(min(t + 2, te - 1), g, cwn[g], scn[g], zzn[g]);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) load_w(tn, g, cwn[g], scn[g], zzn[g]);
+    }
+    // otherwise the activation loads of tile t + 1 are spread over the first
+    // PF_DMA_STEPS steps of tile t (a burst of them stalls the issuing waves
+    // behind the address queue)
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- K tile t from LDS stage t & 1: 8 steps of 16 inputs.  Per step the
@@ -221,21 +270,23 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
     const int zb = ((t & 7) * U) % (32 / kZW);  // zero field of the tile's first unit
     if constexpr (FMT == FMT_NF4) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) ap[g] = (float)(sc[g][0] & 0xFFu) * __builtin_bit_cast(float, zz[g]);
+      for (int g = 0; g < 2; ++g) ap[g] = (float)(scc[g][0] & 0xFFu) * __builtin_bit_cast(float, zzc[g]);
     }
     // B operand of step s for column group g: word j = s >> 1 of the tile, in
     // meta unit j U / 4.  The unit's dequant parameters are formed at the step
     // (a few VALU instructions between MFMAs); formed once per tile and held
     // across it they made the small-M launches of this kernel markedly slower.
     auto operand = [&](int s, int g) -> vec {
-      if constexpr (FMT == FMT_INT4) {
+      if constexpr (FOLD) {
+        return dequant_step<DT, false>(cwc[g][s & 1], s >> 1, rq);
+      } else if constexpr (FMT == FMT_INT4) {
         const int u = (s >> 1) * U / 4;
         QParam<DT> q;
-        q.set((sc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
-              (zz[g] >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
-        return dequant_step<DT, false>(cw[g][s & 1], s >> 1, q);
+        q.set((scc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
+              ((zzc[g] ^ zx) >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
+        return dequant_step<DT, false>(cwc[g][s & 1], s >> 1, q);
       } else {
-        return nf4_operand<DT>(cw[g][s >> 2].w[s & 3], lut, ap[g]);
+        return nf4_operand<DT>(cwc[g][s >> 2].w[s & 3], lut, ap[g]);
       }
     };
     const uint8_t* st = As + ((t - tb) & 1) * PF_STAGE;
@@ -256,8 +307,10 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       // loads i with i * PF_DMA_STEPS / PF_ALD == s go out in step s
       const int i0 = (s * PF_ALD + PF_DMA_STEPS - 1) / PF_DMA_STEPS;
       const int i1 = ((s + 1) * PF_ALD + PF_DMA_STEPS - 1) / PF_DMA_STEPS;
+      if constexpr (!DEEP) {
 #pragma unroll
-      for (int i = i0; i < i1 && i < PF_ALD; ++i) issue_dma(i);
+        for (int i = i0; i < i1 && i < PF_ALD; ++i) issue_dma(i);
+      }
       if (s < 7) {
         const int sn1 = s + 1;
 #if W4A16_PF_APF
@@ -266,16 +319,26 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
 #pragma unroll
         for (int g = 0; g < 2; ++g) bn[g] = operand(sn1, g);
       }
+      if constexpr (FOLD) {
 #pragma unroll
-      for (int m = 0; m < PF_MT; ++m)
+        for (int m = 0; m < PF_MT; ++m) {
 #pragma unroll
-        for (int g = 0; g < 2; ++g) acc[m][g] = mfma32x32x16<DT>(a[m], b[g], acc[m][g]);
+          for (int g = 0; g < 2; ++g)
+            accT[m][g] = mfma32x32x16<DT>(a[m], b[g], s == 0 ? float16_t{} : accT[m][g]);
+          accX[m] = mfma32x32x16<DT>(a[m], ones, s == 0 ? float16_t{} : accX[m]);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < PF_MT; ++m)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) acc[m][g] = mfma32x32x16<DT>(a[m], b[g], acc[m][g]);
+      }
 #if W4A16_PF_SGB
       if (s < 7) {
 #pragma unroll
-        for (int k = 0; k < 2 * PF_MT; ++k) {
+        for (int k = 0; k < (FOLD ? 3 : 2) * PF_MT; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          if (k < i1 - i0 && i0 < PF_ALD)
+          if (!DEEP && k < i1 - i0 && i0 < PF_ALD)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one activation load
 #if W4A16_PF_APF
           if (k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
@@ -298,14 +361,47 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FOLD) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < 2; ++g) {
+        const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(scc[g][0] & 0xFFFFu));
+        const float nz = -(RawQ<DT>::kOffset +
+                           (float)(((zzc[g] ^ zx) >> (kZW * zb)) & ((1u << kZW) - 1u)));  // -(o + z)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) cw[g][h2] = cn[g][h2];
-      sc[g] = sn[g];
-      zz[g] = zn[g];
+        for (int m = 0; m < PF_MT; ++m)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[m][g][r] = __builtin_fmaf(sf, __builtin_fmaf(nz, accX[m][r], accT[m][g][r]),
+                                          acc[m][g][r]);
+      }
     }
-    __syncthreads();  // the LDS writes of tile t + 1 are complete (vmcnt) and visible
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DEEP) {
+      // this wave's activation loads of tile t + 1 are complete (only the kW
+      // weight loads of tile t + 2, issued after them, may be pending), then
+      // every wave's; the memory clobber keeps LDS accesses on their side
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kW) : "memory");
+    }
+  };
+
+  if constexpr (DEEP) {
+    for (int t = tb; t < te; t += 3) {
+      tile(t, cw[0], sc[0], zz[0], cw[2], sc[2], zz[2]);
+      if (t + 1 < te) tile(t + 1, cw[1], sc[1], zz[1], cw[0], sc[0], zz[0]);
+      if (t + 2 < te) tile(t + 2, cw[2], sc[2], zz[2], cw[1], sc[1], zz[1]);
+    }
+  } else {
+    for (int t = tb; t < te; ++t) {
+      tile(t, cw[0], sc[0], zz[0], cw[1], sc[1], zz[1]);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) cw[0][g][h2] = cw[1][g][h2];
+        sc[0][g] = sc[1][g];
+        zz[0][g] = zz[1][g];
+      }
+      __syncthreads();  // the LDS writes of tile t + 1 are complete (vmcnt) and visible
+    }
   }
 
   // ---- epilogue: register r of lane l is row (r & 3) + 4 (l >> 5) + 8 (r >> 2),
