@@ -83,12 +83,16 @@ void launch_int_prefill(const void* x, const void* codes_r, const void* scales_r
 void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                         const float* absmax_scale, const Nf4Table& L, void* out, void* ws,
                         int64_t M, int64_t N, int64_t K, int dtype, hipStream_t stream);
-// Whether nf4_gemm runs the large-M kernel at this shape (its codebook
-// dequant costs about twice the INT4 one, so the crossover is later: from 64
-// rows, or 32 on layers of 32 Mi weights and more), and the workspace bytes
-// it then needs.
+// Whether nf4_gemm runs the large-M kernel at this shape, and the workspace
+// bytes it then needs.  Its codebook dequant costs about twice the INT4 one,
+// so the crossovers (measured on whole calls, bf16) are later than INT4's:
+// from 16 rows on layers of 100 Mi weights and more (28672 x 8192 at M = 16:
+// 81.1 us against 85.9), from 24 rows on layers of 24 Mi weights and more
+// (4096 x 11008 at M = 24: 26.2 against 28.0), from 64 rows otherwise.
 inline bool nf4_use_prefill(int64_t M, int64_t N, int64_t K) {
-  return K % 128 == 0 && (M >= 64 || (M >= 32 && N * K >= (int64_t)32 << 20));
+  const int64_t w = N * K;
+  return K % 128 == 0 && (M >= 64 || (w >= (int64_t)100 << 20 && M >= 16) ||
+                          (w >= (int64_t)24 << 20 && M >= 24));
 }
 int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K);
 

@@ -319,8 +319,9 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_
 
 /*
  * Workspace bytes nf4_gemm needs at this shape: the fp32 split-K partials of
- * the large-M kernel (K % 128 == 0 and M >= 64, or M >= 32 on layers of 32 Mi
- * weights and more) when it splits K; 0 otherwise.
+ * the large-M kernel (K % 128 == 0 and M >= 64; M >= 16 on layers of 100 Mi
+ * weights and more, M >= 24 on layers of 24 Mi weights and more) when it
+ * splits K; 0 otherwise.
  */
 int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
 
