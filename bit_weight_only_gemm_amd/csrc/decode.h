@@ -15,6 +15,9 @@ namespace w4a16 {
 #endif
 constexpr int DW = W4A16_DECODE_WAVES;  // waves per decode workgroup
 constexpr int RUN = 8;                  // K tiles per meta run and ring pass
+#ifndef W4A16_DEC_FOLD
+#define W4A16_DEC_FOLD 1
+#endif
 
 // Activation modes.  PACKED: M <= 4, one 16-byte load per lane and K tile
 // carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
@@ -73,6 +76,9 @@ struct IntW {
   static constexpr int kZW = zero_field_bits(BITS);        // zero field width
   static constexpr int kZWords = U * kZW / 4;              // zero dwords per column and run
   typedef Codes<BITS> CodeT;
+  // one scale and zero per K tile (U = 1) and the codes exact as o + q in the
+  // operand type: the packed modes may apply them after the tile's MFMAs
+  static constexpr bool kFold = U == 1 && !(BITS == 8 && DT == DT_BF16);
   const uint8_t* codes;
   const uint8_t* scales;
   const uint8_t* zeros;
@@ -157,6 +163,20 @@ struct IntW {
       b[j] = dequant_step<DT, false>(w, j, qp);
     }
   }
+  // The codes alone (o + q, RawQ) as the B operands of tile slot s, and the
+  // slot's scale s and -(o + z) for the fold (U = 1: unit r = s).
+  __device__ __forceinline__ void raw_operands(const CodeT& w, typename Op<DT>::vec b[4]) const {
+    const RawQ<DT> rq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = dequant_step<DT, false>(w, j, rq);
+  }
+  __device__ static __forceinline__ void fold_param(const Meta& m, int r, float& sf, float& nz) {
+    constexpr int per = 32 / kZW;
+    sf = (float)__builtin_bit_cast(
+        _Float16, (uint16_t)((m.s[r >> 3][(r & 7) >> 1] >> (16 * (r & 1))) & 0xFFFFu));
+    nz = -(RawQ<DT>::kOffset +
+           (float)((m.z[r / per] >> (kZW * (r % per))) & ((1u << kZW) - 1u)));
+  }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }
 };
 
@@ -172,6 +192,7 @@ struct IntW {
 template <int DT, bool BATCH>
 struct Nf4W {
   static constexpr bool kRaggedK = true;  // K % 64 == 0 only: a last tile may be half
+  static constexpr bool kFold = false;
   typedef u32x4_t CodeT;
   const uint8_t* q;
   const uint8_t* aq;
@@ -372,6 +393,18 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   float4_t acc[NACC];
 #pragma unroll
   for (int q = 0; q < NACC; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // FOLD (packed modes, integer codes with one scale and zero per K tile):
+  // the B operands are the codes alone (o + q, exact), each K tile's 4 steps
+  // go to fresh step tiles, and an MFMA of the same A against ones gives the
+  // tile's row sums of x for every (step, batch row) row of the A operand.
+  // Lane group g's rows are step g's, so the lane keeps
+  //   yf += s (at[g] - (o + z) ax),
+  // s and z of its own column: the scale and zero cost a multiply-add pair
+  // per accumulator and tile instead of VALU work in every operand.  The
+  // weights are never rounded to 16 bits in this form (a one-hot row still
+  // gives round16((q - z) s) exactly).
+  constexpr bool FOLD = W4A16_DEC_FOLD && is_packed(AM) && WP::kFold;
+  float4_t yf = float4_t{0.f, 0.f, 0.f, 0.f};
 
   // Ring of RUN tiles: slot s holds tile i + s of the current pass.  The
   // fill (tiles 0 .. RUN - 1 and the first run's meta) is issued first; each
@@ -427,8 +460,32 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
         const int sa = s % PA;
         if (i + s < n) {  // wave-uniform
           typename Op<DT>::vec b[4];
-          wp.operands(ring[s], s, mc, b);
-          mma_tile<DT, AM, MT, NA, NACC>(b, ra[sa], acc);
+          if constexpr (FOLD) {
+            typedef typename Op<DT>::vec vec;
+            const vec ones = __builtin_bit_cast(
+                vec, DT == DT_F16 ? u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
+                                  : u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+            const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
+            wp.raw_operands(ring[s], b);
+            float4_t at[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[sa][0], b[j], z4);
+            const float4_t ax = mfma16x16x32<DT>(ra[sa][0], ones, z4);
+            float sf, nz;
+            WP::fold_param(mc, s, sf, nz);
+            // at[lane >> 4], as two levels of selects on the bits of the lane
+            // group (a chain of equality tests becomes branches)
+            const bool g0 = lane & 16, g1 = lane & 32;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v01 = g0 ? at[1][e] : at[0][e], v23 = g0 ? at[3][e] : at[2][e];
+              const float v = g1 ? v23 : v01;
+              yf[e] = __builtin_fmaf(sf, __builtin_fmaf(nz, ax[e], v), yf[e]);
+            }
+          } else {
+            wp.operands(ring[s], s, mc, b);
+            mma_tile<DT, AM, MT, NA, NACC>(b, ra[sa], acc);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         ring[s] = wp.load_codes(t0 + min(i + s + RUN, n - 1), lane);
@@ -446,7 +503,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
     // 0..3 of step g: take them and add the 4 lane groups (a shuffle
     // reduction across the wave); lane group 0 then holds rows 0..3.
     const int g = lane >> 4;
-    float4_t v = g == 0 ? acc[0] : (g == 1 ? acc[1] : (g == 2 ? acc[2] : acc[3]));
+    float4_t v = FOLD ? yf : (g == 0 ? acc[0] : (g == 1 ? acc[1] : (g == 2 ? acc[2] : acc[3])));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[e] += __shfl_xor(v[e], 16, 64);

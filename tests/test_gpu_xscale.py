@@ -80,9 +80,11 @@ def test_xscale_unit_scales_equal_plain_gemm(M, dtype):
 @pytest.mark.parametrize("M", [3, 12, 64])
 @pytest.mark.parametrize("act", [False, True])
 def test_xscale_onehot_power_of_two_exact(M, act):
-    # s_k = 2^e_k: x / s is exact, so a one-hot row yields the exactly rounded
-    # product (x_k / s_k) * w[n, k]; a wrong channel's scale shows as a
-    # different power of two
+    # s_k = 2^e_k and x_k = 1: x / s is a power of two, so a one-hot row
+    # yields (x_k / s_k) * w[n, k] exactly, whether or not the kernel rounds
+    # the dequantized weight to 16 bits before the product (its packed and
+    # 32-row paths apply the scale after the K sum); a wrong channel's scale
+    # shows as a different power of two
     N, K, G = 128, 1024, 128
     dtype = "f16"
     say("xscale onehot", M, act)
@@ -92,7 +94,7 @@ def test_xscale_onehot_power_of_two_exact(M, act):
     packed, sb, wd = _awq_setup(tag, N, K, G, False, act, dtype, s32)
     ks = (np.arange(M) * 97 + 5) % K
     x = np.zeros((M, K), dtype=np.float32)
-    x[np.arange(M), ks] = 1.5
+    x[np.arange(M), ks] = 1.0
     xb = synth.to_bits(x, dtype)
     y = tensor_bits(w4.w4a16_gemm_xscale(bits_to_tensor(xb, dtype), bits_to_tensor(sb, dtype),
                                          packed))
