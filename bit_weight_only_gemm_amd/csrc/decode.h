@@ -76,9 +76,10 @@ struct IntW {
   static constexpr int kZW = zero_field_bits(BITS);        // zero field width
   static constexpr int kZWords = U * kZW / 4;              // zero dwords per column and run
   typedef Codes<BITS> CodeT;
-  // one scale and zero per K tile (U = 1) and the codes exact as o + q in the
-  // operand type: the packed modes may apply them after the tile's MFMAs
-  static constexpr bool kFold = U == 1 && !(BITS == 8 && DT == DT_BF16);
+  // the codes exact as o + q in the operand type: the packed modes may apply
+  // the scale and zero after each step's MFMA (a step never spans two meta
+  // units)
+  static constexpr bool kFold = !(BITS == 8 && DT == DT_BF16);
   const uint8_t* codes;
   const uint8_t* scales;
   const uint8_t* zeros;
@@ -163,19 +164,40 @@ struct IntW {
       b[j] = dequant_step<DT, false>(w, j, qp);
     }
   }
-  // The codes alone (o + q, RawQ) as the B operands of tile slot s, and the
-  // slot's scale s and -(o + z) for the fold (U = 1: unit r = s).
+  // The codes alone (o + q, RawQ) as the B operands of tile slot s, and, for
+  // the fold, the scale s and -(o + z) of step g of slot s (unit sU + gU/4;
+  // g is the lane group, so the U candidates are formed and selected on its
+  // bits rather than indexed).
   __device__ __forceinline__ void raw_operands(const CodeT& w, typename Op<DT>::vec b[4]) const {
     const RawQ<DT> rq;
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = dequant_step<DT, false>(w, j, rq);
   }
-  __device__ static __forceinline__ void fold_param(const Meta& m, int r, float& sf, float& nz) {
+  __device__ static __forceinline__ void unit_fold(const Meta& m, int r, float& sf, float& nz) {
     constexpr int per = 32 / kZW;
     sf = (float)__builtin_bit_cast(
         _Float16, (uint16_t)((m.s[r >> 3][(r & 7) >> 1] >> (16 * (r & 1))) & 0xFFFFu));
     nz = -(RawQ<DT>::kOffset +
            (float)((m.z[r / per] >> (kZW * (r % per))) & ((1u << kZW) - 1u)));
+  }
+  __device__ static __forceinline__ void fold_param(const Meta& m, int s, int lane, float& sf,
+                                                    float& nz) {
+    if constexpr (U == 1) {
+      unit_fold(m, s, sf, nz);
+    } else {
+      float a[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) unit_fold(m, s * U + u, a[u], c[u]);
+      // step g = lane >> 4 uses unit g U / 4: g >> 1 for U = 2, g for U = 4
+      const bool b0 = lane & 16, b1 = lane & 32;
+      if constexpr (U == 2) {
+        sf = b1 ? a[1] : a[0];
+        nz = b1 ? c[1] : c[0];
+      } else {
+        sf = b1 ? (b0 ? a[3] : a[2]) : (b0 ? a[1] : a[0]);
+        nz = b1 ? (b0 ? c[3] : c[2]) : (b0 ? c[1] : c[0]);
+      }
+    }
   }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }
 };
@@ -393,14 +415,15 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   float4_t acc[NACC];
 #pragma unroll
   for (int q = 0; q < NACC; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
-  // FOLD (packed modes, integer codes with one scale and zero per K tile):
-  // the B operands are the codes alone (o + q, exact), each K tile's 4 steps
-  // go to fresh step tiles, and an MFMA of the same A against ones gives the
-  // tile's row sums of x for every (step, batch row) row of the A operand.
-  // Lane group g's rows are step g's, so the lane keeps
+  // FOLD (packed modes, integer codes): the B operands are the codes alone
+  // (o + q, exact), each K tile's 4 steps go to fresh step tiles, and an MFMA
+  // of the same A against ones gives the tile's row sums of x for every
+  // (step, batch row) row of the A operand.  Lane group g's rows are step g's,
+  // so the lane keeps
   //   yf += s (at[g] - (o + z) ax),
-  // s and z of its own column: the scale and zero cost a multiply-add pair
-  // per accumulator and tile instead of VALU work in every operand.  The
+  // s and z of its own column and step g's meta unit: the scale and zero cost
+  // a multiply-add pair per accumulator and tile instead of VALU work in every
+  // operand.  The
   // weights are never rounded to 16 bits in this form (a one-hot row still
   // gives round16((q - z) s) exactly).
   constexpr bool FOLD = W4A16_DEC_FOLD && is_packed(AM) && WP::kFold;
@@ -472,7 +495,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
             for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[sa][0], b[j], z4);
             const float4_t ax = mfma16x16x32<DT>(ra[sa][0], ones, z4);
             float sf, nz;
-            WP::fold_param(mc, s, sf, nz);
+            WP::fold_param(mc, s, lane, sf, nz);
             // at[lane >> 4], as two levels of selects on the bits of the lane
             // group (a chain of equality tests becomes branches)
             const bool g0 = lane & 16, g1 = lane & 32;
