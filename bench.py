@@ -54,7 +54,7 @@ def kernel_name(M, K, N):
     layers of 100 Mi weights; 16 on layers of 24 Mi weights with N >= 5120,
     else 24); otherwise the
     decode kernel, where M <= 4 rows are gathered in the kernel when the
-    staged rows + permutation take at most 32 KB per workgroup and 12 MiB over
+    staged rows + permutation take at most 56 KB per workgroup and 12 MiB over
     the N/16 workgroups, else a preparation pass permutes them first."""
     kb = lambda b: (b + 1023) // 1024 * 1024
     w = N * K
@@ -63,7 +63,7 @@ def kernel_name(M, K, N):
         return "wq_prefill_kernel<f16, INT 4-bit>"      # the large-M kernel
     if M <= 4:
         staged = kb(M * K * 2) + kb(K * 4)
-        if staged <= 32 * 1024 and ((N + 15) // 16) * staged <= 12 << 20:
+        if staged <= 56 * 1024 and ((N + 15) // 16) * staged <= 12 << 20:
             return "intb_decode_kernel<f16, MT=1, xgather, 4-bit>"
         return "intb_decode_kernel<f16, MT=1, packed, 4-bit>"
     mt = 1 if M <= 16 else (2 if M <= 32 else 4)

@@ -34,9 +34,10 @@ constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; 
 
 // Largest LDS footprint of the staged activations (+ permutation, + input
 // scales) per workgroup: past it the staging costs more than the separate
-// preparation pass it saves (measured on MI355X), and it leaves room for
-// several workgroups per CU.
-constexpr int64_t kMaxXlds = 32 * 1024;
+// preparation pass it saves (measured on MI355X), and with the reduction
+// buffer it stays within a workgroup's 64 KB and leaves room for two
+// workgroups per CU.
+constexpr int64_t kMaxXlds = 56 * 1024;
 
 // Multiply-accumulate the 4 MFMA steps of one K tile given its 4 B operands.
 template <int DT, int AM, int MT, int NA, int NACC>

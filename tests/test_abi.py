@@ -92,7 +92,7 @@ def test_gemm_validation_without_gpu():
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, NULL, 0, NULL) == 5
     # the size covers every call at a shape, with or without a permutation and
     # AWQ input scales: M <= 4 rows (with the permutation and the scales) that
-    # the decode kernel stages on chip need no workspace (up to 32 KB per
+    # the decode kernel stages on chip need no workspace (up to 56 KB per
     # workgroup and 12 MiB over the grid: 256 x 24 KB here) ...
     assert L.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
     # ... larger ones are prepared in a pass: M * K * 2 bytes
