@@ -78,6 +78,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-nf4", action="store_true")
+    ap.add_argument("--no-qwen", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run each decode call of the workload once, then a 256 MiB device copy "
@@ -304,6 +305,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         result["prefill"] = bench_prefill(L, timer, sptr)
+        result["prefill_m8192"] = bench_prefill(L, timer, sptr, M=8192)
+    if not args.no_qwen:
+        result["qwen_decode"] = bench_qwen_decode()
     if not args.no_nf4:
         result["nf4"] = bench_nf4(L, timer, sptr)
     if not args.no_variants:
@@ -400,7 +404,7 @@ PREFILL_SHAPES = [(5120, 7168), (5120, 5120), (5120, 55296), (27648, 5120)]   # 
 
 
 def bench_prefill(L, timer, sptr, M=2048):
-    """Qwen2.5-32B-shaped prefill layers at M = 2048 tokens, bf16 activations
+    """Qwen2.5-32B-shaped prefill layers at M tokens, bf16 activations
     ~N(0,1) with 1 % of the input channels x20, RTN int4 G=128 weights:
     median kernel time of the fused kernel, and dense bf16 torch.matmul of
     the dequantized weights (the practical matrix-core ceiling) beside it."""
@@ -448,13 +452,79 @@ def bench_prefill(L, timer, sptr, M=2048):
     tot_fl = sum(2.0 * q["M"] * q["N"] * q["K"] for q in pts)
     tot_t = sum(q["us"] for q in pts) * 1e-6
     return {"workload": "Qwen2.5-32B-shaped prefill, int4 G=128, bf16 x with 1% outlier "
-                        "channels x20, M=2048",
+                        "channels x20, M=" + str(M),
             "kernel": "wq_prefill_kernel<bf16, INT 4-bit>",
             "tflops_all_shapes": round(tot_fl / tot_t / 1e12, 1),
             "roofline": {"bound": "mfma", "achieved": best["tflops"],
                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(best["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                          "shape": [best["M"], best["K"], best["N"]]},
+            "points": pts}
+
+
+def graph_call_time(call, ps, stream, n=10, reps=5):
+    """Seconds per call of `call(p)` over the weight copies ps, from HIP-graph
+    replays of n calls (the whole call: any preparation pass and reduction)."""
+    import torch
+    for r in range(3):
+        call(ps[r % len(ps)])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for r in range(n):
+            call(ps[r % len(ps)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / (reps * n)
+
+
+def bench_qwen_decode(Ms=(1, 16, 64)):
+    """The Qwen2.5-32B-shaped layers in AWQ layout (s ~ U[0.5, 2] folded into W,
+    x divided by s before the call), int4 G=128, fp16 activations, at M in
+    {1, 16, 64}: whole calls by HIP-graph replay over rotating weight copies
+    (>= 512 MB), weight-stream GB/s per layer and over the four layers."""
+    import torch
+    import bit_weight_only_gemm_amd as w4
+    from bit_weight_only_gemm_amd import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    pts = []
+    tot = {M: [0.0, 0] for M in Ms}
+    for K, N in PREFILL_SHAPES:
+        W = torch.from_numpy(synth.weights("C3/W/%dx%d" % (K, N), N, K)).to(dev)
+        s = torch.from_numpy(synth.awq_scales("C3/s/%d" % K, K)).to(dev)
+        qw, sc, qz = w4.w4a16_quantize_rtn(W * s[None, :], G)
+        p0 = w4.w4a16_repack(qw, sc, qz)
+        del W, qw, sc, qz
+        wb = weight_bytes(K, N, perm=False)
+        R = max(2, int(np.ceil(512e6 / wb)))
+        ps = [p0] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in p0.items()}
+                     for _ in range(R - 1)]
+        for M in Ms:
+            x = (torch.from_numpy(synth.activations("C3/x/%dx%d" % (M, K), M, K)).to(dev)
+                 / s[None, :]).half()
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            ws = w4.workspace(w4.w4a16_workspace_bytes(M, N, K), dev)
+            t = graph_call_time(lambda p: w4.w4a16_gemm(x, p, out=y, workspace=ws), ps, stream)
+            byt = wb + 2 * M * K + 2 * M * N
+            pts.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 2),
+                        "weight_GBps": round(wb / t / 1e9, 1),
+                        "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1)})
+            tot[M][0] += t
+            tot[M][1] += wb
+            del x, y, ws
+        del ps, p0, s
+        torch.cuda.empty_cache()
+    return {"workload": "Qwen2.5-32B-shaped layers (5120x7168, 5120x5120, 5120x55296, "
+                        "27648x5120), AWQ layout, int4 G=128, fp16, whole calls",
+            "weight_GBps_all_layers": {str(M): round(tot[M][1] / tot[M][0] / 1e9, 1) for M in Ms},
             "points": pts}
 
 
