@@ -21,9 +21,14 @@
 //    and one 4-byte load per lane), and for M <= 4 one 16-byte load per lane
 //    carries the activations of all 4 MFMA steps of the tile (see "packed"
 //    below).
-//  * Each 32-bit code word is dequantized exactly into an 8-element MFMA
-//    operand (the routine the dequant export uses) and multiplied with
-//    v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation.
+//  * Each 32-bit code word becomes an 8-element MFMA operand, multiplied with
+//    v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation.  For M > 4 it is
+//    dequantized exactly (the routine the dequant export uses).  For M <= 4
+//    (integer codes) it is the codes alone, o + q, and each lane applies the
+//    scale and zero of its column and MFMA step after the step's MFMA, with
+//    the step's activation row sums from one more MFMA against ones: the
+//    same real products without a 16-bit rounding of each weight, and far
+//    fewer VALU instructions per code.
 //  * "Packed" activations (M <= 4): the 16 A-operand rows are 4 K-steps x 4
 //    batch rows (row 4j + m holds step j of batch row m), so one load feeds
 //    the 4 MFMAs of a tile; step j accumulates into its own tile acc[j], whose

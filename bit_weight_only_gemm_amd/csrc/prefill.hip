@@ -27,6 +27,11 @@
 //    through LDS.
 //  * The loads of K tile t + 1 are issued before the MFMAs of tile t and land
 //    in the other LDS stage; one barrier per K tile.
+//  * Up to 32 rows (BM = 32) the call is bound by the dequant and by latency,
+//    not by the multiply: the integer codes enter the MFMAs alone (o + q) and
+//    the scale and zero are applied once per K tile after the sum, and the
+//    weights of tile t + 2 stay in flight across the barrier that ends tile t
+//    (see prefill.h).
 #include "prefill.h"
 
 namespace w4a16 {
