@@ -576,6 +576,135 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   }
 }
 
+// Wide packed decode (M <= 4, integer codes, plain activations): each wave
+// owns NC column tiles and feeds every activation load to all of them, so
+// the rows of x are read from L2 once per NC column tiles instead of once per
+// tile (at M = 4 on a 5120 x 55296 layer those re-reads are as many bytes as
+// the weights).  Otherwise as the packed mode of decode_body with the scale
+// and zero applied after each step's MFMA: DW waves split the K tiles of the
+// workgroup's NC column tiles in runs of WRUN tiles, ring of WRUN tiles per
+// column tile, wave partials added in wave order through LDS.
+template <int DT, int U, int BITS, int NC, int WRUN>
+__global__ void __launch_bounds__(64 * DW)
+intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
+                        const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
+                        uint32_t zx, uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+  typedef IntW<DT, U, BITS> WP;
+  typedef typename Op<DT>::vec vec;
+  static_assert(WP::kFold, "the wide mode applies the scale and zero after the sum");
+  static_assert(RUN % WRUN == 0, "a ring pass stays inside one meta run");
+  __shared__ float red[DW * NC * 64 * 4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  WP wp[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    wp[c].codes = codes;
+    wp[c].scales = scales;
+    wp[c].zeros = zeros;
+    wp[c].zx = zx;
+    wp[c].KT = KT;
+    // (column tiles past N lie in the last panel's padding: read, never stored)
+    wp[c].init(blockIdx.x * NC + c, lane, N, K);
+  }
+  const int nrun = (KT + RUN - 1) / RUN;
+  const int r0 = (nrun * wave) / DW, r1 = (nrun * (wave + 1)) / DW;
+  const int t0 = r0 * RUN;
+  const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const vec ones = __builtin_bit_cast(
+      vec, DT == DT_F16 ? u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
+                        : u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
+  const XLds none{nullptr, nullptr, M};
+  const bool g0 = lane & 16, g1 = lane & 32;
+
+  float4_t yf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) yf[c] = z4;
+  typename WP::CodeT ring[WRUN][NC];
+  vec ra[WRUN][1];
+  typename WP::Meta mc[NC], mn[NC];  // the meta of a run, double-buffered
+  if (n > 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) mn[c] = wp[c].load_meta(r0);
+#pragma unroll
+    for (int s = 0; s < WRUN; ++s) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) ring[s][c] = wp[c].load_codes(t0 + min(s, n - 1), lane);
+      load_a<DT, AM_PACKED, 1, 1, WP>(rx, K, t0 + min(s, n - 1), lane, ra[s], none);
+    }
+    for (int i = 0; i < n; i += WRUN) {
+      if (i % RUN == 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          mc[c] = mn[c];
+          mn[c] = wp[c].load_meta(r0 + min(i / RUN + 1, (n - 1) / RUN));
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < WRUN; ++s) {
+        if (i + s < n) {  // wave-uniform
+          const int slot = (i % RUN) + s;  // tile slot within the meta run
+          const float4_t ax = mfma16x16x32<DT>(ra[s][0], ones, z4);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            vec b[4];
+            wp[c].raw_operands(ring[s][c], b);
+            float4_t at[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[s][0], b[j], z4);
+            float sf, nz;
+            WP::fold_param(mc[c], slot, lane, sf, nz);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v01 = g0 ? at[1][e] : at[0][e], v23 = g0 ? at[3][e] : at[2][e];
+              yf[c][e] = __builtin_fmaf(sf, __builtin_fmaf(nz, ax[e], g1 ? v23 : v01), yf[c][e]);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          ring[s][c] = wp[c].load_codes(t0 + min(i + s + WRUN, n - 1), lane);
+        load_a<DT, AM_PACKED, 1, 1, WP>(rx, K, t0 + min(i + s + WRUN, n - 1), lane, ra[s], none);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // lane group g holds batch rows 0..3 of step g: add the 4 lane groups, then
+  // the DW waves' partials through LDS in wave order
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      yf[c][e] += __shfl_xor(yf[c][e], 16, 64);
+      yf[c][e] += __shfl_xor(yf[c][e], 32, 64);
+    }
+    *(float4_t*)(red + ((wave * NC + c) * 64 + lane) * 4) = yf[c];
+  }
+  __syncthreads();
+  if (wave < NC && lane < 16) {
+    const int c = wave;
+    float4_t s4 = *(const float4_t*)(red + ((0 * NC + c) * 64 + lane) * 4);
+#pragma unroll
+    for (int w = 1; w < DW; ++w) {
+      const float4_t v = *(const float4_t*)(red + ((w * NC + c) * 64 + lane) * 4);
+      s4[0] += v[0];
+      s4[1] += v[1];
+      s4[2] += v[2];
+      s4[3] += v[3];
+    }
+    const int col = (blockIdx.x * NC + c) * 16 + lane;
+    if (col < N) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < M) out[(size_t)e * N + col] = round16<DT>(s4[e]);
+    }
+  }
+}
+
 template <int DT, int MT, int AM, int U, bool XS, int BITS>
 __global__ void __launch_bounds__(64 * DW)
 intb_decode_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ xsc,
@@ -675,12 +804,41 @@ static void launch_intb_v(const DecodeArgs& a) {
                (int)a.K, (int)(a.K / 128));
 }
 
+#ifndef W4A16_WIDE_NC
+#define W4A16_WIDE_NC 2
+#endif
+#ifndef W4A16_WIDE_RUN
+#define W4A16_WIDE_RUN 8
+#endif
+#ifndef W4A16_WIDE_MIN_N
+#define W4A16_WIDE_MIN_N 16384
+#endif
+// Wide packed decode for 3 or 4 rows on layers of at least W4A16_WIDE_MIN_N
+// columns (measured on MI355X, 5120 x 55296: 50.4 -> 43.3 us per call at M = 4;
+// within run-to-run noise at M = 2 and no gain at M = 1, where most of each
+// activation load is rows past M; slower on 11008 columns, where half as many
+// waves fill the GPU; 3 or 4 column tiles per wave were slower than 2).
+template <int DT, int U, int BITS>
+static void launch_intb_wide(const DecodeArgs& a) {
+  constexpr int NC = W4A16_WIDE_NC, WR = W4A16_WIDE_RUN;
+  const dim3 grid((unsigned)ceil_div(a.N, (int64_t)16 * NC));
+  const uint32_t zx = a.zeros ? 0u : sym_zero_xor(BITS);
+  launch_timed(intb_decode_wide_kernel<DT, U, BITS, NC, WR>, grid, dim3(64 * DW), 0, a.stream,
+               (const uint16_t*)a.x, (const uint8_t*)a.codes, (const uint8_t*)a.scales,
+               (const uint8_t*)(a.zeros ? a.zeros : a.scales), zx, (uint16_t*)a.out, (int)a.M,
+               (int)a.N, (int)a.K, (int)(a.K / 128));
+}
+
 template <int DT, int U, bool XS, int BITS>
 static void launch_intb_mode(int am, int mt, const DecodeArgs& a) {
   if (am == AM_XGATHER) return launch_intb_v<DT, 1, AM_XGATHER, U, XS, BITS>(a);
   if constexpr (XS) {
     launch_intb_v<DT, 1, AM_XSTAGED, U, true, BITS>(a);  // the only other mode that scales
   } else {
+    if constexpr (IntW<DT, U, BITS>::kFold) {
+      if (am == AM_PACKED && a.M >= 3 && a.N >= W4A16_WIDE_MIN_N)
+        return launch_intb_wide<DT, U, BITS>(a);
+    }
     if (am == AM_PACKED) launch_intb_v<DT, 1, AM_PACKED, U, false, BITS>(a);
     else if (mt == 1) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);
     else if (mt == 2) launch_intb_v<DT, 2, AM_FULL, U, false, BITS>(a);

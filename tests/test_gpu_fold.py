@@ -78,3 +78,47 @@ def test_fold_outlier_channels(bits, G, sym, act, M, dtype):
     err = compare_gemm(y, xb, _wd(W, bits, G, gi, sym, dtype), dtype)
     say("  rel err", err)
     assert err <= TOL
+
+
+# wide layers (N >= 16384): the packed decode runs NC column tiles per wave;
+# N = 16416 leaves a partly filled last panel
+WIDE = [(4, 128, False, True), (4, 32, True, False), (3, 64, False, False), (8, 128, True, False)]
+
+
+@pytest.mark.parametrize("bits,G,sym,act", WIDE)
+@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_wide_layer_sampled_columns(bits, G, sym, act, M, dtype):
+    N, K = 16416, 1024
+    say("fold wide", bits, G, sym, act, M, dtype)
+    tag = "gpu/fold/wide/%d/%d" % (bits, G)
+    W = synth.weights(tag + "/W", N, K)
+    gi = synth.act_order_gidx(tag + "/g", K, G) if act else None
+    packed = _pack(W, bits, G, gi, sym)
+    xb = synth.to_bits(synth.activations(tag + "/x/%d" % M, M, K), dtype)
+    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([np.arange(0, N, 97), np.arange(N - 40, N)]))
+    K_ = W.shape[1]
+    g = K_ if G == -1 else G
+    q, s, z = intb.quantize_rtn(W[cols], bits, g, gi, sym)
+    wd = intb.dequant_codes(q, s, z, bits, gi, g, dtype)
+    assert compare_gemm(y, xb, wd, dtype, cols=cols) <= TOL
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_wide_layer_onehot_exact(dtype):
+    N, K, G = 16416, 512, 128
+    say("fold wide onehot", dtype)
+    W = synth.weights("gpu/fold/wide/oh", N, K)
+    gi = synth.act_order_gidx("gpu/fold/wide/oh/g", K, G)
+    packed = _pack(W, 4, G, gi, False)
+    ks = np.array([3, 200, 511, 77])
+    x = np.zeros((4, K), dtype=np.float32)
+    x[np.arange(4), ks] = 1.0
+    y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, dtype), dtype), packed))
+    cols = np.unique(np.concatenate([np.arange(0, N, 61), np.arange(N - 40, N)]))
+    q, s, z = intb.quantize_rtn(W[cols], 4, G, gi, False)
+    wd = intb.dequant_codes(q, s, z, 4, gi, G, dtype)
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r][cols], wd[:, k]), (r, k)
