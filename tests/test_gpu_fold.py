@@ -80,13 +80,14 @@ def test_fold_outlier_channels(bits, G, sym, act, M, dtype):
     assert err <= TOL
 
 
-# wide layers (N >= 16384): the packed decode runs NC column tiles per wave;
-# N = 16416 leaves a partly filled last panel
+# wide layers (N >= 16384): the packed decode runs 2 column tiles per wave for
+# 3 or 4 rows (M = 1: the one-tile kernel); N = 16416 leaves a partly filled
+# last panel
 WIDE = [(4, 128, False, True), (4, 32, True, False), (3, 64, False, False), (8, 128, True, False)]
 
 
 @pytest.mark.parametrize("bits,G,sym,act", WIDE)
-@pytest.mark.parametrize("M", [1, 2, 4])
+@pytest.mark.parametrize("M", [1, 3, 4])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_wide_layer_sampled_columns(bits, G, sym, act, M, dtype):
     N, K = 16416, 1024

@@ -138,3 +138,23 @@ def test_nf4_large_m_onehot_exact():
     x[np.arange(M), ks] = 1.0
     y = tensor_bits(w4.nf4_gemm(bits_to_tensor(synth.to_bf16_bits(x), "bf16"), p))
     assert np.array_equal(y, wd[:, ks].T)
+
+
+@pytest.mark.parametrize("N,M", [(16416, 3), (16416, 4), (16400, 4)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nf4_wide_layer_sampled_columns(N, M, dtype):
+    # wide layers through the NF4 packed decode (the integer formats run 2
+    # column tiles per wave from N = 16384 on; NF4 keeps one, its dequant
+    # being the bound); every 53rd output column and the last 40
+    K = 1024
+    say("nf4 wide", N, M, dtype)
+    W = synth.weights("gpu/nf4W/W", N, K)
+    xb = synth.to_bits(synth.activations("gpu/nf4W/x/%d" % M, M, K), dtype)
+    p = _pack(W)
+    y = w4.nf4_gemm(bits_to_tensor(xb, dtype), p)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([np.arange(0, N, 53), np.arange(N - 40, N)]))
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)[cols]
+    assert compare_gemm(y, xb, wd, dtype, cols=cols) <= TOL
