@@ -55,7 +55,8 @@ def kernel_name(M, K, N):
     else 24); otherwise the
     decode kernel, where M <= 4 rows are gathered in the kernel when the
     staged rows + permutation take at most 56 KB per workgroup and 12 MiB over
-    the N/16 workgroups, else a preparation pass permutes them first."""
+    the N/16 workgroups, else a preparation pass permutes them first; one row
+    (M = 1) has an instantiation of its own (the one-row form of the fold)."""
     kb = lambda b: (b + 1023) // 1024 * 1024
     w = N * K
     if (M >= 32 or (w >= 100 << 20 and M >= 5)
@@ -63,9 +64,9 @@ def kernel_name(M, K, N):
         return "wq_prefill_kernel<f16, INT 4-bit>"      # the large-M kernel
     if M <= 4:
         staged = kb(M * K * 2) + kb(K * 4)
-        if staged <= 56 * 1024 and ((N + 15) // 16) * staged <= 12 << 20:
-            return "intb_decode_kernel<f16, MT=1, xgather, 4-bit>"
-        return "intb_decode_kernel<f16, MT=1, packed, 4-bit>"
+        mode = ("xgather" if staged <= 56 * 1024 and ((N + 15) // 16) * staged <= 12 << 20
+                else "packed")
+        return "intb_decode_kernel<f16, MT=1, %s, 4-bit%s>" % (mode, ", one row" if M == 1 else "")
     mt = 1 if M <= 16 else (2 if M <= 32 else 4)
     return "intb_decode_kernel<f16, MT=%d, full, 4-bit>" % mt
 
@@ -200,7 +201,7 @@ def main():
     for step_layers, cl in zip(rot, calls):
         tl = []
         for (K, N, M, q), (a, _, _, _) in zip(step_layers, cl):
-            if kernel_name(M, K, N).endswith("xgather>"):
+            if ", xgather," in kernel_name(M, K, N):
                 tl.append(a)
                 continue
             key = ("xp", M, K, N)

@@ -389,8 +389,11 @@ __device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8
 }
 
 // XS: divide the staged activations by the AWQ input scales xsc [K] (staged
-// modes only).
-template <int DT, int MT, int AM, bool XS, class WP>
+// modes only).  ONE: a single batch row (M == 1) in a packed mode with the
+// fold, which then keeps only element 0 of each lane's step tiles (row 4g of
+// the A operand; the others are rows past M): a quarter of the fold's selects
+// and multiply-adds.
+template <int DT, int MT, int AM, bool XS, bool ONE = false, class WP>
 __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ xsc, WP& wp,
                                             uint16_t* __restrict__ out, int M, int N, int K,
@@ -428,6 +431,8 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   // weights are never rounded to 16 bits in this form (a one-hot row still
   // gives round16((q - z) s) exactly).
   constexpr bool FOLD = W4A16_DEC_FOLD && is_packed(AM) && WP::kFold;
+  static_assert(!ONE || FOLD, "the one-row form is a form of the fold");
+  constexpr int FE = ONE ? 1 : 4;  // fold elements per lane
   float4_t yf = float4_t{0.f, 0.f, 0.f, 0.f};
 
   // Ring of RUN tiles: slot s holds tile i + s of the current pass.  The
@@ -501,7 +506,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
             // group (a chain of equality tests becomes branches)
             const bool g0 = lane & 16, g1 = lane & 32;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < FE; ++e) {
               const float v01 = g0 ? at[1][e] : at[0][e], v23 = g0 ? at[3][e] : at[2][e];
               const float v = g1 ? v23 : v01;
               yf[e] = __builtin_fmaf(sf, __builtin_fmaf(nz, ax[e], v), yf[e]);
@@ -705,7 +710,7 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   }
 }
 
-template <int DT, int MT, int AM, int U, bool XS, int BITS>
+template <int DT, int MT, int AM, int U, bool XS, int BITS, bool ONE>
 __global__ void __launch_bounds__(64 * DW)
 intb_decode_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ xsc,
                    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -720,7 +725,7 @@ intb_decode_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   wp.zeros = zeros;
   wp.zx = zx;
   wp.KT = KT;
-  decode_body<DT, MT, AM, XS>(x, xsc, wp, out, M, N, K, KT, red, perm, xlds);
+  decode_body<DT, MT, AM, XS, ONE>(x, xsc, wp, out, M, N, K, KT, red, perm, xlds);
 }
 
 template <int DT, int MT, int AM, bool BATCH>
@@ -788,16 +793,16 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
-template <int DT, int MT, int AM, int U, bool XS, int BITS>
+template <int DT, int MT, int AM, int U, bool XS, int BITS, bool ONE = false>
 static void launch_intb_v(const DecodeArgs& a) {
   const dim3 grid((unsigned)ceil_div(a.N, 16), (unsigned)ceil_div(a.M, 16 * MT));
   const size_t lds =
       is_staged(AM) ? xlds_bytes((int)a.M, (int)a.K, AM == AM_XGATHER, XS) : 0;
-  if (lds) allow_dynamic_lds((const void*)intb_decode_kernel<DT, MT, AM, U, XS, BITS>);
+  if (lds) allow_dynamic_lds((const void*)intb_decode_kernel<DT, MT, AM, U, XS, BITS, ONE>);
   // a symmetric weight: the zeros descriptor gets an empty range over a valid
   // base and every zero field reads 0 ^ 2^(BITS-1)
   const uint32_t zx = a.zeros ? 0u : sym_zero_xor(BITS);
-  launch_timed(intb_decode_kernel<DT, MT, AM, U, XS, BITS>, grid, dim3(64 * DW), lds, a.stream,
+  launch_timed(intb_decode_kernel<DT, MT, AM, U, XS, BITS, ONE>, grid, dim3(64 * DW), lds, a.stream,
                (const uint16_t*)a.x, (const uint16_t*)a.xsc, (const uint8_t*)a.codes,
                (const uint8_t*)a.scales, (const uint8_t*)(a.zeros ? a.zeros : a.scales), zx,
                AM == AM_XGATHER ? a.perm : nullptr, (uint16_t*)a.out, (int)a.M, (int)a.N,
@@ -829,17 +834,29 @@ static void launch_intb_wide(const DecodeArgs& a) {
                (int)a.N, (int)a.K, (int)(a.K / 128));
 }
 
+// A packed mode; one batch row takes the one-row form of the fold (measured on
+// MI355X at M = 1, fp16, whole calls: 4096 x 11008 8.9 -> 8.5 us, 11008 x 4096
+// 9.5 -> 8.9, 5120 x 55296 34.6 -> 33.3; a wave-uniform branch on M inside
+// the loop instead gained nothing).
+template <int DT, int AM, int U, bool XS, int BITS>
+static void launch_intb_packed(const DecodeArgs& a) {
+  if constexpr (W4A16_DEC_FOLD && IntW<DT, U, BITS>::kFold) {
+    if (a.M == 1) return launch_intb_v<DT, 1, AM, U, XS, BITS, true>(a);
+  }
+  launch_intb_v<DT, 1, AM, U, XS, BITS, false>(a);
+}
+
 template <int DT, int U, bool XS, int BITS>
 static void launch_intb_mode(int am, int mt, const DecodeArgs& a) {
-  if (am == AM_XGATHER) return launch_intb_v<DT, 1, AM_XGATHER, U, XS, BITS>(a);
+  if (am == AM_XGATHER) return launch_intb_packed<DT, AM_XGATHER, U, XS, BITS>(a);
   if constexpr (XS) {
-    launch_intb_v<DT, 1, AM_XSTAGED, U, true, BITS>(a);  // the only other mode that scales
+    launch_intb_packed<DT, AM_XSTAGED, U, true, BITS>(a);  // the only other mode that scales
   } else {
     if constexpr (IntW<DT, U, BITS>::kFold) {
       if (am == AM_PACKED && a.M >= 3 && a.N >= W4A16_WIDE_MIN_N)
         return launch_intb_wide<DT, U, BITS>(a);
     }
-    if (am == AM_PACKED) launch_intb_v<DT, 1, AM_PACKED, U, false, BITS>(a);
+    if (am == AM_PACKED) launch_intb_packed<DT, AM_PACKED, U, false, BITS>(a);
     else if (mt == 1) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);
     else if (mt == 2) launch_intb_v<DT, 2, AM_FULL, U, false, BITS>(a);
     else launch_intb_v<DT, 4, AM_FULL, U, false, BITS>(a);
