@@ -54,7 +54,7 @@ def kernel_name(M, K, N):
     layers of 100 Mi weights; 16 on layers of 24 Mi weights with N >= 5120,
     else 24); otherwise the
     decode kernel, where M <= 4 rows are gathered in the kernel when the
-    staged rows + permutation take at most 56 KB per workgroup and 12 MiB over
+    staged rows + permutation take at most 72 KB per workgroup and 17 MiB over
     the N/16 workgroups, else a preparation pass permutes them first; one row
     (M = 1) has an instantiation of its own (the one-row form of the fold)."""
     kb = lambda b: (b + 1023) // 1024 * 1024
@@ -64,7 +64,7 @@ def kernel_name(M, K, N):
         return "wq_prefill_kernel<f16, INT 4-bit>"      # the large-M kernel
     if M <= 4:
         staged = kb(M * K * 2) + kb(K * 4)
-        mode = ("xgather" if staged <= 56 * 1024 and ((N + 15) // 16) * staged <= 12 << 20
+        mode = ("xgather" if staged <= 72 * 1024 and ((N + 15) // 16) * staged <= 17 << 20
                 else "packed")
         return "intb_decode_kernel<f16, MT=1, %s, 4-bit%s>" % (mode, ", one row" if M == 1 else "")
     mt = 1 if M <= 16 else (2 if M <= 32 else 4)

@@ -34,10 +34,11 @@ constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; 
 
 // Largest LDS footprint of the staged activations (+ permutation, + input
 // scales) per workgroup: past it the staging costs more than the separate
-// preparation pass it saves (measured on MI355X), and with the reduction
-// buffer it stays within a workgroup's 64 KB and leaves room for two
-// workgroups per CU.
-constexpr int64_t kMaxXlds = 56 * 1024;
+// preparation pass it saves (measured on MI355X; 72 rather than 56 KB takes
+// the 11008 x 4096 layer at M = 1, 66 KB with its permutation, from 11.7 to
+// 10.8 us per call), and with the reduction buffer it leaves room for two
+// workgroups in a CU's 160 KB.
+constexpr int64_t kMaxXlds = 72 * 1024;
 
 // Multiply-accumulate the 4 MFMA steps of one K tile given its 4 B operands.
 template <int DT, int AM, int MT, int NA, int NACC>
@@ -763,8 +764,9 @@ static void allow_dynamic_lds(const void* kernel) {
 // beats a separate preparation pass: every workgroup copies the rows (and the
 // permutation and scales) from L2, so the cost grows with the grid, while the
 // pass costs about one launch (measured crossover on MI355X: staging saves
-// ~1 us on 4096 x 4096 layers and costs ~10 us on 5120 x 55296 ones).
-constexpr int64_t kMaxStagedTotal = (int64_t)12 << 20;
+// ~1 us on 4096 x 4096 layers, breaks even on 4096 x 11008 at M = 1 (688 x 24
+// KB) and costs ~10 us on 5120 x 55296 ones).
+constexpr int64_t kMaxStagedTotal = (int64_t)17 << 20;
 
 // Activation mode and row tiles per workgroup row block for M rows of a
 // [N, K] layer; gather: an act-order permutation is to be applied, xs: AWQ

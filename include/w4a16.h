@@ -176,8 +176,8 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
  * M >= 5 on layers of 100 Mi weights and more; M >= 16, or 24 when N < 5120, on
  * layers of 24 Mi weights and more) when it splits K over S workgroups.  A given call may need less, or nothing: no pass runs where
  * the decode kernel gathers x[:, perm] and/or divides by s itself (M <= 4,
- * the rows, the permutation and the scales staged on chip: at most 56 KB per
- * workgroup and 12 MiB over its grid of N/16 workgroups); each call
+ * the rows, the permutation and the scales staged on chip: at most 72 KB per
+ * workgroup and 17 MiB over its grid of N/16 workgroups); each call
  * validates what it needs.
  * Calls that overlap in time must not share a workspace.
  */

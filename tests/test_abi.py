@@ -92,13 +92,14 @@ def test_gemm_validation_without_gpu():
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, NULL, 0, NULL) == 5
     # the size covers every call at a shape, with or without a permutation and
     # AWQ input scales: M <= 4 rows (with the permutation and the scales) that
-    # the decode kernel stages on chip need no workspace (up to 56 KB per
-    # workgroup and 12 MiB over the grid: 256 x 24 KB here) ...
+    # the decode kernel stages on chip need no workspace (up to 72 KB per
+    # workgroup and 17 MiB over the grid: 256 x 24 KB and 256 x 56 KB here) ...
     assert L.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
+    assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) == 0
     # ... larger ones are prepared in a pass: M * K * 2 bytes
-    assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) >= 4 * 4096 * 2     # 256 x 56 KB
+    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) >= 11008 * 2     # 88 KB per workgroup
+    assert L.w4a16_workspace_bytes(4, 6144, 4096, 128) >= 4 * 4096 * 2    # 384 x 56 KB
     assert L.w4a16_workspace_bytes(1, 55296, 5120, 128) >= 5120 * 2        # 3456 workgroups
-    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) >= 11008 * 2
     assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) >= 4 * 11008 * 2
     assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 5 * 4096 * 2
     # w4a16_gemm_xscale validates what the call needs (each case below fails
