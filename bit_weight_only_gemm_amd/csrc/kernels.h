@@ -67,13 +67,14 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
 // (HIP graphs of calls over weight sets larger than the caches): from 5 rows
 // on layers of 100 Mi weights and more, from 16 rows on layers of 24 Mi weights
 // and more with N >= 5120 (4096 x 11008 at M = 16: 18.6 us against 20.9), from
-// 24 rows on such layers with fewer columns (11008 x 4096: decode faster
-// through M = 16), and from 32 rows otherwise.
+// 17 rows on such layers with fewer columns (11008 x 4096, act-order: 19.3 us
+// against 21.8 at M = 16, 22.2 against 21.8 at M = 17, where the decode kernel
+// takes 32-row tiles), and from 32 rows otherwise.
 inline bool use_prefill(int64_t M, int64_t N, int64_t K) {
   if (M >= 32) return true;
   const int64_t w = N * K;
   if (w >= (int64_t)100 << 20) return M >= 5;
-  if (w >= (int64_t)24 << 20) return M >= (N >= 5120 ? 16 : 24);
+  if (w >= (int64_t)24 << 20) return M >= (N >= 5120 ? 16 : 17);
   return false;
 }
 void launch_int_prefill(const void* x, const void* codes_r, const void* scales_r,

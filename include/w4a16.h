@@ -173,7 +173,7 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
  * (covering calls with a column permutation and with input scales): room for
  * the prepared activations M*K*2 where a separate pass writes x[:, perm]
  * and/or x / s, plus the fp32 partials S*M*N*4 of the large-M kernel (M >= 32;
- * M >= 5 on layers of 100 Mi weights and more; M >= 16, or 24 when N < 5120, on
+ * M >= 5 on layers of 100 Mi weights and more; M >= 16, or 17 when N < 5120, on
  * layers of 24 Mi weights and more) when it splits K over S workgroups.  A given call may need less, or nothing: no pass runs where
  * the decode kernel gathers x[:, perm] and/or divides by s itself (M <= 4,
  * the rows, the permutation and the scales staged on chip: at most 72 KB per
