@@ -56,7 +56,8 @@ def kernel_name(M, K, N):
     decode kernel, where M <= 4 rows are gathered in the kernel when the
     staged rows + permutation take at most 72 KB per workgroup and 17 MiB over
     the N/16 workgroups, else a preparation pass permutes them first; one row
-    (M = 1) has an instantiation of its own (the one-row form of the fold)."""
+    (M = 1) has an instantiation of its own (the one-row form of the fold);
+    more rows take the full-row modes."""
     kb = lambda b: (b + 1023) // 1024 * 1024
     w = N * K
     if (M >= 32 or (w >= 100 << 20 and M >= 5)
@@ -68,7 +69,10 @@ def kernel_name(M, K, N):
                 else "packed")
         return "intb_decode_kernel<f16, MT=1, %s, 4-bit%s>" % (mode, ", one row" if M == 1 else "")
     mt = 1 if M <= 16 else (2 if M <= 32 else 4)
-    return "intb_decode_kernel<f16, MT=%d, full, 4-bit>" % mt
+    # full rows: direct loads for at most 8 rows on at most 4096 columns, else
+    # whole-line loads and a transpose through LDS
+    return "intb_decode_kernel<f16, MT=%d, %s, 4-bit>" % (mt, "full" if M <= 8 and N <= 4096
+                                                          else "full-t")
 
 
 def parse():

@@ -21,15 +21,17 @@ constexpr int RUN = 8;                  // K tiles per meta run and ring pass
 
 // Activation modes.  PACKED: M <= 4, one 16-byte load per lane and K tile
 // carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
-// tile.  XGATHER: PACKED for an act-order weight, with the M rows of x and
+// tile.  FULLT: FULL with the loads taking whole lines and an LDS transpose
+// to the MFMA layout.  XGATHER: PACKED for an act-order weight, with the M rows of x and
 // the permutation staged in LDS once per workgroup; the operand is gathered
 // from LDS, x[m][perm[k]], so no separate permutation pass runs.  XSTAGED:
 // PACKED with the M rows of x staged in LDS and read from there (used with
 // AWQ input scales, below).  With input scales (XS) the staged rows are
 // divided by s in place, once per workgroup, before the loop: each x element
 // is scaled once per workgroup instead of once per use.
-enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3 };
-constexpr bool is_packed(int am) { return am != AM_FULL; }
+enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3, AM_FULLT = 4 };
+constexpr bool is_full(int am) { return am == AM_FULL || am == AM_FULLT; }
+constexpr bool is_packed(int am) { return !is_full(am); }
 constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; }
 
 // Largest LDS footprint of the staged activations (+ permutation, + input
@@ -297,9 +299,13 @@ struct Nf4W {
 };
 
 // Activations of one K tile.  PACKED: one vector, lane row r = 4 j + m holds
-// step j of batch row m.  FULL: MT x 4 vectors (row tile m, step j), lane row
-// r = batch row.  Rows >= M read 0 through the descriptor range; k >= K (only
-// in a half NF4 tile) uses an out-of-range offset.
+// step j of batch row m.  FULL: MT x 4 vectors, vector 4m + j the A operand
+// of row tile m, step j (lane row r = batch row: 16 rows x 64 bytes per
+// load).  FULLT: vector 4m + i of lane l is 16-byte chunk l & 15 of row
+// 4i + (l >> 4) of row tile m (whole 128-byte lines per load), which xpose_a
+// puts into the MFMA layout through LDS.  Rows >= M read 0 through the
+// descriptor range; k >= K (only in a half NF4 tile) uses an out-of-range
+// offset.
 // Staged activations in LDS: x rows [M][K] at xl, the permutation int32[K] at
 // pl.
 struct XLds {
@@ -342,6 +348,18 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
     uint32_t off = (uint32_t)m * (uint32_t)K * 2u + (uint32_t)kin * 2u;
     if constexpr (WP::kRaggedK) off = (t * 128 + kin < K) ? off : kOutOfRange;
     a[0] = __builtin_bit_cast(typename Op<DT>::vec, bld128(rx, off, t * 256));
+  } else if constexpr (AM == AM_FULLT) {
+    const int c = lane & 15;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t row = (uint32_t)(m * 16 + 4 * i + b);
+        uint32_t off = row * (uint32_t)K * 2u + (uint32_t)c * 16u;
+        if constexpr (WP::kRaggedK) off = (t * 128 + c * 8 < K) ? off : kOutOfRange;
+        a[m * 4 + i] = __builtin_bit_cast(typename Op<DT>::vec, bld128(rx, off, t * 256));
+      }
+    }
   } else {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -356,6 +374,35 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
     }
   }
 }
+
+// FULLT mode: the contiguous chunks of load_a to the A operands of the 4 MFMA
+// steps, through this wave's 4 KB per row tile of LDS at xw.  Chunk c of row R
+// sits in 16-byte slot 16 R + (c ^ R): the stores (a row per 16 lanes) and the
+// loads (16 rows of one chunk per 16 lanes) each cover all 64 banks.
+template <int DT, int MT, class WP>
+__device__ __forceinline__ void xpose_a(const typename Op<DT>::vec (&a)[MT * 4],
+                                        typename Op<DT>::vec (&o)[MT * 4], uint8_t* xw,
+                                        int lane) {
+  typedef typename Op<DT>::vec vec;
+  const int c = lane & 15, b = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int R = 4 * i + b;
+      *(vec*)(xw + (m * 256 + R * 16 + (c ^ R)) * 16) = a[m * 4 + i];
+    }
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ch = WP::xk(j, b) >> 3;
+      o[m * 4 + j] = *(const vec*)(xw + (m * 256 + r * 16 + (ch ^ r)) * 16);
+    }
+}
+
+// LDS bytes of the FULLT mode's transpose: 4 KB per row tile and wave.
+__host__ __device__ constexpr uint32_t xpose_bytes(int MT) { return (uint32_t)(DW * MT * 4096); }
 
 // Bytes of LDS the staged activations and permutation take, each region
 // rounded up to whole 1 KB blocks.
@@ -514,7 +561,13 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
             }
           } else {
             wp.operands(ring[s], s, mc, b);
-            mma_tile<DT, AM, MT, NA, NACC>(b, ra[sa], acc);
+            if constexpr (AM == AM_FULLT) {
+              typename Op<DT>::vec at[NA];
+              xpose_a<DT, MT, WP>(ra[sa], at, xlds + wave * MT * 4096, lane);
+              mma_tile<DT, AM, MT, NA, NACC>(b, at, acc);
+            } else {
+              mma_tile<DT, AM, MT, NA, NACC>(b, ra[sa], acc);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -772,7 +825,14 @@ constexpr int64_t kMaxStagedTotal = (int64_t)17 << 20;
 // [N, K] layer; gather: an act-order permutation is to be applied, xs: AWQ
 // input scales.  For M <= 4 both are done on the rows staged in LDS when they
 // fit and the grid is small enough (staging x alone does not beat per-tile
-// loads).  Otherwise the caller prepares x first.
+// loads).  Otherwise the caller prepares x first.  More rows: FULLT, except
+// for at most 8 rows on layers of at most 4096 columns (at most one
+// workgroup per CU, one wave per SIMD), where the transpose's LDS round trip
+// is not hidden and the direct loads (fewer rows, fewer lines) are faster.
+// Measured on MI355X, act-order whole calls, FULL -> FULLT: 11008 x 4096 at
+// M = 5 14.8 -> 16.3 us, M = 8 15.9 -> 16.5, M = 12 17.8 -> 16.8, M = 16
+// 19.3 -> 17.0; 4096 x 11008 at M = 8 16.6 -> 14.1; 5120 x 5120 at M = 12
+// 13.6 -> 11.1; NF4 28672 x 8192 at M = 8 65.5 -> 54.1.
 static int pick_mode(int64_t M, int64_t N, int64_t K, bool gather, bool xs, int* mt) {
   if (M <= 4) {
     *mt = 1;
@@ -782,7 +842,7 @@ static int pick_mode(int64_t M, int64_t N, int64_t K, bool gather, bool xs, int*
     return AM_PACKED;
   }
   *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  return AM_FULL;
+  return (M <= 8 && N <= 4096) ? AM_FULL : AM_FULLT;
 }
 
 // One decode launch.  a: the call's arguments (xsc non-null only when the
@@ -798,8 +858,8 @@ struct DecodeArgs {
 template <int DT, int MT, int AM, int U, bool XS, int BITS, bool ONE = false>
 static void launch_intb_v(const DecodeArgs& a) {
   const dim3 grid((unsigned)ceil_div(a.N, 16), (unsigned)ceil_div(a.M, 16 * MT));
-  const size_t lds =
-      is_staged(AM) ? xlds_bytes((int)a.M, (int)a.K, AM == AM_XGATHER, XS) : 0;
+  const size_t lds = is_staged(AM) ? xlds_bytes((int)a.M, (int)a.K, AM == AM_XGATHER, XS)
+                                   : (AM == AM_FULLT ? xpose_bytes(MT) : 0);
   if (lds) allow_dynamic_lds((const void*)intb_decode_kernel<DT, MT, AM, U, XS, BITS, ONE>);
   // a symmetric weight: the zeros descriptor gets an empty range over a valid
   // base and every zero field reads 0 ^ 2^(BITS-1)
@@ -859,9 +919,10 @@ static void launch_intb_mode(int am, int mt, const DecodeArgs& a) {
         return launch_intb_wide<DT, U, BITS>(a);
     }
     if (am == AM_PACKED) launch_intb_packed<DT, AM_PACKED, U, false, BITS>(a);
-    else if (mt == 1) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);
-    else if (mt == 2) launch_intb_v<DT, 2, AM_FULL, U, false, BITS>(a);
-    else launch_intb_v<DT, 4, AM_FULL, U, false, BITS>(a);
+    else if (am == AM_FULL) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);
+    else if (mt == 1) launch_intb_v<DT, 1, AM_FULLT, U, false, BITS>(a);
+    else if (mt == 2) launch_intb_v<DT, 2, AM_FULLT, U, false, BITS>(a);
+    else launch_intb_v<DT, 4, AM_FULLT, U, false, BITS>(a);
   }
 }
 

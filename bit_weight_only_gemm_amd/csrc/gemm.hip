@@ -157,7 +157,9 @@ static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, con
                          const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
-  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), 0, stream,
+  const size_t lds = AM == AM_FULLT ? xpose_bytes(MT) : 0;
+  if (lds) allow_dynamic_lds((const void*)nf4_decode_kernel<DT, MT, AM, BATCH>);
+  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), lds, stream,
                (const uint16_t*)x, q, aq, asc, L, (uint16_t*)out, (int)M, (int)N, (int)K,
                (int)ceil_div(K, 128));
 }
@@ -170,12 +172,14 @@ static void launch_nf4_dt(const void* x, const uint8_t* q, const uint8_t* aq, co
   const int am = pick_mode(M, N, K, false, false, &mt);
   if (am == AM_PACKED)
     launch_nf4_v<DT, 1, AM_PACKED, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
-  else if (mt == 1)
+  else if (am == AM_FULL)
     launch_nf4_v<DT, 1, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+  else if (mt == 1)
+    launch_nf4_v<DT, 1, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
   else if (mt == 2)
-    launch_nf4_v<DT, 2, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+    launch_nf4_v<DT, 2, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
   else
-    launch_nf4_v<DT, 4, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+    launch_nf4_v<DT, 4, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
 }
 
 int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K) {
