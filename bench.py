@@ -51,8 +51,8 @@ def call_bytes(M, K, N):
 def kernel_name(M, K, N):
     """Kernel instantiation the library picks for an act-order call with M
     rows (f16).  Mirrors its rules: the large-M kernel from 32 rows (5 on
-    layers of 100 Mi weights; 16 on layers of 24 Mi weights with N >= 5120,
-    else 17); otherwise the
+    layers of 100 Mi weights; 17 on layers of 24 Mi weights with N < 5120);
+    otherwise the
     decode kernel, where M <= 4 rows are gathered in the kernel when the
     staged rows + permutation take at most 72 KB per workgroup and 17 MiB over
     the N/16 workgroups, else a preparation pass permutes them first; one row
@@ -61,7 +61,7 @@ def kernel_name(M, K, N):
     kb = lambda b: (b + 1023) // 1024 * 1024
     w = N * K
     if (M >= 32 or (w >= 100 << 20 and M >= 5)
-            or (w >= 24 << 20 and M >= (16 if N >= 5120 else 17))):
+            or (w >= 24 << 20 and N < 5120 and M >= 17)):
         return "wq_prefill_kernel<f16, INT 4-bit>"      # the large-M kernel
     if M <= 4:
         staged = kb(M * K * 2) + kb(K * 4)

@@ -65,16 +65,17 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
 // kernel's hardly changes with M below 32 rows but carries the fixed cost of
 // its split-K reduction launch.  Measured whole-call crossovers on MI355X
 // (HIP graphs of calls over weight sets larger than the caches): from 5 rows
-// on layers of 100 Mi weights and more, from 16 rows on layers of 24 Mi weights
-// and more with N >= 5120 (4096 x 11008 at M = 16: 18.6 us against 20.9), from
-// 17 rows on such layers with fewer columns (11008 x 4096, act-order: 19.3 us
-// against 21.8 at M = 16, 22.2 against 21.8 at M = 17, where the decode kernel
-// takes 32-row tiles), and from 32 rows otherwise.
+// on layers of 100 Mi weights and more (5120 x 55296 at M = 5: 45.4 us against
+// 52.3), from 17 rows on layers of 24 Mi weights and more with N < 5120
+// (11008 x 4096, act-order: 16.8 us against 21.8 at M = 16, 22.1 against 21.5
+// at M = 20, where the decode kernel takes 32-row tiles on a grid of one
+// workgroup per CU), and from 32 rows otherwise (4096 x 11008, act-order, at
+// M = 24: 17.8 against 19.5; 5120 x 5120 at M = 24: 14.4 against 14.7).
 inline bool use_prefill(int64_t M, int64_t N, int64_t K) {
   if (M >= 32) return true;
   const int64_t w = N * K;
   if (w >= (int64_t)100 << 20) return M >= 5;
-  if (w >= (int64_t)24 << 20) return M >= (N >= 5120 ? 16 : 17);
+  if (w >= (int64_t)24 << 20 && N < 5120) return M >= 17;
   return false;
 }
 void launch_int_prefill(const void* x, const void* codes_r, const void* scales_r,
@@ -86,14 +87,13 @@ void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* ab
                         int64_t M, int64_t N, int64_t K, int dtype, hipStream_t stream);
 // Whether nf4_gemm runs the large-M kernel at this shape, and the workspace
 // bytes it then needs.  Its codebook dequant costs about twice the INT4 one,
-// so the crossovers (measured on whole calls, bf16) are later than INT4's:
-// from 16 rows on layers of 100 Mi weights and more (28672 x 8192 at M = 16:
-// 81.1 us against 85.9), from 24 rows on layers of 24 Mi weights and more
-// (4096 x 11008 at M = 24: 26.2 against 28.0), from 64 rows otherwise.
+// so the crossovers (measured in bf16) are later than INT4's: past the
+// decode kernel's 32-row tiles on layers of 24 Mi weights and more (28672 x
+// 8192: 77.0 us against 80.8 at M = 32, 143.5 against 119.7 at M = 48; 4096 x
+// 11008: 18.9 against 24.8 at M = 32), from 64 rows otherwise.
 inline bool nf4_use_prefill(int64_t M, int64_t N, int64_t K) {
   const int64_t w = N * K;
-  return K % 128 == 0 && (M >= 64 || (w >= (int64_t)100 << 20 && M >= 16) ||
-                          (w >= (int64_t)24 << 20 && M >= 24));
+  return K % 128 == 0 && (M >= 64 || (w >= (int64_t)24 << 20 && M > 32));
 }
 int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K);
 

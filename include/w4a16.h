@@ -173,8 +173,9 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
  * (covering calls with a column permutation and with input scales): room for
  * the prepared activations M*K*2 where a separate pass writes x[:, perm]
  * and/or x / s, plus the fp32 partials S*M*N*4 of the large-M kernel (M >= 32;
- * M >= 5 on layers of 100 Mi weights and more; M >= 16, or 17 when N < 5120, on
- * layers of 24 Mi weights and more) when it splits K over S workgroups.  A given call may need less, or nothing: no pass runs where
+ * M >= 5 on layers of 100 Mi weights and more; M >= 17 on layers of 24 Mi
+ * weights and more with N < 5120) when it splits K over S workgroups.  A
+ * given call may need less, or nothing: no pass runs where
  * the decode kernel gathers x[:, perm] and/or divides by s itself (M <= 4,
  * the rows, the permutation and the scales staged on chip: at most 72 KB per
  * workgroup and 17 MiB over its grid of N/16 workgroups); each call
@@ -319,9 +320,8 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_
 
 /*
  * Workspace bytes nf4_gemm needs at this shape: the fp32 split-K partials of
- * the large-M kernel (K % 128 == 0 and M >= 64; M >= 16 on layers of 100 Mi
- * weights and more, M >= 24 on layers of 24 Mi weights and more) when it
- * splits K; 0 otherwise.
+ * the large-M kernel (K % 128 == 0 and M >= 64; M >= 33 on layers of 24 Mi
+ * weights and more) when it splits K; 0 otherwise.
  */
 int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
 

@@ -130,7 +130,7 @@ def test_nf4_28672x8192():
     aq, asc = nf4.double_quant(absmax)
     wd_sub = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, asc, 64, "bf16", codebook=L)
     wd = wd_sub[2 * np.searchsorted(pairs, 2 * (cols // 2)) + (cols & 1)]
-    for M in (1, 15, 16, 32):      # 15: the decode kernel, 16 and 32: the large-M kernel
+    for M in (1, 15, 32, 33):      # up to 32: the decode kernel, 33: the large-M kernel
         xb = synth.to_bf16_bits(synth.activations("C5/x/%d" % M, M, K))
         y = w4.nf4_gemm(bits_to_tensor(xb, "bf16"), t)
         torch.cuda.synchronize()

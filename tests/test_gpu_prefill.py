@@ -140,12 +140,12 @@ def test_big_layer_m16_uses_large_m_kernel_sampled_columns():
     assert compare_gemm(y, xb, wd, "bf16", cols=cols) <= TOL
 
 
-@pytest.mark.parametrize("M,N,K,dtype", [(5, 20480, 5120, "f16"), (16, 11008, 4096, "bf16"),
-                                         (15, 11008, 4096, "f16"), (17, 4096, 11008, "bf16"),
-                                         (16, 4096, 11008, "f16")])
+@pytest.mark.parametrize("M,N,K,dtype", [(5, 20480, 5120, "f16"), (4, 20480, 5120, "bf16"),
+                                         (32, 11008, 4096, "bf16"), (31, 11008, 4096, "f16"),
+                                         (17, 4096, 11008, "bf16"), (16, 4096, 11008, "f16")])
 def test_kernel_crossover_rows_act_order_sampled_columns(M, N, K, dtype):
     # the fewest rows that take the large-M kernel (32-row workgroup tiles)
-    # on a 100 Mi-weight layer (5) and on 43 Mi-weight layers (16 with 11008
+    # on a 100 Mi-weight layer (5) and on 43 Mi-weight layers (32 with 11008
     # columns, 17 with 4096), and one row fewer (the decode kernel),
     # act-order; every 61st output column
     say("crossover", M, N, K, dtype)
