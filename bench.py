@@ -95,7 +95,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(requested --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

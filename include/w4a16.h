@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   W4A16_OK = 0,
   W4A16_ERR_INVALID_ARG = 1,   /* bad size, NULL required pointer, unknown dtype */
-  W4A16_ERR_UNSUPPORTED = 2,   /* valid request this build does not implement   */
+  W4A16_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement */
   W4A16_ERR_MISALIGNED = 3,    /* a device pointer is not 16-byte aligned        */
   W4A16_ERR_BAD_GIDX = 4,      /* g_idx out of range or a group not of size G     */
   W4A16_ERR_WORKSPACE = 5,     /* workspace given but smaller than required       */
