@@ -228,3 +228,24 @@ def test_gemm_subnormal_activation_is_not_flushed(dtype):
     want = 15 * 1024.0 * sub          # 1.875 * 2^e: exact in both output types
     assert np.all(y[0] == want), y[0][:4]
     assert np.all(y[1] == -want)
+
+
+@pytest.mark.parametrize("M,N,K", [(6, 160, 1024), (12, 160, 1024), (16, 4112, 512), (24, 208, 2048)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_full_row_modes_onehot_exact(M, N, K, dtype):
+    # the decode kernel's full-row modes, act-order: direct loads (6 rows on
+    # 160 columns) and whole-line loads through the LDS transpose (12, 16 on
+    # 4112 columns, 24 rows in two row tiles).  One nonzero 1.0 per row puts
+    # one dequantized weight in each output: any misplaced chunk of the
+    # transpose shows as a wrong value
+    say("full-row onehot", M, N, K, dtype)
+    W, gi, _ = int4_inputs("gpu/gemm/fullrow/%d/%d" % (N, K), N, K, act_order=True)
+    _, packed = gpu_int4_pack(W, gi)
+    ks = (np.arange(M) * 37 + 5) % K
+    x = np.zeros((M, K), dtype=np.float32)
+    x[np.arange(M), ks] = 1.0
+    y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, dtype), dtype), packed))
+    cols = np.unique(np.concatenate([np.arange(0, N, 7), [N - 1]]))
+    wd = oracle_int4_rows(W, gi, cols, dtype)
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r][cols], wd[:, k]), (r, k)
