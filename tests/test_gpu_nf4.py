@@ -158,3 +158,22 @@ def test_nf4_wide_layer_sampled_columns(N, M, dtype):
     aq, sc = nf4.double_quant(absmax)
     wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)[cols]
     assert compare_gemm(y, xb, wd, dtype, cols=cols) <= TOL
+
+
+@pytest.mark.parametrize("M", [12, 20])
+def test_nf4_full_rows_onehot_exact_ragged_k(M):
+    # the decode kernel's whole-line loads and LDS transpose with a half last
+    # K tile (K % 128 == 64): every output is one dequantized weight
+    N, K = 80, 1088
+    say("nf4 full-row onehot", M)
+    W = synth.weights("gpu/nf4/fullrow", N, K)
+    p = _pack(W)
+    codes, absmax = nf4.quantize_nf4(W, 64)
+    aq, sc = nf4.double_quant(absmax)
+    wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, "bf16")
+    ks = (np.arange(M) * 91 + 1087) % K          # includes k = 1087, in the half tile
+    x = np.zeros((M, K), dtype=np.float32)
+    x[np.arange(M), ks] = 1.0
+    y = tensor_bits(w4.nf4_gemm(bits_to_tensor(synth.to_bf16_bits(x), "bf16"), p))
+    for r, k in enumerate(ks):
+        assert np.array_equal(y[r], wd[:, k]), (r, k)
