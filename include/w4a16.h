@@ -191,11 +191,11 @@ int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_siz
  *   w[n, k] = round_dtype(fp32(q - z) * fp32(s))  (q, z, s of column n and the
  *             group of permuted column k; z = 8 when zeros_r is NULL),
  * with fp32 accumulation and one round-to-nearest-even to the output dtype.
- * Paths that apply s and z after a K tile's sum (M <= 4; 5..16 rows with
- * group_size >= 128 where the decode kernel takes the call; the large-M
- * kernel's 32-row tiles; not 8-bit codes in bf16) use fp32(q - z) * fp32(s)
- * without rounding it first: the same real product, at least as close to the
- * exact one.  A row with one nonzero x, a power of two, gives round_dtype(w)
+ * Paths that apply s and z after a K tile's sum use fp32(q - z) * fp32(s)
+ * without rounding it first (the same real product, at least as close to the
+ * exact one): M <= 4; 9..16 rows, or 5..16 on layers of more than 4096
+ * columns, with group_size >= 128 in the decode kernel; the large-M kernel's
+ * 32-row tiles with group_size >= 128; never 8-bit codes in bf16.  A row with one nonzero x, a power of two, gives round_dtype(w)
  * on every path.
  *   x      [M, K] row-major, dtype;  out [M, N] row-major, dtype.
  *   perm   int32 [K] from w4a16_repack (or NULL for identity).
