@@ -1,6 +1,7 @@
 """GPU parity of the kernel paths that apply the scale and zero after the K sum
-(the decode kernel's packed modes, M <= 4; the large-M kernel's 32-row tiles,
-M <= 32): one-hot rows exact for every group size and code form, and
+(the decode kernel's packed modes, M <= 4, and its FULLT mode with one row
+tile, M <= 16 with G >= 128; the large-M kernel's 32-row tiles, M <= 32):
+one-hot rows exact for every group size and code form, and
 activations with large outlier channels within the tolerance (the o + q
 operands put o x in every partial sum, which the fold subtracts again)."""
 
@@ -38,7 +39,7 @@ CASES = [(4, 128, False, True), (4, 64, True, False), (4, 32, False, True), (4, 
 
 
 @pytest.mark.parametrize("bits,G,sym,act", CASES)
-@pytest.mark.parametrize("M", [1, 3, 32])
+@pytest.mark.parametrize("M", [1, 3, 12, 32])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_fold_onehot_exact(bits, G, sym, act, M, dtype):
     N, K = 160, 1024
@@ -57,7 +58,7 @@ def test_fold_onehot_exact(bits, G, sym, act, M, dtype):
 
 
 @pytest.mark.parametrize("bits,G,sym,act", CASES)
-@pytest.mark.parametrize("M", [2, 4, 32])
+@pytest.mark.parametrize("M", [2, 4, 12, 32])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_fold_outlier_channels(bits, G, sym, act, M, dtype):
     # 1 % of the input channels x20 and four channels scaled further (x 2^8 in
