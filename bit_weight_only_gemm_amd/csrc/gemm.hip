@@ -22,18 +22,25 @@
 //    carries the activations of all 4 MFMA steps of the tile (see "packed"
 //    below).
 //  * Each 32-bit code word becomes an 8-element MFMA operand, multiplied with
-//    v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation.  For M > 4 it is
-//    dequantized exactly (the routine the dequant export uses).  For M <= 4
-//    (integer codes) it is the codes alone, o + q, and each lane applies the
-//    scale and zero of its column and MFMA step after the step's MFMA, with
-//    the step's activation row sums from one more MFMA against ones: the
-//    same real products without a 16-bit rounding of each weight, and far
-//    fewer VALU instructions per code.
+//    v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation.  For M <= 4 (integer
+//    codes) it is the codes alone, o + q, and each lane applies the scale and
+//    zero of its column and MFMA step after the step's MFMA, with the step's
+//    activation row sums from one more MFMA against ones: the same real
+//    products without a 16-bit rounding of each weight, and far fewer VALU
+//    instructions per code.  For 5..16 rows with G >= 128 the same is done
+//    per K tile (FULLT mode, below); otherwise the code word is dequantized
+//    exactly (the routine the dequant export uses).
 //  * "Packed" activations (M <= 4): the 16 A-operand rows are 4 K-steps x 4
 //    batch rows (row 4j + m holds step j of batch row m), so one load feeds
 //    the 4 MFMAs of a tile; step j accumulates into its own tile acc[j], whose
 //    rows 4j .. 4j+3 are the wanted products (the other rows mix steps and are
 //    dropped).  At the end a cross-lane shuffle adds the 4 step tiles.
+//  * Full rows (M > 4): 16 A-operand rows per row tile.  The MFMA layout puts
+//    row l & 15 in lane l, so direct 16-byte loads touch 16 rows x 64 bytes
+//    each; the FULLT mode instead loads whole 128-byte lines (lane l: chunk
+//    l & 15 of row 4i + (l >> 4)) and transposes them through a swizzled
+//    4 KB of LDS per wave and row tile.  Direct loads remain for at most 8
+//    rows on layers of at most 4096 columns.
 //  * Latency hiding: a ring of 8 tiles of codes (and of activations) is in
 //    flight per wave.  All loads are buffer loads with per-lane offsets fixed
 //    and the tile index in the wave-uniform offset, so the loop has no
