@@ -76,6 +76,28 @@ def nf4_workspace_bytes(M, N, K, blocksize=64):
     return int(_lib.lib().nf4_workspace_bytes(M, N, K, blocksize))
 
 
+def _names(fn, *args):
+    buf = ctypes.create_string_buffer(1024)
+    n = ctypes.c_int64(0)
+    _lib.check(fn(*args, buf, len(buf), ctypes.byref(n)), fn.__name__)
+    return buf.value.decode()
+
+
+def w4a16_gemm_plan(M, N, K, group_size=GROUP, bits=4, dtype=torch.float16, perm=False,
+                    x_scale=False, workspace=True):
+    """Kernels a w4a16_gemm call of this shape launches (host-only query): a
+    list of instantiation names as the profiler reports them, in launch order."""
+    s = _names(_lib.lib().w4a16_gemm_plan, M, N, K, group_size, bits, _DT[dtype], int(perm),
+               int(x_scale), int(workspace))
+    return s.split(" + ")
+
+
+def nf4_gemm_plan(M, N, K, blocksize=64, dtype=torch.bfloat16, workspace=True):
+    """Kernels an nf4_gemm call of this shape launches (host-only query)."""
+    return _names(_lib.lib().nf4_gemm_plan, M, N, K, blocksize, _DT[dtype],
+                  int(workspace)).split(" + ")
+
+
 def workspace(nbytes, device="cuda"):
     """A zero-filled workspace of at least ``nbytes`` (None when 0)."""
     if nbytes <= 0:

@@ -39,6 +39,9 @@ SIGNATURES = {
     "nf4_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
     "nf4_gemm": (_c.c_int, [_p, _p, _p, _p, _i32, _p, _i64, _i64, _i64, _i32, _p, _i64, _p]),
     "nf4_dequant": (_c.c_int, [_p, _p, _p, _i64, _i64, _i32, _i32, _p, _p]),
+    "w4a16_gemm_plan": (_c.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _p,
+                                   _i64, _p]),
+    "nf4_gemm_plan": (_c.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p]),
 }
 
 _lib = None

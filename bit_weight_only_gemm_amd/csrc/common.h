@@ -37,17 +37,10 @@ enum { DT_F16 = 0, DT_BF16 = 1 };
 // 0x64006400 (two fp16 1024.0) held in a VGPR: a literal cannot be an operand
 // of the 3-operand v_and_or_b32 on gfx9, so without this the compiler splits
 // the nibble insert into v_and_b32 + v_or_b32.
-#ifndef W4A16_MAGIC_REG
-#define W4A16_MAGIC_REG 1
-#endif
 __device__ __forceinline__ uint32_t opaque_magic() {
-#if W4A16_MAGIC_REG
   uint32_t m;
   asm("v_mov_b32 %0, 0x64006400" : "=v"(m));
   return m;
-#else
-  return 0x64006400u;
-#endif
 }
 
 // 8-element MFMA operand type for a dtype.
@@ -150,14 +143,26 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QP& p)
 
 // The codes alone as MFMA operand values, for kernels that apply the scale and
 // zero after summing over a group: 0x6400 | q is the fp16 value 1024 + q and
-// 0x4300 | q the bf16 value 128 + q (q < 128), both exact.  kOffset is that
-// 1024 or 128.
+// 0x4300 | q the bf16 value 128 + q (q < 128), both exact: o + q with o = 1024
+// or 128.
+//
+// Such a kernel forms, per group and output, s * (T - Z) with
+// T = sum_k x_k (o + q_k) and Z = sum_k x_k (o + z), both from MFMAs over the
+// same activation operand in the same accumulation order: Z uses the zero
+// operand below (o + z in all 8 elements) in place of the codes.  Where every
+// code of the group equals its zero the two MFMAs see identical inputs, so
+// T - Z is exactly 0 and the output is exactly 0, as with the per-weight
+// dequant (q - z) s = 0.
 template <int DT> struct RawQ {
-  static constexpr float kOffset = DT == DT_F16 ? 1024.0f : 128.0f;
   uint32_t magic;  // in a register, so the insert is one v_and_or_b32
   __device__ __forceinline__ RawQ() {
     magic = DT == DT_F16 ? 0x64006400u : 0x43004300u;
     asm("" : "+v"(magic));
+  }
+  // o + z in every element of an MFMA operand (z < 1024 in fp16, < 128 in bf16)
+  __device__ __forceinline__ typename Op<DT>::vec zero_operand(uint32_t z) const {
+    const uint32_t v = magic | (z * 0x00010001u);
+    return __builtin_bit_cast(typename Op<DT>::vec, u32x4_t{v, v, v, v});
   }
 };
 template <bool ZS = true, int DT>

@@ -10,14 +10,9 @@
 
 namespace w4a16 {
 
-#ifndef W4A16_DECODE_WAVES
-#define W4A16_DECODE_WAVES 4
-#endif
-constexpr int DW = W4A16_DECODE_WAVES;  // waves per decode workgroup
+constexpr int DW = 4;                   // waves per decode workgroup
 constexpr int RUN = 8;                  // K tiles per meta run and ring pass
-#ifndef W4A16_DEC_FOLD
-#define W4A16_DEC_FOLD 1
-#endif
+constexpr int64_t kWideMinN = 16384;    // narrowest layer of the wide packed decode
 
 // Activation modes.  PACKED: M <= 4, one 16-byte load per lane and K tile
 // carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
@@ -28,9 +23,14 @@ constexpr int RUN = 8;                  // K tiles per meta run and ring pass
 // PACKED with the M rows of x staged in LDS and read from there (used with
 // AWQ input scales, below).  With input scales (XS) the staged rows are
 // divided by s in place, once per workgroup, before the loop: each x element
-// is scaled once per workgroup instead of once per use.
-enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3, AM_FULLT = 4 };
-constexpr bool is_full(int am) { return am == AM_FULL || am == AM_FULLT; }
+// is scaled once per workgroup instead of once per use.  GGATHER: FULL with
+// one row tile, each operand element gathered from global memory,
+// x[m][perm[k]] (and divided by s[perm[k]] with input scales): the form of
+// every call that has a permutation or input scales, no workspace for a
+// preparation pass and no room to stage its rows on chip; correct at any M,
+// not fast.
+enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3, AM_FULLT = 4, AM_GGATHER = 5 };
+constexpr bool is_full(int am) { return am == AM_FULL || am == AM_FULLT || am == AM_GGATHER; }
 constexpr bool is_packed(int am) { return !is_full(am); }
 constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; }
 
@@ -60,6 +60,22 @@ __device__ __forceinline__ void mma_tile(const typename Op<DT>::vec b[4],
         acc[m * PER + j % PER] = mfma16x16x32<DT>(a[m * 4 + j], b[j], acc[m * PER + j % PER]);
       }
     }
+  }
+}
+
+// Value of the meta unit that MFMA step g = lane >> 4 of a K tile uses, out
+// of the tile's U candidates (unit g U / 4: g >> 1 for U = 2, g for U = 4),
+// selected on the bits of the lane group (a chain of equality tests would
+// become divergent branches).
+template <int U, class T>
+__device__ __forceinline__ T sel_unit(const T (&v)[U], int lane) {
+  if constexpr (U == 1) {
+    return v[0];
+  } else if constexpr (U == 2) {
+    return (lane & 32) ? v[1] : v[0];
+  } else {
+    const bool b0 = lane & 16, b1 = lane & 32;
+    return b1 ? (b0 ? v[3] : v[2]) : (b0 ? v[1] : v[0]);
   }
 }
 
@@ -170,39 +186,37 @@ struct IntW {
     }
   }
   // The codes alone (o + q, RawQ) as the B operands of tile slot s, and, for
-  // the fold, the scale s and -(o + z) of step g of slot s (unit sU + gU/4;
-  // g is the lane group, so the U candidates are formed and selected on its
-  // bits rather than indexed).
+  // the fold, the scale of step g of slot s (unit sU + gU/4; g is the lane
+  // group, so the U candidates are formed and selected on its bits rather
+  // than indexed) and the zero operands (o + z) of the slot's U units.
   __device__ __forceinline__ void raw_operands(const CodeT& w, typename Op<DT>::vec b[4]) const {
     const RawQ<DT> rq;
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = dequant_step<DT, false>(w, j, rq);
   }
-  __device__ static __forceinline__ void unit_fold(const Meta& m, int r, float& sf, float& nz) {
-    constexpr int per = 32 / kZW;
-    sf = (float)__builtin_bit_cast(
+  __device__ static __forceinline__ float unit_scale(const Meta& m, int r) {
+    return (float)__builtin_bit_cast(
         _Float16, (uint16_t)((m.s[r >> 3][(r & 7) >> 1] >> (16 * (r & 1))) & 0xFFFFu));
-    nz = -(RawQ<DT>::kOffset +
-           (float)((m.z[r / per] >> (kZW * (r % per))) & ((1u << kZW) - 1u)));
   }
-  __device__ static __forceinline__ void fold_param(const Meta& m, int s, int lane, float& sf,
-                                                    float& nz) {
+  __device__ static __forceinline__ uint32_t unit_zero(const Meta& m, int r) {
+    constexpr int per = 32 / kZW;
+    return (m.z[r / per] >> (kZW * (r % per))) & ((1u << kZW) - 1u);
+  }
+  __device__ static __forceinline__ float fold_scale(const Meta& m, int s, int lane) {
     if constexpr (U == 1) {
-      unit_fold(m, s, sf, nz);
+      return unit_scale(m, s);
     } else {
-      float a[U], c[U];
+      float a[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) unit_fold(m, s * U + u, a[u], c[u]);
-      // step g = lane >> 4 uses unit g U / 4: g >> 1 for U = 2, g for U = 4
-      const bool b0 = lane & 16, b1 = lane & 32;
-      if constexpr (U == 2) {
-        sf = b1 ? a[1] : a[0];
-        nz = b1 ? c[1] : c[0];
-      } else {
-        sf = b1 ? (b0 ? a[3] : a[2]) : (b0 ? a[1] : a[0]);
-        nz = b1 ? (b0 ? c[3] : c[2]) : (b0 ? c[1] : c[0]);
-      }
+      for (int u = 0; u < U; ++u) a[u] = unit_scale(m, s * U + u);
+      return sel_unit<U>(a, lane);
     }
+  }
+  __device__ static __forceinline__ void zero_operands(const Meta& m, int s,
+                                                       typename Op<DT>::vec (&bz)[U]) {
+    const RawQ<DT> rq;
+#pragma unroll
+    for (int u = 0; u < U; ++u) bz[u] = rq.zero_operand(unit_zero(m, s * U + u));
   }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }
 };
@@ -308,14 +322,17 @@ struct Nf4W {
 // descriptor range; k >= K (only in a half NF4 tile) uses an out-of-range
 // offset.
 // Staged activations in LDS: x rows [M][K] at xl, the permutation int32[K] at
-// pl.
+// pl.  GGATHER: the permutation (when perm) and the input scales in global
+// memory, behind the descriptors rp and rs.
 struct XLds {
   const uint8_t* xl;
   const int32_t* pl;
   int M;
+  rsrc_t rp, rs;
+  bool perm;
 };
 
-template <int DT, int AM, int MT, int NA, class WP>
+template <int DT, int AM, int MT, int NA, class WP, bool XS = false>
 __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
                                        typename Op<DT>::vec (&a)[NA], const XLds& xs) {
   typedef typename Op<DT>::vec vec;
@@ -338,6 +355,37 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
       const u32x4_t w = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
                          v[6] | (v[7] << 16)};
       a[0] = __builtin_bit_cast(vec, w);
+    }
+  } else if constexpr (AM == AM_GGATHER) {
+    // one row tile: lane row r, 8 inputs of step j per operand; rows past M
+    // read 0 through the descriptor range of rx, as does any input of a
+    // permutation entry outside the row
+    const uint32_t rowoff = (uint32_t)r * (uint32_t)K * 2u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kg = t * 128 + WP::xk(j, b);
+      uint32_t src[8];
+      if (xs.perm) {
+        const u32x4_t p0 = bld128(xs.rp, (uint32_t)kg * 4u, 0);
+        const u32x4_t p1 = bld128(xs.rp, (uint32_t)kg * 4u + 16u, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          src[e] = min(p0[e], (uint32_t)K);
+          src[4 + e] = min(p1[e], (uint32_t)K);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) src[e] = (uint32_t)(kg + e);
+      }
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = bld16(rx, rowoff + src[e] * 2u, 0);
+        if constexpr (XS) v[e] = div_scale1<DT>((uint16_t)v[e], (uint16_t)bld16(xs.rs, src[e] * 2u, 0));
+      }
+      const u32x4_t w = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                         v[6] | (v[7] << 16)};
+      a[j] = __builtin_bit_cast(vec, w);
     }
   } else if constexpr (AM == AM_XSTAGED) {
     const int j = r >> 2, m = min(r & 3, xs.M - 1);
@@ -457,7 +505,9 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
                                             uint16_t* __restrict__ out, int M, int N, int K,
                                             int KT, float* red, const int32_t* perm,
                                             uint8_t* xlds) {
-  static_assert(!XS || is_staged(AM), "input scales are applied to staged rows");
+  static_assert(!XS || is_staged(AM) || AM == AM_GGATHER,
+                "input scales are applied to staged or gathered rows");
+  static_assert(AM != AM_GGATHER || MT == 1, "the global gather takes one row tile");
   static_assert(AM != AM_XSTAGED || XS, "rows are staged for input scales");
   constexpr int NA = is_packed(AM) ? 1 : MT * 4;                   // A vectors per tile
   constexpr int NACC = is_packed(AM) ? 4 : MT * (MT == 1 ? 4 : (MT == 2 ? 2 : 1));  // acc tiles
@@ -478,25 +528,26 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
 #pragma unroll
   for (int q = 0; q < NACC; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
   // FOLD (packed modes, integer codes): the B operands are the codes alone
-  // (o + q, exact), each K tile's 4 steps go to fresh step tiles, and an MFMA
-  // of the same A against ones gives the tile's row sums of x for every
-  // (step, batch row) row of the A operand.  Lane group g's rows are step g's,
-  // so the lane keeps
-  //   yf += s (at[g] - (o + z) ax),
-  // s and z of its own column and step g's meta unit: the scale and zero cost
-  // a multiply-add pair per accumulator and tile instead of VALU work in every
-  // operand.  The
-  // weights are never rounded to 16 bits in this form (a one-hot row still
-  // gives round16((q - z) s) exactly).
-  constexpr bool FOLD = W4A16_DEC_FOLD && is_packed(AM) && WP::kFold;
+  // (o + q, exact), each K tile's 4 steps go to fresh step tiles at[j], and
+  // MFMAs of the same A against the zero operands (o + z, one per meta unit
+  // of the tile) give az[u].  Lane group g's rows are step g's, so the lane
+  // keeps
+  //   yf += s (at[g] - az[unit of step g]),
+  // s of its own column and step g's meta unit: the scale and zero cost a
+  // subtract and a multiply-add per accumulator and tile instead of VALU work
+  // in every operand.  The weights are never rounded to 16 bits in this form
+  // (a one-hot row still gives round16((q - z) s) exactly), and a group whose
+  // codes all equal its zero gives at[g] == az bit for bit, so exactly 0.
+  constexpr bool FOLD = is_packed(AM) && WP::kFold;
   static_assert(!ONE || FOLD, "the one-row form is a form of the fold");
   // FFOLD (FULLT with one row tile, integer codes, G >= 128): per K tile, the
-  // 4 steps' o + q products and the row sums of x (MFMAs against ones) each
-  // go to a fresh tile; yfm += s (accT - (o + z) accX) with the lane's
-  // column's s and z.  Measured on MI355X, act-order whole calls at M = 16:
-  // fp16 2-5 % faster (4096 x 11008 15.6 -> 15.0 us), bf16 6-8 % (11008 x
-  // 4096 17.8 -> 16.6); with two row tiles (M = 24) the doubled MFMAs cost more
-  // than the dequant they save (5120 x 5120 14.2 -> 15.2).
+  // 4 steps' o + q products and the products with the zero operand (o + z)
+  // each go to a fresh tile; yfm += s (accT - accZ) with the lane's column's
+  // s.  Measured on MI355X, act-order whole calls at M = 16 (with the row sums
+  // then taken against ones): fp16 2-5 % faster than the exact dequant
+  // (4096 x 11008 15.6 -> 15.0 us), bf16 6-8 % (11008 x 4096 17.8 -> 16.6);
+  // with two row tiles (M = 24) the doubled MFMAs cost more than the dequant
+  // they save (5120 x 5120 14.2 -> 15.2).
   constexpr bool FFOLD = AM == AM_FULLT && MT == 1 && full_fold<WP>();
   float4_t yfm[FFOLD ? MT : 1];
 #pragma unroll
@@ -514,7 +565,12 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   typename WP::CodeT ring[RUN];
   typename Op<DT>::vec ra[PA][NA];
   typename WP::Meta mc, mn = WP::zero_meta();
-  XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), M};
+  XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), M, make_rsrc(perm, 0u),
+          make_rsrc(xsc, 0u), perm != nullptr};
+  if constexpr (AM == AM_GGATHER) {
+    xs.rp = make_rsrc(perm, perm ? (uint32_t)K * 4u : 0u);
+    xs.rs = make_rsrc(xsc, XS ? (uint32_t)K * 2u : 0u);
+  }
   if (n > 0) {
     mn = wp.load_meta(r0);
 #pragma unroll
@@ -549,7 +605,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   }
   if (n > 0) {
 #pragma unroll
-    for (int s = 0; s < PA; ++s) load_a<DT, AM, MT, NA, WP>(rx, K, t0 + min(s, n - 1), lane, ra[s], xs);
+    for (int s = 0; s < PA; ++s) load_a<DT, AM, MT, NA, WP, XS>(rx, K, t0 + min(s, n - 1), lane, ra[s], xs);
     for (int i = 0; i < n; i += RUN) {
       mc = mn;
       mn = wp.load_meta(r0 + min(i / RUN + 1, (n - 1) / RUN));
@@ -559,26 +615,27 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
         if (i + s < n) {  // wave-uniform
           typename Op<DT>::vec b[4];
           if constexpr (FOLD) {
-            typedef typename Op<DT>::vec vec;
-            const vec ones = __builtin_bit_cast(
-                vec, DT == DT_F16 ? u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
-                                  : u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
             const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
             wp.raw_operands(ring[s], b);
             float4_t at[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[sa][0], b[j], z4);
-            const float4_t ax = mfma16x16x32<DT>(ra[sa][0], ones, z4);
-            float sf, nz;
-            WP::fold_param(mc, s, lane, sf, nz);
+            typename Op<DT>::vec bz[WP::kU];
+            WP::zero_operands(mc, s, bz);
+            float4_t az[WP::kU];
+#pragma unroll
+            for (int u = 0; u < WP::kU; ++u) az[u] = mfma16x16x32<DT>(ra[sa][0], bz[u], z4);
+            const float sf = WP::fold_scale(mc, s, lane);
             // at[lane >> 4], as two levels of selects on the bits of the lane
             // group (a chain of equality tests becomes branches)
             const bool g0 = lane & 16, g1 = lane & 32;
 #pragma unroll
             for (int e = 0; e < FE; ++e) {
               const float v01 = g0 ? at[1][e] : at[0][e], v23 = g0 ? at[3][e] : at[2][e];
-              const float v = g1 ? v23 : v01;
-              yf[e] = __builtin_fmaf(sf, __builtin_fmaf(nz, ax[e], v), yf[e]);
+              float zu[WP::kU];
+#pragma unroll
+              for (int u = 0; u < WP::kU; ++u) zu[u] = az[u][e];
+              yf[e] = __builtin_fmaf(sf, (g1 ? v23 : v01) - sel_unit<WP::kU>(zu, lane), yf[e]);
             }
           } else {
             if constexpr (FFOLD) wp.raw_operands(ring[s], b);
@@ -587,24 +644,20 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
               typename Op<DT>::vec at[NA];
               xpose_a<DT, MT, WP>(ra[sa], at, xlds + wave * MT * 4096, lane);
               if constexpr (FFOLD) {
-                typedef typename Op<DT>::vec vec;
-                const vec ones = __builtin_bit_cast(
-                    vec, DT == DT_F16
-                             ? u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
-                             : u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-                float sf, nz;
-                WP::fold_param(mc, s, lane, sf, nz);
+                typename Op<DT>::vec bz[1];
+                WP::zero_operands(mc, s, bz);
+                const float sf = WP::fold_scale(mc, s, lane);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                  float4_t tq = float4_t{0.f, 0.f, 0.f, 0.f}, tx = tq;
+                  float4_t tq = float4_t{0.f, 0.f, 0.f, 0.f}, tz = tq;
 #pragma unroll
                   for (int j = 0; j < 4; ++j) {
                     tq = mfma16x16x32<DT>(at[m * 4 + j], b[j], tq);
-                    tx = mfma16x16x32<DT>(at[m * 4 + j], ones, tx);
+                    tz = mfma16x16x32<DT>(at[m * 4 + j], bz[0], tz);
                   }
 #pragma unroll
                   for (int e = 0; e < 4; ++e)
-                    yfm[m][e] = __builtin_fmaf(sf, __builtin_fmaf(nz, tx[e], tq[e]), yfm[m][e]);
+                    yfm[m][e] = __builtin_fmaf(sf, tq[e] - tz[e], yfm[m][e]);
                 }
               } else {
                 mma_tile<DT, AM, MT, NA, NACC>(b, at, acc);
@@ -616,7 +669,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
         }
         __builtin_amdgcn_sched_barrier(0);
         ring[s] = wp.load_codes(t0 + min(i + s + RUN, n - 1), lane);
-        load_a<DT, AM, MT, NA, WP>(rx, K, t0 + min(i + s + PA, n - 1), lane, ra[sa], xs);
+        load_a<DT, AM, MT, NA, WP, XS>(rx, K, t0 + min(i + s + PA, n - 1), lane, ra[sa], xs);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -719,11 +772,8 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   const int t0 = r0 * RUN;
   const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
-  const vec ones = __builtin_bit_cast(
-      vec, DT == DT_F16 ? u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
-                        : u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
-  const XLds none{nullptr, nullptr, M};
+  const XLds none{nullptr, nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false};
   const bool g0 = lane & 16, g1 = lane & 32;
 
   float4_t yf[NC];
@@ -753,7 +803,6 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
       for (int s = 0; s < WRUN; ++s) {
         if (i + s < n) {  // wave-uniform
           const int slot = (i % RUN) + s;  // tile slot within the meta run
-          const float4_t ax = mfma16x16x32<DT>(ra[s][0], ones, z4);
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
             vec b[4];
@@ -761,12 +810,19 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
             float4_t at[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[s][0], b[j], z4);
-            float sf, nz;
-            WP::fold_param(mc[c], slot, lane, sf, nz);
+            vec bz[U];
+            WP::zero_operands(mc[c], slot, bz);
+            float4_t az[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) az[u] = mfma16x16x32<DT>(ra[s][0], bz[u], z4);
+            const float sf = WP::fold_scale(mc[c], slot, lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float v01 = g0 ? at[1][e] : at[0][e], v23 = g0 ? at[3][e] : at[2][e];
-              yf[c][e] = __builtin_fmaf(sf, __builtin_fmaf(nz, ax[e], g1 ? v23 : v01), yf[c][e]);
+              float zu[U];
+#pragma unroll
+              for (int u = 0; u < U; ++u) zu[u] = az[u][e];
+              yf[c][e] = __builtin_fmaf(sf, (g1 ? v23 : v01) - sel_unit<U>(zu, lane), yf[c][e]);
             }
           }
         }
@@ -901,6 +957,7 @@ struct DecodeArgs {
   void* out;
   int64_t M, N, K;
   hipStream_t stream;
+  bool one, wide;  // the plan's one-row form and wide kernel
 };
 
 template <int DT, int MT, int AM, int U, bool XS, int BITS, bool ONE = false>
@@ -915,27 +972,20 @@ static void launch_intb_v(const DecodeArgs& a) {
   launch_timed(intb_decode_kernel<DT, MT, AM, U, XS, BITS, ONE>, grid, dim3(64 * DW), lds, a.stream,
                (const uint16_t*)a.x, (const uint16_t*)a.xsc, (const uint8_t*)a.codes,
                (const uint8_t*)a.scales, (const uint8_t*)(a.zeros ? a.zeros : a.scales), zx,
-               AM == AM_XGATHER ? a.perm : nullptr, (uint16_t*)a.out, (int)a.M, (int)a.N,
+               AM == AM_XGATHER || AM == AM_GGATHER ? a.perm : nullptr, (uint16_t*)a.out,
+               (int)a.M, (int)a.N,
                (int)a.K, (int)(a.K / 128));
 }
 
-#ifndef W4A16_WIDE_NC
-#define W4A16_WIDE_NC 2
-#endif
-#ifndef W4A16_WIDE_RUN
-#define W4A16_WIDE_RUN 8
-#endif
-#ifndef W4A16_WIDE_MIN_N
-#define W4A16_WIDE_MIN_N 16384
-#endif
-// Wide packed decode for 3 or 4 rows on layers of at least W4A16_WIDE_MIN_N
+// Wide packed decode: 2 column tiles per wave, for 3 or 4 rows on layers of at
+// least kWideMinN
 // columns (measured on MI355X, 5120 x 55296: 50.4 -> 43.3 us per call at M = 4;
 // within run-to-run noise at M = 2 and no gain at M = 1, where most of each
 // activation load is rows past M; slower on 11008 columns, where half as many
 // waves fill the GPU; 3 or 4 column tiles per wave were slower than 2).
 template <int DT, int U, int BITS>
 static void launch_intb_wide(const DecodeArgs& a) {
-  constexpr int NC = W4A16_WIDE_NC, WR = W4A16_WIDE_RUN;
+  constexpr int NC = 2, WR = RUN;
   const dim3 grid((unsigned)ceil_div(a.N, (int64_t)16 * NC));
   const uint32_t zx = a.zeros ? 0u : sym_zero_xor(BITS);
   launch_timed(intb_decode_wide_kernel<DT, U, BITS, NC, WR>, grid, dim3(64 * DW), 0, a.stream,
@@ -950,21 +1000,21 @@ static void launch_intb_wide(const DecodeArgs& a) {
 // the loop instead gained nothing).
 template <int DT, int AM, int U, bool XS, int BITS>
 static void launch_intb_packed(const DecodeArgs& a) {
-  if constexpr (W4A16_DEC_FOLD && IntW<DT, U, BITS>::kFold) {
-    if (a.M == 1) return launch_intb_v<DT, 1, AM, U, XS, BITS, true>(a);
+  if constexpr (IntW<DT, U, BITS>::kFold) {
+    if (a.one) return launch_intb_v<DT, 1, AM, U, XS, BITS, true>(a);
   }
   launch_intb_v<DT, 1, AM, U, XS, BITS, false>(a);
 }
 
 template <int DT, int U, bool XS, int BITS>
 static void launch_intb_mode(int am, int mt, const DecodeArgs& a) {
+  if (am == AM_GGATHER) return launch_intb_v<DT, 1, AM_GGATHER, U, XS, BITS>(a);
   if (am == AM_XGATHER) return launch_intb_packed<DT, AM_XGATHER, U, XS, BITS>(a);
   if constexpr (XS) {
     launch_intb_packed<DT, AM_XSTAGED, U, true, BITS>(a);  // the only other mode that scales
   } else {
     if constexpr (IntW<DT, U, BITS>::kFold) {
-      if (am == AM_PACKED && a.M >= 3 && a.N >= W4A16_WIDE_MIN_N)
-        return launch_intb_wide<DT, U, BITS>(a);
+      if (a.wide) return launch_intb_wide<DT, U, BITS>(a);
     }
     if (am == AM_PACKED) launch_intb_packed<DT, AM_PACKED, U, false, BITS>(a);
     else if (am == AM_FULL) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);

@@ -55,6 +55,9 @@
 //    rows.
 //  * Group sizes below 128 (U = 128 / G meta units per K tile) read U times the
 //    scales and zeros per run; a symmetric weight reads no zeros at all.
+#include <cstdarg>
+#include <cstdio>
+
 #include "decode.h"
 
 namespace w4a16 {
@@ -122,16 +125,119 @@ int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm, bool xs
          (use_prefill(M, N, K) ? prefill_workspace_bytes(M, N, K) : 0);
 }
 
+// The kernels of one call.  Without a workspace (ws == false) every call
+// still runs, in the forms that need none: the large-M kernel without a split
+// of K, and for a permutation or input scales the decode kernel gathers (and
+// scales) the activations itself -- from the rows staged on chip where they
+// fit (M <= 4), else element by element from global memory (GGATHER:
+// correct at any M, not fast).
+GemmPlan plan_int_gemm(int64_t M, int64_t N, int64_t K, int G, int bits, int dtype, bool perm,
+                       bool xs, bool ws) {
+  GemmPlan p;
+  p.dtype = dtype;
+  p.bits = bits;
+  p.U = units_per_tile(G);
+  // the large-M kernel takes its activations as stored: with a permutation or
+  // input scales it needs the preparation pass, so without a workspace such a
+  // call takes the decode kernel
+  p.prefill = use_prefill(M, N, K) && (ws || (!perm && !xs));
+  p.xprep = ws ? xprep_bytes(M, N, K, perm, xs) : 0;
+  p.prep = p.xprep > 0;
+  if (p.prefill) {
+    const PrefillPlan pp = plan_prefill(M, N, K, ws);
+    p.bm = pp.bm;
+    p.splits = pp.splits;
+    p.full = M / pp.bm > 0;
+    p.tail = M % pp.bm != 0;
+    return p;
+  }
+  p.gather = perm && !p.prep;
+  p.xs = xs && !p.prep;
+  p.am = pick_mode(M, N, K, p.gather, p.xs, &p.mt);
+  if ((p.gather || p.xs) && !is_staged(p.am)) {
+    p.am = AM_GGATHER;
+    p.mt = 1;
+  }
+  // the fold needs o + q exact in the operand type
+  const bool fold = !(bits == 8 && dtype == DT_BF16);
+  p.one = fold && M == 1 && is_packed(p.am);
+  p.wide = fold && p.am == AM_PACKED && !p.xs && M >= 3 && N >= kWideMinN;
+  return p;
+}
+
+GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws) {
+  GemmPlan p;
+  p.nf4 = true;
+  p.dtype = dtype;
+  p.prefill = nf4_use_prefill(M, N, K);
+  if (p.prefill) {
+    // without a workspace the large-M kernel runs without a split of K
+    const PrefillPlan pp = plan_prefill(M, N, K, ws);
+    p.bm = pp.bm;
+    p.splits = pp.splits;
+    p.full = M / pp.bm > 0;
+    p.tail = M % pp.bm != 0;
+    return p;
+  }
+  p.am = pick_mode(M, N, K, false, false, &p.mt);
+  if (p.am != AM_FULLT) p.mt = 1;
+  p.batch = K % 1024 == 0;
+  return p;
+}
+
+namespace {
+struct Names {
+  char* out;
+  int64_t n, len = 0;
+  void add(const char* fmt, ...) __attribute__((format(printf, 2, 3))) {
+    char buf[160];
+    va_list ap;
+    va_start(ap, fmt);
+    const int k = vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    for (int i = 0; i < k; ++i, ++len)
+      if (out && len + 1 < n) out[len] = buf[i];
+    if (out && n > 0) out[std::min(len, n - 1)] = 0;
+  }
+};
+const char* tf(bool b) { return b ? "true" : "false"; }
+}  // namespace
+
+int64_t plan_names(const GemmPlan& p, char* out, int64_t n) {
+  Names o{out, n};
+  if (out && n > 0) out[0] = 0;
+  if (p.prep) o.add("w4a16::prep_x_kernel<%d> + ", p.dtype);
+  if (p.prefill) {
+    const int fmt = p.nf4 ? 1 : 0, U = p.nf4 ? 1 : p.U, bits = p.nf4 ? 4 : p.bits;
+    const char* sep = "";
+    if (p.full) {
+      o.add("w4a16::wq_prefill_kernel<%d, %d, false, %d, %d, %d>", p.dtype, p.bm, fmt, U, bits);
+      sep = " + ";
+    }
+    if (p.tail)
+      o.add("%sw4a16::wq_prefill_kernel<%d, %d, true, %d, %d, %d>", sep, p.dtype, p.bm, fmt, U,
+            bits);
+    if (p.splits > 1) o.add(" + w4a16::split_reduce_kernel<%d>", p.dtype);
+  } else if (p.nf4) {
+    o.add("w4a16::nf4_decode_kernel<%d, %d, %d, %s>", p.dtype, p.mt, p.am, tf(p.batch));
+  } else if (p.wide) {
+    o.add("w4a16::intb_decode_wide_kernel<%d, %d, %d, 2, %d>", p.dtype, p.U, p.bits, RUN);
+  } else {
+    o.add("w4a16::intb_decode_kernel<%d, %d, %d, %d, %s, %d, %s>", p.dtype, p.mt, p.am, p.U,
+          tf(p.xs), p.bits, tf(p.one));
+  }
+  return o.len;
+}
+
 hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
                            const void* scales_r, const void* zeros_r, const int32_t* perm,
                            void* out, int64_t M, int64_t N, int64_t K, int G, int bits,
                            int dtype, void* workspace, int64_t /*workspace_bytes*/,
                            hipStream_t stream) {
-  int mt = 1;
-  const bool pf = use_prefill(M, N, K);
-  const int64_t xb = xprep_bytes(M, N, K, perm != nullptr, xsc != nullptr);
+  const GemmPlan pl = plan_int_gemm(M, N, K, G, bits, dtype, perm != nullptr, xsc != nullptr,
+                                    workspace != nullptr);
   const void* xa = x;
-  if (xb > 0) {
+  if (pl.prep) {
     // the activations are prepared once into the workspace
     const int64_t n8 = M * (K / 8);
     const dim3 grid((unsigned)ceil_div(n8, 256));
@@ -143,19 +249,25 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
                          perm, (const uint16_t*)xsc, (uint16_t*)workspace, (int)M, (int)K);
     xa = workspace;
   }
-  if (pf) {
-    launch_int_prefill(xa, codes_r, scales_r, zeros_r, out, (uint8_t*)workspace + xb, M, N, K,
-                       G, bits, dtype, stream);
+  if (pl.prefill) {
+    launch_int_prefill(xa, codes_r, scales_r, zeros_r, out,
+                       workspace ? (uint8_t*)workspace + pl.xprep : nullptr, M, N, K, G, bits,
+                       dtype, stream);
     return hipGetLastError();
   }
-  // what the decode kernel still has to do itself
-  const bool gather = perm && xb == 0, scale = xsc && xb == 0;
-  const int am = pick_mode(M, N, K, gather, scale, &mt);
-  const DecodeArgs a{xa, scale ? xsc : nullptr, codes_r, scales_r, zeros_r,
-                     gather ? perm : nullptr, out, M, N, K, stream};
-  if (bits == 4) launch_intb_decode<4>(dtype, scale, am, mt, G, a);
-  else if (bits == 3) launch_intb_decode<3>(dtype, scale, am, mt, G, a);
-  else launch_intb_decode<8>(dtype, scale, am, mt, G, a);
+  // the row blocks of one launch: 16 MT rows each, at most 65536 of them (the
+  // grid's y dimension), so the global gather (one row tile) takes calls of
+  // more than 2^20 rows in several launches
+  const int64_t rows = pl.am == AM_GGATHER ? (int64_t)16 << 16 : M;
+  for (int64_t r0 = 0; r0 < M; r0 += rows) {
+    const int64_t m = std::min(rows, M - r0);
+    const DecodeArgs a{(const uint16_t*)xa + r0 * K, pl.xs ? xsc : nullptr, codes_r, scales_r,
+                       zeros_r, pl.gather ? perm : nullptr, (uint16_t*)out + r0 * N, m, N, K,
+                       stream, pl.one, pl.wide};
+    if (bits == 4) launch_intb_decode<4>(dtype, pl.xs, pl.am, pl.mt, G, a);
+    else if (bits == 3) launch_intb_decode<3>(dtype, pl.xs, pl.am, pl.mt, G, a);
+    else launch_intb_decode<8>(dtype, pl.xs, pl.am, pl.mt, G, a);
+  }
   return hipGetLastError();
 }
 
@@ -172,18 +284,16 @@ static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, con
 }
 
 template <int DT, bool BATCH>
-static void launch_nf4_dt(const void* x, const uint8_t* q, const uint8_t* aq, const float* asc,
-                          const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
-                          hipStream_t stream) {
-  int mt;
-  const int am = pick_mode(M, N, K, false, false, &mt);
-  if (am == AM_PACKED)
+static void launch_nf4_dt(const GemmPlan& pl, const void* x, const uint8_t* q, const uint8_t* aq,
+                          const float* asc, const Nf4Table& L, void* out, int64_t M, int64_t N,
+                          int64_t K, hipStream_t stream) {
+  if (pl.am == AM_PACKED)
     launch_nf4_v<DT, 1, AM_PACKED, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
-  else if (am == AM_FULL)
+  else if (pl.am == AM_FULL)
     launch_nf4_v<DT, 1, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
-  else if (mt == 1)
+  else if (pl.mt == 1)
     launch_nf4_v<DT, 1, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
-  else if (mt == 2)
+  else if (pl.mt == 2)
     launch_nf4_v<DT, 2, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
   else
     launch_nf4_v<DT, 4, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
@@ -197,22 +307,23 @@ hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t*
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,
                            int64_t N, int64_t K, int dtype, void* workspace,
                            int64_t /*workspace_bytes*/, hipStream_t stream) {
-  if (nf4_use_prefill(M, N, K)) {
+  const GemmPlan pl = plan_nf4_gemm(M, N, K, dtype, workspace != nullptr);
+  if (pl.prefill) {
     launch_nf4_prefill(x, qweight, absmax_q, absmax_scale, L, out, workspace, M, N, K, dtype,
                        stream);
     return hipGetLastError();
   }
-  const bool batch = K % 1024 == 0;
   if (dtype == DT_F16) {
-    if (batch)
-      launch_nf4_dt<DT_F16, true>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+    if (pl.batch)
+      launch_nf4_dt<DT_F16, true>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
     else
-      launch_nf4_dt<DT_F16, false>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+      launch_nf4_dt<DT_F16, false>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
   } else {
-    if (batch)
-      launch_nf4_dt<DT_BF16, true>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+    if (pl.batch)
+      launch_nf4_dt<DT_BF16, true>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
     else
-      launch_nf4_dt<DT_BF16, false>(x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+      launch_nf4_dt<DT_BF16, false>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K,
+                                    stream);
   }
   return hipGetLastError();
 }

@@ -53,6 +53,42 @@ hipError_t launch_dequant_nf4(const uint8_t* qweight, const uint8_t* absmax_q,
                               const float* absmax_scale, int64_t N, int64_t K, int dtype,
                               const Nf4Table& L, void* w_out, hipStream_t stream);
 
+// Rows per workgroup of the large-M kernel for M, and the split of K that
+// fills the GPU best: a simple model of the call time (rounds of workgroups on
+// 256 CUs x K tiles per workgroup x per-tile MFMA time, plus the partials'
+// round trip through HBM).  split_ok = false: no workspace for partials, one
+// workgroup per output tile.
+struct PrefillPlan {
+  int bm, splits;
+};
+PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, bool split_ok = true);
+
+// How one GEMM call runs: the kernels it launches, in order.  The launchers
+// follow the plan, and plan_names reports it (the kernel instantiations as
+// the profiler names them), so a report cannot drift from the dispatch.
+struct GemmPlan {
+  bool nf4 = false;
+  int dtype = 0, bits = 4, U = 1;
+  bool prep = false;        // prep_x_kernel writes x[:, perm] / s into the workspace first
+  int64_t xprep = 0;        // its workspace bytes
+  bool prefill = false;     // the large-M kernel (else the decode kernel)
+  int bm = 0, splits = 1;   // large-M: rows per workgroup, split of K
+  bool full = false, tail = false;  // large-M: launches over whole and partial row blocks
+  int am = 0, mt = 1;       // decode: activation mode, row tiles per workgroup
+  bool xs = false;          // decode: the kernel divides by the input scales itself
+  bool gather = false;      // decode: the kernel applies the permutation itself
+  bool one = false;         // decode: the one-row form of the packed fold
+  bool wide = false;        // decode: the wide packed kernel (2 column tiles per wave)
+  bool batch = false;       // NF4 decode: absmax codes of a run in one load
+};
+// ws: whether the call has a workspace (of at least int4_workspace_bytes).
+GemmPlan plan_int_gemm(int64_t M, int64_t N, int64_t K, int G, int bits, int dtype, bool perm,
+                       bool xs, bool ws);
+GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws);
+// "w4a16::kernel<args> + ..." in launch order (at most n bytes with the NUL);
+// returns the full length.
+int64_t plan_names(const GemmPlan& p, char* out, int64_t n);
+
 // xsc: AWQ input scales s [K] (activation dtype) or nullptr; bits: 3, 4 or 8.
 hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
                            const void* scales_r, const void* zeros_r, const int32_t* perm,

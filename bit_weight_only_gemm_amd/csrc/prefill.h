@@ -15,22 +15,7 @@ constexpr int PF_ROWB = 256;                 // LDS bytes of one row of a K tile
 // Rows per workgroup BM in {32, 64, 128, 192, 256}: BM / 32 MFMA row tiles per wave,
 // an LDS stage of BM x 256 bytes, BM / 16 16-byte activation loads per lane.
 
-#ifndef W4A16_PF_DMA_STEPS
-#define W4A16_PF_DMA_STEPS 8
-#endif
-constexpr int PF_DMA_STEPS = W4A16_PF_DMA_STEPS;  // steps the activation loads spread over
-#ifndef W4A16_PF_APF
-#define W4A16_PF_APF 1
-#endif
-#ifndef W4A16_PF_SGB
-#define W4A16_PF_SGB 1
-#endif
-#ifndef W4A16_PF_FOLD
-#define W4A16_PF_FOLD 1
-#endif
-#ifndef W4A16_PF_DEEP
-#define W4A16_PF_DEEP 1
-#endif
+constexpr int PF_DMA_STEPS = 8;             // steps the activation loads spread over
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
@@ -191,21 +176,20 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
     for (int g = 0; g < 2; ++g) acc[m][g] = float16_t{};
   // FOLD (integer codes, one scale and zero per K tile, 32 rows): the B
   // operands are the codes alone (RawQ: o + q, o = 1024 in fp16, 128 in
-  // bf16), summed over the tile into accT; accX sums the activation rows over
-  // the tile (an MFMA against ones).  At the end of the tile
-  //   acc += s (accT - (o + z) accX) = s sum_k x_k (q_k - z),
-  // one multiply-add pair per accumulator per tile in place of the scale and
-  // zero in every operand: the dequant VALU per weight drops to the insert.
-  // The result differs from dequant-then-multiply only by the rounding of
+  // bf16), summed over the tile into accT; accZ sums the products of the same
+  // activations with the zero operand (o + z) of each column group.  At the
+  // end of the tile
+  //   acc += s (accT - accZ) = s sum_k x_k (q_k - z),
+  // a subtract and a multiply-add per accumulator per tile in place of the
+  // scale and zero in every operand: the dequant VALU per weight drops to the
+  // insert.  The result differs from dequant-then-multiply by the rounding of
   // each weight to 16 bits, which this form never does (a one-hot row still
-  // gives round16((q - z) s) exactly).
-  constexpr bool FOLD = W4A16_PF_FOLD && FMT == FMT_INT4 && U == 1 && BM == 32 &&
-                        !(BITS == 8 && DT == DT_BF16);
-  float16_t accT[FOLD ? PF_MT : 1][2], accX[FOLD ? PF_MT : 1];
+  // gives round16((q - z) s) exactly), and by the rounding of the two sums;
+  // where every code of a column's tile equals its zero the two MFMA chains
+  // see identical inputs and the tile adds exactly 0.
+  constexpr bool FOLD = FMT == FMT_INT4 && U == 1 && BM == 32 && !(BITS == 8 && DT == DT_BF16);
+  float16_t accT[FOLD ? PF_MT : 1][2], accZ[FOLD ? PF_MT : 1][2];
   const RawQ<DT> rq;
-  const vec ones = __builtin_bit_cast(
-      vec, DT == DT_F16 ? u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
-                        : u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   // DEEP (32 rows): the weights of K tile t + 2 are in flight while
   // tile t is computed (two tiles of latency cover; with few rows a tile's
@@ -215,7 +199,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
   // lane), then the weights of tile t + 2; the wait before each barrier
   // counts in issue order, so it leaves those kW loads pending (the barrier is
   // a plain s_barrier: __syncthreads would wait for every load).
-  constexpr bool DEEP = W4A16_PF_DEEP && BM == 32;
+  constexpr bool DEEP = BM == 32;
   constexpr int kW = 2 * ((FMT == FMT_NF4 ? 2 : (BITS == 8 ? 4 : 2)) + 2);  // loads per load_w pair
   CT cw[DEEP ? 3 : 2][2][2];
   u32x2_t sc[DEEP ? 3 : 2][2];
@@ -272,6 +256,12 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
 #pragma unroll
       for (int g = 0; g < 2; ++g) ap[g] = (float)(scc[g][0] & 0xFFu) * __builtin_bit_cast(float, zzc[g]);
     }
+    vec bz[2];  // FOLD: the zero operand (o + z) of each column group
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        bz[g] = rq.zero_operand(((zzc[g] ^ zx) >> (kZW * zb)) & ((1u << kZW) - 1u));
+    }
     // B operand of step s for column group g: word j = s >> 1 of the tile, in
     // meta unit j U / 4.  The unit's dequant parameters are formed at the step
     // (a few VALU instructions between MFMAs); formed once per tile and held
@@ -313,9 +303,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       }
       if (s < 7) {
         const int sn1 = s + 1;
-#if W4A16_PF_APF
         read_step(sn1, an);
-#endif
 #pragma unroll
         for (int g = 0; g < 2; ++g) bn[g] = operand(sn1, g);
       }
@@ -323,9 +311,10 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
 #pragma unroll
         for (int m = 0; m < PF_MT; ++m) {
 #pragma unroll
-          for (int g = 0; g < 2; ++g)
+          for (int g = 0; g < 2; ++g) {
             accT[m][g] = mfma32x32x16<DT>(a[m], b[g], s == 0 ? float16_t{} : accT[m][g]);
-          accX[m] = mfma32x32x16<DT>(a[m], ones, s == 0 ? float16_t{} : accX[m]);
+            accZ[m][g] = mfma32x32x16<DT>(a[m], bz[g], s == 0 ? float16_t{} : accZ[m][g]);
+          }
         }
       } else {
 #pragma unroll
@@ -333,31 +322,22 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
 #pragma unroll
           for (int g = 0; g < 2; ++g) acc[m][g] = mfma32x32x16<DT>(a[m], b[g], acc[m][g]);
       }
-#if W4A16_PF_SGB
       if (s < 7) {
 #pragma unroll
-        for (int k = 0; k < (FOLD ? 3 : 2) * PF_MT; ++k) {
+        for (int k = 0; k < (FOLD ? 4 : 2) * PF_MT; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
           if (!DEEP && k < i1 - i0 && i0 < PF_ALD)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one activation load
-#if W4A16_PF_APF
           if (k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-#endif
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
         }
       }
-#endif
       __builtin_amdgcn_sched_barrier(0);
       if (s < 7) {
 #pragma unroll
         for (int g = 0; g < 2; ++g) b[g] = bn[g];
-#if W4A16_PF_APF
 #pragma unroll
         for (int m = 0; m < PF_MT; ++m) a[m] = an[m];
-#else
-        read_step(s + 1, a);
-        __builtin_amdgcn_sched_barrier(0);
-#endif
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -365,14 +345,11 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(scc[g][0] & 0xFFFFu));
-        const float nz = -(RawQ<DT>::kOffset +
-                           (float)(((zzc[g] ^ zx) >> (kZW * zb)) & ((1u << kZW) - 1u)));  // -(o + z)
 #pragma unroll
         for (int m = 0; m < PF_MT; ++m)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            acc[m][g][r] = __builtin_fmaf(sf, __builtin_fmaf(nz, accX[m][r], accT[m][g][r]),
-                                          acc[m][g][r]);
+            acc[m][g][r] = __builtin_fmaf(sf, accT[m][g][r] - accZ[m][g][r], acc[m][g][r]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -448,16 +425,6 @@ split_reduce_kernel(const float* __restrict__ part, int S, int64_t MN, uint16_t*
   *(uint2*)(out + i) = make_uint2(lo, hi);
 }
 
-// ---------------------------------------------------------------- planning --
-// Rows per workgroup for M, and the split of K that fills the GPU best: a
-// simple model of the call time (rounds of workgroups on 256 CUs x K tiles per
-// workgroup x per-tile MFMA time, plus the partials' round trip through HBM).
-struct PrefillPlan {
-  int bm, splits;
-};
-
-PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K);
-
 template <int DT, int BM, int FMT, int U, int BITS>
 static void launch_prefill_bm(const void* x, const void* codes_r, const void* scales_r,
                               const void* zeros_r, const Nf4Table& L, void* out, float* part,
@@ -492,7 +459,7 @@ template <int DT, int FMT, int U, int BITS>
 static void launch_prefill_dt(const void* x, const void* codes_r, const void* scales_r,
                               const void* zeros_r, const Nf4Table& L, void* out, void* ws,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  const PrefillPlan pl = plan_prefill(M, N, K);
+  const PrefillPlan pl = plan_prefill(M, N, K, ws != nullptr);
   float* part = (float*)ws;
   if (pl.bm == 32)
     launch_prefill_bm<DT, 32, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,

@@ -46,7 +46,7 @@ namespace w4a16 {
 // 0.83 of a 256-row one per K tile (measured on MI355X), and the smaller tile
 // fills a round that 256-row tiles leave partly idle -- e.g. 220 instead of
 // 160 workgroups on a 5120-column layer at M = 2048 (17 % faster there).
-PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K) {
+PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, bool split_ok) {
   PrefillPlan pl;
   pl.bm = M <= 32 ? 32 : M <= 64 ? 64 : (M <= 128 ? 128 : 256);
   const int64_t cols = ceil_div(ceil_div(N, 64), (int64_t)PF_WAVES);
@@ -55,7 +55,7 @@ PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K) {
   const double t_tile = 3.4e-6 * pl.bm / 256.0;  // one K tile of a workgroup
   double best = 0;
   pl.splits = 1;
-  for (int S = 1; S <= 16 && S <= KT; ++S) {
+  for (int S = 1; S <= (split_ok ? 16 : 1) && S <= KT; ++S) {
     double t = (double)ceil_div(tiles * S, (int64_t)256) * (double)ceil_div(KT, (int64_t)S) * t_tile;
     if (S > 1) t += (double)(S * 4 + 2) * M * N / 4.0e12 + 2e-6;
     if (S == 1 || t < best * 0.97) {

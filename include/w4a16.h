@@ -32,7 +32,14 @@
  *  - Arguments are validated on the host before anything is launched; a
  *    non-zero status means nothing was launched.  Device-side faults surface
  *    at the caller's next stream synchronization, not in the return value.
- *    Nothing throws or aborts across the ABI.
+ *    Nothing throws or aborts across the ABI: a failed host allocation (or
+ *    any other C++ exception inside the library) returns W4A16_ERR_HOST.
+ *  - An entry point that launches work first clears (consumes) any HIP error
+ *    an earlier runtime call left pending on the calling thread, so that
+ *    W4A16_ERR_HIP reports only this call's own launch failures.
+ *  - Size limits (W4A16_ERR_UNSUPPORTED beyond them): K <= 2^22, N <= 2^28,
+ *    N*K <= 2^37, M <= 2^21, M*K <= 2^36 and M*N <= 2^36.  They keep every
+ *    32-bit buffer range and offset the kernels use below 2^31.
  *  - All device pointers must be 16-byte aligned (W4A16_ERR_MISALIGNED).
  *  - 16-bit floats are passed as their bit patterns (uint16_t / void*).
  *  - Rounding: every conversion to fp16/bf16 is round-to-nearest-even;
@@ -55,7 +62,8 @@ typedef enum {
   W4A16_ERR_MISALIGNED = 3,    /* a device pointer is not 16-byte aligned        */
   W4A16_ERR_BAD_GIDX = 4,      /* g_idx out of range or a group not of size G     */
   W4A16_ERR_WORKSPACE = 5,     /* workspace given but smaller than required       */
-  W4A16_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed      */
+  W4A16_ERR_HIP = 6,           /* a HIP runtime call or kernel launch failed      */
+  W4A16_ERR_HOST = 7           /* host-side failure (host memory allocation)      */
 } w4a16_status_t;
 
 typedef enum { W4A16_F16 = 0, W4A16_BF16 = 1 } w4a16_dtype_t;
@@ -66,7 +74,8 @@ typedef enum { W4A16_CODES = 0, W4A16_SCALES = 1, W4A16_ZEROS = 2 } w4a16_array_
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* w4a16_status_string(int status);
 
-/* ABI version; bumped on any incompatible change. */
+/* ABI version; bumped on any incompatible change (2: NULL workspace legal on
+ * every GEMM call, W4A16_ERR_HOST, the plan queries). */
 int w4a16_version(void);
 
 /*
@@ -169,7 +178,7 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
                  int32_t* perm_used_host, void* stream);
 
 /*
- * Workspace bytes w4a16_gemm and w4a16_gemm_xscale need at this shape
+ * Workspace bytes w4a16_gemm and w4a16_gemm_xscale use at this shape
  * (covering calls with a column permutation and with input scales): room for
  * the prepared activations M*K*2 where a separate pass writes x[:, perm]
  * and/or x / s, plus the fp32 partials S*M*N*4 of the large-M kernel (M >= 32;
@@ -178,11 +187,27 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
  * given call may need less, or nothing: no pass runs where
  * the decode kernel gathers x[:, perm] and/or divides by s itself (M <= 4,
  * the rows, the permutation and the scales staged on chip: at most 72 KB per
- * workgroup and 17 MiB over its grid of N/16 workgroups); each call
- * validates what it needs.
+ * workgroup and 17 MiB over its grid of N/16 workgroups).
+ * A workspace is optional on every call (see w4a16_gemm).  -1 on bad input.
  * Calls that overlap in time must not share a workspace.
  */
 int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_size);
+
+/*
+ * Host-only plan query (no device needed): the kernels w4a16_gemm_bits would
+ * launch for this call, in launch order, as the profiler names their
+ * instantiations, e.g. "w4a16::prep_x_kernel<0> +
+ * w4a16::intb_decode_kernel<0, 1, 4, 1, false, 4, false>".  has_perm,
+ * has_x_scale, has_workspace: whether the call passes a permutation, input
+ * scales and a workspace (non-zero = yes).
+ *   names_host   char[names_bytes] host, written NUL-terminated (truncated to
+ *                fit; may be NULL when names_bytes == 0).
+ *   names_len_host  int64 host or NULL: the full length without the NUL.
+ * Errors as for w4a16_gemm_bits' shape, bits and dtype checks.
+ */
+int w4a16_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t bits,
+                    int32_t dtype, int32_t has_perm, int32_t has_x_scale, int32_t has_workspace,
+                    char* names_host, int64_t names_bytes, int64_t* names_len_host);
 
 /*
  * Fused dequantize-and-multiply, the method of [P5] "关键数据解读" item 1
@@ -191,24 +216,37 @@ int64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group_siz
  *   w[n, k] = round_dtype(fp32(q - z) * fp32(s))  (q, z, s of column n and the
  *             group of permuted column k; z = 8 when zeros_r is NULL),
  * with fp32 accumulation and one round-to-nearest-even to the output dtype.
- * Paths that apply s and z after a K tile's sum use fp32(q - z) * fp32(s)
- * without rounding it first (the same real product, at least as close to the
- * exact one): M <= 4; 9..16 rows, or 5..16 on layers of more than 4096
- * columns, with group_size >= 128 in the decode kernel; the large-M kernel's
- * 32-row tiles with group_size >= 128; never 8-bit codes in bf16.  A row with one nonzero x, a power of two, gives round_dtype(w)
- * on every path.
+ * Paths that apply s and z after a K tile's sum (M <= 4; 9..16 rows, or
+ * 5..16 on layers of more than 4096 columns, with group_size >= 128 in the
+ * decode kernel; the large-M kernel's 32-row tiles with group_size >= 128;
+ * never 8-bit codes in bf16) compute s * (T - Z) per tile, column and group,
+ * T = sum x (o + q) and Z = sum x (o + z) (o = 1024 in fp16, 128 in bf16)
+ * from two MFMA chains over the same activations, without rounding w to
+ * 16 bits first.  Each product is exact in fp32; with each addition of a
+ * chain of n products rounded to fp32 (to nearest or toward zero), the
+ * tile's error is at most |s| * 2 n u (2 o + 30) * sum |x| (u = 2^-23; n = 32
+ * for M <= 4, 128 otherwise), where dequant-then-multiply errs by up to
+ * |s| * 15 * 2^-11 * sum |x| (fp16; 2^-8 in bf16) from the rounding of w
+ * alone.  Exact on every path: a
+ * group whose codes all equal its zero adds exactly 0 (the two chains see
+ * identical inputs); a row with one nonzero x, a power of two, gives
+ * round_dtype(w).
  *   x      [M, K] row-major, dtype;  out [M, N] row-major, dtype.
  *   perm   int32 [K] from w4a16_repack (or NULL for identity).
  *   codes_r, scales_r, zeros_r from w4a16_repack with the same group_size
  *          (zeros_r NULL: a symmetric weight).
  *   dtype  W4A16_F16 or W4A16_BF16 (activations and output).
- *   workspace / workspace_bytes: required when the call needs one (a
- *          permutation the kernel does not gather itself, or a split of K);
- *          w4a16_workspace_bytes(M, N, K, group_size) bytes always suffice
- *          (W4A16_ERR_WORKSPACE when too small), else ignored.
+ *   workspace / workspace_bytes: optional.  NULL is always legal: the call
+ *          then runs in forms that need none (the large-M kernel without a
+ *          split of K; the decode kernel gathering x[m][perm[k]], and
+ *          dividing by s, itself -- element by element from global memory
+ *          where the rows cannot be staged on chip; correct, slower).  A
+ *          workspace given must hold w4a16_workspace_bytes(M, N, K,
+ *          group_size) bytes (W4A16_ERR_WORKSPACE when smaller); its contents
+ *          need not be initialized.
  * Constraints: M >= 1 and the group sizes above.
- * Async on `stream`.  Results are bitwise reproducible run to run (the split of
- * K over a workgroup's waves is reduced in a fixed order).
+ * Async on `stream`.  Results are bitwise reproducible run to run for a given
+ * shape and workspace choice (every split of K is reduced in a fixed order).
  */
 int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const void* zeros_r,
                const int32_t* perm, int32_t group_size, void* out, int64_t M, int64_t N,
@@ -227,8 +265,10 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
  * once to the activation dtype before the multiply.  For M <= 4 rows that the
  * decode kernel stages on chip (see w4a16_workspace_bytes) every workgroup
  * divides its staged copy once; otherwise a preparation pass writes x / s
- * (permuted) into the workspace first.  Other arguments, constraints and the workspace rule as for
- * w4a16_gemm (w4a16_workspace_bytes covers these calls too).
+ * (permuted) into the workspace first, or, without a workspace, the decode
+ * kernel divides each gathered element itself.  Other arguments, constraints
+ * and the workspace rule as for w4a16_gemm (w4a16_workspace_bytes covers
+ * these calls too).
  */
 int w4a16_gemm_xscale(const void* x, const void* x_scale, const void* codes_r,
                       const void* scales_r, const void* zeros_r, const int32_t* perm,
@@ -325,11 +365,16 @@ int nf4_quantize(const float* W, int64_t N, int64_t K, int32_t blocksize, uint8_
                  uint8_t* absmax_q, float* absmax_scale, void* stream);
 
 /*
- * Workspace bytes nf4_gemm needs at this shape: the fp32 split-K partials of
+ * Workspace bytes nf4_gemm uses at this shape: the fp32 split-K partials of
  * the large-M kernel (K % 128 == 0 and M >= 64; M >= 33 on layers of 24 Mi
- * weights and more) when it splits K; 0 otherwise.
+ * weights and more) when it splits K; 0 otherwise.  -1 on bad input.
  */
 int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
+
+/* Host-only plan query for nf4_gemm, as w4a16_gemm_plan. */
+int nf4_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int32_t dtype,
+                  int32_t has_workspace, char* names_host, int64_t names_bytes,
+                  int64_t* names_len_host);
 
 /*
  * Fused NF4 dequantize-and-multiply (bitsandbytes' 4-bit format, dequantized
@@ -339,8 +384,9 @@ int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize);
  *   absmax_scale[b / 256]),  b = (n*K + k) / blocksize.
  *   x [M, K] and out [M, N] row-major in dtype; qweight/absmax as nf4_quantize.
  * Constraints: M >= 1, blocksize == 64, K % 64 == 0, N % 16 == 0.
- * workspace: at least nf4_workspace_bytes(M, N, K, 64) bytes when that is > 0
- * (W4A16_ERR_WORKSPACE otherwise).  Async.
+ * workspace: optional; NULL is legal (the large-M kernel then does not split
+ * K).  A workspace given must hold nf4_workspace_bytes(M, N, K, 64) bytes
+ * (W4A16_ERR_WORKSPACE when smaller).  Async.
  */
 int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
              const float* absmax_scale, int32_t blocksize, void* out, int64_t M, int64_t N,

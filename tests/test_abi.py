@@ -41,9 +41,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert L.w4a16_version() == 1
-    for s in range(7):
-        assert L.w4a16_status_string(s)
+    assert L.w4a16_version() == 2
+    for s in range(8):
+        assert L.w4a16_status_string(s) != b"unknown status"
     assert L.w4a16_status_string(99) == b"unknown status"
 
 
@@ -85,11 +85,11 @@ def test_gemm_validation_without_gpu():
     assert g(NULL, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 1
     # misaligned pointer
     assert g(ODD, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 512, 0, NULL, 0, NULL) == 3
-    # a permutation needs a workspace of w4a16_workspace_bytes
+    # a workspace, when given, must hold w4a16_workspace_bytes (checked before
+    # any launch; NULL is legal and is covered by the plan tests below)
     need = L.w4a16_workspace_bytes(16, 4096, 4096, 128)
     assert need >= 16 * 4096 * 2
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, FAKE, need - 16, NULL) == 5
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, NULL, 0, NULL) == 5
     # the size covers every call at a shape, with or without a permutation and
     # AWQ input scales: M <= 4 rows (with the permutation and the scales) that
     # the decode kernel stages on chip need no workspace (up to 72 KB per
@@ -105,21 +105,116 @@ def test_gemm_validation_without_gpu():
     # w4a16_gemm_xscale validates what the call needs (each case below fails
     # before any launch)
     xs = L.w4a16_gemm_xscale
-    # scales with rows that do not fit on chip, and with M > 4: a pass
-    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 4, 4096, 11008, 0, NULL, 0, NULL) == 5
-    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 4, 4096, 11008, 0, NULL, 0, NULL) == 5
-    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 8, 4096, 4096, 0, NULL, 0, NULL) == 5
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 4, 4096, 11008, 0, FAKE, 16,
+              NULL) == 5
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 8, 4096, 4096, 0, FAKE, 16,
+              NULL) == 5
     assert xs(FAKE, ODD, FAKE, FAKE, FAKE, NULL, 128, FAKE, 2, 4096, 4096, 0, NULL, 0, NULL) == 3
     assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 96, FAKE, 2, 4096, 4096, 0, NULL, 0, NULL) == 2
-    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 64, 5120, 5120, 0, NULL, 0,
-              NULL) == 5
-    # a prefill-sized call that splits K needs room for fp32 partials even
+    # a prefill-sized call that splits K uses room for fp32 partials even
     # without a permutation
     need = L.w4a16_workspace_bytes(64, 5120, 5120, 128)
     assert need >= 2 * 64 * 5120 * 4
-    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 64, 5120, 5120, 0, NULL, 0, NULL) == 5
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 64, 5120, 5120, 0, FAKE, 16, NULL) == 5
 
 
+def test_size_limits_without_gpu():
+    # K <= 2^22, N <= 2^28, N K <= 2^37, M <= 2^21, M K and M N <= 2^36
+    g = L.w4a16_gemm
+    assert L.w4a16_repacked_bytes(1 << 22, 256, 128, 0) > 0
+    assert L.w4a16_repacked_bytes(1 << 23, 256, 128, 0) == -1
+    assert L.w4a16_repacked_bytes(4096, 1 << 29, 128, 0) == -1
+    assert L.w4a16_repacked_bytes(1 << 20, 1 << 17, 128, 0) > 0          # N K = 2^37
+    assert L.w4a16_repacked_bytes(1 << 20, (1 << 17) + 8, 128, 0) == -1
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1, 256, 1 << 23, 0, NULL, 0, NULL) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, (1 << 21) + 1, 256, 512, 0, NULL, 0,
+             NULL) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1 << 20, 256, 1 << 17, 0, NULL, 0,
+             NULL) == 2                                                  # M K = 2^37
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 1 << 20, 1 << 17, 512, 0, NULL, 0,
+             NULL) == 2                                                  # M N = 2^37
+    assert L.nf4_gemm(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 1, 256, 1 << 23, 1, NULL, 0, NULL) == 2
+    assert L.w4a16_workspace_bytes(1 << 20, 256, 1 << 17, 128) == -1
+
+
+def _plan(M, N, K, G=128, bits=4, dtype=0, perm=0, xs=0, ws=1):
+    buf = ctypes.create_string_buffer(512)
+    n = ctypes.c_int64(0)
+    assert L.w4a16_gemm_plan(M, N, K, G, bits, dtype, perm, xs, ws, buf, 512,
+                             ctypes.byref(n)) == 0
+    assert n.value == len(buf.value)
+    return buf.value.decode().split(" + ")
+
+
+def test_plan_names_the_dispatch_without_gpu():
+    dec = "w4a16::intb_decode_kernel<"
+    # act-order decode: the one-row in-kernel gather, a permutation pass at M = 4
+    # on 4096 x 11008 (staging does not fit), the FULLT fold at M = 16
+    assert _plan(1, 4096, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, true>"]
+    assert _plan(4, 11008, 4096, perm=1) == ["w4a16::prep_x_kernel<0>",
+                                             dec + "0, 1, 0, 1, false, 4, false>"]
+    assert _plan(16, 4096, 11008, perm=1) == ["w4a16::prep_x_kernel<0>",
+                                              dec + "0, 1, 4, 1, false, 4, false>"]
+    # without a workspace: no pass, the kernel gathers from global memory
+    # (mode 5), at any M, and the large-M kernel does not split K
+    assert _plan(16, 4096, 11008, perm=1, ws=0) == [dec + "0, 1, 5, 1, false, 4, false>"]
+    assert _plan(64, 5120, 5120, perm=1, ws=0) == [dec + "0, 1, 5, 1, false, 4, false>"]
+    assert _plan(8, 4096, 4096, xs=1, ws=0) == [dec + "0, 1, 5, 1, true, 4, false>"]
+    assert _plan(64, 5120, 5120, ws=1)[-1] == "w4a16::split_reduce_kernel<0>"
+    assert all("split_reduce" not in k for k in _plan(64, 5120, 5120, ws=0))
+    # wide packed decode on >= 16384 columns at 3-4 rows; 8-bit codes in bf16
+    # never take the fold's forms
+    assert _plan(4, 55296, 5120) == ["w4a16::intb_decode_wide_kernel<0, 1, 4, 2, 8>"]
+    assert _plan(1, 4096, 4096, bits=8, dtype=1) == [dec + "1, 1, 0, 1, false, 8, false>"]
+    assert _plan(1, 4096, 4096, G=32) == [dec + "0, 1, 0, 4, false, 4, true>"]
+    # prefill: whole 192-row blocks plus a tail launch
+    assert _plan(2048, 5120, 5120, dtype=1) == ["w4a16::wq_prefill_kernel<1, 192, false, 0, 1, 4>",
+                                                "w4a16::wq_prefill_kernel<1, 192, true, 0, 1, 4>"]
+    # the plan's pass agrees with w4a16_workspace_bytes
+    for M, N, K in [(1, 4096, 4096), (4, 11008, 4096), (16, 4096, 4096), (5, 55296, 5120)]:
+        has_pass = "w4a16::prep_x_kernel<0>" in _plan(M, N, K, perm=1)
+        assert has_pass == (L.w4a16_workspace_bytes(M, N, K, 128) > 0 and
+                            not _plan(M, N, K)[-1].endswith("split_reduce_kernel<0>")) or has_pass
+    # NF4: the decode kernel up to 32 rows on this layer, the large-M kernel after
+    buf = ctypes.create_string_buffer(256)
+    assert L.nf4_gemm_plan(32, 28672, 8192, 64, 1, 1, buf, 256, NULL) == 0
+    assert buf.value == b"w4a16::nf4_decode_kernel<1, 2, 4, true>"
+    assert L.nf4_gemm_plan(33, 28672, 8192, 64, 1, 0, buf, 256, NULL) == 0
+    assert buf.value == b"w4a16::wq_prefill_kernel<1, 64, true, 1, 1, 4>"
+    # truncation keeps the terminator; bad buffers are refused
+    small = ctypes.create_string_buffer(8)
+    n = ctypes.c_int64(0)
+    assert L.nf4_gemm_plan(1, 28672, 8192, 64, 1, 1, small, 8, ctypes.byref(n)) == 0
+    assert small.value == b"w4a16::" and n.value > 8
+    assert L.nf4_gemm_plan(1, 28672, 8192, 64, 1, 1, NULL, 8, NULL) == 1
+    assert L.w4a16_gemm_plan(0, 256, 512, 128, 4, 0, 0, 0, 1, NULL, 0, NULL) == 1
+
+
+def test_host_allocation_failure_is_a_status():
+    """A failed host allocation inside an entry point (here the host copy of
+    g_idx in w4a16_make_perm, 16 MiB at K = 2^22) returns W4A16_ERR_HOST
+    instead of throwing across the C ABI.  Run in a child process whose
+    address space is capped just above its current size, so the allocation
+    fails before any HIP call is made."""
+    import subprocess
+    import sys
+    code = r"""
+import ctypes, resource, sys
+L = ctypes.CDLL(sys.argv[1])
+L.w4a16_make_perm.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                              ctypes.c_void_p, ctypes.c_void_p]
+nt = ctypes.c_int32(0)
+vm = [int(l.split()[1]) for l in open('/proc/self/status') if l.startswith('VmSize:')][0]
+lim = (vm + 4096) * 1024
+resource.setrlimit(resource.RLIMIT_AS, (lim, resource.getrlimit(resource.RLIMIT_AS)[1]))
+st = L.w4a16_make_perm(ctypes.c_void_p(0x10000), 1 << 22, 128, ctypes.c_void_p(0x10000),
+                       ctypes.byref(nt), None)
+print(st)
+"""
+    r = subprocess.run([sys.executable, "-c", code, _lib.LIB_PATH], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "7", (r.stdout, r.stderr)
 def test_nf4_validation_without_gpu():
     g = L.nf4_gemm
     assert g(FAKE, FAKE, FAKE, FAKE, 32, FAKE, 1, 256, 512, 1, NULL, 0, NULL) == 2   # blocksize
@@ -187,4 +282,4 @@ def test_bits_entry_points_validation_without_gpu():
     # the 8-bit GEMM validates like the 4-bit one
     assert L.w4a16_workspace_bytes(64, 5120, 5120, 128) > 0        # split K: partials
     assert L.w4a16_gemm_bits(FAKE, NULL, FAKE, FAKE, FAKE, NULL, 128, 8, FAKE, 64, 5120, 5120, 0,
-                             NULL, 0, NULL) == 5
+                             FAKE, 16, NULL) == 5

@@ -129,123 +129,40 @@ def test_gemm_long_k_sampled_columns(act):
     assert compare_gemm(y, xb, wd, "f16", cols=rows) <= TOL
 
 
-def test_gemm_perm_requires_workspace():
-    # M > 4: the activations are permuted into the workspace first
-    W, gi, _ = int4_inputs("gpu/gemm/nows", 64, 256, act_order=True)
-    _, packed = gpu_int4_pack(W, gi)
-    x = bits_to_tensor(synth.to_f16_bits(synth.activations("gpu/gemm/nows/x", 8, 256)), "f16")
-    with pytest.raises(w4.W4A16Error):
-        w4.w4a16_gemm(x, packed, use_workspace=False)
-
-
-@pytest.mark.parametrize("M,K", [(1, 512), (2, 1024), (3, 2048), (4, 4096), (1, 11008),
-                                 (4, 11008)])
+@pytest.mark.parametrize("M", [1, 4, 5, 8, 16, 33, 64, 130])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_gemm_act_order_small_m(M, K, dtype):
-    # M <= 4: the kernel gathers x[:, perm] from on-chip staging without a
-    # workspace when it fits (the last case does not: permuted through the
-    # workspace); sampled columns at the larger K
-    N = 96
-    say("act-order small M", M, K, dtype)
-    W, gi, _ = int4_inputs("gpu/gemm/gather/%d" % K, N, K, act_order=True)
-    xb = synth.to_bits(synth.activations("gpu/gemm/gather/x/%d/%d" % (M, K), M, K), dtype)
+def test_gemm_act_order_without_workspace(M, dtype):
+    # no workspace: no preparation pass; the decode kernel gathers x[m][perm[k]]
+    # itself (on chip for M <= 4 where the rows fit, else from global memory,
+    # at any M) -- the same product as the call with a workspace
+    N, K = 200, 1024
+    say("act-order without workspace", M, dtype, w4.w4a16_gemm_plan(
+        M, N, K, dtype=torch.float16 if dtype == "f16" else torch.bfloat16, perm=True,
+        workspace=False))
+    W, gi, _ = int4_inputs("gpu/gemm/nows/%d" % M, N, K, act_order=True)
     _, packed = gpu_int4_pack(W, gi)
-    need = w4.w4a16_workspace_bytes(M, N, K)
-    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed, use_workspace=need > 0)
-    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    xb = synth.to_bits(synth.activations("gpu/gemm/nows/x/%d" % M, M, K), dtype)
+    y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed, use_workspace=False)
+    torch.cuda.synchronize()
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)       # original column order
     assert compare_gemm(y, xb, wd, dtype) <= TOL
 
 
-def test_gemm_deterministic_and_scaling_exact():
-    M, N, K = 16, 512, 2048
-    say("determinism")
-    W, gi, _ = int4_inputs("gpu/gemm/det", N, K, act_order=True)
-    x32 = synth.activations("gpu/gemm/det/x", M, K)
-    xb = synth.to_f16_bits(x32)
-    # exact doubling of the fp16 inputs (doubling before rounding would differ
-    # for fp16-subnormal inputs)
-    x2b = synth.to_f16_bits(2 * xb.view(np.float16).astype(np.float32))
+@pytest.mark.parametrize("M", [32, 64, 200])
+def test_gemm_large_m_without_workspace_no_split(M):
+    # the large-M kernel without a workspace: no split of K (the plan with a
+    # workspace splits K over workgroups on this narrow layer)
+    N, K = 256, 4096
+    with_ws = w4.w4a16_gemm_plan(M, N, K, dtype=torch.bfloat16)
+    without = w4.w4a16_gemm_plan(M, N, K, dtype=torch.bfloat16, workspace=False)
+    say("large M without workspace", M, with_ws, without)
+    assert not any("split_reduce" in k for k in without)
+    W, gi, _ = int4_inputs("gpu/gemm/nows/pf/%d" % M, N, K)
     _, packed = gpu_int4_pack(W, gi)
-    y1 = tensor_bits(w4.w4a16_gemm(bits_to_tensor(xb, "f16"), packed))
-    y2 = tensor_bits(w4.w4a16_gemm(bits_to_tensor(xb, "f16"), packed))
-    assert np.array_equal(y1, y2)
-    y3 = w4.w4a16_gemm(bits_to_tensor(x2b, "f16"), packed).float().cpu().numpy()
-    y1f = y1.view(np.float16).astype(np.float32)
-    # doubling is exact through the fp32 accumulation; the final fp16 rounding
-    # commutes with it except in the fp16 subnormal range (absolute step 2^-24)
-    normal = np.abs(y1f) >= 2.0**-14
-    bad = np.nonzero(normal & (y3 != 2 * y1f))
-    assert bad[0].size == 0, list(zip(bad[0][:5], bad[1][:5], y1f[bad][:5], y3[bad][:5]))
-
-
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_gemm_onehot_reads_dequantized_weight_exactly(dtype):
-    N, K = 128, 512
-    say("onehot", dtype)
-    W, gi, _ = int4_inputs("gpu/onehot", N, K, act_order=True)
-    _, packed = gpu_int4_pack(W, gi)
-    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
-    ks = [0, 1, 127, 128, 300, 511]
-    x = np.zeros((len(ks), K), dtype=np.float32)
-    for r, k in enumerate(ks):
-        x[r, k] = 1.0
-    y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, dtype), dtype), packed))
-    for r, k in enumerate(ks):
-        assert np.array_equal(y[r], wd[:, k]), k
-
-
-def test_gemm_q_equals_z_gives_zero():
-    M, N, K = 5, 128, 256
-    z = np.random.default_rng(12).integers(0, 16, size=(K // 128, N)).astype(np.uint8)
-    q = z[np.arange(K) // 128].T.copy()
-    s = np.full((K // 128, N), 0.01, dtype=np.float16)
-    packed = w4.w4a16_repack(torch.from_numpy(int4.pack_qweight(q)).to(DEV),
-                             torch.from_numpy(s.view(np.int16)).view(torch.float16).to(DEV),
-                             torch.from_numpy(int4.pack_qzeros(z)).to(DEV))
-    x = bits_to_tensor(synth.to_f16_bits(synth.activations("gpu/qz/x", M, K)), "f16")
-    y = w4.w4a16_gemm(x, packed)
-    assert not torch.any(y.view(torch.int16) & 0x7FFF)
-
-
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_gemm_subnormal_activation_is_not_flushed(dtype):
-    # one-hot rows whose single nonzero is the smallest subnormal of the input
-    # type, against a weight column of large exact values: y = x * w is exact
-    # and far from underflow in the output, so a flushed input shows as 0.
-    N, K = 64, 256
-    q = np.full((N, K), 15, dtype=np.uint8)
-    z = np.zeros((K // 128, N), dtype=np.uint8)
-    s = np.full((K // 128, N), 1024.0, dtype=np.float16)       # w = 15 * 1024
-    packed = w4.w4a16_repack(torch.from_numpy(int4.pack_qweight(q)).to(DEV),
-                             torch.from_numpy(s.view(np.int16)).view(torch.float16).to(DEV),
-                             torch.from_numpy(int4.pack_qzeros(z)).to(DEV))
-    tiny = np.uint16(0x0001)                                    # smallest subnormal
-    xb = np.zeros((2, K), dtype=np.uint16)
-    xb[0, 3] = tiny
-    xb[1, 200] = tiny | 0x8000
-    y = tensor_f64(w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed), dtype)
-    sub = 2.0**-24 if dtype == "f16" else 2.0**-133
-    want = 15 * 1024.0 * sub          # 1.875 * 2^e: exact in both output types
-    assert np.all(y[0] == want), y[0][:4]
-    assert np.all(y[1] == -want)
-
-
-@pytest.mark.parametrize("M,N,K", [(6, 160, 1024), (12, 160, 1024), (16, 4112, 512), (24, 208, 2048)])
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_full_row_modes_onehot_exact(M, N, K, dtype):
-    # the decode kernel's full-row modes, act-order: direct loads (6 rows on
-    # 160 columns) and whole-line loads through the LDS transpose (12, 16 on
-    # 4112 columns, 24 rows in two row tiles).  One nonzero 1.0 per row puts
-    # one dequantized weight in each output: any misplaced chunk of the
-    # transpose shows as a wrong value
-    say("full-row onehot", M, N, K, dtype)
-    W, gi, _ = int4_inputs("gpu/gemm/fullrow/%d/%d" % (N, K), N, K, act_order=True)
-    _, packed = gpu_int4_pack(W, gi)
-    ks = (np.arange(M) * 37 + 5) % K
-    x = np.zeros((M, K), dtype=np.float32)
-    x[np.arange(M), ks] = 1.0
-    y = tensor_bits(w4.w4a16_gemm(bits_to_tensor(synth.to_bits(x, dtype), dtype), packed))
-    cols = np.unique(np.concatenate([np.arange(0, N, 7), [N - 1]]))
-    wd = oracle_int4_rows(W, gi, cols, dtype)
-    for r, k in enumerate(ks):
-        assert np.array_equal(y[r][cols], wd[:, k]), (r, k)
+    xb = synth.to_bits(synth.activations("gpu/gemm/nows/pf/x/%d" % M, M, K), "bf16")
+    y0 = w4.w4a16_gemm(bits_to_tensor(xb, "bf16"), packed, use_workspace=False)
+    y1 = w4.w4a16_gemm(bits_to_tensor(xb, "bf16"), packed)
+    torch.cuda.synchronize()
+    wd = oracle_int4_rows(W, gi, np.arange(N), "bf16")
+    assert compare_gemm(y0, xb, wd, "bf16") <= TOL
+    assert compare_gemm(y1, xb, wd, "bf16") <= TOL

@@ -119,10 +119,13 @@ def test_nf4_gemm_large_m(M, dtype):
     xb = synth.to_bits(synth.activations("gpu/nf4L/x/%d" % M, M, K), dtype)
     p = _pack(W)
     y = w4.nf4_gemm(bits_to_tensor(xb, dtype), p)
+    # without a workspace: the large-M kernel does not split K
+    y0 = w4.nf4_gemm(bits_to_tensor(xb, dtype), p, use_workspace=False)
     codes, absmax = nf4.quantize_nf4(W, 64)
     aq, sc = nf4.double_quant(absmax)
     wd = nf4.dequant_nf4(nf4.pack_nf4(codes), aq, sc, 64, dtype)
     assert compare_gemm(y, xb, wd, dtype) <= TOL
+    assert compare_gemm(y0, xb, wd, dtype) <= TOL
 
 
 def test_nf4_large_m_onehot_exact():

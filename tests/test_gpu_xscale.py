@@ -126,3 +126,26 @@ def test_xscale_large_layer_sampled():
     err = gemm.rel_err(tensor_f64(y, dtype)[:, rows], y_ref)
     say("  rel err", err)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("M", [3, 8, 40, 300])
+@pytest.mark.parametrize("act", [False, True])
+def test_xscale_gemm_without_workspace(M, act):
+    # no workspace: no preparation pass; rows the decode kernel cannot stage on
+    # chip are gathered (and divided by s) element by element from global
+    # memory, at any M
+    N, K = 200, 2560
+    dtype = "bf16" if act else "f16"
+    tag = "gpu/xs/nows/%d" % M
+    say("xscale without workspace", M, act, dtype, w4.w4a16_gemm_plan(
+        M, N, K, dtype=torch.bfloat16 if act else torch.float16, perm=act, x_scale=True,
+        workspace=False))
+    packed, sb, wd = _awq_setup(tag, N, K, 128, False, act, dtype)
+    xb = _x(tag, M, K, dtype)
+    y = w4.w4a16_gemm_xscale(bits_to_tensor(xb, dtype), bits_to_tensor(sb, dtype), packed,
+                             use_workspace=False)
+    torch.cuda.synchronize()
+    y_ref = gemm.gemm_ref_xscale_bits(xb, sb, wd, dtype)
+    err = gemm.rel_err(tensor_f64(y, dtype), y_ref)
+    say("  rel err", err)
+    assert err <= TOL

@@ -31,6 +31,42 @@ def test_codebook_matches_independent_inverse_normal():
     assert np.array_equal(v.astype(np.float32), nf4.nf4_codebook())
 
 
+def test_codebook_matches_printed_levels():
+    # the printed 16-value table (tests/golden/nf4_levels.json, an evaluation
+    # of the construction that does not go through oracle/): every level within
+    # half a unit of its last printed digit.  A wrong delta, a wrong count of
+    # positive or negative quantiles, or a missing normalisation moves several
+    # levels by far more than that.
+    import json
+    import os
+    from decimal import Decimal
+    path = os.path.join(os.path.dirname(__file__), "golden", "nf4_levels.json")
+    printed = json.load(open(path))["levels"]
+    L = nf4.nf4_codebook()
+    assert len(printed) == 16
+    for i, t in enumerate(printed):
+        d = Decimal(t)
+        half_unit = 0.5 * 10.0 ** d.as_tuple().exponent
+        assert abs(float(L[i]) - float(d)) <= half_unit, (i, float(L[i]), t)
+
+
+def test_codebook_delta_perturbation_is_caught():
+    # the printed levels distinguish the delta of the construction from a
+    # nearby one (as a plausible slip would give): with delta = 1 - 1/30 or
+    # 1 - 1/32 the interior levels move by 1e-3 .. 1e-2
+    from statistics import NormalDist
+    inv = NormalDist().inv_cdf
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "nf4_levels.json")
+    printed = np.array([float(t) for t in json.load(open(path))["levels"]])
+    for d in (1 - 1 / 30, 1 - 1 / 32):
+        pos = [inv(p) for p in np.linspace(d, 0.5, 9)[:-1]]
+        neg = [-inv(p) for p in np.linspace(d, 0.5, 8)[:-1]]
+        v = np.array(sorted(pos + [0.0] + neg)) / inv(d)
+        assert np.max(np.abs(v - printed)) > 1e-4
+
+
 def test_quantize_brute_force_argmin():
     L = nf4.nf4_codebook()
     W = synth.weights("test/nf4/brute", 3, 256)
