@@ -12,14 +12,19 @@ resident in HBM before timing starts.
 
 Printed: ONE JSON line with the weight-stream GB/s of the step (value), the
 effective TFLOP/s, the roofline of the dominant kernel (HIP-event durations of
-every GEMM launch in the timed region), and the CPU oracle timed on a bounded
-sample on this host.
+every GEMM launch in the timed region), per-call figures against the plain
+streaming-read ceiling of the same bytes, the unfused comparator (dequantize
+to 16 bits, then multiply), prefill / Qwen-shaped / NF4 / format-variant
+figures, and the CPU oracle timed on a bounded sample on this host.  Kernel
+names come from the library's own plan query (w4a16_gemm_plan), the names
+the profiler reports.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 import argparse
 import ctypes
+import glob
 import json
 import os
 import sys
@@ -31,10 +36,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 MFMA
 SHAPES = [(4096, 4096), (4096, 11008), (11008, 4096)]   # (K, N)
 MS = [1, 4, 16]
 G = 128
+PREFILL_SHAPES = [(5120, 7168), (5120, 5120), (5120, 55296), (27648, 5120)]   # (K, N)
 
 
 def weight_bytes(K, N, perm=True):
@@ -44,35 +50,20 @@ def weight_bytes(K, N, perm=True):
 def call_bytes(M, K, N):
     """Algorithmic bytes of the GEMM kernel itself: codes + scales + zeros, the
     (permuted) activations and the output.  The permutation vector is read by
-    the separate act-order gather kernel."""
+    the gather (in the kernel, or the separate preparation pass)."""
     return weight_bytes(K, N, perm=False) + 2 * M * K + 2 * M * N
 
 
-def kernel_name(M, K, N):
-    """Kernel instantiation the library picks for an act-order call with M
-    rows (f16).  Mirrors its rules: the large-M kernel from 32 rows (5 on
-    layers of 100 Mi weights; 17 on layers of 24 Mi weights with N < 5120);
-    otherwise the
-    decode kernel, where M <= 4 rows are gathered in the kernel when the
-    staged rows + permutation take at most 72 KB per workgroup and 17 MiB over
-    the N/16 workgroups, else a preparation pass permutes them first; one row
-    (M = 1) has an instantiation of its own (the one-row form of the fold);
-    more rows take the full-row modes."""
-    kb = lambda b: (b + 1023) // 1024 * 1024
-    w = N * K
-    if (M >= 32 or (w >= 100 << 20 and M >= 5)
-            or (w >= 24 << 20 and N < 5120 and M >= 17)):
-        return "wq_prefill_kernel<f16, INT 4-bit>"      # the large-M kernel
-    if M <= 4:
-        staged = kb(M * K * 2) + kb(K * 4)
-        mode = ("xgather" if staged <= 72 * 1024 and ((N + 15) // 16) * staged <= 17 << 20
-                else "packed")
-        return "intb_decode_kernel<f16, MT=1, %s, 4-bit%s>" % (mode, ", one row" if M == 1 else "")
-    mt = 1 if M <= 16 else (2 if M <= 32 else 4)
-    # full rows: direct loads for at most 8 rows on at most 4096 columns, else
-    # whole-line loads and a transpose through LDS
-    return "intb_decode_kernel<f16, MT=%d, %s, 4-bit>" % (mt, "full" if M <= 8 and N <= 4096
-                                                          else "full-t")
+def plan(w4, M, N, K, dtype, perm=False, xs=False, ws=True):
+    import torch
+    return w4.w4a16_gemm_plan(M, N, K, G, 4, torch.float16 if dtype == "f16" else torch.bfloat16,
+                              perm=perm, x_scale=xs, workspace=ws)
+
+
+def main_kernel(kernels):
+    """The call's GEMM kernel: the first launch that is not the preparation
+    pass (the one the timing events attach to)."""
+    return [k for k in kernels if "prep_x_kernel" not in k][0]
 
 
 def parse():
@@ -85,11 +76,148 @@ def parse():
     ap.add_argument("--no-nf4", action="store_true")
     ap.add_argument("--no-qwen", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--prefill-only", type=str, default=None,
+                    help="run only the prefill of one layer, 'K,N,M' (for a per-shape profile)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run each decode call of the workload once, then a 256 MiB device copy "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), and exit")
     ap.add_argument("--min-rotation-mb", type=float, default=512.0)
     return ap.parse_args()
+
+
+def host_info(torch, dev):
+    """Provenance of the measurement: GPU, CUs, current and top sclk (sysfs),
+    ROCm version, host CPU model and count.  Reads files only."""
+    props = torch.cuda.get_device_properties(dev)
+    info = {"gpu": props.name, "cus": props.multi_processor_count}
+    try:
+        arch = getattr(props, "gcnArchName", None)
+        if arch:
+            info["arch"] = arch
+    except Exception:
+        pass
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            lines = [l.strip() for l in open(path) if l.strip()]
+        except OSError:
+            continue
+        mhz = [int(l.split(":")[1].strip().split("Mhz")[0].split("MHz")[0]) for l in lines
+               if ":" in l and "hz" in l.lower()]
+        cur = [l for l in lines if l.endswith("*")]
+        if mhz:
+            info["sclk_mhz_max"] = max(mhz)
+            if cur:
+                info["sclk_mhz_now"] = int(cur[0].split(":")[1].strip().split("M")[0])
+            break
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            info["rocm"] = open(path).read().strip()
+            break
+        except OSError:
+            pass
+    try:
+        for l in open("/proc/cpuinfo"):
+            if l.startswith("model name"):
+                info["host_cpu"] = l.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info["host_cpus"] = os.cpu_count()
+    info["torch"] = torch.__version__
+    return info
+
+
+class KernelTimer:
+    """Durations of the library's main kernel launch, from hipExtLaunchKernel
+    start/stop events (w4a16_set_timing_events) on the stream it runs on."""
+
+    def __init__(self, L, hip):
+        self.L, self.hip = L, hip
+        self.ev = (ctypes.c_void_p * 2)()
+        for k in range(2):
+            if hip.hipEventCreate(ctypes.byref(self.ev, k * ctypes.sizeof(ctypes.c_void_p))):
+                raise RuntimeError("hipEventCreate failed")
+
+    def time(self, call, reps, warm=3, stat="median"):
+        import torch
+        ts = []
+        ms = ctypes.c_float(0.0)
+        for r in range(warm + reps):
+            self.L.w4a16_set_timing_events(ctypes.c_void_p(self.ev[0]),
+                                           ctypes.c_void_p(self.ev[1]))
+            if call() != 0:
+                raise RuntimeError("library call failed")
+            torch.cuda.synchronize()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[0]),
+                                            ctypes.c_void_p(self.ev[1])) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            if r >= warm:
+                ts.append(ms.value * 1e-3)
+        return float(np.median(ts) if stat == "median" else np.mean(ts))
+
+
+def graph_time(fns, stream, reps=5):
+    """Seconds per replay of a HIP graph that runs fns in order."""
+    import torch
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fns:
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+class StreamCeiling:
+    """The plain streaming read of the library (w4a16_stream_read) over a given
+    number of bytes, from rotating buffers past the caches: per-call kernel
+    time (HIP events) and whole-call time (HIP-graph replays of 10 calls), the
+    best of 256 / 512 / 1024 workgroups."""
+
+    def __init__(self, L, timer, stream):
+        self.L, self.timer, self.stream = L, timer, stream
+        self.cache = {}
+
+    def __call__(self, nbytes):
+        import torch
+        nb = (nbytes + 15) // 16 * 16
+        if nb in self.cache:
+            return self.cache[nb]
+        R = max(2, int(np.ceil(600e6 / nb)))
+        bufs = [torch.ones(nb // 4, dtype=torch.int32, device="cuda") for _ in range(R)]
+        best = None
+        sp = ctypes.c_void_p(self.stream.cuda_stream)
+        for wg in (256, 512, 1024):
+            out = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+            k = [0]
+
+            def one(b=None):
+                b = bufs[k[0] % R] if b is None else b
+                k[0] += 1
+                return self.L.w4a16_stream_read(ctypes.c_void_p(b.data_ptr()), nb, wg,
+                                                ctypes.c_void_p(out.data_ptr()), sp)
+            kt = self.timer.time(one, 20)
+            gt = graph_time([lambda b=bufs[i % R]: one(b) for i in range(10)], self.stream) / 10
+            if best is None or kt < best["kernel_us"] * 1e-6:
+                best = {"bytes": nb, "workgroups": wg, "kernel_us": round(kt * 1e6, 2),
+                        "call_us": round(gt * 1e6, 2)}
+            del out
+        best["pct_hbm_kernel"] = round(100 * nb / (best["kernel_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)
+        del bufs
+        torch.cuda.empty_cache()
+        self.cache[nb] = best
+        return best
 
 
 def main():
@@ -111,6 +239,12 @@ def main():
     stream = torch.cuda.Stream()          # graphs are captured on a non-default stream
     torch.cuda.set_stream(stream)
     sptr = ctypes.c_void_p(stream.cuda_stream)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    timer = KernelTimer(L, hip)
+    if args.prefill_only:
+        K, N, M = (int(v) for v in args.prefill_only.split(","))
+        print(json.dumps(bench_prefill(L, timer, sptr, M=M, shapes=[(K, N)])), flush=True)
+        return
 
     # ---- inputs: weights quantized + repacked on the device, x per M
     base = {}
@@ -167,27 +301,52 @@ def main():
         run_step(i)
     torch.cuda.synchronize()
 
-    # ---- one HIP graph per weight-rotation set: a step is one graph replay
-    # (the 9 GEMM calls with their act-order permutation kernels), so host
-    # launch overhead is out of the measured step.
-    graphs = []
+    # ---- HIP graphs.  One graph holds R consecutive steps, one over each
+    # rotating weight copy (9 R GEMM calls with their act-order permutation
+    # passes), the way a serving engine captures a whole model's decode step
+    # (hundreds of GEMMs) in one graph: each graph launch costs a fixed gap on
+    # this stack (about 20 us), which a real step amortizes over all its
+    # layers.  K steps are K // R replays of it plus one replay of a graph of
+    # the first K % R steps.  For reference, one-step graphs are timed too.
+    def capture(nsteps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(nsteps):
+                run_step(r)
+        return g
+    g_all = capture(R)
+    g_rest = capture(args.steps % R) if args.steps % R else None
+    g_one = [None] * R
     for r in range(R):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             run_step(r)
-        graphs.append(g)
+        g_one[r] = g
     torch.cuda.synchronize()
-    for i in range(max(args.warmup, R)):
-        graphs[i % R].replay()
+    for i in range(max(1, args.warmup // R)):
+        g_all.replay()
     torch.cuda.synchronize()
 
-    # ---- timed region, part 1: K steps (graph replays), synchronized both sides
+    # ---- timed region, part 1: exactly K steps (graph replays), synchronized
+    # both sides
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[i % R].replay()
+    for i in range(args.steps // R):
+        g_all.replay()
+    if g_rest is not None:
+        g_rest.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
+    # (context: the same steps with one graph per step)
+    for i in range(R):
+        g_one[i].replay()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        g_one[i % R].replay()
+    torch.cuda.synchronize()
+    step1_s = (time.perf_counter() - t2) / args.steps
+    graphs = [g_all, g_rest] + g_one
 
     # ---- timed region, part 2: the same K steps launched eagerly with HIP
     # timing events attached to every GEMM kernel's own dispatch
@@ -199,13 +358,15 @@ def main():
     # library's permutation pass in front of it), and the stream is drained
     # after every call, before the next one is queued.  (The step time above
     # includes the pass and runs the calls back to back.)
-    hip = ctypes.CDLL("libamdhip64.so.7")
     nper = len(calls[0])
+    kern = {}
     tcalls = []
     for step_layers, cl in zip(rot, calls):
         tl = []
         for (K, N, M, q), (a, _, _, _) in zip(step_layers, cl):
-            if ", xgather," in kernel_name(M, K, N):
+            ks = plan(w4, M, N, K, "f16", perm=True)
+            kern[(M, K, N)] = ks
+            if "prep_x_kernel" not in ks[0]:
                 tl.append(a)
                 continue
             key = ("xp", M, K, N)
@@ -248,21 +409,26 @@ def main():
     # the dominant kernel: the instantiation with the most time per step
     groups = {}
     for j, (K, N, M, _) in enumerate(rot[0]):
-        groups.setdefault(kernel_name(M, K, N), []).append(j)
+        groups.setdefault(main_kernel(kern[(M, K, N)]), []).append(j)
     dom = max(groups, key=lambda g: dur[:, groups[g]].sum())
     dj = groups[dom]
     avg_launch_s = float(dur[:, dj].mean())
     dom_bytes = float(np.mean([calls[0][j][1] for j in dj]))
     achieved = dom_bytes / avg_launch_s / 1e9
+
+    # ---- context: the streaming-read ceiling of each call's weight bytes
+    ceil = StreamCeiling(L, timer, stream)
     per_point = []
     for j, (K, N, M, _) in enumerate(rot[0]):
         d = float(dur[:, j].mean())
-        per_point.append({"M": M, "K": K, "N": N, "kernel": kernel_name(M, K, N),
+        c = ceil(call_bytes(M, K, N))
+        per_point.append({"M": M, "K": K, "N": N, "kernels": kern[(M, K, N)],
                           "us": round(d * 1e6, 2),
                           "weight_GBps": round(weight_bytes(K, N) / d / 1e9, 1),
-                          "pct_hbm": round(100 * call_bytes(M, K, N) / d / 1e9 / HBM_PEAK_GBS, 1)})
+                          "pct_hbm": round(100 * call_bytes(M, K, N) / d / 1e9 / HBM_PEAK_GBS, 1),
+                          "stream_read_us": c["kernel_us"],
+                          "x_stream_read": round(d * 1e6 / c["kernel_us"], 2)})
 
-    props = torch.cuda.get_device_properties(dev)
     result = {
         "metric": "W4A16 GEMM TFLOP/s + weight GB/s (% of HBM/MFMA peak), M=1..16 and M=2048",
         "value": round(step_wbytes / step_s / 1e9, 1),
@@ -276,18 +442,18 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic (seeded N(0,0.02) weights RTN-quantized on device, N(0,1) activations)",
-        "config": {
+        "config": dict({
             "workload": "Llama-2-7B-shaped decode GEMMs, GPTQ act-order int4 G=128: "
                         "(K,N) in {(4096,4096),(4096,11008),(11008,4096)} x M in {1,4,16}",
             "gemm_calls_per_step": nper,
-            "step_timing": "HIP graph replay per step (the GEMM kernels, plus the act-order "
-                           "permutation pass where the kernel does not gather itself)",
+            "step_timing": "HIP graphs of R consecutive steps (one per rotating weight copy; "
+                           "the GEMM kernels, plus the act-order permutation pass where the "
+                           "kernel does not gather itself)",
             "weight_rotation_copies": R,
+            "ms_per_step_one_step_graphs": round(step1_s * 1e3, 4),
             "tflops": round(step_flops / step_s / 1e12, 3),
             "pct_hbm_step": round(100 * step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 1),
-            "gpu": props.name,
-            "cus": props.multi_processor_count,
-        },
+        }, **host_info(torch, dev)),
         "roofline": {
             "bound": "hbm",
             "kernel": dom,
@@ -305,26 +471,69 @@ def main():
         },
         "points": per_point,
     }
-    timer = KernelTimer(L, hip)
+    if not args.no_unfused:
+        result["unfused"] = bench_unfused(w4, rot, xs, stream, step_s)
     del rot, calls, graphs, base
     torch.cuda.empty_cache()
     if not args.no_prefill:
         result["prefill"] = bench_prefill(L, timer, sptr)
         result["prefill_m8192"] = bench_prefill(L, timer, sptr, M=8192)
     if not args.no_qwen:
-        result["qwen_decode"] = bench_qwen_decode()
+        result["qwen_decode"] = bench_qwen_decode(w4, ceil)
     if not args.no_nf4:
-        result["nf4"] = bench_nf4(L, timer, sptr)
+        result["nf4"] = bench_nf4(L, w4, timer, sptr, ceil)
     if not args.no_variants:
         result["variants"] = bench_variants()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(xs, outs)
+    result["child_processes_at_exit"] = child_processes()
     print(json.dumps(result), flush=True)
+
+
+def child_processes():
+    """Processes this bench left running (it starts none itself)."""
+    try:
+        import psutil
+        return [" ".join(p.cmdline()[:3]) for p in psutil.Process().children(recursive=True)]
+    except Exception as e:
+        return "unknown (%s)" % type(e).__name__
+
+
+def bench_unfused(w4, rot, xs, stream, fused_step_s):
+    """The pages' "default kernel": the weights dequantized to 16 bits on every
+    forward, then a dense multiply -- here the library's dequant export
+    (w4a16_dequant, W [N, K] fp16 in permuted column order) followed by
+    torch's x[:, perm] and F.linear (hipBLASLt), for each call of the decode
+    step, over the same rotating weight sets; one HIP graph per step."""
+    import torch
+    import torch.nn.functional as F
+    R = len(rot)
+    wbuf = {}
+    for K, N, M, q in rot[0]:
+        wbuf.setdefault((K, N), torch.empty((N, K), dtype=torch.float16, device="cuda"))
+
+    perm64 = {id(q): q["perm"].long() for r in range(min(R, 3)) for _, _, _, q in rot[r]}
+
+    def step_fns(r):
+        fns = []
+        for K, N, M, q in rot[r]:
+            def f(K=K, N=N, M=M, q=q):
+                wd = w4.w4a16_dequant(q, torch.float16, out=wbuf[(K, N)])
+                F.linear(xs[(M, K)].index_select(1, perm64[id(q)]), wd)
+            fns.append(f)
+        return fns
+    times = [graph_time(step_fns(r), stream) for r in range(min(R, 3))]
+    t = float(np.median(times))
+    return {"what": "w4a16_dequant (fp16 W written to HBM) + x[:, perm] + F.linear per call, "
+                    "the 9 calls of the step in one HIP graph",
+            "ms_per_step": round(t * 1e3, 4),
+            "fused_speedup": round(t / fused_step_s, 2)}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "int4_decode_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_only_gemm_amd", "csrc", f)
-                  for f in ("gemm.hip", "decode.h", "common.h", "prefill.h", "prefill.hip")]
+                  for f in ("gemm.hip", "decode.h", "common.h", "kernels.h", "prefill.h",
+                            "prefill.hip")]
 
 
 def kernel_source_hash():
@@ -357,6 +566,7 @@ def pmc_probe(L, dev):
     import torch
     import bit_weight_only_gemm_amd as w4
     from bit_weight_only_gemm_amd import synth
+    print("source_hash %s" % kernel_source_hash(), flush=True)
     for K, N in SHAPES:
         W = torch.from_numpy(synth.weights("C2/W/%dx%d" % (K, N), N, K)).to(dev)
         gi = torch.from_numpy(synth.act_order_gidx("C2/gidx/%dx%d" % (K, N), K, G)).to(dev)
@@ -368,8 +578,9 @@ def pmc_probe(L, dev):
             x = torch.from_numpy(xb.view(np.int16)).view(torch.float16).to(dev)
             w4.w4a16_gemm(x, p)
             torch.cuda.synchronize()
-            print("call M=%d K=%d N=%d kernel=%s algorithmic_bytes=%d"
-                  % (M, K, N, kernel_name(M, K, N), call_bytes(M, K, N)), flush=True)
+            print("call M=%d K=%d N=%d kernels=%s algorithmic_bytes=%d"
+                  % (M, K, N, " + ".join(plan(w4, M, N, K, "f16", perm=True)),
+                     call_bytes(M, K, N)), flush=True)
     src = torch.ones(64 * 2**20, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -378,47 +589,20 @@ def pmc_probe(L, dev):
     print("copy bytes_read=%d bytes_written=%d" % (src.numel() * 4, dst.numel() * 4), flush=True)
 
 
-class KernelTimer:
-    """Durations of the library's main kernel launch, from hipExtLaunchKernel
-    start/stop events (w4a16_set_timing_events) on the stream it runs on."""
-
-    def __init__(self, L, hip):
-        self.L, self.hip = L, hip
-        self.ev = (ctypes.c_void_p * 2)()
-        for k in range(2):
-            if hip.hipEventCreate(ctypes.byref(self.ev, k * ctypes.sizeof(ctypes.c_void_p))):
-                raise RuntimeError("hipEventCreate failed")
-
-    def time(self, call, reps, warm=3):
-        import torch
-        ts = []
-        ms = ctypes.c_float(0.0)
-        for r in range(warm + reps):
-            self.L.w4a16_set_timing_events(ctypes.c_void_p(self.ev[0]), ctypes.c_void_p(self.ev[1]))
-            if call() != 0:
-                raise RuntimeError("library call failed")
-            torch.cuda.synchronize()
-            self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[0]),
-                                         ctypes.c_void_p(self.ev[1]))
-            if r >= warm:
-                ts.append(ms.value * 1e-3)
-        return float(np.median(ts))
-
-
-PREFILL_SHAPES = [(5120, 7168), (5120, 5120), (5120, 55296), (27648, 5120)]   # (K, N)
-
-
-def bench_prefill(L, timer, sptr, M=2048):
+def bench_prefill(L, timer, sptr, M=2048, shapes=PREFILL_SHAPES):
     """Qwen2.5-32B-shaped prefill layers at M tokens, bf16 activations
     ~N(0,1) with 1 % of the input channels x20, RTN int4 G=128 weights:
-    median kernel time of the fused kernel, and dense bf16 torch.matmul of
-    the dequantized weights (the practical matrix-core ceiling) beside it."""
+    median kernel time of the fused kernel (all its launches: the main
+    kernel's events cover the first, the whole call is timed too), and dense
+    bf16 torch.matmul of the dequantized weights (the practical matrix-core
+    ceiling) beside it.  The roofline fraction is over all the shapes
+    together (total flops / total time); the best shape is reported too."""
     import torch
     import bit_weight_only_gemm_amd as w4
     from bit_weight_only_gemm_amd import synth
     dev = torch.device("cuda:0")
     pts = []
-    for K, N in PREFILL_SHAPES:
+    for K, N in shapes:
         W = torch.from_numpy(synth.weights("C4/W/%dx%d" % (K, N), N, K)).to(dev)
         qw, sc, qz = w4.w4a16_quantize_rtn(W, G)
         p = w4.w4a16_repack(qw, sc, qz, None)
@@ -435,9 +619,18 @@ def bench_prefill(L, timer, sptr, M=2048):
              ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), wsb, sptr)
         for _ in range(20):          # clocks up before the first timed shape
             L.w4a16_gemm(*a)
-        t = timer.time(lambda: L.w4a16_gemm(*a), 10)
-        wd = w4.w4a16_dequant(p, torch.bfloat16)
+        kernels = plan(w4, M, N, K, "bf16")
+        t_main = timer.time(lambda: L.w4a16_gemm(*a), 10)
+        # the whole call (every launch of it), event-timed around 10 calls
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            L.w4a16_gemm(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / 10
+        wd = w4.w4a16_dequant(p, torch.bfloat16)
         for _ in range(3):
             torch.matmul(x, wd.t())
         e0.record()
@@ -447,7 +640,8 @@ def bench_prefill(L, timer, sptr, M=2048):
         torch.cuda.synchronize()
         td = e0.elapsed_time(e1) * 1e-3 / 10
         fl = 2.0 * M * N * K
-        pts.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 1),
+        pts.append({"M": M, "K": K, "N": N, "kernels": kernels, "us": round(t * 1e6, 1),
+                    "main_kernel_us": round(t_main * 1e6, 1),
                     "tflops": round(fl / t / 1e12, 1),
                     "pct_mfma": round(100 * fl / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 1),
                     "dense_bf16_matmul_tflops": round(fl / td / 1e12, 1)})
@@ -456,47 +650,26 @@ def bench_prefill(L, timer, sptr, M=2048):
     best = max(pts, key=lambda q: q["tflops"])
     tot_fl = sum(2.0 * q["M"] * q["N"] * q["K"] for q in pts)
     tot_t = sum(q["us"] for q in pts) * 1e-6
+    allt = tot_fl / tot_t / 1e12
     return {"workload": "Qwen2.5-32B-shaped prefill, int4 G=128, bf16 x with 1% outlier "
                         "channels x20, M=" + str(M),
-            "kernel": "wq_prefill_kernel<bf16, INT 4-bit>",
-            "tflops_all_shapes": round(tot_fl / tot_t / 1e12, 1),
-            "roofline": {"bound": "mfma", "achieved": best["tflops"],
+            "tflops_all_shapes": round(allt, 1),
+            "roofline": {"bound": "mfma", "achieved": round(allt, 1),
                          "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(best["tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
-                         "shape": [best["M"], best["K"], best["N"]]},
+                         "frac": round(allt / MFMA_F16_PEAK_TFLOPS, 4),
+                         "over": "all shapes (total flops / total whole-call time)",
+                         "best_shape": [best["M"], best["K"], best["N"]],
+                         "best_shape_frac": round(best["tflops"] / MFMA_F16_PEAK_TFLOPS, 4)},
             "points": pts}
 
 
-def graph_call_time(call, ps, stream, n=10, reps=5):
-    """Seconds per call of `call(p)` over the weight copies ps, from HIP-graph
-    replays of n calls (the whole call: any preparation pass and reduction)."""
-    import torch
-    for r in range(3):
-        call(ps[r % len(ps)])
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for r in range(n):
-            call(ps[r % len(ps)])
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    del g
-    return e0.elapsed_time(e1) * 1e-3 / (reps * n)
-
-
-def bench_qwen_decode(Ms=(1, 16, 64)):
+def bench_qwen_decode(w4, ceil, Ms=(1, 16, 64)):
     """The Qwen2.5-32B-shaped layers in AWQ layout (s ~ U[0.5, 2] folded into W,
     x divided by s before the call), int4 G=128, fp16 activations, at M in
     {1, 16, 64}: whole calls by HIP-graph replay over rotating weight copies
-    (>= 512 MB), weight-stream GB/s per layer and over the four layers."""
+    (>= 512 MB), weight-stream GB/s per layer and over the four layers, with
+    the streaming-read ceiling of the same bytes (whole calls too)."""
     import torch
-    import bit_weight_only_gemm_amd as w4
     from bit_weight_only_gemm_amd import synth
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -517,11 +690,16 @@ def bench_qwen_decode(Ms=(1, 16, 64)):
                  / s[None, :]).half()
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
             ws = w4.workspace(w4.w4a16_workspace_bytes(M, N, K), dev)
-            t = graph_call_time(lambda p: w4.w4a16_gemm(x, p, out=y, workspace=ws), ps, stream)
+            t = graph_time([lambda p=ps[i % R]: w4.w4a16_gemm(x, p, out=y, workspace=ws)
+                            for i in range(10)], stream) / 10
             byt = wb + 2 * M * K + 2 * M * N
-            pts.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 2),
+            c = ceil(byt)
+            pts.append({"M": M, "K": K, "N": N, "kernels": plan(w4, M, N, K, "f16"),
+                        "us": round(t * 1e6, 2),
                         "weight_GBps": round(wb / t / 1e9, 1),
-                        "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1)})
+                        "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1),
+                        "stream_read_call_us": c["call_us"],
+                        "x_stream_read": round(t * 1e6 / c["call_us"], 2)})
             tot[M][0] += t
             tot[M][1] += wb
             del x, y, ws
@@ -566,11 +744,11 @@ def bench_variants(K=5120, N=55296, Ms=(1, 2048)):
     s_awq = torch.from_numpy(synth.to_bf16_bits(synth.awq_scales("C6/s/%d" % K, K)[None, :])[0]
                              .view(np.int16)).view(torch.bfloat16).to(dev)
     pts = []
-    for label, bits, G, sym, xs in VARIANTS:
-        qw, sc, qz = w4.w4a16_quantize_rtn(W, G, sym=sym, bits=bits)
-        p0 = w4.w4a16_repack(qw, sc, qz, None, G, bits=bits)
+    for label, bits, G_, sym, xsc in VARIANTS:
+        qw, sc, qz = w4.w4a16_quantize_rtn(W, G_, sym=sym, bits=bits)
+        p0 = w4.w4a16_repack(qw, sc, qz, None, G_, bits=bits)
         del qw, sc, qz
-        wb = variant_weight_bytes(K, N, bits, G, sym)
+        wb = variant_weight_bytes(K, N, bits, G_, sym)
         R = max(2, int(np.ceil(512e6 / wb)))
         ps = [p0] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in p0.items()}
                      for _ in range(R - 1)]
@@ -578,31 +756,18 @@ def bench_variants(K=5120, N=55296, Ms=(1, 2048)):
             x32 = synth.activations("C6/x/%d" % M, M, K)
             x = torch.from_numpy(synth.to_bf16_bits(x32).view(np.int16)).view(torch.bfloat16).to(dev)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            ws = w4.workspace(w4.w4a16_workspace_bytes(M, N, K, G), dev)
+            ws = w4.workspace(w4.w4a16_workspace_bytes(M, N, K, G_), dev)
 
             def call(p):
-                if xs:
+                if xsc:
                     w4.w4a16_gemm_xscale(x, s_awq, p, out=y, workspace=ws)
                 else:
                     w4.w4a16_gemm(x, p, out=y, workspace=ws)
-            for r in range(3):
-                call(ps[r % R])
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for r in range(10):
-                    call(ps[r % R])
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(5):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / 50
-            pt = {"variant": label, "bits": bits, "group_size": G, "symmetric": sym,
-                  "awq_input_scales": xs, "M": M, "us": round(t * 1e6, 2)}
+            t = graph_time([lambda p=ps[i % R]: call(p) for i in range(10)], stream) / 10
+            pt = {"variant": label, "bits": bits, "group_size": G_, "symmetric": sym,
+                  "awq_input_scales": xsc, "M": M, "us": round(t * 1e6, 2),
+                  "kernels": w4.w4a16_gemm_plan(M, N, K, G_, bits, torch.bfloat16,
+                                                x_scale=xsc)}
             if M >= 1024:
                 fl = 2.0 * M * N * K
                 pt.update(tflops=round(fl / t / 1e12, 1),
@@ -612,7 +777,7 @@ def bench_variants(K=5120, N=55296, Ms=(1, 2048)):
                 pt.update(weight_bytes=wb, GBps=round(byt / t / 1e9, 1),
                           pct_hbm=round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1))
             pts.append(pt)
-            del x, y, ws, g
+            del x, y, ws
         del ps, p0
         torch.cuda.empty_cache()
     return {"workload": "5120 x 55296 layer, bf16 activations ~N(0,1), RTN weights of each "
@@ -620,12 +785,12 @@ def bench_variants(K=5120, N=55296, Ms=(1, 2048)):
             "points": pts}
 
 
-def bench_nf4(L, timer, sptr, K=8192, N=28672):
+def bench_nf4(L, w4, timer, sptr, ceil, K=8192, N=28672):
     """The NF4 projection: W [28672, 8192] ~N(0, 0.02), blocksize 64, double
     quant over 256 blocks, bf16 x ~N(0,1) at M in {1, 32}; 4 rotating weight
-    copies so the weights stream from HBM."""
+    copies so the weights stream from HBM; main-kernel time (HIP events) and
+    the streaming-read ceiling of the same bytes."""
     import torch
-    import bit_weight_only_gemm_amd as w4
     from bit_weight_only_gemm_amd import synth
     dev = torch.device("cuda:0")
     W = torch.from_numpy(synth.weights("C5/W/%dx%d" % (K, N), N, K)).to(dev)
@@ -653,11 +818,14 @@ def bench_nf4(L, timer, sptr, K=8192, N=28672):
                               ctypes.c_void_p(y.data_ptr()), M, N, K, w4.BF16, wsp, wsb, sptr)
         t = timer.time(call, 20)
         byt = wb + 2 * M * K + 2 * M * N
-        pts.append({"M": M, "K": K, "N": N, "us": round(t * 1e6, 2),
+        c = ceil(byt)
+        pts.append({"M": M, "K": K, "N": N, "kernels": w4.nf4_gemm_plan(M, N, K),
+                    "us": round(t * 1e6, 2),
                     "weight_GBps": round(wb / t / 1e9, 1),
-                    "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1)})
+                    "pct_hbm": round(100 * byt / t / 1e9 / HBM_PEAK_GBS, 1),
+                    "stream_read_us": c["kernel_us"],
+                    "x_stream_read": round(t * 1e6 / c["kernel_us"], 2)})
     return {"workload": "NF4 28672x8192, blocksize 64, double quant 256, bf16",
-            "kernel": "nf4_decode_kernel<bf16> (M=1), wq_prefill_kernel<bf16, NF4> (M=32)",
             "points": pts}
 
 

@@ -230,10 +230,14 @@ def _int4_gemm(x, x_scale, packed, out, workspace, use_workspace, stream):
     return out
 
 
-def w4a16_dequant(packed, dtype=torch.float16, stream=None):
+def w4a16_dequant(packed, dtype=torch.float16, stream=None, out=None):
     """Dequantized weights [N, K] (permuted column order) via the device routine."""
     K, N = packed["K"], packed["N"]
-    w = torch.empty((N, K), dtype=dtype, device=packed["codes"].device)
+    if out is None:
+        w = torch.empty((N, K), dtype=dtype, device=packed["codes"].device)
+    else:
+        _need(out, dtype, "out", N * K)
+        w = out
     bits = packed.get("bits", 4)
     arrays = (_ptr(packed["codes"]), _ptr(packed["scales"]), _ptr(packed["zeros"]), K, N,
               packed["group_size"])

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
 SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_b3.hip", "gemm_b8.hip", "prefill.hip",
-           "prefill_b3.hip", "prefill_b8.hip"]
+           "prefill_b3.hip", "prefill_b8.hip", "measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

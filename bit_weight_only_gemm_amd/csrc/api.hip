@@ -278,6 +278,19 @@ int w4a16_set_timing_events(void* start_event, void* stop_event) {
   return W4A16_OK;
 }
 
+int w4a16_stream_read(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* out,
+                      void* stream) {
+  return guarded([&]() -> int {
+    if (bytes <= 0 || bytes > ((int64_t)1 << 40) || workgroups <= 0 ||
+        workgroups > (1 << 20))
+      return W4A16_ERR_INVALID_ARG;
+    if (ceil_div(bytes, (int64_t)workgroups) > ((int64_t)1 << 30)) return W4A16_ERR_UNSUPPORTED;
+    if (int s = check_ptrs({buf, out})) return s;
+    clear_pending_error();
+    return hip_status(launch_stream_read(buf, bytes, workgroups, out, (hipStream_t)stream));
+  });
+}
+
 int w4a16_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t bits,
                     int32_t dtype, int32_t has_perm, int32_t has_x_scale, int32_t has_workspace,
                     char* names_host, int64_t names_bytes, int64_t* names_len_host) {

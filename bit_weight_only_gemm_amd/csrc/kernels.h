@@ -138,4 +138,9 @@ hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t*
                            int64_t N, int64_t K, int dtype, void* workspace,
                            int64_t workspace_bytes, hipStream_t stream);
 
+// A plain streaming read of `bytes` by `workgroups` workgroups of 256 lanes
+// (the practical HBM read ceiling); out: uint32 [workgroups * 256].
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int workgroups, uint32_t* out,
+                              hipStream_t stream);
+
 }  // namespace w4a16

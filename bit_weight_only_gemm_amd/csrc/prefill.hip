@@ -40,34 +40,36 @@ namespace w4a16 {
 // Rows per workgroup for M, and the split of K that fills the GPU best: a
 // simple model of the call time (rounds of workgroups on 256 CUs x K tiles per
 // workgroup x per-tile MFMA time, plus the partials' round trip through HBM).
+// Whole row blocks and a partial last one are separate launches (the partial
+// one puts its row in the per-lane offset), so they count as separate rounds.
 //
 // For M > 128, when 256-row tiles need no split of K, 192-row tiles are taken
 // instead if they finish in fewer tile-times: a 192-row workgroup takes about
 // 0.83 of a 256-row one per K tile (measured on MI355X), and the smaller tile
-// fills a round that 256-row tiles leave partly idle -- e.g. 220 instead of
-// 160 workgroups on a 5120-column layer at M = 2048 (17 % faster there).
+// can fill a round that 256-row tiles leave partly idle.
 PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, bool split_ok) {
   PrefillPlan pl;
   pl.bm = M <= 32 ? 32 : M <= 64 ? 64 : (M <= 128 ? 128 : 256);
   const int64_t cols = ceil_div(ceil_div(N, 64), (int64_t)PF_WAVES);
-  const int64_t tiles = cols * ceil_div(M, (int64_t)pl.bm);
   const int64_t KT = K / 128;
+  auto rounds = [&](int64_t bm, int64_t S) {
+    const int64_t full = M / bm;
+    return (double)(ceil_div(full * cols * S, (int64_t)256) +
+                    (M % bm ? ceil_div(cols * S, (int64_t)256) : 0));
+  };
   const double t_tile = 3.4e-6 * pl.bm / 256.0;  // one K tile of a workgroup
   double best = 0;
   pl.splits = 1;
   for (int S = 1; S <= (split_ok ? 16 : 1) && S <= KT; ++S) {
-    double t = (double)ceil_div(tiles * S, (int64_t)256) * (double)ceil_div(KT, (int64_t)S) * t_tile;
+    double t = rounds(pl.bm, S) * (double)ceil_div(KT, (int64_t)S) * t_tile;
     if (S > 1) t += (double)(S * 4 + 2) * M * N / 4.0e12 + 2e-6;
     if (S == 1 || t < best * 0.97) {
       best = t;
       pl.splits = S;
     }
   }
-  if (pl.bm == 256 && pl.splits == 1) {
-    const double r256 = (double)ceil_div(tiles, (int64_t)256);
-    const double r192 = (double)ceil_div(cols * ceil_div(M, (int64_t)192), (int64_t)256);
-    if (r192 * 0.83 < r256 * 0.95) pl.bm = 192;
-  }
+  if (pl.bm == 256 && pl.splits == 1 && rounds(192, 1) * 0.83 < rounds(256, 1) * 0.95)
+    pl.bm = 192;
   return pl;
 }
 

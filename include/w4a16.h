@@ -88,6 +88,22 @@ int w4a16_version(void);
  */
 int w4a16_set_timing_events(void* start_event, void* stop_event);
 
+/*
+ * Measurement export (not part of the GEMM): a plain streaming read of
+ * `bytes` bytes of device memory by `workgroups` workgroups of 256 lanes,
+ * 16-byte loads, eight in flight per lane; each workgroup reads one
+ * contiguous chunk.  Its time is the practical HBM read ceiling for a weight
+ * stream of that size, against which the decode calls are reported ([P5]
+ * "关键数据解读" item 3: decode time follows the weight bytes moved).
+ *   buf   device, bytes readable (16-byte aligned).
+ *   out   uint32 [workgroups * 256] device, written (each lane's xor of what
+ *         it read).
+ * Constraints: 0 < bytes <= 2^40, 0 < workgroups <= 2^20, at most 2^30 bytes
+ * per workgroup.  Async; honours w4a16_set_timing_events.
+ */
+int w4a16_stream_read(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* out,
+                      void* stream);
+
 /* ------------------------------------------------------------------ INT4 --- */
 
 /*

@@ -167,9 +167,12 @@ def test_plan_names_the_dispatch_without_gpu():
     assert _plan(4, 55296, 5120) == ["w4a16::intb_decode_wide_kernel<0, 1, 4, 2, 8>"]
     assert _plan(1, 4096, 4096, bits=8, dtype=1) == [dec + "1, 1, 0, 1, false, 8, false>"]
     assert _plan(1, 4096, 4096, G=32) == [dec + "0, 1, 0, 4, false, 4, true>"]
-    # prefill: whole 192-row blocks plus a tail launch
-    assert _plan(2048, 5120, 5120, dtype=1) == ["w4a16::wq_prefill_kernel<1, 192, false, 0, 1, 4>",
-                                                "w4a16::wq_prefill_kernel<1, 192, true, 0, 1, 4>"]
+    # prefill: whole row blocks, and a separate launch for a partial last one
+    # (which the planner counts as a round of its own)
+    assert _plan(2048, 5120, 5120, dtype=1) == ["w4a16::wq_prefill_kernel<1, 256, false, 0, 1, 4>"]
+    assert _plan(2100, 5120, 55296, dtype=1)[:2] == [
+        "w4a16::wq_prefill_kernel<1, 256, false, 0, 1, 4>",
+        "w4a16::wq_prefill_kernel<1, 256, true, 0, 1, 4>"]
     # the plan's pass agrees with w4a16_workspace_bytes
     for M, N, K in [(1, 4096, 4096), (4, 11008, 4096), (16, 4096, 4096), (5, 55296, 5120)]:
         has_pass = "w4a16::prep_x_kernel<0>" in _plan(M, N, K, perm=1)
