@@ -230,6 +230,31 @@ def _int4_gemm(x, x_scale, packed, out, workspace, use_workspace, stream):
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def w4a16_gemm_noalloc(x, packed, x_scale=None, out=None, stream=None):
+    """y = (x [/ s]) @ dequant(W)^T through the entry point that allocates
+    nothing (the library's fixed per-GPU scratch instead of a workspace);
+    ``out`` may be given to avoid the output allocation here too."""
+    if x.dtype not in _DT:
+        raise TypeError("x must be float16 or bfloat16")
+    _need(x, x.dtype, "x")
+    K, N, G = packed["K"], packed["N"], packed["group_size"]
+    M = x.numel() // K
+    if x_scale is not None:
+        _need(x_scale, x.dtype, "x_scale", K)
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    else:
+        _need(out, x.dtype, "out", M * N)
+    _lib.check(_lib.lib().w4a16_gemm_noalloc(
+        _ptr(x), _ptr(x_scale), _ptr(packed["codes"]), _ptr(packed["scales"]),
+        _ptr(packed["zeros"]), _ptr(packed["perm"]), G, packed.get("bits", 4), _ptr(out), M, N,
+        K, _DT[x.dtype], _stream(stream)), "w4a16_gemm_noalloc")
+    return out
+
+
 def w4a16_dequant(packed, dtype=torch.float16, stream=None, out=None):
     """Dequantized weights [N, K] (permuted column order) via the device routine."""
     K, N = packed["K"], packed["N"]

@@ -43,6 +43,8 @@ SIGNATURES = {
                                    _i64, _p]),
     "nf4_gemm_plan": (_c.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p]),
     "w4a16_stream_read": (_c.c_int, [_p, _i64, _i32, _p, _p]),
+    "w4a16_gemm_noalloc": (_c.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _i64, _i64, _i64,
+                                      _i32, _p]),
 }
 
 _lib = None

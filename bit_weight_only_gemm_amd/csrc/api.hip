@@ -17,6 +17,8 @@
 
 using namespace w4a16;
 
+static_assert(kScratchBytes == W4A16_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+
 namespace {
 
 constexpr int64_t kMaxM = (int64_t)1 << 21;  // keeps every row-block grid dimension < 65536
@@ -333,6 +335,31 @@ int w4a16_gemm_bits(const void* x, const void* x_scale, const void* codes_r,
     return hip_status(launch_int_gemm(x, x_scale, codes_r, scales_r, zeros_r, perm, out, M, N,
                                       K, (int)resolve_group(K, group_size), bits, dtype,
                                       workspace, workspace_bytes, (hipStream_t)stream));
+  });
+}
+
+int w4a16_gemm_noalloc(const void* x, const void* x_scale, const void* codes_r,
+                       const void* scales_r, const void* zeros_r, const int32_t* perm,
+                       int32_t group_size, int32_t bits, void* out, int64_t M, int64_t N,
+                       int64_t K, int32_t dtype, void* stream) {
+  return guarded([&]() -> int {
+    if (M <= 0) return W4A16_ERR_INVALID_ARG;
+    if (int s = validate_int4_shape(K, N, group_size)) return s;
+    if (too_big_m(M, N, K)) return W4A16_ERR_UNSUPPORTED;
+    if (int s = validate_bits(bits)) return s;
+    if (int s = validate_dtype(dtype)) return s;
+    if (int s = check_ptrs({x, codes_r, scales_r, out})) return s;
+    if (zeros_r && !aligned16(zeros_r)) return W4A16_ERR_MISALIGNED;
+    if (x_scale && !aligned16(x_scale)) return W4A16_ERR_MISALIGNED;
+    if (perm && !aligned16(perm)) return W4A16_ERR_MISALIGNED;
+    const int64_t need = int4_workspace_bytes(M, N, K, perm != nullptr, x_scale != nullptr);
+    if (need > kScratchBytes) return W4A16_ERR_WORKSPACE;
+    clear_pending_error();
+    void* ws = nullptr;
+    if (int s = hip_status(scratch_address(&ws))) return s;
+    return hip_status(launch_int_gemm(x, x_scale, codes_r, scales_r, zeros_r, perm, out, M, N,
+                                      K, (int)resolve_group(K, group_size), bits, dtype, ws,
+                                      kScratchBytes, (hipStream_t)stream));
   });
 }
 

@@ -57,6 +57,7 @@
 //    scales and zeros per run; a symmetric weight reads no zeros at all.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "decode.h"
 
@@ -269,6 +270,37 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
     else launch_intb_decode<8>(dtype, pl.xs, pl.am, pl.mt, G, a);
   }
   return hipGetLastError();
+}
+
+// ---- the fixed scratch of w4a16_gemm_noalloc: a file-scope device array,
+// allocated once per GPU when the library's code object is loaded there and
+// held until the process ends.  Host code never uses the array's name as an
+// address (in host code it is a host-side stand-in): the device address is
+// taken once per GPU with hipGetSymbolAddress, with that GPU current, and
+// kept.  Every call on one GPU shares its copy; each call writes every
+// scratch byte it later reads (the prepared activations, the split-K
+// partials), so nothing needs clearing between calls, but calls that overlap
+// in time on one GPU (different streams) race.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t scratch_address(void** ptr) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 template <int DT, int MT, int AM, bool BATCH>

@@ -89,6 +89,11 @@ GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws);
 // returns the full length.
 int64_t plan_names(const GemmPlan& p, char* out, int64_t n);
 
+// Bytes of the fixed device scratch that w4a16_gemm_noalloc uses in place of
+// a workspace, and its device address on the current GPU (taken once per GPU).
+constexpr int64_t kScratchBytes = (int64_t)32 << 20;
+hipError_t scratch_address(void** ptr);
+
 // xsc: AWQ input scales s [K] (activation dtype) or nullptr; bits: 3, 4 or 8.
 hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
                            const void* scales_r, const void* zeros_r, const int32_t* perm,

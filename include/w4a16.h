@@ -270,6 +270,31 @@ int w4a16_gemm(const void* x, const void* codes_r, const void* scales_r, const v
                void* stream);
 
 /*
+ * w4a16_gemm_bits without any allocation or workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the call runs exactly as
+ * w4a16_gemm_bits with a workspace -- the same kernels, bitwise the same
+ * output -- but the workspace is a fixed scratch array of
+ * W4A16_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ * each GPU from the first such call until the process ends.  The library
+ * calls no hipMalloc, hipFree or allocating routine here.
+ *   Arguments: as w4a16_gemm_bits (x_scale NULL: no input scales; bits 3, 4
+ *   or 8), on the current GPU's stream.
+ *   Calls whose workspace need (w4a16_workspace_bytes) exceeds the scratch
+ *   return W4A16_ERR_WORKSPACE (nothing launched); w4a16_gemm_bits with
+ *   workspace = NULL also allocates nothing and has no size limit.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in
+ * time on one GPU (different streams, or threads) race and must be ordered
+ * by the caller.  Each call writes every scratch byte it reads, so no
+ * clearing is needed between calls.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES ((int64_t)32 << 20)
+int w4a16_gemm_noalloc(const void* x, const void* x_scale, const void* codes_r,
+                       const void* scales_r, const void* zeros_r, const int32_t* perm,
+                       int32_t group_size, int32_t bits, void* out, int64_t M, int64_t N,
+                       int64_t K, int32_t dtype, void* stream);
+
+/*
  * w4a16_gemm with AWQ input scales ([P3] §4.1: the weights of salient input
  * channels are scaled up by s_k before quantization and the activations
  * divided by s_k; here the division is applied by the GEMM, so callers pass
