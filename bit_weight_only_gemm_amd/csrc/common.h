@@ -69,11 +69,21 @@ template <> struct QParam<DT_F16> {
   half2_t hz;  // (1024 + z) in both halves
   half2_t s2;  // s in both halves
   uint32_t magic;  // 0x64006400 in a register, so the nibble insert is one v_and_or_b32
+  // 4-bit words (HI4): the codes of the odd element pairs are inserted at
+  // bits 4-7 of 0x5400, which is 64 + q exactly (see dequant_word4_f16)
+  half2_t hz_hi;      // (64 + z) in both halves
+  uint32_t magic_hi;  // 0x54005400 in a register
+  template <bool HI4 = false>
   __device__ __forceinline__ void set(uint32_t scale_bits, uint32_t z) {
     magic = opaque_magic();
     uint32_t hzb = 0x6400u | z;
     hz = __builtin_bit_cast(half2_t, hzb | (hzb << 16));
     s2 = __builtin_bit_cast(half2_t, scale_bits | (scale_bits << 16));
+    if constexpr (HI4) {
+      asm("v_mov_b32 %0, 0x54005400" : "=v"(magic_hi));
+      const uint32_t h = 0x5400u | (z << 4);
+      hz_hi = __builtin_bit_cast(half2_t, h | (h << 16));
+    }
   }
 };
 template <> struct QParam<DT_BF16> {
@@ -82,6 +92,7 @@ template <> struct QParam<DT_BF16> {
   float nz;    // -0.0, opaque to the compiler so that the fma below stays an fma
   float nc;    // -(1024 + z) s, exact in fp32 (an 11-bit integer times an 11-bit significand)
   uint32_t magic;  // 0x64006400 in a register, so the nibble insert is one v_and_or_b32
+  template <bool HI4 = false>
   __device__ __forceinline__ void set(uint32_t scale_bits, uint32_t z) {
     magic = opaque_magic();
     uint32_t hzb = 0x6400u | z;
@@ -154,20 +165,56 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, int i, const QP& p)
 // T - Z is exactly 0 and the output is exactly 0, as with the per-weight
 // dequant (q - z) s = 0.
 template <int DT> struct RawQ {
-  uint32_t magic;  // in a register, so the insert is one v_and_or_b32
+  uint32_t magic;     // in a register, so the insert is one v_and_or_b32
+  uint32_t magic_hi;  // fp16 4-bit words: 0x54005400 (odd element pairs, 64 + q)
   __device__ __forceinline__ RawQ() {
     magic = DT == DT_F16 ? 0x64006400u : 0x43004300u;
+    magic_hi = 0x54005400u;
     asm("" : "+v"(magic));
+    if constexpr (DT == DT_F16) asm("" : "+v"(magic_hi));
   }
-  // o + z in every element of an MFMA operand (z < 1024 in fp16, < 128 in bf16)
+  // The zero operand: o + z in every element of an MFMA operand, with o the
+  // offset of each element's code form (z < 1024 in fp16, < 128 in bf16; for
+  // 4-bit codes in fp16 the odd element pairs carry 64 + z, as their codes
+  // carry 64 + q).
+  template <int BITS>
   __device__ __forceinline__ typename Op<DT>::vec zero_operand(uint32_t z) const {
     const uint32_t v = magic | (z * 0x00010001u);
-    return __builtin_bit_cast(typename Op<DT>::vec, u32x4_t{v, v, v, v});
+    if constexpr (DT == DT_F16 && BITS == 4) {
+      const uint32_t h = magic_hi | (z * 0x00100010u);
+      return __builtin_bit_cast(typename Op<DT>::vec, u32x4_t{v, h, v, h});
+    } else {
+      return __builtin_bit_cast(typename Op<DT>::vec, u32x4_t{v, v, v, v});
+    }
   }
 };
 template <bool ZS = true, int DT>
 __device__ __forceinline__ uint32_t dequant_fields(uint32_t f, const RawQ<DT>& p) {
   return f | p.magic;
+}
+
+// One repacked 4-bit word into an fp16 MFMA operand with a single shift.  The
+// pairs (0, 1) and (4, 5) have their codes at bits 0-3 / 16-19 of w and of
+// w >> 8, the pairs (2, 3) and (6, 7) at bits 4-7 / 20-23: 0x6400 | q is the
+// fp16 value 1024 + q, and 0x5400 | (q << 4) is 64 + q exactly (the fp16 ulp
+// at 64 is 1/16), so every code is inserted where it lies.  With a QParam the
+// dequant then subtracts 1024 + z or 64 + z (exact) and multiplies by s (one
+// rounding): the same value as the routine above.  With a RawQ the operand
+// holds the codes alone, o + q with o = 1024 or 64 by element, and the zero
+// operand carries the same offsets.
+__device__ __forceinline__ uint32_t f16_hi_fields(uint32_t f, const QParam<DT_F16>& p) {
+  const half2_t r = (__builtin_bit_cast(half2_t, f | p.magic_hi) - p.hz_hi) * p.s2;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t f16_hi_fields(uint32_t f, const RawQ<DT_F16>& p) {
+  return f | p.magic_hi;
+}
+template <bool ZS, class QP>
+__device__ __forceinline__ half8_t dequant_word4_f16(uint32_t w, const QP& p) {
+  const uint32_t t = w >> 8;
+  const u32x4_t r = {dequant_fields<ZS>(w & 0x000F000Fu, p), f16_hi_fields(w & 0x00F000F0u, p),
+                     dequant_fields<ZS>(t & 0x000F000Fu, p), f16_hi_fields(t & 0x00F000F0u, p)};
+  return __builtin_bit_cast(half8_t, r);
 }
 
 // Exact dequantization of one repacked 4-bit word into an 8-element MFMA operand
@@ -236,7 +283,8 @@ __host__ __device__ constexpr uint32_t sym_zero_xor(int bits) {
 template <int DT, bool ZS = true, class QP>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<4>& c, int j,
                                                              const QP& p) {
-  return dequant_word<DT, ZS>(c.w[j], p);
+  if constexpr (DT == DT_F16) return dequant_word4_f16<ZS>(c.w[j], p);
+  else return dequant_word<DT, ZS>(c.w[j], p);
 }
 template <int DT, bool ZS = true, class QP>
 __device__ __forceinline__ typename Op<DT>::vec dequant_step(const Codes<8>& c, int j,

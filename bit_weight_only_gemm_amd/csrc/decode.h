@@ -172,8 +172,8 @@ struct IntW {
   }
   __device__ static __forceinline__ void unit_param(const Meta& m, int r, QParam<DT>& qp) {
     constexpr int per = 32 / kZW;  // fields per dword
-    qp.set((m.s[r >> 3][(r & 7) >> 1] >> (16 * (r & 1))) & 0xFFFFu,
-           (m.z[r / per] >> (kZW * (r % per))) & ((1u << kZW) - 1u));
+    qp.template set<BITS == 4>((m.s[r >> 3][(r & 7) >> 1] >> (16 * (r & 1))) & 0xFFFFu,
+                               (m.z[r / per] >> (kZW * (r % per))) & ((1u << kZW) - 1u));
   }
   // B operands of tile slot s (0..7 within the run) from the exact dequant.
   __device__ __forceinline__ void operands(const CodeT& w, int s, const Meta& m,
@@ -216,7 +216,7 @@ struct IntW {
                                                        typename Op<DT>::vec (&bz)[U]) {
     const RawQ<DT> rq;
 #pragma unroll
-    for (int u = 0; u < U; ++u) bz[u] = rq.zero_operand(unit_zero(m, s * U + u));
+    for (int u = 0; u < U; ++u) bz[u] = rq.template zero_operand<BITS>(unit_zero(m, s * U + u));
   }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * j + 8 * b; }
 };

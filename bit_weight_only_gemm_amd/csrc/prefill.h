@@ -260,7 +260,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
     if constexpr (FOLD) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
-        bz[g] = rq.zero_operand(((zzc[g] ^ zx) >> (kZW * zb)) & ((1u << kZW) - 1u));
+        bz[g] = rq.template zero_operand<BITS>(((zzc[g] ^ zx) >> (kZW * zb)) & ((1u << kZW) - 1u));
     }
     // B operand of step s for column group g: word j = s >> 1 of the tile, in
     // meta unit j U / 4.  The unit's dequant parameters are formed at the step
@@ -272,8 +272,8 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       } else if constexpr (FMT == FMT_INT4) {
         const int u = (s >> 1) * U / 4;
         QParam<DT> q;
-        q.set((scc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
-              ((zzc[g] ^ zx) >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
+        q.template set<BITS == 4>((scc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
+                                  ((zzc[g] ^ zx) >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
         return dequant_step<DT, false>(cwc[g][s & 1], s >> 1, q);
       } else {
         return nf4_operand<DT>(cwc[g][s >> 2].w[s & 3], lut, ap[g]);

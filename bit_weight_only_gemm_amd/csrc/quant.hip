@@ -344,7 +344,7 @@ dequant_int_kernel(const uint8_t* __restrict__ codes_r, const uint16_t* __restri
                                    ((1u << kZW) - 1u)
                              : (1u << (BITS - 1));
   QParam<DT> qp;
-  qp.set(scales_r[meta * 8 * U + r], z);
+  qp.template set<BITS == 4>(scales_r[meta * 8 * U + r], z);
   const auto v = dequant_step<DT>(w, j, qp);
   const int64_t k = t * 128 + j * 32 + (lane >> 4) * 8;
   *(u32x4_t*)(w_out + n * K + k) = __builtin_bit_cast(u32x4_t, v);
