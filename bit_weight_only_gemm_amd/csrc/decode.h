@@ -41,6 +41,9 @@ constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; 
 // 10.8 us per call), and with the reduction buffer it leaves room for two
 // workgroups in a CU's 160 KB.
 constexpr int64_t kMaxXlds = 72 * 1024;
+// On a grid of at most 256 workgroups (one per CU anyway) a workgroup may take
+// up to this much LDS for its staged rows, permutation and permuted rows.
+constexpr int64_t kMaxXldsOne = 144 * 1024;
 
 // Multiply-accumulate the 4 MFMA steps of one K tile given its 4 B operands.
 template <int DT, int AM, int MT, int NA, int NACC>
@@ -322,7 +325,8 @@ struct Nf4W {
 // descriptor range; k >= K (only in a half NF4 tile) uses an out-of-range
 // offset.
 // Staged activations in LDS: x rows [M][K] at xl, the permutation int32[K] at
-// pl.  GGATHER: the permutation (when perm) and the input scales in global
+// pl, the permuted rows at xp (XGATHER; chunk c of row m at c * xstride +
+// 16 m).  GGATHER: the permutation (when perm) and the input scales in global
 // memory, behind the descriptors rp and rs.
 struct XLds {
   const uint8_t* xl;
@@ -330,6 +334,8 @@ struct XLds {
   int M;
   rsrc_t rp, rs;
   bool perm;
+  const uint8_t* xp;
+  uint32_t xstride;
 };
 
 template <int DT, int AM, int MT, int NA, class WP, bool XS = false>
@@ -338,24 +344,12 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
   typedef typename Op<DT>::vec vec;
   const int r = lane & 15, b = lane >> 4;
   if constexpr (AM == AM_XGATHER) {
-    // rows m >= M only feed output rows that are never stored, so they read
-    // row M - 1 instead of zeros (K % 128 == 0: no half tiles)
+    // the rows permuted in LDS (see permute_staged); rows m >= M only feed
+    // output rows that are never stored, so they read row M - 1 instead of
+    // zeros (K % 128 == 0: no half tiles)
     const int j = r >> 2, m = min(r & 3, xs.M - 1);
-    const int kg = t * 128 + WP::xk(j, b);
-    {
-      const u32x4_t p0 = *(const u32x4_t*)(xs.pl + kg);
-      const u32x4_t p1 = *(const u32x4_t*)(xs.pl + kg + 4);
-      const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
-      uint32_t v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = *(const uint16_t*)(row + p0[e] * 2u);
-        v[4 + e] = *(const uint16_t*)(row + p1[e] * 2u);
-      }
-      const u32x4_t w = {v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                         v[6] | (v[7] << 16)};
-      a[0] = __builtin_bit_cast(vec, w);
-    }
+    const uint32_t c = (uint32_t)(t * 128 + WP::xk(j, b)) >> 3;
+    a[0] = *(const vec*)(xs.xp + c * xs.xstride + (uint32_t)m * 16u);
   } else if constexpr (AM == AM_GGATHER) {
     // one row tile: lane row r, 8 inputs of step j per operand; rows past M
     // read 0 through the descriptor range of rx, as does any input of a
@@ -465,16 +459,30 @@ __host__ __device__ constexpr uint32_t xpose_bytes(int MT) { return (uint32_t)(D
 // Bytes of LDS the staged activations and permutation take, each region
 // rounded up to whole 1 KB blocks.
 // Staged LDS layout: x rows [M][K], then (gather) the permutation int32[K],
-// then (input scales) s [K].
+// then (input scales) s [K], then (gather, 3-4 rows) the permuted rows.
+// XGATHER permutes the staged rows once per workgroup: chunk c (permuted
+// columns 8c .. 8c + 7) of row m goes to 16 bytes at c * stride + 16 m, over
+// the permutation's own chunk c (32 bytes) for 1-2 rows, else in a region of
+// 64 bytes per chunk.
 __host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
   return (uint32_t)((M * K * 2 + 1023) / 1024 * 1024);
 }
 __host__ __device__ constexpr uint32_t xlds_perm_bytes(int K, bool perm) {
   return perm ? (uint32_t)((K * 4 + 1023) / 1024 * 1024) : 0u;
 }
+__host__ __device__ constexpr uint32_t xlds_s_bytes(int K, bool xs) {
+  return xs ? (uint32_t)((K * 2 + 1023) / 1024 * 1024) : 0u;
+}
+__host__ __device__ constexpr uint32_t xlds_xp_bytes(int M, int K, bool perm) {
+  return (perm && M > 2) ? (uint32_t)((K * 8 + 1023) / 1024 * 1024) : 0u;
+}
+// what is copied from memory into each workgroup's LDS
+__host__ __device__ constexpr uint32_t xlds_staged_bytes(int M, int K, bool perm, bool xs) {
+  return xlds_x_bytes(M, K) + xlds_perm_bytes(K, perm) + xlds_s_bytes(K, xs);
+}
+// the LDS footprint
 __host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool perm, bool xs) {
-  return xlds_x_bytes(M, K) + xlds_perm_bytes(K, perm) +
-         (xs ? (uint32_t)((K * 2 + 1023) / 1024 * 1024) : 0u);
+  return xlds_staged_bytes(M, K, perm, xs) + xlds_xp_bytes(M, K, perm);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
@@ -492,6 +500,33 @@ __device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8
   const int nblk = (int)((bytes + 1023) / 1024);
   for (int blk = wave; blk < nblk; blk += DW)
     lds_dma16(r, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), 0);
+}
+
+// XGATHER: the staged rows permuted once per workgroup, x_p[m][k] =
+// x[m][perm[k]], into the layout the loop reads (chunk c = permuted columns
+// 8c .. 8c + 7 of row m at xp + c * xstride + 16 m): each thread takes whole
+// chunks, reads the chunk's 8 permutation entries, gathers them from each
+// staged row and writes the chunk.  For 1-2 rows the chunk is written over
+// the permutation's own chunk (32 bytes), which only this thread reads.
+__device__ __forceinline__ void permute_staged(const XLds& xs, int K) {
+  const int nch = K >> 3;
+  uint8_t* xp = const_cast<uint8_t*>(xs.xp);
+  for (int c = threadIdx.x; c < nch; c += 64 * DW) {
+    const u32x4_t p0 = *(const u32x4_t*)(xs.pl + 8 * c);
+    const u32x4_t p1 = *(const u32x4_t*)(xs.pl + 8 * c + 4);
+    for (int m = 0; m < xs.M; ++m) {
+      const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = *(const uint16_t*)(row + p0[e] * 2u);
+        v[4 + e] = *(const uint16_t*)(row + p1[e] * 2u);
+      }
+      *(u32x4_t*)(xp + (uint32_t)c * xs.xstride + (uint32_t)m * 16u) =
+          u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                  v[6] | (v[7] << 16)};
+    }
+  }
 }
 
 // XS: divide the staged activations by the AWQ input scales xsc [K] (staged
@@ -566,7 +601,11 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   typename Op<DT>::vec ra[PA][NA];
   typename WP::Meta mc, mn = WP::zero_meta();
   XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), M, make_rsrc(perm, 0u),
-          make_rsrc(xsc, 0u), perm != nullptr};
+          make_rsrc(xsc, 0u), perm != nullptr, nullptr, 0u};
+  if constexpr (AM == AM_XGATHER) {
+    xs.xp = M <= 2 ? (const uint8_t*)xs.pl : xlds + xlds_staged_bytes(M, K, true, XS);
+    xs.xstride = M <= 2 ? 32u : 64u;
+  }
   if constexpr (AM == AM_GGATHER) {
     xs.rp = make_rsrc(perm, perm ? (uint32_t)K * 4u : 0u);
     xs.rs = make_rsrc(xsc, XS ? (uint32_t)K * 2u : 0u);
@@ -600,6 +639,10 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
                               ((uint32_t)mul_round16<DT>((uint16_t)(v >> 16), r1) << 16);
         }
       }
+      __syncthreads();
+    }
+    if constexpr (AM == AM_XGATHER) {
+      permute_staged(xs, K);
       __syncthreads();
     }
   }
@@ -906,14 +949,24 @@ nf4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
 
 // ---------------------------------------------------------------- planning --
 
-// Raise a kernel's dynamic LDS limit to kMaxXlds (once per kernel; the call
-// is idempotent, so a race between host threads is harmless).
+// Raise a kernel's dynamic LDS limit to what a CU holds beside the kernel's
+// static LDS, at most kMaxXldsOne (once per kernel; the call is idempotent,
+// so a race between host threads is harmless).  A refusal is consumed here
+// so it cannot be reported by a later launch: a launch that then asks for
+// more than the old limit fails on its own.
 static void allow_dynamic_lds(const void* kernel) {
+  constexpr int kLdsPerCu = 160 * 1024;
   static thread_local const void* done[32];
   static thread_local int ndone = 0;
   for (int i = 0; i < ndone; ++i)
     if (done[i] == kernel) return;
-  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxXlds);
+  hipFuncAttributes fa{};
+  int limit = (int)kMaxXlds;
+  if (hipFuncGetAttributes(&fa, kernel) == hipSuccess)
+    limit = (int)std::min<int64_t>(kMaxXldsOne, kLdsPerCu - (int64_t)fa.sharedSizeBytes);
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, limit) !=
+      hipSuccess)
+    (void)hipGetLastError();
   if (ndone < 32) done[ndone++] = kernel;
 }
 
@@ -940,8 +993,11 @@ constexpr int64_t kMaxStagedTotal = (int64_t)17 << 20;
 static int pick_mode(int64_t M, int64_t N, int64_t K, bool gather, bool xs, int* mt) {
   if (M <= 4) {
     *mt = 1;
-    const int64_t b = xlds_bytes((int)M, (int)K, gather, xs);
-    if ((gather || xs) && b <= kMaxXlds && ceil_div(N, 16) * b <= kMaxStagedTotal)
+    const int64_t wgs = ceil_div(N, 16);
+    const int64_t lds = xlds_bytes((int)M, (int)K, gather, xs);
+    const int64_t staged = xlds_staged_bytes((int)M, (int)K, gather, xs);
+    if ((gather || xs) && lds <= (wgs <= 256 ? kMaxXldsOne : kMaxXlds) &&
+        wgs * staged <= kMaxStagedTotal)
       return gather ? AM_XGATHER : AM_XSTAGED;
     return AM_PACKED;
   }
