@@ -324,13 +324,12 @@ struct Nf4W {
 // puts into the MFMA layout through LDS.  Rows >= M read 0 through the
 // descriptor range; k >= K (only in a half NF4 tile) uses an out-of-range
 // offset.
-// Staged activations in LDS: x rows [M][K] at xl, the permutation int32[K] at
-// pl, the permuted rows at xp (XGATHER; chunk c of row m at c * xstride +
-// 16 m).  GGATHER: the permutation (when perm) and the input scales in global
-// memory, behind the descriptors rp and rs.
+// Staged activations in LDS: x rows [M][K] at xl, the permuted rows at xp
+// (XGATHER; chunk c of row m at c * xstride + 16 m, xstride = 16 M).
+// GGATHER: the permutation (when perm) and the input scales in global memory,
+// behind the descriptors rp and rs.
 struct XLds {
   const uint8_t* xl;
-  const int32_t* pl;
   int M;
   rsrc_t rp, rs;
   bool perm;
@@ -456,33 +455,31 @@ constexpr bool full_fold() {
 // LDS bytes of the FULLT mode's transpose: 4 KB per row tile and wave.
 __host__ __device__ constexpr uint32_t xpose_bytes(int MT) { return (uint32_t)(DW * MT * 4096); }
 
-// Bytes of LDS the staged activations and permutation take, each region
-// rounded up to whole 1 KB blocks.
-// Staged LDS layout: x rows [M][K], then (gather) the permutation int32[K],
-// then (input scales) s [K], then (gather, 3-4 rows) the permuted rows.
-// XGATHER permutes the staged rows once per workgroup: chunk c (permuted
-// columns 8c .. 8c + 7) of row m goes to 16 bytes at c * stride + 16 m, over
-// the permutation's own chunk c (32 bytes) for 1-2 rows, else in a region of
-// 64 bytes per chunk.
+// Staged LDS layout, each region rounded up to whole 1 KB blocks: x rows
+// [M][K], then (input scales) s [K], then (gather) the permuted rows.  XGATHER
+// permutes the staged rows once per workgroup: chunk c (permuted columns
+// 8c .. 8c + 7) of row m goes to the 16 bytes at c * 16 M + 16 m.  The
+// permutation itself is read from memory into registers (kPermRegs chunks of
+// 8 entries per thread), so the gather takes K <= 64 DW 8 kPermRegs.
+constexpr int kPermRegs = 6;
+constexpr int64_t kMaxGatherK = (int64_t)64 * DW * 8 * kPermRegs;
 __host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
   return (uint32_t)((M * K * 2 + 1023) / 1024 * 1024);
-}
-__host__ __device__ constexpr uint32_t xlds_perm_bytes(int K, bool perm) {
-  return perm ? (uint32_t)((K * 4 + 1023) / 1024 * 1024) : 0u;
 }
 __host__ __device__ constexpr uint32_t xlds_s_bytes(int K, bool xs) {
   return xs ? (uint32_t)((K * 2 + 1023) / 1024 * 1024) : 0u;
 }
 __host__ __device__ constexpr uint32_t xlds_xp_bytes(int M, int K, bool perm) {
-  return (perm && M > 2) ? (uint32_t)((K * 8 + 1023) / 1024 * 1024) : 0u;
+  return perm ? xlds_x_bytes(M, K) : 0u;
 }
-// what is copied from memory into each workgroup's LDS
+// what each workgroup reads from memory besides the weights: the rows, the
+// permutation and the input scales
 __host__ __device__ constexpr uint32_t xlds_staged_bytes(int M, int K, bool perm, bool xs) {
-  return xlds_x_bytes(M, K) + xlds_perm_bytes(K, perm) + xlds_s_bytes(K, xs);
+  return (uint32_t)(M * K * 2) + (perm ? (uint32_t)(K * 4) : 0u) + (xs ? (uint32_t)(K * 2) : 0u);
 }
 // the LDS footprint
 __host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool perm, bool xs) {
-  return xlds_staged_bytes(M, K, perm, xs) + xlds_xp_bytes(M, K, perm);
+  return xlds_x_bytes(M, K) + xlds_s_bytes(K, xs) + xlds_xp_bytes(M, K, perm);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
@@ -502,31 +499,62 @@ __device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8
     lds_dma16(r, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), 0);
 }
 
+// XGATHER: the permutation chunks of this thread (chunk c = entries
+// 8c .. 8c + 7, c = thread + i 64 DW), loaded from memory before the rows
+// are staged; chunks past K read 0 and are not used.
+__device__ __forceinline__ void load_perm_chunks(const int32_t* perm, int K,
+                                                 u32x4_t (&pr)[kPermRegs][2]) {
+  const rsrc_t rp = make_rsrc(perm, (uint32_t)K * 4u);
+#pragma unroll
+  for (int i = 0; i < kPermRegs; ++i) {
+    const uint32_t c = threadIdx.x + (uint32_t)(i * 64 * DW);
+    pr[i][0] = bld128(rp, c * 32u, 0);
+    pr[i][1] = bld128(rp, c * 32u + 16u, 0);
+  }
+}
+
 // XGATHER: the staged rows permuted once per workgroup, x_p[m][k] =
-// x[m][perm[k]], into the layout the loop reads (chunk c = permuted columns
-// 8c .. 8c + 7 of row m at xp + c * xstride + 16 m): each thread takes whole
-// chunks, reads the chunk's 8 permutation entries, gathers them from each
-// staged row and writes the chunk.  For 1-2 rows the chunk is written over
-// the permutation's own chunk (32 bytes), which only this thread reads.
-__device__ __forceinline__ void permute_staged(const XLds& xs, int K) {
+// x[m][perm[k]], into the layout the loop reads: each thread gathers its
+// chunks of one row from LDS (all reads of the row before its writes), then
+// the next row.
+__device__ __forceinline__ void permute_staged(const XLds& xs, int K,
+                                               const u32x4_t (&pr)[kPermRegs][2]) {
   const int nch = K >> 3;
+  const int nit = (nch + 64 * DW - 1) / (64 * DW);  // passes over the workgroup's threads
   uint8_t* xp = const_cast<uint8_t*>(xs.xp);
-  for (int c = threadIdx.x; c < nch; c += 64 * DW) {
-    const u32x4_t p0 = *(const u32x4_t*)(xs.pl + 8 * c);
-    const u32x4_t p1 = *(const u32x4_t*)(xs.pl + 8 * c + 4);
-    for (int m = 0; m < xs.M; ++m) {
-      const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
+  for (int m = 0; m < xs.M; ++m) {
+    const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
+    // (the workgroup's last pass may hold chunks past K: entries 0, gathered
+    // from column 0 and never written)
+    u32x4_t w[kPermRegs];
+#pragma unroll
+    for (int i = 0; i < kPermRegs; ++i) {
+      if (i >= nit) break;  // workgroup-uniform
       uint32_t v[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v[e] = *(const uint16_t*)(row + p0[e] * 2u);
-        v[4 + e] = *(const uint16_t*)(row + p1[e] * 2u);
+        v[e] = *(const uint16_t*)(row + pr[i][0][e] * 2u);
+        v[4 + e] = *(const uint16_t*)(row + pr[i][1][e] * 2u);
       }
-      *(u32x4_t*)(xp + (uint32_t)c * xs.xstride + (uint32_t)m * 16u) =
-          u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                  v[6] | (v[7] << 16)};
+      w[i] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                     v[6] | (v[7] << 16)};
+    }
+#pragma unroll
+    for (int i = 0; i < kPermRegs; ++i) {
+      if (i >= nit) break;
+      const int c = threadIdx.x + i * 64 * DW;
+      if (c < nch) *(u32x4_t*)(xp + (uint32_t)c * xs.xstride + (uint32_t)m * 16u) = w[i];
     }
   }
+}
+
+// A workgroup barrier for LDS data: this wave's LDS writes (and LDS DMA) are
+// complete before it, other waves' are visible after it; loads from global
+// memory in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // XS: divide the staged activations by the AWQ input scales xsc [K] (staged
@@ -600,34 +628,40 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   typename WP::CodeT ring[RUN];
   typename Op<DT>::vec ra[PA][NA];
   typename WP::Meta mc, mn = WP::zero_meta();
-  XLds xs{xlds, (const int32_t*)(xlds + xlds_x_bytes(M, K)), M, make_rsrc(perm, 0u),
-          make_rsrc(xsc, 0u), perm != nullptr, nullptr, 0u};
+  XLds xs{xlds, M, make_rsrc(perm, 0u), make_rsrc(xsc, 0u), perm != nullptr, nullptr, 0u};
   if constexpr (AM == AM_XGATHER) {
-    xs.xp = M <= 2 ? (const uint8_t*)xs.pl : xlds + xlds_staged_bytes(M, K, true, XS);
-    xs.xstride = M <= 2 ? 32u : 64u;
+    xs.xp = xlds + xlds_x_bytes(M, K) + xlds_s_bytes(K, XS);
+    xs.xstride = 16u * (uint32_t)M;
   }
   if constexpr (AM == AM_GGATHER) {
     xs.rp = make_rsrc(perm, perm ? (uint32_t)K * 4u : 0u);
     xs.rs = make_rsrc(xsc, XS ? (uint32_t)K * 2u : 0u);
   }
-  if (n > 0) {
+  // Staged modes: the permutation chunks (into registers) and the LDS DMA of
+  // the rows (and input scales) go out before the first code tiles, so the
+  // staging barrier waits only for them while the tiles stay in flight.
+  u32x4_t pr[AM == AM_XGATHER ? kPermRegs : 1][2];
+  if constexpr (AM == AM_XGATHER) load_perm_chunks(perm, K, pr);
+  if constexpr (is_staged(AM)) {
+    stage_lds(x, (uint32_t)(M * K * 2), xlds, wave, lane);
+    if constexpr (XS) stage_lds(xsc, (uint32_t)(K * 2), xlds + xlds_x_bytes(M, K), wave, lane);
+  }
+  // (staged: unconditional, a wave without tiles reading its first tile, so
+  // that the staging barrier's wait counts the same loads on every path)
+  if constexpr (is_staged(AM)) __builtin_amdgcn_sched_barrier(0);
+  if (is_staged(AM) || n > 0) {
     mn = wp.load_meta(r0);
 #pragma unroll
-    for (int s = 0; s < RUN; ++s) ring[s] = wp.load_codes(t0 + min(s, n - 1), lane);
+    for (int s = 0; s < RUN; ++s) ring[s] = wp.load_codes(t0 + max(min(s, n - 1), 0), lane);
   }
+  if constexpr (is_staged(AM)) __builtin_amdgcn_sched_barrier(0);
   if constexpr (is_staged(AM)) {
-    // every wave takes part in staging the M rows of x (and the permutation,
-    // and the input scales) while its first code tiles are in flight
-    const uint32_t xb = xlds_x_bytes(M, K), pb = xlds_perm_bytes(K, AM == AM_XGATHER);
-    stage_lds(x, (uint32_t)(M * K * 2), xlds, wave, lane);
-    if constexpr (AM == AM_XGATHER) stage_lds(perm, (uint32_t)(K * 4), xlds + xb, wave, lane);
-    if constexpr (XS) stage_lds(xsc, (uint32_t)(K * 2), xlds + xb + pb, wave, lane);
-    __syncthreads();
+    lds_barrier();
     if constexpr (XS) {
       // x[m][k] / s[k] in place (original column order): a pair of columns per
       // step, their reciprocals shared by the M rows
       uint32_t* xw = (uint32_t*)xlds;
-      const uint32_t* sw = (const uint32_t*)(xlds + xb + pb);
+      const uint32_t* sw = (const uint32_t*)(xlds + xlds_x_bytes(M, K));
       const int half = K >> 1;
       for (int kp = threadIdx.x; kp < half; kp += 64 * DW) {
         const uint32_t sv = sw[kp];
@@ -639,11 +673,11 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
                               ((uint32_t)mul_round16<DT>((uint16_t)(v >> 16), r1) << 16);
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     if constexpr (AM == AM_XGATHER) {
-      permute_staged(xs, K);
-      __syncthreads();
+      permute_staged(xs, K, pr);
+      lds_barrier();
     }
   }
   if (n > 0) {
@@ -816,7 +850,7 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
-  const XLds none{nullptr, nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false};
+  const XLds none{nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, nullptr, 0u};
   const bool g0 = lane & 16, g1 = lane & 32;
 
   float4_t yf[NC];
@@ -997,7 +1031,7 @@ static int pick_mode(int64_t M, int64_t N, int64_t K, bool gather, bool xs, int*
     const int64_t lds = xlds_bytes((int)M, (int)K, gather, xs);
     const int64_t staged = xlds_staged_bytes((int)M, (int)K, gather, xs);
     if ((gather || xs) && lds <= (wgs <= 256 ? kMaxXldsOne : kMaxXlds) &&
-        wgs * staged <= kMaxStagedTotal)
+        wgs * staged <= kMaxStagedTotal && (!gather || K <= kMaxGatherK))
       return gather ? AM_XGATHER : AM_XSTAGED;
     return AM_PACKED;
   }
