@@ -28,9 +28,15 @@ constexpr int64_t kWideMinN = 16384;    // narrowest layer of the wide packed de
 // x[m][perm[k]] (and divided by s[perm[k]] with input scales): the form of
 // every call that has a permutation or input scales, no workspace for a
 // preparation pass and no room to stage its rows on chip; correct at any M,
-// not fast.
-enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3, AM_FULLT = 4, AM_GGATHER = 5 };
-constexpr bool is_full(int am) { return am == AM_FULL || am == AM_FULLT || am == AM_GGATHER; }
+// not fast.  TILED: FULL with the activations prepared by the preparation
+// pass in the operand layout itself (tile t, row tile R, step j, lane l: the
+// 16 bytes lane l feeds to MFMA step j of row tile R), so that each operand
+// is one 1 KB coalesced load per wave and no transpose runs.
+enum { AM_PACKED = 0, AM_FULL = 1, AM_XGATHER = 2, AM_XSTAGED = 3, AM_FULLT = 4, AM_GGATHER = 5,
+       AM_TILED = 6 };
+constexpr bool is_full(int am) {
+  return am == AM_FULL || am == AM_FULLT || am == AM_GGATHER || am == AM_TILED;
+}
 constexpr bool is_packed(int am) { return !is_full(am); }
 constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; }
 
@@ -327,7 +333,8 @@ struct Nf4W {
 // Staged activations in LDS: x rows [M][K] at xl, the permuted rows at xp
 // (XGATHER; chunk c of row m at c * xstride + 16 m, xstride = 16 M).
 // GGATHER: the permutation (when perm) and the input scales in global memory,
-// behind the descriptors rp and rs.
+// behind the descriptors rp and rs.  TILED: rt row tiles in the prepared
+// buffer, rt0 the workgroup's first.
 struct XLds {
   const uint8_t* xl;
   int M;
@@ -335,6 +342,7 @@ struct XLds {
   bool perm;
   const uint8_t* xp;
   uint32_t xstride;
+  int rt, rt0;
 };
 
 template <int DT, int AM, int MT, int NA, class WP, bool XS = false>
@@ -390,6 +398,16 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
     uint32_t off = (uint32_t)m * (uint32_t)K * 2u + (uint32_t)kin * 2u;
     if constexpr (WP::kRaggedK) off = (t * 128 + kin < K) ? off : kOutOfRange;
     a[0] = __builtin_bit_cast(typename Op<DT>::vec, bld128(rx, off, t * 256));
+  } else if constexpr (AM == AM_TILED) {
+    // rx covers the whole prepared buffer (row tiles past it read 0)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a[m * 4 + j] = __builtin_bit_cast(
+            typename Op<DT>::vec,
+            bld128(rx, (uint32_t)(j * 1024 + lane * 16), (t * xs.rt + xs.rt0 + m) * 4096));
+    }
   } else if constexpr (AM == AM_FULLT) {
     const int c = lane & 15;
 #pragma unroll
@@ -585,7 +603,10 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   const int t0 = r0 * RUN;
   const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
   const int vrows = min(16 * MT, M - row0);
-  const rsrc_t rx = make_rsrc(x + (size_t)row0 * K, (uint32_t)vrows * (uint32_t)K * 2u);
+  const int rtiles = (M + 15) >> 4;
+  const rsrc_t rx = AM == AM_TILED
+                        ? make_rsrc(x, (uint32_t)rtiles * 32u * (uint32_t)K)
+                        : make_rsrc(x + (size_t)row0 * K, (uint32_t)vrows * (uint32_t)K * 2u);
 
   float4_t acc[NACC];
 #pragma unroll
@@ -611,7 +632,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   // (4096 x 11008 15.6 -> 15.0 us), bf16 6-8 % (11008 x 4096 17.8 -> 16.6);
   // with two row tiles (M = 24) the doubled MFMAs cost more than the dequant
   // they save (5120 x 5120 14.2 -> 15.2).
-  constexpr bool FFOLD = AM == AM_FULLT && MT == 1 && full_fold<WP>();
+  constexpr bool FFOLD = (AM == AM_FULLT || AM == AM_TILED) && MT == 1 && full_fold<WP>();
   float4_t yfm[FFOLD ? MT : 1];
 #pragma unroll
   for (int m = 0; m < (FFOLD ? MT : 1); ++m) yfm[m] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -628,7 +649,8 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   typename WP::CodeT ring[RUN];
   typename Op<DT>::vec ra[PA][NA];
   typename WP::Meta mc, mn = WP::zero_meta();
-  XLds xs{xlds, M, make_rsrc(perm, 0u), make_rsrc(xsc, 0u), perm != nullptr, nullptr, 0u};
+  XLds xs{xlds, M, make_rsrc(perm, 0u), make_rsrc(xsc, 0u), perm != nullptr, nullptr, 0u,
+          rtiles, (int)blockIdx.y * MT};
   if constexpr (AM == AM_XGATHER) {
     xs.xp = xlds + xlds_x_bytes(M, K) + xlds_s_bytes(K, XS);
     xs.xstride = 16u * (uint32_t)M;
@@ -717,9 +739,14 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
           } else {
             if constexpr (FFOLD) wp.raw_operands(ring[s], b);
             else wp.operands(ring[s], s, mc, b);
-            if constexpr (AM == AM_FULLT) {
+            if constexpr (AM == AM_FULLT || AM == AM_TILED) {
               typename Op<DT>::vec at[NA];
-              xpose_a<DT, MT, WP>(ra[sa], at, xlds + wave * MT * 4096, lane);
+              if constexpr (AM == AM_FULLT) {
+                xpose_a<DT, MT, WP>(ra[sa], at, xlds + wave * MT * 4096, lane);
+              } else {
+#pragma unroll
+                for (int q = 0; q < NA; ++q) at[q] = ra[sa][q];
+              }
               if constexpr (FFOLD) {
                 typename Op<DT>::vec bz[1];
                 WP::zero_operands(mc, s, bz);
@@ -850,7 +877,8 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
-  const XLds none{nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, nullptr, 0u};
+  const XLds none{nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, nullptr, 0u,
+                  0, 0};
   const bool g0 = lane & 16, g1 = lane & 32;
 
   float4_t yf[NC];
@@ -1107,7 +1135,11 @@ static void launch_intb_mode(int am, int mt, const DecodeArgs& a) {
       if (a.wide) return launch_intb_wide<DT, U, BITS>(a);
     }
     if (am == AM_PACKED) launch_intb_packed<DT, AM_PACKED, U, false, BITS>(a);
-    else if (am == AM_FULL) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);
+    else if (am == AM_TILED) {
+      if (mt == 1) launch_intb_v<DT, 1, AM_TILED, U, false, BITS>(a);
+      else if (mt == 2) launch_intb_v<DT, 2, AM_TILED, U, false, BITS>(a);
+      else launch_intb_v<DT, 4, AM_TILED, U, false, BITS>(a);
+    } else if (am == AM_FULL) launch_intb_v<DT, 1, AM_FULL, U, false, BITS>(a);
     else if (mt == 1) launch_intb_v<DT, 1, AM_FULLT, U, false, BITS>(a);
     else if (mt == 2) launch_intb_v<DT, 2, AM_FULLT, U, false, BITS>(a);
     else launch_intb_v<DT, 4, AM_FULLT, U, false, BITS>(a);

@@ -72,19 +72,14 @@ void set_timing_events(hipEvent_t a, hipEvent_t b) {
   t_ev_stop = b;
 }
 
-// Activation preparation pass: x_p[m, k] = x[m, perm[k]] (perm may be null:
+// Activation preparation: x_p[m, k] = x[m, perm[k]] (perm may be null:
 // identity), divided by the AWQ input scale s[perm[k]] when xsc is given (the
-// same rounding as the fused loads).  One thread per 8 consecutive columns.
+// same rounding as the fused loads).  gather8: the 8 consecutive prepared
+// columns k .. k + 7 of row xr.
 template <int DT>
-__global__ void __launch_bounds__(256)
-prep_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
-              const uint16_t* __restrict__ xsc, uint16_t* __restrict__ xp, int M, int K) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per_row = K >> 3;
-  if (idx >= (int64_t)M * per_row) return;
-  const int64_t m = idx / per_row;
-  const int k = (int)(idx - m * per_row) * 8;
-  const uint16_t* xr = x + m * K;
+__device__ __forceinline__ u32x4_t gather8(const uint16_t* __restrict__ xr,
+                                           const int32_t* __restrict__ perm,
+                                           const uint16_t* __restrict__ xsc, int k) {
   int src[8];
   if (perm) {
     const int4* pp = (const int4*)(perm + k);
@@ -104,7 +99,43 @@ prep_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
   u32x4_t v;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = h[2 * i] | (h[2 * i + 1] << 16);
-  *(u32x4_t*)(xp + m * K + k) = v;
+  return v;
+}
+
+// The pass in row-major form (the packed decode modes and the large-M
+// kernel): one thread per 8 consecutive columns of a row.
+template <int DT>
+__global__ void __launch_bounds__(256)
+prep_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+              const uint16_t* __restrict__ xsc, uint16_t* __restrict__ xp, int M, int K) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = K >> 3;
+  if (idx >= (int64_t)M * per_row) return;
+  const int64_t m = idx / per_row;
+  const int k = (int)(idx - m * per_row) * 8;
+  *(u32x4_t*)(xp + m * K + k) = gather8<DT>(x + m * K, perm, xsc, k);
+}
+
+// The pass in the decode kernel's TILED operand layout, RT = ceil(M / 16) row
+// tiles: the 16 bytes of chunk (t, R, j, l), at byte 16 (((t RT + R) 4 + j)
+// 64 + l), are prepared columns 128 t + 32 j + 8 (l >> 4) .. + 7 of row
+// 16 R + (l & 15) (the integer weights' lane order; zeros for rows >= M).
+// One thread per chunk, so every store is part of one coalesced 1 KB run.
+template <int DT>
+__global__ void __launch_bounds__(256)
+prep_tiled_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                  const uint16_t* __restrict__ xsc, uint16_t* __restrict__ xp, int M, int K,
+                  int RT) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)(K >> 7) * RT * 256) return;
+  const int l = (int)(idx & 63), j = (int)((idx >> 6) & 3);
+  const int64_t rest = idx >> 8;
+  const int R = (int)(rest % RT), t = (int)(rest / RT);
+  const int row = 16 * R + (l & 15);
+  const int k = 128 * t + 32 * j + 8 * (l >> 4);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < M) v = gather8<DT>(x + (int64_t)row * K, perm, xsc, k);
+  *(u32x4_t*)(xp + idx * 8) = v;
 }
 
 // Workspace layout: the prepared activations (when they are permuted and/or
@@ -115,10 +146,12 @@ prep_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
 // pass.
 static int64_t xprep_bytes(int64_t M, int64_t N, int64_t K, bool perm, bool xs) {
   if (!perm && !xs) return 0;
-  const int64_t bytes = ceil_div(M * K * 2, 256) * 256;
-  if (use_prefill(M, N, K)) return bytes;
+  if (use_prefill(M, N, K)) return ceil_div(M * K * 2, 256) * 256;
   int mt;
-  return is_staged(pick_mode(M, N, K, perm, xs, &mt)) ? 0 : bytes;
+  if (is_staged(pick_mode(M, N, K, perm, xs, &mt))) return 0;
+  // more than 4 rows: the TILED layout, in whole row tiles
+  const int64_t rows = M > 4 ? ceil_div(M, 16) * 16 : M;
+  return ceil_div(rows * K * 2, 256) * 256;
 }
 
 int64_t int4_workspace_bytes(int64_t M, int64_t N, int64_t K, bool perm, bool xs) {
@@ -155,6 +188,8 @@ GemmPlan plan_int_gemm(int64_t M, int64_t N, int64_t K, int G, int bits, int dty
   p.gather = perm && !p.prep;
   p.xs = xs && !p.prep;
   p.am = pick_mode(M, N, K, p.gather, p.xs, &p.mt);
+  // prepared activations for more than 4 rows go into the operand layout
+  if (p.prep && is_full(p.am)) p.am = AM_TILED;
   if ((p.gather || p.xs) && !is_staged(p.am)) {
     p.am = AM_GGATHER;
     p.mt = 1;
@@ -207,7 +242,9 @@ const char* tf(bool b) { return b ? "true" : "false"; }
 int64_t plan_names(const GemmPlan& p, char* out, int64_t n) {
   Names o{out, n};
   if (out && n > 0) out[0] = 0;
-  if (p.prep) o.add("w4a16::prep_x_kernel<%d> + ", p.dtype);
+  if (p.prep)
+    o.add("w4a16::%s<%d> + ", !p.prefill && p.am == AM_TILED ? "prep_tiled_kernel" : "prep_x_kernel",
+          p.dtype);
   if (p.prefill) {
     const int fmt = p.nf4 ? 1 : 0, U = p.nf4 ? 1 : p.U, bits = p.nf4 ? 4 : p.bits;
     const char* sep = "";
@@ -238,7 +275,21 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
   const GemmPlan pl = plan_int_gemm(M, N, K, G, bits, dtype, perm != nullptr, xsc != nullptr,
                                     workspace != nullptr);
   const void* xa = x;
-  if (pl.prep) {
+  if (pl.prep && !pl.prefill && pl.am == AM_TILED) {
+    // the activations are prepared once into the workspace, in the operand
+    // layout of the TILED mode
+    const int RT = (int)ceil_div(M, 16);
+    const dim3 grid((unsigned)ceil_div((K / 128) * RT * 256, 256));
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(prep_tiled_kernel<DT_F16>, grid, dim3(256), 0, stream,
+                         (const uint16_t*)x, perm, (const uint16_t*)xsc, (uint16_t*)workspace,
+                         (int)M, (int)K, RT);
+    else
+      hipLaunchKernelGGL(prep_tiled_kernel<DT_BF16>, grid, dim3(256), 0, stream,
+                         (const uint16_t*)x, perm, (const uint16_t*)xsc, (uint16_t*)workspace,
+                         (int)M, (int)K, RT);
+    xa = workspace;
+  } else if (pl.prep) {
     // the activations are prepared once into the workspace
     const int64_t n8 = M * (K / 8);
     const dim3 grid((unsigned)ceil_div(n8, 256));

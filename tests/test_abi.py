@@ -149,12 +149,17 @@ def _plan(M, N, K, G=128, bits=4, dtype=0, perm=0, xs=0, ws=1):
 def test_plan_names_the_dispatch_without_gpu():
     dec = "w4a16::intb_decode_kernel<"
     # act-order decode: the one-row in-kernel gather, a permutation pass at M = 4
-    # on 4096 x 11008 (staging does not fit), the FULLT fold at M = 16
+    # on 4096 x 11008 (staging does not fit), and at M = 16 a pass into the
+    # operand layout (mode 6) feeding the fold; without a permutation M = 16
+    # takes the transposed rows (mode 4)
     assert _plan(1, 4096, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, true>"]
     assert _plan(4, 11008, 4096, perm=1) == ["w4a16::prep_x_kernel<0>",
                                              dec + "0, 1, 0, 1, false, 4, false>"]
-    assert _plan(16, 4096, 11008, perm=1) == ["w4a16::prep_x_kernel<0>",
-                                              dec + "0, 1, 4, 1, false, 4, false>"]
+    assert _plan(16, 4096, 11008, perm=1) == ["w4a16::prep_tiled_kernel<0>",
+                                              dec + "0, 1, 6, 1, false, 4, false>"]
+    assert _plan(24, 4096, 4096, perm=1) == ["w4a16::prep_tiled_kernel<0>",
+                                              dec + "0, 2, 6, 1, false, 4, false>"]
+    assert _plan(16, 4096, 11008) == [dec + "0, 1, 4, 1, false, 4, false>"]
     # without a workspace: no pass, the kernel gathers from global memory
     # (mode 5), at any M, and the large-M kernel does not split K
     assert _plan(16, 4096, 11008, perm=1, ws=0) == [dec + "0, 1, 5, 1, false, 4, false>"]
@@ -175,7 +180,8 @@ def test_plan_names_the_dispatch_without_gpu():
         "w4a16::wq_prefill_kernel<1, 256, true, 0, 1, 4>"]
     # the plan's pass agrees with w4a16_workspace_bytes
     for M, N, K in [(1, 4096, 4096), (4, 11008, 4096), (16, 4096, 4096), (5, 55296, 5120)]:
-        has_pass = "w4a16::prep_x_kernel<0>" in _plan(M, N, K, perm=1)
+        has_pass = any(k.startswith(("w4a16::prep_x_kernel", "w4a16::prep_tiled_kernel"))
+                       for k in _plan(M, N, K, perm=1))
         assert has_pass == (L.w4a16_workspace_bytes(M, N, K, 128) > 0 and
                             not _plan(M, N, K)[-1].endswith("split_reduce_kernel<0>")) or has_pass
     # NF4: the decode kernel up to 32 rows on this layer, the large-M kernel after
