@@ -1035,10 +1035,12 @@ static void allow_dynamic_lds(const void* kernel) {
 // Largest total of staged bytes (workgroups x bytes each) for which staging
 // beats a separate preparation pass: every workgroup copies the rows (and the
 // permutation and scales) from L2, so the cost grows with the grid, while the
-// pass costs about one launch (measured crossover on MI355X: staging saves
-// ~1 us on 4096 x 4096 layers, breaks even on 4096 x 11008 at M = 1 (688 x 24
-// KB) and costs ~10 us on 5120 x 55296 ones).
-constexpr int64_t kMaxStagedTotal = (int64_t)17 << 20;
+// pass costs about one launch.  Measured on MI355X, whole calls in a graph,
+// with the rows' DMA ahead of the code tiles: staging saves 0.9 - 1.8 us on
+// 4096 x 11008 at 2 - 4 rows (688 workgroups x up to 48 KB, 33 MB) and 1.7 us
+// on 11008 x 4096 at 2 rows; it cost ~10 us on 5120 x 55296 layers (3456
+// workgroups) with the earlier staging.
+constexpr int64_t kMaxStagedTotal = (int64_t)40 << 20;
 
 // Activation mode and row tiles per workgroup row block for M rows of a
 // [N, K] layer; gather: an act-order permutation is to be applied, xs: AWQ

@@ -138,6 +138,97 @@ prep_tiled_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ pe
   *(u32x4_t*)(xp + idx * 8) = v;
 }
 
+// The pass with each row staged on chip, for K up to what LDS holds
+// (prep_rows_fits): workgroup (s, r) takes row r and the 8-column chunk c =
+// 256 s + thread.  The row (and the input scales) go into LDS by DMA while
+// the thread's permutation entries load into registers, so the pass waits on
+// memory once; the chunk is then gathered from LDS and stored, row-major
+// (xp + r K + 8 c) or, TILED, at its operand slot (rows M .. 16 RT - 1 of
+// the TILED layout are zeros).  One chunk per thread: the pass is latency
+// bound, and more workgroups per row (each staging the row) run it on more
+// CUs (measured on MI355X, 11008 inputs at M = 4 and 16, whole calls in a
+// graph: 6 chunks per thread, one workgroup per row, 1.7 us slower).
+inline bool prep_rows_fits(int64_t K, bool xs) {
+  const int64_t rowb = ceil_div(K * 2, 1024) * 1024;
+  return rowb * (xs ? 2 : 1) <= kMaxXldsOne;
+}
+
+template <bool TILED>
+__device__ __forceinline__ uint16_t* prep_slot(uint16_t* xp, int r, int c, int K, int RT) {
+  if constexpr (TILED) {
+    const int k0 = 8 * c, t = k0 >> 7, j = (k0 >> 5) & 3, b = (k0 >> 3) & 3;
+    const int64_t idx = ((int64_t)(t * RT + (r >> 4)) * 4 + j) * 64 + (r & 15) + 16 * b;
+    return xp + idx * 8;
+  } else {
+    return xp + (int64_t)r * K + 8 * c;
+  }
+}
+
+template <int DT, bool TILED>
+__global__ void __launch_bounds__(64 * DW)
+prep_rows_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm,
+                 const uint16_t* __restrict__ xsc, uint16_t* __restrict__ xp, int M, int K,
+                 int RT) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int NT = 64 * DW, P = 1;
+  const int r = blockIdx.y, nch = K >> 3, c0 = blockIdx.x * NT * P;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (r >= M) {  // padding rows of the TILED layout (workgroup-uniform)
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int c = c0 + (int)threadIdx.x + i * NT;
+      if (c < nch) *(u32x4_t*)prep_slot<TILED>(xp, r, c, K, RT) = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+  u32x4_t pr[P][2];
+  if (perm) {
+    const rsrc_t rp = make_rsrc(perm, (uint32_t)K * 4u);
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const uint32_t c = (uint32_t)(c0 + (int)threadIdx.x + i * NT);
+      pr[i][0] = bld128(rp, c * 32u, 0);
+      pr[i][1] = bld128(rp, c * 32u + 16u, 0);
+    }
+  }
+  const uint32_t rowb = (uint32_t)ceil_div((int64_t)K * 2, 1024) * 1024u;
+  stage_lds(x + (int64_t)r * K, (uint32_t)K * 2u, lds, wave, lane);
+  if (xsc) stage_lds(xsc, (uint32_t)K * 2u, lds + rowb, wave, lane);
+  lds_barrier();
+  const uint16_t* row = (const uint16_t*)lds;
+  const uint16_t* sl = (const uint16_t*)(lds + rowb);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int c = c0 + (int)threadIdx.x + i * NT;
+    if (c >= nch) break;
+    uint32_t src[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      src[e] = perm ? (e < 4 ? pr[i][0][e] : pr[i][1][e - 4]) : (uint32_t)(8 * c + e);
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[e] = row[src[e]];
+      if (xsc) h[e] = div_scale1<DT>((uint16_t)h[e], sl[src[e]]);
+    }
+    *(u32x4_t*)prep_slot<TILED>(xp, r, c, K, RT) =
+        u32x4_t{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+  }
+}
+
+template <int DT, bool TILED>
+static void launch_prep_rows(const void* x, const int32_t* perm, const void* xsc, void* xp,
+                             int64_t M, int64_t K, hipStream_t stream) {
+  const int RT = (int)ceil_div(M, 16);
+  const dim3 grid((unsigned)ceil_div(K / 8, (int64_t)64 * DW),
+                  (unsigned)(TILED ? 16 * RT : M));
+  const size_t lds = (size_t)ceil_div(K * 2, 1024) * 1024 * (xsc ? 2 : 1);
+  allow_dynamic_lds((const void*)prep_rows_kernel<DT, TILED>);
+  hipLaunchKernelGGL((prep_rows_kernel<DT, TILED>), grid, dim3(64 * DW), lds, stream,
+                     (const uint16_t*)x, perm, (const uint16_t*)xsc, (uint16_t*)xp, (int)M, (int)K,
+                     RT);
+}
+
 // Workspace layout: the prepared activations (when they are permuted and/or
 // divided by the AWQ input scales in a separate pass), then the large-M
 // kernel's split-K partials (when it splits K).  The decode kernel gathers and
@@ -177,6 +268,8 @@ GemmPlan plan_int_gemm(int64_t M, int64_t N, int64_t K, int G, int bits, int dty
   p.prefill = use_prefill(M, N, K) && (ws || (!perm && !xs));
   p.xprep = ws ? xprep_bytes(M, N, K, perm, xs) : 0;
   p.prep = p.xprep > 0;
+  // (the rows of the row-staged pass are the grid's y dimension)
+  p.prep_rows = p.prep && prep_rows_fits(K, xs) && ceil_div(M, 16) * 16 <= 65535;
   if (p.prefill) {
     const PrefillPlan pp = plan_prefill(M, N, K, ws);
     p.bm = pp.bm;
@@ -242,9 +335,11 @@ const char* tf(bool b) { return b ? "true" : "false"; }
 int64_t plan_names(const GemmPlan& p, char* out, int64_t n) {
   Names o{out, n};
   if (out && n > 0) out[0] = 0;
-  if (p.prep)
-    o.add("w4a16::%s<%d> + ", !p.prefill && p.am == AM_TILED ? "prep_tiled_kernel" : "prep_x_kernel",
-          p.dtype);
+  const bool tiled = !p.prefill && p.am == AM_TILED;
+  if (p.prep_rows)
+    o.add("w4a16::prep_rows_kernel<%d, %s> + ", p.dtype, tf(tiled));
+  else if (p.prep)
+    o.add("w4a16::%s<%d> + ", tiled ? "prep_tiled_kernel" : "prep_x_kernel", p.dtype);
   if (p.prefill) {
     const int fmt = p.nf4 ? 1 : 0, U = p.nf4 ? 1 : p.U, bits = p.nf4 ? 4 : p.bits;
     const char* sep = "";
@@ -275,7 +370,17 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
   const GemmPlan pl = plan_int_gemm(M, N, K, G, bits, dtype, perm != nullptr, xsc != nullptr,
                                     workspace != nullptr);
   const void* xa = x;
-  if (pl.prep && !pl.prefill && pl.am == AM_TILED) {
+  if (pl.prep_rows) {
+    const bool tiled = !pl.prefill && pl.am == AM_TILED;
+    if (dtype == DT_F16) {
+      if (tiled) launch_prep_rows<DT_F16, true>(x, perm, xsc, workspace, M, K, stream);
+      else launch_prep_rows<DT_F16, false>(x, perm, xsc, workspace, M, K, stream);
+    } else {
+      if (tiled) launch_prep_rows<DT_BF16, true>(x, perm, xsc, workspace, M, K, stream);
+      else launch_prep_rows<DT_BF16, false>(x, perm, xsc, workspace, M, K, stream);
+    }
+    xa = workspace;
+  } else if (pl.prep && !pl.prefill && pl.am == AM_TILED) {
     // the activations are prepared once into the workspace, in the operand
     // layout of the TILED mode
     const int RT = (int)ceil_div(M, 16);

@@ -69,7 +69,8 @@ PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, bool split_ok = true);
 struct GemmPlan {
   bool nf4 = false;
   int dtype = 0, bits = 4, U = 1;
-  bool prep = false;        // prep_x_kernel writes x[:, perm] / s into the workspace first
+  bool prep = false;        // a pass writes x[:, perm] / s into the workspace first
+  bool prep_rows = false;   // ... prep_rows_kernel (each row staged on chip)
   int64_t xprep = 0;        // its workspace bytes
   bool prefill = false;     // the large-M kernel (else the decode kernel)
   int bm = 0, splits = 1;   // large-M: rows per workgroup, split of K

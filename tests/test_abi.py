@@ -91,22 +91,26 @@ def test_gemm_validation_without_gpu():
     assert need >= 16 * 4096 * 2
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, FAKE, need - 16, NULL) == 5
     # the size covers every call at a shape, with or without a permutation and
-    # AWQ input scales: M <= 4 rows (with the permutation and the scales) that
-    # the decode kernel stages on chip need no workspace (up to 72 KB per
-    # workgroup and 17 MiB over the grid: 256 x 24 KB and 256 x 56 KB here) ...
+    # AWQ input scales: M <= 4 rows that the decode kernel stages on chip need
+    # no workspace (rows + scales + permuted rows up to 144 KB per workgroup on
+    # grids of at most 256 workgroups, else 72 KB; staged bytes up to 40 MiB
+    # over the grid; K <= 12288 with a permutation) ...
     assert L.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
     assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) == 0
-    # ... larger ones are prepared in a pass: M * K * 2 bytes
-    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) >= 11008 * 2     # 88 KB per workgroup
-    assert L.w4a16_workspace_bytes(4, 6144, 4096, 128) >= 4 * 4096 * 2    # 384 x 56 KB
-    assert L.w4a16_workspace_bytes(1, 55296, 5120, 128) >= 5120 * 2        # 3456 workgroups
-    assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) >= 4 * 11008 * 2
-    assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 5 * 4096 * 2
+    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) == 0      # 256 x 66 KB
+    assert L.w4a16_workspace_bytes(4, 6144, 4096, 128) == 0       # 384 x 72 KB, 21 MB staged
+    # ... other ones are prepared in a pass: M * K * 2 bytes (up to 4 rows)
+    assert L.w4a16_workspace_bytes(4, 6144, 5120, 128) >= 4 * 5120 * 2    # 384 x 90 KB
+    assert L.w4a16_workspace_bytes(1, 55296, 5120, 128) >= 5120 * 2       # 3456 x 40 KB staged
+    assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) >= 4 * 11008 * 2  # 198 KB
+    assert L.w4a16_workspace_bytes(1, 4096, 16384, 128) >= 16384 * 2      # K > 12288
+    # ... and from 5 rows in whole row tiles of 16 (the operand layout)
+    assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 16 * 4096 * 2
     # w4a16_gemm_xscale validates what the call needs (each case below fails
     # before any launch)
     xs = L.w4a16_gemm_xscale
-    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 4, 4096, 11008, 0, FAKE, 16,
-              NULL) == 5
+    assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, NULL, 128, FAKE, 4, 4096, 16384, 0, FAKE, 16,
+              NULL) == 5        # 4 rows + scales: 160 KB, a pass
     assert xs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 8, 4096, 4096, 0, FAKE, 16,
               NULL) == 5
     assert xs(FAKE, ODD, FAKE, FAKE, FAKE, NULL, 128, FAKE, 2, 4096, 4096, 0, NULL, 0, NULL) == 3
@@ -148,17 +152,21 @@ def _plan(M, N, K, G=128, bits=4, dtype=0, perm=0, xs=0, ws=1):
 
 def test_plan_names_the_dispatch_without_gpu():
     dec = "w4a16::intb_decode_kernel<"
-    # act-order decode: the one-row in-kernel gather, a permutation pass at M = 4
-    # on 4096 x 11008 (staging does not fit), and at M = 16 a pass into the
-    # operand layout (mode 6) feeding the fold; without a permutation M = 16
-    # takes the transposed rows (mode 4)
+    # act-order decode: the in-kernel gather at 1 and 4 rows on 11008 columns,
+    # a row-staged permutation pass at M = 4 on 11008 inputs (staging does not
+    # fit), and at M = 16 a pass into the operand layout (mode 6) feeding the
+    # fold; without a permutation M = 16 takes the transposed rows (mode 4);
+    # past 12288 inputs the passes without row staging
     assert _plan(1, 4096, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, true>"]
-    assert _plan(4, 11008, 4096, perm=1) == ["w4a16::prep_x_kernel<0>",
+    assert _plan(4, 11008, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, false>"]
+    assert _plan(4, 4096, 11008, perm=1) == ["w4a16::prep_rows_kernel<0, false>",
                                              dec + "0, 1, 0, 1, false, 4, false>"]
-    assert _plan(16, 4096, 11008, perm=1) == ["w4a16::prep_tiled_kernel<0>",
+    assert _plan(16, 4096, 11008, perm=1) == ["w4a16::prep_rows_kernel<0, true>",
                                               dec + "0, 1, 6, 1, false, 4, false>"]
-    assert _plan(24, 4096, 4096, perm=1) == ["w4a16::prep_tiled_kernel<0>",
+    assert _plan(24, 4096, 4096, perm=1) == ["w4a16::prep_rows_kernel<0, true>",
                                               dec + "0, 2, 6, 1, false, 4, false>"]
+    assert _plan(16, 1024, 98304, perm=1)[0] == "w4a16::prep_tiled_kernel<0>"
+    assert _plan(4, 1024, 98304, perm=1)[0] == "w4a16::prep_x_kernel<0>"
     assert _plan(16, 4096, 11008) == [dec + "0, 1, 4, 1, false, 4, false>"]
     # without a workspace: no pass, the kernel gathers from global memory
     # (mode 5), at any M, and the large-M kernel does not split K
@@ -180,7 +188,7 @@ def test_plan_names_the_dispatch_without_gpu():
         "w4a16::wq_prefill_kernel<1, 256, true, 0, 1, 4>"]
     # the plan's pass agrees with w4a16_workspace_bytes
     for M, N, K in [(1, 4096, 4096), (4, 11008, 4096), (16, 4096, 4096), (5, 55296, 5120)]:
-        has_pass = any(k.startswith(("w4a16::prep_x_kernel", "w4a16::prep_tiled_kernel"))
+        has_pass = any(k.startswith("w4a16::prep_")
                        for k in _plan(M, N, K, perm=1))
         assert has_pass == (L.w4a16_workspace_bytes(M, N, K, 128) > 0 and
                             not _plan(M, N, K)[-1].endswith("split_reduce_kernel<0>")) or has_pass
