@@ -74,17 +74,27 @@ __device__ __forceinline__ void mma_tile(const typename Op<DT>::vec b[4],
 
 // Value of the meta unit that MFMA step g = lane >> 4 of a K tile uses, out
 // of the tile's U candidates (unit g U / 4: g >> 1 for U = 2, g for U = 4),
-// selected on the bits of the lane group (a chain of equality tests would
-// become divergent branches).
+// blended bitwise on the bits of the lane group: a chain of equality tests
+// would become divergent branches, and a select between two elements of one
+// local array can be turned into a load at a per-lane index, which puts the
+// array in scratch memory.
 template <int U, class T>
 __device__ __forceinline__ T sel_unit(const T (&v)[U], int lane) {
+  static_assert(sizeof(T) == 4, "32-bit values");
   if constexpr (U == 1) {
     return v[0];
-  } else if constexpr (U == 2) {
-    return (lane & 32) ? v[1] : v[0];
   } else {
-    const bool b0 = lane & 16, b1 = lane & 32;
-    return b1 ? (b0 ? v[3] : v[2]) : (b0 ? v[1] : v[0]);
+    uint32_t b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) b[u] = __builtin_bit_cast(uint32_t, v[u]);
+    const uint32_t m5 = 0u - (uint32_t)((lane >> 5) & 1);
+    if constexpr (U == 2) {
+      return __builtin_bit_cast(T, b[0] ^ ((b[0] ^ b[1]) & m5));
+    } else {
+      const uint32_t m4 = 0u - (uint32_t)((lane >> 4) & 1);
+      const uint32_t lo = b[0] ^ ((b[0] ^ b[1]) & m4), hi = b[2] ^ ((b[2] ^ b[3]) & m4);
+      return __builtin_bit_cast(T, lo ^ ((lo ^ hi) & m5));
+    }
   }
 }
 
@@ -330,8 +340,8 @@ struct Nf4W {
 // puts into the MFMA layout through LDS.  Rows >= M read 0 through the
 // descriptor range; k >= K (only in a half NF4 tile) uses an out-of-range
 // offset.
-// Staged activations in LDS: x rows [M][K] at xl, the permuted rows at xp
-// (XGATHER; chunk c of row m at c * xstride + 16 m, xstride = 16 M).
+// Staged activations in LDS: x rows [M][K] at xl (XGATHER: permuted in
+// place, chunk c of row m at 2 K m + 16 (c ^ 4 (m & 3))).
 // GGATHER: the permutation (when perm) and the input scales in global memory,
 // behind the descriptors rp and rs.  TILED: rt row tiles in the prepared
 // buffer, rt0 the workgroup's first.
@@ -340,8 +350,6 @@ struct XLds {
   int M;
   rsrc_t rp, rs;
   bool perm;
-  const uint8_t* xp;
-  uint32_t xstride;
   int rt, rt0;
 };
 
@@ -356,7 +364,7 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
     // zeros (K % 128 == 0: no half tiles)
     const int j = r >> 2, m = min(r & 3, xs.M - 1);
     const uint32_t c = (uint32_t)(t * 128 + WP::xk(j, b)) >> 3;
-    a[0] = *(const vec*)(xs.xp + c * xs.xstride + (uint32_t)m * 16u);
+    a[0] = *(const vec*)(xs.xl + (uint32_t)m * (uint32_t)K * 2u + ((c ^ ((uint32_t)(m & 3) << 2)) << 4));
   } else if constexpr (AM == AM_GGATHER) {
     // one row tile: lane row r, 8 inputs of step j per operand; rows past M
     // read 0 through the descriptor range of rx, as does any input of a
@@ -474,11 +482,13 @@ constexpr bool full_fold() {
 __host__ __device__ constexpr uint32_t xpose_bytes(int MT) { return (uint32_t)(DW * MT * 4096); }
 
 // Staged LDS layout, each region rounded up to whole 1 KB blocks: x rows
-// [M][K], then (input scales) s [K], then (gather) the permuted rows.  XGATHER
-// permutes the staged rows once per workgroup: chunk c (permuted columns
-// 8c .. 8c + 7) of row m goes to the 16 bytes at c * 16 M + 16 m.  The
-// permutation itself is read from memory into registers (kPermRegs chunks of
-// 8 entries per thread), so the gather takes K <= 64 DW 8 kPermRegs.
+// [M][K], then (input scales) s [K].  XGATHER permutes the staged rows once
+// per workgroup, each row in place: chunk c (permuted columns 8c .. 8c + 7)
+// of row m goes to the 16 bytes at 2 K m + 16 (c ^ 4 (m & 3)) (the xor puts
+// the chunks that one operand load takes from the 4 rows in different LDS
+// banks).  The permutation itself is read from memory into registers
+// (kPermRegs chunks of 8 entries per thread), so the gather takes
+// K <= 64 DW 8 kPermRegs.
 constexpr int kPermRegs = 6;
 constexpr int64_t kMaxGatherK = (int64_t)64 * DW * 8 * kPermRegs;
 __host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
@@ -487,9 +497,6 @@ __host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
 __host__ __device__ constexpr uint32_t xlds_s_bytes(int K, bool xs) {
   return xs ? (uint32_t)((K * 2 + 1023) / 1024 * 1024) : 0u;
 }
-__host__ __device__ constexpr uint32_t xlds_xp_bytes(int M, int K, bool perm) {
-  return perm ? xlds_x_bytes(M, K) : 0u;
-}
 // what each workgroup reads from memory besides the weights: the rows, the
 // permutation and the input scales
 __host__ __device__ constexpr uint32_t xlds_staged_bytes(int M, int K, bool perm, bool xs) {
@@ -497,7 +504,7 @@ __host__ __device__ constexpr uint32_t xlds_staged_bytes(int M, int K, bool perm
 }
 // the LDS footprint
 __host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool perm, bool xs) {
-  return xlds_x_bytes(M, K) + xlds_s_bytes(K, xs) + xlds_xp_bytes(M, K, perm);
+  return (void)perm, xlds_x_bytes(M, K) + xlds_s_bytes(K, xs);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
@@ -517,6 +524,15 @@ __device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8
     lds_dma16(r, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), 0);
 }
 
+// A workgroup barrier for LDS data: this wave's LDS writes (and LDS DMA) are
+// complete before it, other waves' are visible after it; loads from global
+// memory in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // XGATHER: the permutation chunks of this thread (chunk c = entries
 // 8c .. 8c + 7, c = thread + i 64 DW), loaded from memory before the rows
 // are staged; chunks past K read 0 and are not used.
@@ -531,17 +547,16 @@ __device__ __forceinline__ void load_perm_chunks(const int32_t* perm, int K,
   }
 }
 
-// XGATHER: the staged rows permuted once per workgroup, x_p[m][k] =
-// x[m][perm[k]], into the layout the loop reads: each thread gathers its
-// chunks of one row from LDS (all reads of the row before its writes), then
-// the next row.
+// XGATHER: the staged rows permuted once per workgroup, in place, x_p[m][k]
+// = x[m][perm[k]], into the layout the loop reads: row by row, each thread
+// gathers its chunks of the row from LDS into registers, then (after a
+// barrier: every read of the row is done) writes them over the row.
 __device__ __forceinline__ void permute_staged(const XLds& xs, int K,
                                                const u32x4_t (&pr)[kPermRegs][2]) {
   const int nch = K >> 3;
   const int nit = (nch + 64 * DW - 1) / (64 * DW);  // passes over the workgroup's threads
-  uint8_t* xp = const_cast<uint8_t*>(xs.xp);
   for (int m = 0; m < xs.M; ++m) {
-    const uint8_t* row = xs.xl + (uint32_t)m * (uint32_t)K * 2u;
+    uint8_t* row = const_cast<uint8_t*>(xs.xl) + (uint32_t)m * (uint32_t)K * 2u;
     // (the workgroup's last pass may hold chunks past K: entries 0, gathered
     // from column 0 and never written)
     u32x4_t w[kPermRegs];
@@ -557,22 +572,15 @@ __device__ __forceinline__ void permute_staged(const XLds& xs, int K,
       w[i] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
                      v[6] | (v[7] << 16)};
     }
+    lds_barrier();
+    const uint32_t sw = (uint32_t)(m & 3) << 2;
 #pragma unroll
     for (int i = 0; i < kPermRegs; ++i) {
       if (i >= nit) break;
       const int c = threadIdx.x + i * 64 * DW;
-      if (c < nch) *(u32x4_t*)(xp + (uint32_t)c * xs.xstride + (uint32_t)m * 16u) = w[i];
+      if (c < nch) *(u32x4_t*)(row + (((uint32_t)c ^ sw) << 4)) = w[i];
     }
   }
-}
-
-// A workgroup barrier for LDS data: this wave's LDS writes (and LDS DMA) are
-// complete before it, other waves' are visible after it; loads from global
-// memory in flight are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // XS: divide the staged activations by the AWQ input scales xsc [K] (staged
@@ -649,12 +657,8 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   typename WP::CodeT ring[RUN];
   typename Op<DT>::vec ra[PA][NA];
   typename WP::Meta mc, mn = WP::zero_meta();
-  XLds xs{xlds, M, make_rsrc(perm, 0u), make_rsrc(xsc, 0u), perm != nullptr, nullptr, 0u,
-          rtiles, (int)blockIdx.y * MT};
-  if constexpr (AM == AM_XGATHER) {
-    xs.xp = xlds + xlds_x_bytes(M, K) + xlds_s_bytes(K, XS);
-    xs.xstride = 16u * (uint32_t)M;
-  }
+  XLds xs{xlds, M, make_rsrc(perm, 0u), make_rsrc(xsc, 0u), perm != nullptr, rtiles,
+          (int)blockIdx.y * MT};
   if constexpr (AM == AM_GGATHER) {
     xs.rp = make_rsrc(perm, perm ? (uint32_t)K * 4u : 0u);
     xs.rs = make_rsrc(xsc, XS ? (uint32_t)K * 2u : 0u);
@@ -877,8 +881,7 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
-  const XLds none{nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, nullptr, 0u,
-                  0, 0};
+  const XLds none{nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, 0, 0};
   const bool g0 = lane & 16, g1 = lane & 32;
 
   float4_t yf[NC];

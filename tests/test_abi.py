@@ -92,17 +92,17 @@ def test_gemm_validation_without_gpu():
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, FAKE, need - 16, NULL) == 5
     # the size covers every call at a shape, with or without a permutation and
     # AWQ input scales: M <= 4 rows that the decode kernel stages on chip need
-    # no workspace (rows + scales + permuted rows up to 144 KB per workgroup on
-    # grids of at most 256 workgroups, else 72 KB; staged bytes up to 40 MiB
-    # over the grid; K <= 12288 with a permutation) ...
+    # no workspace (rows + scales up to 144 KB per workgroup on grids of at
+    # most 256 workgroups, else 72 KB; staged bytes, permutation included, up
+    # to 40 MiB over the grid; K <= 12288 with a permutation) ...
     assert L.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
     assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) == 0
-    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) == 0      # 256 x 66 KB
-    assert L.w4a16_workspace_bytes(4, 6144, 4096, 128) == 0       # 384 x 72 KB, 21 MB staged
+    assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) == 0      # 256 x 44 KB
+    assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) == 0      # 256 x 110 KB, 39 MB staged
+    assert L.w4a16_workspace_bytes(4, 6144, 5120, 128) == 0       # 384 x 50 KB
     # ... other ones are prepared in a pass: M * K * 2 bytes (up to 4 rows)
-    assert L.w4a16_workspace_bytes(4, 6144, 5120, 128) >= 4 * 5120 * 2    # 384 x 90 KB
+    assert L.w4a16_workspace_bytes(4, 6144, 8192, 128) >= 4 * 8192 * 2    # 384 x 80 KB
     assert L.w4a16_workspace_bytes(1, 55296, 5120, 128) >= 5120 * 2       # 3456 x 40 KB staged
-    assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) >= 4 * 11008 * 2  # 198 KB
     assert L.w4a16_workspace_bytes(1, 4096, 16384, 128) >= 16384 * 2      # K > 12288
     # ... and from 5 rows in whole row tiles of 16 (the operand layout)
     assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 16 * 4096 * 2
@@ -152,14 +152,15 @@ def _plan(M, N, K, G=128, bits=4, dtype=0, perm=0, xs=0, ws=1):
 
 def test_plan_names_the_dispatch_without_gpu():
     dec = "w4a16::intb_decode_kernel<"
-    # act-order decode: the in-kernel gather at 1 and 4 rows on 11008 columns,
-    # a row-staged permutation pass at M = 4 on 11008 inputs (staging does not
-    # fit), and at M = 16 a pass into the operand layout (mode 6) feeding the
+    # act-order decode: the in-kernel gather at 1 and 4 rows on the Llama
+    # layers, a row-staged permutation pass at M = 4 past 12288 inputs, and at
+    # M = 16 a pass into the operand layout (mode 6) feeding the
     # fold; without a permutation M = 16 takes the transposed rows (mode 4);
     # past 12288 inputs the passes without row staging
     assert _plan(1, 4096, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, true>"]
     assert _plan(4, 11008, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, false>"]
-    assert _plan(4, 4096, 11008, perm=1) == ["w4a16::prep_rows_kernel<0, false>",
+    assert _plan(4, 4096, 11008, perm=1) == [dec + "0, 1, 2, 1, false, 4, false>"]
+    assert _plan(4, 4096, 16384, perm=1) == ["w4a16::prep_rows_kernel<0, false>",
                                              dec + "0, 1, 0, 1, false, 4, false>"]
     assert _plan(16, 4096, 11008, perm=1) == ["w4a16::prep_rows_kernel<0, true>",
                                               dec + "0, 1, 6, 1, false, 4, false>"]

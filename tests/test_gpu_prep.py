@@ -26,8 +26,8 @@ TDT = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 # (M, N, K, act-order, input scales, dtype, the pass the plan must name)
 CASES = [
-    (4, 256, 11008, True, False, "f16", "prep_rows_kernel<0, false>"),
-    (3, 208, 11008, True, True, "bf16", "prep_rows_kernel<1, false>"),
+    (4, 256, 16384, True, False, "f16", "prep_rows_kernel<0, false>"),
+    (3, 208, 16384, True, True, "bf16", "prep_rows_kernel<1, false>"),
     (16, 208, 11008, True, False, "bf16", "prep_rows_kernel<1, true>"),
     (13, 256, 4096, False, True, "f16", "prep_rows_kernel<0, true>"),
     (20, 208, 4096, True, True, "f16", "prep_rows_kernel<0, true>"),
@@ -45,6 +45,38 @@ def test_prepared_activations_match_oracle(M, N, K, act, xs, dtype, pass_name):
     say("prep", M, N, K, act, xs, dtype, plan)
     assert plan[0] == "w4a16::" + pass_name
     W, gi, s = int4_inputs(tag, N, K, act_order=act, awq=xs)
+    _, packed = gpu_int4_pack(W, gi)
+    xb = synth.to_bits(synth.activations(tag + "/x", M, K), dtype)
+    wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
+    if xs:
+        sb = synth.to_bits(s[None, :], dtype)[0]
+        y = w4.w4a16_gemm_xscale(bits_to_tensor(xb, dtype), bits_to_tensor(sb, dtype), packed)
+        torch.cuda.synchronize()
+        err = gemm.rel_err(tensor_f64(y, dtype), gemm.gemm_ref_xscale_bits(xb, sb, wd, dtype))
+    else:
+        y = w4.w4a16_gemm(bits_to_tensor(xb, dtype), packed)
+        torch.cuda.synchronize()
+        err = gemm.rel_err(tensor_f64(y, dtype), gemm.gemm_ref_bits(xb, wd, dtype))
+    say("  rel err", err)
+    assert err <= TOL
+
+
+# (M, K, input scales, dtype): 1-4 rows gathered and scaled on chip by the
+# decode kernel itself, each row permuted in place in LDS
+STAGED = [(1, 11008, False, "f16"), (2, 11008, True, "bf16"), (3, 11008, False, "bf16"),
+          (4, 11008, True, "f16"), (4, 12288, False, "f16"), (3, 4096, True, "f16")]
+
+
+@pytest.mark.parametrize("M,K,xs,dtype", STAGED)
+def test_staged_gather_matches_oracle(M, K, xs, dtype):
+    N = 208
+    tag = "gpu/prep/staged/%d/%d/%d" % (M, K, xs)
+    plan = w4.w4a16_gemm_plan(M, N, K, dtype=TDT[dtype], perm=True, x_scale=xs)
+    say("staged gather", M, N, K, xs, dtype, plan)
+    assert plan == ["w4a16::intb_decode_kernel<%d, 1, 2, 1, %s, 4, %s>"
+                    % (0 if dtype == "f16" else 1, "true" if xs else "false",
+                       "true" if M == 1 else "false")]
+    W, gi, s = int4_inputs(tag, N, K, act_order=True, awq=xs)
     _, packed = gpu_int4_pack(W, gi)
     xb = synth.to_bits(synth.activations(tag + "/x", M, K), dtype)
     wd = oracle_int4_rows(W, gi, np.arange(N), dtype)
