@@ -63,7 +63,7 @@ def plan(w4, M, N, K, dtype, perm=False, xs=False, ws=True):
 def main_kernel(kernels):
     """The call's GEMM kernel: the first launch that is not the preparation
     pass (the one the timing events attach to)."""
-    return [k for k in kernels if "prep_x_kernel" not in k][0]
+    return [k for k in kernels if not k.startswith("w4a16::prep_")][0]
 
 
 def parse():
@@ -352,28 +352,19 @@ def main():
     # timing events attached to every GEMM kernel's own dispatch
     # (hipExtLaunchKernel start/stop), on the stream the kernels run on.  A
     # dispatch's start event is taken when it is queued, so a kernel queued
-    # behind another one would be charged that kernel's tail: calls whose
-    # kernel does not gather x itself get their activations already permuted
-    # (perm = NULL; the same kernel instantiation on the same data without the
-    # library's permutation pass in front of it), and the stream is drained
-    # after every call, before the next one is queued.  (The step time above
-    # includes the pass and runs the calls back to back.)
+    # behind another one would be charged that kernel's tail: a call with a
+    # preparation pass drains the stream after the pass before it launches the
+    # timed kernel (the library does so while timing events are pending), and
+    # the stream is drained after every call, before the next one is queued.
+    # (The step time above includes the pass and runs the calls back to back.)
     nper = len(calls[0])
     kern = {}
     tcalls = []
     for step_layers, cl in zip(rot, calls):
         tl = []
         for (K, N, M, q), (a, _, _, _) in zip(step_layers, cl):
-            ks = plan(w4, M, N, K, "f16", perm=True)
-            kern[(M, K, N)] = ks
-            if "prep_x_kernel" not in ks[0]:
-                tl.append(a)
-                continue
-            key = ("xp", M, K, N)
-            if key not in xs:
-                xs[key] = xs[(M, K)][:, q["perm"].long()].contiguous()
-            tl.append((ctypes.c_void_p(xs[key].data_ptr()),) + a[1:4] + (ctypes.c_void_p(0),)
-                      + a[5:])
+            kern[(M, K, N)] = plan(w4, M, N, K, "f16", perm=True)
+            tl.append(a)
         tcalls.append(tl)
     torch.cuda.synchronize()
     nev = args.steps * nper

@@ -406,6 +406,11 @@ hipError_t launch_int_gemm(const void* x, const void* xsc, const void* codes_r,
                          perm, (const uint16_t*)xsc, (uint16_t*)workspace, (int)M, (int)K);
     xa = workspace;
   }
+  // a timed call: the events bracket the GEMM kernel alone (the timing
+  // events' contract)
+  if (pl.prep && (t_ev_start || t_ev_stop)) {
+    if (hipError_t e = hipStreamSynchronize(stream)) return e;
+  }
   if (pl.prefill) {
     launch_int_prefill(xa, codes_r, scales_r, zeros_r, out,
                        workspace ? (uint8_t*)workspace + pl.xprep : nullptr, M, N, K, G, bits,

@@ -84,7 +84,11 @@ int w4a16_version(void);
  * launches from the calling host thread.  The events are recorded by the
  * kernel's own dispatch (hipExtLaunchKernel), so hipEventElapsedTime between
  * them is that kernel's execution time.  One-shot: cleared by that launch.
- * Passing NULLs clears a pending request.  Do not use under graph capture.
+ * A call whose activations go through a preparation pass first (the
+ * permutation, the AWQ input scales) then waits on the host for that pass to
+ * finish (hipStreamSynchronize) before it launches the timed kernel, so that
+ * the start event does not take in the pass's tail.  Passing NULLs clears a
+ * pending request.  Do not use under graph capture.
  */
 int w4a16_set_timing_events(void* start_event, void* stop_event);
 
