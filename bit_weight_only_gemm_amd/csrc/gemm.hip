@@ -274,8 +274,8 @@ GemmPlan plan_int_gemm(int64_t M, int64_t N, int64_t K, int G, int bits, int dty
     const PrefillPlan pp = plan_prefill(M, N, K, ws);
     p.bm = pp.bm;
     p.splits = pp.splits;
-    p.full = M / pp.bm > 0;
-    p.tail = M % pp.bm != 0;
+    p.full = !pp.single && M / pp.bm > 0;
+    p.tail = pp.single || M % pp.bm != 0;
     return p;
   }
   p.gather = perm && !p.prep;
@@ -304,8 +304,8 @@ GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws) {
     const PrefillPlan pp = plan_prefill(M, N, K, ws);
     p.bm = pp.bm;
     p.splits = pp.splits;
-    p.full = M / pp.bm > 0;
-    p.tail = M % pp.bm != 0;
+    p.full = !pp.single && M / pp.bm > 0;
+    p.tail = pp.single || M % pp.bm != 0;
     return p;
   }
   p.am = pick_mode(M, N, K, false, false, &p.mt);

@@ -60,6 +60,7 @@ hipError_t launch_dequant_nf4(const uint8_t* qweight, const uint8_t* absmax_q,
 // workgroup per output tile.
 struct PrefillPlan {
   int bm, splits;
+  bool single;  // one launch of the ragged-tail form covers every row block
 };
 PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, bool split_ok = true);
 

@@ -41,9 +41,11 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff,
       r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-// TAIL: the row block may hold fewer than 256 rows; the row of each load is
-// then part of the per-lane offset so that rows past M read 0.  Full blocks
-// put it in the scalar offset (fewer registers).
+// TAIL: the row block may hold fewer than BM rows; the row of each load is
+// then part of the per-lane offset so that rows past M read 0 (a launch of
+// this form may also cover whole row blocks).  Full blocks put it in the
+// scalar offset (fewer registers).  Row block of a workgroup: rb0 +
+// blockIdx.y.
 // Split-K: workgroup z of S takes K tiles [z KT / S, (z + 1) KT / S) and, when
 // S > 1, writes its fp32 partial tile to part[z][M][N] for split_reduce_kernel.
 //
@@ -65,7 +67,8 @@ __global__ void __launch_bounds__(64 * PF_WAVES) __attribute__((amdgpu_waves_per
 wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                   const uint8_t* __restrict__ scales, const uint8_t* __restrict__ zeros,
                   uint32_t zx, Nf4Table L, uint16_t* __restrict__ out,
-                  float* __restrict__ part, int M, int N, int K, int KT, int NP, int S) {
+                  float* __restrict__ part, int M, int N, int K, int KT, int NP, int S,
+                  int rb0) {
   typedef typename Op<DT>::vec vec;
   typedef Codes<FMT == FMT_NF4 ? 4 : BITS> CT;     // NF4: its 16-byte loads as Codes<4>
   constexpr int kTile = 256 * BITS;                 // INT: bytes per column tile, K tile
@@ -82,7 +85,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row0 = (TAIL ? M / PF_BM : blockIdx.y) * PF_BM;
+  const int row0 = (rb0 + (int)blockIdx.y) * PF_BM;
   const int z = blockIdx.z;
   const int tb = (int)((int64_t)z * KT / S), te = (int)((int64_t)(z + 1) * KT / S);
   const int p = blockIdx.x * PF_WAVES + wave;  // this wave's 64-column panel
@@ -428,11 +431,14 @@ split_reduce_kernel(const float* __restrict__ part, int S, int64_t MN, uint16_t*
 template <int DT, int BM, int FMT, int U, int BITS>
 static void launch_prefill_bm(const void* x, const void* codes_r, const void* scales_r,
                               const void* zeros_r, const Nf4Table& L, void* out, float* part,
-                              int S, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                              int S, bool single, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream) {
   const int64_t NP = ceil_div(N, 64);
   const int KT = (int)(K / 128);
   const unsigned gx = (unsigned)ceil_div(NP, PF_WAVES);
-  const int64_t full = M / BM;
+  // single: every row block in one launch of the ragged-tail form
+  const int64_t full = single ? 0 : M / BM;
+  const int64_t tail_rb0 = full, tail_blocks = single ? ceil_div(M, (int64_t)BM) : 1;
   // INT codes without zeros (symmetric): an empty zeros range over a valid
   // base, every zero field read as 0 ^ 2^(BITS-1)
   const uint32_t zx = (FMT == FMT_INT4 && !zeros_r) ? sym_zero_xor(BITS) : 0u;
@@ -442,12 +448,12 @@ static void launch_prefill_bm(const void* x, const void* codes_r, const void* sc
     launch_timed(wq_prefill_kernel<DT, BM, false, FMT, U, BITS>,
                  dim3(gx, (unsigned)full, (unsigned)S), dim3(64 * PF_WAVES), 0, stream,
                  (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r, zp, zx, L,
-                 (uint16_t*)out, part, (int)M, (int)N, (int)K, KT, (int)NP, S);
-  if (M % BM)
-    launch_timed(wq_prefill_kernel<DT, BM, true, FMT, U, BITS>, dim3(gx, 1, (unsigned)S),
-                 dim3(64 * PF_WAVES), 0, stream, (const uint16_t*)x, (const uint8_t*)codes_r,
-                 (const uint8_t*)scales_r, zp, zx, L, (uint16_t*)out, part, (int)M, (int)N,
-                 (int)K, KT, (int)NP, S);
+                 (uint16_t*)out, part, (int)M, (int)N, (int)K, KT, (int)NP, S, 0);
+  if (single || M % BM)
+    launch_timed(wq_prefill_kernel<DT, BM, true, FMT, U, BITS>,
+                 dim3(gx, (unsigned)tail_blocks, (unsigned)S), dim3(64 * PF_WAVES), 0, stream,
+                 (const uint16_t*)x, (const uint8_t*)codes_r, (const uint8_t*)scales_r, zp, zx, L,
+                 (uint16_t*)out, part, (int)M, (int)N, (int)K, KT, (int)NP, S, (int)tail_rb0);
   if (S > 1) {
     const int64_t MN = M * N;
     hipLaunchKernelGGL(split_reduce_kernel<DT>, dim3((unsigned)ceil_div(MN / 4, (int64_t)256)),
@@ -462,20 +468,20 @@ static void launch_prefill_dt(const void* x, const void* codes_r, const void* sc
   const PrefillPlan pl = plan_prefill(M, N, K, ws != nullptr);
   float* part = (float*)ws;
   if (pl.bm == 32)
-    launch_prefill_bm<DT, 32, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
-                                      N, K, stream);
+    launch_prefill_bm<DT, 32, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part,
+                                           pl.splits, pl.single, M, N, K, stream);
   else if (pl.bm == 64)
-    launch_prefill_bm<DT, 64, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
-                                      N, K, stream);
+    launch_prefill_bm<DT, 64, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part,
+                                           pl.splits, pl.single, M, N, K, stream);
   else if (pl.bm == 128)
-    launch_prefill_bm<DT, 128, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
-                                       N, K, stream);
+    launch_prefill_bm<DT, 128, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part,
+                                           pl.splits, pl.single, M, N, K, stream);
   else if (pl.bm == 192)
-    launch_prefill_bm<DT, 192, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
-                                       N, K, stream);
+    launch_prefill_bm<DT, 192, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part,
+                                           pl.splits, pl.single, M, N, K, stream);
   else
-    launch_prefill_bm<DT, 256, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part, pl.splits, M,
-                                       N, K, stream);
+    launch_prefill_bm<DT, 256, FMT, U, BITS>(x, codes_r, scales_r, zeros_r, L, out, part,
+                                           pl.splits, pl.single, M, N, K, stream);
 }
 
 template <int DT, int BITS>

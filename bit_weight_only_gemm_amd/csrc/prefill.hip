@@ -48,28 +48,48 @@ namespace w4a16 {
 // 0.83 of a 256-row one per K tile (measured on MI355X), and the smaller tile
 // can fill a round that 256-row tiles leave partly idle.
 PrefillPlan plan_prefill(int64_t M, int64_t N, int64_t K, bool split_ok) {
-  PrefillPlan pl;
-  pl.bm = M <= 32 ? 32 : M <= 64 ? 64 : (M <= 128 ? 128 : 256);
   const int64_t cols = ceil_div(ceil_div(N, 64), (int64_t)PF_WAVES);
   const int64_t KT = K / 128;
-  auto rounds = [&](int64_t bm, int64_t S) {
+  // Rounds of the grid over 256 CUs (one workgroup each): whole row blocks
+  // and a ragged last one in launches of their own (each a round of its
+  // own), or every row block in one launch of the ragged-tail form.
+  auto rounds = [&](int64_t bm, int64_t S, bool single) {
+    if (single) return (double)ceil_div(ceil_div(M, bm) * cols * S, (int64_t)256);
     const int64_t full = M / bm;
     return (double)(ceil_div(full * cols * S, (int64_t)256) +
                     (M % bm ? ceil_div(cols * S, (int64_t)256) : 0));
   };
-  const double t_tile = 3.4e-6 * pl.bm / 256.0;  // one K tile of a workgroup
-  double best = 0;
-  pl.splits = 1;
-  for (int S = 1; S <= (split_ok ? 16 : 1) && S <= KT; ++S) {
-    double t = rounds(pl.bm, S) * (double)ceil_div(KT, (int64_t)S) * t_tile;
+  // Time of one K tile of a workgroup: 3.4 us with 256 rows (measured on
+  // MI355X); 192 rows take 0.874 of that (their dequantized weights serve
+  // fewer rows), smaller blocks their share of rows; the ragged-tail form
+  // about 2 % more.  A split of K adds its partials' write and read.
+  auto cost = [&](int bm, int64_t S, bool single) {
+    const double t_tile = 3.4e-6 * (bm == 192 ? 0.874 : bm / 256.0) * (single ? 1.02 : 1.0);
+    double t = rounds(bm, S, single) * (double)ceil_div(KT, S) * t_tile;
     if (S > 1) t += (double)(S * 4 + 2) * M * N / 4.0e12 + 2e-6;
-    if (S == 1 || t < best * 0.97) {
-      best = t;
-      pl.splits = S;
-    }
+    return t;
+  };
+  PrefillPlan pl;
+  pl.bm = M <= 32 ? 32 : M <= 64 ? 64 : (M <= 128 ? 128 : 256);
+  pl.splits = 1;
+  pl.single = false;
+  double best = cost(pl.bm, 1, false);
+  // other forms must save 3 %: 256-row blocks (large M), splits of K, the
+  // single ragged-tail launch, 192-row blocks
+  const int bms[2] = {pl.bm, 192};
+  for (int bi = 0; bi < (pl.bm == 256 ? 2 : 1); ++bi) {
+    const int bm = bms[bi];
+    for (int single = 0; single < (M % bm ? 2 : 1); ++single)
+      for (int S = 1; S <= (split_ok ? 16 : 1) && S <= KT; ++S) {
+        const double t = cost(bm, S, single != 0);
+        if (t < best * 0.97) {
+          best = t;
+          pl.bm = bm;
+          pl.splits = S;
+          pl.single = single != 0;
+        }
+      }
   }
-  if (pl.bm == 256 && pl.splits == 1 && rounds(192, 1) * 0.83 < rounds(256, 1) * 0.95)
-    pl.bm = 192;
   return pl;
 }
 

@@ -182,9 +182,14 @@ def test_plan_names_the_dispatch_without_gpu():
     assert _plan(1, 4096, 4096, bits=8, dtype=1) == [dec + "1, 1, 0, 1, false, 8, false>"]
     assert _plan(1, 4096, 4096, G=32) == [dec + "0, 1, 0, 4, false, 4, true>"]
     # prefill: whole row blocks, and a separate launch for a partial last one
-    # (which the planner counts as a round of its own)
-    assert _plan(2048, 5120, 5120, dtype=1) == ["w4a16::wq_prefill_kernel<1, 256, false, 0, 1, 4>"]
-    assert _plan(2100, 5120, 55296, dtype=1)[:2] == [
+    # (which the planner counts as a round of its own), or one launch of the
+    # ragged-tail form over every row block where that fits the CUs in fewer
+    # rounds (5120 x 5120 at M = 2048: 11 x 20 blocks of 192 rows in one
+    # round, against 8 x 20 of 256)
+    assert _plan(2048, 7168, 5120, dtype=1) == ["w4a16::wq_prefill_kernel<1, 256, false, 0, 1, 4>"]
+    assert _plan(2048, 5120, 5120, dtype=1) == ["w4a16::wq_prefill_kernel<1, 192, true, 0, 1, 4>"]
+    assert _plan(2100, 7168, 5120, dtype=1) == ["w4a16::wq_prefill_kernel<1, 256, true, 0, 1, 4>"]
+    assert _plan(2100, 55296, 5120, dtype=1)[:2] == [
         "w4a16::wq_prefill_kernel<1, 256, false, 0, 1, 4>",
         "w4a16::wq_prefill_kernel<1, 256, true, 0, 1, 4>"]
     # the plan's pass agrees with w4a16_workspace_bytes
