@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run each decode call of the workload once, then a 256 MiB device copy "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), and exit")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write %s from the counter CSVs of two --pmc-probe runs under "
+                         "rocprofv3 (--pmc FETCH_SIZE, then --pmc WRITE_SIZE), and exit"
+                         % os.path.join("profiles", "int4_decode_traffic.json"))
     ap.add_argument("--min-rotation-mb", type=float, default=512.0)
     return ap.parse_args()
 
@@ -230,6 +234,9 @@ def main():
     import bit_weight_only_gemm_amd as w4
     from bit_weight_only_gemm_amd import synth, _lib
 
+    if args.traffic_summary:
+        traffic_summary(w4, *args.traffic_summary)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = _lib.load()
@@ -578,6 +585,72 @@ def pmc_probe(L, dev):
     dst.copy_(src)
     torch.cuda.synchronize()
     print("copy bytes_read=%d bytes_written=%d" % (src.numel() * 4, dst.numel() * 4), flush=True)
+
+
+def _counter_rows(d, counter):
+    """(kernel name without 'void ' and the argument list, value) per
+    dispatch, in dispatch order, from rocprofv3's counter CSV under d."""
+    import csv
+    path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    rows = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            name = name[5:] if name.startswith("void ") else name
+            depth, cut = 0, len(name)
+            for i, ch in enumerate(name):      # the argument list: the first '(' outside <>
+                depth += ch == "<"
+                depth -= ch == ">"
+                if ch == "(" and depth == 0:
+                    cut = i
+                    break
+            did = int(r["Dispatch_Id"])
+            rows[did] = (name[:cut], rows.get(did, (None, 0.0))[1] + float(r["Counter_Value"]))
+    return [rows[k] for k in sorted(rows)]
+
+
+def traffic_summary(w4, fetch_dir, write_dir):
+    """HBM bytes per launch of each main kernel of the workload's decode calls
+    (the --pmc-probe sequence: SHAPES x MS once each, then a 256 MiB copy):
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what they read for
+    the copy (its last dispatch), against the calls' algorithmic bytes."""
+    fetch, write = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    copy_bytes = 64 * 2**20 * 4
+    fscale = copy_bytes / (fetch[-1][1] * 1024)
+    wscale = copy_bytes / (write[-1][1] * 1024)
+    kernels, fi, wi = {}, 0, 0
+    for K, N in SHAPES:
+        for M in MS:
+            main = main_kernel(plan(w4, M, N, K, "f16", perm=True))
+            while fetch[fi][0] != main:
+                fi += 1
+            while write[wi][0] != main:
+                wi += 1
+            hbm = fetch[fi][1] * 1024 * fscale + write[wi][1] * 1024 * wscale
+            k = kernels.setdefault(main, {"hbm": [], "alg": []})
+            k["hbm"].append(hbm)
+            k["alg"].append(call_bytes(M, K, N))
+            fi += 1
+            wi += 1
+    out = {"source_hash": kernel_source_hash(),
+           "kernels": {n: {"hbm_bytes_per_launch": round(float(np.mean(v["hbm"]))),
+                           "algorithmic_bytes_per_launch": round(float(np.mean(v["alg"]))),
+                           "launches": len(v["hbm"])} for n, v in kernels.items()},
+           "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+           "calibration": "256 MiB device copy: FETCH_SIZE %d KiB, WRITE_SIZE %d KiB"
+                          % (fetch[-1][1], write[-1][1]),
+           "command": "cd /tmp && export TMPDIR=/tmp; rocprofv3 --pmc FETCH_SIZE "
+                      "--output-format csv -d $REPO/gpurun_out/pmc_fetch -o run -- python3 "
+                      "$REPO/bench.py --pmc-probe; rocprofv3 --pmc WRITE_SIZE --output-format "
+                      "csv -d $REPO/gpurun_out/pmc_write -o run -- python3 $REPO/bench.py "
+                      "--pmc-probe; python3 $REPO/bench.py --traffic-summary "
+                      "$REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write"}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def bench_prefill(L, timer, sptr, M=2048, shapes=PREFILL_SHAPES):
