@@ -237,11 +237,13 @@ int w4a16_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t
  *             group of permuted column k; z = 8 when zeros_r is NULL),
  * with fp32 accumulation and one round-to-nearest-even to the output dtype.
  * Paths that apply s and z after a K tile's sum (M <= 4; 9..16 rows, or
- * 5..16 on layers of more than 4096 columns, with group_size >= 128 in the
- * decode kernel; the large-M kernel's 32-row tiles with group_size >= 128;
- * never 8-bit codes in bf16) compute s * (T - Z) per tile, column and group,
- * T = sum x (o + q) and Z = sum x (o + z) (o = 1024 in fp16, 128 in bf16)
- * from two MFMA chains over the same activations, without rounding w to
+ * 5..16 on layers of more than 4096 columns or with prepared activations,
+ * with group_size >= 128 in the decode kernel; the large-M kernel's 32-row
+ * tiles with group_size >= 128; never 8-bit codes in bf16) compute
+ * s * (T - Z) per tile, column and group, T = sum x (o + q) and
+ * Z = sum x (o + z) (o = 1024 in fp16, or 64 for the high nibble of each byte
+ * of 4-bit codes; 128 in bf16) from two MFMA chains over the same
+ * activations, without rounding w to
  * 16 bits first.  Each product is exact in fp32; with each addition of a
  * chain of n products rounded to fp32 (to nearest or toward zero), the
  * tile's error is at most |s| * 2 n u (2 o + 30) * sum |x| (u = 2^-23; n = 32
