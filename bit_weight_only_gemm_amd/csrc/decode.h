@@ -17,9 +17,17 @@ constexpr int64_t kWideMinN = 16384;    // narrowest layer of the wide packed de
 // Activation modes.  PACKED: M <= 4, one 16-byte load per lane and K tile
 // carries the 4 MFMA steps (rows 4 j + m).  FULL: 16 MT rows, 4 MT loads per
 // tile.  FULLT: FULL with the loads taking whole lines and an LDS transpose
-// to the MFMA layout.  XGATHER: PACKED for an act-order weight, with the M rows of x and
-// the permutation staged in LDS once per workgroup; the operand is gathered
-// from LDS, x[m][perm[k]], so no separate permutation pass runs.  XSTAGED:
+// to the MFMA layout.  XGATHER: PACKED for an act-order weight, with the M
+// rows of x (in their original column order) and the permutation staged in
+// LDS once per workgroup; the loop gathers each operand from LDS,
+// x[m][perm[k]], two tiles ahead of its use (one row: the 4 lanes of a quad,
+// which carry the same inputs, gather 2 of the 8 each and share them by DPP),
+// so neither a permutation pass nor a permute phase before the loop runs.
+// Measured on MI355X against permuting the staged rows in place before the
+// loop, whole calls in a graph, fp16: 11008 x 4096 at M = 4 11.57 -> 10.19
+// us, M = 3 10.57 -> 9.86; 4096 x 11008 at M = 4 10.87 -> 9.98, M = 1 8.49 ->
+// 7.77; 4096 x 4096 at M = 4 6.56 -> 5.56; 11008 x 4096 at M = 1 level (8.07
+// -> 8.14).  XSTAGED:
 // PACKED with the M rows of x staged in LDS and read from there (used with
 // AWQ input scales, below).  With input scales (XS) the staged rows are
 // divided by s in place, once per workgroup, before the loop: each x element
@@ -48,8 +56,9 @@ constexpr bool is_staged(int am) { return am == AM_XGATHER || am == AM_XSTAGED; 
 // workgroups in a CU's 160 KB.
 constexpr int64_t kMaxXlds = 72 * 1024;
 // On a grid of at most 256 workgroups (one per CU anyway) a workgroup may take
-// up to this much LDS for its staged rows, permutation and permuted rows.
-constexpr int64_t kMaxXldsOne = 144 * 1024;
+// up to this much LDS for its staged rows, permutation and input scales (with
+// the 4 KB reduction buffer, within a CU's 160 KB).
+constexpr int64_t kMaxXldsOne = 152 * 1024;
 
 // Multiply-accumulate the 4 MFMA steps of one K tile given its 4 B operands.
 template <int DT, int AM, int MT, int NA, int NACC>
@@ -340,13 +349,16 @@ struct Nf4W {
 // puts into the MFMA layout through LDS.  Rows >= M read 0 through the
 // descriptor range; k >= K (only in a half NF4 tile) uses an out-of-range
 // offset.
-// Staged activations in LDS: x rows [M][K] at xl (XGATHER: permuted in
-// place, chunk c of row m at 2 K m + 16 (c ^ 4 (m & 3))).
+// Staged activations in LDS: x rows [M][K] at xl, row m at m * pitch
+// (XGATHER: the rows in their original column order and the permutation at
+// pl, gathered per operand in the loop).
 // GGATHER: the permutation (when perm) and the input scales in global memory,
 // behind the descriptors rp and rs.  TILED: rt row tiles in the prepared
 // buffer, rt0 the workgroup's first.
 struct XLds {
   const uint8_t* xl;
+  const uint8_t* pl;
+  uint32_t pitch;
   int M;
   rsrc_t rp, rs;
   bool perm;
@@ -358,14 +370,8 @@ __device__ __forceinline__ void load_a(rsrc_t rx, int K, int t, int lane,
                                        typename Op<DT>::vec (&a)[NA], const XLds& xs) {
   typedef typename Op<DT>::vec vec;
   const int r = lane & 15, b = lane >> 4;
-  if constexpr (AM == AM_XGATHER) {
-    // the rows permuted in LDS (see permute_staged); rows m >= M only feed
-    // output rows that are never stored, so they read row M - 1 instead of
-    // zeros (K % 128 == 0: no half tiles)
-    const int j = r >> 2, m = min(r & 3, xs.M - 1);
-    const uint32_t c = (uint32_t)(t * 128 + WP::xk(j, b)) >> 3;
-    a[0] = *(const vec*)(xs.xl + (uint32_t)m * (uint32_t)K * 2u + ((c ^ ((uint32_t)(m & 3) << 2)) << 4));
-  } else if constexpr (AM == AM_GGATHER) {
+  static_assert(AM != AM_XGATHER, "XGATHER operands are gathered by xg_perm / xg_gather");
+  if constexpr (AM == AM_GGATHER) {
     // one row tile: lane row r, 8 inputs of step j per operand; rows past M
     // read 0 through the descriptor range of rx, as does any input of a
     // permutation entry outside the row
@@ -482,20 +488,22 @@ constexpr bool full_fold() {
 __host__ __device__ constexpr uint32_t xpose_bytes(int MT) { return (uint32_t)(DW * MT * 4096); }
 
 // Staged LDS layout, each region rounded up to whole 1 KB blocks: x rows
-// [M][K], then (input scales) s [K].  XGATHER permutes the staged rows once
-// per workgroup, each row in place: chunk c (permuted columns 8c .. 8c + 7)
-// of row m goes to the 16 bytes at 2 K m + 16 (c ^ 4 (m & 3)) (the xor puts
-// the chunks that one operand load takes from the 4 rows in different LDS
-// banks).  The permutation itself is read from memory into registers
-// (kPermRegs chunks of 8 entries per thread), so the gather takes
-// K <= 64 DW 8 kPermRegs.
-constexpr int kPermRegs = 6;
-constexpr int64_t kMaxGatherK = (int64_t)64 * DW * 8 * kPermRegs;
-__host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K) {
-  return (uint32_t)((M * K * 2 + 1023) / 1024 * 1024);
+// [M][K] at a pitch of 2 K bytes (XSTAGED) or 2 K + 32 (XGATHER: the 4 rows
+// that one gather reads for an input sit 8 banks apart), then (input
+// scales) s [K], then (XGATHER) the permutation [K] as int32.  XGATHER keeps
+// the rows in their original column order: the loop gathers each operand
+// from them through the staged permutation (xg_perm, xg_gather).
+__host__ __device__ constexpr uint32_t xlds_pitch(int K, bool perm) {
+  return (uint32_t)(2 * K + (perm ? 32 : 0));
+}
+__host__ __device__ constexpr uint32_t xlds_x_bytes(int M, int K, bool perm) {
+  return (uint32_t)(((int64_t)M * xlds_pitch(K, perm) + 1023) / 1024 * 1024);
 }
 __host__ __device__ constexpr uint32_t xlds_s_bytes(int K, bool xs) {
   return xs ? (uint32_t)((K * 2 + 1023) / 1024 * 1024) : 0u;
+}
+__host__ __device__ constexpr uint32_t xlds_p_bytes(int K, bool perm) {
+  return perm ? (uint32_t)((K * 4 + 1023) / 1024 * 1024) : 0u;
 }
 // what each workgroup reads from memory besides the weights: the rows, the
 // permutation and the input scales
@@ -504,7 +512,7 @@ __host__ __device__ constexpr uint32_t xlds_staged_bytes(int M, int K, bool perm
 }
 // the LDS footprint
 __host__ __device__ constexpr uint32_t xlds_bytes(int M, int K, bool perm, bool xs) {
-  return (void)perm, xlds_x_bytes(M, K) + xlds_s_bytes(K, xs);
+  return xlds_x_bytes(M, K, perm) + xlds_s_bytes(K, xs) + xlds_p_bytes(K, perm);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's data lands at
@@ -524,6 +532,21 @@ __device__ __forceinline__ void stage_lds(const void* src, uint32_t bytes, uint8
     lds_dma16(r, lds + blk * 1024, (uint32_t)(blk * 1024 + lane * 16), 0);
 }
 
+// Copy exactly `bytes` (a multiple of 256) from offset `off` of r to LDS: whole
+// 1 KB blocks by 16-byte lanes, the rest by 4-byte lanes (256 bytes per wave
+// instruction), so nothing past the span is written.
+__device__ __forceinline__ void stage_exact(rsrc_t r, uint32_t off, uint32_t bytes, uint8_t* lds,
+                                            int wave, int lane) {
+  const int nk = (int)(bytes >> 10);
+  for (int blk = wave; blk < nk; blk += DW)
+    lds_dma16(r, lds + blk * 1024, off + (uint32_t)(blk * 1024 + lane * 16), 0);
+  const int nq = (int)((bytes & 1023u) >> 8);
+  if (wave < nq)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(lds + nk * 1024 + wave * 256), 4,
+        off + (uint32_t)(nk * 1024 + wave * 256 + lane * 4), 0, 0, 0);
+}
+
 // A workgroup barrier for LDS data: this wave's LDS writes (and LDS DMA) are
 // complete before it, other waves' are visible after it; loads from global
 // memory in flight are not waited for.
@@ -533,54 +556,60 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// XGATHER: the permutation chunks of this thread (chunk c = entries
-// 8c .. 8c + 7, c = thread + i 64 DW), loaded from memory before the rows
-// are staged; chunks past K read 0 and are not used.
-__device__ __forceinline__ void load_perm_chunks(const int32_t* perm, int K,
-                                                 u32x4_t (&pr)[kPermRegs][2]) {
-  const rsrc_t rp = make_rsrc(perm, (uint32_t)K * 4u);
+// XGATHER: the 8 permutation entries of this lane's operand of tile t (inputs
+// 128 t + 32 j + 8 b .. + 7 of A row 4 j + m, lane group b), from the staged
+// permutation.
+template <class WP>
+__device__ __forceinline__ void xg_perm(const XLds& xs, int t, int lane, u32x4_t (&pq)[2]) {
+  const int j = (lane & 15) >> 2, b = lane >> 4;
+  const uint8_t* pp = xs.pl + (uint32_t)(t * 128 + WP::xk(j, b)) * 4u;
+  pq[0] = *(const u32x4_t*)pp;
+  pq[1] = *(const u32x4_t*)(pp + 16);
+}
+// ... and the operand itself, x[m][perm[k]] for those 8 inputs, gathered from
+// the staged row (rows m >= M only feed output rows that are never stored,
+// so they read row M - 1).
+template <int DT>
+__device__ __forceinline__ typename Op<DT>::vec xg_gather(const XLds& xs, int lane,
+                                                          const u32x4_t (&pq)[2]) {
+  const uint8_t* rb = xs.xl + (uint32_t)min(lane & 3, xs.M - 1) * xs.pitch;
+  // (16-bit values as pairs built from two loads: the odd one loads into the
+  // high half in place)
+  u32x4_t w;
 #pragma unroll
-  for (int i = 0; i < kPermRegs; ++i) {
-    const uint32_t c = threadIdx.x + (uint32_t)(i * 64 * DW);
-    pr[i][0] = bld128(rp, c * 32u, 0);
-    pr[i][1] = bld128(rp, c * 32u + 16u, 0);
+  for (int q = 0; q < 4; ++q) {
+    half2_t h;
+    h[0] = *(const _Float16*)(rb + pq[q >> 1][2 * (q & 1)] * 2u);
+    h[1] = *(const _Float16*)(rb + pq[q >> 1][2 * (q & 1) + 1] * 2u);
+    w[q] = __builtin_bit_cast(uint32_t, h);
   }
+  return __builtin_bit_cast(typename Op<DT>::vec, w);
 }
 
-// XGATHER: the staged rows permuted once per workgroup, in place, x_p[m][k]
-// = x[m][perm[k]], into the layout the loop reads: row by row, each thread
-// gathers its chunks of the row from LDS into registers, then (after a
-// barrier: every read of the row is done) writes them over the row.
-__device__ __forceinline__ void permute_staged(const XLds& xs, int K,
-                                               const u32x4_t (&pr)[kPermRegs][2]) {
-  const int nch = K >> 3;
-  const int nit = (nch + 64 * DW - 1) / (64 * DW);  // passes over the workgroup's threads
-  for (int m = 0; m < xs.M; ++m) {
-    uint8_t* row = const_cast<uint8_t*>(xs.xl) + (uint32_t)m * (uint32_t)K * 2u;
-    // (the workgroup's last pass may hold chunks past K: entries 0, gathered
-    // from column 0 and never written)
-    u32x4_t w[kPermRegs];
-#pragma unroll
-    for (int i = 0; i < kPermRegs; ++i) {
-      if (i >= nit) break;  // workgroup-uniform
-      uint32_t v[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = *(const uint16_t*)(row + pr[i][0][e] * 2u);
-        v[4 + e] = *(const uint16_t*)(row + pr[i][1][e] * 2u);
-      }
-      w[i] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                     v[6] | (v[7] << 16)};
-    }
-    lds_barrier();
-    const uint32_t sw = (uint32_t)(m & 3) << 2;
-#pragma unroll
-    for (int i = 0; i < kPermRegs; ++i) {
-      if (i >= nit) break;
-      const int c = threadIdx.x + i * 64 * DW;
-      if (c < nch) *(u32x4_t*)(row + (((uint32_t)c ^ sw) << 4)) = w[i];
-    }
-  }
+// The same for one batch row (M == 1), shared by the 4 lanes of a quad (lane
+// bits 0-1, which hold the 4 rows of A that only that row feeds): lane q of
+// the quad gathers inputs 2q and 2q + 1 of the 8 (xg_perm1, xg_gather1) and
+// the operand is assembled at its use from the quad's 4 pairs by DPP
+// broadcasts (xg_assemble1).
+template <class WP>
+__device__ __forceinline__ u32x2_t xg_perm1(const XLds& xs, int t, int lane) {
+  const int j = (lane & 15) >> 2, b = lane >> 4;
+  return *(const u32x2_t*)(xs.pl + (uint32_t)(t * 128 + WP::xk(j, b) + 2 * (lane & 3)) * 4u);
+}
+__device__ __forceinline__ uint32_t xg_gather1(const XLds& xs, u32x2_t p) {
+  half2_t h;
+  h[0] = *(const _Float16*)(xs.xl + p[0] * 2u);
+  h[1] = *(const _Float16*)(xs.xl + p[1] * 2u);
+  return __builtin_bit_cast(uint32_t, h);
+}
+template <int DT>
+__device__ __forceinline__ typename Op<DT>::vec xg_assemble1(uint32_t d) {
+  // quad_perm [q, q, q, q]: every lane of the quad takes lane q's pair
+  const u32x4_t w = {(uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0x00, 0xF, 0xF, false),
+                     (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0x55, 0xF, 0xF, false),
+                     (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0xAA, 0xF, 0xF, false),
+                     (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0xFF, 0xF, 0xF, false)};
+  return __builtin_bit_cast(typename Op<DT>::vec, w);
 }
 
 // XS: divide the staged activations by the AWQ input scales xsc [K] (staged
@@ -600,7 +629,9 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   static_assert(AM != AM_XSTAGED || XS, "rows are staged for input scales");
   constexpr int NA = is_packed(AM) ? 1 : MT * 4;                   // A vectors per tile
   constexpr int NACC = is_packed(AM) ? 4 : MT * (MT == 1 ? 4 : (MT == 2 ? 2 : 1));  // acc tiles
-  constexpr int PA = is_packed(AM) ? RUN : (MT == 1 ? 2 : 1);      // A ring depth
+  // A ring depth (XGATHER: operands gathered two tiles ahead, their
+  // permutation entries read one tile before that)
+  constexpr int PA = AM == AM_XGATHER ? 2 : (is_packed(AM) ? RUN : (MT == 1 ? 2 : 1));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ct = blockIdx.x;
@@ -657,20 +688,30 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   typename WP::CodeT ring[RUN];
   typename Op<DT>::vec ra[PA][NA];
   typename WP::Meta mc, mn = WP::zero_meta();
-  XLds xs{xlds, M, make_rsrc(perm, 0u), make_rsrc(xsc, 0u), perm != nullptr, rtiles,
+  constexpr bool XG = AM == AM_XGATHER;
+  XLds xs{xlds, xlds + xlds_x_bytes(M, K, XG) + xlds_s_bytes(K, XS), xlds_pitch(K, XG), M,
+          make_rsrc(perm, 0u), make_rsrc(xsc, 0u), perm != nullptr, rtiles,
           (int)blockIdx.y * MT};
   if constexpr (AM == AM_GGATHER) {
     xs.rp = make_rsrc(perm, perm ? (uint32_t)K * 4u : 0u);
     xs.rs = make_rsrc(xsc, XS ? (uint32_t)K * 2u : 0u);
   }
-  // Staged modes: the permutation chunks (into registers) and the LDS DMA of
-  // the rows (and input scales) go out before the first code tiles, so the
-  // staging barrier waits only for them while the tiles stay in flight.
-  u32x4_t pr[AM == AM_XGATHER ? kPermRegs : 1][2];
-  if constexpr (AM == AM_XGATHER) load_perm_chunks(perm, K, pr);
-  if constexpr (is_staged(AM)) {
+  // Staged modes: the LDS DMA of the rows (and input scales, and the
+  // permutation) goes out before the first code tiles, so the staging
+  // barrier waits only for it while the tiles stay in flight.
+  if constexpr (XG) {
+    const rsrc_t rxa = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    for (int m = 0; m < M; ++m)
+      stage_exact(rxa, (uint32_t)m * (uint32_t)K * 2u, (uint32_t)K * 2u, xlds + m * xs.pitch, wave,
+                  lane);
+    if constexpr (XS)
+      stage_exact(make_rsrc(xsc, (uint32_t)K * 2u), 0u, (uint32_t)K * 2u,
+                  xlds + xlds_x_bytes(M, K, true), wave, lane);
+    stage_exact(make_rsrc(perm, (uint32_t)K * 4u), 0u, (uint32_t)K * 4u, const_cast<uint8_t*>(xs.pl),
+                wave, lane);
+  } else if constexpr (is_staged(AM)) {
     stage_lds(x, (uint32_t)(M * K * 2), xlds, wave, lane);
-    if constexpr (XS) stage_lds(xsc, (uint32_t)(K * 2), xlds + xlds_x_bytes(M, K), wave, lane);
+    if constexpr (XS) stage_lds(xsc, (uint32_t)(K * 2), xlds + xlds_x_bytes(M, K, false), wave, lane);
   }
   // (staged: unconditional, a wave without tiles reading its first tile, so
   // that the staging barrier's wait counts the same loads on every path)
@@ -686,29 +727,44 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
     if constexpr (XS) {
       // x[m][k] / s[k] in place (original column order): a pair of columns per
       // step, their reciprocals shared by the M rows
-      uint32_t* xw = (uint32_t*)xlds;
-      const uint32_t* sw = (const uint32_t*)(xlds + xlds_x_bytes(M, K));
+      const uint32_t* sw = (const uint32_t*)(xlds + xlds_x_bytes(M, K, XG));
       const int half = K >> 1;
       for (int kp = threadIdx.x; kp < half; kp += 64 * DW) {
         const uint32_t sv = sw[kp];
         const float r0 = recip_scale<DT>((uint16_t)(sv & 0xFFFFu));
         const float r1 = recip_scale<DT>((uint16_t)(sv >> 16));
         for (int m = 0; m < M; ++m) {
-          const uint32_t v = xw[m * half + kp];
-          xw[m * half + kp] = (uint32_t)mul_round16<DT>((uint16_t)(v & 0xFFFFu), r0) |
-                              ((uint32_t)mul_round16<DT>((uint16_t)(v >> 16), r1) << 16);
+          uint32_t* xw = (uint32_t*)(xlds + m * xs.pitch) + kp;
+          const uint32_t v = *xw;
+          *xw = (uint32_t)mul_round16<DT>((uint16_t)(v & 0xFFFFu), r0) |
+                ((uint32_t)mul_round16<DT>((uint16_t)(v >> 16), r1) << 16);
         }
       }
       lds_barrier();
     }
-    if constexpr (AM == AM_XGATHER) {
-      permute_staged(xs, K, pr);
-      lds_barrier();
-    }
   }
+  u32x4_t pq[2];   // XGATHER: permutation entries of the next operand to gather
+  u32x2_t pq1;     // (one row: this lane's 2 of them)
+  uint32_t g1[PA];  // (one row: this lane's gathered pair per ring slot)
   if (n > 0) {
+    if constexpr (XG && ONE) {
+      pq1 = xg_perm1<WP>(xs, t0, lane);
 #pragma unroll
-    for (int s = 0; s < PA; ++s) load_a<DT, AM, MT, NA, WP, XS>(rx, K, t0 + min(s, n - 1), lane, ra[s], xs);
+      for (int s = 0; s < PA; ++s) {
+        g1[s] = xg_gather1(xs, pq1);
+        pq1 = xg_perm1<WP>(xs, t0 + min(s + 1, n - 1), lane);
+      }
+    } else if constexpr (XG) {
+      xg_perm<WP>(xs, t0, lane, pq);
+#pragma unroll
+      for (int s = 0; s < PA; ++s) {
+        ra[s][0] = xg_gather<DT>(xs, lane, pq);
+        xg_perm<WP>(xs, t0 + min(s + 1, n - 1), lane, pq);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < PA; ++s) load_a<DT, AM, MT, NA, WP, XS>(rx, K, t0 + min(s, n - 1), lane, ra[s], xs);
+    }
     for (int i = 0; i < n; i += RUN) {
       mc = mn;
       mn = wp.load_meta(r0 + min(i / RUN + 1, (n - 1) / RUN));
@@ -719,6 +775,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
           typename Op<DT>::vec b[4];
           if constexpr (FOLD) {
             const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (XG && ONE) ra[sa][0] = xg_assemble1<DT>(g1[sa]);
             wp.raw_operands(ring[s], b);
             float4_t at[4];
 #pragma unroll
@@ -777,7 +834,16 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
         }
         __builtin_amdgcn_sched_barrier(0);
         ring[s] = wp.load_codes(t0 + min(i + s + RUN, n - 1), lane);
-        load_a<DT, AM, MT, NA, WP, XS>(rx, K, t0 + min(i + s + PA, n - 1), lane, ra[sa], xs);
+        if constexpr (XG && ONE) {
+          g1[sa] = xg_gather1(xs, pq1);
+          pq1 = xg_perm1<WP>(xs, t0 + min(i + s + PA + 1, n - 1), lane);
+        } else if constexpr (XG) {
+          // pq holds the entries of tile i + s + PA (clamped)
+          ra[sa][0] = xg_gather<DT>(xs, lane, pq);
+          xg_perm<WP>(xs, t0 + min(i + s + PA + 1, n - 1), lane, pq);
+        } else {
+          load_a<DT, AM, MT, NA, WP, XS>(rx, K, t0 + min(i + s + PA, n - 1), lane, ra[sa], xs);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -881,7 +947,7 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   const int n = min(KT, r1 * RUN) - t0;  // tiles of this wave (wave-uniform)
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
-  const XLds none{nullptr, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, 0, 0};
+  const XLds none{nullptr, nullptr, 0u, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, 0, 0};
   const bool g0 = lane & 16, g1 = lane & 32;
 
   float4_t yf[NC];
@@ -1039,10 +1105,10 @@ static void allow_dynamic_lds(const void* kernel) {
 // beats a separate preparation pass: every workgroup copies the rows (and the
 // permutation and scales) from L2, so the cost grows with the grid, while the
 // pass costs about one launch.  Measured on MI355X, whole calls in a graph,
-// with the rows' DMA ahead of the code tiles: staging saves 0.9 - 1.8 us on
-// 4096 x 11008 at 2 - 4 rows (688 workgroups x up to 48 KB, 33 MB) and 1.7 us
-// on 11008 x 4096 at 2 rows; it cost ~10 us on 5120 x 55296 layers (3456
-// workgroups) with the earlier staging.
+// with the rows' DMA ahead of the code tiles and the rows permuted in place
+// before the loop: staging saved 0.9 - 1.8 us on 4096 x 11008 at 2 - 4 rows
+// (688 workgroups x up to 48 KB, 33 MB) and 1.7 us on 11008 x 4096 at 2 rows;
+// it cost ~10 us on 5120 x 55296 layers (3456 workgroups).
 constexpr int64_t kMaxStagedTotal = (int64_t)40 << 20;
 
 // Activation mode and row tiles per workgroup row block for M rows of a
@@ -1064,7 +1130,7 @@ static int pick_mode(int64_t M, int64_t N, int64_t K, bool gather, bool xs, int*
     const int64_t lds = xlds_bytes((int)M, (int)K, gather, xs);
     const int64_t staged = xlds_staged_bytes((int)M, (int)K, gather, xs);
     if ((gather || xs) && lds <= (wgs <= 256 ? kMaxXldsOne : kMaxXlds) &&
-        wgs * staged <= kMaxStagedTotal && (!gather || K <= kMaxGatherK))
+        wgs * staged <= kMaxStagedTotal)
       return gather ? AM_XGATHER : AM_XSTAGED;
     return AM_PACKED;
   }

@@ -148,9 +148,10 @@ prep_tiled_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ pe
 // bound, and more workgroups per row (each staging the row) run it on more
 // CUs (measured on MI355X, 11008 inputs at M = 4 and 16, whole calls in a
 // graph: 6 chunks per thread, one workgroup per row, 1.7 us slower).
+constexpr int64_t kMaxPrepLds = 144 * 1024;
 inline bool prep_rows_fits(int64_t K, bool xs) {
   const int64_t rowb = ceil_div(K * 2, 1024) * 1024;
-  return rowb * (xs ? 2 : 1) <= kMaxXldsOne;
+  return rowb * (xs ? 2 : 1) <= kMaxPrepLds;
 }
 
 template <bool TILED>

@@ -92,18 +92,19 @@ def test_gemm_validation_without_gpu():
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 4096, 4096, 0, FAKE, need - 16, NULL) == 5
     # the size covers every call at a shape, with or without a permutation and
     # AWQ input scales: M <= 4 rows that the decode kernel stages on chip need
-    # no workspace (rows + scales up to 144 KB per workgroup on grids of at
-    # most 256 workgroups, else 72 KB; staged bytes, permutation included, up
-    # to 40 MiB over the grid; K <= 12288 with a permutation) ...
+    # no workspace (rows, scales and permutation up to 152 KB per workgroup
+    # on grids of at most 256 workgroups, else 72 KB; staged bytes up to
+    # 40 MiB over the grid) ...
     assert L.w4a16_workspace_bytes(1, 4096, 4096, 128) == 0
     assert L.w4a16_workspace_bytes(4, 4096, 4096, 128) == 0
     assert L.w4a16_workspace_bytes(1, 4096, 11008, 128) == 0      # 256 x 44 KB
-    assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) == 0      # 256 x 110 KB, 39 MB staged
+    assert L.w4a16_workspace_bytes(4, 4096, 11008, 128) == 0      # 256 x 152 KB, 39 MB staged
+    assert L.w4a16_workspace_bytes(1, 4096, 16384, 128) == 0      # 256 x 129 KB
     assert L.w4a16_workspace_bytes(4, 6144, 5120, 128) == 0       # 384 x 50 KB
     # ... other ones are prepared in a pass: M * K * 2 bytes (up to 4 rows)
     assert L.w4a16_workspace_bytes(4, 6144, 8192, 128) >= 4 * 8192 * 2    # 384 x 80 KB
     assert L.w4a16_workspace_bytes(1, 55296, 5120, 128) >= 5120 * 2       # 3456 x 40 KB staged
-    assert L.w4a16_workspace_bytes(1, 4096, 16384, 128) >= 16384 * 2      # K > 12288
+    assert L.w4a16_workspace_bytes(1, 4096, 24576, 128) >= 24576 * 2      # 193 KB
     # ... and from 5 rows in whole row tiles of 16 (the operand layout)
     assert L.w4a16_workspace_bytes(5, 4096, 4096, 128) >= 16 * 4096 * 2
     # w4a16_gemm_xscale validates what the call needs (each case below fails
@@ -153,10 +154,11 @@ def _plan(M, N, K, G=128, bits=4, dtype=0, perm=0, xs=0, ws=1):
 def test_plan_names_the_dispatch_without_gpu():
     dec = "w4a16::intb_decode_kernel<"
     # act-order decode: the in-kernel gather at 1 and 4 rows on the Llama
-    # layers, a row-staged permutation pass at M = 4 past 12288 inputs, and at
-    # M = 16 a pass into the operand layout (mode 6) feeding the
-    # fold; without a permutation M = 16 takes the transposed rows (mode 4);
-    # past 12288 inputs the passes without row staging
+    # layers, a row-staged permutation pass at M = 4 where the rows and the
+    # permutation outgrow LDS (16384 inputs), and at M = 16 a pass into the
+    # operand layout (mode 6) feeding the fold; without a permutation M = 16
+    # takes the transposed rows (mode 4); past 73728 inputs the passes
+    # without row staging
     assert _plan(1, 4096, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, true>"]
     assert _plan(4, 11008, 4096, perm=1) == [dec + "0, 1, 2, 1, false, 4, false>"]
     assert _plan(4, 4096, 11008, perm=1) == [dec + "0, 1, 2, 1, false, 4, false>"]

@@ -62,9 +62,13 @@ def test_prepared_activations_match_oracle(M, N, K, act, xs, dtype, pass_name):
 
 
 # (M, K, input scales, dtype): 1-4 rows gathered and scaled on chip by the
-# decode kernel itself, each row permuted in place in LDS
+# decode kernel itself, the rows and the permutation staged in LDS and each
+# operand gathered in the loop (one row: a quad's lanes gather 2 inputs each
+# and share them), up to what LDS holds (4 rows of 12288 inputs with the
+# permutation; 4 rows of 11008 with the permutation and input scales)
 STAGED = [(1, 11008, False, "f16"), (2, 11008, True, "bf16"), (3, 11008, False, "bf16"),
-          (4, 11008, True, "f16"), (4, 12288, False, "f16"), (3, 4096, True, "f16")]
+          (4, 11008, True, "f16"), (4, 12288, False, "f16"), (3, 4096, True, "f16"),
+          (1, 16384, False, "bf16"), (1, 4096, True, "bf16"), (2, 16384, False, "f16")]
 
 
 @pytest.mark.parametrize("M,K,xs,dtype", STAGED)

@@ -22,7 +22,7 @@ TDT = {"f16": torch.float16, "bf16": torch.bfloat16}
 def _one(tag, M, N, K, act, dtype):
     plan = w4.w4a16_gemm_plan(M, N, K, dtype=TDT[dtype], perm=act)
     say("noalloc", tag, M, N, K, act, dtype, plan)
-    assert "prep_x_kernel" in plan[0] or plan[-1].startswith("w4a16::split_reduce_kernel")
+    assert plan[0].startswith("w4a16::prep_") or plan[-1].startswith("w4a16::split_reduce_kernel")
     W, gi, _ = int4_inputs(tag, N, K, act_order=act)
     _, packed = gpu_int4_pack(W, gi)
     xb = synth.to_bits(synth.activations(tag + "/x", M, K), dtype)
