@@ -221,6 +221,44 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
               TAIL ? tb * 256 : (int)((uint32_t)i * astride) + tb * 256);
   __syncthreads();
 
+  // B operand of step s for column group g from the weight slot (cwx, scx,
+  // zzx) of a K tile whose first meta unit is zero field zbx (NF4: a' = apx):
+  // word j = s >> 1 of the tile, in meta unit j U / 4.  The unit's dequant
+  // parameters are formed at the step (a few VALU instructions between MFMAs);
+  // formed once per tile and held across it they made the small-M launches of
+  // this kernel markedly slower.
+  auto operand_of = [&](int s, int g, const CT (&cwx)[2][2], const u32x2_t (&scx)[2],
+                        const uint32_t (&zzx)[2], int zbx, float apx) -> vec {
+    if constexpr (FOLD) {
+      return dequant_step<DT, false>(cwx[g][s & 1], s >> 1, rq);
+    } else if constexpr (FMT == FMT_INT4) {
+      const int u = (s >> 1) * U / 4;
+      QParam<DT> q;
+      q.template set<BITS == 4>((scx[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
+                                ((zzx[g] ^ zx) >> (kZW * (zbx + u))) & ((1u << kZW) - 1u));
+      return dequant_step<DT, false>(cwx[g][s & 1], s >> 1, q);
+    } else {
+      return nf4_operand<DT>(cwx[g][s >> 2].w[s & 3], lut, apx);
+    }
+  };
+  auto zb_of = [&](int t) { return ((t & 7) * U) % (32 / kZW); };  // zero field of tile t's first unit
+  auto ap_of = [&](const u32x2_t (&scx)[2], const uint32_t (&zzx)[2], int g) {
+    return (float)(scx[g][0] & 0xFFu) * __builtin_bit_cast(float, zzx[g]);
+  };
+  // XPIPE (the two-stage tile loop): the step-0 B operands of tile t + 1 are
+  // dequantized during step 7 of tile t, between its MFMAs, and carried across
+  // the barrier in bcar, so a tile starts with its MFMAs instead of a dequant
+  // that nothing overlaps (per-tile timestamps on MI355X, 256 rows: 0.5 of
+  // 3.0 us went to that preamble).
+  constexpr bool XPIPE = !DEEP;
+  vec bcar[2];
+  if constexpr (XPIPE) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      bcar[g] = operand_of(0, g, cw[0], sc[0], zz[0], zb_of(tb),
+                           FMT == FMT_NF4 ? ap_of(sc[0], zz[0], g) : 0.f);
+  }
+
   // One K tile: compute tile t from the weight slot (cwc, scc, zzc) while the
   // weights of tile t + 1 (t + 2 when DEEP) are loaded into (cwn, scn, zzn).
   auto tile = [&](const int t, CT (&cwc)[2][2], u32x2_t (&scc)[2], uint32_t (&zzc)[2],
@@ -240,13 +278,11 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < 2; ++g) load_w(min(t + 2, te - 1), g, cwn[g], scn[g], zzn[g]);
-    } else {
-#pragma unroll
-      for (int g = 0; g < 2; ++g) load_w(tn, g, cwn[g], scn[g], zzn[g]);
     }
-    // otherwise the activation loads of tile t + 1 are spread over the first
-    // PF_DMA_STEPS steps of tile t (a burst of them stalls the issuing waves
-    // behind the address queue)
+    // otherwise the weights of tile t + 1 are loaded in step 0 and its
+    // activation loads spread over the first PF_DMA_STEPS steps of tile t, each
+    // load between two MFMAs (a burst of them at the start of the tile stalls
+    // the issuing wave behind the address queue while the matrix pipe idles)
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- K tile t from LDS stage t & 1: 8 steps of 16 inputs.  Per step the
@@ -254,10 +290,10 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
     // spread between the step's MFMAs (each 32 x 32 x 16 MFMA keeps the matrix
     // pipe busy long enough to issue several VALU instructions behind it).
     float ap[2];  // NF4: a' of this lane's block
-    const int zb = ((t & 7) * U) % (32 / kZW);  // zero field of the tile's first unit
+    const int zb = zb_of(t);
     if constexpr (FMT == FMT_NF4) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g) ap[g] = (float)(scc[g][0] & 0xFFu) * __builtin_bit_cast(float, zzc[g]);
+      for (int g = 0; g < 2; ++g) ap[g] = ap_of(scc, zzc, g);
     }
     vec bz[2];  // FOLD: the zero operand (o + z) of each column group
     if constexpr (FOLD) {
@@ -265,22 +301,8 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       for (int g = 0; g < 2; ++g)
         bz[g] = rq.template zero_operand<BITS>(((zzc[g] ^ zx) >> (kZW * zb)) & ((1u << kZW) - 1u));
     }
-    // B operand of step s for column group g: word j = s >> 1 of the tile, in
-    // meta unit j U / 4.  The unit's dequant parameters are formed at the step
-    // (a few VALU instructions between MFMAs); formed once per tile and held
-    // across it they made the small-M launches of this kernel markedly slower.
     auto operand = [&](int s, int g) -> vec {
-      if constexpr (FOLD) {
-        return dequant_step<DT, false>(cwc[g][s & 1], s >> 1, rq);
-      } else if constexpr (FMT == FMT_INT4) {
-        const int u = (s >> 1) * U / 4;
-        QParam<DT> q;
-        q.template set<BITS == 4>((scc[g][u >> 1] >> (16 * (u & 1))) & 0xFFFFu,
-                                  ((zzc[g] ^ zx) >> (kZW * (zb + u))) & ((1u << kZW) - 1u));
-        return dequant_step<DT, false>(cwc[g][s & 1], s >> 1, q);
-      } else {
-        return nf4_operand<DT>(cwc[g][s >> 2].w[s & 3], lut, ap[g]);
-      }
+      return operand_of(s, g, cwc, scc, zzc, zb, FMT == FMT_NF4 ? ap[g] : 0.f);
     };
     const uint8_t* st = As + ((t - tb) & 1) * PF_STAGE;
     auto read_step = [&](int s, vec (&a)[PF_MT]) {
@@ -292,7 +314,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
     };
     vec b[2], a[PF_MT];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) b[g] = operand(0, g);
+    for (int g = 0; g < 2; ++g) b[g] = XPIPE ? bcar[g] : operand(0, g);
     read_step(0, a);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -303,12 +325,24 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       if constexpr (!DEEP) {
 #pragma unroll
         for (int i = i0; i < i1 && i < PF_ALD; ++i) issue_dma(i);
+        if (s == 0) {
+#pragma unroll
+          for (int g = 0; g < 2; ++g) load_w(tn, g, cwn[g], scn[g], zzn[g]);
+        }
       }
+      // memory loads of this step, one after each of the first MFMAs
+      const int nvm = (i0 < PF_ALD ? min(i1, PF_ALD) - i0 : 0) + (!DEEP && s == 0 ? kW : 0);
       if (s < 7) {
         const int sn1 = s + 1;
         read_step(sn1, an);
 #pragma unroll
         for (int g = 0; g < 2; ++g) bn[g] = operand(sn1, g);
+      } else if constexpr (XPIPE) {
+        // step 0 of tile t + 1 (on the last tile: a re-read of it, unused)
+        const int zbn = zb_of(t + 1);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+          bn[g] = operand_of(0, g, cwn, scn, zzn, zbn, FMT == FMT_NF4 ? ap_of(scn, zzn, g) : 0.f);
       }
       if constexpr (FOLD) {
 #pragma unroll
@@ -325,13 +359,13 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
 #pragma unroll
           for (int g = 0; g < 2; ++g) acc[m][g] = mfma32x32x16<DT>(a[m], b[g], acc[m][g]);
       }
-      if (s < 7) {
+      if (s < 7 || XPIPE) {
 #pragma unroll
         for (int k = 0; k < (FOLD ? 4 : 2) * PF_MT; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          if (!DEEP && k < i1 - i0 && i0 < PF_ALD)
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one activation load
-          if (k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          if (!DEEP && k < nvm)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one memory load
+          if (s < 7 && k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
         }
       }
@@ -341,6 +375,9 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
         for (int g = 0; g < 2; ++g) b[g] = bn[g];
 #pragma unroll
         for (int m = 0; m < PF_MT; ++m) a[m] = an[m];
+      } else if constexpr (XPIPE) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) bcar[g] = bn[g];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
