@@ -365,7 +365,11 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
           if (!DEEP && k < nvm)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one memory load
-          if (s < 7 && k < PF_MT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          // the next step's operand reads early, 4 after each of the first
+          // MFMAs, so they have landed when that step starts (one read per
+          // MFMA left the last ones in flight there: whole calls at M = 2048
+          // 1-3 % slower on MI355X)
+          if (s < 7 && k < (PF_MT + 3) / 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
         }
       }
