@@ -206,8 +206,9 @@ int w4a16_repack(const int32_t* qweight, const uint16_t* scales, const int32_t* 
  * weights and more with N < 5120) when it splits K over S workgroups.  A
  * given call may need less, or nothing: no pass runs where
  * the decode kernel gathers x[:, perm] and/or divides by s itself (M <= 4,
- * the rows, the permutation and the scales staged on chip: at most 72 KB per
- * workgroup and 17 MiB over its grid of N/16 workgroups).
+ * the rows, the permutation and the scales staged on chip: at most 152 KB per
+ * workgroup on grids of at most 256 workgroups, else 72 KB, and 40 MiB over
+ * its grid of N/16 workgroups).
  * A workspace is optional on every call (see w4a16_gemm).  -1 on bad input.
  * Calls that overlap in time must not share a workspace.
  */
@@ -254,7 +255,8 @@ int w4a16_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t group_size, int32_t
  * identical inputs); a row with one nonzero x, a power of two, gives
  * round_dtype(w).
  *   x      [M, K] row-major, dtype;  out [M, N] row-major, dtype.
- *   perm   int32 [K] from w4a16_repack (or NULL for identity).
+ *   perm   int32 [K] from w4a16_repack (or NULL for identity): a
+ *          permutation of 0 .. K-1; other entries give unspecified outputs.
  *   codes_r, scales_r, zeros_r from w4a16_repack with the same group_size
  *          (zeros_r NULL: a symmetric weight).
  *   dtype  W4A16_F16 or W4A16_BF16 (activations and output).
