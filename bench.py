@@ -529,9 +529,9 @@ def bench_unfused(w4, rot, xs, stream, fused_step_s):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "int4_decode_traffic.json")
+# the translation unit of the decode kernels and what it includes
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_weight_only_gemm_amd", "csrc", f)
-                  for f in ("gemm.hip", "decode.h", "common.h", "kernels.h", "prefill.h",
-                            "prefill.hip")]
+                  for f in ("gemm.hip", "decode.h", "common.h", "kernels.h", "launch.h")]
 
 
 def kernel_source_hash():
