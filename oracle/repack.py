@@ -284,3 +284,49 @@ def unrepack_ref_bits(codes_r, scales_r, zeros_r, K, N, bits, group_size=GROUP):
         zu = zf.transpose(1, 4, 5, 0, 2, 3).reshape(KT8 * 8 * U, NP * 64)[:KT * U, :N]
         z = from_units(zu)
     return q.copy(), s.copy(), z
+
+
+# ---- NF4 codes in the same 1 KB tiles (test infrastructure only).
+#
+# NF4 weights keep their canonical scales (absmax_q, absmax_scale); only the
+# codes are re-laid, once, into tiles of 16 output rows x 128 inputs, so that a
+# wavefront reads a tile as one contiguous 1 KB block instead of 16 rows of
+# 64 bytes at the row pitch (the point of [P5] "关键数据解读" item 4: layout is
+# translated once, offline, never per run).  With KT = ceil(K / 128):
+#
+# * codes_r uint8 [N / 16][KT][64][16]; entry [c][t][l][j] is byte
+#   64 t + 16 (l >> 4) + j of canonical row 16 c + (l & 15) (that row's codes
+#   of inputs 128 t + 32 (l >> 4) + 2 j and + 1, low nibble first), 0 past the
+#   row's K / 2 bytes.
+
+def repack_nf4_ref(qweight, N, K):
+    """qweight uint8 [N, K/2] (canonical NF4 packing) -> codes_r (flat uint8)."""
+    assert N % 16 == 0 and K % 64 == 0
+    KT = (K + TILE - 1) // TILE
+    rows_bytes = K // 2
+    out = np.zeros((N // 16, KT, 64, 16), dtype=np.uint8)
+    for c in range(N // 16):
+        for t in range(KT):
+            for l in range(64):
+                row = 16 * c + (l & 15)
+                b0 = 64 * t + 16 * (l >> 4)
+                for j in range(16):
+                    if b0 + j < rows_bytes:
+                        out[c, t, l, j] = qweight[row, b0 + j]
+    return out.reshape(-1)
+
+
+def unrepack_nf4_ref(codes_r, N, K):
+    """The inverse: codes_r -> canonical qweight uint8 [N, K/2]."""
+    KT = (K + TILE - 1) // TILE
+    r = np.asarray(codes_r, dtype=np.uint8).reshape(N // 16, KT, 64, 16)
+    q = np.zeros((N, K // 2), dtype=np.uint8)
+    for c in range(N // 16):
+        for t in range(KT):
+            for l in range(64):
+                row = 16 * c + (l & 15)
+                b0 = 64 * t + 16 * (l >> 4)
+                for j in range(16):
+                    if b0 + j < K // 2:
+                        q[row, b0 + j] = r[c, t, l, j]
+    return q

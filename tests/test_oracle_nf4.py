@@ -155,3 +155,31 @@ def test_dequant_nf4_vs_exact_rational():
                 t = t.to(torch.bfloat16 if dtype == "bf16" else torch.float16)
                 want = t.view(torch.int16).numpy().view(np.uint16)[0]
                 assert got[n, k] == want, (n, k, dtype)
+
+
+def test_repack_nf4_ref_layout_and_inverse():
+    # every (row, input) code found where the tile layout puts it, by the
+    # input index (tile k // 128, lane group (k % 128) // 32, byte (k % 32) // 2,
+    # nibble k & 1), padding past K zero, and the inverse restores the codes;
+    # K = 320 leaves the last tile half full
+    from oracle import repack
+    rng = np.random.default_rng(5)
+    for N, K in [(16, 128), (32, 320), (48, 512)]:
+        codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+        q = nf4.pack_nf4(codes)
+        r = repack.repack_nf4_ref(q, N, K)
+        KT = (K + 127) // 128
+        assert r.size == (N // 16) * KT * 1024
+        t4 = r.reshape(N // 16, KT, 64, 16)
+        for n in range(N):
+            for k in range(K):
+                t, b, j = k // 128, (k % 128) // 32, (k % 32) // 2
+                byte = t4[n // 16, t, (n % 16) + 16 * b, j]
+                assert ((byte >> (4 * (k & 1))) & 0xF) == codes[n, k]
+        used = np.zeros_like(t4, dtype=bool)
+        for t in range(KT):
+            for l in range(64):
+                for j in range(16):
+                    used[:, t, l, j] = 64 * t + 16 * (l >> 4) + j < K // 2
+        assert not t4[~used].any()
+        assert np.array_equal(repack.unrepack_nf4_ref(r, N, K), q)
