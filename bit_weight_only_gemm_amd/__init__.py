@@ -296,8 +296,30 @@ def nf4_quantize(W, blocksize=64, stream=None):
             "blocksize": blocksize}
 
 
+def nf4_repack(nf4, stream=None):
+    """The NF4 codes re-laid into 1 KB tiles (once per layer): a copy of the
+    weight dict with "qweight_r" added, which nf4_gemm then uses."""
+    N, K, bs = nf4["N"], nf4["K"], nf4["blocksize"]
+    nb = int(_lib.lib().nf4_repacked_bytes(N, K, bs))
+    if nb < 0:
+        raise ValueError("nf4_repack: unsupported shape N=%d K=%d" % (N, K))
+    r = torch.empty(nb, dtype=torch.uint8, device=nf4["qweight"].device)
+    _lib.check(_lib.lib().nf4_repack(_ptr(nf4["qweight"]), N, K, bs, _ptr(r), _stream(stream)),
+               "nf4_repack")
+    out = dict(nf4)
+    out["qweight_r"] = r
+    return out
+
+
+def nf4_gemm_repacked_plan(M, N, K, blocksize=64, dtype=torch.bfloat16, workspace=True):
+    """Kernels an nf4_gemm_repacked call of this shape launches (host-only query)."""
+    return _names(_lib.lib().nf4_gemm_repacked_plan, M, N, K, blocksize, _DT[dtype],
+                  int(workspace)).split(" + ")
+
+
 def nf4_gemm(x, nf4, out=None, workspace=None, use_workspace=True, stream=None):
-    """y = x @ dequant_nf4(W)^T for x [M, K] fp16/bf16."""
+    """y = x @ dequant_nf4(W)^T for x [M, K] fp16/bf16 (on the repacked codes
+    when the dict carries them, see nf4_repack)."""
     if x.dtype not in _DT:
         raise TypeError("x must be float16 or bfloat16")
     _need(x, x.dtype, "x")
@@ -315,10 +337,12 @@ def nf4_gemm(x, nf4, out=None, workspace=None, use_workspace=True, stream=None):
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     else:
         workspace = None
-    _lib.check(_lib.lib().nf4_gemm(_ptr(x), _ptr(nf4["qweight"]), _ptr(nf4["absmax_q"]),
-                                   _ptr(nf4["absmax_scale"]), bs, _ptr(out), M, N, K,
-                                   _DT[x.dtype], _ptr(workspace), ws_bytes, _stream(stream)),
-               "nf4_gemm")
+    rp = "qweight_r" in nf4
+    fn = _lib.lib().nf4_gemm_repacked if rp else _lib.lib().nf4_gemm
+    _lib.check(fn(_ptr(x), _ptr(nf4["qweight_r" if rp else "qweight"]), _ptr(nf4["absmax_q"]),
+                  _ptr(nf4["absmax_scale"]), bs, _ptr(out), M, N, K, _DT[x.dtype],
+                  _ptr(workspace), ws_bytes, _stream(stream)),
+               "nf4_gemm_repacked" if rp else "nf4_gemm")
     return out
 
 

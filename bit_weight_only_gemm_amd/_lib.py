@@ -42,6 +42,11 @@ SIGNATURES = {
     "w4a16_gemm_plan": (_c.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _p,
                                    _i64, _p]),
     "nf4_gemm_plan": (_c.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p]),
+    "nf4_gemm_repacked_plan": (_c.c_int, [_i64, _i64, _i64, _i32, _i32, _i32, _p, _i64, _p]),
+    "nf4_repacked_bytes": (_i64, [_i64, _i64, _i32]),
+    "nf4_repack": (_c.c_int, [_p, _i64, _i64, _i32, _p, _p]),
+    "nf4_gemm_repacked": (_c.c_int, [_p, _p, _p, _p, _i32, _p, _i64, _i64, _i64, _i32, _p, _i64,
+                                     _p]),
     "w4a16_stream_read": (_c.c_int, [_p, _i64, _i32, _p, _p]),
     "w4a16_gemm_noalloc": (_c.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p, _i64, _i64, _i64,
                                       _i32, _p]),

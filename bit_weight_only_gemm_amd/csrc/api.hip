@@ -434,9 +434,9 @@ int64_t nf4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t blocksize) 
   return nf4_workspace_bytes_for(M, N, K);
 }
 
-int nf4_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int32_t dtype,
-                  int32_t has_workspace, char* names_host, int64_t names_bytes,
-                  int64_t* names_len_host) {
+static int nf4_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int32_t dtype,
+                    int32_t has_workspace, char* names_host, int64_t names_bytes,
+                    int64_t* names_len_host, bool repacked) {
   return guarded([&]() -> int {
     if (M <= 0) return W4A16_ERR_INVALID_ARG;
     if (int s = validate_nf4_shape(N, K, blocksize)) return s;
@@ -444,16 +444,47 @@ int nf4_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int32_t dt
     if (too_big_m(M, N, K)) return W4A16_ERR_UNSUPPORTED;
     if (int s = validate_dtype(dtype)) return s;
     if (names_bytes < 0 || (names_bytes > 0 && !names_host)) return W4A16_ERR_INVALID_ARG;
-    const int64_t len = plan_names(plan_nf4_gemm(M, N, K, dtype, has_workspace != 0), names_host,
-                                   names_bytes);
+    const int64_t len = plan_names(plan_nf4_gemm(M, N, K, dtype, has_workspace != 0, repacked),
+                                   names_host, names_bytes);
     if (names_len_host) *names_len_host = len;
     return W4A16_OK;
   });
 }
 
-int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
-             const float* absmax_scale, int32_t blocksize, void* out, int64_t M, int64_t N,
-             int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+int nf4_gemm_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int32_t dtype,
+                  int32_t has_workspace, char* names_host, int64_t names_bytes,
+                  int64_t* names_len_host) {
+  return nf4_plan(M, N, K, blocksize, dtype, has_workspace, names_host, names_bytes,
+                  names_len_host, false);
+}
+
+int nf4_gemm_repacked_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int32_t dtype,
+                           int32_t has_workspace, char* names_host, int64_t names_bytes,
+                           int64_t* names_len_host) {
+  return nf4_plan(M, N, K, blocksize, dtype, has_workspace, names_host, names_bytes,
+                  names_len_host, true);
+}
+
+int64_t nf4_repacked_bytes(int64_t N, int64_t K, int32_t blocksize) {
+  if (validate_nf4_shape(N, K, blocksize) != W4A16_OK || N % 16 != 0) return -1;
+  return nf4_repacked_bytes_for(N, K);
+}
+
+int nf4_repack(const uint8_t* qweight, int64_t N, int64_t K, int32_t blocksize,
+               uint8_t* qweight_r, void* stream) {
+  return guarded([&]() -> int {
+    if (int s = validate_nf4_shape(N, K, blocksize)) return s;
+    if (N % 16 != 0) return W4A16_ERR_INVALID_ARG;
+    if (int s = check_ptrs({qweight, qweight_r})) return s;
+    clear_pending_error();
+    return hip_status(launch_nf4_repack(qweight, N, K, qweight_r, (hipStream_t)stream));
+  });
+}
+
+static int nf4_gemm_any(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
+                        const float* absmax_scale, int32_t blocksize, void* out, int64_t M,
+                        int64_t N, int64_t K, int32_t dtype, void* workspace,
+                        int64_t workspace_bytes, void* stream, bool repacked) {
   return guarded([&]() -> int {
     if (M <= 0) return W4A16_ERR_INVALID_ARG;
     if (int s = validate_nf4_shape(N, K, blocksize)) return s;
@@ -467,8 +498,24 @@ int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
       return W4A16_ERR_WORKSPACE;
     clear_pending_error();
     return hip_status(launch_nf4_gemm(x, qweight, absmax_q, absmax_scale, codebook(), out, M, N,
-                                      K, dtype, workspace, workspace_bytes, (hipStream_t)stream));
+                                      K, dtype, workspace, workspace_bytes, repacked,
+                                      (hipStream_t)stream));
   });
+}
+
+int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
+             const float* absmax_scale, int32_t blocksize, void* out, int64_t M, int64_t N,
+             int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  return nf4_gemm_any(x, qweight, absmax_q, absmax_scale, blocksize, out, M, N, K, dtype,
+                      workspace, workspace_bytes, stream, false);
+}
+
+int nf4_gemm_repacked(const void* x, const uint8_t* qweight_r, const uint8_t* absmax_q,
+                      const float* absmax_scale, int32_t blocksize, void* out, int64_t M,
+                      int64_t N, int64_t K, int32_t dtype, void* workspace,
+                      int64_t workspace_bytes, void* stream) {
+  return nf4_gemm_any(x, qweight_r, absmax_q, absmax_scale, blocksize, out, M, N, K, dtype,
+                      workspace, workspace_bytes, stream, true);
 }
 
 int nf4_dequant(const uint8_t* qweight, const uint8_t* absmax_q, const float* absmax_scale,

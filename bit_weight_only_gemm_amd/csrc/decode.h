@@ -258,7 +258,11 @@ struct IntW {
 // BATCH (K % 1024 == 0): the 16 absmax bytes of a run of 8 tiles of a row are
 // one aligned 16-byte load and share one double-quant scale (a run of 16
 // blocks never straddles a group of 256); otherwise they are loaded per tile.
-template <int DT, bool BATCH>
+// RP: the codes repacked into 1 KB tiles (nf4_repack): lane l's 16 bytes of
+// K tile t are at byte 1024 t + 16 l of its column tile's run of tiles, so a
+// wave's load of a tile is one contiguous 1 KB block (the canonical rows put
+// its 16 rows of 64 bytes a row pitch apart).
+template <int DT, bool BATCH, bool RP = false>
 struct Nf4W {
   static constexpr bool kRaggedK = true;  // K % 64 == 0 only: a last tile may be half
   static constexpr bool kFold = false;
@@ -284,12 +288,17 @@ struct Nf4W {
     const size_t n0 = (size_t)ct * 16;
     const int nloc = lane & 15;
     kb = lane >> 4;
-    rq = make_rsrc(q + n0 * (K >> 1), 16u * (uint32_t)(K >> 1));
+    if constexpr (RP) {
+      const uint32_t KTc = (uint32_t)(K + 127) / 128u;
+      rq = make_rsrc(q + (size_t)ct * KTc * 1024, KTc * 1024u);
+    } else {
+      rq = make_rsrc(q + n0 * (K >> 1), 16u * (uint32_t)(K >> 1));
+    }
     raq = make_rsrc(aq + n0 * (K >> 6), 16u * (uint32_t)(K >> 6));
     const size_t nblocks = (size_t)N * (K >> 6);
     ras = make_rsrc(asc, (uint32_t)(((nblocks + 255) >> 8) * 4));
     blk0 = (uint32_t)(n0 * (K >> 6));
-    voq = (uint32_t)(nloc * (K >> 1) + 16 * kb);
+    voq = RP ? (uint32_t)lane * 16u : (uint32_t)(nloc * (K >> 1) + 16 * kb);
     vob = (uint32_t)(nloc * (K >> 6));
   }
   __device__ static __forceinline__ Meta zero_meta() {
@@ -322,7 +331,7 @@ struct Nf4W {
   // out-of-range per-lane offset and read zeros.
   __device__ __forceinline__ u32x4_t load_codes(int t, int /*lane*/) const {
     const uint32_t vq = (t * 128 + 32 * kb < K) ? voq : kOutOfRange;
-    return bld128(rq, vq, t * 64);
+    return bld128(rq, vq, t * (RP ? 1024 : 64));
   }
   __device__ __forceinline__ void operands(const u32x4_t& w4, int s, const Meta& m,
                                            typename Op<DT>::vec b[4]) const {
@@ -1060,22 +1069,41 @@ intb_decode_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ 
   decode_body<DT, MT, AM, XS, ONE>(x, xsc, wp, out, M, N, K, KT, red, perm, xlds);
 }
 
-template <int DT, int MT, int AM, bool BATCH>
-__global__ void __launch_bounds__(64 * DW)
-nf4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
-                  const uint8_t* __restrict__ aq, const float* __restrict__ asc, Nf4Table L,
-                  uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+template <int DT, int MT, int AM, bool BATCH, bool RP>
+__device__ __forceinline__ void nf4_decode(const uint16_t* __restrict__ x,
+                                           const uint8_t* __restrict__ q,
+                                           const uint8_t* __restrict__ aq,
+                                           const float* __restrict__ asc, const Nf4Table& L,
+                                           uint16_t* __restrict__ out, int M, int N, int K,
+                                           int KT) {
   __shared__ float red[DW * MT * 64 * 4];
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
   __syncthreads();
   extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
-  Nf4W<DT, BATCH> wp;
+  Nf4W<DT, BATCH, RP> wp;
   wp.q = q;
   wp.aq = aq;
   wp.asc = asc;
   wp.lut = lut;
   decode_body<DT, MT, AM, false>(x, nullptr, wp, out, M, N, K, KT, red, nullptr, xlds);
+}
+
+template <int DT, int MT, int AM, bool BATCH>
+__global__ void __launch_bounds__(64 * DW)
+nf4_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
+                  const uint8_t* __restrict__ aq, const float* __restrict__ asc, Nf4Table L,
+                  uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+  nf4_decode<DT, MT, AM, BATCH, false>(x, q, aq, asc, L, out, M, N, K, KT);
+}
+
+// The same on the repacked codes (nf4_repack).
+template <int DT, int MT, int AM, bool BATCH>
+__global__ void __launch_bounds__(64 * DW)
+nf4r_decode_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ q,
+                   const uint8_t* __restrict__ aq, const float* __restrict__ asc, Nf4Table L,
+                   uint16_t* __restrict__ out, int M, int N, int K, int KT) {
+  nf4_decode<DT, MT, AM, BATCH, true>(x, q, aq, asc, L, out, M, N, K, KT);
 }
 
 // ---------------------------------------------------------------- planning --

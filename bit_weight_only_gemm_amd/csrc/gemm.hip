@@ -295,9 +295,10 @@ GemmPlan plan_int_gemm(int64_t M, int64_t N, int64_t K, int G, int bits, int dty
   return p;
 }
 
-GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws) {
+GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws, bool repacked) {
   GemmPlan p;
   p.nf4 = true;
+  p.repacked = repacked;
   p.dtype = dtype;
   p.prefill = nf4_use_prefill(M, N, K);
   if (p.prefill) {
@@ -342,7 +343,7 @@ int64_t plan_names(const GemmPlan& p, char* out, int64_t n) {
   else if (p.prep)
     o.add("w4a16::%s<%d> + ", tiled ? "prep_tiled_kernel" : "prep_x_kernel", p.dtype);
   if (p.prefill) {
-    const int fmt = p.nf4 ? 1 : 0, U = p.nf4 ? 1 : p.U, bits = p.nf4 ? 4 : p.bits;
+    const int fmt = p.nf4 ? (p.repacked ? 2 : 1) : 0, U = p.nf4 ? 1 : p.U, bits = p.nf4 ? 4 : p.bits;
     const char* sep = "";
     if (p.full) {
       o.add("w4a16::wq_prefill_kernel<%d, %d, false, %d, %d, %d>", p.dtype, p.bm, fmt, U, bits);
@@ -353,7 +354,8 @@ int64_t plan_names(const GemmPlan& p, char* out, int64_t n) {
             bits);
     if (p.splits > 1) o.add(" + w4a16::split_reduce_kernel<%d>", p.dtype);
   } else if (p.nf4) {
-    o.add("w4a16::nf4_decode_kernel<%d, %d, %d, %s>", p.dtype, p.mt, p.am, tf(p.batch));
+    o.add("w4a16::%s<%d, %d, %d, %s>", p.repacked ? "nf4r_decode_kernel" : "nf4_decode_kernel",
+          p.dtype, p.mt, p.am, tf(p.batch));
   } else if (p.wide) {
     o.add("w4a16::intb_decode_wide_kernel<%d, %d, %d, 2, %d>", p.dtype, p.U, p.bits, RUN);
   } else {
@@ -465,32 +467,40 @@ hipError_t scratch_address(void** ptr) {
   return hipSuccess;
 }
 
-template <int DT, int MT, int AM, bool BATCH>
+template <int DT, int MT, int AM, bool BATCH, bool RP>
 static void launch_nf4_v(const void* x, const uint8_t* q, const uint8_t* aq, const float* asc,
                          const Nf4Table& L, void* out, int64_t M, int64_t N, int64_t K,
                          hipStream_t stream) {
   const dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(M, 16 * MT));
   const size_t lds = AM == AM_FULLT ? xpose_bytes(MT) : 0;
-  if (lds) allow_dynamic_lds((const void*)nf4_decode_kernel<DT, MT, AM, BATCH>);
-  launch_timed(nf4_decode_kernel<DT, MT, AM, BATCH>, grid, dim3(64 * DW), lds, stream,
-               (const uint16_t*)x, q, aq, asc, L, (uint16_t*)out, (int)M, (int)N, (int)K,
-               (int)ceil_div(K, 128));
+  auto kernel = RP ? nf4r_decode_kernel<DT, MT, AM, BATCH> : nf4_decode_kernel<DT, MT, AM, BATCH>;
+  if (lds) allow_dynamic_lds((const void*)kernel);
+  launch_timed(kernel, grid, dim3(64 * DW), lds, stream, (const uint16_t*)x, q, aq, asc, L,
+               (uint16_t*)out, (int)M, (int)N, (int)K, (int)ceil_div(K, 128));
 }
 
-template <int DT, bool BATCH>
+template <int DT, bool BATCH, bool RP>
 static void launch_nf4_dt(const GemmPlan& pl, const void* x, const uint8_t* q, const uint8_t* aq,
                           const float* asc, const Nf4Table& L, void* out, int64_t M, int64_t N,
                           int64_t K, hipStream_t stream) {
   if (pl.am == AM_PACKED)
-    launch_nf4_v<DT, 1, AM_PACKED, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+    launch_nf4_v<DT, 1, AM_PACKED, BATCH, RP>(x, q, aq, asc, L, out, M, N, K, stream);
   else if (pl.am == AM_FULL)
-    launch_nf4_v<DT, 1, AM_FULL, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+    launch_nf4_v<DT, 1, AM_FULL, BATCH, RP>(x, q, aq, asc, L, out, M, N, K, stream);
   else if (pl.mt == 1)
-    launch_nf4_v<DT, 1, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+    launch_nf4_v<DT, 1, AM_FULLT, BATCH, RP>(x, q, aq, asc, L, out, M, N, K, stream);
   else if (pl.mt == 2)
-    launch_nf4_v<DT, 2, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+    launch_nf4_v<DT, 2, AM_FULLT, BATCH, RP>(x, q, aq, asc, L, out, M, N, K, stream);
   else
-    launch_nf4_v<DT, 4, AM_FULLT, BATCH>(x, q, aq, asc, L, out, M, N, K, stream);
+    launch_nf4_v<DT, 4, AM_FULLT, BATCH, RP>(x, q, aq, asc, L, out, M, N, K, stream);
+}
+
+template <int DT, bool RP>
+static void launch_nf4_dec(const GemmPlan& pl, const void* x, const uint8_t* q, const uint8_t* aq,
+                           const float* asc, const Nf4Table& L, void* out, int64_t M, int64_t N,
+                           int64_t K, hipStream_t stream) {
+  if (pl.batch) launch_nf4_dt<DT, true, RP>(pl, x, q, aq, asc, L, out, M, N, K, stream);
+  else launch_nf4_dt<DT, false, RP>(pl, x, q, aq, asc, L, out, M, N, K, stream);
 }
 
 int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K) {
@@ -500,24 +510,19 @@ int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,
                            int64_t N, int64_t K, int dtype, void* workspace,
-                           int64_t /*workspace_bytes*/, hipStream_t stream) {
-  const GemmPlan pl = plan_nf4_gemm(M, N, K, dtype, workspace != nullptr);
+                           int64_t /*workspace_bytes*/, bool repacked, hipStream_t stream) {
+  const GemmPlan pl = plan_nf4_gemm(M, N, K, dtype, workspace != nullptr, repacked);
   if (pl.prefill) {
     launch_nf4_prefill(x, qweight, absmax_q, absmax_scale, L, out, workspace, M, N, K, dtype,
-                       stream);
+                       repacked, stream);
     return hipGetLastError();
   }
   if (dtype == DT_F16) {
-    if (pl.batch)
-      launch_nf4_dt<DT_F16, true>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
-    else
-      launch_nf4_dt<DT_F16, false>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+    if (repacked) launch_nf4_dec<DT_F16, true>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+    else launch_nf4_dec<DT_F16, false>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
   } else {
-    if (pl.batch)
-      launch_nf4_dt<DT_BF16, true>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
-    else
-      launch_nf4_dt<DT_BF16, false>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K,
-                                    stream);
+    if (repacked) launch_nf4_dec<DT_BF16, true>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
+    else launch_nf4_dec<DT_BF16, false>(pl, x, qweight, absmax_q, absmax_scale, L, out, M, N, K, stream);
   }
   return hipGetLastError();
 }

@@ -82,11 +82,12 @@ struct GemmPlan {
   bool one = false;         // decode: the one-row form of the packed fold
   bool wide = false;        // decode: the wide packed kernel (2 column tiles per wave)
   bool batch = false;       // NF4 decode: absmax codes of a run in one load
+  bool repacked = false;    // NF4: the codes in the tile layout (nf4_repack)
 };
 // ws: whether the call has a workspace (of at least int4_workspace_bytes).
 GemmPlan plan_int_gemm(int64_t M, int64_t N, int64_t K, int G, int bits, int dtype, bool perm,
                        bool xs, bool ws);
-GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws);
+GemmPlan plan_nf4_gemm(int64_t M, int64_t N, int64_t K, int dtype, bool ws, bool repacked = false);
 // "w4a16::kernel<args> + ..." in launch order (at most n bytes with the NUL);
 // returns the full length.
 int64_t plan_names(const GemmPlan& p, char* out, int64_t n);
@@ -125,9 +126,11 @@ void launch_int_prefill(const void* x, const void* codes_r, const void* scales_r
                         const void* zeros_r, void* out, void* ws, int64_t M, int64_t N,
                         int64_t K, int G, int bits, int dtype, hipStream_t stream);
 
+// repacked: the NF4 codes in the tile layout of launch_nf4_repack
 void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                         const float* absmax_scale, const Nf4Table& L, void* out, void* ws,
-                        int64_t M, int64_t N, int64_t K, int dtype, hipStream_t stream);
+                        int64_t M, int64_t N, int64_t K, int dtype, bool repacked,
+                        hipStream_t stream);
 // Whether nf4_gemm runs the large-M kernel at this shape, and the workspace
 // bytes it then needs.  Its codebook dequant costs about twice the INT4 one,
 // so the crossovers (measured in bf16) are later than INT4's: past the
@@ -143,7 +146,13 @@ int64_t nf4_workspace_bytes_for(int64_t M, int64_t N, int64_t K);
 hipError_t launch_nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                            const float* absmax_scale, const Nf4Table& L, void* out, int64_t M,
                            int64_t N, int64_t K, int dtype, void* workspace,
-                           int64_t workspace_bytes, hipStream_t stream);
+                           int64_t workspace_bytes, bool repacked, hipStream_t stream);
+// NF4 codes re-laid into tiles of 16 rows x 128 inputs (1 KB; lane r of tile
+// (c, t) holds bytes 64 t + 16 (r >> 4) .. + 15 of row 16 c + (r & 15), zeros
+// past the row): N / 16 x ceil(K / 128) KB.
+inline int64_t nf4_repacked_bytes_for(int64_t N, int64_t K) { return N / 16 * ((K + 127) / 128) * 1024; }
+hipError_t launch_nf4_repack(const uint8_t* qweight, int64_t N, int64_t K, uint8_t* qweight_r,
+                             hipStream_t stream);
 
 // A plain streaming read of `bytes` by `workgroups` workgroups of 256 lanes
 // (the practical HBM read ceiling); out: uint32 [workgroups * 256].

@@ -57,7 +57,12 @@ __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, uint32_t voff,
 // is then chunk 8 (l >> 5) + j of the tile (the K order inside a tile is the
 // same permutation on both sides).  Dequant: w = round16(L[c] * a'), a' =
 // absmax_q * absmax_scale, L from LDS.  NF4 here needs K % 128 == 0.
-enum { FMT_INT4 = 0, FMT_NF4 = 1 };
+// NF4R: NF4 with the codes re-laid once into the tiles of the integer
+// formats' code layout (16 rows x 128 inputs, 1 KB, lane r holding bytes
+// 64 t + 16 (r >> 4) .. + 15 of row r & 15): lane l's 32 bytes are then the
+// 16-byte chunks of repacked lanes (l & 15) + 32 (l >> 5) and + 16.
+enum { FMT_INT4 = 0, FMT_NF4 = 1, FMT_NF4R = 2 };
+constexpr bool is_nf4_fmt(int fmt) { return fmt != FMT_INT4; }
 
 // INT codes of BITS bits (3, 4 or 8; the Codes<BITS> forms of common.h): a
 // column tile's K tile is 256 BITS bytes, repacked lane r's codes at 12 r
@@ -70,12 +75,12 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
                   float* __restrict__ part, int M, int N, int K, int KT, int NP, int S,
                   int rb0) {
   typedef typename Op<DT>::vec vec;
-  typedef Codes<FMT == FMT_NF4 ? 4 : BITS> CT;     // NF4: its 16-byte loads as Codes<4>
+  typedef Codes<is_nf4_fmt(FMT) ? 4 : BITS> CT;     // NF4: its 16-byte loads as Codes<4>
   constexpr int kTile = 256 * BITS;                 // INT: bytes per column tile, K tile
   constexpr int kZW = zero_field_bits(BITS);        // INT: zero field width
   constexpr int kZWords = U * kZW / 4;              // INT: zero dwords per column and run
   __shared__ float lut[16];
-  if (FMT == FMT_NF4 && threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
+  if (is_nf4_fmt(FMT) && threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
   constexpr int PF_BM = BM;
   constexpr int PF_MT = BM / 32;
   constexpr int PF_STAGE = BM * PF_ROWB;
@@ -129,14 +134,22 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
     // rows of this panel (N % 16 == 0; rows past N read 0 -> a' = 0)
     const int nrows = pv ? min(64, N - p * 64) : 0;
     const uint32_t Kb = (uint32_t)K / 2u, Kblk = (uint32_t)K / 64u;
-    rc = make_rsrc(codes + pp * 64 * Kb, (uint32_t)nrows * Kb);
+    if constexpr (FMT == FMT_NF4R)
+      rc = make_rsrc(codes + pp * 4 * KT * 1024, (uint32_t)(nrows / 16) * (uint32_t)KT * 1024u);
+    else
+      rc = make_rsrc(codes + pp * 64 * Kb, (uint32_t)nrows * Kb);
     rs = make_rsrc(scales + pp * 64 * Kblk, (uint32_t)nrows * Kblk);
     rz = make_rsrc(zeros, (uint32_t)(((int64_t)N * Kblk + 255) / 256 * 4));
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int c = 32 * g + (lane & 31);
-      vcode[g][0] = (uint32_t)c * Kb + 32u * (uint32_t)h;
-      vcode[g][1] = vcode[g][0] + 16u;
+      if constexpr (FMT == FMT_NF4R) {
+        vcode[g][0] = (uint32_t)(((c >> 4) * KT * 64 + i16 + 32 * h) * 16);
+        vcode[g][1] = vcode[g][0] + 256u;
+      } else {
+        vcode[g][0] = (uint32_t)c * Kb + 32u * (uint32_t)h;
+        vcode[g][1] = vcode[g][0] + 16u;
+      }
       vmeta[g] = (uint32_t)c * Kblk + (uint32_t)h;
       gblk[g] = (uint32_t)(pp * 64 + c) * Kblk + (uint32_t)h;
     }
@@ -165,8 +178,9 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
       za = bld32(rz, vmeta[g] * 4u * kZWords,
                  (t >> 3) * 256 * kZWords + (((t & 7) * U * kZW) >> 5) * 4);
     } else {
-      w[0].w = bld128(rc, vcode[g][0], t * 64);
-      w[1].w = bld128(rc, vcode[g][1], t * 64);
+      constexpr int kStep = FMT == FMT_NF4R ? 1024 : 64;  // bytes per K tile
+      w[0].w = bld128(rc, vcode[g][0], t * kStep);
+      w[1].w = bld128(rc, vcode[g][1], t * kStep);
       sa = u32x2_t{__builtin_amdgcn_raw_buffer_load_b8(rs, vmeta[g], 2 * t, 0), 0u};
       za = bld32(rz, ((gblk[g] + 2u * (uint32_t)t) >> 8) * 4u, 0);
     }
@@ -203,7 +217,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
   // counts in issue order, so it leaves those kW loads pending (the barrier is
   // a plain s_barrier: __syncthreads would wait for every load).
   constexpr bool DEEP = BM == 32;
-  constexpr int kW = 2 * ((FMT == FMT_NF4 ? 2 : (BITS == 8 ? 4 : 2)) + 2);  // loads per load_w pair
+  constexpr int kW = 2 * ((is_nf4_fmt(FMT) ? 2 : (BITS == 8 ? 4 : 2)) + 2);  // loads per load_w pair
   CT cw[DEEP ? 3 : 2][2][2];
   u32x2_t sc[DEEP ? 3 : 2][2];
   uint32_t zz[DEEP ? 3 : 2][2];
@@ -256,7 +270,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
 #pragma unroll
     for (int g = 0; g < 2; ++g)
       bcar[g] = operand_of(0, g, cw[0], sc[0], zz[0], zb_of(tb),
-                           FMT == FMT_NF4 ? ap_of(sc[0], zz[0], g) : 0.f);
+                           is_nf4_fmt(FMT) ? ap_of(sc[0], zz[0], g) : 0.f);
   }
 
   // One K tile: compute tile t from the weight slot (cwc, scc, zzc) while the
@@ -291,7 +305,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
     // pipe busy long enough to issue several VALU instructions behind it).
     float ap[2];  // NF4: a' of this lane's block
     const int zb = zb_of(t);
-    if constexpr (FMT == FMT_NF4) {
+    if constexpr (is_nf4_fmt(FMT)) {
 #pragma unroll
       for (int g = 0; g < 2; ++g) ap[g] = ap_of(scc, zzc, g);
     }
@@ -302,7 +316,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
         bz[g] = rq.template zero_operand<BITS>(((zzc[g] ^ zx) >> (kZW * zb)) & ((1u << kZW) - 1u));
     }
     auto operand = [&](int s, int g) -> vec {
-      return operand_of(s, g, cwc, scc, zzc, zb, FMT == FMT_NF4 ? ap[g] : 0.f);
+      return operand_of(s, g, cwc, scc, zzc, zb, is_nf4_fmt(FMT) ? ap[g] : 0.f);
     };
     const uint8_t* st = As + ((t - tb) & 1) * PF_STAGE;
     auto read_step = [&](int s, vec (&a)[PF_MT]) {
@@ -342,7 +356,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
         const int zbn = zb_of(t + 1);
 #pragma unroll
         for (int g = 0; g < 2; ++g)
-          bn[g] = operand_of(0, g, cwn, scn, zzn, zbn, FMT == FMT_NF4 ? ap_of(scn, zzn, g) : 0.f);
+          bn[g] = operand_of(0, g, cwn, scn, zzn, zbn, is_nf4_fmt(FMT) ? ap_of(scn, zzn, g) : 0.f);
       }
       if constexpr (FOLD) {
 #pragma unroll

@@ -117,13 +117,22 @@ void launch_int_prefill(const void* x, const void* codes_r, const void* scales_r
 
 void launch_nf4_prefill(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
                         const float* absmax_scale, const Nf4Table& L, void* out, void* ws,
-                        int64_t M, int64_t N, int64_t K, int dtype, hipStream_t stream) {
-  if (dtype == DT_F16)
+                        int64_t M, int64_t N, int64_t K, int dtype, bool repacked,
+                        hipStream_t stream) {
+  if (repacked) {
+    if (dtype == DT_F16)
+      launch_prefill_dt<DT_F16, FMT_NF4R, 1, 4>(x, qweight, absmax_q, absmax_scale, L, out, ws,
+                                                M, N, K, stream);
+    else
+      launch_prefill_dt<DT_BF16, FMT_NF4R, 1, 4>(x, qweight, absmax_q, absmax_scale, L, out, ws,
+                                                 M, N, K, stream);
+  } else if (dtype == DT_F16) {
     launch_prefill_dt<DT_F16, FMT_NF4, 1, 4>(x, qweight, absmax_q, absmax_scale, L, out, ws, M,
                                              N, K, stream);
-  else
+  } else {
     launch_prefill_dt<DT_BF16, FMT_NF4, 1, 4>(x, qweight, absmax_q, absmax_scale, L, out, ws, M,
                                               N, K, stream);
+  }
 }
 
 template void launch_intb_prefill<4>(W4A16_PREFILL_ARGS);

@@ -412,4 +412,32 @@ hipError_t launch_dequant_nf4(const uint8_t* qweight, const uint8_t* absmax_q,
   return hipGetLastError();
 }
 
+// NF4 codes into tiles of 16 rows x 128 inputs: one thread per 16-byte chunk
+// (c, t, l) of the output, at byte 16 ((c KT + t) 64 + l), holding bytes
+// 64 t + 16 (l >> 4) .. + 15 of row 16 c + (l & 15) (rows are K / 2 bytes,
+// a multiple of 32, so a chunk lies wholly inside the row or wholly past it:
+// then zeros).
+__global__ void __launch_bounds__(256)
+nf4_repack_kernel(const uint8_t* __restrict__ qweight, int64_t rowb, int KT, int64_t chunks,
+                  uint8_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= chunks) return;
+  const int l = (int)(idx & 63);
+  const int64_t ct = (idx >> 6) / KT;
+  const int t = (int)((idx >> 6) - ct * KT);
+  const int64_t b0 = 64 * (int64_t)t + 16 * (l >> 4);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (b0 < rowb) v = *(const u32x4_t*)(qweight + (16 * ct + (l & 15)) * rowb + b0);
+  *(u32x4_t*)(out + idx * 16) = v;
+}
+
+hipError_t launch_nf4_repack(const uint8_t* qweight, int64_t N, int64_t K, uint8_t* qweight_r,
+                             hipStream_t stream) {
+  const int KT = (int)((K + 127) / 128);
+  const int64_t chunks = N / 16 * KT * 64;
+  hipLaunchKernelGGL(nf4_repack_kernel, dim3((unsigned)ceil_div(chunks, (int64_t)256)),
+                     dim3(256), 0, stream, qweight, K / 2, KT, chunks, qweight_r);
+  return hipGetLastError();
+}
+
 }  // namespace w4a16

@@ -441,6 +441,40 @@ int nf4_gemm(const void* x, const uint8_t* qweight, const uint8_t* absmax_q,
              const float* absmax_scale, int32_t blocksize, void* out, int64_t M, int64_t N,
              int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * NF4 codes re-laid once, offline, into the 1 KB tiles the decode and large-M
+ * kernels read contiguously ([P5] "关键数据解读" item 4: a layout is translated
+ * once, not on every run): tiles of 16 output rows x 128 inputs, tile (c, t)
+ * at byte 1024 (c ceil(K/128) + t), its 16-byte chunk l holding bytes
+ * 64 t + 16 (l >> 4) .. + 15 of canonical row 16 c + (l & 15) (the codes of
+ * inputs 128 t + 32 (l >> 4) .. + 31, low nibble first), zeros past the row's
+ * K / 2 bytes.  The absmax codes and scales stay as nf4_quantize writes them.
+ *   nf4_repacked_bytes: N / 16 * ceil(K / 128) * 1024, or -1 on bad input
+ *   (N % 16 != 0, or the shape rules of nf4_gemm).
+ *   nf4_repack: qweight uint8 [N, K/2] (device, canonical) -> qweight_r
+ *   (device, nf4_repacked_bytes); the two must not overlap.  Async; errors as
+ *   for nf4_gemm's shape and pointer checks.
+ */
+int64_t nf4_repacked_bytes(int64_t N, int64_t K, int32_t blocksize);
+int nf4_repack(const uint8_t* qweight, int64_t N, int64_t K, int32_t blocksize,
+               uint8_t* qweight_r, void* stream);
+
+/*
+ * nf4_gemm on repacked codes (nf4_repack): the same product, the same
+ * kernels' arithmetic in the same order -- bitwise the same output as
+ * nf4_gemm on the canonical codes -- reading each tile of codes as one
+ * contiguous block.  Arguments, constraints, workspace and errors as for
+ * nf4_gemm (nf4_workspace_bytes covers these calls too).
+ */
+int nf4_gemm_repacked(const void* x, const uint8_t* qweight_r, const uint8_t* absmax_q,
+                      const float* absmax_scale, int32_t blocksize, void* out, int64_t M,
+                      int64_t N, int64_t K, int32_t dtype, void* workspace,
+                      int64_t workspace_bytes, void* stream);
+/* Host-only plan query for nf4_gemm_repacked, as w4a16_gemm_plan. */
+int nf4_gemm_repacked_plan(int64_t M, int64_t N, int64_t K, int32_t blocksize, int32_t dtype,
+                           int32_t has_workspace, char* names_host, int64_t names_bytes,
+                           int64_t* names_len_host);
+
 /* Test/debug export: dequantized NF4 weights w [N, K] in dtype.  Async. */
 int nf4_dequant(const uint8_t* qweight, const uint8_t* absmax_q, const float* absmax_scale,
                 int64_t N, int64_t K, int32_t blocksize, int32_t dtype, void* w_out,

@@ -86,6 +86,16 @@ static void plan_names(void) {
       free(b);
     }
   }
+  for (int64_t M = 1; M <= 2048; M *= 8) {
+    int64_t full = -1;
+    EXPECT(nf4_gemm_repacked_plan(M, 28672, 8192, 64, 1, 1, NULL, 0, &full) == 0);
+    for (int64_t n = 1; n <= full + 2; ++n) {
+      char* b = (char*)malloc((size_t)n);
+      EXPECT(nf4_gemm_repacked_plan(M, 28672, 8192, 64, 1, 1, b, n, NULL) == 0);
+      EXPECT((int64_t)strlen(b) == (n - 1 < full ? n - 1 : full));
+      free(b);
+    }
+  }
   EXPECT(nf4_gemm_plan(1, 28672, 8192, 64, 1, 1, NULL, 8, NULL) == W4A16_ERR_INVALID_ARG);
   EXPECT(w4a16_gemm_plan(0, 256, 512, 128, 4, 0, 0, 0, 1, NULL, 0, NULL) ==
          W4A16_ERR_INVALID_ARG);
@@ -133,6 +143,11 @@ static void validation(void) {
   EXPECT(nf4_gemm(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 1, 256, 96, 1, NULL, 0, NULL) == 1);
   EXPECT(nf4_gemm(FAKE, NULL, FAKE, FAKE, 64, FAKE, 1, 256, 512, 1, NULL, 0, NULL) == 1);
   EXPECT(nf4_quantize(FAKE, 16, 100, 64, FAKE, FAKE, FAKE, NULL) == 1);
+  EXPECT(nf4_repacked_bytes(16, 320, 64) == 3 * 1024);
+  EXPECT(nf4_repacked_bytes(20, 320, 64) == -1);
+  EXPECT(nf4_repack(FAKE, 20, 320, 64, FAKE, NULL) == 1);
+  EXPECT(nf4_gemm_repacked(FAKE, FAKE, FAKE, FAKE, 32, FAKE, 1, 256, 512, 1, NULL, 0, NULL) ==
+         2);
   EXPECT(w4a16_set_timing_events(NULL, NULL) == 0);
 }
 

@@ -308,3 +308,27 @@ def test_bits_entry_points_validation_without_gpu():
     assert L.w4a16_workspace_bytes(64, 5120, 5120, 128) > 0        # split K: partials
     assert L.w4a16_gemm_bits(FAKE, NULL, FAKE, FAKE, FAKE, NULL, 128, 8, FAKE, 64, 5120, 5120, 0,
                              FAKE, 16, NULL) == 5
+
+
+def test_nf4_repack_entry_points_without_gpu():
+    # tiles of 16 rows x 128 inputs, 1 KB each; N % 16 and the NF4 shape rules
+    assert L.nf4_repacked_bytes(28672, 8192, 64) == 28672 // 16 * 64 * 1024
+    assert L.nf4_repacked_bytes(16, 320, 64) == 3 * 1024          # a half last tile
+    assert L.nf4_repacked_bytes(20, 320, 64) == -1
+    assert L.nf4_repacked_bytes(16, 96, 64) == -1
+    assert L.nf4_repacked_bytes(16, 128, 32) == -1
+    assert L.nf4_repack(FAKE, 20, 320, 64, FAKE, NULL) == 1
+    assert L.nf4_repack(FAKE, 16, 320, 32, FAKE, NULL) == 2
+    assert L.nf4_repack(NULL, 16, 320, 64, FAKE, NULL) == 1
+    assert L.nf4_repack(FAKE, 16, 320, 64, ODD, NULL) == 3
+    g = L.nf4_gemm_repacked
+    assert g(FAKE, FAKE, FAKE, FAKE, 32, FAKE, 1, 256, 512, 1, NULL, 0, NULL) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, 64, FAKE, 1, 250, 512, 1, NULL, 0, NULL) == 1
+    assert g(FAKE, NULL, FAKE, FAKE, 64, FAKE, 1, 256, 512, 1, NULL, 0, NULL) == 1
+    # the plan names the kernels that read the tiles: nf4r_decode_kernel, and
+    # the large-M kernel's format 2
+    buf = ctypes.create_string_buffer(256)
+    assert L.nf4_gemm_repacked_plan(1, 28672, 8192, 64, 1, 1, buf, 256, NULL) == 0
+    assert buf.value == b"w4a16::nf4r_decode_kernel<1, 1, 0, true>"
+    assert L.nf4_gemm_repacked_plan(2048, 28672, 8192, 64, 1, 1, buf, 256, NULL) == 0
+    assert buf.value == b"w4a16::wq_prefill_kernel<1, 256, false, 2, 1, 4>"
