@@ -166,3 +166,18 @@ def test_gemm_large_m_without_workspace_no_split(M):
     wd = oracle_int4_rows(W, gi, np.arange(N), "bf16")
     assert compare_gemm(y0, xb, wd, "bf16") <= TOL
     assert compare_gemm(y1, xb, wd, "bf16") <= TOL
+
+
+@pytest.mark.parametrize("M", list(range(1, 18)) + [63, 64, 65])
+@pytest.mark.parametrize("act", [False, True])
+def test_gemm_m_sweep_bf16_every_small_m(M, act):
+    # every M from 1 to 17 (the decode forms: packed, staged gather, one-row
+    # fold, full rows, transposed rows, the operand layout after the pass,
+    # two row tiles at 17) and 63-65 (row tiles / large-M block edges), with
+    # and without act-order, K with 5 K tiles (a partial run of 8) and ragged N
+    N, K = 208, 640
+    say("gemm bf16 sweep M", M, "act", act, w4.w4a16_gemm_plan(M, N, K, dtype=torch.bfloat16,
+                                                                 perm=act))
+    y, xb, W, gi, _ = _run_gemm("gpu/gemm/sweep/%d/%d" % (M, act), M, N, K, "bf16", act=act)
+    wd = oracle_int4_rows(W, gi, np.arange(N), "bf16")
+    assert compare_gemm(y, xb, wd, "bf16") <= TOL
