@@ -266,6 +266,7 @@ template <int DT, bool BATCH, bool RP = false>
 struct Nf4W {
   static constexpr bool kRaggedK = true;  // K % 64 == 0 only: a last tile may be half
   static constexpr bool kFold = false;
+  static constexpr int kU = 1;
   typedef u32x4_t CodeT;
   const uint8_t* q;
   const uint8_t* aq;
@@ -686,6 +687,46 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   for (int m = 0; m < (FFOLD ? MT : 1); ++m) yfm[m] = float4_t{0.f, 0.f, 0.f, 0.f};
   constexpr int FE = ONE ? 1 : 4;  // fold elements per lane
   float4_t yf = float4_t{0.f, 0.f, 0.f, 0.f};
+  // Deferred fold (FOLD, FFOLD): a tile's MFMA results are folded into the
+  // accumulators in the next tile's slot, after that tile's MFMAs have been
+  // issued, so each tile's MFMA latency is covered by the other tile's work
+  // instead of stalling the wave (one wave per SIMD on most decode grids).
+  // The tiles are still folded one after another in K order, so the sums are
+  // the same bit for bit; the pending results start at zero (a fold of zeros
+  // leaves the accumulators unchanged) and the last tile is folded after the
+  // loop.
+  constexpr int PDA = FOLD ? 4 : (FFOLD ? MT : 1), PDZ = FOLD ? WP::kU : (FFOLD ? MT : 1);
+  float4_t pat[PDA], paz[PDZ];
+#pragma unroll
+  for (int q = 0; q < PDA; ++q) pat[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < PDZ; ++q) paz[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float psf = 0.f;
+  // FOLD: yf += s (at[lane group] - az[unit of the lane group's step]), the
+  // step tile taken as two levels of selects on the bits of the lane group
+  // (a chain of equality tests becomes branches)
+  auto fold_packed = [&](const float4_t (&a)[PDA], const float4_t (&z)[PDZ], float sf) {
+    if constexpr (FOLD) {
+      const bool h0 = lane & 16, h1 = lane & 32;
+#pragma unroll
+      for (int e = 0; e < FE; ++e) {
+        const float v01 = h0 ? a[1][e] : a[0][e], v23 = h0 ? a[3][e] : a[2][e];
+        float zu[WP::kU];
+#pragma unroll
+        for (int u = 0; u < WP::kU; ++u) zu[u] = z[u][e];
+        yf[e] = __builtin_fmaf(sf, (h1 ? v23 : v01) - sel_unit<WP::kU>(zu, lane), yf[e]);
+      }
+    }
+  };
+  // FFOLD: yfm += s (accT - accZ) per row tile
+  auto fold_full = [&](const float4_t (&a)[PDA], const float4_t (&z)[PDZ], float sf) {
+    if constexpr (FFOLD) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yfm[m][e] = __builtin_fmaf(sf, a[m][e] - z[m][e], yfm[m][e]);
+    }
+  };
 
   // Ring of RUN tiles: slot s holds tile i + s of the current pass.  The
   // fill (tiles 0 .. RUN - 1 and the first run's meta) is issued first; each
@@ -795,17 +836,13 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
 #pragma unroll
             for (int u = 0; u < WP::kU; ++u) az[u] = mfma16x16x32<DT>(ra[sa][0], bz[u], z4);
             const float sf = WP::fold_scale(mc, s, lane);
-            // at[lane >> 4], as two levels of selects on the bits of the lane
-            // group (a chain of equality tests becomes branches)
-            const bool g0 = lane & 16, g1 = lane & 32;
+            // the previous tile's results, while this tile's MFMAs run
+            fold_packed(pat, paz, psf);
 #pragma unroll
-            for (int e = 0; e < FE; ++e) {
-              const float v01 = g0 ? at[1][e] : at[0][e], v23 = g0 ? at[3][e] : at[2][e];
-              float zu[WP::kU];
+            for (int j = 0; j < 4; ++j) pat[j] = at[j];
 #pragma unroll
-              for (int u = 0; u < WP::kU; ++u) zu[u] = az[u][e];
-              yf[e] = __builtin_fmaf(sf, (g1 ? v23 : v01) - sel_unit<WP::kU>(zu, lane), yf[e]);
-            }
+            for (int u = 0; u < WP::kU; ++u) paz[u] = az[u];
+            psf = sf;
           } else {
             if constexpr (FFOLD) wp.raw_operands(ring[s], b);
             else wp.operands(ring[s], s, mc, b);
@@ -821,18 +858,25 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
                 typename Op<DT>::vec bz[1];
                 WP::zero_operands(mc, s, bz);
                 const float sf = WP::fold_scale(mc, s, lane);
+                float4_t tq[MT], tz[MT];
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                  float4_t tq = float4_t{0.f, 0.f, 0.f, 0.f}, tz = tq;
+                  tq[m] = float4_t{0.f, 0.f, 0.f, 0.f};
+                  tz[m] = tq[m];
 #pragma unroll
                   for (int j = 0; j < 4; ++j) {
-                    tq = mfma16x16x32<DT>(at[m * 4 + j], b[j], tq);
-                    tz = mfma16x16x32<DT>(at[m * 4 + j], bz[0], tz);
+                    tq[m] = mfma16x16x32<DT>(at[m * 4 + j], b[j], tq[m]);
+                    tz[m] = mfma16x16x32<DT>(at[m * 4 + j], bz[0], tz[m]);
                   }
-#pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    yfm[m][e] = __builtin_fmaf(sf, tq[e] - tz[e], yfm[m][e]);
                 }
+                // the previous tile's sums, while this tile's MFMAs run
+                fold_full(pat, paz, psf);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                  pat[m] = tq[m];
+                  paz[m] = tz[m];
+                }
+                psf = sf;
               } else {
                 mma_tile<DT, AM, MT, NA, NACC>(b, at, acc);
               }
@@ -856,6 +900,9 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // the last tile's results
+    fold_packed(pat, paz, psf);
+    fold_full(pat, paz, psf);
   }
 
   // ---- v_mfma_f32_16x16x32 result layout: element e of lane l is row
