@@ -228,23 +228,19 @@ __device__ __forceinline__ typename Op<DT>::vec dequant_word(uint32_t w, const Q
 }
 
 // NF4 operand of one 32-bit code word (element e in nibble e): w = round16(L[c]
-// a') with the fp32 product, L a 16-entry fp32 table in LDS.  The table byte
-// offsets 4 c of the even and odd elements are formed for all four bytes at
-// once ((w << 2) and (w >> 2) masked to 0x3C per byte), so each lookup address
-// is a single byte extract.
+// a') with the fp32 product.  The levels come from a 256-entry table of pairs
+// in LDS: entry b (8 bytes) holds {L[b & 15], L[b >> 4]}, the levels of the two
+// codes one byte of w carries (low nibble: element 2 j, high nibble: element
+// 2 j + 1), so one 8-byte lookup serves two codes and its address is the byte
+// shifted by 3 (one shift with a byte-select operand).
 template <int DT>
-__device__ __forceinline__ typename Op<DT>::vec nf4_operand(uint32_t w, const float* lut,
-                                                           float a) {
-  uint32_t lo = (w << 2) & 0x3C3C3C3Cu, hi = (w >> 2) & 0x3C3C3C3Cu;
-  // opaque to the compiler, which would otherwise fold each extract back into
-  // a shift and a mask of w
-  asm("" : "+v"(lo), "+v"(hi));
-  const char* base = (const char*)lut;
+__device__ __forceinline__ typename Op<DT>::vec nf4_pair_operand(uint32_t w, const float2* lut2,
+                                                                float a) {
   typename Op<DT>::vec v;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float f0 = *(const float*)(base + ((lo >> (8 * j)) & 0xFFu)) * a;
-    const float f1 = *(const float*)(base + ((hi >> (8 * j)) & 0xFFu)) * a;
+    const float2 l = lut2[(w >> (8 * j)) & 0xFFu];
+    const float f0 = l.x * a, f1 = l.y * a;
     if constexpr (DT == DT_F16) {
       v[2 * j] = (_Float16)f0;
       v[2 * j + 1] = (_Float16)f1;

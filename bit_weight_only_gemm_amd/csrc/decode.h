@@ -271,7 +271,7 @@ struct Nf4W {
   const uint8_t* q;
   const uint8_t* aq;
   const float* asc;
-  const float* lut;
+  const float2* lut2;
   int N, K;
   rsrc_t rq, raq, ras;
   int kb;
@@ -346,7 +346,7 @@ struct Nf4W {
       a = m.a[s];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = nf4_operand<DT>(w4[j], lut, a);
+    for (int j = 0; j < 4; ++j) b[j] = nf4_pair_operand<DT>(w4[j], lut2, a);
   }
   __device__ static __forceinline__ int xk(int j, int b) { return 32 * b + 8 * j; }
 };
@@ -1124,15 +1124,17 @@ __device__ __forceinline__ void nf4_decode(const uint16_t* __restrict__ x,
                                            uint16_t* __restrict__ out, int M, int N, int K,
                                            int KT) {
   __shared__ float red[DW * MT * 64 * 4];
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
+  // the levels of every code byte (64 * DW == 256 threads, one entry each)
+  __shared__ float2 lut2[256];
+  static_assert(64 * DW == 256, "one thread per code byte");
+  lut2[threadIdx.x] = make_float2(L.v[threadIdx.x & 15u], L.v[threadIdx.x >> 4]);
   __syncthreads();
   extern __shared__ __attribute__((aligned(16))) uint8_t xlds[];
   Nf4W<DT, BATCH, RP> wp;
   wp.q = q;
   wp.aq = aq;
   wp.asc = asc;
-  wp.lut = lut;
+  wp.lut2 = lut2;
   decode_body<DT, MT, AM, false>(x, nullptr, wp, out, M, N, K, KT, red, nullptr, xlds);
 }
 

@@ -79,8 +79,10 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
   constexpr int kTile = 256 * BITS;                 // INT: bytes per column tile, K tile
   constexpr int kZW = zero_field_bits(BITS);        // INT: zero field width
   constexpr int kZWords = U * kZW / 4;              // INT: zero dwords per column and run
-  __shared__ float lut[16];
-  if (is_nf4_fmt(FMT) && threadIdx.x < 16) lut[threadIdx.x] = L.v[threadIdx.x];
+  // NF4: the levels of every code byte, one entry per thread
+  __shared__ float2 lut2[256];
+  static_assert(64 * PF_WAVES == 256, "one thread per code byte");
+  if (is_nf4_fmt(FMT)) lut2[threadIdx.x] = make_float2(L.v[threadIdx.x & 15u], L.v[threadIdx.x >> 4]);
   constexpr int PF_BM = BM;
   constexpr int PF_MT = BM / 32;
   constexpr int PF_STAGE = BM * PF_ROWB;
@@ -252,7 +254,7 @@ wq_prefill_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ co
                                 ((zzx[g] ^ zx) >> (kZW * (zbx + u))) & ((1u << kZW) - 1u));
       return dequant_step<DT, false>(cwx[g][s & 1], s >> 1, q);
     } else {
-      return nf4_operand<DT>(cwx[g][s >> 2].w[s & 3], lut, apx);
+      return nf4_pair_operand<DT>(cwx[g][s >> 2].w[s & 3], lut2, apx);
     }
   };
   auto zb_of = [&](int t) { return ((t & 7) * U) % (32 / kZW); };  // zero field of tile t's first unit
