@@ -177,11 +177,13 @@ template <int DT> struct RawQ {
   // offset of each element's code form (z < 1024 in fp16, < 128 in bf16; for
   // 4-bit codes in fp16 the odd element pairs carry 64 + z, as their codes
   // carry 64 + q).
+  // (The fields of z land on zero bits of the offsets, so the sums below are
+  // the bitwise ors, and each is one multiply-add.)
   template <int BITS>
   __device__ __forceinline__ typename Op<DT>::vec zero_operand(uint32_t z) const {
-    const uint32_t v = magic | (z * 0x00010001u);
+    const uint32_t v = magic + z * 0x00010001u;
     if constexpr (DT == DT_F16 && BITS == 4) {
-      const uint32_t h = magic_hi | (z * 0x00100010u);
+      const uint32_t h = magic_hi + z * 0x00100010u;
       return __builtin_bit_cast(typename Op<DT>::vec, u32x4_t{v, h, v, h});
     } else {
       return __builtin_bit_cast(typename Op<DT>::vec, u32x4_t{v, v, v, v});

@@ -217,8 +217,8 @@ struct IntW {
   // the fold, the scale of step g of slot s (unit sU + gU/4; g is the lane
   // group, so the U candidates are formed and selected on its bits rather
   // than indexed) and the zero operands (o + z) of the slot's U units.
-  __device__ __forceinline__ void raw_operands(const CodeT& w, typename Op<DT>::vec b[4]) const {
-    const RawQ<DT> rq;
+  __device__ __forceinline__ void raw_operands(const CodeT& w, const RawQ<DT>& rq,
+                                               typename Op<DT>::vec b[4]) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = dequant_step<DT, false>(w, j, rq);
   }
@@ -240,9 +240,8 @@ struct IntW {
       return sel_unit<U>(a, lane);
     }
   }
-  __device__ static __forceinline__ void zero_operands(const Meta& m, int s,
+  __device__ static __forceinline__ void zero_operands(const Meta& m, int s, const RawQ<DT>& rq,
                                                        typename Op<DT>::vec (&bz)[U]) {
-    const RawQ<DT> rq;
 #pragma unroll
     for (int u = 0; u < U; ++u) bz[u] = rq.template zero_operand<BITS>(unit_zero(m, s * U + u));
   }
@@ -702,6 +701,10 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
 #pragma unroll
   for (int q = 0; q < PDZ; ++q) paz[q] = float4_t{0.f, 0.f, 0.f, 0.f};
   float psf = 0.f;
+  // FOLD, FFOLD: the offsets of the raw code and zero operands, set once and
+  // held in registers for the whole loop (made per tile, each tile's branch
+  // would set them again)
+  const RawQ<DT> rq;
   // FOLD: yf += s (at[lane group] - az[unit of the lane group's step]), the
   // step tile taken as two levels of selects on the bits of the lane group
   // (a chain of equality tests becomes branches)
@@ -826,12 +829,12 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
           if constexpr (FOLD) {
             const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
             if constexpr (XG && ONE) ra[sa][0] = xg_assemble1<DT>(g1[sa]);
-            wp.raw_operands(ring[s], b);
+            wp.raw_operands(ring[s], rq, b);
             float4_t at[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[sa][0], b[j], z4);
             typename Op<DT>::vec bz[WP::kU];
-            WP::zero_operands(mc, s, bz);
+            WP::zero_operands(mc, s, rq, bz);
             float4_t az[WP::kU];
 #pragma unroll
             for (int u = 0; u < WP::kU; ++u) az[u] = mfma16x16x32<DT>(ra[sa][0], bz[u], z4);
@@ -844,7 +847,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
             for (int u = 0; u < WP::kU; ++u) paz[u] = az[u];
             psf = sf;
           } else {
-            if constexpr (FFOLD) wp.raw_operands(ring[s], b);
+            if constexpr (FFOLD) wp.raw_operands(ring[s], rq, b);
             else wp.operands(ring[s], s, mc, b);
             if constexpr (AM == AM_FULLT || AM == AM_TILED) {
               typename Op<DT>::vec at[NA];
@@ -856,7 +859,7 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
               }
               if constexpr (FFOLD) {
                 typename Op<DT>::vec bz[1];
-                WP::zero_operands(mc, s, bz);
+                WP::zero_operands(mc, s, rq, bz);
                 const float sf = WP::fold_scale(mc, s, lane);
                 float4_t tq[MT], tz[MT];
 #pragma unroll
@@ -1005,6 +1008,8 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
   const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
   const XLds none{nullptr, nullptr, 0u, M, make_rsrc(nullptr, 0u), make_rsrc(nullptr, 0u), false, 0, 0};
   const bool g0 = lane & 16, g1 = lane & 32;
+  // the operand offsets, held in registers for the whole loop
+  const RawQ<DT> rq;
 
   float4_t yf[NC];
 #pragma unroll
@@ -1036,12 +1041,12 @@ intb_decode_wide_kernel(const uint16_t* __restrict__ x, const uint8_t* __restric
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
             vec b[4];
-            wp[c].raw_operands(ring[s][c], b);
+            wp[c].raw_operands(ring[s][c], rq, b);
             float4_t at[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[s][0], b[j], z4);
             vec bz[U];
-            WP::zero_operands(mc[c], slot, bz);
+            WP::zero_operands(mc[c], slot, rq, bz);
             float4_t az[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) az[u] = mfma16x16x32<DT>(ra[s][0], bz[u], z4);
