@@ -695,12 +695,25 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
   // leaves the accumulators unchanged) and the last tile is folded after the
   // loop.
   constexpr int PDA = FOLD ? 4 : (FFOLD ? MT : 1), PDZ = FOLD ? WP::kU : (FFOLD ? MT : 1);
-  float4_t pat[PDA], paz[PDZ];
+  // NB = 2: two sets of pending results, by the parity of the tile (a run of
+  // RUN tiles is even and the slots are unrolled, so each slot's set is
+  // fixed): a tile's results go to its own set while the other set, the
+  // previous tile's, is folded, so they need not be copied between registers
+  // (4-13 fewer VALU instructions per K tile).  The packed modes over several
+  // rows without the on-chip gather keep one set (a copy per tile): with two
+  // they pass 128 VGPRs, which would cut the waves a CU holds from 4 to 3.
+  static_assert(RUN % 2 == 0, "the pending sets alternate by slot parity");
+  constexpr int NB = (is_packed(AM) && AM != AM_XGATHER && !ONE) ? 1 : 2;
+  float4_t pat[NB][PDA], paz[NB][PDZ];
+  float psf[NB];
 #pragma unroll
-  for (int q = 0; q < PDA; ++q) pat[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) {
+    psf[b] = 0.f;
 #pragma unroll
-  for (int q = 0; q < PDZ; ++q) paz[q] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float psf = 0.f;
+    for (int q = 0; q < PDA; ++q) pat[b][q] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < PDZ; ++q) paz[b][q] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
   // FOLD, FFOLD: the offsets of the raw code and zero operands, set once and
   // held in registers for the whole loop (made per tile, each tile's branch
   // would set them again)
@@ -830,6 +843,8 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
             const float4_t z4 = float4_t{0.f, 0.f, 0.f, 0.f};
             if constexpr (XG && ONE) ra[sa][0] = xg_assemble1<DT>(g1[sa]);
             wp.raw_operands(ring[s], rq, b);
+            // this tile's set and the previous tile's (unrolled: fixed)
+            const int cb = NB == 2 ? (s & 1) : 0, pb = NB == 2 ? (cb ^ 1) : 0;
             float4_t at[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) at[j] = mfma16x16x32<DT>(ra[sa][0], b[j], z4);
@@ -840,12 +855,12 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
             for (int u = 0; u < WP::kU; ++u) az[u] = mfma16x16x32<DT>(ra[sa][0], bz[u], z4);
             const float sf = WP::fold_scale(mc, s, lane);
             // the previous tile's results, while this tile's MFMAs run
-            fold_packed(pat, paz, psf);
+            fold_packed(pat[pb], paz[pb], psf[pb]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pat[j] = at[j];
+            for (int j = 0; j < 4; ++j) pat[cb][j] = at[j];
 #pragma unroll
-            for (int u = 0; u < WP::kU; ++u) paz[u] = az[u];
-            psf = sf;
+            for (int u = 0; u < WP::kU; ++u) paz[cb][u] = az[u];
+            psf[cb] = sf;
           } else {
             if constexpr (FFOLD) wp.raw_operands(ring[s], rq, b);
             else wp.operands(ring[s], s, mc, b);
@@ -860,26 +875,21 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
               if constexpr (FFOLD) {
                 typename Op<DT>::vec bz[1];
                 WP::zero_operands(mc, s, rq, bz);
-                const float sf = WP::fold_scale(mc, s, lane);
-                float4_t tq[MT], tz[MT];
+                // this tile's set and the previous tile's (unrolled: fixed)
+                const int cb = s & 1, pb = cb ^ 1;
+                psf[cb] = WP::fold_scale(mc, s, lane);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                  tq[m] = float4_t{0.f, 0.f, 0.f, 0.f};
-                  tz[m] = tq[m];
+                  pat[cb][m] = float4_t{0.f, 0.f, 0.f, 0.f};
+                  paz[cb][m] = pat[cb][m];
 #pragma unroll
                   for (int j = 0; j < 4; ++j) {
-                    tq[m] = mfma16x16x32<DT>(at[m * 4 + j], b[j], tq[m]);
-                    tz[m] = mfma16x16x32<DT>(at[m * 4 + j], bz[0], tz[m]);
+                    pat[cb][m] = mfma16x16x32<DT>(at[m * 4 + j], b[j], pat[cb][m]);
+                    paz[cb][m] = mfma16x16x32<DT>(at[m * 4 + j], bz[0], paz[cb][m]);
                   }
                 }
                 // the previous tile's sums, while this tile's MFMAs run
-                fold_full(pat, paz, psf);
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                  pat[m] = tq[m];
-                  paz[m] = tz[m];
-                }
-                psf = sf;
+                fold_full(pat[pb], paz[pb], psf[pb]);
               } else {
                 mma_tile<DT, AM, MT, NA, NACC>(b, at, acc);
               }
@@ -903,9 +913,15 @@ __device__ __forceinline__ void decode_body(const uint16_t* __restrict__ x,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the last tile's results
-    fold_packed(pat, paz, psf);
-    fold_full(pat, paz, psf);
+    // the last tile's results: its set is that of its slot, (n - 1) % RUN,
+    // whose parity is that of n - 1
+    if (NB == 2 && ((n - 1) & 1)) {
+      fold_packed(pat[NB - 1], paz[NB - 1], psf[NB - 1]);
+      fold_full(pat[NB - 1], paz[NB - 1], psf[NB - 1]);
+    } else {
+      fold_packed(pat[0], paz[0], psf[0]);
+      fold_full(pat[0], paz[0], psf[0]);
+    }
   }
 
   // ---- v_mfma_f32_16x16x32 result layout: element e of lane l is row
